@@ -1,0 +1,81 @@
+"""Mutation check of the oracle pins (CPU only).
+
+Each mutant is a copy of oracle/oracle.c with one plausible mistake planted in
+it (a dropped term, a wrong sign or offset, swapped nibbles, a transposed
+operand, a misused leading dimension, a wrong tie rule, a wrong rounding).
+The mutant is compiled into a temporary library and every pin in
+test_oracle_pins.py is run against it: at least one pin must fail.  The
+planted mistakes exist only in the temporary copies, never in oracle.c.
+"""
+import inspect
+import os
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.c")
+
+MUTANTS = [
+    ("nibble order swapped", "int lo = wb[2 + i] & 0x0F;   /* weight i      */\n                    int hi = wb[2 + i] >> 4;",
+     "int lo = wb[2 + i] >> 4;   /* weight i      */\n                    int hi = wb[2 + i] & 0x0F;"),
+    ("offset -8 dropped", "isum += (lo - 8) * q8[i] + (hi - 8) * q8[i + 16];", "isum += lo * q8[i] + hi * q8[i + 16];"),
+    ("offset sign flipped on high nibble", "(hi - 8) * q8[i + 16]", "(hi + 8) * q8[i + 16]"),
+    ("high nibble paired with wrong activation", "(hi - 8) * q8[i + 16]", "(hi - 8) * q8[i]"),
+    ("activation scale taken from column 0", "const uint8_t* xb = Xq + (m * nb + b) * 36;", "const uint8_t* xb = Xq + b * 36;"),
+    ("weight scale ignored", "acc += d4 * d8 * (double)isum;", "acc += d8 * (double)isum;"),
+    ("last dense term dropped", "for (int64_t k = 0; k < K; ++k)\n            acc += orc_half_to_double",
+     "for (int64_t k = 0; k + 1 < K; ++k)\n            acc += orc_half_to_double"),
+    ("dense W transposed", "acc += orc_half_to_double(W[n * ldw + k])", "acc += orc_half_to_double(W[k * ldw + n])"),
+    ("leading dimension ignored", "acc += orc_bf16_to_double(W[n * ldw + k])", "acc += orc_bf16_to_double(W[n * K + k])"),
+    ("half subnormal exponent off by one", "v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    ("half normal bias off by one", "v = ldexp((double)(1024 + frac), expo - 25);", "v = ldexp((double)(1024 + frac), expo - 24);"),
+    ("bf16 bias off by one", "v = ldexp((double)(128 + frac), expo - 134);", "v = ldexp((double)(128 + frac), expo - 133);"),
+    ("half rounding ties away", "return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
+    ("q4_0 scale sign dropped", "float d = m / -8.0f;", "float d = m / 8.0f;"),
+    ("q4_0 rounding offset", "float v = x[j] / d + 8.5f;", "float v = x[j] / d + 8.0f;"),
+    ("q4_0 magnitude ties take the last", "if (a > amax) { amax = a; m = x[j]; }", "if (a >= amax) { amax = a; m = x[j]; }"),
+    ("q8_1 rounds half to even", "float r = roundf(x[j] / d);", "float r = rintf(x[j] / d);"),
+    ("q8_1 block sum unscaled", "orc_float_to_half_rne(d * (float)sum)", "orc_float_to_half_rne((float)sum)"),
+    ("argmax last index wins ties", "if (isnan(v) || v > bv)", "if (isnan(v) || v >= bv)"),
+    ("argmax ignores NaN", "if (isnan(v) || v > bv)", "if (v > bv)"),
+    ("argmax ignores ld", "const float* row = x + r * ld;", "const float* row = x + r * C;"),
+    ("checksum xor instead of add", "for (size_t i = 0; i < n; ++i) s += w[i];", "for (size_t i = 0; i < n; ++i) s ^= w[i];"),
+]
+
+
+def _pin_calls():
+    calls = []
+    for name, fn in sorted(vars(pins).items()):
+        if not name.startswith("test_") or not callable(fn):
+            continue
+        params = inspect.signature(fn).parameters
+        if "fmt" in params:
+            calls += [(f"{name}[{f}]", fn, {"fmt": f}) for f in ("f16", "bf16")]
+        else:
+            calls.append((name, fn, {}))
+    return calls
+
+
+def test_mutant_list_applies_to_the_current_source():
+    src = open(SRC).read()
+    for name, old, _ in MUTANTS:
+        assert src.count(old) >= 1, name
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_some_pin_catches_the_mutant(tmp_path, orc, name, old, new):
+    src = open(SRC).read()
+    assert old in src
+    mutant = tmp_path / "oracle_mutant.c"
+    mutant.write_text(src.replace(old, new, 1))
+    lib = oracle.compile_c(str(mutant), str(tmp_path / "liboracle_mutant.so"))
+    failed = []
+    with oracle.use_library(lib):
+        for pin_name, fn, kw in _pin_calls():
+            try:
+                fn(orc, **kw)
+            except (AssertionError, ValueError, IndexError, OverflowError):
+                failed.append(pin_name)
+    assert failed, f"no pin caught the mutant '{name}'"

@@ -1,0 +1,352 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each test ties an oracle routine to the pages' definitions, to exact
+mathematics (rational arithmetic, closed forms, brute force on tiny inputs) or
+to an independent library routine (numpy's binary16 casts, numpy.argmax), so
+that a plausible mistake -- a dropped term, a wrong sign, a swapped nibble, a
+transposed operand, a misused leading dimension -- fails at least one of them.
+CPU only.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _hex(s):
+    return np.frombuffer(bytes.fromhex(s.replace(" ", "")), dtype=np.uint8)
+
+
+# ---------------------------------------------------------------------------
+# binary16 / bfloat16 decoding and rounding (IEEE-754 definition vs numpy)
+# ---------------------------------------------------------------------------
+
+def test_half_decode_matches_numpy_for_every_pattern(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([orc.half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # sign of zero is kept
+    assert math.copysign(1.0, orc.half_to_double(0x8000)) == -1.0
+
+
+def test_bf16_decode_matches_float32_upper_half_for_every_pattern(orc):
+    bits = np.arange(65536, dtype=np.uint32)
+    ref = (bits << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    got = np.array([orc.bf16_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_float_to_half_rne_matches_numpy(orc):
+    g = np.random.default_rng(1)
+    # random bit patterns over every exponent, plus exact midpoints between halves
+    rnd = g.integers(0, 2**32, size=200_000, dtype=np.uint64).astype(np.uint32).view(np.float32)
+    h = np.arange(0, 0x7C00, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    mids = ((h[:-1] + h[1:]) / 2).astype(np.float32)          # exact in float32 (12 bits)
+    near = np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf))
+    edge = np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 65536.0, 1e30, 5.96e-8, 2.98e-8,
+                     2.9802322e-08, 2.9802326e-08, 6.1e-5, np.inf, -np.inf], dtype=np.float32)
+    vals = np.concatenate([rnd, mids, -mids, near[0], near[1], edge]).astype(np.float32)
+    ref = vals.astype(np.float16).view(np.uint16)
+    got = np.array([orc.float_to_half_rne(float(v)) for v in vals], dtype=np.uint16)
+    isn = np.isnan(vals)
+    assert np.array_equal(got[~isn], ref[~isn])
+    assert np.all((got[isn] & 0x7C00) == 0x7C00) and np.all((got[isn] & 0x3FF) != 0)
+
+
+# ---------------------------------------------------------------------------
+# dense GEMV: exact rational sums, closed forms, layout
+# ---------------------------------------------------------------------------
+
+def _exact_gemv(Wf, xf):
+    """Exact rational y = W x from float64 values (binary16/bfloat16 are exact there)."""
+    out = []
+    for row in Wf:
+        out.append(sum((Fraction(float(a)) * Fraction(float(b)) for a, b in zip(row, xf)), Fraction(0)))
+    return out
+
+
+def _check_fp64_sum(y, Wf, xf):
+    """|y - exact| <= gamma_K * sum |w x|, the error bound of a recursive fp64 sum."""
+    K = Wf.shape[1]
+    u = 2.0 ** -53
+    gamma = K * u / (1 - K * u)
+    exact = _exact_gemv(Wf, xf)
+    for n in range(Wf.shape[0]):
+        bound = gamma * float(np.sum(np.abs(Wf[n] * xf)))
+        assert abs(Fraction(float(y[n])) - exact[n]) <= Fraction(bound) + Fraction(0), (n, y[n], float(exact[n]))
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_dense_gemv_against_exact_rationals_non_square(orc, fmt):
+    g = np.random.default_rng(7)
+    N, K = 5, 24                         # N != K catches a transposed operand
+    Wf32 = (g.standard_normal((N, K)) * 0.02).astype(np.float32)
+    xf32 = g.standard_normal(K).astype(np.float32)
+    # adversarial row: large cancelling terms plus small ones
+    Wf32[2, :4] = [1000.0, -1000.0, 0.001, 3.0]
+    if fmt == "f16":
+        Wb, xb = Wf32.astype(np.float16).view(np.uint16), xf32.astype(np.float16).view(np.uint16)
+        Wf, xf = Wb.view(np.float16).astype(np.float64), xb.view(np.float16).astype(np.float64)
+        y = orc.gemv_f16(Wb, xb)
+    else:
+        import synth
+        Wb, xb = synth.to_bf16_bits(Wf32), synth.to_bf16_bits(xf32)
+        Wf = (Wb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        xf = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        y = orc.gemv_bf16(Wb, xb)
+    assert y.shape == (N,)
+    _check_fp64_sum(y, Wf, xf)
+    # a dropped term anywhere shows up: every product is far above the fp64 error
+    prods = np.abs(Wf * xf)
+    assert np.all(np.abs(y - Wf @ xf) < 1e-3 * prods[prods > 0].min())
+
+
+def test_gemv_f16_small_integers_are_exact(orc):
+    # all-ones W with small-integer x: y = sum x exactly
+    K = 40
+    x = np.arange(-20, 20, dtype=np.float16)
+    W = np.ones((3, K), dtype=np.float16)
+    W[1] *= -1
+    W[2, ::2] = 0
+    y = orc.gemv_f16(W.view(np.uint16), x.view(np.uint16))
+    assert y.tolist() == [float(x.astype(np.float64).sum()), -float(x.astype(np.float64).sum()),
+                          float(x.astype(np.float64)[1::2].sum())]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_one_hot_x_selects_a_column_and_ldw_padding_is_ignored(orc, fmt):
+    import synth
+    g = np.random.default_rng(3)
+    N, K, ldw = 6, 16, 24
+    Wf32 = g.standard_normal((N, ldw)).astype(np.float32)
+    Wb = Wf32.astype(np.float16).view(np.uint16) if fmt == "f16" else synth.to_bf16_bits(Wf32)
+    Wb = Wb.copy()
+    Wb[:, K:] = 0x7E00 if fmt == "f16" else 0x7FC0      # NaN in the padding
+    dec = (lambda b: b.view(np.float16).astype(np.float64)) if fmt == "f16" else \
+          (lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    fn = orc.gemv_f16 if fmt == "f16" else orc.gemv_bf16
+    one = np.uint16(0x3C00 if fmt == "f16" else 0x3F80)
+    for k in (0, 5, K - 1):
+        x = np.zeros(K, dtype=np.uint16)
+        x[k] = one
+        y = fn(Wb, x, N=N, K=K, ldw=ldw)
+        assert np.array_equal(y, dec(Wb[:, k]))
+
+
+def test_dense_gemv_agrees_with_numpy_fp64_matmul(orc):
+    import synth
+    W = synth.normal_f16_bits((0, 0, 0, 0), (64, 512), 0.02)
+    x = synth.normal_f16_bits((0, 1, 0, 0), (512,), 1.0)
+    y = orc.gemv_f16(W, x)
+    ref = W.view(np.float16).astype(np.float64) @ x.view(np.float16).astype(np.float64)
+    assert np.max(np.abs(y - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+def test_subnormal_halves_are_kept(orc):
+    # a row made only of binary16 subnormals (|w| < 2^-14) times x = 1
+    W = np.arange(1, 1025, dtype=np.uint32).astype(np.uint16).reshape(1, -1)      # every positive subnormal
+    x = np.full(1024, 0x3C00, dtype=np.uint16)
+    y = orc.gemv_f16(W, x)
+    assert y[0] == sum(range(1, 1025)) * 2.0 ** -24
+
+
+# ---------------------------------------------------------------------------
+# Q4_0 x Q8_1
+# ---------------------------------------------------------------------------
+
+def _golden():
+    with open(os.path.join(GOLDEN, "q4_0_q8_1_worked.json")) as f:
+        return json.load(f)
+
+
+def test_q4_0_worked_blocks(orc):
+    for ex in _golden()["dot_examples"]:
+        W, X = _hex(ex["q4_0_block_hex"]), _hex(ex["q8_1_block_hex"])
+        assert W.size == 18 and X.size == 36
+        y = orc.gemv_q4_0_q8_1(W, X, N=1, K=32, M=1)
+        assert y[0, 0] == ex["y"], ex["name"]
+
+
+def _py_decode_q4_0(blk):
+    d = Fraction(float(np.frombuffer(bytes(blk[:2]), dtype=np.float16)[0]))
+    vals = [None] * 32
+    for i in range(16):
+        vals[i] = (int(blk[2 + i]) & 15) - 8
+        vals[i + 16] = (int(blk[2 + i]) >> 4) - 8
+    return [d * v for v in vals]
+
+
+def _py_decode_q8_1(blk):
+    d = Fraction(float(np.frombuffer(bytes(blk[:2]), dtype=np.float16)[0]))
+    return [d * int(v) for v in np.frombuffer(bytes(blk[4:36]), dtype=np.int8)]
+
+
+def _random_blocks(g, nblk, kind):
+    size = 18 if kind == "q4" else 36
+    b = g.integers(0, 256, size=(nblk, size), dtype=np.uint8)
+    scales = (g.standard_normal(nblk) * 0.3).astype(np.float16).view(np.uint16)
+    b[:, 0] = scales & 0xFF
+    b[:, 1] = scales >> 8
+    return b
+
+
+def test_q4_0_against_brute_force_dequantise_then_dot(orc):
+    """Dequantise every weight and activation to an exact rational and sum all
+    products: a different route to the same definition, in exact arithmetic."""
+    g = np.random.default_rng(11)
+    N, K, M = 3, 96, 2
+    nb = K // 32
+    W = _random_blocks(g, N * nb, "q4")
+    X = _random_blocks(g, M * nb, "q8")
+    Y = orc.gemv_q4_0_q8_1(W, X, N=N, K=K, M=M)
+    for m in range(M):
+        xv = sum((_py_decode_q8_1(X[m * nb + b]) for b in range(nb)), [])
+        for n in range(N):
+            wv = sum((_py_decode_q4_0(W[n * nb + b]) for b in range(nb)), [])
+            exact = sum((a * c for a, c in zip(wv, xv)), Fraction(0))
+            # the oracle's only rounding is the fp64 sum over nb exactly-scaled blocks
+            assert abs(Fraction(float(Y[m, n])) - exact) <= abs(exact) * Fraction(nb, 2 ** 52) + Fraction(1, 2 ** 1000)
+
+
+def test_q4_0_oracle_dequant_helpers_match_python_decoding(orc):
+    g = np.random.default_rng(5)
+    for blk in _random_blocks(g, 8, "q4"):
+        assert [Fraction(v) for v in orc.dequant_q4_0_block(blk)] == _py_decode_q4_0(blk)
+    for blk in _random_blocks(g, 8, "q8"):
+        assert [Fraction(v) for v in orc.dequant_q8_1_block(blk)] == _py_decode_q8_1(blk)
+
+
+def test_q4_0_invariants(orc):
+    g = np.random.default_rng(13)
+    N, K = 4, 128
+    nb = K // 32
+    W = _random_blocks(g, N * nb, "q4")
+    X1 = _random_blocks(g, nb, "q8")
+    # identical activation columns give identical output columns
+    X = np.concatenate([X1, X1, X1])
+    Y = orc.gemv_q4_0_q8_1(W, X, N=N, K=K, M=3)
+    assert np.array_equal(Y[0], Y[1]) and np.array_equal(Y[0], Y[2])
+    # doubling every weight scale (exact in binary16 here) doubles y exactly
+    d = W[:, :2].copy().view(np.uint16).reshape(-1).view(np.float16)
+    if np.all(np.abs(d.astype(np.float32)) < 1000):
+        W2 = W.copy()
+        W2[:, :2] = (d.astype(np.float32) * 2).astype(np.float16).view(np.uint8).reshape(-1, 2)
+        Y2 = orc.gemv_q4_0_q8_1(W2, X1, N=N, K=K, M=1)
+        assert np.array_equal(Y2[0], 2 * Y[0])
+    # the -8 offset: codes all 8 give y = 0 whatever the activations
+    W8 = W.copy()
+    W8[:, 2:] = 0x88
+    assert np.all(orc.gemv_q4_0_q8_1(W8, X1, N=N, K=K, M=1) == 0)
+
+
+def test_q4_0_quantiser_worked_blocks(orc):
+    for ex in _golden()["q4_0_quantiser_examples"]:
+        j = np.arange(32)
+        tie = np.zeros(32)
+        tie[:2] = [-2, 2]
+        x = {"(j-16)/4 for j in 0..31": (j - 16) / 4, "(16-j)/4 for j in 0..31": (16 - j) / 4,
+             "0 for j in 0..31": np.zeros(32), "[-2, 2, 0 x 30]": tie}[ex["x"]].astype(np.float32)
+        got = orc.quantize_q4_0(x.reshape(1, 32))
+        assert bytes(got.reshape(-1)) == bytes(_hex(ex["block_hex"])), ex["name"]
+
+
+def test_q8_1_quantiser_worked_blocks(orc):
+    for ex in _golden()["q8_1_quantiser_examples"]:
+        x = np.array(ex["x"], dtype=np.float32).reshape(1, 32)
+        got = orc.quantize_q8_1(x)
+        assert bytes(got.reshape(-1)) == bytes(_hex(ex["block_hex"])), ex["name"]
+
+
+def test_quantiser_properties_on_random_blocks(orc):
+    g = np.random.default_rng(17)
+    w = g.standard_normal((64, 256)).astype(np.float32)
+    Wq = orc.quantize_q4_0(w).reshape(-1, 18)
+    blocks = w.reshape(-1, 32)
+    for blk, x in zip(Wq, blocks):
+        m = x[np.argmax(np.abs(x))]
+        d32 = np.float32(m) / np.float32(-8.0)
+        assert np.frombuffer(bytes(blk[:2]), np.float16)[0] == np.float16(d32)
+        codes = np.concatenate([blk[2:] & 15, blk[2:] >> 4]).astype(np.int64)
+        assert codes[np.argmax(np.abs(x))] == 0                 # the extreme value maps to q = 0
+        err = np.abs(x.astype(np.float64) - (codes - 8) * float(d32))
+        clamped = codes == 15
+        assert np.all(err[~clamped] <= abs(float(d32)) * (0.5 + 1e-5))
+        assert np.all(err[clamped] <= abs(float(d32)) * (1.0 + 1e-5))
+    a = g.standard_normal((8, 256)).astype(np.float32)
+    Xq = orc.quantize_q8_1(a).reshape(-1, 36)
+    for blk, x in zip(Xq, a.reshape(-1, 32)):
+        d32 = np.float32(np.max(np.abs(x))) / np.float32(127.0)
+        q = np.frombuffer(bytes(blk[4:]), np.int8).astype(np.int64)
+        assert np.frombuffer(bytes(blk[:2]), np.float16)[0] == np.float16(d32)
+        assert abs(q[np.argmax(np.abs(x))]) == 127
+        assert np.all(np.abs(x - q * float(d32)) <= float(d32) * (0.5 + 1e-5))
+        s = np.frombuffer(bytes(blk[2:4]), np.float16)[0]
+        assert s == np.float16(d32 * np.float32(q.sum()))
+
+
+# ---------------------------------------------------------------------------
+# argmax
+# ---------------------------------------------------------------------------
+
+def _parse(v):
+    return {"-0": -0.0, "+0": 0.0, "nan": math.nan, "inf": math.inf, "-inf": -math.inf}.get(v, v) \
+        if isinstance(v, str) else float(v)
+
+
+def test_argmax_hand_rows(orc):
+    with open(os.path.join(GOLDEN, "argmax_rows.json")) as f:
+        rows = json.load(f)["rows"]
+    for r in rows:
+        x = np.array([_parse(v) for v in r["x"]], dtype=np.float32)
+        assert orc.argmax_rows(x)[0] == r["idx"], r
+
+
+def test_argmax_brute_force_against_numpy_with_heavy_ties(orc):
+    g = np.random.default_rng(19)
+    R, C, ld = 200, 77, 80
+    x = g.integers(0, 3, size=(R, ld)).astype(np.float32)
+    x[:, C:] = 1e30                                   # padding beyond C must be ignored
+    x[5, 10] = np.nan
+    x[6, [3, 40]] = np.nan
+    x[7, :] = -0.0
+    x[7, 9] = 0.0
+    idx = orc.argmax_rows(x, C=C, ld=ld)
+    ref = np.argmax(x[:, :C], axis=1)                 # numpy: first max, first NaN
+    assert np.array_equal(idx, ref)
+
+
+def test_argmax_is_invariant_under_any_chunking(orc):
+    g = np.random.default_rng(23)
+    x = g.integers(0, 4, size=(1, 1000)).astype(np.float32)
+    whole = orc.argmax_rows(x)[0]
+    for chunk in (1, 7, 64, 333):
+        best = None
+        for c0 in range(0, 1000, chunk):
+            i = c0 + int(orc.argmax_rows(x[:, c0:c0 + chunk].copy())[0])
+            if best is None or x[0, i] > x[0, best]:
+                best = i
+        assert best == whole
+
+
+# ---------------------------------------------------------------------------
+# streaming-read checksum
+# ---------------------------------------------------------------------------
+
+def test_checksum_closed_forms(orc):
+    assert orc.checksum_u32(np.zeros(1000, np.uint32)) == 0
+    n = 1 << 20
+    assert orc.checksum_u32(np.arange(n, dtype=np.uint32)) == (n * (n - 1) // 2) % 2**32
+    assert orc.checksum_u32(np.full(3, 0xFFFFFFFF, np.uint32)) == (3 * 0xFFFFFFFF) % 2**32
+    g = np.random.default_rng(29)
+    w = g.integers(0, 2**32, size=12345, dtype=np.uint64).astype(np.uint32)
+    assert orc.checksum_u32(w) == int(sum(int(v) for v in w)) % 2**32
