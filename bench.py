@@ -1,0 +1,513 @@
+#!/usr/bin/env python3
+"""Benchmark of the decode GEMV path on one MI355X.
+
+Default run (the headline line): one "step" is one batch-1 decode pass over the
+two M = 1 GEMVs the metric names:
+  * fp16 y[4096] = W[4096x4096] x[4096], W rotated over 32 seeded copies (1.07 GB);
+  * Q4_0 x Q8_1 y[28672] = W[28672x8192] x[8192], W rotated over 9 seeded copies
+    (1.19 GB), fp32 out.
+Working sets exceed four times the 256 MB last-level cache, so every weight
+byte comes from HBM.  Inputs are synthetic (seeded device-side draws of the
+pages' distributions), resident in HBM before the timed region.  The timed
+region replays a HIP graph of exactly --steps steps between two events (launch
+overhead of a per-call Python loop would otherwise dominate a 5 us kernel).
+
+Printed: ONE JSON line with the aggregate algorithmic GB/s of the step, a
+per-kernel breakdown (us/call as the median of 30 repetitions of back-to-back
+rotated calls after 10 warm-ups, GB/s, bandwidth utilisation against the
+streaming-read ceiling measured in the same run and against the 8 TB/s spec),
+the roofline of the dominant kernel (Q4_0) and the CPU oracle timed on a
+bounded sample.
+
+--suite instead measures every configuration of the path (ceiling sweep, the
+fp16 ablation variants, bf16 decoder shapes, the lm-head, Q4_0 M = 1..24,
+argmax, the greedy tail) and writes one JSON record per measurement.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "M=1 decode GEMV µs/call, achieved HBM GB/s and MBU (fp16 and Q4_0)"
+SPEC_GBPS = 8000.0
+LLC_BYTES = 256 << 20
+GIB = 1 << 30
+
+
+# ---------------------------------------------------------------------------
+# byte models (algorithmic bytes: every byte counted once)
+# ---------------------------------------------------------------------------
+
+def bytes_dense(N, K, out_bytes):
+    return 2 * N * K + 2 * K + out_bytes * N
+
+
+def bytes_q4(N, K, M):
+    return 18 * N * K // 32 + M * 36 * K // 32 + 4 * M * N
+
+
+def copies_for(nbytes, floor=4 * LLC_BYTES):
+    return max(2, -(-floor // nbytes))
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def capture(calls):
+    """A HIP graph of the given launches (each a zero-argument callable)."""
+    torch = _torch()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in calls[: min(len(calls), 4)]:
+            c()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_per_call(calls, reps=30, warm=10, graph=True):
+    """Median and inter-quartile range (us per call) of `reps` timed runs of the
+    back-to-back calls, after `warm` untimed runs."""
+    torch = _torch()
+    if graph:
+        g = capture(calls)
+        run = g.replay
+    else:
+        def run():
+            for c in calls:
+                c()
+    for _ in range(warm):
+        run()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / len(calls))
+    ts.sort()
+    q = statistics.quantiles(ts, n=4) if len(ts) >= 4 else [ts[0], ts[len(ts) // 2], ts[-1]]
+    return statistics.median(ts), q[2] - q[0]
+
+
+def record(name, us, iqr, nbytes, ceiling, **extra):
+    gbps = nbytes / (us * 1e-6) / 1e9
+    r = {"name": name, "us_per_call": round(us, 3), "iqr_us": round(iqr, 3), "bytes": int(nbytes),
+         "gbps": round(gbps, 1), "mbu_spec": round(gbps / SPEC_GBPS, 4)}
+    if ceiling:
+        r["mbu_ceiling"] = round(gbps / ceiling, 4)
+    r.update(extra)
+    return r
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# operand builders (device-side seeded draws; quantisation by the library)
+# ---------------------------------------------------------------------------
+
+def dense_copies(cfg, N, K, ncopies, dtype):
+    import synth
+    torch = _torch()
+    Ws = [synth.gpu_normal((cfg, synth.KIND_W, c, 0), (N, K), 0.02, dtype) for c in range(ncopies)]
+    x = synth.gpu_normal((cfg, synth.KIND_X, 0, 0), (K,), 1.0, dtype)
+    torch.cuda.synchronize()
+    return Ws, x
+
+
+def q4_copies(cfg, N, K, ncopies):
+    import synth
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    Ws = []
+    for c in range(ncopies):
+        w = synth.gpu_normal((cfg, synth.KIND_W, c, 0), (N, K), 1.0, torch.float32)
+        Wq = torch.empty(N * (K // 32) * 18, dtype=torch.uint8, device="cuda")
+        dg.dg_quantize_q4_0(w, Wq, N, K)
+        torch.cuda.synchronize()
+        del w
+        Ws.append(Wq)
+    return Ws
+
+
+def q8_columns(cfg, K, M):
+    import synth
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    x = torch.stack([synth.gpu_normal((cfg, synth.KIND_X, 0, m), (K,), 1.0, torch.float32) for m in range(M)])
+    Xq = torch.empty(M * (K // 32) * 36, dtype=torch.uint8, device="cuda")
+    dg.dg_quantize_q8_1(x.contiguous(), Xq, M, K)
+    torch.cuda.synchronize()
+    return Xq
+
+
+# ---------------------------------------------------------------------------
+# the streaming-read ceiling
+# ---------------------------------------------------------------------------
+
+def measure_ceiling(full_sweep=False, records=None):
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    nbytes = 8 * GIB
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(1)
+    cs = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grids = [1024, 2048, 4096, 8192, 16384] if full_sweep else [2048, 4096, 8192]
+    blocks = [256, 512, 1024] if full_sweep else [256, 512]
+    nts = [1, 0] if full_sweep else [1]
+    best = None
+    for nt in nts:
+        for grid in grids:
+            for block in blocks:
+                def call(grid=grid, block=block, nt=nt):
+                    dg.dg_stream_read(buf, cs, nbytes=nbytes, grid_blocks=grid, block_threads=block, nontemporal=nt)
+                us, iqr = time_per_call([call] * 20, reps=5, warm=10, graph=False)
+                gbps = nbytes / (us * 1e-6) / 1e9
+                if records is not None:
+                    records.append(record("stream_read", us, iqr, nbytes, None, grid=grid, block=block,
+                                          nontemporal=nt))
+                if best is None or gbps > best[0]:
+                    best = (gbps, dict(grid=grid, block=block, nontemporal=nt), us)
+    del buf
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    log(f"[ceiling] {best[0]:.1f} GB/s at {best[1]} ({best[2]:.1f} us per 8 GiB read)")
+    return best
+
+
+# ---------------------------------------------------------------------------
+# the headline step
+# ---------------------------------------------------------------------------
+
+FP16_N = FP16_K = 4096
+Q4_N, Q4_K = 28672, 8192
+
+
+def traffic_from_profiles(kernel_src, per_launch_key):
+    """HBM bytes per launch from the committed counter summary, only while the
+    kernel source is unchanged since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        ent = data.get(per_launch_key)
+        if not ent:
+            return None
+        with open(kernel_src, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()[:16]
+        if ent.get("source_sha256_16") != h:
+            return None
+        return ent.get("hbm_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands (single-threaded C, fp64), timed on this host on a
+    bounded sample of the step: the full fp16 GEMV plus a quarter of the Q4_0
+    rows, repeated until the budget is spent."""
+    import numpy as np
+    import oracle
+    import synth
+    oracle.build()
+    Wb = synth.normal_f16_bits((0, synth.KIND_W, 0, 0), (FP16_N, FP16_K), 0.02)
+    xb = synth.normal_f16_bits((0, synth.KIND_X, 0, 0), (FP16_K,), 1.0)
+    rows = Q4_N // 4
+    Wq = oracle.quantize_q4_0(synth.normal_f32((2, synth.KIND_W, 0, 0), (rows, Q4_K)))
+    Xq = oracle.quantize_q8_1(synth.normal_f32((2, synth.KIND_X, 0, 0), (1, Q4_K)))
+    per = bytes_dense(FP16_N, FP16_K, 2) + bytes_q4(rows, Q4_K, 1)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemv_f16(Wb, xb)
+        oracle.gemv_q4_0_q8_1(Wq, Xq, rows, Q4_K, 1)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    del np
+    return {"value": round(per * n / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} x (fp16 GEMV 4096x4096 + Q4_0xQ8_1 GEMV {rows} of 28672 rows x 8192), "
+                      f"{el:.1f} s single-threaded on the host CPU"}
+
+
+def headline(args):
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    torch.cuda.init()
+    ceil_gbps, ceil_cfg, _ = measure_ceiling(full_sweep=False)
+
+    n16 = copies_for(2 * FP16_N * FP16_K)            # 32
+    W16, x16 = dense_copies(0, FP16_N, FP16_K, n16, torch.float16)
+    y16 = torch.empty(FP16_N, dtype=torch.float16, device="cuda")
+    nq = copies_for(18 * Q4_N * Q4_K // 32)          # 9
+    Wq = q4_copies(2, Q4_N, Q4_K, nq)
+    Xq = q8_columns(2, Q4_K, 1)
+    Yq = torch.empty(Q4_N, dtype=torch.float32, device="cuda")
+
+    def f16_call(c):
+        return lambda: dg.dg_gemv_f16(W16[c % n16], x16, y16)
+
+    def q4_call(c):
+        return lambda: dg.dg_gemv_q4_0(Wq[c % nq], Xq, Yq, Q4_N, Q4_K, 1)
+
+    b16 = bytes_dense(FP16_N, FP16_K, 2)
+    bq4 = bytes_q4(Q4_N, Q4_K, 1)
+
+    # per-kernel: back-to-back rotated calls (a whole rotation per timed run)
+    us16, iqr16 = time_per_call([f16_call(i) for i in range(max(20, n16))])
+    usq, iqrq = time_per_call([q4_call(i) for i in range(max(20, 3 * nq))])
+    log(f"[fp16 4096x4096] {us16:.2f} us/call, {b16 / us16 / 1e3:.0f} GB/s")
+    log(f"[q4_0 28672x8192] {usq:.2f} us/call, {bq4 / usq / 1e3:.0f} GB/s")
+
+    # the timed steps: exactly --steps steps in one graph, after --warmup steps
+    steps, warm = args.steps, args.warmup
+    step_calls = []
+    for s in range(steps):
+        step_calls += [f16_call(s), q4_call(s)]
+    g = capture(step_calls)
+    if warm:
+        gw = capture([c for s in range(warm) for c in (f16_call(s), q4_call(s))])
+        gw.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record()
+    g.replay()
+    e1.record()
+    e1.synchronize()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / steps
+    value = (b16 + bq4) / (ms_per_step * 1e-3) / 1e9
+
+    q4_src = os.path.join(ROOT, "memory_bound_decode_gemv_amd", "csrc", "gemv_q4_0.hip")
+    achieved = bq4 / (usq * 1e-6) / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16,q4_0xq8_1 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode GEMV step (batch 1): fp16 W[4096x4096] x[4096] over 32 rotated copies "
+                        "(1.07 GB) + Q4_0 W[28672x8192] x Q8_1 x[8192] over 9 rotated copies (1.19 GB)",
+            "launch": "one HIP graph of the timed steps",
+            "timed_wall_s": round(t_wall, 4),
+        },
+        "ceiling": {"gbps": round(ceil_gbps, 1), **ceil_cfg, "buffer_bytes": 8 * GIB},
+        "breakdown": {
+            "gemv_f16_4096x4096": record("gemv_f16", us16, iqr16, b16, ceil_gbps),
+            "gemv_q4_0_28672x8192_m1": record("gemv_q4_0", usq, iqrq, bq4, ceil_gbps),
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "gemv_q4_0 M=1 28672x8192",
+            "achieved": round(achieved, 1), "peak": SPEC_GBPS, "unit": "GB/s",
+            "frac": round(achieved / SPEC_GBPS, 4),
+            "traffic": traffic_from_profiles(q4_src, "gemv_q4_0_m1_28672x8192"),
+            "algorithmic_bytes_per_launch": bq4,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# the full suite
+# ---------------------------------------------------------------------------
+
+def suite(args):
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    recs = []
+
+    def emit(r):
+        recs.append(r)
+        log(json.dumps(r))
+        if args.suite_out:
+            with open(args.suite_out, "a") as f:
+                f.write(json.dumps(r) + "\n")
+
+    sweep = []
+    ceil_gbps, ceil_cfg, _ = measure_ceiling(full_sweep=True, records=sweep)
+    for r in sweep:
+        emit(r)
+    emit({"name": "ceiling", "gbps": round(ceil_gbps, 1), **ceil_cfg})
+
+    # fp16 4096x4096: the page's three versions and launch shapes
+    n16 = copies_for(2 * 4096 * 4096)
+    W16, x16 = dense_copies(0, 4096, 4096, n16, torch.float16)
+    y16 = torch.empty(4096, dtype=torch.float16, device="cuda")
+    b16 = bytes_dense(4096, 4096, 2)
+    variants = [("narrow1", dict(variant=3)), ("narrow4", dict(variant=4)), ("wide", dict(variant=1)),
+                ("xreg", dict(variant=2))]
+    for vname, v in variants:
+        for block in (64, 256):
+            for grid in (256, 512, 1024, 2048, 4096):
+                if grid * block // 64 > 4096 * 4:
+                    continue
+                launch = dict(v, grid=grid, block=block)
+                calls = [(lambda c=c, launch=launch: dg.dg_gemv_f16(W16[c % n16], x16, y16, launch=launch))
+                         for c in range(n16)]
+                us, iqr = time_per_call(calls)
+                emit(record("gemv_f16 4096x4096", us, iqr, b16, ceil_gbps, variant=vname, grid=grid, block=block))
+    calls = [(lambda c=c: dg.dg_gemv_f16(W16[c % n16], x16, y16)) for c in range(n16)]
+    us, iqr = time_per_call(calls)
+    emit(record("gemv_f16 4096x4096", us, iqr, b16, ceil_gbps, variant="default"))
+    us, iqr = time_per_call(calls, graph=False)
+    emit(record("gemv_f16 4096x4096", us, iqr, b16, ceil_gbps, variant="default", launch="eager"))
+    del W16
+    torch.cuda.empty_cache()
+
+    # bf16 decoder-layer shapes and the lm-head
+    for (N, K) in [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336), (128256, 4096)]:
+        nc = copies_for(2 * N * K)
+        Wb, xb = dense_copies(1, N, K, nc, torch.bfloat16)
+        yb = torch.empty(N, dtype=torch.float32, device="cuda")
+        nb = bytes_dense(N, K, 4)
+        calls = [(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, yb)) for c in range(max(nc, 8))]
+        us, iqr = time_per_call(calls)
+        emit(record(f"gemv_bf16 {N}x{K}", us, iqr, nb, ceil_gbps, copies=nc))
+        for grid in (512, 1024, 2048):
+            launch = dict(variant=1, grid=grid, block=256)
+            calls = [(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, yb, launch=launch)) for c in range(max(nc, 8))]
+            us, iqr = time_per_call(calls)
+            emit(record(f"gemv_bf16 {N}x{K}", us, iqr, nb, ceil_gbps, copies=nc, grid=grid, block=256))
+        del Wb
+        torch.cuda.empty_cache()
+
+    # Q4_0 M = 1 at the 70B MLP shape, default and variants
+    nq = copies_for(18 * Q4_N * Q4_K // 32)
+    Wq = q4_copies(2, Q4_N, Q4_K, nq)
+    Xq = q8_columns(2, Q4_K, 1)
+    Yq = torch.empty(Q4_N, dtype=torch.float32, device="cuda")
+    bq = bytes_q4(Q4_N, Q4_K, 1)
+    launches = [("default", None)] + [(f"regs g{g} b{b}", dict(variant=11, grid=g, block=b))
+                                      for g in (512, 1024, 2048, 4096, 7168) for b in (64, 256)] + \
+               [(f"lds R{r}", dict(variant=12, unroll=r)) for r in (1, 2, 4)]
+    for lname, launch in launches:
+        calls = [(lambda c=c, launch=launch: dg.dg_gemv_q4_0(Wq[c % nq], Xq, Yq, Q4_N, Q4_K, 1, launch=launch))
+                 for c in range(3 * nq)]
+        us, iqr = time_per_call(calls)
+        emit(record("gemv_q4_0 28672x8192 M=1", us, iqr, bq, ceil_gbps, variant=lname))
+    del Wq
+    torch.cuda.empty_cache()
+
+    # Q4_0 small-M sweep over the four 8B shapes
+    for (N, K) in [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)]:
+        nc = copies_for(18 * N * K // 32)
+        Wq = q4_copies(3, N, K, nc)
+        prev = None
+        for M in (1, 2, 4, 8, 12, 16, 24):
+            Xq = q8_columns(3, K, M)
+            Y = torch.empty(M * N, dtype=torch.float32, device="cuda")
+            calls = [(lambda c=c: dg.dg_gemv_q4_0(Wq[c % nc], Xq, Y, N, K, M)) for c in range(max(nc, 20))]
+            us, iqr = time_per_call(calls)
+            cps = M / (us * 1e-6)
+            dip = None if prev is None else round(cps / prev - 1.0, 4)
+            prev = cps
+            emit(record(f"gemv_q4_0 {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M, copies=nc,
+                        columns_per_s=round(cps, 1), change_vs_prev_M=dip))
+        del Wq
+        torch.cuda.empty_cache()
+
+    # argmax: hot (one buffer) and cold (rotated copies for the 256 MB shape)
+    import synth
+    for (R, C) in [(1, 128000), (32, 128000), (64, 1000000), (1, 128256)]:
+        ncold = copies_for(4 * R * C) if 4 * R * C >= LLC_BYTES // 4 else 1
+        xs = [synth.gpu_uniform((5, synth.KIND_X, c, 0), (R, C), -10.0, 10.0) for c in range(ncold)]
+        idx = torch.empty(R, dtype=torch.int64, device="cuda")
+        ws = torch.empty(max(8, dg.dg_argmax_workspace_bytes(R, C)), dtype=torch.uint8, device="cuda")
+        nb = 4 * R * C + 8 * R
+        calls = [(lambda: dg.dg_argmax_rows(xs[0], idx, ws=ws))] * 20
+        us, iqr = time_per_call(calls)
+        emit(record(f"argmax_rows [{R},{C}]", us, iqr, nb, ceil_gbps, cache="hot"))
+        if ncold > 1:
+            calls = [(lambda c=c: dg.dg_argmax_rows(xs[c % ncold], idx, ws=ws)) for c in range(max(20, ncold))]
+            us, iqr = time_per_call(calls)
+            emit(record(f"argmax_rows [{R},{C}]", us, iqr, nb, ceil_gbps, cache="cold", copies=ncold))
+        del xs
+        torch.cuda.empty_cache()
+
+    # the greedy tail: lm-head bf16 GEMV -> fp32 logits -> argmax
+    N, K = 128256, 4096
+    nc = copies_for(2 * N * K)
+    Wb, xb = dense_copies(4, N, K, nc, torch.bfloat16)
+    logits = torch.empty(N, dtype=torch.float32, device="cuda")
+    idx = torch.empty(1, dtype=torch.int64, device="cuda")
+    ws = torch.empty(dg.dg_argmax_workspace_bytes(1, N), dtype=torch.uint8, device="cuda")
+    calls = []
+    for c in range(8):
+        calls.append(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, logits))
+        calls.append(lambda: dg.dg_argmax_rows(logits.view(1, N), idx, ws=ws))
+    us, iqr = time_per_call(calls)
+    emit(record("greedy tail lm-head 128256x4096 + argmax", 2 * us, 2 * iqr,
+                bytes_dense(N, K, 4) + 4 * N + 8, ceil_gbps, note="us per token (two launches)"))
+    return recs
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--suite", action="store_true", help="measure every configuration instead")
+    ap.add_argument("--suite-out", default=None, help="append suite records (JSON lines) to this file")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards by output rows with no exchange, but no multi-GPU run exists here.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+    import memory_bound_decode_gemv_amd as dg
+    dg.raw()
+    if args.suite:
+        suite(args)
+    else:
+        headline(args)
+
+
+if __name__ == "__main__":
+    main()

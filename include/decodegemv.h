@@ -1,0 +1,222 @@
+/*
+ * decodegemv.h -- C ABI of libdecodegemv, the batch-1 / small-batch LLM decode
+ * matrix-vector product y = W x for AMD Instinct MI355X (gfx950, wave64).
+ *
+ * Every weight byte of a decode step is read once and never reused, so a call
+ * costs (bytes moved) / (HBM bandwidth); the kernels behind these calls are
+ * bandwidth kernels (batch1-cdna README, opening paragraph and "FP16 GEMV"
+ * section).
+ *
+ * Conventions shared by every call
+ *  - Pointers named d_* or documented as "device" are device (HBM) pointers
+ *    owned by the caller; the library never frees, retains or allocates them
+ *    and allocates no device memory of its own.
+ *  - Every call only enqueues work on `stream` (a hipStream_t; NULL means the
+ *    null stream) and returns without synchronising.  Outputs are valid once
+ *    the stream has reached that point.
+ *  - Arguments are checked before anything is enqueued.  On any error the
+ *    call returns a non-zero dg_status, launches nothing and writes nothing.
+ *    The library never aborts or exits.
+ *  - Sizes are element counts unless the name says bytes.  Empty work (a zero
+ *    row or column count) returns DG_OK and launches nothing.
+ *  - Thread-safety: calls carry no shared mutable state except the per-thread
+ *    text of the last HIP error.
+ */
+#ifndef DECODEGEMV_H
+#define DECODEGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DG_OK = 0,
+    DG_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    DG_ERR_MISALIGNED = 2,  /* a pointer or leading dimension breaks its alignment */
+    DG_ERR_SHAPE = 3,       /* a size or count is outside the documented contract  */
+    DG_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required          */
+    DG_ERR_HIP = 5,         /* the HIP runtime reported an error when launching    */
+    DG_ERR_ARG = 6          /* another argument (a launch override) is invalid     */
+} dg_status;
+
+/* A hipStream_t, kept opaque so that this header needs no HIP include. */
+typedef void* dg_stream;
+
+/* Static text for a status code. */
+const char* dg_status_string(dg_status status);
+
+/* Text of the last DG_ERR_HIP seen by the calling thread ("" if none). */
+const char* dg_last_hip_error(void);
+
+/* ------------------------------------------------------------------------
+ * Streaming-read ceiling probe
+ *
+ * Reads every byte of `buf` exactly once, 16 bytes per lane per load, in a
+ * grid-stride loop, and ADDS the wrapping (mod 2^32) sum of its little-endian
+ * 32-bit words into *d_checksum; the sum is what keeps the loads alive.  This
+ * is the denominator measurement of the batch1-cdna README ("01-ceiling":
+ * grid-stride read of a buffer far larger than the last-level cache with
+ * 4 x 32-bit vector loads, normal or non-temporal).
+ *
+ *   buf          device, 16-byte aligned, `bytes` long.
+ *   bytes        multiple of 16 (0 is allowed: nothing is launched).
+ *   d_checksum   device uint32; the caller zeroes it for a fresh sum.
+ *   grid_blocks  workgroups to launch; 0 = library default (2048).
+ *   block_threads threads per workgroup, a multiple of 64 in [64, 1024];
+ *                0 = library default (256).
+ *   nontemporal  0 = ordinary loads, 1 = non-temporal loads.
+ * Errors: DG_ERR_NULL (buf or d_checksum NULL with bytes > 0),
+ * DG_ERR_MISALIGNED (buf not 16-byte aligned, d_checksum not 4-byte aligned),
+ * DG_ERR_SHAPE (bytes % 16 != 0), DG_ERR_ARG (grid/block out of range).
+ * ------------------------------------------------------------------------ */
+dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_checksum,
+                         int grid_blocks, int block_threads, int nontemporal,
+                         dg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Dense GEMV, batch 1, fp32 accumulation
+ *
+ *   y[n] = sum_{k<K} W[n*ldw + k] * x[k],   0 <= n < N
+ *
+ * batch1-cdna README, "FP16 GEMV" section: one output element per row as the
+ * dot product of x with one row of W, products accumulated in fp32 and
+ * reduced across the lanes of a wavefront.  The summation order inside a row
+ * is fixed by the kernel, so results are bit-reproducible run to run.
+ *
+ *   W    device, row-major [N][ldw] of 16-bit values, 16-byte aligned.
+ *   x    device, [K] 16-bit values, 16-byte aligned.
+ *   N    rows (>= 0; 0 launches nothing).  N < 2^31.
+ *   K    columns used, multiple of 8, 0 <= K < 2^31 (K = 0 writes zeros).
+ *   ldw  row stride in elements, ldw >= K, ldw % 8 == 0.
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED (W or x not 16-byte aligned, y not
+ * aligned to its element), DG_ERR_SHAPE (K % 8, ldw < K, ldw % 8, negative or
+ * too large sizes), DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+
+/* binary16 operands; y is [N] binary16, rounded to nearest-even from the
+ * fp32 sum. */
+dg_status dg_gemv_f16(const void* W, const void* x, void* y,
+                      int64_t N, int64_t K, int64_t ldw, dg_stream stream);
+
+/* bfloat16 operands; y is [N] float32 (the fp32 sum itself). */
+dg_status dg_gemv_bf16(const void* W, const void* x, float* y,
+                       int64_t N, int64_t K, int64_t ldw, dg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Q4_0 weights x Q8_1 activations, M = 1..24 activation columns
+ *
+ *   Y[m][n] = sum_b d4(n,b) * d8(m,b) * sum_{j<32} (q4(n,b,j) - 8) * q8(m,b,j)
+ *
+ * The quantised-weight decode GEMV of "The kernel that waited for itself"
+ * (Q4_0/Q8_1 harness; the small-batch kernel for 1..24 columns) and of the
+ * 4-bit M = 1 GEMV of the bitsandbytes issue on 70B 4-bit decode.  The inner
+ * 32-term sum is exact in int32; the scaling and the sum over blocks are
+ * fp32.  The fp16 block sum s of Q8_1 is not used.
+ *
+ *   Wq  device, N rows of K/32 Q4_0 blocks, 18 bytes each (binary16 d, then 16
+ *       code bytes: byte i = weight i in the low nibble, weight i+16 in the
+ *       high nibble), rows packed back to back; 16-byte aligned.
+ *   Xq  device, M columns of K/32 Q8_1 blocks, 36 bytes each (binary16 d,
+ *       binary16 s, 32 int8 codes), column m starting at block m*K/32;
+ *       4-byte aligned.
+ *   Y   device float32 [M][N] (column m of the result at Y + m*N).
+ *   N   rows, 0 <= N < 2^31.  K: multiple of 256, 0 <= K < 2^31.
+ *   M   columns, 0 <= M <= 24 (0 launches nothing).
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+dg_status dg_gemv_q4_0(const void* Wq, const void* Xq, float* Y,
+                       int64_t N, int64_t K, int M, dg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Quantisers (the step before dg_gemv_q4_0)
+ *
+ * Q8_1, per 32-activation block: a = max|x|; d = a/127 (fp32); q = x/d
+ * rounded half away from zero, clamped to [-127, 127] (d = 0 gives q = 0);
+ * stored d = binary16(d), stored s = binary16(d * sum q).
+ * Q4_0, per 32-weight block: m = the first element of largest |x|, sign
+ * kept; d = m/-8 (fp32); q = min(15, floor(x/d + 8.5)) (d = 0 gives q = 8);
+ * stored d = binary16(d).
+ * The per-call conversion cost of activations is the subject of the
+ * "Capability Gain" paper's note on unfused conversion; the formats are those
+ * of the Q4_0/Q8_1 harness in "The kernel that waited for itself".
+ *
+ *   x / w   device float32 [M][K] / [N][K], 16-byte aligned, rows packed.
+ *   Xq / Wq device output, layouts as for dg_gemv_q4_0; Xq 4-byte aligned,
+ *           Wq 2-byte aligned.
+ *   K       multiple of 32.
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+dg_status dg_quantize_q8_1(const float* x, void* Xq, int64_t M, int64_t K,
+                           dg_stream stream);
+dg_status dg_quantize_q4_0(const float* w, void* Wq, int64_t N, int64_t K,
+                           dg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * argmax over rows (greedy sampling), lowest index on ties
+ *
+ *   idx[r] = min{ c < C : x[r*ld + c] = max_{c'<C} x[r*ld + c'] }
+ *
+ * IEEE comparisons (-0 equals +0); a NaN counts as larger than every number
+ * and the first NaN of a row wins.  Split reduction: each row is cut into
+ * chunks reduced by separate workgroups, then merged (IREE discussion
+ * "ArgCompare Benchmark Results", "VD_Split" in "Implementations Compared";
+ * the result does not depend on the chunking).  Any C is handled (no
+ * power-of-two padding).
+ *
+ *   x        device float32 [R][ld], 4-byte aligned.
+ *   idx      device int64 [R], 8-byte aligned.
+ *   R        rows, 0 <= R < 2^31 (0 launches nothing).
+ *   C        1 <= C < 2^31 - 1.   ld >= C.
+ *   ws       device workspace of at least dg_argmax_workspace_bytes(R, C)
+ *            bytes, 8-byte aligned; contents on entry do not matter; the
+ *            call owns it until the stream passes the call.  NULL is allowed
+ *            when the required size is 0.
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_WORKSPACE,
+ * DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+size_t dg_argmax_workspace_bytes(int64_t R, int64_t C);
+dg_status dg_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C,
+                         int64_t ld, void* ws, size_t ws_bytes, dg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Launch overrides (measurement and A/B runs)
+ *
+ * The *_ex variants take a launch configuration instead of the library's
+ * choice; a zero field means "library default".  `variant` selects a kernel
+ * variant by the ids below; 0 = default.  Invalid combinations return
+ * DG_ERR_ARG.  Results are identical to the plain calls except where a
+ * variant's summation order differs (documented per variant).
+ * ------------------------------------------------------------------------ */
+typedef struct {
+    int variant;   /* kernel variant id, 0 = default                       */
+    int grid;      /* workgroups, 0 = default                              */
+    int block;     /* threads per workgroup (multiple of 64), 0 = default  */
+    int unroll;    /* loads in flight per lane per step, 0 = default       */
+} dg_launch;
+
+enum {
+    /* dense GEMV */
+    DG_VARIANT_DENSE_WIDE = 1,      /* 16 B per lane, x reloaded per row (default for large K) */
+    DG_VARIANT_DENSE_XREG = 2,      /* 16 B per lane, x held in registers across rows (K <= 64*8*unroll) */
+    DG_VARIANT_DENSE_NARROW1 = 3,   /* 4 B per lane, one accumulator (ablation baseline)       */
+    DG_VARIANT_DENSE_NARROW4 = 4,   /* 4 B per lane, four accumulators (ablation)              */
+    /* Q4_0 */
+    DG_VARIANT_Q4_REGS = 11,        /* activations in registers, one row per wave (M = 1)       */
+    DG_VARIANT_Q4_LDS = 12          /* activations staged in LDS, several rows per wave          */
+};
+
+dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K,
+                         int64_t ldw, const dg_launch* cfg, dg_stream stream);
+dg_status dg_gemv_bf16_ex(const void* W, const void* x, float* y, int64_t N, int64_t K,
+                          int64_t ldw, const dg_launch* cfg, dg_stream stream);
+dg_status dg_gemv_q4_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K,
+                          int M, const dg_launch* cfg, dg_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODEGEMV_H */

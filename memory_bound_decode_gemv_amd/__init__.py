@@ -1,0 +1,267 @@
+"""Python binding of libdecodegemv (argument marshalling only).
+
+Each function has the name of the C entry point it calls (declared in
+include/decodegemv.h) and takes torch tensors that live in device memory.  It
+checks dtypes and devices, passes raw pointers, sizes and the current HIP
+stream to the C ABI, and raises DGError on a non-zero status.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback of any
+kind: without the built library on a GPU machine, every call raises.
+
+PyTorch is used only for device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdecodegemv.so")
+
+DG_OK = 0
+DG_ERR_NULL = 1
+DG_ERR_MISALIGNED = 2
+DG_ERR_SHAPE = 3
+DG_ERR_WORKSPACE = 4
+DG_ERR_HIP = 5
+DG_ERR_ARG = 6
+
+DG_VARIANT_DENSE_WIDE = 1
+DG_VARIANT_DENSE_XREG = 2
+DG_VARIANT_DENSE_NARROW1 = 3
+DG_VARIANT_DENSE_NARROW4 = 4
+DG_VARIANT_Q4_REGS = 11
+DG_VARIANT_Q4_LDS = 12
+
+# Every symbol include/decodegemv.h declares.
+EXPORTED = (
+    "dg_status_string", "dg_last_hip_error", "dg_stream_read",
+    "dg_gemv_f16", "dg_gemv_bf16", "dg_gemv_q4_0",
+    "dg_quantize_q8_1", "dg_quantize_q4_0",
+    "dg_argmax_workspace_bytes", "dg_argmax_rows",
+    "dg_gemv_f16_ex", "dg_gemv_bf16_ex", "dg_gemv_q4_0_ex",
+)
+
+
+class DGError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib().dg_status_string(status).decode()
+        if status == DG_ERR_HIP:
+            msg += " (" + _lib().dg_last_hip_error().decode() + ")"
+        super().__init__(f"{where}: {msg}")
+
+
+class dg_launch(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int), ("grid", ctypes.c_int),
+                ("block", ctypes.c_int), ("unroll", ctypes.c_int)]
+
+
+_handle = None
+
+
+def _hip_runtimes_mapped():
+    """Paths of every HIP runtime (libamdhip64) mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def _lib():
+    global _handle
+    if _handle is not None:
+        return _handle
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    # torch ships its own HIP runtime (same soname, libamdhip64.so.7).  Importing
+    # torch first makes libdecodegemv bind to that one runtime; loaded the other
+    # way round, the process would hold two runtimes that share neither streams
+    # nor graphs.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"two HIP runtimes are mapped into this process: {sorted(runtimes)}")
+    P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    st = ctypes.c_int
+    lib.dg_status_string.argtypes = [st]
+    lib.dg_status_string.restype = ctypes.c_char_p
+    lib.dg_last_hip_error.argtypes = []
+    lib.dg_last_hip_error.restype = ctypes.c_char_p
+    lib.dg_stream_read.argtypes = [P, ctypes.c_size_t, P, I32, I32, I32, P]
+    lib.dg_stream_read.restype = st
+    for n in ("dg_gemv_f16", "dg_gemv_bf16"):
+        getattr(lib, n).argtypes = [P, P, P, I64, I64, I64, P]
+        getattr(lib, n).restype = st
+        getattr(lib, n + "_ex").argtypes = [P, P, P, I64, I64, I64, ctypes.POINTER(dg_launch), P]
+        getattr(lib, n + "_ex").restype = st
+    lib.dg_gemv_q4_0.argtypes = [P, P, P, I64, I64, I32, P]
+    lib.dg_gemv_q4_0.restype = st
+    lib.dg_gemv_q4_0_ex.argtypes = [P, P, P, I64, I64, I32, ctypes.POINTER(dg_launch), P]
+    lib.dg_gemv_q4_0_ex.restype = st
+    lib.dg_quantize_q8_1.argtypes = [P, P, I64, I64, P]
+    lib.dg_quantize_q8_1.restype = st
+    lib.dg_quantize_q4_0.argtypes = [P, P, I64, I64, P]
+    lib.dg_quantize_q4_0.restype = st
+    lib.dg_argmax_workspace_bytes.argtypes = [I64, I64]
+    lib.dg_argmax_workspace_bytes.restype = ctypes.c_size_t
+    lib.dg_argmax_rows.argtypes = [P, P, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.dg_argmax_rows.restype = st
+    _handle = lib
+    return lib
+
+
+def raw():
+    """The ctypes handle of libdecodegemv.so (for tests that call the C ABI directly)."""
+    return _lib()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, dtypes, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check(status, where):
+    if status != DG_OK:
+        raise DGError(status, where)
+
+
+def _cfg(variant=0, grid=0, block=0, unroll=0):
+    return dg_launch(variant, grid, block, unroll)
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def dg_stream_read(buf, checksum, nbytes=None, grid_blocks=0, block_threads=0,
+                   nontemporal=1, stream=None):
+    """Adds the wrapping uint32 word sum of buf's bytes into checksum (int32[1])."""
+    torch = _torch()
+    _need(checksum, (torch.int32,), "checksum")
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    _check(_lib().dg_stream_read(_ptr(buf), nbytes, _ptr(checksum), int(grid_blocks),
+                                 int(block_threads), int(nontemporal), _stream(stream)),
+           "dg_stream_read")
+
+
+def _dense(name, W, x, y, N, K, ldw, launch, stream, wdtype, ydtype):
+    _need(W, (wdtype,), "W")
+    _need(x, (wdtype,), "x")
+    _need(y, (ydtype,), "y")
+    if N is None:
+        N = W.shape[0]
+    if K is None:
+        K = x.numel()
+    if ldw is None:
+        ldw = W.shape[1] if W.dim() == 2 else K
+    lib = _lib()
+    if launch is None:
+        st = getattr(lib, name)(_ptr(W), _ptr(x), _ptr(y), N, K, ldw, _stream(stream))
+    else:
+        st = getattr(lib, name + "_ex")(_ptr(W), _ptr(x), _ptr(y), N, K, ldw,
+                                        ctypes.byref(_cfg(**launch)), _stream(stream))
+    _check(st, name)
+    return y
+
+
+def dg_gemv_f16(W, x, y, N=None, K=None, ldw=None, launch=None, stream=None):
+    """y[N] (float16) = W[N][ldw] (float16) . x[K] (float16), fp32 accumulation."""
+    torch = _torch()
+    return _dense("dg_gemv_f16", W, x, y, N, K, ldw, launch, stream, torch.float16, torch.float16)
+
+
+def dg_gemv_bf16(W, x, y, N=None, K=None, ldw=None, launch=None, stream=None):
+    """y[N] (float32) = W[N][ldw] (bfloat16) . x[K] (bfloat16), fp32 accumulation."""
+    torch = _torch()
+    return _dense("dg_gemv_bf16", W, x, y, N, K, ldw, launch, stream, torch.bfloat16, torch.float32)
+
+
+def dg_gemv_q4_0(Wq, Xq, Y, N, K, M, launch=None, stream=None):
+    """Y[M][N] (float32) from Q4_0 weight bytes and Q8_1 activation bytes (uint8 tensors)."""
+    torch = _torch()
+    _need(Wq, (torch.uint8,), "Wq")
+    _need(Xq, (torch.uint8,), "Xq")
+    _need(Y, (torch.float32,), "Y")
+    lib = _lib()
+    if launch is None:
+        st = lib.dg_gemv_q4_0(_ptr(Wq), _ptr(Xq), _ptr(Y), int(N), int(K), int(M), _stream(stream))
+    else:
+        st = lib.dg_gemv_q4_0_ex(_ptr(Wq), _ptr(Xq), _ptr(Y), int(N), int(K), int(M),
+                                 ctypes.byref(_cfg(**launch)), _stream(stream))
+    _check(st, "dg_gemv_q4_0")
+    return Y
+
+
+def dg_quantize_q8_1(x, Xq, M, K, stream=None):
+    """float32 [M][K] -> Q8_1 bytes (uint8 [M*K/32*36])."""
+    torch = _torch()
+    _need(x, (torch.float32,), "x")
+    _need(Xq, (torch.uint8,), "Xq")
+    _check(_lib().dg_quantize_q8_1(_ptr(x), _ptr(Xq), int(M), int(K), _stream(stream)), "dg_quantize_q8_1")
+    return Xq
+
+
+def dg_quantize_q4_0(w, Wq, N, K, stream=None):
+    """float32 [N][K] -> Q4_0 bytes (uint8 [N*K/32*18])."""
+    torch = _torch()
+    _need(w, (torch.float32,), "w")
+    _need(Wq, (torch.uint8,), "Wq")
+    _check(_lib().dg_quantize_q4_0(_ptr(w), _ptr(Wq), int(N), int(K), _stream(stream)), "dg_quantize_q4_0")
+    return Wq
+
+
+def dg_argmax_workspace_bytes(R, C):
+    return int(_lib().dg_argmax_workspace_bytes(int(R), int(C)))
+
+
+def dg_argmax_rows(x, idx, R=None, C=None, ld=None, ws=None, stream=None):
+    """idx[R] (int64) = lowest index of each row's maximum of x (float32 [R][ld])."""
+    torch = _torch()
+    _need(x, (torch.float32,), "x")
+    _need(idx, (torch.int64,), "idx")
+    if R is None:
+        R = x.shape[0] if x.dim() == 2 else 1
+    if C is None:
+        C = x.shape[-1]
+    if ld is None:
+        ld = x.shape[-1]
+    need = dg_argmax_workspace_bytes(R, C)
+    if ws is None:
+        raise ValueError(f"dg_argmax_rows needs a device workspace of {need} bytes")
+    _need(ws, (torch.uint8, torch.int64), "ws")
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib().dg_argmax_rows(_ptr(x), _ptr(idx), int(R), int(C), int(ld), _ptr(ws), ws_bytes,
+                                 _stream(stream)), "dg_argmax_rows")
+    return idx

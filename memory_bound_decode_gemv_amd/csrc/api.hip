@@ -1,0 +1,180 @@
+// api.hip -- the extern "C" entry points of libdecodegemv: argument checks
+// (all done before anything touches the HIP runtime), launch-configuration
+// defaults, and error reporting.  The contracts are documented in
+// include/decodegemv.h.
+#include <atomic>
+#include <string>
+
+#include "dg_device.h"
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+constexpr int64_t kI32Max = 2147483647;
+
+dg_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return DG_OK;
+    g_last_hip_error = std::string(hipGetErrorName(e)) + ": " + hipGetErrorString(e);
+    return DG_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool launch_ok(const dg_launch* cfg) {
+    if (!cfg) return true;
+    if (cfg->variant < 0 || cfg->grid < 0 || cfg->block < 0 || cfg->unroll < 0) return false;
+    if (cfg->block && (cfg->block % kWave != 0 || cfg->block > 1024)) return false;
+    return true;
+}
+
+__global__ void k_fill_zero_f32(float* __restrict__ y, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = 0.0f;
+}
+
+dg_status gemv_dense_checked(bool bf16, const void* W, const void* x, void* y, int64_t N, int64_t K,
+                             int64_t ldw, const dg_launch* cfg, dg_stream stream) {
+    if (N < 0 || N > kI32Max || K < 0 || K > kI32Max || K % 8 != 0 || ldw < K || ldw % 8 != 0)
+        return DG_ERR_SHAPE;
+    if (!launch_ok(cfg)) return DG_ERR_ARG;
+    if (N == 0) return DG_OK;
+    if (!y || (K > 0 && (!W || !x))) return DG_ERR_NULL;
+    if (!aligned(y, bf16 ? 4 : 2)) return DG_ERR_MISALIGNED;
+    if (K > 0 && (!aligned(W, 16) || !aligned(x, 16))) return DG_ERR_MISALIGNED;
+    hipError_t e = launch_gemv_dense(bf16, W, x, y, (int)N, (int)K, ldw, cfg, (hipStream_t)stream);
+    if (e == hipErrorInvalidValue && cfg && (cfg->variant || cfg->unroll)) return DG_ERR_ARG;
+    return hip_status(e);
+}
+
+dg_status gemv_q4_0_checked(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                            const dg_launch* cfg, dg_stream stream) {
+    if (N < 0 || N > kI32Max || K < 0 || K > kI32Max || K % 256 != 0 || M < 0 || M > 24)
+        return DG_ERR_SHAPE;
+    if (!launch_ok(cfg)) return DG_ERR_ARG;
+    if (N == 0 || M == 0) return DG_OK;
+    if (!Y || (K > 0 && (!Wq || !Xq))) return DG_ERR_NULL;
+    if (!aligned(Y, 4)) return DG_ERR_MISALIGNED;
+    if (K > 0 && (!aligned(Wq, 16) || !aligned(Xq, 4))) return DG_ERR_MISALIGNED;
+    if (K == 0) {   // empty sums: Y = 0
+        const int64_t n = N * (int64_t)M;
+        hipLaunchKernelGGL(k_fill_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           (hipStream_t)stream, Y, n);
+        return hip_status(hipGetLastError());
+    }
+    hipError_t e = launch_gemv_q4_0(Wq, Xq, Y, (int)N, (int)K, M, cfg, (hipStream_t)stream);
+    if (e == hipErrorInvalidValue && cfg && (cfg->variant || cfg->unroll || cfg->block)) return DG_ERR_ARG;
+    return hip_status(e);
+}
+
+}  // namespace
+
+int device_cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev].store(v, std::memory_order_relaxed);
+    return v;
+}
+
+}  // namespace dg
+
+using namespace dg;
+
+extern "C" {
+
+const char* dg_status_string(dg_status status) {
+    switch (status) {
+        case DG_OK: return "DG_OK";
+        case DG_ERR_NULL: return "DG_ERR_NULL: a required pointer is NULL";
+        case DG_ERR_MISALIGNED: return "DG_ERR_MISALIGNED: a pointer breaks its alignment contract";
+        case DG_ERR_SHAPE: return "DG_ERR_SHAPE: a size is outside the documented contract";
+        case DG_ERR_WORKSPACE: return "DG_ERR_WORKSPACE: workspace missing or too small";
+        case DG_ERR_HIP: return "DG_ERR_HIP: the HIP runtime reported an error";
+        case DG_ERR_ARG: return "DG_ERR_ARG: invalid argument or launch override";
+    }
+    return "unknown dg_status";
+}
+
+const char* dg_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_checksum, int grid_blocks,
+                         int block_threads, int nontemporal, dg_stream stream) {
+    if (bytes % 16 != 0) return DG_ERR_SHAPE;
+    if (grid_blocks < 0 || block_threads < 0 || (nontemporal != 0 && nontemporal != 1)) return DG_ERR_ARG;
+    if (block_threads && (block_threads % kWave != 0 || block_threads > 1024)) return DG_ERR_ARG;
+    if (bytes == 0) return DG_OK;
+    if (!buf || !d_checksum) return DG_ERR_NULL;
+    if (!aligned(buf, 16) || !aligned(d_checksum, 4)) return DG_ERR_MISALIGNED;
+    const int grid = grid_blocks ? grid_blocks : 2048;
+    const int block = block_threads ? block_threads : 256;
+    return hip_status(launch_stream_read(buf, bytes, d_checksum, grid, block, nontemporal != 0,
+                                         (hipStream_t)stream));
+}
+
+dg_status dg_gemv_f16(const void* W, const void* x, void* y, int64_t N, int64_t K, int64_t ldw,
+                      dg_stream stream) {
+    return gemv_dense_checked(false, W, x, y, N, K, ldw, nullptr, stream);
+}
+
+dg_status dg_gemv_bf16(const void* W, const void* x, float* y, int64_t N, int64_t K, int64_t ldw,
+                       dg_stream stream) {
+    return gemv_dense_checked(true, W, x, y, N, K, ldw, nullptr, stream);
+}
+
+dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K, int64_t ldw,
+                         const dg_launch* cfg, dg_stream stream) {
+    return gemv_dense_checked(false, W, x, y, N, K, ldw, cfg, stream);
+}
+
+dg_status dg_gemv_bf16_ex(const void* W, const void* x, float* y, int64_t N, int64_t K, int64_t ldw,
+                          const dg_launch* cfg, dg_stream stream) {
+    return gemv_dense_checked(true, W, x, y, N, K, ldw, cfg, stream);
+}
+
+dg_status dg_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                       dg_stream stream) {
+    return gemv_q4_0_checked(Wq, Xq, Y, N, K, M, nullptr, stream);
+}
+
+dg_status dg_gemv_q4_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                          const dg_launch* cfg, dg_stream stream) {
+    return gemv_q4_0_checked(Wq, Xq, Y, N, K, M, cfg, stream);
+}
+
+dg_status dg_quantize_q8_1(const float* x, void* Xq, int64_t M, int64_t K, dg_stream stream) {
+    if (M < 0 || K < 0 || K % 32 != 0 || M * (K / 32) > kI32Max * 256LL) return DG_ERR_SHAPE;
+    if (M == 0 || K == 0) return DG_OK;
+    if (!x || !Xq) return DG_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(Xq, 4)) return DG_ERR_MISALIGNED;
+    return hip_status(launch_quantize_q8_1(x, Xq, M, K, (hipStream_t)stream));
+}
+
+dg_status dg_quantize_q4_0(const float* w, void* Wq, int64_t N, int64_t K, dg_stream stream) {
+    if (N < 0 || K < 0 || K % 32 != 0 || N * (K / 32) > kI32Max * 256LL) return DG_ERR_SHAPE;
+    if (N == 0 || K == 0) return DG_OK;
+    if (!w || !Wq) return DG_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(Wq, 2)) return DG_ERR_MISALIGNED;
+    return hip_status(launch_quantize_q4_0(w, Wq, N, K, (hipStream_t)stream));
+}
+
+size_t dg_argmax_workspace_bytes(int64_t R, int64_t C) { return argmax_workspace_bytes(R, C); }
+
+dg_status dg_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld, void* ws,
+                         size_t ws_bytes, dg_stream stream) {
+    if (R < 0 || R > kI32Max || C < 1 || C >= kI32Max || ld < C) return DG_ERR_SHAPE;
+    if (R == 0) return DG_OK;
+    if (!x || !idx) return DG_ERR_NULL;
+    if (!aligned(x, 4) || !aligned(idx, 8)) return DG_ERR_MISALIGNED;
+    const size_t need = argmax_workspace_bytes(R, C);
+    if (need > 0 && (!ws || ws_bytes < need)) return DG_ERR_WORKSPACE;
+    if (ws && !aligned(ws, 8)) return DG_ERR_MISALIGNED;
+    return hip_status(launch_argmax_rows(x, idx, R, C, ld, ws, (hipStream_t)stream));
+}
+
+}  // extern "C"

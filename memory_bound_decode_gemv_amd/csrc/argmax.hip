@@ -1,0 +1,162 @@
+// argmax.hip -- per-row argmax of float32 logits, lowest index on ties.
+//
+// IEEE discussion "ArgCompare Benchmark Results and Performance Analysis":
+// "VD_Split" tiles a long reduction over many workgroups and merges their
+// results, which is what keeps a single 128K-vocabulary row from being
+// serialised on one workgroup; the reductions inside a wave are cross-lane.
+// Any row length is handled by masking (the discussion's VD pipeline needed
+// power-of-two padding instead).
+//
+// Determinism: every element is mapped to a 64-bit key
+//   (order-preserving 32-bit image of the value) << 32 | (0xFFFFFFFF - index)
+// so that "larger key" means "larger value, or equal value at a lower index".
+// -0 is folded onto +0 before the mapping (IEEE equality) and every NaN maps
+// to the largest image (a NaN beats every number; among NaNs the lowest index
+// wins).  The maximum of keys is order-independent, so the split into chunks
+// and the order of the merges cannot change the result.
+#include "dg_device.h"
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+constexpr int kArgBlock = 256;
+constexpr int kMaxChunk = 16384;
+constexpr int kMinChunk = 1024;
+constexpr int kTargetGroups = 256;
+
+__device__ __forceinline__ uint32_t order_image(float v) {
+    uint32_t u = __builtin_bit_cast(uint32_t, v);
+    if (v != v) return 0xFFFFFFFFu;       // NaN above everything
+    if (u == 0x80000000u) u = 0u;         // -0 == +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t pack_key(uint32_t img, uint32_t idx) {
+    return ((uint64_t)img << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off, kWave);
+        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off, kWave);
+        v = umax64(v, ((uint64_t)hi << 32) | lo);
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v) {
+    __shared__ uint64_t part[kArgBlock / kWave];
+    v = wave_max_u64(v);
+    const int wave = threadIdx.x / kWave;
+    if (lane_id() == 0) part[wave] = v;
+    __syncthreads();
+    uint64_t r = part[0];
+#pragma unroll
+    for (int w = 1; w < kArgBlock / kWave; ++w) r = umax64(r, part[w]);
+    return r;
+}
+
+// Pass 1: workgroup (s, r) reduces elements [s*chunk, min(C, (s+1)*chunk)) of
+// row r into one key.  VEC: rows are 16-byte aligned and chunk % 4 == 0, so
+// every thread reads float4s; each thread visits its elements in increasing
+// index order and keeps the first of equal maxima.
+template <bool VEC>
+__global__ void __launch_bounds__(kArgBlock)
+k_argmax_partial(const float* __restrict__ x, uint64_t* __restrict__ ws, int C, int64_t ld, int chunk) {
+    const int r = blockIdx.y;
+    const int s = blockIdx.x;
+    const float* __restrict__ row = x + (int64_t)r * ld;
+    const int c0 = s * chunk;
+    const int c1 = min(C, c0 + chunk);
+    uint32_t best = 0u, bidx = 0xFFFFFFFFu;
+    if constexpr (VEC) {
+        constexpr int kU = 4;   // float4 loads in flight per thread
+        const float4* __restrict__ rv = reinterpret_cast<const float4*>(row);
+        const int v0 = c0 >> 2;
+        const int v1 = (c1 + 3) >> 2;   // the last vector may be partial
+        const int vlast = (C - 1) >> 2;
+        for (int vb = v0 + threadIdx.x; vb < v1; vb += kU * kArgBlock) {
+            float4 f[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int v = vb + u * kArgBlock;
+                f[u] = rv[v < v1 ? v : vlast];
+            }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int v = vb + u * kArgBlock;
+                const float e[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = 4 * v + j;
+                    const uint32_t img = order_image(e[j]);
+                    if (v < v1 && c < c1 && img > best) { best = img; bidx = (uint32_t)c; }
+                }
+            }
+        }
+    } else {
+        for (int c = c0 + threadIdx.x; c < c1; c += kArgBlock) {
+            const uint32_t img = order_image(row[c]);
+            if (img > best) { best = img; bidx = (uint32_t)c; }
+        }
+    }
+    const uint64_t k = block_max_u64(bidx == 0xFFFFFFFFu ? 0ull : pack_key(best, bidx));
+    if (threadIdx.x == 0) ws[(int64_t)r * gridDim.x + s] = k;
+}
+
+// Pass 2: one wave per row merges the row's S chunk keys.
+__global__ void __launch_bounds__(256)
+k_argmax_final(const uint64_t* __restrict__ ws, int64_t* __restrict__ idx, int R, int S) {
+    const int r = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (r >= R) return;
+    const uint64_t* __restrict__ kr = ws + (int64_t)r * S;
+    uint64_t best = 0ull;
+    for (int s = lane_id(); s < S; s += kWave) best = umax64(best, kr[s]);
+    best = wave_max_u64(best);
+    if (lane_id() == 0) idx[r] = (int64_t)(0xFFFFFFFFu - (uint32_t)best);
+}
+
+int pick_chunk(int64_t R, int64_t C) {
+    int chunk = kMaxChunk;
+    while (chunk > kMinChunk && R * ((C + chunk - 1) / chunk) < kTargetGroups) chunk >>= 1;
+    return chunk;
+}
+
+}  // namespace
+
+size_t argmax_workspace_bytes(int64_t R, int64_t C) {
+    if (R <= 0 || C <= 0) return 0;
+    const int chunk = pick_chunk(R, C);
+    const int64_t S = (C + chunk - 1) / chunk;
+    return (size_t)(R * S) * sizeof(uint64_t);
+}
+
+hipError_t launch_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld,
+                              void* ws, hipStream_t s) {
+    const int chunk = pick_chunk(R, C);
+    const int S = (int)((C + chunk - 1) / chunk);
+    // float4 path only when no vector can reach past column C-1 of any row
+    const bool vec = ((uintptr_t)x % 16 == 0) && (ld % 4 == 0) && (C % 4 == 0);
+    uint64_t* w = (uint64_t*)ws;
+    constexpr int64_t kMaxGridY = 65535;
+    for (int64_t r0 = 0; r0 < R; r0 += kMaxGridY) {   // grid.y is limited to 65535 rows per launch
+        const int64_t rn = R - r0 < kMaxGridY ? R - r0 : kMaxGridY;
+        dim3 g1((unsigned)S, (unsigned)rn);
+        const float* xr = x + r0 * ld;
+        uint64_t* wr = w + r0 * S;
+        if (vec) hipLaunchKernelGGL(k_argmax_partial<true>, g1, dim3(kArgBlock), 0, s, xr, wr, (int)C, ld, chunk);
+        else hipLaunchKernelGGL(k_argmax_partial<false>, g1, dim3(kArgBlock), 0, s, xr, wr, (int)C, ld, chunk);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int rows_per_block = 256 / kWave;
+    hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)((R + rows_per_block - 1) / rows_per_block)), dim3(256), 0, s,
+                       (const uint64_t*)w, idx, (int)R, S);
+    return hipGetLastError();
+}
+
+}  // namespace dg

@@ -1,0 +1,42 @@
+// dg_internal.h -- host-side declarations shared by the C-ABI layer (api.hip)
+// and the kernel launchers in the other translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "decodegemv.h"
+
+namespace dg {
+
+// A resolved launch configuration (no zero fields left).
+struct Launch {
+    int variant;
+    int grid;
+    int block;
+    int unroll;
+};
+
+// Device properties used to size grids; cached per device.
+int device_cu_count();
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* d_checksum,
+                              int grid, int block, bool nontemporal, hipStream_t s);
+
+// Dense GEMV launcher; `bf16` selects bfloat16 operands with fp32 output,
+// otherwise binary16 operands with binary16 output.  Returns hipErrorInvalidValue
+// for a variant that cannot run this shape.
+hipError_t launch_gemv_dense(bool bf16, const void* W, const void* x, void* y,
+                             int N, int K, int64_t ldw, const dg_launch* cfg, hipStream_t s);
+
+hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int K, int M,
+                            const dg_launch* cfg, hipStream_t s);
+
+hipError_t launch_quantize_q8_1(const float* x, void* Xq, int64_t M, int64_t K, hipStream_t s);
+hipError_t launch_quantize_q4_0(const float* w, void* Wq, int64_t N, int64_t K, hipStream_t s);
+
+size_t argmax_workspace_bytes(int64_t R, int64_t C);
+hipError_t launch_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld,
+                              void* ws, hipStream_t s);
+
+}  // namespace dg

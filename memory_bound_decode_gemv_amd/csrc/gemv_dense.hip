@@ -1,0 +1,232 @@
+// gemv_dense.hip -- batch-1 GEMV y = W x over binary16 or bfloat16 weights.
+//
+// batch1-cdna README, "FP16 GEMV" section: each wavefront computes one output
+// element as the dot product of x with one row of W; lanes stride across the
+// row so that one load instruction of the wave touches one contiguous span;
+// products accumulate in fp32 (v_dot2_f32_f16) and the lanes' partial sums are
+// reduced with a DPP row_shr / row_bcast chain.  The page's three versions
+// (one accumulator; four accumulators with the loads issued as a batch; 16
+// bytes per lane) are all here: the last is the default, the first two are
+// kept as the ablation variants.
+//
+// gfx950 specifics: wave64; 16-byte non-temporal loads (the weights are read
+// once, so installing them in the last-level cache only evicts other lines);
+// U independent loads and accumulators per lane so that all of a row's loads
+// are in flight before the first wait.
+#include "dg_device.h"
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+template <bool BF16>
+__device__ __forceinline__ float dot8(u32x4 w, u32x4 x, float acc) {
+    if constexpr (BF16) return dot8_bf16(w, x, acc);
+    else return dot8_f16(w, x, acc);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float dot2(uint32_t w, uint32_t x, float acc) {
+    if constexpr (BF16) return dot2_bf16(w, x, acc);
+    else return dot2_f16(w, x, acc);
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store_out(void* y, int row, float s) {
+    if constexpr (BF16) reinterpret_cast<float*>(y)[row] = s;
+    else reinterpret_cast<_Float16*>(y)[row] = (_Float16)s;  // round to nearest even
+}
+
+// Wave-uniform wave index inside the workgroup.
+__device__ __forceinline__ int wave_in_block() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
+// 16 bytes (8 elements) per lane; U loads in flight per lane per step.
+// XREG: the lane's share of x (at most U vectors) is loaded once and kept in
+// registers for every row the wave handles; requires K/8 <= 64*U.
+template <bool BF16, int U, bool XREG>
+__global__ void __launch_bounds__(1024)
+k_gemv_wide(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
+            void* __restrict__ y, int N, int K, int64_t ldw) {
+    const int lane = lane_id();
+    const int wpb = blockDim.x / kWave;
+    const int nvec = K >> 3;
+    const u32x4* __restrict__ xv = reinterpret_cast<const u32x4*>(x);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+
+    u32x4 xr[XREG ? U : 1];
+    if constexpr (XREG) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int idx = u * kWave + lane;
+            xr[u] = (idx < nvec) ? xv[idx] : zero;
+        }
+    }
+
+    for (int row = blockIdx.x * wpb + wave_in_block(); row < N; row += gridDim.x * wpb) {
+        const u32x4* __restrict__ wr = reinterpret_cast<const u32x4*>(W + (int64_t)row * ldw);
+        float acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = 0.0f;
+
+        if constexpr (XREG) {
+            if (nvec > 0) {
+                u32x4 wv[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int idx = u * kWave + lane;
+                    wv[u] = load_vec<true>(wr + (idx < nvec ? idx : nvec - 1));
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int idx = u * kWave + lane;
+                    acc[u] = dot8<BF16>(idx < nvec ? wv[u] : zero, xr[u], acc[u]);
+                }
+            }
+        } else {
+            int v0 = 0;
+            for (; v0 + kWave * U <= nvec; v0 += kWave * U) {
+                u32x4 wv[U], xw[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) wv[u] = load_vec<true>(wr + v0 + u * kWave + lane);
+#pragma unroll
+                for (int u = 0; u < U; ++u) xw[u] = xv[v0 + u * kWave + lane];
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc[u] = dot8<BF16>(wv[u], xw[u], acc[u]);
+            }
+            if (v0 < nvec) {  // ragged last step: out-of-range lanes read a valid vector, then zero it
+                u32x4 wv[U], xw[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int idx = v0 + u * kWave + lane;
+                    const int idc = idx < nvec ? idx : nvec - 1;
+                    wv[u] = load_vec<true>(wr + idc);
+                    xw[u] = xv[idc];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const bool ok = v0 + u * kWave + lane < nvec;
+                    acc[u] = dot8<BF16>(ok ? wv[u] : zero, ok ? xw[u] : zero, acc[u]);
+                }
+            }
+        }
+        float s = 0.0f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) s += acc[u];
+        s = wave_sum_f32(s);
+        if (lane == 0) store_out<BF16>(y, row, s);
+    }
+}
+
+// Ablation variants with 4 bytes (one half2 / bf16x2 pair) per lane.
+// NACC = 1: one accumulator, each iteration's load consumed immediately.
+// NACC = 4: four independent accumulators, four loads issued as a batch.
+template <bool BF16, int NACC>
+__global__ void __launch_bounds__(1024)
+k_gemv_narrow(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
+              void* __restrict__ y, int N, int K, int64_t ldw) {
+    const int lane = lane_id();
+    const int wpb = blockDim.x / kWave;
+    const int n2 = K >> 1;
+    const uint32_t* __restrict__ x2 = reinterpret_cast<const uint32_t*>(x);
+    for (int row = blockIdx.x * wpb + wave_in_block(); row < N; row += gridDim.x * wpb) {
+        const uint32_t* __restrict__ w2 = reinterpret_cast<const uint32_t*>(W + (int64_t)row * ldw);
+        float acc[NACC];
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[a] = 0.0f;
+        int k = lane;
+        for (; k + (NACC - 1) * kWave < n2; k += NACC * kWave) {
+            uint32_t wv[NACC], xw[NACC];
+#pragma unroll
+            for (int a = 0; a < NACC; ++a) wv[a] = load_u32<true>(w2 + k + a * kWave);
+#pragma unroll
+            for (int a = 0; a < NACC; ++a) xw[a] = x2[k + a * kWave];
+#pragma unroll
+            for (int a = 0; a < NACC; ++a) acc[a] = dot2<BF16>(wv[a], xw[a], acc[a]);
+        }
+        for (; k < n2; k += kWave) acc[0] = dot2<BF16>(load_u32<true>(w2 + k), x2[k], acc[0]);
+        float s = 0.0f;
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) s += acc[a];
+        s = wave_sum_f32(s);
+        if (lane == 0) store_out<BF16>(y, row, s);
+    }
+}
+
+template <bool BF16>
+hipError_t launch_wide(int U, bool xreg, const void* W, const void* x, void* y, int N, int K,
+                       int64_t ldw, int grid, int block, hipStream_t s) {
+    const uint16_t* w16 = (const uint16_t*)W;
+    const uint16_t* x16 = (const uint16_t*)x;
+#define DG_WIDE_CASE(UU)                                                                       \
+    case UU:                                                                                   \
+        if (xreg)                                                                              \
+            hipLaunchKernelGGL((k_gemv_wide<BF16, UU, true>), dim3(grid), dim3(block), 0, s,   \
+                               w16, x16, y, N, K, ldw);                                        \
+        else                                                                                   \
+            hipLaunchKernelGGL((k_gemv_wide<BF16, UU, false>), dim3(grid), dim3(block), 0, s,  \
+                               w16, x16, y, N, K, ldw);                                        \
+        break;
+    switch (U) {
+        DG_WIDE_CASE(1)
+        DG_WIDE_CASE(2)
+        DG_WIDE_CASE(4)
+        DG_WIDE_CASE(8)
+        DG_WIDE_CASE(16)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef DG_WIDE_CASE
+    return hipGetLastError();
+}
+
+int round_up_pow2_unroll(int v) {
+    int u = 1;
+    while (u < v && u < 16) u *= 2;
+    return u;
+}
+
+}  // namespace
+
+hipError_t launch_gemv_dense(bool bf16, const void* W, const void* x, void* y,
+                             int N, int K, int64_t ldw, const dg_launch* cfg, hipStream_t s) {
+    const int nvec = K / 8;
+    int variant = cfg && cfg->variant ? cfg->variant : DG_VARIANT_DENSE_WIDE;
+    int block = cfg && cfg->block ? cfg->block : 256;
+    const int wpb = block / kWave;
+    const int rows_per_grid_default = (N + wpb - 1) / wpb;   // one row per wave
+    int grid = cfg && cfg->grid ? cfg->grid : rows_per_grid_default;
+    if (grid < 1) grid = 1;
+
+    if (variant == DG_VARIANT_DENSE_WIDE || variant == DG_VARIANT_DENSE_XREG) {
+        const bool xreg = variant == DG_VARIANT_DENSE_XREG;
+        int U = cfg && cfg->unroll ? cfg->unroll : 8;
+        if (xreg) {
+            const int need = round_up_pow2_unroll((nvec + kWave - 1) / kWave);
+            if (cfg && cfg->unroll) {
+                if (cfg->unroll * kWave < nvec) return hipErrorInvalidValue;
+            } else {
+                U = need < 1 ? 1 : need;
+            }
+            if (U * kWave < nvec) return hipErrorInvalidValue;
+        }
+        return bf16 ? launch_wide<true>(U, xreg, W, x, y, N, K, ldw, grid, block, s)
+                    : launch_wide<false>(U, xreg, W, x, y, N, K, ldw, grid, block, s);
+    }
+    if (variant == DG_VARIANT_DENSE_NARROW1 || variant == DG_VARIANT_DENSE_NARROW4) {
+        const uint16_t* w16 = (const uint16_t*)W;
+        const uint16_t* x16 = (const uint16_t*)x;
+        if (variant == DG_VARIANT_DENSE_NARROW1) {
+            if (bf16) hipLaunchKernelGGL((k_gemv_narrow<true, 1>), dim3(grid), dim3(block), 0, s, w16, x16, y, N, K, ldw);
+            else hipLaunchKernelGGL((k_gemv_narrow<false, 1>), dim3(grid), dim3(block), 0, s, w16, x16, y, N, K, ldw);
+        } else {
+            if (bf16) hipLaunchKernelGGL((k_gemv_narrow<true, 4>), dim3(grid), dim3(block), 0, s, w16, x16, y, N, K, ldw);
+            else hipLaunchKernelGGL((k_gemv_narrow<false, 4>), dim3(grid), dim3(block), 0, s, w16, x16, y, N, K, ldw);
+        }
+        return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dg

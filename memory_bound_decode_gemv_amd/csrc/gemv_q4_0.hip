@@ -1,0 +1,345 @@
+// gemv_q4_0.hip -- Q4_0 weights x Q8_1 activations, M = 1..24 columns.
+//
+// Y[m][n] = sum_b d4(n,b) d8(m,b) sum_{j<32} (q4 - 8) q8, the quantised decode
+// GEMV of "The kernel that waited for itself" (Q4_0/Q8_1 harness, small-batch
+// kernel for many columns) and of the bitsandbytes issue on 4-bit M = 1 decode
+// (70B MLP shape).  Design rules taken from those pages and kept here:
+//  * dequantise inside the load loop, never as a separate pass (bitsandbytes
+//    issue, "Path Comparison": fused 1147 us vs dequantise + matmul 7574 us);
+//  * one 64-lane wavefront per row, consecutive lanes reading consecutive
+//    bytes of the row (same issue, 64 threads per block and coalescing notes);
+//  * loads issued as a batch before any is consumed, and register use kept low
+//    enough for several waves per SIMD ("The kernel that waited for itself",
+//    the 105-117 VGPR / 2 waves per SIMD wall);
+//  * one kernel family for every column count, so there is no dispatch cliff
+//    between 12 and 16 columns (same page, "A dip at sixteen").
+//
+// Arithmetic.  Each lane owns pairs of consecutive blocks (36 bytes, dword
+// aligned because rows are 16-byte aligned when K % 256 == 0).  The 16 code
+// bytes of a block split into low nibbles (weights 0..15) and high nibbles
+// (weights 16..31) with one mask each; the unsigned codes 0..15 go straight
+// into v_dot4_i32_i8 against the signed activation codes, and the -8 offset
+// enters as the initial accumulator -8 * sum(q8), computed exactly once per
+// activation block.  The int32 block sum is then scaled by d4 * d8 in fp32.
+#include "dg_device.h"
+#include "dg_internal.h"
+
+namespace dg {
+namespace {
+
+constexpr uint32_t kNib = 0x0F0F0F0Fu;
+constexpr int kPairBytes = 36;   // two Q4_0 blocks
+constexpr int kQ81Bytes = 36;    // one Q8_1 block
+
+// One column's activations for one block pair: codes of block a and block b
+// (element 4i..4i+3 in dword i), scales as fp32, and c = -8 * sum(q8).
+struct ActPair {
+    uint32_t qa[8];
+    uint32_t qb[8];
+    float da, db;
+    int ca, cb;
+};
+
+__device__ __forceinline__ int block_code_sum(const uint32_t* q) {
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s = dot4_i8(q[i], 0x01010101u, s);
+    return s;
+}
+
+// Reads the Q8_1 blocks 2p and 2p+1 of a column (72 bytes, 8-byte aligned
+// when the column start is) from global memory.
+__device__ __forceinline__ void load_act_pair(const uint8_t* col, int p, ActPair& a) {
+    const uint32_t* b = reinterpret_cast<const uint32_t*>(col + (size_t)p * (2 * kQ81Bytes));
+    uint32_t v[18];
+#pragma unroll
+    for (int i = 0; i < 18; ++i) v[i] = b[i];
+    a.da = half_lo_to_f32(v[0]);
+    a.db = half_lo_to_f32(v[9]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a.qa[i] = v[1 + i];
+        a.qb[i] = v[10 + i];
+    }
+    a.ca = -8 * block_code_sum(a.qa);
+    a.cb = -8 * block_code_sum(a.qb);
+}
+
+// Loads the 9 dwords of block pair p of a weight row (non-temporal).
+__device__ __forceinline__ void load_weight_pair(const uint8_t* row, int p, uint32_t w[9]) {
+    const uint32_t* b = reinterpret_cast<const uint32_t*>(row + (size_t)p * kPairBytes);
+    const u32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(b));
+    const u32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(b + 4));
+    w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w;
+    w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
+    w[8] = __builtin_nontemporal_load(b + 8);
+}
+
+// The unpacked codes of one weight pair: lo[i]/hi[i] of block a in 0..3,
+// block b in 4..7, and the two scales.
+struct WeightPair {
+    uint32_t lo[8];
+    uint32_t hi[8];
+    float d4a, d4b;
+};
+
+__device__ __forceinline__ void unpack_weight_pair(const uint32_t w[9], WeightPair& u) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // block a: scale in bytes 0-1, codes in bytes 2..17 (straddling dwords)
+        const uint32_t ca = __builtin_amdgcn_alignbit(w[i + 1], w[i], 16);
+        u.lo[i] = ca & kNib;
+        u.hi[i] = (ca >> 4) & kNib;
+        // block b: scale in bytes 18-19, codes in bytes 20..35 (dwords 5..8)
+        const uint32_t cb = w[5 + i];
+        u.lo[4 + i] = cb & kNib;
+        u.hi[4 + i] = (cb >> 4) & kNib;
+    }
+    u.d4a = half_lo_to_f32(w[0]);
+    u.d4b = half_hi_to_f32(w[4]);
+}
+
+__device__ __forceinline__ float pair_dot(const WeightPair& u, const uint32_t* qa, const uint32_t* qb,
+                                          float da, float db, int ca, int cb, float acc) {
+    int sa = ca, sb = cb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sa = dot4_i8(u.lo[i], qa[i], sa);       // weights 4i..4i+3
+        sa = dot4_i8(u.hi[i], qa[4 + i], sa);   // weights 16+4i..16+4i+3
+        sb = dot4_i8(u.lo[4 + i], qb[i], sb);
+        sb = dot4_i8(u.hi[4 + i], qb[4 + i], sb);
+    }
+    acc = fmaf((float)sa, u.d4a * da, acc);
+    acc = fmaf((float)sb, u.d4b * db, acc);
+    return acc;
+}
+
+__device__ __forceinline__ int wave_in_block() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+}
+
+// ---------------------------------------------------------------------------
+// M = 1: the lane's activation pairs stay in registers for every row the wave
+// handles; the wave issues all of a row's weight loads (S pairs per lane)
+// before it consumes any.  S * 64 pairs cover one row.
+// ---------------------------------------------------------------------------
+template <int S>
+__global__ void __launch_bounds__(256)
+k_q4_m1_regs(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
+             float* __restrict__ Y, int N, int K) {
+    const int lane = lane_id();
+    const int wpb = blockDim.x / kWave;
+    const int npairs = K >> 6;
+    const size_t row_bytes = (size_t)(K >> 5) * 18;
+
+    ActPair act[S];
+    int pc[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int p = s * kWave + lane;
+        pc[s] = p < npairs ? p : npairs - 1;
+        load_act_pair(Xq, pc[s], act[s]);
+        if (p >= npairs) {  // lanes past the end of the row contribute exactly 0
+            act[s].da = 0.0f;
+            act[s].db = 0.0f;
+            act[s].ca = 0;
+            act[s].cb = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { act[s].qa[i] = 0; act[s].qb[i] = 0; }
+        }
+    }
+
+    for (int row = blockIdx.x * wpb + wave_in_block(); row < N; row += gridDim.x * wpb) {
+        const uint8_t* wrow = Wq + (size_t)row * row_bytes;
+        uint32_t w[S][9];
+#pragma unroll
+        for (int s = 0; s < S; ++s) load_weight_pair(wrow, pc[s], w[s]);
+        float acc = 0.0f;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            WeightPair u;
+            unpack_weight_pair(w[s], u);
+            acc = pair_dot(u, act[s].qa, act[s].qb, act[s].da, act[s].db, act[s].ca, act[s].cb, acc);
+        }
+        acc = wave_sum_f32(acc);
+        if (lane == 0) Y[row] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// General M: activations of a 64-pair (4096-element) chunk of K, for all M
+// columns, are staged once per workgroup in LDS in structure-of-arrays form
+// (quad j of pair p of column m at ((m*5 + j)*64 + p)): quads 0-1 hold block
+// a's codes, 2-3 block b's, quad 4 holds (d8a, d8b, ca, cb).  Lane p of every
+// wave reads pair p, so one ds_read_b128 of the wave covers 1 KiB of
+// consecutive LDS.  Each wave owns R rows; each activation quad read from LDS
+// serves all R rows.
+// ---------------------------------------------------------------------------
+constexpr int kChunkPairs = 64;
+constexpr int kQuadsPerPair = 5;
+constexpr int kLdsBlock = 256;   // threads per workgroup of the LDS kernel
+
+template <int M, int R>
+__global__ void __launch_bounds__(kLdsBlock)
+k_q4_lds(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
+         float* __restrict__ Y, int N, int K) {
+    extern __shared__ u32x4 lds[];
+    const int lane = lane_id();
+    const int wave = wave_in_block();
+    constexpr int kWaves = kLdsBlock / kWave;
+    const int npairs = K >> 6;
+    const int nblk = K >> 5;
+    const size_t row_bytes = (size_t)nblk * 18;
+    const int ntiles = (N + kWaves * R - 1) / (kWaves * R);
+
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const int row0 = tile * kWaves * R + wave * R;
+        float acc[R][M];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+
+        for (int c0 = 0; c0 < npairs; c0 += kChunkPairs) {
+            // weights of this chunk: issued before the staging so that they are in flight meanwhile
+            const int gp = c0 + lane;
+            const bool pvalid = gp < npairs;
+            const int gpc = pvalid ? gp : npairs - 1;
+            uint32_t w[R][9];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int row = row0 + r < N ? row0 + r : N - 1;
+                load_weight_pair(Wq + (size_t)row * row_bytes, gpc, w[r]);
+            }
+
+            __syncthreads();   // the previous chunk's readers are done
+            for (int e = threadIdx.x; e < M * 2 * kChunkPairs; e += kLdsBlock) {
+                const int m = e / (2 * kChunkPairs);
+                const int bl = e % (2 * kChunkPairs);
+                const int p = bl >> 1, half = bl & 1;
+                const int gb = 2 * (c0 + p) + half;
+                uint32_t q[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                float d = 0.0f;
+                int c = 0;
+                if (c0 + p < npairs) {
+                    const uint32_t* b = reinterpret_cast<const uint32_t*>(
+                        Xq + ((size_t)m * nblk + gb) * kQ81Bytes);
+                    const uint32_t d0 = b[0];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) q[i] = b[1 + i];
+                    d = half_lo_to_f32(d0);
+                    c = -8 * block_code_sum(q);
+                }
+                u32x4* base = lds + (m * kQuadsPerPair) * kChunkPairs + p;
+                base[(half * 2 + 0) * kChunkPairs] = u32x4{q[0], q[1], q[2], q[3]};
+                base[(half * 2 + 1) * kChunkPairs] = u32x4{q[4], q[5], q[6], q[7]};
+                uint32_t* sc = reinterpret_cast<uint32_t*>(base + 4 * kChunkPairs);
+                sc[half] = __builtin_bit_cast(uint32_t, d);
+                sc[2 + half] = (uint32_t)c;
+            }
+            __syncthreads();
+
+            WeightPair u[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) unpack_weight_pair(w[r], u[r]);
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const u32x4* base = lds + (m * kQuadsPerPair) * kChunkPairs + lane;
+                const u32x4 a0 = base[0 * kChunkPairs];
+                const u32x4 a1 = base[1 * kChunkPairs];
+                const u32x4 b0 = base[2 * kChunkPairs];
+                const u32x4 b1 = base[3 * kChunkPairs];
+                const u32x4 sc = base[4 * kChunkPairs];
+                const uint32_t qa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                const uint32_t qb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                const float da = __builtin_bit_cast(float, (uint32_t)sc.x);
+                const float db = __builtin_bit_cast(float, (uint32_t)sc.y);
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    acc[r][m] = pair_dot(u[r], qa, qb, da, db, (int)sc.z, (int)sc.w, acc[r][m]);
+            }
+        }
+
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) {
+                const float s = wave_sum_f32(acc[r][m]);
+                if (lane == 0 && row0 + r < N) Y[(size_t)m * N + row0 + r] = s;
+            }
+        }
+    }
+}
+
+size_t lds_bytes(int M) { return (size_t)M * kQuadsPerPair * kChunkPairs * sizeof(u32x4); }
+
+template <int M, int R>
+hipError_t launch_lds_mr(const void* Wq, const void* Xq, float* Y, int N, int K, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((k_q4_lds<M, R>), dim3(grid), dim3(kLdsBlock), lds_bytes(M), s,
+                       (const uint8_t*)Wq, (const uint8_t*)Xq, Y, N, K);
+    return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_lds_m(int R, const void* Wq, const void* Xq, float* Y, int N, int K, int grid, hipStream_t s) {
+    if (R == 1) return launch_lds_mr<M, 1>(Wq, Xq, Y, N, K, grid, s);
+    if (R == 2) return launch_lds_mr<M, 2>(Wq, Xq, Y, N, K, grid, s);
+    if constexpr (M <= 4) {
+        if (R == 4) return launch_lds_mr<M, 4>(Wq, Xq, Y, N, K, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_lds(int M, int R, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
+                      hipStream_t s) {
+    switch (M) {
+#define DG_M(MM) case MM: return launch_lds_m<MM>(R, Wq, Xq, Y, N, K, grid, s);
+        DG_M(1) DG_M(2) DG_M(3) DG_M(4) DG_M(5) DG_M(6) DG_M(7) DG_M(8)
+        DG_M(9) DG_M(10) DG_M(11) DG_M(12) DG_M(13) DG_M(14) DG_M(15) DG_M(16)
+        DG_M(17) DG_M(18) DG_M(19) DG_M(20) DG_M(21) DG_M(22) DG_M(23) DG_M(24)
+#undef DG_M
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_regs(int S, const void* Wq, const void* Xq, float* Y, int N, int K, int grid, int block,
+                       hipStream_t s) {
+    const uint8_t* w = (const uint8_t*)Wq;
+    const uint8_t* x = (const uint8_t*)Xq;
+    switch (S) {
+        case 1: hipLaunchKernelGGL((k_q4_m1_regs<1>), dim3(grid), dim3(block), 0, s, w, x, Y, N, K); break;
+        case 2: hipLaunchKernelGGL((k_q4_m1_regs<2>), dim3(grid), dim3(block), 0, s, w, x, Y, N, K); break;
+        case 3: hipLaunchKernelGGL((k_q4_m1_regs<3>), dim3(grid), dim3(block), 0, s, w, x, Y, N, K); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int K, int M,
+                            const dg_launch* cfg, hipStream_t s) {
+    const int npairs = K / 64;
+    const int S = (npairs + kWave - 1) / kWave;
+    int variant = cfg && cfg->variant ? cfg->variant : 0;
+    if (variant == 0) variant = (M == 1 && S <= 3) ? DG_VARIANT_Q4_REGS : DG_VARIANT_Q4_LDS;
+
+    if (variant == DG_VARIANT_Q4_REGS) {
+        if (M != 1 || S > 3) return hipErrorInvalidValue;
+        const int block = cfg && cfg->block ? cfg->block : 256;
+        const int wpb = block / kWave;
+        const int grid = cfg && cfg->grid ? cfg->grid : (N + wpb - 1) / wpb;
+        return launch_regs(S, Wq, Xq, Y, N, K, grid, block, s);
+    }
+    if (variant == DG_VARIANT_Q4_LDS) {
+        if (cfg && cfg->block && cfg->block != kLdsBlock) return hipErrorInvalidValue;
+        int R = cfg && cfg->unroll ? cfg->unroll : (M <= 8 ? 2 : 1);
+        const int rows_per_tile = (kLdsBlock / kWave) * R;
+        const int ntiles = (N + rows_per_tile - 1) / rows_per_tile;
+        const int grid = cfg && cfg->grid ? cfg->grid : ntiles;
+        return launch_lds(M, R, Wq, Xq, Y, N, K, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dg

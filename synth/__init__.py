@@ -47,8 +47,8 @@ def to_f16_bits(a: np.ndarray) -> np.ndarray:
 
 def to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)   # no wrap for finite u
     return r.astype(np.uint16)
 
 

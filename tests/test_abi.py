@@ -1,0 +1,117 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects invalid arguments before touching the HIP runtime
+(no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decodegemv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import memory_bound_decode_gemv_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from memory_bound_decode_gemv_amd import _build
+        _build.build()
+    return m.raw()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dg_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 13
+    import memory_bound_decode_gemv_amd as m
+    assert sorted(m.EXPORTED) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.dg_status_string(s).startswith(b"DG_")
+
+
+P = ctypes.c_void_p
+A16 = P(0x1000)       # a 16-byte-aligned fake device address (never dereferenced)
+A2 = P(0x1002)
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A16, A16, A16, 4, 12, 16), 3),      # K % 8
+    ((A16, A16, A16, 4, 16, 8), 3),       # ldw < K
+    ((A16, A16, A16, 4, 16, 20), 3),      # ldw % 8
+    ((A16, A16, A16, -1, 16, 16), 3),     # N < 0
+    ((A16, A16, A16, 1 << 31, 16, 16), 3),
+    ((None, A16, A16, 4, 16, 16), 1),     # NULL W
+    ((A16, A16, None, 4, 16, 16), 1),     # NULL y
+    ((A2, A16, A16, 4, 16, 16), 2),       # W misaligned
+    ((A16, A2, A16, 4, 16, 16), 2),       # x misaligned
+    ((A16, A16, P(0x1001), 4, 16, 16), 2),  # y misaligned
+    ((None, None, None, 0, 16, 16), 0),   # empty: nothing launched
+])
+def test_gemv_f16_rejects_before_launch(lib, args, expect):
+    assert lib.dg_gemv_f16(*args, None) == expect
+    if expect != 2 or args[2] != P(0x1001):
+        assert lib.dg_gemv_bf16(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A16, A16, A16, 4, 100, 1), 3),      # K % 256
+    ((A16, A16, A16, 4, 256, 25), 3),     # M > 24
+    ((A16, A16, A16, 4, 256, -1), 3),
+    ((None, A16, A16, 4, 256, 1), 1),
+    ((A16, None, A16, 4, 256, 1), 1),
+    ((A2, A16, A16, 4, 256, 1), 2),       # Wq must be 16-byte aligned
+    ((A16, A16, A2, 4, 256, 1), 2),       # Y must be 4-byte aligned
+    ((None, None, None, 4, 256, 0), 0),   # M = 0
+    ((None, None, None, 0, 256, 3), 0),   # N = 0
+])
+def test_gemv_q4_0_rejects_before_launch(lib, args, expect):
+    assert lib.dg_gemv_q4_0(*args, None) == expect
+
+
+def test_launch_overrides_rejected(lib):
+    import memory_bound_decode_gemv_amd as m
+    bad = [m.dg_launch(-1, 0, 0, 0), m.dg_launch(0, 0, 100, 0), m.dg_launch(0, 0, 2048, 0)]
+    for cfg in bad:
+        assert lib.dg_gemv_f16_ex(A16, A16, A16, 4, 16, 16, ctypes.byref(cfg), None) == 6
+        assert lib.dg_gemv_q4_0_ex(A16, A16, A16, 4, 256, 1, ctypes.byref(cfg), None) == 6
+
+
+def test_stream_read_rejects_before_launch(lib):
+    assert lib.dg_stream_read(A16, 24, A16, 0, 0, 1, None) == 3          # bytes % 16
+    assert lib.dg_stream_read(A16, 32, A16, 0, 96, 1, None) == 6         # block not a multiple of 64
+    assert lib.dg_stream_read(A16, 32, A16, 0, 0, 2, None) == 6          # nontemporal flag
+    assert lib.dg_stream_read(None, 32, A16, 0, 0, 1, None) == 1
+    assert lib.dg_stream_read(A2, 32, A16, 0, 0, 1, None) == 2
+    assert lib.dg_stream_read(None, 0, None, 0, 0, 1, None) == 0         # empty
+
+
+def test_argmax_rejects_before_launch(lib):
+    need = lib.dg_argmax_workspace_bytes(64, 1000000)
+    assert need == 64 * 62 * 8
+    assert lib.dg_argmax_workspace_bytes(0, 10) == 0
+    assert lib.dg_argmax_rows(A16, A16, 4, 0, 4, A16, 1 << 20, None) == 3    # C = 0
+    assert lib.dg_argmax_rows(A16, A16, 4, 10, 9, A16, 1 << 20, None) == 3   # ld < C
+    assert lib.dg_argmax_rows(A16, A16, 64, 1000000, 1000000, A16, need - 1, None) == 4
+    assert lib.dg_argmax_rows(A16, A16, 64, 1000000, 1000000, None, need, None) == 4
+    assert lib.dg_argmax_rows(None, A16, 4, 10, 10, A16, 1 << 20, None) == 1
+    assert lib.dg_argmax_rows(A16, P(0x1004), 4, 10, 10, A16, 1 << 20, None) == 2
+    assert lib.dg_argmax_rows(None, None, 0, 10, 10, None, 0, None) == 0
+
+
+def test_quantisers_reject_before_launch(lib):
+    assert lib.dg_quantize_q8_1(A16, A16, 2, 48, None) == 3
+    assert lib.dg_quantize_q4_0(A16, A16, 2, 48, None) == 3
+    assert lib.dg_quantize_q8_1(A2, A16, 2, 64, None) == 2
+    assert lib.dg_quantize_q4_0(None, A16, 2, 64, None) == 1
+    assert lib.dg_quantize_q8_1(None, None, 0, 64, None) == 0

@@ -1,0 +1,148 @@
+"""Parity of dg_gemv_q4_0 (Q4_0 x Q8_1, M = 1..24) with the oracle (GPU).
+
+Operands are quantised on the CPU by the oracle's quantisers from seeded
+N(0, 1) draws, so no input comes from the GPU path; the GPU's own quantisers
+are checked separately, byte for byte, in test_gpu_quantize.py.
+"""
+import functools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import synth
+from tests._parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-3   # per-row floored relative error vs the oracle
+
+
+@functools.lru_cache(maxsize=8)
+def _weights(orc, cfg, N, K, copy):
+    return orc.quantize_q4_0(synth.normal_f32((cfg, synth.KIND_W, copy, 0), (N, K)))
+
+
+def _operands(orc, cfg, N, K, M, copy=0, same_columns=False):
+    Wq = _weights(orc, cfg, N, K, copy)
+    cols = []
+    for m in range(M):
+        cols.append(synth.normal_f32((cfg, synth.KIND_X, copy, 0 if same_columns else m), (K,)))
+    Xq = orc.quantize_q8_1(np.stack(cols))
+    return Wq, Xq
+
+
+def _gpu(dg, dev, Wq, Xq, N, K, M, launch=None):
+    import torch
+    W = torch.from_numpy(np.ascontiguousarray(Wq).reshape(-1)).to(dev)
+    X = torch.from_numpy(np.ascontiguousarray(Xq).reshape(-1)).to(dev)
+    Y = torch.full((max(M, 1), max(N, 1)), float("nan"), dtype=torch.float32, device=dev)
+    dg.dg_gemv_q4_0(W, X, Y, N, K, M, launch=launch)
+    torch.cuda.synchronize()
+    return Y[:M, :N].cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("M", list(range(1, 25)))
+def test_q4_0_every_column_count_small(dg, dev, orc, M):
+    # K = 768: 12 block pairs per row, far from a full 64-pair step (ragged tail)
+    N, K = 41, 768
+    Wq, Xq = _operands(orc, 200 + M, N, K, M)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M)
+    ref = orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M)
+    for m in range(M):
+        assert_close(got[m], ref[m], TOL, f"M={M} column {m}")
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (7, 4096), (70, 4352), (33, 8192), (64, 12288), (19, 14336), (5, 16384)])
+@pytest.mark.parametrize("M", [1, 2, 5, 16, 24])
+def test_q4_0_shapes_span_steps_and_tails(dg, dev, orc, N, K, M):
+    Wq, Xq = _operands(orc, 210, N, K, M)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M)
+    ref = orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M)
+    assert_close(got, ref, TOL, f"{N}x{K} M={M}")
+
+
+VARIANTS = [
+    dict(variant=11), dict(variant=11, grid=3, block=64), dict(variant=11, block=128),
+    dict(variant=12, unroll=1), dict(variant=12, unroll=2), dict(variant=12, unroll=4), dict(variant=12, grid=2),
+]
+
+
+@pytest.mark.parametrize("launch", VARIANTS, ids=[str(v) for v in VARIANTS])
+def test_q4_0_m1_variants(dg, dev, orc, launch):
+    N, K = 301, 8192
+    Wq, Xq = _operands(orc, 220, N, K, 1)
+    got = _gpu(dg, dev, Wq, Xq, N, K, 1, launch=launch)
+    assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, str(launch))
+
+
+@pytest.mark.parametrize("M,R", [(2, 1), (2, 2), (3, 4), (8, 1), (8, 2), (24, 1), (24, 2)])
+def test_q4_0_lds_rows_per_wave(dg, dev, orc, M, R):
+    N, K = 77, 4608
+    Wq, Xq = _operands(orc, 230, N, K, M)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=dict(variant=12, unroll=R))
+    assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M), TOL, f"M={M} R={R}")
+
+
+def test_q4_0_70b_mlp_shape_sampled_rows(dg, dev, orc):
+    """The 4-bit M = 1 decode shape: N = 28672, K = 8192."""
+    N, K = 28672, 8192
+    Wq, Xq = _operands(orc, 2, N, K, 1)
+    got = _gpu(dg, dev, Wq, Xq, N, K, 1)
+    rows = np.unique(np.concatenate([np.arange(0, N, 37), [N - 1]]))
+    ref = orc.gemv_q4_0_q8_1(Wq.reshape(N, -1)[rows], Xq, len(rows), K, 1)
+    assert_close(got[0, rows], ref[0], TOL, "28672x8192 sampled")
+
+
+@pytest.mark.parametrize("N,K", [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 12, 16, 24])
+def test_q4_0_decoder_layer_shapes_sampled_rows(dg, dev, orc, N, K, M):
+    Wq, Xq = _operands(orc, 3, N, K, M)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M)
+    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 97)), [N - 1]]))
+    ref = orc.gemv_q4_0_q8_1(Wq.reshape(N, -1)[rows], Xq, len(rows), K, M)
+    assert_close(got[:, rows], ref, TOL, f"{N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("M", [2, 13, 16, 24])
+def test_q4_0_identical_columns_give_identical_outputs(dg, dev, orc, M):
+    N, K = 300, 4096
+    Wq, Xq = _operands(orc, 240, N, K, M, same_columns=True)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M)
+    for m in range(1, M):
+        assert np.array_equal(got[m], got[0])
+
+
+def test_q4_0_worked_blocks_tiled(dg, dev):
+    """The hand-worked blocks of tests/golden, each repeated 8 times along K
+    (K = 256): y = 8 times the block's value, exact in fp32."""
+    with open(os.path.join(os.path.dirname(__file__), "golden", "q4_0_q8_1_worked.json")) as f:
+        ex = json.load(f)["dot_examples"]
+    for e in ex:
+        w = np.frombuffer(bytes.fromhex(e["q4_0_block_hex"].replace(" ", "")), np.uint8)
+        x = np.frombuffer(bytes.fromhex(e["q8_1_block_hex"].replace(" ", "")), np.uint8)
+        got = _gpu(dg, dev, np.tile(w, 8), np.tile(x, 8), 1, 256, 1)
+        assert got[0, 0] == 8 * e["y"], e["name"]
+
+
+def test_q4_0_k_zero_and_empty(dg, dev):
+    import torch
+    W = torch.zeros(64, dtype=torch.uint8, device=dev)
+    X = torch.zeros(64, dtype=torch.uint8, device=dev)
+    Y = torch.full((3, 5), 9.0, dtype=torch.float32, device=dev)
+    dg.dg_gemv_q4_0(W, X, Y, 5, 256, 0)      # M = 0: nothing written
+    dg.dg_gemv_q4_0(W, X, Y, 0, 256, 3)      # N = 0: nothing written
+    torch.cuda.synchronize()
+    assert torch.all(Y == 9.0)
+    dg.dg_gemv_q4_0(W, X, Y, 5, 0, 3)        # K = 0: empty sums
+    torch.cuda.synchronize()
+    assert torch.all(Y == 0.0)
+
+
+def test_q4_0_deterministic(dg, dev, orc):
+    N, K, M = 1000, 8192, 3
+    Wq, Xq = _operands(orc, 250, N, K, M)
+    a = _gpu(dg, dev, Wq, Xq, N, K, M)
+    b = _gpu(dg, dev, Wq, Xq, N, K, M)
+    assert np.array_equal(a, b)

@@ -1,0 +1,50 @@
+"""dg_stream_read reads every byte exactly once: its checksum equals the
+oracle's wrapping word sum (GPU)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(dg, dev, buf, nbytes, **kw):
+    import torch
+    cs = torch.zeros(1, dtype=torch.int32, device=dev)
+    dg.dg_stream_read(buf, cs, nbytes=nbytes, **kw)
+    torch.cuda.synchronize()
+    return int(cs.cpu().numpy().view(np.uint32)[0])
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, 1 << 20, (64 << 20) + 48])
+@pytest.mark.parametrize("launch", [dict(nontemporal=1), dict(nontemporal=0),
+                                    dict(grid_blocks=1, block_threads=64), dict(grid_blocks=7, block_threads=1024),
+                                    dict(grid_blocks=4096, block_threads=512)])
+def test_stream_checksum_matches_oracle(dg, dev, orc, nbytes, launch):
+    import torch
+    g = np.random.default_rng(nbytes)
+    words = g.integers(0, 2**32, size=nbytes // 4, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to(dev)
+    assert _run(dg, dev, buf, nbytes, **launch) == orc.checksum_u32(words)
+
+
+def test_stream_checksum_accumulates(dg, dev, orc):
+    import torch
+    words = np.arange(1 << 16, dtype=np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).to(dev)
+    cs = torch.zeros(1, dtype=torch.int32, device=dev)
+    dg.dg_stream_read(buf, cs)
+    dg.dg_stream_read(buf, cs)
+    torch.cuda.synchronize()
+    assert int(cs.cpu().numpy().view(np.uint32)[0]) == (2 * orc.checksum_u32(words)) % 2**32
+
+
+def test_stream_full_size_closed_form(dg, dev):
+    """The ceiling workload, an 8 GiB buffer (32 x the 256 MiB last-level cache),
+    filled with w_i = i: the wrapping sum has the closed form n(n-1)/2 mod 2^32."""
+    import torch
+    n = (8 << 30) // 4
+    buf = torch.arange(n, dtype=torch.int32, device=dev)    # 0 .. 2^31 - 1
+    expect = (n * (n - 1) // 2) % 2**32
+    for nt in (1, 0):
+        assert _run(dg, dev, buf, n * 4, nontemporal=nt, grid_blocks=2048) == expect
+    del buf
+    torch.cuda.empty_cache()
