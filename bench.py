@@ -172,28 +172,33 @@ def q8_columns(cfg, K, M):
 # ---------------------------------------------------------------------------
 
 def measure_ceiling(full_sweep=False, records=None):
+    """Best streaming-read rate over access orders and launch shapes (8 GiB,
+    32 x the last-level cache; median of 5 runs of 20 reads after 10 warm-ups)."""
     import memory_bound_decode_gemv_amd as dg
     torch = _torch()
     nbytes = 8 * GIB
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
     buf.fill_(1)
     cs = torch.zeros(1, dtype=torch.int32, device="cuda")
-    grids = [1024, 2048, 4096, 8192, 16384] if full_sweep else [2048, 4096, 8192]
-    blocks = [256, 512, 1024] if full_sweep else [256, 512]
-    nts = [1, 0] if full_sweep else [1]
+    if full_sweep:
+        shapes = [(g, b, f) for f in (1, 5) for g in (128, 256, 384, 512, 768, 1024, 2048)
+                  for b in (64, 128, 256, 512)]
+        shapes += [(g, 256, 1) for g in (16384, 65536, 262144)]        # about one 8 KiB chunk per wave
+        shapes += [(g, b, f) for f in (0, 3, 2) for g in (512, 1024, 2048) for b in (256, 512)]
+    else:
+        shapes = [(512, 256, 1), (384, 256, 1), (256, 512, 1), (512, 256, 5), (262144, 256, 1)]
     best = None
-    for nt in nts:
-        for grid in grids:
-            for block in blocks:
-                def call(grid=grid, block=block, nt=nt):
-                    dg.dg_stream_read(buf, cs, nbytes=nbytes, grid_blocks=grid, block_threads=block, nontemporal=nt)
-                us, iqr = time_per_call([call] * 20, reps=5, warm=10, graph=False)
-                gbps = nbytes / (us * 1e-6) / 1e9
-                if records is not None:
-                    records.append(record("stream_read", us, iqr, nbytes, None, grid=grid, block=block,
-                                          nontemporal=nt))
-                if best is None or gbps > best[0]:
-                    best = (gbps, dict(grid=grid, block=block, nontemporal=nt), us)
+    for grid, block, flags in shapes:
+        def call(grid=grid, block=block, flags=flags):
+            dg.dg_stream_read(buf, cs, nbytes=nbytes, grid_blocks=grid, block_threads=block, flags=flags)
+        us, iqr = time_per_call([call] * 20, reps=5, warm=10, graph=False)
+        gbps = nbytes / (us * 1e-6) / 1e9
+        cfg = dict(grid=grid, block=block, nontemporal=flags & 1,
+                   order="grid-stride" if flags & 2 else "wave-contiguous", loads_per_lane=16 if flags & 4 else 8)
+        if records is not None:
+            records.append(record("stream_read", us, iqr, nbytes, None, **cfg))
+        if best is None or gbps > best[0]:
+            best = (gbps, cfg, us)
     del buf
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -372,6 +377,13 @@ def suite(args):
         emit(r)
     emit({"name": "ceiling", "gbps": round(ceil_gbps, 1), **ceil_cfg})
 
+    # the launch floor: a 16-byte read by one wave, back to back in a graph
+    tiny = torch.zeros(64, dtype=torch.int32, device="cuda")
+    cs = torch.zeros(1, dtype=torch.int32, device="cuda")
+    calls = [(lambda: dg.dg_stream_read(tiny, cs, nbytes=16, grid_blocks=1, block_threads=64))] * 64
+    us, iqr = time_per_call(calls)
+    emit(record("launch floor (16-byte read, 1 wave)", us, iqr, 16, None))
+
     # fp16 4096x4096: the page's three versions and launch shapes
     n16 = copies_for(2 * 4096 * 4096)
     W16, x16 = dense_copies(0, 4096, 4096, n16, torch.float16)
@@ -389,6 +401,14 @@ def suite(args):
                          for c in range(n16)]
                 us, iqr = time_per_call(calls)
                 emit(record("gemv_f16 4096x4096", us, iqr, b16, ceil_gbps, variant=vname, grid=grid, block=block))
+    for unroll in (8, 4, 104, 102, 108, 302, 304):
+        for block in (256, 512):
+            launch = dict(variant=1, unroll=unroll, block=block)
+            calls = [(lambda c=c, launch=launch: dg.dg_gemv_f16(W16[c % n16], x16, y16, launch=launch))
+                     for c in range(n16)]
+            us, iqr = time_per_call(calls)
+            emit(record("gemv_f16 4096x4096", us, iqr, b16, ceil_gbps, variant="wide", U=unroll % 100,
+                        KS=unroll // 100 + 1, block=block))
     calls = [(lambda c=c: dg.dg_gemv_f16(W16[c % n16], x16, y16)) for c in range(n16)]
     us, iqr = time_per_call(calls)
     emit(record("gemv_f16 4096x4096", us, iqr, b16, ceil_gbps, variant="default"))
@@ -405,12 +425,13 @@ def suite(args):
         nb = bytes_dense(N, K, 4)
         calls = [(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, yb)) for c in range(max(nc, 8))]
         us, iqr = time_per_call(calls)
-        emit(record(f"gemv_bf16 {N}x{K}", us, iqr, nb, ceil_gbps, copies=nc))
-        for grid in (512, 1024, 2048):
-            launch = dict(variant=1, grid=grid, block=256)
+        emit(record(f"gemv_bf16 {N}x{K}", us, iqr, nb, ceil_gbps, copies=nc, variant="default"))
+        for unroll in (8, 4, 104, 108, 102, 304, 302):
+            launch = dict(variant=1, unroll=unroll, block=256)
             calls = [(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, yb, launch=launch)) for c in range(max(nc, 8))]
             us, iqr = time_per_call(calls)
-            emit(record(f"gemv_bf16 {N}x{K}", us, iqr, nb, ceil_gbps, copies=nc, grid=grid, block=256))
+            emit(record(f"gemv_bf16 {N}x{K}", us, iqr, nb, ceil_gbps, copies=nc, U=unroll % 100,
+                        KS=unroll // 100 + 1))
         del Wb
         torch.cuda.empty_cache()
 
@@ -421,8 +442,10 @@ def suite(args):
     Yq = torch.empty(Q4_N, dtype=torch.float32, device="cuda")
     bq = bytes_q4(Q4_N, Q4_K, 1)
     launches = [("default", None)] + [(f"regs g{g} b{b}", dict(variant=11, grid=g, block=b))
-                                      for g in (512, 1024, 2048, 4096, 7168) for b in (64, 256)] + \
-               [(f"lds R{r}", dict(variant=12, unroll=r)) for r in (1, 2, 4)]
+                                      for g in (256, 512, 768, 1024, 2048, 7168) for b in (64, 128, 256)] + \
+               [(f"lds R{r}", dict(variant=12, unroll=r)) for r in (1, 2, 4)] + \
+               [(f"ldsrow d{d} g{g} b{b}", dict(variant=13, grid=g, block=b, unroll=d))
+                for d in (2, 3, 4) for g in (0, 512, 768, 1024, 2048) for b in (128, 256)]
     for lname, launch in launches:
         calls = [(lambda c=c, launch=launch: dg.dg_gemv_q4_0(Wq[c % nq], Xq, Yq, Q4_N, Q4_K, 1, launch=launch))
                  for c in range(3 * nq)]

@@ -54,26 +54,33 @@ const char* dg_last_hip_error(void);
 /* ------------------------------------------------------------------------
  * Streaming-read ceiling probe
  *
- * Reads every byte of `buf` exactly once, 16 bytes per lane per load, in a
- * grid-stride loop, and ADDS the wrapping (mod 2^32) sum of its little-endian
- * 32-bit words into *d_checksum; the sum is what keeps the loads alive.  This
- * is the denominator measurement of the batch1-cdna README ("01-ceiling":
- * grid-stride read of a buffer far larger than the last-level cache with
- * 4 x 32-bit vector loads, normal or non-temporal).
+ * Reads every byte of `buf` exactly once, 16 bytes per lane per load, and
+ * ADDS the wrapping (mod 2^32) sum of its little-endian 32-bit words into
+ * *d_checksum; the sum is what keeps the loads alive.  This is the
+ * denominator measurement of the batch1-cdna README ("01-ceiling": a read of a
+ * buffer far larger than the last-level cache with 4 x 32-bit vector loads,
+ * normal or non-temporal).
  *
  *   buf          device, 16-byte aligned, `bytes` long.
  *   bytes        multiple of 16 (0 is allowed: nothing is launched).
  *   d_checksum   device uint32; the caller zeroes it for a fresh sum.
- *   grid_blocks  workgroups to launch; 0 = library default (2048).
+ *   grid_blocks  workgroups to launch; 0 = library default (1024).
  *   block_threads threads per workgroup, a multiple of 64 in [64, 1024];
- *                0 = library default (256).
- *   nontemporal  0 = ordinary loads, 1 = non-temporal loads.
+ *                0 = library default (512).
+ *   flags        DG_READ_NONTEMPORAL: non-temporal loads (else ordinary);
+ *                DG_READ_GRID_STRIDE: the page's order, consecutive lanes of
+ *                the whole grid on consecutive vectors (else each wave reads
+ *                8 KiB of consecutive bytes per step);
+ *                DG_READ_DEEP: 16 loads in flight per lane instead of 8
+ *                (wave-contiguous order only).
  * Errors: DG_ERR_NULL (buf or d_checksum NULL with bytes > 0),
  * DG_ERR_MISALIGNED (buf not 16-byte aligned, d_checksum not 4-byte aligned),
- * DG_ERR_SHAPE (bytes % 16 != 0), DG_ERR_ARG (grid/block out of range).
+ * DG_ERR_SHAPE (bytes % 16 != 0), DG_ERR_ARG (grid/block/flags out of range).
  * ------------------------------------------------------------------------ */
+enum { DG_READ_NONTEMPORAL = 1, DG_READ_GRID_STRIDE = 2, DG_READ_DEEP = 4 };
+
 dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_checksum,
-                         int grid_blocks, int block_threads, int nontemporal,
+                         int grid_blocks, int block_threads, int flags,
                          dg_stream stream);
 
 /* ------------------------------------------------------------------------
@@ -194,7 +201,10 @@ typedef struct {
     int variant;   /* kernel variant id, 0 = default                       */
     int grid;      /* workgroups, 0 = default                              */
     int block;     /* threads per workgroup (multiple of 64), 0 = default  */
-    int unroll;    /* loads in flight per lane per step, 0 = default       */
+    int unroll;    /* loads in flight per lane per step, 0 = default;
+                      dense DG_VARIANT_DENSE_WIDE: U + 100*(S-1) also splits
+                      each row's K over S in {1,2,4} waves of a workgroup;
+                      Q4_0 DG_VARIANT_Q4_LDS: rows per wave (1, 2, 4)       */
 } dg_launch;
 
 enum {
@@ -205,7 +215,8 @@ enum {
     DG_VARIANT_DENSE_NARROW4 = 4,   /* 4 B per lane, four accumulators (ablation)              */
     /* Q4_0 */
     DG_VARIANT_Q4_REGS = 11,        /* activations in registers, one row per wave (M = 1)       */
-    DG_VARIANT_Q4_LDS = 12          /* activations staged in LDS, several rows per wave          */
+    DG_VARIANT_Q4_LDS = 12,         /* activations staged in LDS, several rows per wave          */
+    DG_VARIANT_Q4_LDSROW = 13       /* M = 1: weight rows copied to LDS with coalesced loads     */
 };
 
 dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K,

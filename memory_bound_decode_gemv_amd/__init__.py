@@ -25,12 +25,17 @@ DG_ERR_WORKSPACE = 4
 DG_ERR_HIP = 5
 DG_ERR_ARG = 6
 
+DG_READ_NONTEMPORAL = 1
+DG_READ_GRID_STRIDE = 2
+DG_READ_DEEP = 4
+
 DG_VARIANT_DENSE_WIDE = 1
 DG_VARIANT_DENSE_XREG = 2
 DG_VARIANT_DENSE_NARROW1 = 3
 DG_VARIANT_DENSE_NARROW4 = 4
 DG_VARIANT_Q4_REGS = 11
 DG_VARIANT_Q4_LDS = 12
+DG_VARIANT_Q4_LDSROW = 13
 
 # Every symbol include/decodegemv.h declares.
 EXPORTED = (
@@ -166,13 +171,13 @@ def _cfg(variant=0, grid=0, block=0, unroll=0):
 # ---------------------------------------------------------------------------
 
 def dg_stream_read(buf, checksum, nbytes=None, grid_blocks=0, block_threads=0,
-                   nontemporal=1, stream=None):
+                   flags=DG_READ_NONTEMPORAL, stream=None):
     """Adds the wrapping uint32 word sum of buf's bytes into checksum (int32[1])."""
     torch = _torch()
     _need(checksum, (torch.int32,), "checksum")
     nbytes = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
     _check(_lib().dg_stream_read(_ptr(buf), nbytes, _ptr(checksum), int(grid_blocks),
-                                 int(block_threads), int(nontemporal), _stream(stream)),
+                                 int(block_threads), int(flags), _stream(stream)),
            "dg_stream_read")
 
 

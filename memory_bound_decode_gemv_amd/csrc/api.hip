@@ -82,6 +82,19 @@ int device_cu_count() {
     return v;
 }
 
+size_t device_max_lds_per_block() {
+    static std::atomic<long long> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 64 * 1024;
+    long long v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return (size_t)v;
+    int a = 0;
+    if (hipDeviceGetAttribute(&a, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || a <= 0)
+        a = 64 * 1024;
+    cached[dev].store(a, std::memory_order_relaxed);
+    return (size_t)a;
+}
+
 }  // namespace dg
 
 using namespace dg;
@@ -104,17 +117,17 @@ const char* dg_status_string(dg_status status) {
 const char* dg_last_hip_error(void) { return g_last_hip_error.c_str(); }
 
 dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_checksum, int grid_blocks,
-                         int block_threads, int nontemporal, dg_stream stream) {
+                         int block_threads, int flags, dg_stream stream) {
     if (bytes % 16 != 0) return DG_ERR_SHAPE;
-    if (grid_blocks < 0 || block_threads < 0 || (nontemporal != 0 && nontemporal != 1)) return DG_ERR_ARG;
+    if (grid_blocks < 0 || block_threads < 0 || (flags & ~(DG_READ_NONTEMPORAL | DG_READ_GRID_STRIDE | DG_READ_DEEP)))
+        return DG_ERR_ARG;
     if (block_threads && (block_threads % kWave != 0 || block_threads > 1024)) return DG_ERR_ARG;
     if (bytes == 0) return DG_OK;
     if (!buf || !d_checksum) return DG_ERR_NULL;
     if (!aligned(buf, 16) || !aligned(d_checksum, 4)) return DG_ERR_MISALIGNED;
-    const int grid = grid_blocks ? grid_blocks : 2048;
-    const int block = block_threads ? block_threads : 256;
-    return hip_status(launch_stream_read(buf, bytes, d_checksum, grid, block, nontemporal != 0,
-                                         (hipStream_t)stream));
+    const int grid = grid_blocks ? grid_blocks : 1024;
+    const int block = block_threads ? block_threads : 512;
+    return hip_status(launch_stream_read(buf, bytes, d_checksum, grid, block, flags, (hipStream_t)stream));
 }
 
 dg_status dg_gemv_f16(const void* W, const void* x, void* y, int64_t N, int64_t K, int64_t ldw,

@@ -17,11 +17,12 @@ struct Launch {
     int unroll;
 };
 
-// Device properties used to size grids; cached per device.
+// Device properties used to size grids and check launches; cached per device.
 int device_cu_count();
+size_t device_max_lds_per_block();
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* d_checksum,
-                              int grid, int block, bool nontemporal, hipStream_t s);
+                              int grid, int block, int flags, hipStream_t s);
 
 // Dense GEMV launcher; `bf16` selects bfloat16 operands with fp32 output,
 // otherwise binary16 operands with binary16 output.  Returns hipErrorInvalidValue

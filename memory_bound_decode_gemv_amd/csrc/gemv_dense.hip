@@ -45,15 +45,27 @@ __device__ __forceinline__ int wave_in_block() {
 // 16 bytes (8 elements) per lane; U loads in flight per lane per step.
 // XREG: the lane's share of x (at most U vectors) is loaded once and kept in
 // registers for every row the wave handles; requires K/8 <= 64*U.
-template <bool BF16, int U, bool XREG>
+// KS (split K): KS waves of a workgroup share one row, wave j taking the
+// steps j, j+KS, j+2KS, ... of 64*U vectors; their partial sums meet in LDS
+// and are added in the fixed order 0..KS-1 (deterministic).  This multiplies
+// the waves, and so the bytes in flight, of shapes with few rows.  The row loop
+// runs the same number of times in every wave of a workgroup, so that every
+// wave reaches every barrier.
+template <bool BF16, int U, bool XREG, int KS>
 __global__ void __launch_bounds__(1024)
 k_gemv_wide(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
             void* __restrict__ y, int N, int K, int64_t ldw) {
+    static_assert(!XREG || KS == 1, "x in registers needs whole rows per wave");
     const int lane = lane_id();
+    const int wave = wave_in_block();
     const int wpb = blockDim.x / kWave;
+    const int rows_per_block = wpb / KS;
+    const int kpart = wave % KS;
+    const int rslot = wave / KS;
     const int nvec = K >> 3;
     const u32x4* __restrict__ xv = reinterpret_cast<const u32x4*>(x);
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    __shared__ float part[KS > 1 ? 1024 / kWave : 1];
 
     u32x4 xr[XREG ? U : 1];
     if constexpr (XREG) {
@@ -64,58 +76,73 @@ k_gemv_wide(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
         }
     }
 
-    for (int row = blockIdx.x * wpb + wave_in_block(); row < N; row += gridDim.x * wpb) {
-        const u32x4* __restrict__ wr = reinterpret_cast<const u32x4*>(W + (int64_t)row * ldw);
-        float acc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] = 0.0f;
-
-        if constexpr (XREG) {
-            if (nvec > 0) {
-                u32x4 wv[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int idx = u * kWave + lane;
-                    wv[u] = load_vec<true>(wr + (idx < nvec ? idx : nvec - 1));
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int idx = u * kWave + lane;
-                    acc[u] = dot8<BF16>(idx < nvec ? wv[u] : zero, xr[u], acc[u]);
-                }
-            }
-        } else {
-            int v0 = 0;
-            for (; v0 + kWave * U <= nvec; v0 += kWave * U) {
-                u32x4 wv[U], xw[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) wv[u] = load_vec<true>(wr + v0 + u * kWave + lane);
-#pragma unroll
-                for (int u = 0; u < U; ++u) xw[u] = xv[v0 + u * kWave + lane];
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc[u] = dot8<BF16>(wv[u], xw[u], acc[u]);
-            }
-            if (v0 < nvec) {  // ragged last step: out-of-range lanes read a valid vector, then zero it
-                u32x4 wv[U], xw[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int idx = v0 + u * kWave + lane;
-                    const int idc = idx < nvec ? idx : nvec - 1;
-                    wv[u] = load_vec<true>(wr + idc);
-                    xw[u] = xv[idc];
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const bool ok = v0 + u * kWave + lane < nvec;
-                    acc[u] = dot8<BF16>(ok ? wv[u] : zero, ok ? xw[u] : zero, acc[u]);
-                }
-            }
-        }
+    for (int row0 = blockIdx.x * rows_per_block; row0 < N; row0 += gridDim.x * rows_per_block) {
+        const int row = row0 + rslot;
         float s = 0.0f;
+        if (row < N) {   // wave-uniform
+            const u32x4* __restrict__ wr = reinterpret_cast<const u32x4*>(W + (int64_t)row * ldw);
+            float acc[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) s += acc[u];
-        s = wave_sum_f32(s);
-        if (lane == 0) store_out<BF16>(y, row, s);
+            for (int u = 0; u < U; ++u) acc[u] = 0.0f;
+
+            if constexpr (XREG) {
+                if (nvec > 0) {
+                    u32x4 wv[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int idx = u * kWave + lane;
+                        wv[u] = load_vec<true>(wr + (idx < nvec ? idx : nvec - 1));
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int idx = u * kWave + lane;
+                        acc[u] = dot8<BF16>(idx < nvec ? wv[u] : zero, xr[u], acc[u]);
+                    }
+                }
+            } else {
+                int v0 = kpart * kWave * U;
+                for (; v0 + kWave * U <= nvec; v0 += KS * kWave * U) {
+                    u32x4 wv[U], xw[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) wv[u] = load_vec<true>(wr + v0 + u * kWave + lane);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) xw[u] = xv[v0 + u * kWave + lane];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) acc[u] = dot8<BF16>(wv[u], xw[u], acc[u]);
+                }
+                if (v0 < nvec) {  // ragged last step: out-of-range lanes read a valid vector, then zero it
+                    u32x4 wv[U], xw[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int idx = v0 + u * kWave + lane;
+                        const int idc = idx < nvec ? idx : nvec - 1;
+                        wv[u] = load_vec<true>(wr + idc);
+                        xw[u] = xv[idc];
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const bool ok = v0 + u * kWave + lane < nvec;
+                        acc[u] = dot8<BF16>(ok ? wv[u] : zero, ok ? xw[u] : zero, acc[u]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) s += acc[u];
+            s = wave_sum_f32(s);
+        }
+        if constexpr (KS == 1) {
+            if (row < N && lane == 0) store_out<BF16>(y, row, s);
+        } else {
+            if (lane == 0) part[wave] = s;
+            __syncthreads();
+            if (kpart == 0 && row < N && lane == 0) {
+                float t = part[wave];
+#pragma unroll
+                for (int j = 1; j < KS; ++j) t += part[wave + j];
+                store_out<BF16>(y, row, t);
+            }
+            __syncthreads();
+        }
     }
 }
 
@@ -154,31 +181,45 @@ k_gemv_narrow(const uint16_t* __restrict__ W, const uint16_t* __restrict__ x,
     }
 }
 
-template <bool BF16>
-hipError_t launch_wide(int U, bool xreg, const void* W, const void* x, void* y, int N, int K,
-                       int64_t ldw, int grid, int block, hipStream_t s) {
-    const uint16_t* w16 = (const uint16_t*)W;
-    const uint16_t* x16 = (const uint16_t*)x;
-#define DG_WIDE_CASE(UU)                                                                       \
-    case UU:                                                                                   \
-        if (xreg)                                                                              \
-            hipLaunchKernelGGL((k_gemv_wide<BF16, UU, true>), dim3(grid), dim3(block), 0, s,   \
-                               w16, x16, y, N, K, ldw);                                        \
-        else                                                                                   \
-            hipLaunchKernelGGL((k_gemv_wide<BF16, UU, false>), dim3(grid), dim3(block), 0, s,  \
-                               w16, x16, y, N, K, ldw);                                        \
+template <bool BF16, int KS>
+hipError_t launch_wide_ks(int U, bool xreg, const uint16_t* w16, const uint16_t* x16, void* y, int N, int K,
+                          int64_t ldw, int grid, int block, hipStream_t s) {
+#define DG_WIDE_CASE(UU)                                                                         \
+    case UU:                                                                                     \
+        if (xreg) {                                                                              \
+            if constexpr (KS == 1)                                                               \
+                hipLaunchKernelGGL((k_gemv_wide<BF16, UU, true, 1>), dim3(grid), dim3(block), 0, \
+                                   s, w16, x16, y, N, K, ldw);                                   \
+            else                                                                                 \
+                return hipErrorInvalidValue;                                                     \
+        } else {                                                                                 \
+            hipLaunchKernelGGL((k_gemv_wide<BF16, UU, false, KS>), dim3(grid), dim3(block), 0,   \
+                               s, w16, x16, y, N, K, ldw);                                       \
+        }                                                                                        \
         break;
     switch (U) {
         DG_WIDE_CASE(1)
         DG_WIDE_CASE(2)
         DG_WIDE_CASE(4)
         DG_WIDE_CASE(8)
-        DG_WIDE_CASE(16)
         default:
             return hipErrorInvalidValue;
     }
 #undef DG_WIDE_CASE
     return hipGetLastError();
+}
+
+template <bool BF16>
+hipError_t launch_wide(int U, int KS, bool xreg, const void* W, const void* x, void* y, int N, int K,
+                       int64_t ldw, int grid, int block, hipStream_t s) {
+    const uint16_t* w16 = (const uint16_t*)W;
+    const uint16_t* x16 = (const uint16_t*)x;
+    switch (KS) {
+        case 1: return launch_wide_ks<BF16, 1>(U, xreg, w16, x16, y, N, K, ldw, grid, block, s);
+        case 2: return launch_wide_ks<BF16, 2>(U, xreg, w16, x16, y, N, K, ldw, grid, block, s);
+        case 4: return launch_wide_ks<BF16, 4>(U, xreg, w16, x16, y, N, K, ldw, grid, block, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 int round_up_pow2_unroll(int v) {
@@ -192,28 +233,37 @@ int round_up_pow2_unroll(int v) {
 hipError_t launch_gemv_dense(bool bf16, const void* W, const void* x, void* y,
                              int N, int K, int64_t ldw, const dg_launch* cfg, hipStream_t s) {
     const int nvec = K / 8;
-    int variant = cfg && cfg->variant ? cfg->variant : DG_VARIANT_DENSE_WIDE;
-    int block = cfg && cfg->block ? cfg->block : 256;
+    const int variant = cfg && cfg->variant ? cfg->variant : DG_VARIANT_DENSE_WIDE;
+    const int block = cfg && cfg->block ? cfg->block : 256;
     const int wpb = block / kWave;
-    const int rows_per_grid_default = (N + wpb - 1) / wpb;   // one row per wave
-    int grid = cfg && cfg->grid ? cfg->grid : rows_per_grid_default;
-    if (grid < 1) grid = 1;
 
     if (variant == DG_VARIANT_DENSE_WIDE || variant == DG_VARIANT_DENSE_XREG) {
         const bool xreg = variant == DG_VARIANT_DENSE_XREG;
-        int U = cfg && cfg->unroll ? cfg->unroll : 8;
+        int U = 8, KS = 1;
         if (xreg) {
-            const int need = round_up_pow2_unroll((nvec + kWave - 1) / kWave);
-            if (cfg && cfg->unroll) {
-                if (cfg->unroll * kWave < nvec) return hipErrorInvalidValue;
-            } else {
-                U = need < 1 ? 1 : need;
-            }
-            if (U * kWave < nvec) return hipErrorInvalidValue;
+            U = round_up_pow2_unroll((nvec + kWave - 1) / kWave);
+            if (cfg && cfg->unroll) U = cfg->unroll;
+            if (U * kWave < nvec || U > 8) return hipErrorInvalidValue;
+        } else if (cfg && cfg->unroll) {
+            // explicit: unroll = U + 100 * (KS - 1) lets a sweep pick both
+            U = cfg->unroll % 100;
+            KS = cfg->unroll / 100 + 1;
+        } else {
+            // Measured on MI355X over the decoder shapes and the lm-head: two
+            // 16-byte loads per lane per step with each row's K split over two
+            // waves (four below 2048 rows) keep the most bytes in flight, since
+            // the small register footprint lets more waves stay resident.
+            U = 2;
+            if (wpb >= 2 && nvec >= 2 * kWave * U) KS = 2;
+            if (wpb >= 4 && N < 2048 && nvec >= 4 * kWave * U) KS = 4;
         }
-        return bf16 ? launch_wide<true>(U, xreg, W, x, y, N, K, ldw, grid, block, s)
-                    : launch_wide<false>(U, xreg, W, x, y, N, K, ldw, grid, block, s);
+        if (wpb % KS != 0) return hipErrorInvalidValue;
+        const int rows_per_block = wpb / KS;
+        const int grid = cfg && cfg->grid ? cfg->grid : (N + rows_per_block - 1) / rows_per_block;
+        return bf16 ? launch_wide<true>(U, KS, xreg, W, x, y, N, K, ldw, grid, block, s)
+                    : launch_wide<false>(U, KS, xreg, W, x, y, N, K, ldw, grid, block, s);
     }
+    const int grid = cfg && cfg->grid ? cfg->grid : (N + wpb - 1) / wpb;
     if (variant == DG_VARIANT_DENSE_NARROW1 || variant == DG_VARIANT_DENSE_NARROW4) {
         const uint16_t* w16 = (const uint16_t*)W;
         const uint16_t* x16 = (const uint16_t*)x;

@@ -1,37 +1,32 @@
 // stream_read.hip -- HBM streaming-read ceiling probe.
 //
-// batch1-cdna README, "01-ceiling": a grid-stride read of a buffer many times
-// larger than the last-level cache, 16 bytes per lane per load, with ordinary
-// or non-temporal loads; the achieved rate is the denominator of every
-// bandwidth-utilisation figure.  Here the loaded words are summed into a
-// wrapping uint32 checksum (one atomic add per workgroup) so that the loads
-// stay live and the result can be checked exactly.
+// batch1-cdna README, "01-ceiling": a read of a buffer many times larger than
+// the last-level cache, 16 bytes per lane per load, with ordinary or
+// non-temporal loads; the achieved rate is the denominator of every
+// bandwidth-utilisation figure.  The loaded words are summed into a wrapping
+// uint32 checksum (one atomic add per workgroup) so that the loads stay live
+// and the result can be checked exactly.
+//
+// Two access orders:
+//  * wave-contiguous (default): each wave reads 64 lanes x U x 16 B = 8 KiB
+//    (U = 8) or 16 KiB (U = 16, DG_READ_DEEP) of consecutive bytes per step,
+//    then jumps by the whole grid's share -- the order in which a GEMV wave
+//    reads its weight row;
+//  * grid-stride (the page's kernel): consecutive lanes of the whole grid read
+//    consecutive 16-byte vectors, and a lane's kUnroll loads in flight are one
+//    grid-size apart.
+// The ceiling is the best rate over both orders and the launch shapes.
 #include "dg_device.h"
 #include "dg_internal.h"
 
 namespace dg {
 namespace {
 
-constexpr int kUnroll = 8;  // 16-byte loads in flight per lane per step
+constexpr int kUnroll = 8;  // 16-byte loads in flight per lane per step (grid-stride order)
 
-template <bool NT>
-__global__ void __launch_bounds__(1024)
-k_stream_read(const u32x4* __restrict__ p, uint64_t nvec, uint32_t* __restrict__ checksum) {
-    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    uint32_t acc = 0;
-    // Full steps: kUnroll independent loads are issued before any is consumed.
-    for (; i + (kUnroll - 1) * stride < nvec; i += kUnroll * stride) {
-        u32x4 v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) v[u] = load_vec<NT>(p + i + u * stride);
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) acc += (v[u].x + v[u].y) + (v[u].z + v[u].w);
-    }
-    for (; i < nvec; i += stride) {
-        u32x4 v = load_vec<NT>(p + i);
-        acc += (v.x + v.y) + (v.z + v.w);
-    }
+__device__ __forceinline__ uint32_t add4(u32x4 v) { return (v.x + v.y) + (v.z + v.w); }
+
+__device__ __forceinline__ void finish(uint32_t acc, uint32_t* __restrict__ checksum) {
     acc = wave_sum_u32(acc);
     __shared__ uint32_t part[1024 / kWave];
     const int wave = threadIdx.x / kWave;
@@ -44,17 +39,63 @@ k_stream_read(const u32x4* __restrict__ p, uint64_t nvec, uint32_t* __restrict__
     }
 }
 
+template <bool NT>
+__global__ void __launch_bounds__(1024)
+k_stream_read_grid(const u32x4* __restrict__ p, uint64_t nvec, uint32_t* __restrict__ checksum) {
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (kUnroll - 1) * stride < nvec; i += kUnroll * stride) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) v[u] = load_vec<NT>(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) acc += add4(v[u]);
+    }
+    for (; i < nvec; i += stride) acc += add4(load_vec<NT>(p + i));
+    finish(acc, checksum);
+}
+
+template <bool NT, int U>
+__global__ void __launch_bounds__(1024)
+k_stream_read_wave(const u32x4* __restrict__ p, uint64_t nvec, uint32_t* __restrict__ checksum) {
+    constexpr uint64_t kChunk = (uint64_t)kWave * U;   // vectors per wave step
+    const uint64_t nwaves = (uint64_t)gridDim.x * (blockDim.x / kWave);
+    const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    const int lane = lane_id();
+    uint32_t acc = 0;
+    uint64_t c = wave;
+    for (; (c + 1) * kChunk <= nvec; c += nwaves) {
+        const u32x4* q = p + c * kChunk + lane;
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = load_vec<NT>(q + u * kWave);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc += add4(v[u]);
+    }
+    if (c * kChunk < nvec) {   // the one partial chunk at the end of the buffer
+        for (uint64_t i = c * kChunk + lane; i < nvec; i += kWave) acc += add4(load_vec<NT>(p + i));
+    }
+    finish(acc, checksum);
+}
+
 }  // namespace
 
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* d_checksum,
-                              int grid, int block, bool nontemporal, hipStream_t s) {
+                              int grid, int block, int flags, hipStream_t s) {
     const uint64_t nvec = bytes / 16;
-    if (nontemporal)
-        hipLaunchKernelGGL(k_stream_read<true>, dim3(grid), dim3(block), 0, s,
-                           (const u32x4*)buf, nvec, d_checksum);
-    else
-        hipLaunchKernelGGL(k_stream_read<false>, dim3(grid), dim3(block), 0, s,
-                           (const u32x4*)buf, nvec, d_checksum);
+    const bool nt = flags & DG_READ_NONTEMPORAL;
+    const u32x4* p = (const u32x4*)buf;
+    if (flags & DG_READ_GRID_STRIDE) {
+        if (nt) hipLaunchKernelGGL(k_stream_read_grid<true>, dim3(grid), dim3(block), 0, s, p, nvec, d_checksum);
+        else hipLaunchKernelGGL(k_stream_read_grid<false>, dim3(grid), dim3(block), 0, s, p, nvec, d_checksum);
+    } else if (flags & DG_READ_DEEP) {
+        if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, 16>), dim3(grid), dim3(block), 0, s, p, nvec, d_checksum);
+        else hipLaunchKernelGGL((k_stream_read_wave<false, 16>), dim3(grid), dim3(block), 0, s, p, nvec, d_checksum);
+    } else {
+        if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, 8>), dim3(grid), dim3(block), 0, s, p, nvec, d_checksum);
+        else hipLaunchKernelGGL((k_stream_read_wave<false, 8>), dim3(grid), dim3(block), 0, s, p, nvec, d_checksum);
+    }
     return hipGetLastError();
 }
 

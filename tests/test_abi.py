@@ -90,7 +90,7 @@ def test_launch_overrides_rejected(lib):
 def test_stream_read_rejects_before_launch(lib):
     assert lib.dg_stream_read(A16, 24, A16, 0, 0, 1, None) == 3          # bytes % 16
     assert lib.dg_stream_read(A16, 32, A16, 0, 96, 1, None) == 6         # block not a multiple of 64
-    assert lib.dg_stream_read(A16, 32, A16, 0, 0, 2, None) == 6          # nontemporal flag
+    assert lib.dg_stream_read(A16, 32, A16, 0, 0, 8, None) == 6          # unknown flag
     assert lib.dg_stream_read(None, 32, A16, 0, 0, 1, None) == 1
     assert lib.dg_stream_read(A2, 32, A16, 0, 0, 1, None) == 2
     assert lib.dg_stream_read(None, 0, None, 0, 0, 1, None) == 0         # empty

@@ -66,6 +66,8 @@ VARIANTS = [
     dict(variant=1, unroll=1), dict(variant=1, unroll=2), dict(variant=1, unroll=4), dict(variant=1, unroll=8),
     dict(variant=2), dict(variant=3), dict(variant=4),
     dict(variant=1, grid=7, block=64), dict(variant=1, grid=3, block=1024), dict(variant=2, grid=5, block=128),
+    dict(variant=1, unroll=102), dict(variant=1, unroll=304), dict(variant=1, unroll=108, block=128),
+    dict(variant=1, unroll=301, grid=5, block=512), dict(variant=1, unroll=304, grid=2, block=1024),
 ]
 
 
@@ -76,6 +78,18 @@ def test_dense_variants_and_launch_shapes(dg, dev, orc, fmt, launch):
     Wb, xb = _inputs(fmt, 102, N, K)
     got = _run(dg, dev, fmt, Wb, xb, N, K, K, launch=launch)
     assert_close(got, _ref(orc, fmt, Wb, xb, N, K, K), TOL, str(launch))
+
+
+def test_dense_invalid_overrides_are_rejected(dg, dev):
+    import torch
+    W = torch.zeros((8, 64), dtype=torch.float16, device=dev)
+    x = torch.zeros(64, dtype=torch.float16, device=dev)
+    y = torch.zeros(8, dtype=torch.float16, device=dev)
+    for launch in (dict(variant=1, unroll=204), dict(variant=1, unroll=3), dict(variant=1, unroll=300, block=64),
+                   dict(variant=2, unroll=16), dict(variant=9)):
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_gemv_f16(W, x, y, launch=launch)
+        assert e.value.status == dg.DG_ERR_ARG, launch
 
 
 def test_dense_f16_full_size_all_rows(dg, dev, orc):

@@ -66,6 +66,8 @@ def test_q4_0_shapes_span_steps_and_tails(dg, dev, orc, N, K, M):
 VARIANTS = [
     dict(variant=11), dict(variant=11, grid=3, block=64), dict(variant=11, block=128),
     dict(variant=12, unroll=1), dict(variant=12, unroll=2), dict(variant=12, unroll=4), dict(variant=12, grid=2),
+    dict(variant=13), dict(variant=13, grid=3, block=64), dict(variant=13, grid=5, block=192),
+    dict(variant=13, block=128),
 ]
 
 
@@ -75,6 +77,17 @@ def test_q4_0_m1_variants(dg, dev, orc, launch):
     Wq, Xq = _operands(orc, 220, N, K, 1)
     got = _gpu(dg, dev, Wq, Xq, N, K, 1, launch=launch)
     assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, str(launch))
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (7, 4096), (70, 4352), (33, 8192), (64, 12288), (130, 2304)])
+@pytest.mark.parametrize("launch", [dict(variant=13), dict(variant=13, grid=2, block=128),
+                                    dict(variant=13, unroll=2, grid=3, block=64),
+                                    dict(variant=13, unroll=4, grid=2, block=64),
+                                    dict(variant=13, unroll=3, grid=1, block=256)])
+def test_q4_0_lds_row_copy_shapes(dg, dev, orc, N, K, launch):
+    Wq, Xq = _operands(orc, 225, N, K, 1)
+    got = _gpu(dg, dev, Wq, Xq, N, K, 1, launch=launch)
+    assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"{N}x{K} {launch}")
 
 
 @pytest.mark.parametrize("M,R", [(2, 1), (2, 2), (3, 4), (8, 1), (8, 2), (24, 1), (24, 2)])
@@ -112,6 +125,23 @@ def test_q4_0_identical_columns_give_identical_outputs(dg, dev, orc, M):
     got = _gpu(dg, dev, Wq, Xq, N, K, M)
     for m in range(1, M):
         assert np.array_equal(got[m], got[0])
+
+
+def test_q4_0_overrides_beyond_kernel_limits_are_rejected(dg, dev):
+    """Launch overrides a kernel cannot take (more threads than it was compiled
+    for, a variant for another column count) return an argument error instead
+    of launching."""
+    import torch
+    N, K = 64, 8192
+    W = torch.zeros(N * K // 32 * 18, dtype=torch.uint8, device=dev)
+    X = torch.zeros(2 * K // 32 * 36, dtype=torch.uint8, device=dev)
+    Y = torch.zeros(2 * N, dtype=torch.float32, device=dev)
+    for M, launch in ((1, dict(variant=11, block=512)), (1, dict(variant=13, block=1024)),
+                      (2, dict(variant=11)), (2, dict(variant=13)), (1, dict(variant=12, block=128)),
+                      (5, dict(variant=12, unroll=4)), (1, dict(variant=99))):
+        with pytest.raises(dg.DGError) as e:
+            dg.dg_gemv_q4_0(W, X, Y, N, K, M, launch=launch)
+        assert e.value.status == dg.DG_ERR_ARG, launch
 
 
 def test_q4_0_worked_blocks_tiled(dg, dev):

@@ -15,9 +15,11 @@ def _run(dg, dev, buf, nbytes, **kw):
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096 + 16, 1 << 20, (64 << 20) + 48])
-@pytest.mark.parametrize("launch", [dict(nontemporal=1), dict(nontemporal=0),
+@pytest.mark.parametrize("launch", [dict(flags=1), dict(flags=0), dict(flags=2), dict(flags=3),
                                     dict(grid_blocks=1, block_threads=64), dict(grid_blocks=7, block_threads=1024),
-                                    dict(grid_blocks=4096, block_threads=512)])
+                                    dict(grid_blocks=4096, block_threads=512, flags=3),
+                                    dict(grid_blocks=3, block_threads=192, flags=1), dict(flags=5),
+                                    dict(grid_blocks=9, block_threads=128, flags=4)])
 def test_stream_checksum_matches_oracle(dg, dev, orc, nbytes, launch):
     import torch
     g = np.random.default_rng(nbytes)
@@ -44,7 +46,7 @@ def test_stream_full_size_closed_form(dg, dev):
     n = (8 << 30) // 4
     buf = torch.arange(n, dtype=torch.int32, device=dev)    # 0 .. 2^31 - 1
     expect = (n * (n - 1) // 2) % 2**32
-    for nt in (1, 0):
-        assert _run(dg, dev, buf, n * 4, nontemporal=nt, grid_blocks=2048) == expect
+    for flags in (0, 1, 2, 3, 5):
+        assert _run(dg, dev, buf, n * 4, flags=flags) == expect
     del buf
     torch.cuda.empty_cache()
