@@ -186,7 +186,7 @@ def measure_ceiling(full_sweep=False, records=None):
         shapes += [(g, 256, 1) for g in (16384, 65536, 262144)]        # about one 8 KiB chunk per wave
         shapes += [(g, b, f) for f in (0, 3, 2) for g in (512, 1024, 2048) for b in (256, 512)]
     else:
-        shapes = [(512, 256, 1), (384, 256, 1), (256, 512, 1), (512, 256, 5), (262144, 256, 1)]
+        shapes = [(768, 64, 1), (768, 64, 5), (384, 128, 1), (512, 256, 1), (256, 512, 1)]
     best = None
     for grid, block, flags in shapes:
         def call(grid=grid, block=block, flags=flags):
@@ -214,24 +214,21 @@ FP16_N = FP16_K = 4096
 Q4_N, Q4_K = 28672, 8192
 
 
-def traffic_from_profiles(kernel_src, per_launch_key):
-    """HBM bytes per launch from the committed counter summary, only while the
-    kernel source is unchanged since the counters were taken."""
+def traffic_from_profiles(key):
+    """HBM bytes per launch from the committed counter summary (profiles/
+    counters.json), only while the kernel's sources are unchanged since the
+    counters were taken; otherwise None."""
+    from memory_bound_decode_gemv_amd import profiling
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
-            data = json.load(f)
-        ent = data.get(per_launch_key)
-        if not ent:
-            return None
-        with open(kernel_src, "rb") as f:
-            h = hashlib.sha256(f.read()).hexdigest()[:16]
-        if ent.get("source_sha256_16") != h:
+            ent = json.load(f).get(key)
+        if not ent or ent.get("source_sha256_16") != profiling.sources_hash(ent["sources"]):
             return None
         return ent.get("hbm_bytes_per_launch")
-    except Exception:
+    except (OSError, ValueError, KeyError):
         return None
 
 
@@ -316,7 +313,6 @@ def headline(args):
     ms_per_step = ms / steps
     value = (b16 + bq4) / (ms_per_step * 1e-3) / 1e9
 
-    q4_src = os.path.join(ROOT, "memory_bound_decode_gemv_amd", "csrc", "gemv_q4_0.hip")
     achieved = bq4 / (usq * 1e-6) / 1e9
     out = {
         "metric": METRIC,
@@ -346,7 +342,7 @@ def headline(args):
             "bound": "hbm", "kernel": "gemv_q4_0 M=1 28672x8192",
             "achieved": round(achieved, 1), "peak": SPEC_GBPS, "unit": "GB/s",
             "frac": round(achieved / SPEC_GBPS, 4),
-            "traffic": traffic_from_profiles(q4_src, "gemv_q4_0_m1_28672x8192"),
+            "traffic": traffic_from_profiles("gemv_q4_0_m1_28672x8192"),
             "algorithmic_bytes_per_launch": bq4,
         },
     }
@@ -371,11 +367,30 @@ def suite(args):
             with open(args.suite_out, "a") as f:
                 f.write(json.dumps(r) + "\n")
 
+    only = set(args.only.split(",")) if args.only else None
+
+    def want(section):
+        return only is None or section in only
+
     sweep = []
-    ceil_gbps, ceil_cfg, _ = measure_ceiling(full_sweep=True, records=sweep)
+    ceil_gbps, ceil_cfg, _ = measure_ceiling(full_sweep=want("ceiling"), records=sweep)
     for r in sweep:
         emit(r)
     emit({"name": "ceiling", "gbps": round(ceil_gbps, 1), **ceil_cfg})
+    if want("dense"):
+        suite_dense(dg, torch, emit, ceil_gbps)
+    if want("q4m1"):
+        suite_q4_m1(dg, torch, emit, ceil_gbps)
+    if want("q4m"):
+        suite_q4_small_m(dg, torch, emit, ceil_gbps)
+    if want("argmax"):
+        suite_argmax(dg, torch, emit, ceil_gbps)
+    if want("tail"):
+        suite_tail(dg, torch, emit, ceil_gbps)
+    return recs
+
+
+def suite_dense(dg, torch, emit, ceil_gbps):
 
     # the launch floor: a 16-byte read by one wave, back to back in a graph
     tiny = torch.zeros(64, dtype=torch.int32, device="cuda")
@@ -435,6 +450,9 @@ def suite(args):
         del Wb
         torch.cuda.empty_cache()
 
+
+
+def suite_q4_m1(dg, torch, emit, ceil_gbps):
     # Q4_0 M = 1 at the 70B MLP shape, default and variants
     nq = copies_for(18 * Q4_N * Q4_K // 32)
     Wq = q4_copies(2, Q4_N, Q4_K, nq)
@@ -454,6 +472,9 @@ def suite(args):
     del Wq
     torch.cuda.empty_cache()
 
+
+
+def suite_q4_small_m(dg, torch, emit, ceil_gbps):
     # Q4_0 small-M sweep over the four 8B shapes
     for (N, K) in [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)]:
         nc = copies_for(18 * N * K // 32)
@@ -469,9 +490,22 @@ def suite(args):
             prev = cps
             emit(record(f"gemv_q4_0 {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M, copies=nc,
                         columns_per_s=round(cps, 1), change_vs_prev_M=dip))
+            if M in (2, 8, 16, 24):
+                for unroll in (116, 216, 416, 132, 232, 432):
+                    if unroll == 432 and M > 16:
+                        continue
+                    launch = dict(variant=14, unroll=unroll)
+                    calls = [(lambda c=c: dg.dg_gemv_q4_0(Wq[c % nc], Xq, Y, N, K, M, launch=launch))
+                             for c in range(max(nc, 20))]
+                    us, iqr = time_per_call(calls)
+                    emit(record(f"gemv_q4_0 {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M, copies=nc,
+                                variant="mfma", CB=unroll % 100, KS=unroll // 100))
         del Wq
         torch.cuda.empty_cache()
 
+
+
+def suite_argmax(dg, torch, emit, ceil_gbps):
     # argmax: hot (one buffer) and cold (rotated copies for the 256 MB shape)
     import synth
     for (R, C) in [(1, 128000), (32, 128000), (64, 1000000), (1, 128256)]:
@@ -490,6 +524,9 @@ def suite(args):
         del xs
         torch.cuda.empty_cache()
 
+
+
+def suite_tail(dg, torch, emit, ceil_gbps):
     # the greedy tail: lm-head bf16 GEMV -> fp32 logits -> argmax
     N, K = 128256, 4096
     nc = copies_for(2 * N * K)
@@ -504,7 +541,37 @@ def suite(args):
     us, iqr = time_per_call(calls)
     emit(record("greedy tail lm-head 128256x4096 + argmax", 2 * us, 2 * iqr,
                 bytes_dense(N, K, 4) + 4 * N + 8, ceil_gbps, note="us per token (two launches)"))
-    return recs
+
+
+def profile_kernels(args):
+    """Launches each profiled kernel eagerly (one dispatch each) on known
+    workloads, for rocprofv3 counter runs: the Q4_0 M=1 decode GEMV at
+    28672x8192, the fp16 GEMV at 4096x4096, the streaming read of 1 GiB, and a
+    plain 1 GiB device-to-device copy whose FETCH_SIZE / WRITE_SIZE calibrate
+    the counters (known bytes read and written)."""
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    nq = copies_for(18 * Q4_N * Q4_K // 32)
+    Wq = q4_copies(2, Q4_N, Q4_K, nq)
+    Xq = q8_columns(2, Q4_K, 1)
+    Yq = torch.empty(Q4_N, dtype=torch.float32, device="cuda")
+    n16 = copies_for(2 * FP16_N * FP16_K)
+    W16, x16 = dense_copies(0, FP16_N, FP16_K, n16, torch.float16)
+    y16 = torch.empty(FP16_N, dtype=torch.float16, device="cuda")
+    src = torch.empty(GIB // 4, dtype=torch.int32, device="cuda").fill_(3)
+    dst = torch.empty_like(src)
+    cs = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    for c in range(2 * nq):
+        dg.dg_gemv_q4_0(Wq[c % nq], Xq, Yq, Q4_N, Q4_K, 1)
+    for c in range(n16):
+        dg.dg_gemv_f16(W16[c], x16, y16)
+    for _ in range(4):
+        dg.dg_stream_read(src, cs, grid_blocks=768, block_threads=64, flags=dg.DG_READ_NONTEMPORAL)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[profile-kernels] q4_0 x{2 * nq}, f16 x{n16}, stream_read 1 GiB x4, copy 1 GiB x4")
 
 
 def main():
@@ -514,6 +581,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--suite", action="store_true", help="measure every configuration instead")
     ap.add_argument("--suite-out", default=None, help="append suite records (JSON lines) to this file")
+    ap.add_argument("--profile-kernels", action="store_true",
+                    help="launch each profiled kernel eagerly on known workloads (for rocprofv3 --pmc)")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated suite sections: ceiling,dense,q4m1,q4m,argmax,tail")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     args = ap.parse_args()
@@ -526,7 +597,9 @@ def main():
         ap.error("--steps must be >= 1 and --warmup >= 0")
     import memory_bound_decode_gemv_amd as dg
     dg.raw()
-    if args.suite:
+    if args.profile_kernels:
+        profile_kernels(args)
+    elif args.suite:
         suite(args)
     else:
         headline(args)

@@ -216,7 +216,8 @@ enum {
     /* Q4_0 */
     DG_VARIANT_Q4_REGS = 11,        /* activations in registers, one row per wave (M = 1)       */
     DG_VARIANT_Q4_LDS = 12,         /* activations staged in LDS, several rows per wave          */
-    DG_VARIANT_Q4_LDSROW = 13       /* M = 1: weight rows copied to LDS with coalesced loads     */
+    DG_VARIANT_Q4_LDSROW = 13,      /* M = 1: weight rows copied to LDS with coalesced loads     */
+    DG_VARIANT_Q4_MFMA = 14         /* int8 matrix cores, 16 rows x 16 columns per instruction   */
 };
 
 dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K,

@@ -36,6 +36,7 @@ DG_VARIANT_DENSE_NARROW4 = 4
 DG_VARIANT_Q4_REGS = 11
 DG_VARIANT_Q4_LDS = 12
 DG_VARIANT_Q4_LDSROW = 13
+DG_VARIANT_Q4_MFMA = 14
 
 # Every symbol include/decodegemv.h declares.
 EXPORTED = (

@@ -21,102 +21,13 @@
 // into v_dot4_i32_i8 against the signed activation codes, and the -8 offset
 // enters as the initial accumulator -8 * sum(q8), computed exactly once per
 // activation block.  The int32 block sum is then scaled by d4 * d8 in fp32.
-#include "dg_device.h"
 #include "dg_internal.h"
+#include "q4_common.h"
 
 namespace dg {
 namespace {
 
-constexpr uint32_t kNib = 0x0F0F0F0Fu;
-constexpr int kPairBytes = 36;   // two Q4_0 blocks
-constexpr int kQ81Bytes = 36;    // one Q8_1 block
-
-// One column's activations for one block pair: codes of block a and block b
-// (element 4i..4i+3 in dword i), scales as fp32, and c = -8 * sum(q8).
-struct ActPair {
-    uint32_t qa[8];
-    uint32_t qb[8];
-    float da, db;
-    int ca, cb;
-};
-
-__device__ __forceinline__ int block_code_sum(const uint32_t* q) {
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s = dot4_i8(q[i], 0x01010101u, s);
-    return s;
-}
-
-// Reads the Q8_1 blocks 2p and 2p+1 of a column (72 bytes, 8-byte aligned
-// when the column start is) from global memory.
-__device__ __forceinline__ void load_act_pair(const uint8_t* col, int p, ActPair& a) {
-    const uint32_t* b = reinterpret_cast<const uint32_t*>(col + (size_t)p * (2 * kQ81Bytes));
-    uint32_t v[18];
-#pragma unroll
-    for (int i = 0; i < 18; ++i) v[i] = b[i];
-    a.da = half_lo_to_f32(v[0]);
-    a.db = half_lo_to_f32(v[9]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        a.qa[i] = v[1 + i];
-        a.qb[i] = v[10 + i];
-    }
-    a.ca = -8 * block_code_sum(a.qa);
-    a.cb = -8 * block_code_sum(a.qb);
-}
-
-// Loads the 9 dwords of block pair p of a weight row (non-temporal).
-__device__ __forceinline__ void load_weight_pair(const uint8_t* row, int p, uint32_t w[9]) {
-    const uint32_t* b = reinterpret_cast<const uint32_t*>(row + (size_t)p * kPairBytes);
-    const u32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(b));
-    const u32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(b + 4));
-    w[0] = lo.x; w[1] = lo.y; w[2] = lo.z; w[3] = lo.w;
-    w[4] = hi.x; w[5] = hi.y; w[6] = hi.z; w[7] = hi.w;
-    w[8] = __builtin_nontemporal_load(b + 8);
-}
-
-// The unpacked codes of one weight pair: lo[i]/hi[i] of block a in 0..3,
-// block b in 4..7, and the two scales.
-struct WeightPair {
-    uint32_t lo[8];
-    uint32_t hi[8];
-    float d4a, d4b;
-};
-
-__device__ __forceinline__ void unpack_weight_pair(const uint32_t w[9], WeightPair& u) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // block a: scale in bytes 0-1, codes in bytes 2..17 (straddling dwords)
-        const uint32_t ca = __builtin_amdgcn_alignbit(w[i + 1], w[i], 16);
-        u.lo[i] = ca & kNib;
-        u.hi[i] = (ca >> 4) & kNib;
-        // block b: scale in bytes 18-19, codes in bytes 20..35 (dwords 5..8)
-        const uint32_t cb = w[5 + i];
-        u.lo[4 + i] = cb & kNib;
-        u.hi[4 + i] = (cb >> 4) & kNib;
-    }
-    u.d4a = half_lo_to_f32(w[0]);
-    u.d4b = half_hi_to_f32(w[4]);
-}
-
-__device__ __forceinline__ float pair_dot(const WeightPair& u, const uint32_t* qa, const uint32_t* qb,
-                                          float da, float db, int ca, int cb, float acc) {
-    int sa = ca, sb = cb;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        sa = dot4_i8(u.lo[i], qa[i], sa);       // weights 4i..4i+3
-        sa = dot4_i8(u.hi[i], qa[4 + i], sa);   // weights 16+4i..16+4i+3
-        sb = dot4_i8(u.lo[4 + i], qb[i], sb);
-        sb = dot4_i8(u.hi[4 + i], qb[4 + i], sb);
-    }
-    acc = fmaf((float)sa, u.d4a * da, acc);
-    acc = fmaf((float)sb, u.d4b * db, acc);
-    return acc;
-}
-
-__device__ __forceinline__ int wave_in_block() {
-    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-}
+using namespace q4;
 
 // ---------------------------------------------------------------------------
 // M = 1: the lane's activation pairs stay in registers for every row the wave
@@ -188,139 +99,6 @@ k_q4_m1_regs(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
 #pragma unroll
             for (int i = 0; i < 9; ++i) w[s][i] = wn[s][i];
         row = next;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// M = 1 with coalesced weight loads through LDS.  A packed Q4_0 row is a
-// contiguous, 16-byte aligned run of 18-byte blocks; read 16 bytes per lane at
-// a 36-byte lane stride (the block pairs), every cache line is touched by
-// three separate load instructions.  Here the wave instead copies the row
-// into its own LDS buffer with global_load_lds_dwordx4 (64 lanes x 16 B = one
-// contiguous KiB per instruction, straight into LDS without passing through
-// VGPRs; non-temporal), then each lane reads its block pairs back with
-// ds_read2_b32 at a 9-dword lane stride (9 is odd: no bank conflicts).  DEPTH
-// row buffers per wave keep DEPTH - 1 rows in flight while one is computed.
-//
-// The compiler does not track these LDS writes, so the waits are explicit.
-// Loads complete in issue order, and each of the C loads of a row has at least
-// one active lane; so once the wave has issued the loads of q further rows
-// after row r, "at most q*C vector-memory operations outstanding" implies that
-// row r has arrived (stores only make the wait longer).  C = ceil(row bytes /
-// 1 KiB) is a template parameter because the wait count is an immediate.
-// ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-constexpr int kAuxNonTemporal = 2;   // cache-policy operand of global_load_lds: nt
-
-template <int C>
-__device__ __forceinline__ void copy_row_to_lds(const uint8_t* __restrict__ row, uint8_t* buf, int nchunks,
-                                                int lane) {
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-        const int c = j * kWave + lane;
-        if (c < nchunks)
-            __builtin_amdgcn_global_load_lds(row + (size_t)c * 16, (lds_void_t*)(buf + j * 1024), 16, 0,
-                                             kAuxNonTemporal);
-    }
-}
-
-template <int N_OUTSTANDING>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N_OUTSTANDING >= 0 && N_OUTSTANDING <= 31, "wait count out of range");
-#define DG_WAIT(n) if constexpr (N_OUTSTANDING == n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory");
-    DG_WAIT(0) DG_WAIT(1) DG_WAIT(2) DG_WAIT(3) DG_WAIT(4) DG_WAIT(5) DG_WAIT(6) DG_WAIT(7)
-    DG_WAIT(8) DG_WAIT(9) DG_WAIT(10) DG_WAIT(11) DG_WAIT(12) DG_WAIT(13) DG_WAIT(14) DG_WAIT(15)
-    DG_WAIT(16) DG_WAIT(17) DG_WAIT(18) DG_WAIT(19) DG_WAIT(20) DG_WAIT(21) DG_WAIT(22) DG_WAIT(23)
-    DG_WAIT(24) DG_WAIT(25) DG_WAIT(26) DG_WAIT(27) DG_WAIT(28) DG_WAIT(29) DG_WAIT(30) DG_WAIT(31)
-#undef DG_WAIT
-}
-
-// Waits until at most q*C vector-memory operations are outstanding (q < DEPTH).
-template <int C, int DEPTH>
-__device__ __forceinline__ void wait_rows_ahead(int q) {
-    if (q == 0) wait_vmcnt<0>();
-    else if (DEPTH > 2 && q == 1) wait_vmcnt<C>();
-    else if (DEPTH > 3 && q == 2) wait_vmcnt<(DEPTH > 3 ? 2 * C : 0)>();
-    else wait_vmcnt<(DEPTH - 1) * C>();
-}
-
-__device__ __forceinline__ void read_pair_lds(const uint8_t* buf, int p, uint32_t w[9]) {
-    const uint32_t* b = reinterpret_cast<const uint32_t*>(buf + (size_t)p * kPairBytes);
-#pragma unroll
-    for (int i = 0; i < 9; ++i) w[i] = b[i];
-}
-
-template <int S, int C, int DEPTH>
-__global__ void __launch_bounds__(256)
-k_q4_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
-               float* __restrict__ Y, int N, int K) {
-    static_assert(DEPTH >= 2 && DEPTH <= 4, "pipeline depth");
-    extern __shared__ u32x4 lds_rows[];
-    const int lane = lane_id();
-    const int wave = wave_in_block();
-    const int wpb = blockDim.x / kWave;
-    const int npairs = K >> 6;
-    const int row_bytes = (K >> 5) * 18;
-    const int nchunks = row_bytes >> 4;
-    const int rstride = gridDim.x * wpb;
-    const int row0 = blockIdx.x * wpb + wave;
-    if (row0 >= N) return;
-    // Byte offset of the wave's buffers; addresses are always formed from the
-    // __shared__ array itself, so that they stay LDS addresses (ds_read) rather
-    // than generic ones (flat_load).
-    const int buf_off = wave * DEPTH * row_bytes;
-    uint8_t* const lds_base = reinterpret_cast<uint8_t*>(lds_rows) + buf_off;
-
-    // rows row0 + i*rstride for i = 0, 1, ...; the first DEPTH - 1 are requested now
-#pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d) {
-        const int r = row0 + d * rstride;
-        if (r < N) copy_row_to_lds<C>(Wq + (size_t)r * row_bytes, lds_base + d * row_bytes, nchunks, lane);
-    }
-
-    int pc[S];
-    ActPair act[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int p = s * kWave + lane;
-        pc[s] = p < npairs ? p : npairs - 1;
-        load_act_pair(Xq, pc[s], act[s]);
-        if (p >= npairs) {   // lanes past the end of the row contribute exactly 0
-            act[s].da = 0.0f;
-            act[s].db = 0.0f;
-            act[s].ca = 0;
-            act[s].cb = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) { act[s].qa[i] = 0; act[s].qb[i] = 0; }
-        }
-    }
-
-    int slot = 0;   // buffer of the current row
-    for (int row = row0; row < N; row += rstride) {
-        const int ahead = row + (DEPTH - 1) * rstride;
-        if (ahead < N) {
-            int aslot = slot + DEPTH - 1;
-            if (aslot >= DEPTH) aslot -= DEPTH;
-            copy_row_to_lds<C>(Wq + (size_t)ahead * row_bytes, lds_base + aslot * row_bytes, nchunks, lane);
-        }
-        // rows requested after this one: min(DEPTH - 1, rows left after it)
-        const int left = __builtin_amdgcn_readfirstlane((N - 1 - row) / rstride);   // wave-uniform
-        wait_rows_ahead<C, DEPTH>(left < DEPTH - 1 ? left : DEPTH - 1);
-
-        const uint8_t* rowbuf = lds_base + slot * row_bytes;
-        float acc = 0.0f;
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-            uint32_t w[9];
-            read_pair_lds(rowbuf, pc[s], w);
-            WeightPair u;
-            unpack_weight_pair(w, u);
-            acc = pair_dot(u, act[s].qa, act[s].qb, act[s].da, act[s].db, act[s].ca, act[s].cb, acc);
-        }
-        acc = wave_sum_f32(acc);
-        if (lane == 0) Y[row] = acc;
-        slot = slot + 1 == DEPTH ? 0 : slot + 1;
     }
 }
 
@@ -461,29 +239,6 @@ hipError_t launch_lds(int M, int R, const void* Wq, const void* Xq, float* Y, in
     }
 }
 
-hipError_t launch_ldsrow(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid, int block,
-                         hipStream_t s) {
-    const uint8_t* w = (const uint8_t*)Wq;
-    const uint8_t* x = (const uint8_t*)Xq;
-    const size_t row_bytes = (size_t)(K / 32) * 18;
-    const size_t lds = (size_t)(block / kWave) * depth * row_bytes;
-    if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
-    const int C = (int)((row_bytes + 1023) / 1024);
-    const int S = (K / 64 + kWave - 1) / kWave;
-#define DG_SCD(SS, CC, DD)                                                                              \
-    else if (S == SS && C == CC && depth == DD)                                                         \
-        hipLaunchKernelGGL((k_q4_m1_ldsrow<SS, CC, DD>), dim3(grid), dim3(block), lds, s, w, x, Y, N, K);
-#define DG_SC(SS, CC) DG_SCD(SS, CC, 2) DG_SCD(SS, CC, 3) DG_SCD(SS, CC, 4)
-    if (false) {
-    }
-    DG_SC(1, 1) DG_SC(1, 2) DG_SC(1, 3) DG_SC(2, 3) DG_SC(2, 4) DG_SC(2, 5) DG_SC(3, 5) DG_SC(3, 6) DG_SC(3, 7)
-    DG_SC(4, 7) DG_SC(4, 8) DG_SC(4, 9)
-    else return hipErrorInvalidValue;
-#undef DG_SC
-#undef DG_SCD
-    return hipGetLastError();
-}
-
 hipError_t launch_regs(int S, const void* Wq, const void* Xq, float* Y, int N, int K, int grid, int block,
                        hipStream_t s) {
     const uint8_t* w = (const uint8_t*)Wq;
@@ -504,7 +259,7 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
     const int npairs = K / 64;
     const int S = (npairs + kWave - 1) / kWave;
     int variant = cfg && cfg->variant ? cfg->variant : 0;
-    if (variant == 0) variant = (M == 1 && S <= 4) ? DG_VARIANT_Q4_LDSROW : DG_VARIANT_Q4_LDS;
+    if (variant == 0) variant = M == 1 ? (S <= 4 ? DG_VARIANT_Q4_LDSROW : DG_VARIANT_Q4_LDS) : DG_VARIANT_Q4_MFMA;
 
     if (variant == DG_VARIANT_Q4_REGS) {
         const int block = cfg && cfg->block ? cfg->block : 256;
@@ -514,15 +269,13 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
         return launch_regs(S, Wq, Xq, Y, N, K, grid, block, s);
     }
     if (variant == DG_VARIANT_Q4_LDSROW) {
-        const int block = cfg && cfg->block ? cfg->block : 256;
-        if (M != 1 || block > 256) return hipErrorInvalidValue;             // compiled for <= 256 threads
-        // Measured on MI355X at 28672 x 8192: two row buffers per wave and at
-        // most 2048 workgroups of four waves (a few rows per wave) read fastest.
-        const int depth = cfg && cfg->unroll ? cfg->unroll : 2;
-        const int wpb = block / kWave;
-        const int rows_grid = (N + wpb - 1) / wpb;
-        const int grid = cfg && cfg->grid ? cfg->grid : (rows_grid < 2048 ? rows_grid : 2048);
-        return launch_ldsrow(K, depth, Wq, Xq, Y, N, grid, block, s);
+        if (M != 1) return hipErrorInvalidValue;
+        return launch_q4_m1_ldsrow(K, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, cfg ? cfg->grid : 0,
+                                   cfg ? cfg->block : 0, s);
+    }
+    if (variant == DG_VARIANT_Q4_MFMA) {
+        if (cfg && cfg->block && cfg->block != 256) return hipErrorInvalidValue;
+        return launch_q4_mfma(M, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, K, cfg ? cfg->grid : 0, s);
     }
     if (variant == DG_VARIANT_Q4_LDS) {
         if (cfg && cfg->block && cfg->block != kLdsBlock) return hipErrorInvalidValue;

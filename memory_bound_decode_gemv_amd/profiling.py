@@ -1,0 +1,192 @@
+"""Summaries of rocprofv3 runs for the profiles/ directory (host-side, reads CSVs).
+
+Counters: two `rocprofv3 --pmc` runs (FETCH_SIZE, then WRITE_SIZE) of
+`bench.py --profile-kernels`, which launches each kernel eagerly on a known
+workload next to a plain 1 GiB device-to-device copy.  The copy's counters
+calibrate the others: on MI355X FETCH_SIZE reads about half the bytes a
+kernel actually fetches while WRITE_SIZE reads them exactly, so each counter
+is scaled by (bytes the copy moved) / (what the counter read for it).  The
+HBM traffic per launch of a kernel is then
+    FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale     (KiB * 1024).
+Each entry records a hash of the kernel's source files; bench.py reports the
+traffic only while that hash still matches the tree.
+
+    python -m memory_bound_decode_gemv_amd.profiling counters FETCH.csv WRITE.csv
+    python -m memory_bound_decode_gemv_amd.profiling trace KERNEL_STATS.csv --md OUT.md
+    python -m memory_bound_decode_gemv_amd.profiling suite SUITE.jsonl --md OUT.md
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+GIB = 1 << 30
+
+# Profiled kernels: key -> (kernel-name pattern, workload, algorithmic bytes per launch, sources)
+KERNELS = {
+    "gemv_q4_0_m1_28672x8192": (
+        r"k_q4_m1_ldsrow<", "Q4_0 x Q8_1, M = 1, N = 28672, K = 8192",
+        18 * 28672 * 8192 // 32 + 36 * 8192 // 32 + 4 * 28672,
+        ["gemv_q4_0_m1.hip", "q4_common.h", "dg_device.h"]),
+    "gemv_f16_4096x4096": (
+        r"k_gemv_wide<false", "fp16 GEMV, N = K = 4096",
+        2 * 4096 * 4096 + 2 * 4096 + 2 * 4096,
+        ["gemv_dense.hip", "dg_device.h"]),
+    "stream_read_1GiB": (
+        r"k_stream_read_wave<", "streaming read of 1 GiB", GIB,
+        ["stream_read.hip", "dg_device.h"]),
+}
+CALIBRATION = (r"__amd_rocclr_copyBuffer", GIB)   # the 1 GiB copy: GIB read, GIB written
+
+
+def sources_hash(files) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    n = name.replace("dg::(anonymous namespace)::", "")
+    return re.sub(r"\((unsigned|float|int|long|void|short)[^)]*\)$", "", n)[:80]
+
+
+def load_counter_csv(path):
+    d = collections.defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            d[(row["Kernel_Name"], row["Counter_Name"])].append(float(row["Counter_Value"]))
+    return d
+
+
+def _values(d, pattern, counter):
+    out = []
+    for (name, c), v in d.items():
+        if c == counter and re.search(pattern, name):
+            out.extend(v)
+    return out
+
+
+def counters_summary(fetch_csv, write_csv):
+    fetch = load_counter_csv(fetch_csv)
+    write = load_counter_csv(write_csv)
+    cal_pat, cal_bytes = CALIBRATION
+    cal_f = max(_values(fetch, cal_pat, "FETCH_SIZE"))
+    cal_w = max(_values(write, cal_pat, "WRITE_SIZE"))
+    fs = cal_bytes / (cal_f * 1024)
+    ws = cal_bytes / (cal_w * 1024)
+    out = {"calibration": {"kernel": "1 GiB device-to-device copy", "bytes": cal_bytes,
+                           "fetch_kib": cal_f, "write_kib": cal_w,
+                           "fetch_scale": round(fs, 5), "write_scale": round(ws, 5)}}
+    for key, (pat, what, alg, files) in KERNELS.items():
+        fv = _values(fetch, pat, "FETCH_SIZE")
+        wv = _values(write, pat, "WRITE_SIZE")
+        if not fv or not wv:
+            continue
+        f_kib = sum(fv) / len(fv)
+        w_kib = sum(wv) / len(wv)
+        traffic = int(round((f_kib * fs + w_kib * ws) * 1024))
+        out[key] = {"workload": what, "dispatches": len(fv), "fetch_kib": round(f_kib, 2),
+                    "write_kib": round(w_kib, 2), "hbm_bytes_per_launch": traffic,
+                    "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4),
+                    "sources": files, "source_sha256_16": sources_hash(files)}
+    return out
+
+
+def counters_markdown(summary, command_fetch, command_write):
+    lines = ["# HBM traffic per launch from rocprofv3 counters", "",
+             "Commands (run from /tmp on the MI355X box, repository at $R):", "",
+             f"    {command_fetch}", f"    {command_write}", "",
+             "Calibration: " + json.dumps(summary["calibration"]), "",
+             "| kernel | workload | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch "
+             "| algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|"]
+    for k, v in summary.items():
+        if k == "calibration":
+            continue
+        lines.append(f"| {k} | {v['workload']} | {v['dispatches']} | {v['fetch_kib']} | {v['write_kib']} | "
+                     f"{v['hbm_bytes_per_launch']} | {v['algorithmic_bytes_per_launch']} | "
+                     f"{v['traffic_over_algorithmic']} |")
+    return "\n".join(lines) + "\n"
+
+
+def trace_markdown(stats_csv, command):
+    lines = ["# Kernel durations from rocprofv3 --kernel-trace --stats", "", "Command:", "", f"    {command}", "",
+             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    with open(stats_csv) as f:
+        for row in csv.DictReader(f):
+            if "dg::" not in row["Name"]:
+                continue
+            lines.append(f"| {short_name(row['Name'])} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.3f} | "
+                         f"{float(row['MinNs']) / 1e3:.3f} | {float(row['MaxNs']) / 1e3:.3f} | "
+                         f"{float(row['Percentage']):.2f} |")
+    return "\n".join(lines) + "\n"
+
+
+def suite_markdown(jsonl, command, name_filter=None):
+    """A table of `bench.py --suite` records (one JSON object per line)."""
+    recs = []
+    with open(jsonl) as f:
+        for line in f:
+            r = json.loads(line)
+            if name_filter and not re.search(name_filter, r.get("name", "")):
+                continue
+            recs.append(r)
+    keys = ("name", "us_per_call", "iqr_us", "gbps", "mbu_ceiling", "mbu_spec")
+    extra = sorted({k for r in recs for k in r} - set(keys) - {"bytes"})
+    lines = ["# bench.py --suite records", "", "Command:", "", f"    {command}", "",
+             "| " + " | ".join(keys + tuple(extra)) + " |", "|" + "---|" * (len(keys) + len(extra))]
+    for r in recs:
+        lines.append("| " + " | ".join(str(r.get(k, "")) for k in keys + tuple(extra)) + " |")
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("fetch_csv")
+    c.add_argument("write_csv")
+    c.add_argument("--json", default=os.path.join(PROFILES, "counters.json"))
+    c.add_argument("--md", default=os.path.join(PROFILES, "hbm_traffic_counters.md"))
+    c.add_argument("--command-fetch", default="")
+    c.add_argument("--command-write", default="")
+    q = sub.add_parser("suite")
+    q.add_argument("jsonl")
+    q.add_argument("--md", required=True)
+    q.add_argument("--command", default="")
+    q.add_argument("--filter", default=None)
+    t = sub.add_parser("trace")
+    t.add_argument("stats_csv")
+    t.add_argument("--md", required=True)
+    t.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        s = counters_summary(a.fetch_csv, a.write_csv)
+        with open(a.json, "w") as f:
+            json.dump(s, f, indent=1)
+            f.write("\n")
+        with open(a.md, "w") as f:
+            f.write(counters_markdown(s, a.command_fetch, a.command_write))
+        print(json.dumps(s, indent=1))
+    elif a.cmd == "suite":
+        with open(a.md, "w") as f:
+            f.write(suite_markdown(a.jsonl, a.command, a.filter))
+    else:
+        with open(a.md, "w") as f:
+            f.write(trace_markdown(a.stats_csv, a.command))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

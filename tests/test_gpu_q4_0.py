@@ -90,6 +90,20 @@ def test_q4_0_lds_row_copy_shapes(dg, dev, orc, N, K, launch):
     assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"{N}x{K} {launch}")
 
 
+MFMA_CFGS = [dict(variant=14)] + [dict(variant=14, unroll=cb + 100 * ks) for cb in (16, 32) for ks in (1, 2, 4)]
+
+
+@pytest.mark.parametrize("launch", MFMA_CFGS, ids=[str(v) for v in MFMA_CFGS])
+@pytest.mark.parametrize("N,K,M", [(37, 256, 2), (130, 4352, 7), (64, 8192, 16), (200, 2304, 17), (33, 12544, 24),
+                                   (16, 512, 3), (1, 1024, 24), (700, 4096, 12)])
+def test_q4_0_mfma_matches_oracle(dg, dev, orc, launch, N, K, M):
+    if launch.get("unroll") == 432 and M > 16:
+        pytest.skip("32-block chunks with four K parts and two column tiles exceed the LDS of one workgroup")
+    Wq, Xq = _operands(orc, 260, N, K, M)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
+    assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M), TOL, f"mfma {launch} {N}x{K} M={M}")
+
+
 @pytest.mark.parametrize("M,R", [(2, 1), (2, 2), (3, 4), (8, 1), (8, 2), (24, 1), (24, 2)])
 def test_q4_0_lds_rows_per_wave(dg, dev, orc, M, R):
     N, K = 77, 4608
