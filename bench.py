@@ -179,7 +179,7 @@ def measure_ceiling(full_sweep=False, records=None):
     nbytes = 8 * GIB
     buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
     buf.fill_(1)
-    cs = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cs = torch.zeros(1 << 18, dtype=torch.int32, device="cuda")     # one partial per workgroup
     if full_sweep:
         shapes = [(g, b, f) for f in (1, 5) for g in (128, 256, 384, 512, 768, 1024, 2048)
                   for b in (64, 128, 256, 512)]
@@ -204,6 +204,34 @@ def measure_ceiling(full_sweep=False, records=None):
     torch.cuda.empty_cache()
     log(f"[ceiling] {best[0]:.1f} GB/s at {best[1]} ({best[2]:.1f} us per 8 GiB read)")
     return best
+
+
+READ_PROBE_SHAPES = [(g, b, f) for f in (1, 5) for g in (256, 512, 1024, 2048) for b in (256, 512)]
+
+
+def read_probe(bufs, shapes=READ_PROBE_SHAPES, records=None, label=""):
+    """The best per-launch time of the streaming-read probe over the same rotated
+    buffers a GEMV reads (back-to-back launches in a graph, like the GEMV's own
+    timing): the fastest a kernel that only reads those bytes runs, launch and
+    ramp costs included."""
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    cs = torch.zeros(max(g for g, _, _ in shapes), dtype=torch.int32, device="cuda")
+    n = len(bufs)
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+    best = None
+    for grid, block, flags in shapes:
+        calls = [(lambda c=c, g=grid, b=block, f=flags: dg.dg_stream_read(bufs[c % n], cs, grid_blocks=g,
+                                                                           block_threads=b, flags=f))
+                 for c in range(max(20, n))]
+        us, iqr = time_per_call(calls)
+        cfg = dict(grid=grid, block=block, nontemporal=flags & 1, loads_per_lane=16 if flags & 4 else 8)
+        if records is not None:
+            records.append(record(f"stream_read {label}", us, iqr, nbytes, None, **cfg))
+        if best is None or us < best[0]:
+            best = (us, cfg)
+    return {"us_per_call": round(best[0], 3), "bytes": nbytes,
+            "gbps": round(nbytes / (best[0] * 1e-6) / 1e9, 1), **best[1]}
 
 
 # ---------------------------------------------------------------------------
@@ -288,6 +316,9 @@ def headline(args):
     usq, iqrq = time_per_call([q4_call(i) for i in range(max(20, 3 * nq))])
     log(f"[fp16 4096x4096] {us16:.2f} us/call, {b16 / us16 / 1e3:.0f} GB/s")
     log(f"[q4_0 28672x8192] {usq:.2f} us/call, {bq4 / usq / 1e3:.0f} GB/s")
+    rp16 = read_probe(W16)
+    rpq = read_probe(Wq)
+    log(f"[read probe, same bytes] fp16 weights {rp16['us_per_call']} us; q4_0 weights {rpq['us_per_call']} us")
 
     # the timed steps: exactly --steps steps in one graph, after --warmup steps
     steps, warm = args.steps, args.warmup
@@ -335,8 +366,10 @@ def headline(args):
         },
         "ceiling": {"gbps": round(ceil_gbps, 1), **ceil_cfg, "buffer_bytes": 8 * GIB},
         "breakdown": {
-            "gemv_f16_4096x4096": record("gemv_f16", us16, iqr16, b16, ceil_gbps),
-            "gemv_q4_0_28672x8192_m1": record("gemv_q4_0", usq, iqrq, bq4, ceil_gbps),
+            "gemv_f16_4096x4096": record("gemv_f16", us16, iqr16, b16, ceil_gbps, read_probe_same_weights=rp16,
+                                         read_probe_over_gemv=round(rp16["us_per_call"] / us16, 4)),
+            "gemv_q4_0_28672x8192_m1": record("gemv_q4_0", usq, iqrq, bq4, ceil_gbps, read_probe_same_weights=rpq,
+                                              read_probe_over_gemv=round(rpq["us_per_call"] / usq, 4)),
         },
         "roofline": {
             "bound": "hbm", "kernel": "gemv_q4_0 M=1 28672x8192",
@@ -377,6 +410,8 @@ def suite(args):
     for r in sweep:
         emit(r)
     emit({"name": "ceiling", "gbps": round(ceil_gbps, 1), **ceil_cfg})
+    if want("readsize"):
+        suite_read_sizes(dg, torch, emit)
     if want("dense"):
         suite_dense(dg, torch, emit, ceil_gbps)
     if want("q4m1"):
@@ -388,6 +423,25 @@ def suite(args):
     if want("tail"):
         suite_tail(dg, torch, emit, ceil_gbps)
     return recs
+
+
+def suite_read_sizes(dg, torch, emit):
+    """The streaming-read probe at the working-set sizes of single GEMVs (rotated
+    copies filling 4 x the last-level cache), over a wider launch sweep."""
+    shapes = [(g, b, f) for f in (1, 5) for g in (128, 256, 384, 512, 768, 1024, 2048, 4096)
+              for b in (64, 128, 256, 512)]
+    for nbytes in (2 * 1024 * 4096, 2 * 4096 * 4096, 18 * Q4_N * Q4_K // 32, 2 * 14336 * 4096):
+        n = copies_for(nbytes)
+        big = torch.ones(n * nbytes // 4, dtype=torch.int32, device="cuda")
+        bufs = [big[c * nbytes // 4:(c + 1) * nbytes // 4] for c in range(n)]
+        recs = []
+        best = read_probe(bufs, shapes=shapes, records=recs, label=f"{nbytes} B x {n} copies")
+        for r in recs:
+            emit(r)
+        emit({"name": f"read probe best {nbytes} B", **best})
+        del bufs, big
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
 
 
 def suite_dense(dg, torch, emit, ceil_gbps):
@@ -474,7 +528,14 @@ def suite_q4_m1(dg, torch, emit, ceil_gbps):
 
 
 
-def suite_q4_small_m(dg, torch, emit, ceil_gbps):
+# matrix-core configurations (RT, KS, DEPTH, CB) -> the largest column count they serve;
+# launch override unroll = RT*10000 + KS*100 + DEPTH*10 + CB/8
+MFMA_BUILT = {(1, 16, 1, 8): 16, (4, 4, 2, 8): 8, (1, 8, 2, 8): 16,
+              (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (2, 4, 2, 8): 24, (4, 2, 2, 8): 24, (8, 1, 2, 8): 24,
+              (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24, (1, 4, 2, 8): 24}
+
+
+def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
     # Q4_0 small-M sweep over the four 8B shapes
     for (N, K) in [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)]:
         nc = copies_for(18 * N * K // 32)
@@ -489,17 +550,21 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps):
             dip = None if prev is None else round(cps / prev - 1.0, 4)
             prev = cps
             emit(record(f"gemv_q4_0 {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M, copies=nc,
-                        columns_per_s=round(cps, 1), change_vs_prev_M=dip))
-            if M in (2, 8, 16, 24):
-                for unroll in (116, 216, 416, 132, 232, 432):
-                    if unroll == 432 and M > 16:
-                        continue
-                    launch = dict(variant=14, unroll=unroll)
-                    calls = [(lambda c=c: dg.dg_gemv_q4_0(Wq[c % nc], Xq, Y, N, K, M, launch=launch))
+                        variant="default", columns_per_s=round(cps, 1), change_vs_prev_M=dip))
+            if M in (2, 4, 8, 12, 16, 24) and sweep:
+                launches = [(dict(variant=14, unroll=rt * 10000 + ks * 100 + d * 10 + cb // 8),
+                             dict(variant="mfma", RT=rt, KS=ks, DEPTH=d, CB=cb))
+                            for (rt, ks, d, cb), mmax in MFMA_BUILT.items() if M <= mmax]
+                launches += [(dict(variant=12, unroll=r), dict(variant="dot4-lds", R=r)) for r in (1, 2, 4)]
+                for launch, tag in launches:
+                    calls = [(lambda c=c, launch=launch: dg.dg_gemv_q4_0(Wq[c % nc], Xq, Y, N, K, M, launch=launch))
                              for c in range(max(nc, 20))]
+                    try:
+                        calls[0]()
+                    except dg.DGError:   # an ablation variant that does not take this column count
+                        continue
                     us, iqr = time_per_call(calls)
-                    emit(record(f"gemv_q4_0 {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M, copies=nc,
-                                variant="mfma", CB=unroll % 100, KS=unroll // 100))
+                    emit(record(f"gemv_q4_0 {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M, copies=nc, **tag))
         del Wq
         torch.cuda.empty_cache()
 
@@ -560,7 +625,7 @@ def profile_kernels(args):
     y16 = torch.empty(FP16_N, dtype=torch.float16, device="cuda")
     src = torch.empty(GIB // 4, dtype=torch.int32, device="cuda").fill_(3)
     dst = torch.empty_like(src)
-    cs = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cs = torch.zeros(768, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
     for c in range(2 * nq):
         dg.dg_gemv_q4_0(Wq[c % nq], Xq, Yq, Q4_N, Q4_K, 1)
@@ -584,7 +649,7 @@ def main():
     ap.add_argument("--profile-kernels", action="store_true",
                     help="launch each profiled kernel eagerly on known workloads (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
-                    help="comma-separated suite sections: ceiling,dense,q4m1,q4m,argmax,tail")
+                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,argmax,tail")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     args = ap.parse_args()

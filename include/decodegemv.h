@@ -54,17 +54,22 @@ const char* dg_last_hip_error(void);
 /* ------------------------------------------------------------------------
  * Streaming-read ceiling probe
  *
- * Reads every byte of `buf` exactly once, 16 bytes per lane per load, and
- * ADDS the wrapping (mod 2^32) sum of its little-endian 32-bit words into
- * *d_checksum; the sum is what keeps the loads alive.  This is the
+ * Reads every byte of `buf` exactly once, 16 bytes per lane per load.  Each
+ * workgroup b stores the wrapping (mod 2^32) sum of the little-endian 32-bit
+ * words it read into d_partials[b] (a plain store, overwriting); the wrapping
+ * sum of all G partials is the sum of every word of the buffer.  The sums are
+ * what keep the loads alive.  No atomics are used: one same-address atomic per
+ * workgroup would serialise and be measured instead of HBM.  This is the
  * denominator measurement of the batch1-cdna README ("01-ceiling": a read of a
  * buffer far larger than the last-level cache with 4 x 32-bit vector loads,
  * normal or non-temporal).
  *
  *   buf          device, 16-byte aligned, `bytes` long.
- *   bytes        multiple of 16 (0 is allowed: nothing is launched).
- *   d_checksum   device uint32; the caller zeroes it for a fresh sum.
- *   grid_blocks  workgroups to launch; 0 = library default (1024).
+ *   bytes        multiple of 16 (0 is allowed: nothing is launched or written).
+ *   d_partials   device uint32[G], 4-byte aligned, where G = grid_blocks, or
+ *                DG_READ_DEFAULT_GRID when grid_blocks is 0; every entry is
+ *                written (workgroups with no bytes to read store 0).
+ *   grid_blocks  workgroups to launch; 0 = DG_READ_DEFAULT_GRID.
  *   block_threads threads per workgroup, a multiple of 64 in [64, 1024];
  *                0 = library default (512).
  *   flags        DG_READ_NONTEMPORAL: non-temporal loads (else ordinary);
@@ -73,13 +78,13 @@ const char* dg_last_hip_error(void);
  *                8 KiB of consecutive bytes per step);
  *                DG_READ_DEEP: 16 loads in flight per lane instead of 8
  *                (wave-contiguous order only).
- * Errors: DG_ERR_NULL (buf or d_checksum NULL with bytes > 0),
- * DG_ERR_MISALIGNED (buf not 16-byte aligned, d_checksum not 4-byte aligned),
+ * Errors: DG_ERR_NULL (buf or d_partials NULL with bytes > 0),
+ * DG_ERR_MISALIGNED (buf not 16-byte aligned, d_partials not 4-byte aligned),
  * DG_ERR_SHAPE (bytes % 16 != 0), DG_ERR_ARG (grid/block/flags out of range).
  * ------------------------------------------------------------------------ */
-enum { DG_READ_NONTEMPORAL = 1, DG_READ_GRID_STRIDE = 2, DG_READ_DEEP = 4 };
+enum { DG_READ_NONTEMPORAL = 1, DG_READ_GRID_STRIDE = 2, DG_READ_DEEP = 4, DG_READ_DEFAULT_GRID = 1024 };
 
-dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_checksum,
+dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_partials,
                          int grid_blocks, int block_threads, int flags,
                          dg_stream stream);
 
@@ -128,7 +133,7 @@ dg_status dg_gemv_bf16(const void* W, const void* x, float* y,
  *       high nibble), rows packed back to back; 16-byte aligned.
  *   Xq  device, M columns of K/32 Q8_1 blocks, 36 bytes each (binary16 d,
  *       binary16 s, 32 int8 codes), column m starting at block m*K/32;
- *       4-byte aligned.
+ *       16-byte aligned (the kernels copy it in 16-byte pieces).
  *   Y   device float32 [M][N] (column m of the result at Y + m*N).
  *   N   rows, 0 <= N < 2^31.  K: multiple of 256, 0 <= K < 2^31.
  *   M   columns, 0 <= M <= 24 (0 launches nothing).

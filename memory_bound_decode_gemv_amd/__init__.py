@@ -28,6 +28,7 @@ DG_ERR_ARG = 6
 DG_READ_NONTEMPORAL = 1
 DG_READ_GRID_STRIDE = 2
 DG_READ_DEEP = 4
+DG_READ_DEFAULT_GRID = 1024
 
 DG_VARIANT_DENSE_WIDE = 1
 DG_VARIANT_DENSE_XREG = 2
@@ -158,6 +159,13 @@ def _need(t, dtypes, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _fits(t, nbytes, name):
+    """Raises unless tensor t spans at least nbytes (the extent the call reads or writes)."""
+    have = t.numel() * t.element_size()
+    if nbytes > have:
+        raise ValueError(f"{name} holds {have} bytes but the call touches {nbytes}")
+
+
 def _check(status, where):
     if status != DG_OK:
         raise DGError(status, where)
@@ -171,13 +179,22 @@ def _cfg(variant=0, grid=0, block=0, unroll=0):
 # entry points
 # ---------------------------------------------------------------------------
 
-def dg_stream_read(buf, checksum, nbytes=None, grid_blocks=0, block_threads=0,
+def dg_stream_read(buf, partials, nbytes=None, grid_blocks=0, block_threads=0,
                    flags=DG_READ_NONTEMPORAL, stream=None):
-    """Adds the wrapping uint32 word sum of buf's bytes into checksum (int32[1])."""
+    """Reads every byte of buf once; workgroup b stores the wrapping uint32 sum
+    of the words it read into partials[b] (int32 [G], G = grid_blocks or
+    DG_READ_DEFAULT_GRID).  The buffer's word sum is the wrapping sum of the
+    G partials."""
     torch = _torch()
-    _need(checksum, (torch.int32,), "checksum")
+    _need(partials, (torch.int32,), "partials")
+    if not buf.is_cuda:
+        raise ValueError("buf must be a device tensor")
     nbytes = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
-    _check(_lib().dg_stream_read(_ptr(buf), nbytes, _ptr(checksum), int(grid_blocks),
+    _fits(buf, nbytes, "buf")
+    grid = int(grid_blocks) if grid_blocks else DG_READ_DEFAULT_GRID
+    if grid > 0 and nbytes > 0:
+        _fits(partials, grid * 4, "partials")
+    _check(_lib().dg_stream_read(_ptr(buf), nbytes, _ptr(partials), int(grid_blocks),
                                  int(block_threads), int(flags), _stream(stream)),
            "dg_stream_read")
 
@@ -192,6 +209,11 @@ def _dense(name, W, x, y, N, K, ldw, launch, stream, wdtype, ydtype):
         K = x.numel()
     if ldw is None:
         ldw = W.shape[1] if W.dim() == 2 else K
+    N, K, ldw = int(N), int(K), int(ldw)
+    if N > 0 and K > 0 and 0 <= K <= ldw:
+        _fits(W, ((N - 1) * ldw + K) * 2, "W")
+        _fits(x, K * 2, "x")
+    _fits(y, max(N, 0) * y.element_size(), "y")
     lib = _lib()
     if launch is None:
         st = getattr(lib, name)(_ptr(W), _ptr(x), _ptr(y), N, K, ldw, _stream(stream))
@@ -220,6 +242,12 @@ def dg_gemv_q4_0(Wq, Xq, Y, N, K, M, launch=None, stream=None):
     _need(Wq, (torch.uint8,), "Wq")
     _need(Xq, (torch.uint8,), "Xq")
     _need(Y, (torch.float32,), "Y")
+    N, K, M = int(N), int(K), int(M)
+    if N > 0 and K > 0 and M > 0:
+        _fits(Wq, N * (K // 32) * 18, "Wq")
+        _fits(Xq, M * (K // 32) * 36, "Xq")
+    if N > 0 and M > 0:
+        _fits(Y, M * N * 4, "Y")
     lib = _lib()
     if launch is None:
         st = lib.dg_gemv_q4_0(_ptr(Wq), _ptr(Xq), _ptr(Y), int(N), int(K), int(M), _stream(stream))
@@ -235,6 +263,9 @@ def dg_quantize_q8_1(x, Xq, M, K, stream=None):
     torch = _torch()
     _need(x, (torch.float32,), "x")
     _need(Xq, (torch.uint8,), "Xq")
+    if M > 0 and K > 0:
+        _fits(x, int(M) * int(K) * 4, "x")
+        _fits(Xq, int(M) * (int(K) // 32) * 36, "Xq")
     _check(_lib().dg_quantize_q8_1(_ptr(x), _ptr(Xq), int(M), int(K), _stream(stream)), "dg_quantize_q8_1")
     return Xq
 
@@ -244,6 +275,9 @@ def dg_quantize_q4_0(w, Wq, N, K, stream=None):
     torch = _torch()
     _need(w, (torch.float32,), "w")
     _need(Wq, (torch.uint8,), "Wq")
+    if N > 0 and K > 0:
+        _fits(w, int(N) * int(K) * 4, "w")
+        _fits(Wq, int(N) * (int(K) // 32) * 18, "Wq")
     _check(_lib().dg_quantize_q4_0(_ptr(w), _ptr(Wq), int(N), int(K), _stream(stream)), "dg_quantize_q4_0")
     return Wq
 
@@ -263,6 +297,10 @@ def dg_argmax_rows(x, idx, R=None, C=None, ld=None, ws=None, stream=None):
         C = x.shape[-1]
     if ld is None:
         ld = x.shape[-1]
+    R, C, ld = int(R), int(C), int(ld)
+    if R > 0 and C > 0 and ld >= C:
+        _fits(x, ((R - 1) * ld + C) * 4, "x")
+        _fits(idx, R * 8, "idx")
     need = dg_argmax_workspace_bytes(R, C)
     if ws is None:
         raise ValueError(f"dg_argmax_rows needs a device workspace of {need} bytes")

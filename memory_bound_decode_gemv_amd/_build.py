@@ -34,13 +34,18 @@ def common_flags() -> list[str]:
     ]
 
 
+# Per-source flags.  The matrix-core kernel keeps MFMA results in VGPRs (gfx950
+# allows it) instead of AGPRs that every result would have to be copied out of.
+EXTRA_FLAGS = {"gemv_q4_0_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", src, "-o", obj]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}\n{r.stderr}")
@@ -65,7 +70,8 @@ def build(jobs: int | None = None) -> str:
 
 def device_asm(src: str, out: str) -> str:
     """gfx950 assembly of one source (device side only), for the assembly audit."""
-    cmd = [hipcc(), *common_flags(), "--cuda-device-only", "-S", src, "-o", out]
+    cmd = [hipcc(), *common_flags(), *EXTRA_FLAGS.get(os.path.basename(src), []), "--cuda-device-only", "-S",
+           src, "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc -S failed on {src}:\n{r.stdout}\n{r.stderr}")

@@ -57,7 +57,7 @@ dg_status gemv_q4_0_checked(const void* Wq, const void* Xq, float* Y, int64_t N,
     if (N == 0 || M == 0) return DG_OK;
     if (!Y || (K > 0 && (!Wq || !Xq))) return DG_ERR_NULL;
     if (!aligned(Y, 4)) return DG_ERR_MISALIGNED;
-    if (K > 0 && (!aligned(Wq, 16) || !aligned(Xq, 4))) return DG_ERR_MISALIGNED;
+    if (K > 0 && (!aligned(Wq, 16) || !aligned(Xq, 16))) return DG_ERR_MISALIGNED;
     if (K == 0) {   // empty sums: Y = 0
         const int64_t n = N * (int64_t)M;
         hipLaunchKernelGGL(k_fill_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
@@ -116,18 +116,18 @@ const char* dg_status_string(dg_status status) {
 
 const char* dg_last_hip_error(void) { return g_last_hip_error.c_str(); }
 
-dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_checksum, int grid_blocks,
+dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_partials, int grid_blocks,
                          int block_threads, int flags, dg_stream stream) {
     if (bytes % 16 != 0) return DG_ERR_SHAPE;
     if (grid_blocks < 0 || block_threads < 0 || (flags & ~(DG_READ_NONTEMPORAL | DG_READ_GRID_STRIDE | DG_READ_DEEP)))
         return DG_ERR_ARG;
     if (block_threads && (block_threads % kWave != 0 || block_threads > 1024)) return DG_ERR_ARG;
     if (bytes == 0) return DG_OK;
-    if (!buf || !d_checksum) return DG_ERR_NULL;
-    if (!aligned(buf, 16) || !aligned(d_checksum, 4)) return DG_ERR_MISALIGNED;
-    const int grid = grid_blocks ? grid_blocks : 1024;
+    if (!buf || !d_partials) return DG_ERR_NULL;
+    if (!aligned(buf, 16) || !aligned(d_partials, 4)) return DG_ERR_MISALIGNED;
+    const int grid = grid_blocks ? grid_blocks : DG_READ_DEFAULT_GRID;
     const int block = block_threads ? block_threads : 512;
-    return hip_status(launch_stream_read(buf, bytes, d_checksum, grid, block, flags, (hipStream_t)stream));
+    return hip_status(launch_stream_read(buf, bytes, d_partials, grid, block, flags, (hipStream_t)stream));
 }
 
 dg_status dg_gemv_f16(const void* W, const void* x, void* y, int64_t N, int64_t K, int64_t ldw,

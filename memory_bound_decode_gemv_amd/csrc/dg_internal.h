@@ -21,7 +21,7 @@ struct Launch {
 int device_cu_count();
 size_t device_max_lds_per_block();
 
-hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* d_checksum,
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* d_partials,
                               int grid, int block, int flags, hipStream_t s);
 
 // Dense GEMV launcher; `bf16` selects bfloat16 operands with fp32 output,

@@ -259,7 +259,23 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
     const int npairs = K / 64;
     const int S = (npairs + kWave - 1) / kWave;
     int variant = cfg && cfg->variant ? cfg->variant : 0;
-    if (variant == 0) variant = M == 1 ? (S <= 4 ? DG_VARIANT_Q4_LDSROW : DG_VARIANT_Q4_LDS) : DG_VARIANT_Q4_MFMA;
+    int lds_rows = 0;   // rows per wave of the dot4 LDS kernel chosen by default
+    if (variant == 0) {
+        // Measured on MI355X over the decoder shapes and M = 1..24 (every
+        // kernel family is exact to the same bound, so the choice is speed
+        // only): one column streams rows through LDS; two columns, and every
+        // column count of a matrix of at most 1024 rows, take the dot4
+        // kernel (the matrix cores' fixed cost per 16 x 16 tile does not pay
+        // there); the rest take the matrix cores.
+        if (M == 1) {
+            variant = S <= 4 ? DG_VARIANT_Q4_LDSROW : DG_VARIANT_Q4_LDS;
+        } else if (M == 2 || N <= 1024) {
+            variant = DG_VARIANT_Q4_LDS;
+            lds_rows = N > 2048 ? 2 : 1;
+        } else {
+            variant = DG_VARIANT_Q4_MFMA;
+        }
+    }
 
     if (variant == DG_VARIANT_Q4_REGS) {
         const int block = cfg && cfg->block ? cfg->block : 256;
@@ -274,12 +290,12 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
                                    cfg ? cfg->block : 0, s);
     }
     if (variant == DG_VARIANT_Q4_MFMA) {
-        if (cfg && cfg->block && cfg->block != 256) return hipErrorInvalidValue;
+        if (cfg && cfg->block) return hipErrorInvalidValue;   // the configuration fixes the workgroup size
         return launch_q4_mfma(M, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, K, cfg ? cfg->grid : 0, s);
     }
     if (variant == DG_VARIANT_Q4_LDS) {
         if (cfg && cfg->block && cfg->block != kLdsBlock) return hipErrorInvalidValue;
-        int R = cfg && cfg->unroll ? cfg->unroll : (M <= 8 ? 2 : 1);
+        int R = cfg && cfg->unroll ? cfg->unroll : (lds_rows ? lds_rows : (M <= 8 ? 2 : 1));
         const int rows_per_tile = (kLdsBlock / kWave) * R;
         const int ntiles = (N + rows_per_tile - 1) / rows_per_tile;
         const int grid = cfg && cfg->grid ? cfg->grid : ntiles;

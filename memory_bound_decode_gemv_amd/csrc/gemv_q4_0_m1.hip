@@ -73,6 +73,14 @@ k_q4_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
         }
     }
 
+    // Results are held back and stored 64 rows at a time (lane i holds the
+    // i-th row of the batch): a store between two rows' loads would count
+    // in vmcnt ahead of the next row's copies, so every row wait would also
+    // wait for the previous row's write to be acknowledged.
+    float out = 0.0f;
+    int nout = 0;
+    int out_row0 = row0;
+
     int slot = 0;   // buffer of the current row
     for (int row = row0; row < N; row += rstride) {
         const int ahead = row + (DEPTH - 1) * rstride;
@@ -95,10 +103,16 @@ k_q4_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
             unpack_weight_pair(w, u);
             acc = pair_dot(u, act[s].qa, act[s].qb, act[s].da, act[s].db, act[s].ca, act[s].cb, acc);
         }
-        acc = wave_sum_f32(acc);
-        if (lane == 0) Y[row] = acc;
+        acc = wave_sum_f32(acc);   // wave-uniform
+        if (lane == nout) out = acc;
+        if (++nout == kWave) {
+            Y[out_row0 + (int64_t)lane * rstride] = out;
+            nout = 0;
+            out_row0 = row + rstride;
+        }
         slot = slot + 1 == DEPTH ? 0 : slot + 1;
     }
+    if (lane < nout) Y[out_row0 + (int64_t)lane * rstride] = out;
 }
 
 }  // namespace

@@ -16,277 +16,362 @@ using namespace q4;
 // pushed the mini-GEMM of "The kernel that waited for itself" to 76% of the
 // decode step.  The sum over one Q4_0 block is an int8 contraction of length
 // 32, exactly the K of v_mfma_i32_16x16x32_i8, so every block keeps its own
-// scales:
-//   A (16 x 32, int8)  = the q8 codes of 16 activation columns for block b,
-//   B (32 x 16, int8)  = the 4-bit codes (0..15) of 16 weight rows for block b,
-//   C (16 x 16, int32) = -8 * sum(q8) per column (the offset of q - 8),
-//   D = A*B + C        = the exact int32 block sums, then scaled by d4*d8 in fp32.
+// scales.  Per block b and per tile of 16 weight rows x 16 columns:
+//   A (16 x 32, int8)  = the q8 codes of 16 activation columns,
+//   B (32 x 16, int8)  = the 4-bit codes (0..15) of 16 weight rows,
+//   D0 = A * (-8)      = -8 * sum(q8) per column (a second MFMA against a
+//                        constant operand: the offset of q - 8, exact),
+//   D  = A * B + D0    = the exact int32 block sums, scaled by d4 * d8 in fp32.
 // The order of the 32 terms inside the instruction is irrelevant (integers);
 // each lane supplies A and B bytes for the same 8 k-slots: lane group g = l/16
 // carries weights 4g..4g+3 (low nibbles of code dword g) and 16+4g..16+4g+3
-// (high nibbles), and the matching activation dwords g and 4+g.  Output lane
-// l holds D[4g + r][l % 16]: columns m = 4g + r of weight row l % 16.
+// (high nibbles), and the matching activation code dwords g and 4+g.  Output
+// lane l holds D[4g + r][l % 16]: column m = 4g + r of weight row l % 16.
 //
-// Data flow per workgroup (4 waves = RT row tiles of 16 rows x KS parts of K):
-//  * each wave copies its 16 weight rows x CB blocks (one chunk) from HBM to a
-//    private LDS buffer with global_load_lds_dwordx4 (coalesced 1 KiB per
-//    instruction; rows padded to an odd number of 16-byte slots against bank
-//    conflicts), the next chunk in flight while the current one is computed;
-//  * all 256 threads stage the matching activation chunks in LDS in operand
-//    order (A dwords per lane, and per column group the -8*sum(q8) and d8);
-//  * the KS partial results of a row tile meet in LDS in the fixed order
-//    0..KS-1 (deterministic).
-// Every lane of every copy instruction is active (lanes without a slot of the
-// chunk re-read the tile's first slot into an unused LDS slot), so a chunk is
-// always exactly C vector-memory instructions and the explicit vmcnt waits
-// are exact.
+// Data flow.  A workgroup of W = RT * KS waves (4, 8 or 16) covers RT row
+// tiles, each split into KS parts of K, so that small matrices still give
+// every CU several waves; K is walked in chunks of CB blocks, iteration `it`
+// giving part p the chunk it * KS + p.  Everything reaches LDS by
+// global_load_lds_dwordx4 (1 KiB of contiguous LDS per instruction, no VGPRs):
+//  * each wave copies its 16 rows x CB blocks of weights (non-temporal: read
+//    once) into a private buffer, rows padded to an odd number of 16-byte
+//    slots so that the 16 rows of a lane group fall in different banks;
+//  * the W waves together copy the raw Q8_1 blocks of the iteration's KS
+//    activation chunks for MP >= M columns (MP = 4, 8, 16 or 32; 36 bytes per
+//    block, column spans padded to an odd number of slots) into a buffer
+//    shared by the workgroup; every weight row tile reuses it, and L2 serves
+//    it to every workgroup.  With MP < 16 the MFMA rows past MP re-read
+//    columns (their results are discarded).
+// DEPTH buffers of each kind keep DEPTH - 1 iterations in flight while one is
+// computed.  No global load goes through VGPRs inside the loop, so the only
+// vector-memory operations a wave has outstanding are its own copies, which
+// complete in issue order; each wave issues exactly kCw + kCa copy
+// instructions per iteration (lanes without a slot of the data re-read a
+// valid address next to the real data into a slot nobody reads, so that no
+// line becomes a hot spot for the whole chip), so "at most q * (kCw + kCa) outstanding"
+// proves that the iteration q steps back has landed, and a barrier after each
+// wave's own wait makes the shared activation chunk complete for all.
+// Outputs: the KS partial results of a row tile meet in LDS and are added in
+// the fixed order 0..KS-1 (deterministic).
 // ---------------------------------------------------------------------------
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int CB>
+constexpr long kNeg8 = (long)0xF8F8F8F8F8F8F8F8ull;   // eight int8 k-slots of -8
+
+template <int CB, int MP, int RT, int KS>
 struct MfmaGeom {
     static_assert(CB % 8 == 0, "chunks hold whole 144-byte groups of 8 blocks");
-    static constexpr int kSlotsUsed = CB * 18 / 16;        // 16-byte slots of one row's chunk
-    static constexpr int kRowSlots = kSlotsUsed + 1;         // odd stride in slots
-    static constexpr int kC = (16 * kRowSlots + 63) / 64;    // copy instructions per chunk
-    static constexpr int kBufBytes = kC * 1024;              // per wave, per buffer
+    static_assert(MP == 4 || MP == 8 || MP == 16 || MP == 32, "padded column count");
+    static constexpr int kW = RT * KS;                           // waves per workgroup
+    static_assert(kW == 4 || kW == 8 || kW == 16, "4, 8 or 16 waves");
+    static constexpr int kNT = (MP + 15) / 16;                   // 16-column MFMA tiles
+    // weights: 16 rows x CB blocks of 18 bytes
+    static constexpr int kWSlotsUsed = CB * 18 / 16;
+    static constexpr int kWRowSlots = kWSlotsUsed | 1;           // odd stride in slots
+    static constexpr int kCw = (16 * kWRowSlots + 63) / 64;      // copy instructions per wave
+    static constexpr int kWBufBytes = kCw * 1024;                // per wave, per buffer
+    // activations: KS parts x MP columns x CB blocks of 36 bytes
+    static constexpr int kASlotsUsed = CB * 36 / 16;
+    static constexpr int kAColSlots = kASlotsUsed | 1;           // odd stride in slots
+    static constexpr int kAPartSlots = MP * kAColSlots;
+    static constexpr int kASlots = KS * kAPartSlots;
+    static constexpr int kCa = (kASlots + kW * 64 - 1) / (kW * 64);  // copy instructions per wave
+    static constexpr int kABufBytes = kCa * kW * 1024;           // per workgroup, per buffer
+    static constexpr int kCopies = kCw + kCa;                    // per wave, per iteration
+    static constexpr int kStageBytes = kW * kWBufBytes + kABufBytes;
 };
 
-template <int CB, int NT>
-struct MfmaActGeom {
-    // A operand: [block][tile][lane] x 8 bytes; scales: [block][tile][group] x 32 bytes
-    static constexpr int kABytes = CB * NT * 64 * 8;
-    static constexpr int kSBytes = CB * NT * 4 * 32;
-    static constexpr int kBytes = kABytes + kSBytes;
-};
-
-template <int CB, int NT, int KS>
+// LDS: DEPTH stages, then one fp32 table of d8 per wave (CB x MP scales of
+// the chunk it computes); after the loop the stages hold the KS partial sums.
+template <int CB, int MP, int RT, int KS, int DEPTH>
 constexpr size_t mfma_lds_bytes() {
-    return (size_t)4 * 2 * MfmaGeom<CB>::kBufBytes + (size_t)KS * MfmaActGeom<CB, NT>::kBytes;
+    using G = MfmaGeom<CB, MP, RT, KS>;
+    const size_t main = (size_t)DEPTH * G::kStageBytes;
+    const size_t red = (size_t)G::kW * G::kNT * 4 * 64 * 4;   // partial sums of the KS parts
+    return (main > red ? main : red) + (size_t)G::kW * CB * MP * 4;
 }
 
-// Copies 16 rows x cb blocks (starting at block blk0) into buf.  cb <= CB,
-// cb % 8 == 0.  Rows past the end of the matrix are clamped to the last row.
-template <int CB>
-__device__ __forceinline__ void mfma_copy_chunk(const uint8_t* __restrict__ Wq, size_t row_bytes, int n0, int N,
-                                                int blk0, int cb, uint8_t* buf, int lane) {
-    using G = MfmaGeom<CB>;
-    const int slots_used = cb * 18 / 16;
-    const uint8_t* safe = Wq + (size_t)(n0 < N ? n0 : N - 1) * row_bytes + (size_t)blk0 * 18;
+// This wave's weight copies of chunk ch: 16 rows from n0, blocks [ch*CB, ..).
+// Every lane loads a valid address: rows past N, slots past the chunk and
+// chunks past the end are clamped onto real data (that the compute skips).
+template <int CB, int MP, int RT, int KS>
+__device__ __forceinline__ void copy_weights(const uint8_t* __restrict__ Wq, size_t row_bytes, int n0, int N,
+                                             int nblk, int nchunks, int ch, uint8_t* buf, int lane) {
+    using G = MfmaGeom<CB, MP, RT, KS>;
+    const int chc = ch < nchunks ? ch : nchunks - 1;
+    const int blk0 = chc * CB;
+    const int cb = nblk - blk0 < CB ? nblk - blk0 : CB;
+    const int used = cb * 18 / 16;
 #pragma unroll
-    for (int j = 0; j < G::kC; ++j) {
+    for (int j = 0; j < G::kCw; ++j) {
         const int q = j * kWave + lane;
-        const int r = q / G::kRowSlots;
-        const int c = q - r * G::kRowSlots;
-        const uint8_t* src = safe;
-        if (r < 16 && c < slots_used) {
-            const int n = n0 + r < N ? n0 + r : N - 1;
-            src = Wq + (size_t)n * row_bytes + (size_t)blk0 * 18 + (size_t)c * 16;
-        }
+        const int r = q / G::kWRowSlots;
+        const int c = q - r * G::kWRowSlots;
+        const int rc = r < 16 ? r : 15;
+        const int n = n0 + rc < N ? n0 + rc : N - 1;
+        const int cc = c < used ? c : used - 1;
+        const uint8_t* src = Wq + (size_t)n * row_bytes + (size_t)blk0 * 18 + (size_t)cc * 16;
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + j * 1024), 16, 0, kAuxNonTemporal);
     }
 }
 
-// Stages the activation chunks of the KS parts of one iteration: item e of
-// part s2 is column m = e / CB, block b = e % CB (consecutive threads read
-// consecutive blocks of one column).  Each thread owns kItems items, and all
-// of their global loads are issued before any is consumed, so the staging
-// costs one L2 round trip rather than one per item.
-template <int CB, int NT, int KS>
-__device__ __forceinline__ void mfma_stage_acts(const uint8_t* __restrict__ Xq, int nblk, int M, int it,
-                                                int nchunks, uint8_t* abase) {
-    using A = MfmaActGeom<CB, NT>;
-    constexpr int kPerPart = CB * 16 * NT;
-    constexpr int kItems = (kPerPart * KS + 255) / 256;
-    uint32_t q[kItems][8];
-    uint32_t d0[kItems];
+// This wave's share (instructions wave*kCa .. wave*kCa + kCa - 1) of the
+// activation copies of iteration it: slot s of the buffer is part p, column m,
+// 16-byte slot c of that column's CB blocks.  Clamped like the weights.
+template <int CB, int MP, int RT, int KS>
+__device__ __forceinline__ void copy_acts(const uint8_t* __restrict__ Xq, int nblk, int nchunks, int M, int it,
+                                          int wave, uint8_t* abuf, int lane) {
+    using G = MfmaGeom<CB, MP, RT, KS>;
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-        const int e = threadIdx.x + i * 256;
-        const int s2 = e / kPerPart;
-        const int e2 = e - s2 * kPerPart;
-        const int m = e2 / CB;
-        const int b = e2 - m * CB;
-        const int ch = it * KS + s2;
+    for (int j = 0; j < G::kCa; ++j) {
+        const int s = (wave * G::kCa + j) * kWave + lane;
+        int p = s / G::kAPartSlots;
+        const int e = s - p * G::kAPartSlots;
+        const int m = e / G::kAColSlots;
+        const int c = e - m * G::kAColSlots;
+        p = p < KS ? p : KS - 1;
+        int ch = it * KS + p;
+        ch = ch < nchunks ? ch : nchunks - 1;
         const int blk0 = ch * CB;
-        const bool ok = e < kPerPart * KS && ch < nchunks && m < M && blk0 + b < nblk;
-        d0[i] = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) q[i][j] = 0;
-        if (ok) {
-            const uint32_t* src = reinterpret_cast<const uint32_t*>(Xq + ((size_t)m * nblk + blk0 + b) * kQ81Bytes);
-            d0[i] = src[0];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) q[i][j] = src[1 + j];
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-        const int e = threadIdx.x + i * 256;
-        if (e >= kPerPart * KS) continue;
-        const int s2 = e / kPerPart;
-        const int e2 = e - s2 * kPerPart;
-        const int m = e2 / CB;
-        const int b = e2 - m * CB;
-        uint8_t* abuf = abase + s2 * A::kBytes;
-        uint64_t* a64 = reinterpret_cast<uint64_t*>(abuf);
-        uint32_t* sc = reinterpret_cast<uint32_t*>(abuf + A::kABytes);
-        const float d = half_lo_to_f32(d0[i]);
-        const int c = -8 * block_code_sum(q[i]);
-        const int t = m >> 4, mm = m & 15, g = mm >> 2, r = mm & 3;
-#pragma unroll
-        for (int gg = 0; gg < 4; ++gg)
-            a64[(b * NT + t) * 64 + gg * 16 + mm] = (uint64_t)q[i][gg] | ((uint64_t)q[i][4 + gg] << 32);
-        uint32_t* rec = sc + ((b * NT + t) * 4 + g) * 8;
-        rec[r] = (uint32_t)c;
-        rec[4 + r] = __builtin_bit_cast(uint32_t, d);
+        const int cb = nblk - blk0 < CB ? nblk - blk0 : CB;
+        const int used = cb * 36 / 16;
+        const int mc = m < M ? m : M - 1;
+        const int cc = c < used ? c : used - 1;
+        const uint8_t* src = Xq + ((size_t)mc * nblk + blk0) * kQ81Bytes + (size_t)cc * 16;
+        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(abuf + (wave * G::kCa + j) * 1024), 16, 0, 0);
     }
 }
 
-template <int CB, int NT, int KS>
-__global__ void __launch_bounds__(256)
+// Waits until at most q iterations' copies of this wave are outstanding.
+template <int COPIES, int DEPTH>
+__device__ __forceinline__ void wait_iterations_ahead(int q) {
+    if (DEPTH == 1 || q == 0) wait_vmcnt<0>();
+    else if (DEPTH > 2 && q == 1) wait_vmcnt<COPIES>();
+    else if (DEPTH > 3 && q == 2) wait_vmcnt<(DEPTH > 3 ? 2 * COPIES : 0)>();
+    else wait_vmcnt<(DEPTH > 1 ? (DEPTH - 1) * COPIES : 0)>();
+}
+
+template <int CB, int MP, int RT, int KS, int DEPTH>
+__global__ void __launch_bounds__(64 * RT * KS)
 k_q4_mfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
           int N, int K, int M) {
-    using G = MfmaGeom<CB>;
-    using A = MfmaActGeom<CB, NT>;
-    constexpr int RT = 4 / KS;                 // row tiles per workgroup
+    using G = MfmaGeom<CB, MP, RT, KS>;
+    constexpr int NT = G::kNT;
+    static_assert(DEPTH >= 1 && DEPTH <= 3, "pipeline depth");
+    static_assert(G::kCopies * (DEPTH - 1) <= 63, "wait count exceeds the vmcnt field");
     extern __shared__ u32x4 mfma_lds[];
     uint8_t* const lds = reinterpret_cast<uint8_t*>(mfma_lds);
     const int lane = lane_id();
     const int wave = wave_in_block();
-    const int tile = wave / KS;                // this wave's row tile
+    const int tile = wave / KS;                // this wave's row tile in the group
     const int part = wave - tile * KS;         // this wave's part of K
     const int g = lane >> 4, rn = lane & 15;
     const int nblk = K >> 5;
     const size_t row_bytes = (size_t)nblk * 18;
     const int nchunks = (nblk + CB - 1) / CB;
     const int iters = (nchunks + KS - 1) / KS;
-    const int n0 = (blockIdx.x * RT + tile) * 16;
-    uint8_t* const wbuf = lds + wave * 2 * G::kBufBytes;
-    uint8_t* const abase = lds + 4 * 2 * G::kBufBytes;
+    const int ngroups = (N + 16 * RT - 1) / (16 * RT);
+    // A-operand column of this lane and d8 columns of its outputs (MP < 16:
+    // the MFMA rows past MP re-read columns m % MP; those results are dropped)
+    const int acol = MP < 16 ? (rn & (MP - 1)) : rn;
+    auto wbuf = [&](int d) { return lds + d * G::kStageBytes + wave * G::kWBufBytes; };
+    auto abuf = [&](int d) { return lds + d * G::kStageBytes + G::kW * G::kWBufBytes; };
+    constexpr size_t kTabOff = mfma_lds_bytes<CB, MP, RT, KS, DEPTH>() - (size_t)G::kW * CB * MP * 4;
+    float* const d8tab = reinterpret_cast<float*>(lds + kTabOff) + wave * CB * MP;
 
-    f32x4 acc[NT];
+    for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {   // workgroup-uniform
+        const int n0 = (grp * RT + tile) * 16;
+        auto issue = [&](int it2, int d) {
+            copy_weights<CB, MP, RT, KS>(Wq, row_bytes, n0, N, nblk, nchunks, it2 * KS + part, wbuf(d), lane);
+            copy_acts<CB, MP, RT, KS>(Xq, nblk, nchunks, M, it2, wave, abuf(d), lane);
+        };
+        lds_barrier();   // the previous group's reads of every buffer are done
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int d = 0; d < DEPTH - 1; ++d)
+            if (d < iters) issue(d, d);
 
-    // chunk handled by this wave in iteration it: it*KS + part.  Order inside an
-    // iteration: barrier; stage the activations (their loads drain this
-    // wave's copy of the current chunk, which is needed now anyway); request
-    // the next chunk; barrier; compute while that copy is in flight.
-    if (part < nchunks) {
-        const int cb = nblk - part * CB < CB ? nblk - part * CB : CB;
-        mfma_copy_chunk<CB>(Wq, row_bytes, n0, N, part * CB, cb, wbuf, lane);
-    }
-    for (int it = 0; it < iters; ++it) {
-        const int ch = it * KS + part;
-        const int nch = ch + KS;
-        const bool have = ch < nchunks;                 // wave-uniform
-        const bool ahead = nch < nchunks;               // wave-uniform
-        lds_barrier();   // every wave is done reading the previous activation chunks
-        mfma_stage_acts<CB, NT, KS>(Xq, nblk, M, it, nchunks, abase);
-        if (ahead) {
-            const int cbn = nblk - nch * CB < CB ? nblk - nch * CB : CB;
-            mfma_copy_chunk<CB>(Wq, row_bytes, n0, N, nch * CB, cbn, wbuf + ((it + 1) & 1) * G::kBufBytes, lane);
-        }
-        lds_barrier();   // activation chunks staged
-        if (ahead) wait_vmcnt<G::kC>();   // the current chunk's copy is complete
-        else wait_vmcnt<0>();
-        if (have) {
-            const int cb = nblk - ch * CB < CB ? nblk - ch * CB : CB;
-            const uint8_t* rowp = wbuf + (it & 1) * G::kBufBytes + rn * G::kRowSlots * 16;
-            const uint8_t* abuf = abase + part * A::kBytes;
-            const uint64_t* a64 = reinterpret_cast<const uint64_t*>(abuf);
-            const i32x4* sci = reinterpret_cast<const i32x4*>(abuf + A::kABytes);
-#pragma unroll 4
-            for (int p = 0; p < (cb >> 1); ++p) {   // cb / 2 is a multiple of 4
-                const uint32_t* w = reinterpret_cast<const uint32_t*>(rowp + p * kPairBytes);
-                const uint32_t wg0 = w[g], wg1 = w[g + 1], ws0 = w[0], ws4 = w[4], wb = w[5 + g];
+        f32x4 acc[NT];
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t code = h == 0 ? __builtin_amdgcn_alignbit(wg1, wg0, 16) : wb;
-                    const float d4 = h == 0 ? half_lo_to_f32(ws0) : half_hi_to_f32(ws4);
-                    const long bop = (long)((uint64_t)(code & kNib) | ((uint64_t)((code >> 4) & kNib) << 32));
-                    const int b = 2 * p + h;
+        for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+        int slot = 0;
+        for (int it = 0; it < iters; ++it) {
+            lds_barrier();   // every wave is done with the buffer the next copies overwrite
+            const int ahead = it + DEPTH - 1;
+            if (ahead < iters) {
+                int aslot = slot + DEPTH - 1;
+                if (aslot >= DEPTH) aslot -= DEPTH;
+                issue(ahead, aslot);
+            }
+            const int left = iters - 1 - it;
+            wait_iterations_ahead<G::kCopies, DEPTH>(left < DEPTH - 1 ? left : DEPTH - 1);
+            lds_barrier();   // every wave's copies of this iteration have landed
+
+            const int ch = it * KS + part;
+            if (ch < nchunks) {   // wave-uniform
+                const int cb = nblk - ch * CB < CB ? nblk - ch * CB : CB;   // a multiple of 8
+                const uint8_t* rowp = wbuf(slot) + rn * G::kWRowSlots * 16;
+                const uint8_t* ap = abuf(slot) + part * G::kAPartSlots * 16;
+                // d8 of the chunk as fp32, [block][column], converted once per wave
+                // (the same wave reads it back: LDS operations of a wave are in order)
+#pragma unroll
+                for (int i = 0; i < (CB * MP + kWave - 1) / kWave; ++i) {
+                    const int e = i * kWave + lane;
+                    if (CB * MP % kWave == 0 || e < CB * MP) {
+                        const int b = e / MP, m = e - (e / MP) * MP;
+                        const uint32_t dw = *reinterpret_cast<const uint32_t*>(
+                            ap + (m * G::kAColSlots * 16 + b * kQ81Bytes));
+                        d8tab[e] = half_lo_to_f32(dw);
+                    }
+                }
+                // Groups of 8 blocks in three phases, so that the 16 (or 32)
+                // matrix-core operations of a group are independent of one
+                // another and of the scaling (each block has its own result
+                // registers): operands, then every MFMA, then the fp32 scaling.
+                for (int o = 0; o < cb; o += 8) {
+                    long bop[8];
+                    float d4[8];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {   // block pairs o + 2p, o + 2p + 1
+                        const uint32_t* w = reinterpret_cast<const uint32_t*>(rowp + ((o >> 1) + p) * kPairBytes);
+                        const uint32_t wg0 = w[g], wg1 = w[g + 1], ws0 = w[0], ws4 = w[4], wb = w[5 + g];
+                        const uint32_t c0 = __builtin_amdgcn_alignbit(wg1, wg0, 16);
+                        bop[2 * p] = (long)((uint64_t)(c0 & kNib) | ((uint64_t)((c0 >> 4) & kNib) << 32));
+                        bop[2 * p + 1] = (long)((uint64_t)(wb & kNib) | ((uint64_t)((wb >> 4) & kNib) << 32));
+                        d4[2 * p] = half_lo_to_f32(ws0);
+                        d4[2 * p + 1] = half_hi_to_f32(ws4);
+                    }
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
-                        const long aop = (long)a64[(b * NT + t) * 64 + lane];
-                        const i32x4 cinit = sci[((b * NT + t) * 4 + g) * 2];
-                        const f32x4 d8 = __builtin_bit_cast(f32x4, sci[((b * NT + t) * 4 + g) * 2 + 1]);
-                        const i32x4 dsum = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, cinit, 0, 0, 0);
+                        long aop[8];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)dsum[r], d4 * d8[r], acc[t][r]);
+                        for (int i = 0; i < 8; ++i) {
+                            // A: code dwords g and 4 + g of column 16t + acol, block o + i
+                            const uint32_t* ab = reinterpret_cast<const uint32_t*>(
+                                ap + ((16 * t + acol) * G::kAColSlots * 16 + (o + i) * kQ81Bytes + 4 * g));
+                            aop[i] = (long)((uint64_t)ab[1] | ((uint64_t)ab[5] << 32));
+                        }
+                        i32x4 dsum[8];
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            dsum[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[i], kNeg8, i32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            dsum[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[i], bop[i], dsum[i], 0, 0, 0);
+                        // d8 of output columns 16t + 4g + r, r = 0..3 (columns past MP wrap)
+                        const int c0 = MP < 16 ? ((4 * g) & (MP - 1)) : 16 * t + 4 * g;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            const f32x4 d8 = *reinterpret_cast<const f32x4*>(d8tab + (o + i) * MP + c0);
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                acc[t][r] = fmaf((float)dsum[i][r], d4[i] * d8[r], acc[t][r]);
+                        }
                     }
                 }
             }
+            slot = slot + 1 == DEPTH ? 0 : slot + 1;
         }
-    }
 
-    // combine the KS parts of each row tile (fixed order) and store
-    if constexpr (KS > 1) {
-        lds_barrier();   // all activation reads done: reuse the activation area
-        float* red = reinterpret_cast<float*>(abase);
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) red[((wave * NT + t) * 4 + r) * 64 + lane] = acc[t][r];
-        lds_barrier();
-        if (part == 0) {
+        // combine the KS parts of each row tile (fixed order) and store
+        if constexpr (KS > 1) {
+            lds_barrier();   // every wave is done reading the buffers: reuse them
+            float* red = reinterpret_cast<float*>(lds);
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    float v = acc[t][r];
-                    for (int s2 = 1; s2 < KS; ++s2) v += red[(((wave + s2) * NT + t) * 4 + r) * 64 + lane];
-                    acc[t][r] = v;
-                }
+                for (int r = 0; r < 4; ++r) red[((wave * NT + t) * 4 + r) * 64 + lane] = acc[t][r];
+            lds_barrier();
+            if (part == 0) {
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        float v = acc[t][r];
+                        for (int s2 = 1; s2 < KS; ++s2) v += red[(((wave + s2) * NT + t) * 4 + r) * 64 + lane];
+                        acc[t][r] = v;
+                    }
+            }
         }
-    }
-    if (part == 0) {
-        const int n = n0 + rn;
-        if (n < N) {
+        if (part == 0) {
+            const int n = n0 + rn;
+            if (n < N) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
+                for (int t = 0; t < NT; ++t)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = t * 16 + g * 4 + r;
-                    if (m < M) Y[(size_t)m * N + n] = acc[t][r];
-                }
+                    for (int r = 0; r < 4; ++r) {
+                        const int m = t * 16 + g * 4 + r;
+                        if (m < M) Y[(size_t)m * N + n] = acc[t][r];
+                    }
+            }
         }
     }
 }
 
-template <int CB, int NT, int KS>
+template <int CB, int MP, int RT, int KS, int DEPTH>
 hipError_t launch_mfma_cfg(const void* Wq, const void* Xq, float* Y, int N, int K, int M, int grid, hipStream_t s) {
-    const size_t lds = mfma_lds_bytes<CB, NT, KS>();
+    const size_t lds = mfma_lds_bytes<CB, MP, RT, KS, DEPTH>();
     if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
-    constexpr int rows_per_block = 16 * (4 / KS);
-    const int g = grid ? grid : (N + rows_per_block - 1) / rows_per_block;
-    hipLaunchKernelGGL((k_q4_mfma<CB, NT, KS>), dim3(g), dim3(256), lds, s, (const uint8_t*)Wq, (const uint8_t*)Xq,
-                       Y, N, K, M);
+    const int groups = (N + 16 * RT - 1) / (16 * RT);
+    const int g = grid ? grid : groups;
+    hipLaunchKernelGGL((k_q4_mfma<CB, MP, RT, KS, DEPTH>), dim3(g), dim3(64 * RT * KS), lds, s,
+                       (const uint8_t*)Wq, (const uint8_t*)Xq, Y, N, K, M);
     return hipGetLastError();
+}
+
+// The built configurations for one padded column count MP.
+template <int MP>
+hipError_t launch_mfma_mp(int RT, int KS, int DEPTH, int CB, const void* Wq, const void* Xq, float* Y, int N, int K,
+                          int M, int grid, hipStream_t s) {
+#define DG_MF(RR, SS, DD, CC)                                      \
+    if (RT == RR && KS == SS && DEPTH == DD && CB == CC)           \
+        return launch_mfma_cfg<CC, MP, RR, SS, DD>(Wq, Xq, Y, N, K, M, grid, s);
+    // 16 waves
+    if constexpr (MP <= 16) { DG_MF(1, 16, 1, 8) DG_MF(2, 8, 1, 8) }   // (2, 8, 1) spills at 32 columns
+    if constexpr (MP <= 8) { DG_MF(4, 4, 2, 8) }
+    // 8 waves
+    DG_MF(1, 8, 1, 8) DG_MF(2, 4, 2, 8) DG_MF(4, 2, 2, 8) DG_MF(8, 1, 2, 8)
+    if constexpr (MP <= 16) { DG_MF(1, 8, 2, 8) }
+    // 4 waves
+    DG_MF(4, 1, 2, 8) DG_MF(4, 1, 3, 8) DG_MF(2, 2, 2, 8) DG_MF(1, 4, 2, 8)
+#undef DG_MF
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// unroll selects the chunk and K split for sweeps: CB (16 or 32) + 100 * KS (1, 2, 4).
+// unroll = RT * 10000 + KS * 100 + DEPTH * 10 + CB / 8 selects a configuration
+// for sweeps (0: the default for the shape); the padded column count follows M.
 hipError_t launch_q4_mfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
-                       hipStream_t s) {
-    int CB = 16, KS = 1;
+                          hipStream_t s) {
+    int RT, KS, DEPTH, CB;
     if (unroll) {
-        CB = unroll % 100;
-        KS = unroll / 100;
+        RT = unroll / 10000;
+        KS = (unroll / 100) % 100;
+        DEPTH = (unroll / 10) % 10;
+        CB = (unroll % 10) * 8;
     } else {
+        // Measured on MI355X (decoder shapes, M = 2..24): split K over 8 waves
+        // (4 for 9..16 columns) when there are few row tiles; share each
+        // activation chunk between two row tiles when there are many.
         const int tiles = (N + 15) / 16;
-        KS = tiles >= 1024 ? 1 : (tiles >= 512 ? 2 : 4);
+        CB = 8;
+        if (tiles <= 512) {
+            RT = 1;
+            KS = (M <= 8 || M > 16) ? 8 : 4;
+            DEPTH = M > 16 ? 1 : 2;
+        } else {
+            DEPTH = 2;
+            if (M <= 4) { RT = 2; KS = 4; }
+            else if (M <= 8) { RT = 4; KS = 2; }
+            else { RT = 2; KS = 2; }
+        }
     }
-    const int NT = M <= 16 ? 1 : 2;
-#define DG_MF(CC, TT, SS) \
-    if (CB == CC && NT == TT && KS == SS) return launch_mfma_cfg<CC, TT, SS>(Wq, Xq, Y, N, K, M, grid, s);
-    DG_MF(16, 1, 1) DG_MF(16, 1, 2) DG_MF(16, 1, 4) DG_MF(16, 2, 1) DG_MF(16, 2, 2) DG_MF(16, 2, 4)
-    DG_MF(32, 1, 1) DG_MF(32, 1, 2) DG_MF(32, 1, 4) DG_MF(32, 2, 1) DG_MF(32, 2, 2)
-#undef DG_MF
-    return hipErrorInvalidValue;
+    if (M <= 4) return launch_mfma_mp<4>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
+    if (M <= 8) return launch_mfma_mp<8>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
+    if (M <= 16) return launch_mfma_mp<16>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
+    return launch_mfma_mp<32>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
 }
 
 }  // namespace dg

@@ -118,12 +118,12 @@ __device__ __forceinline__ void copy_row_to_lds(const uint8_t* __restrict__ row,
 
 template <int N_OUTSTANDING>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N_OUTSTANDING >= 0 && N_OUTSTANDING <= 31, "wait count out of range");
+    static_assert(N_OUTSTANDING >= 0 && N_OUTSTANDING <= 63, "wait count out of range (6-bit vmcnt)");
 #define DG_WAIT(n) if constexpr (N_OUTSTANDING == n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory");
-    DG_WAIT(0) DG_WAIT(1) DG_WAIT(2) DG_WAIT(3) DG_WAIT(4) DG_WAIT(5) DG_WAIT(6) DG_WAIT(7)
-    DG_WAIT(8) DG_WAIT(9) DG_WAIT(10) DG_WAIT(11) DG_WAIT(12) DG_WAIT(13) DG_WAIT(14) DG_WAIT(15)
-    DG_WAIT(16) DG_WAIT(17) DG_WAIT(18) DG_WAIT(19) DG_WAIT(20) DG_WAIT(21) DG_WAIT(22) DG_WAIT(23)
-    DG_WAIT(24) DG_WAIT(25) DG_WAIT(26) DG_WAIT(27) DG_WAIT(28) DG_WAIT(29) DG_WAIT(30) DG_WAIT(31)
+#define DG_WAIT8(b) DG_WAIT(b) DG_WAIT(b + 1) DG_WAIT(b + 2) DG_WAIT(b + 3) DG_WAIT(b + 4) DG_WAIT(b + 5) \
+    DG_WAIT(b + 6) DG_WAIT(b + 7)
+    DG_WAIT8(0) DG_WAIT8(8) DG_WAIT8(16) DG_WAIT8(24) DG_WAIT8(32) DG_WAIT8(40) DG_WAIT8(48) DG_WAIT8(56)
+#undef DG_WAIT8
 #undef DG_WAIT
 }
 

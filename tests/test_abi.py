@@ -72,6 +72,7 @@ def test_gemv_f16_rejects_before_launch(lib, args, expect):
     ((A16, None, A16, 4, 256, 1), 1),
     ((A2, A16, A16, 4, 256, 1), 2),       # Wq must be 16-byte aligned
     ((A16, A16, A2, 4, 256, 1), 2),       # Y must be 4-byte aligned
+    ((A16, P(0x1004), A16, 4, 256, 1), 2),  # Xq must be 16-byte aligned
     ((None, None, None, 4, 256, 0), 0),   # M = 0
     ((None, None, None, 0, 256, 3), 0),   # N = 0
 ])
@@ -93,6 +94,8 @@ def test_stream_read_rejects_before_launch(lib):
     assert lib.dg_stream_read(A16, 32, A16, 0, 0, 8, None) == 6          # unknown flag
     assert lib.dg_stream_read(None, 32, A16, 0, 0, 1, None) == 1
     assert lib.dg_stream_read(A2, 32, A16, 0, 0, 1, None) == 2
+    assert lib.dg_stream_read(A16, 32, A2, 0, 0, 1, None) == 2          # partials not 4-byte aligned
+    assert lib.dg_stream_read(A16, 32, None, 0, 0, 1, None) == 1
     assert lib.dg_stream_read(None, 0, None, 0, 0, 1, None) == 0         # empty
 
 
@@ -115,3 +118,18 @@ def test_quantisers_reject_before_launch(lib):
     assert lib.dg_quantize_q8_1(A2, A16, 2, 64, None) == 2
     assert lib.dg_quantize_q4_0(None, A16, 2, 64, None) == 1
     assert lib.dg_quantize_q8_1(None, None, 0, 64, None) == 0
+
+
+def test_binding_refuses_tensors_smaller_than_the_call_touches():
+    """The binding checks that each tensor spans what the call would read or
+    write, so a size argument larger than its tensor never reaches a kernel."""
+    import torch
+    import memory_bound_decode_gemv_amd as dg
+    t = torch.zeros(10, dtype=torch.uint8)
+    dg._fits(t, 10, "t")
+    with pytest.raises(ValueError, match="holds 10 bytes"):
+        dg._fits(t, 11, "t")
+    f = torch.zeros((3, 4), dtype=torch.float32)
+    dg._fits(f[1:], 32, "f")
+    with pytest.raises(ValueError):
+        dg._fits(f[1:], 33, "f")

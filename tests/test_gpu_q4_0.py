@@ -79,6 +79,19 @@ def test_q4_0_m1_variants(dg, dev, orc, launch):
     assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, str(launch))
 
 
+@pytest.mark.parametrize("N,launch", [(300, dict(variant=13, grid=1, block=64)),
+                                      (129, dict(variant=13, grid=1, block=64, unroll=3)),
+                                      (1000, dict(variant=13, grid=2, block=128, unroll=4)),
+                                      (64, dict(variant=13, grid=1, block=64))])
+def test_q4_0_m1_many_rows_per_wave(dg, dev, orc, N, launch):
+    """One wave computing more than 64 rows: its results are stored 64 rows at
+    a time, then the remainder."""
+    K = 512
+    Wq, Xq = _operands(orc, 227, N, K, 1)
+    got = _gpu(dg, dev, Wq, Xq, N, K, 1, launch=launch)
+    assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"{N} {launch}")
+
+
 @pytest.mark.parametrize("N,K", [(1, 256), (7, 4096), (70, 4352), (33, 8192), (64, 12288), (130, 2304)])
 @pytest.mark.parametrize("launch", [dict(variant=13), dict(variant=13, grid=2, block=128),
                                     dict(variant=13, unroll=2, grid=3, block=64),
@@ -90,18 +103,49 @@ def test_q4_0_lds_row_copy_shapes(dg, dev, orc, N, K, launch):
     assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"{N}x{K} {launch}")
 
 
-MFMA_CFGS = [dict(variant=14)] + [dict(variant=14, unroll=cb + 100 * ks) for cb in (16, 32) for ks in (1, 2, 4)]
+# Matrix-core configurations the library builds: (RT row tiles, KS parts of K,
+# DEPTH, CB) -> the largest column count they serve (their LDS must fit one
+# workgroup).  Launch override: unroll = RT*10000 + KS*100 + DEPTH*10 + CB/8.
+MFMA_TABLE = {(1, 16, 1, 8): 16, (4, 4, 2, 8): 8, (1, 8, 2, 8): 16,
+              (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (2, 4, 2, 8): 24, (4, 2, 2, 8): 24, (8, 1, 2, 8): 24,
+              (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24, (1, 4, 2, 8): 24}
+
+
+def _mfma_unroll(rt, ks, d, cb):
+    return rt * 10000 + ks * 100 + d * 10 + cb // 8
+
+
+MFMA_CFGS = [dict(variant=14)] + [dict(variant=14, unroll=_mfma_unroll(*c)) for c in MFMA_TABLE]
+
+
+def _mfma_supported(launch, M):
+    u = launch.get("unroll", 0)
+    if not u:
+        return True
+    return M <= MFMA_TABLE[(u // 10000, (u // 100) % 100, (u // 10) % 10, (u % 10) * 8)]
 
 
 @pytest.mark.parametrize("launch", MFMA_CFGS, ids=[str(v) for v in MFMA_CFGS])
 @pytest.mark.parametrize("N,K,M", [(37, 256, 2), (130, 4352, 7), (64, 8192, 16), (200, 2304, 17), (33, 12544, 24),
-                                   (16, 512, 3), (1, 1024, 24), (700, 4096, 12)])
+                                   (16, 512, 3), (1, 1024, 24), (700, 4096, 12), (90, 2560, 4), (50, 1792, 8),
+                                   (45, 3328, 1)])
 def test_q4_0_mfma_matches_oracle(dg, dev, orc, launch, N, K, M):
-    if launch.get("unroll") == 432 and M > 16:
-        pytest.skip("32-block chunks with four K parts and two column tiles exceed the LDS of one workgroup")
+    if not _mfma_supported(launch, M):
+        pytest.skip("configuration not built for this column count (LDS of one workgroup)")
     Wq, Xq = _operands(orc, 260, N, K, M)
     got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
     assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M), TOL, f"mfma {launch} {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("grid", [1, 3, 7])
+@pytest.mark.parametrize("unroll", [0, 11611, 40221, 40131])
+def test_q4_0_mfma_any_grid_covers_every_row_tile(dg, dev, orc, grid, unroll):
+    """A grid smaller than the number of row-tile groups loops over them."""
+    N, K, M = 333, 2304, 5
+    Wq, Xq = _operands(orc, 265, N, K, M)
+    launch = dict(variant=14, grid=grid, unroll=unroll)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
+    assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M), TOL, str(launch))
 
 
 @pytest.mark.parametrize("M,R", [(2, 1), (2, 2), (3, 4), (8, 1), (8, 2), (24, 1), (24, 2)])
@@ -148,11 +192,14 @@ def test_q4_0_overrides_beyond_kernel_limits_are_rejected(dg, dev):
     import torch
     N, K = 64, 8192
     W = torch.zeros(N * K // 32 * 18, dtype=torch.uint8, device=dev)
-    X = torch.zeros(2 * K // 32 * 36, dtype=torch.uint8, device=dev)
-    Y = torch.zeros(2 * N, dtype=torch.float32, device=dev)
+    X = torch.zeros(24 * K // 32 * 36, dtype=torch.uint8, device=dev)
+    Y = torch.zeros(24 * N, dtype=torch.float32, device=dev)
     for M, launch in ((1, dict(variant=11, block=512)), (1, dict(variant=13, block=1024)),
                       (2, dict(variant=11)), (2, dict(variant=13)), (1, dict(variant=12, block=128)),
-                      (5, dict(variant=12, unroll=4)), (1, dict(variant=99))):
+                      (5, dict(variant=12, unroll=4)), (1, dict(variant=99)),
+                      (4, dict(variant=14, unroll=124)), (4, dict(variant=14, unroll=21622)),
+                      (4, dict(variant=14, unroll=10412)), (4, dict(variant=14, unroll=10441)),
+                      (20, dict(variant=14, unroll=11611)), (20, dict(variant=14, unroll=10821))):
         with pytest.raises(dg.DGError) as e:
             dg.dg_gemv_q4_0(W, X, Y, N, K, M, launch=launch)
         assert e.value.status == dg.DG_ERR_ARG, launch

@@ -1,17 +1,24 @@
-"""dg_stream_read reads every byte exactly once: its checksum equals the
-oracle's wrapping word sum (GPU)."""
+"""dg_stream_read reads every byte exactly once: the wrapping sum of its
+per-workgroup partials equals the oracle's wrapping word sum (GPU)."""
 import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
 
 
+def _total(parts):
+    return int(parts.cpu().numpy().view(np.uint32).astype(np.uint64).sum() % 2**32)
+
+
 def _run(dg, dev, buf, nbytes, **kw):
     import torch
-    cs = torch.zeros(1, dtype=torch.int32, device=dev)
-    dg.dg_stream_read(buf, cs, nbytes=nbytes, **kw)
+    grid = kw.get("grid_blocks") or dg.DG_READ_DEFAULT_GRID
+    # one spare entry past the grid, poisoned: the probe must not write it
+    parts = torch.full((grid + 1,), -1, dtype=torch.int32, device=dev)
+    dg.dg_stream_read(buf, parts[:grid], nbytes=nbytes, **kw)
     torch.cuda.synchronize()
-    return int(cs.cpu().numpy().view(np.uint32)[0])
+    assert int(parts[grid]) == -1
+    return _total(parts[:grid])
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096 + 16, 1 << 20, (64 << 20) + 48])
@@ -28,15 +35,21 @@ def test_stream_checksum_matches_oracle(dg, dev, orc, nbytes, launch):
     assert _run(dg, dev, buf, nbytes, **launch) == orc.checksum_u32(words)
 
 
-def test_stream_checksum_accumulates(dg, dev, orc):
+def test_stream_partials_overwrite_and_cover_every_workgroup(dg, dev, orc):
+    """Every one of the G partials is written (stale values are overwritten),
+    whether or not its workgroup had bytes to read."""
     import torch
     words = np.arange(1 << 16, dtype=np.uint32)
     buf = torch.from_numpy(words.view(np.int32)).to(dev)
-    cs = torch.zeros(1, dtype=torch.int32, device=dev)
-    dg.dg_stream_read(buf, cs)
-    dg.dg_stream_read(buf, cs)
-    torch.cuda.synchronize()
-    assert int(cs.cpu().numpy().view(np.uint32)[0]) == (2 * orc.checksum_u32(words)) % 2**32
+    for grid in (0, 3, 5000):
+        g = grid or dg.DG_READ_DEFAULT_GRID
+        parts = torch.full((g,), 12345, dtype=torch.int32, device=dev)
+        dg.dg_stream_read(buf, parts, grid_blocks=grid, block_threads=256)
+        dg.dg_stream_read(buf, parts, grid_blocks=grid, block_threads=256)
+        torch.cuda.synchronize()
+        assert _total(parts) == orc.checksum_u32(words), grid
+        if g == 5000:   # 64 Ki words read by 8 KiB wave steps: most workgroups have nothing to read
+            assert int((parts == 0).sum()) > 0
 
 
 def test_stream_full_size_closed_form(dg, dev):
