@@ -1,0 +1,90 @@
+"""Audit of the gfx950 assembly the library is built from (CPU; hipcc only).
+
+The batch1-cdna README's measurement rules check the generated assembly of
+every experiment, because several failure modes (a reduction hoisted out of a
+loop, DPP not emitted, a dot instruction lowered to plain arithmetic) give
+plausible timings and wrong conclusions.  These checks pin the instructions
+each kernel's design relies on, and forbid what must never appear:
+  * writes through the scalar data cache (scalar stores, scalar atomics,
+    scalar cache write-back or discard);
+  * packed fp32 arithmetic (the build disables it);
+  * register spills to scratch memory.
+"""
+import concurrent.futures as cf
+import os
+import re
+
+import pytest
+
+from memory_bound_decode_gemv_amd import _build
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    d = tmp_path_factory.mktemp("asm")
+    srcs = _build.sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        outs = list(ex.map(lambda s: _build.device_asm(s, str(d / (os.path.basename(s) + ".s"))), srcs))
+    return {os.path.basename(s): open(o).read() for s, o in zip(srcs, outs)}
+
+
+def _kernels(text):
+    """(mangled name, body) of every kernel in an assembly file."""
+    out = []
+    for m in re.finditer(r"^(_Z\w+):", text, re.M):
+        end = text.find("s_endpgm", m.end())
+        out.append((m.group(1), text[m.end():end]))
+    return out
+
+
+def test_every_source_has_kernels(asm):
+    for name, text in asm.items():
+        if name != "api.hip":
+            assert _kernels(text), name
+
+
+def test_no_scalar_cache_writes(asm):
+    bad = re.compile(r"^\s*(s_store|s_buffer_store|s_atomic|s_buffer_atomic|s_dcache_wb|s_dcache_discard|"
+                     r"s_scratch_store)", re.M)
+    for name, text in asm.items():
+        assert not bad.search(text), name
+
+
+def test_no_packed_fp32(asm):
+    bad = re.compile(r"^\s*v_pk_(add|mul|fma|mov)_f32", re.M)
+    for name, text in asm.items():
+        assert not bad.search(text), name
+
+
+def test_no_spills_or_scratch(asm):
+    for name, text in asm.items():
+        for m in re.finditer(r"\.private_segment_fixed_size:\s*(\d+)", text):
+            assert int(m.group(1)) == 0, name
+        for m in re.finditer(r"\.vgpr_spill_count:\s*(\d+)", text):
+            assert int(m.group(1)) == 0, name
+
+
+def test_dense_gemv_uses_dot2_nontemporal_loads_and_dpp(asm):
+    t = asm["gemv_dense.hip"]
+    assert "v_dot2_f32_f16" in t or "v_dot2c_f32_f16" in t
+    assert "v_dot2_f32_bf16" in t or "v_dot2c_f32_bf16" in t
+    assert re.search(r"global_load_dwordx4 .* nt", t)
+    assert "row_shr:1" in t and "row_bcast:15" in t and "row_bcast:31" in t
+
+
+def test_q4_kernels_use_dot4_lds_dma_and_matrix_cores(asm):
+    m1 = asm["gemv_q4_0_m1.hip"]
+    assert "global_load_lds_dwordx4" in m1
+    assert "v_dot4_i32_i8" in m1 or "v_dot4c_i32_i8" in m1
+    assert "flat_load" not in m1           # LDS addresses stay LDS addresses
+    mf = asm["gemv_q4_0_mfma.hip"]
+    assert "v_mfma_i32_16x16x32_i8" in mf
+    assert "global_load_lds_dwordx4" in mf
+    assert "flat_load" not in mf
+    assert not re.search(r"v_accvgpr_read", mf)   # results stay in VGPRs
+
+
+def test_stream_probe_has_no_atomics(asm):
+    t = asm["stream_read.hip"]
+    assert "global_atomic" not in t
+    assert re.search(r"global_load_dwordx4 .* nt", t)
