@@ -577,7 +577,7 @@ def suite_argmax(dg, torch, emit, ceil_gbps):
         ncold = copies_for(4 * R * C) if 4 * R * C >= LLC_BYTES // 4 else 1
         xs = [synth.gpu_uniform((5, synth.KIND_X, c, 0), (R, C), -10.0, 10.0) for c in range(ncold)]
         idx = torch.empty(R, dtype=torch.int64, device="cuda")
-        ws = torch.empty(max(8, dg.dg_argmax_workspace_bytes(R, C)), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(max(8, dg.dg_argmax_workspace_bytes(R, C)), dtype=torch.uint8, device="cuda")
         nb = 4 * R * C + 8 * R
         calls = [(lambda: dg.dg_argmax_rows(xs[0], idx, ws=ws))] * 20
         us, iqr = time_per_call(calls)
@@ -598,7 +598,7 @@ def suite_tail(dg, torch, emit, ceil_gbps):
     Wb, xb = dense_copies(4, N, K, nc, torch.bfloat16)
     logits = torch.empty(N, dtype=torch.float32, device="cuda")
     idx = torch.empty(1, dtype=torch.int64, device="cuda")
-    ws = torch.empty(dg.dg_argmax_workspace_bytes(1, N), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(dg.dg_argmax_workspace_bytes(1, N), dtype=torch.uint8, device="cuda")
     calls = []
     for c in range(8):
         calls.append(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, logits))

@@ -19,7 +19,7 @@ def _gpu_argmax(dg, dev, x, C=None, ld=None):
     ld = x.shape[1] if ld is None else ld
     t = torch.from_numpy(x).to(dev)
     idx = torch.full((R,), -1, dtype=torch.int64, device=dev)
-    ws = torch.empty(max(1, dg.dg_argmax_workspace_bytes(R, C)), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(max(1, dg.dg_argmax_workspace_bytes(R, C)), dtype=torch.uint8, device=dev)
     dg.dg_argmax_rows(t, idx, R=R, C=C, ld=ld, ws=ws)
     torch.cuda.synchronize()
     return idx.cpu().numpy()
@@ -91,3 +91,18 @@ def test_argmax_workspace_contract(dg, dev):
     with pytest.raises(dg.DGError) as e:
         dg.dg_argmax_rows(x, idx, ws=small)
     assert e.value.status == dg.DG_ERR_WORKSPACE
+
+
+def test_argmax_workspace_contents_do_not_matter_and_it_is_reusable(dg, dev, orc):
+    """One workspace, filled with garbage before the first call, serves calls of
+    different shapes in a row."""
+    import torch
+    shapes = [(3, 70000), (1, 128000), (40, 5000), (2, 4), (7, 33333), (1, 1)]
+    size = max(dg.dg_argmax_workspace_bytes(R, C) for R, C in shapes)
+    ws = torch.full((size,), 0xAB, dtype=torch.uint8, device=dev)
+    for i, (R, C) in enumerate(shapes * 2):
+        x, _ = synth.argmax_logits(500 + i, R, C)
+        idx = torch.full((R,), -1, dtype=torch.int64, device=dev)
+        dg.dg_argmax_rows(torch.from_numpy(x).to(dev), idx, ws=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), orc.argmax_rows(x)), (R, C)

@@ -39,7 +39,7 @@ def test_graph_replays_match_eager(dg, dev):
     y = torch.empty(N, dtype=torch.float16, device=dev)
     yq = torch.empty(Nq, dtype=torch.float32, device=dev)
     idx = torch.empty(1, dtype=torch.int64, device=dev)
-    ws = torch.empty(dg.dg_argmax_workspace_bytes(1, Nq), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(dg.dg_argmax_workspace_bytes(1, Nq), dtype=torch.uint8, device=dev)
 
     def step():
         dg.dg_quantize_q8_1(xf, Xq, 1, Kq)

@@ -16,7 +16,7 @@ def test_greedy_tail_lm_head_then_argmax(dg, dev, orc):
     x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
     logits = torch.empty(N, dtype=torch.float32, device=dev)
     idx = torch.empty(1, dtype=torch.int64, device=dev)
-    ws = torch.empty(dg.dg_argmax_workspace_bytes(1, N), dtype=torch.uint8, device=dev)
+    ws = torch.zeros(dg.dg_argmax_workspace_bytes(1, N), dtype=torch.uint8, device=dev)
     dg.dg_gemv_bf16(W, x, logits)
     dg.dg_argmax_rows(logits.view(1, N), idx, ws=ws)
     torch.cuda.synchronize()
