@@ -517,7 +517,7 @@ def suite_q4_m1(dg, torch, emit, ceil_gbps):
                                       for g in (256, 512, 768, 1024, 2048, 7168) for b in (64, 128, 256)] + \
                [(f"lds R{r}", dict(variant=12, unroll=r)) for r in (1, 2, 4)] + \
                [(f"ldsrow d{d} g{g} b{b}", dict(variant=13, grid=g, block=b, unroll=d))
-                for d in (2, 3, 4) for g in (0, 512, 768, 1024, 2048) for b in (128, 256)]
+                for d in (2, 3, 4) for g in (0, 512, 768, 1024, 1792, 2048, 3584, 7168) for b in (128, 256)]
     for lname, launch in launches:
         calls = [(lambda c=c, launch=launch: dg.dg_gemv_q4_0(Wq[c % nq], Xq, Yq, Q4_N, Q4_K, 1, launch=launch))
                  for c in range(3 * nq)]

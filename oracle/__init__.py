@@ -73,6 +73,9 @@ def _bind(lib):
     lib.orc_dequant_q8_1_block.argtypes = [P, P]
     lib.orc_quantize_q4_0.argtypes = [P, P, I64, I64]
     lib.orc_quantize_q8_1.argtypes = [P, P, I64, I64]
+    lib.orc_gemv_q8_0_q8_1.argtypes = [P, P, P, I64, I64, I64]
+    lib.orc_dequant_q8_0_block.argtypes = [P, P]
+    lib.orc_quantize_q8_0.argtypes = [P, P, I64, I64]
     lib.orc_argmax_rows.argtypes = [P, P, I64, I64, I64]
     lib.orc_checksum_u32.argtypes = [P, ctypes.c_size_t]
     lib.orc_checksum_u32.restype = ctypes.c_uint32
@@ -202,6 +205,39 @@ def quantize_q8_1(x: np.ndarray) -> np.ndarray:
     assert K % 32 == 0
     out = np.zeros((M, K // 32 * 36), dtype=np.uint8)
     _load().orc_quantize_q8_1(_ptr(x), _ptr(out), M, K)
+    return out
+
+
+# ---- Q8_0 x Q8_1 -----------------------------------------------------------
+
+def gemv_q8_0_q8_1(Wq: np.ndarray, Xq: np.ndarray, N: int, K: int, M: int) -> np.ndarray:
+    """fp64 Y[M][N] from Q8_0 weight bytes and Q8_1 activation bytes."""
+    assert K % 32 == 0
+    W = _c(Wq, np.uint8).reshape(-1)
+    X = _c(Xq, np.uint8).reshape(-1)
+    assert W.size >= N * (K // 32) * 34 and X.size >= M * (K // 32) * 36
+    Y = np.zeros((M, N), dtype=np.float64)
+    _load().orc_gemv_q8_0_q8_1(_ptr(W), _ptr(X), _ptr(Y), N, K, M)
+    return Y
+
+
+def dequant_q8_0_block(blk: bytes | np.ndarray) -> np.ndarray:
+    b = _c(np.frombuffer(bytes(blk), dtype=np.uint8) if isinstance(blk, (bytes, bytearray)) else blk, np.uint8)
+    assert b.size >= 34
+    out = np.zeros(32, dtype=np.float64)
+    _load().orc_dequant_q8_0_block(_ptr(b), _ptr(out))
+    return out
+
+
+def quantize_q8_0(w: np.ndarray) -> np.ndarray:
+    """w: float32 [N][K] -> Q8_0 bytes, shape [N, K//32*34]."""
+    w = _c(w, np.float32)
+    if w.ndim == 1:
+        w = w.reshape(1, -1)
+    N, K = w.shape
+    assert K % 32 == 0
+    out = np.zeros((N, K // 32 * 34), dtype=np.uint8)
+    _load().orc_quantize_q8_0(_ptr(w), _ptr(out), N, K)
     return out
 
 

@@ -222,6 +222,67 @@ void orc_quantize_q8_1(const float* xs, uint8_t* Xq, int64_t M, int64_t K)
 }
 
 /* ---------------------------------------------------------------------- */
+/* Q8_0 x Q8_1                                                            */
+/* ---------------------------------------------------------------------- */
+
+void orc_dequant_q8_0_block(const uint8_t* blk, double out[32])
+{
+    const double d = orc_half_to_double(load_u16le(blk));
+    const int8_t* q = (const int8_t*)(blk + 2);
+    for (int j = 0; j < 32; ++j) out[j] = (double)q[j] * d;
+}
+
+void orc_gemv_q8_0_q8_1(const uint8_t* Wq, const uint8_t* Xq, double* Y,
+                        int64_t N, int64_t K, int64_t M)
+{
+    const int64_t nb = K / 32;
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t b = 0; b < nb; ++b) {
+                const uint8_t* wb = Wq + (n * nb + b) * 34;
+                const uint8_t* xb = Xq + (m * nb + b) * 36;
+                const int8_t* qw = (const int8_t*)(wb + 2);
+                const int8_t* q8 = (const int8_t*)(xb + 4);
+                int32_t isum = 0;
+                for (int j = 0; j < 32; ++j) isum += (int32_t)qw[j] * q8[j];
+                const double dw = orc_half_to_double(load_u16le(wb));
+                const double d8 = orc_half_to_double(load_u16le(xb));
+                acc += dw * d8 * (double)isum;
+            }
+            Y[m * N + n] = acc;
+        }
+    }
+}
+
+void orc_quantize_q8_0(const float* w, uint8_t* Wq, int64_t N, int64_t K)
+{
+    const int64_t nb = K / 32;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < nb; ++b) {
+            const float* x = w + n * K + b * 32;
+            float amax = 0.0f;
+            for (int j = 0; j < 32; ++j) {
+                float a = fabsf(x[j]);
+                if (a > amax) amax = a;
+            }
+            const float d = amax / 127.0f;
+            uint8_t* blk = Wq + (n * nb + b) * 34;
+            store_u16le(blk, orc_float_to_half_rne(d));
+            for (int j = 0; j < 32; ++j) {
+                int c = 0;
+                if (d != 0.0f) {
+                    c = (int)roundf(x[j] / d);   /* halves away from zero */
+                    if (c > 127) c = 127;
+                    if (c < -127) c = -127;
+                }
+                blk[2 + j] = (uint8_t)(int8_t)c;
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* argmax                                                                 */
 /* ---------------------------------------------------------------------- */
 

@@ -94,6 +94,27 @@ void orc_dequant_q8_1_block(const uint8_t* blk, double out[32]);
 void orc_quantize_q4_0(const float* w, uint8_t* Wq, int64_t N, int64_t K);
 void orc_quantize_q8_1(const float* x, uint8_t* Xq, int64_t M, int64_t K);
 
+/* ---- Q8_0 x Q8_1 ---- */
+
+/* Q8_0 block, 34 bytes (GGUF): binary16 scale d, then 32 int8 codes; the
+ * weight's value is q * d.  W holds N rows of K/32 Q8_0 blocks; X and Y as
+ * for Q4_0 above:
+ *   Y[m][n] = sum_b dw(n,b) * d8(m,b) * sum_{j<32} qw(n,b,j) * q8(m,b,j)
+ * with the inner sum in exact integers and the rest in double ("The kernel
+ * that waited for itself" runs its Q8_0 model files through the same
+ * Q8_1-activation path as Q4_0).  K must be a multiple of 32. */
+void orc_gemv_q8_0_q8_1(const uint8_t* Wq, const uint8_t* Xq, double* Y,
+                        int64_t N, int64_t K, int64_t M);
+
+/* Decodes one Q8_0 block into 32 doubles (q * d). */
+void orc_dequant_q8_0_block(const uint8_t* blk, double out[32]);
+
+/* Q8_0 quantiser for test operands, per 32-weight block: a = max |x|;
+ * d = a / 127 in binary32; code q = x/d rounded half away from zero, clamped
+ * to [-127, 127]; a block of zeros gets d = 0 and codes 0; stored
+ * d = binary16(d).  w is [N][K]. */
+void orc_quantize_q8_0(const float* w, uint8_t* Wq, int64_t N, int64_t K);
+
 /* ---- argmax over rows ---- */
 
 /* idx[r] = the lowest c < C with x[r*ld + c] equal to the row maximum.

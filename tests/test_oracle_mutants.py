@@ -41,6 +41,16 @@ MUTANTS = [
     ("argmax last index wins ties", "if (isnan(v) || v > bv)", "if (isnan(v) || v >= bv)"),
     ("argmax ignores NaN", "if (isnan(v) || v > bv)", "if (v > bv)"),
     ("argmax ignores ld", "const float* row = x + r * ld;", "const float* row = x + r * C;"),
+    ("q8_0 codes read unsigned", "const int8_t* qw = (const int8_t*)(wb + 2);",
+     "const uint8_t* qw = (const uint8_t*)(wb + 2);"),
+    ("q8_0 weight scale ignored", "acc += dw * d8 * (double)isum;", "acc += d8 * (double)isum;"),
+    ("q8_0 block stride 32 bytes", "const uint8_t* wb = Wq + (n * nb + b) * 34;",
+     "const uint8_t* wb = Wq + (n * nb + b) * 32;"),
+    ("q8_0 activation scale taken from column 0",
+     "const uint8_t* wb = Wq + (n * nb + b) * 34;\n                const uint8_t* xb = Xq + (m * nb + b) * 36;",
+     "const uint8_t* wb = Wq + (n * nb + b) * 34;\n                const uint8_t* xb = Xq + b * 36;"),
+    ("q8_0 quantiser rounds half to even", "c = (int)roundf(x[j] / d);   /* halves away from zero */",
+     "c = (int)rintf(x[j] / d);"),
     ("checksum xor instead of add", "for (size_t i = 0; i < n; ++i) s += w[i];", "for (size_t i = 0; i < n; ++i) s ^= w[i];"),
 ]
 

@@ -295,6 +295,83 @@ def test_quantiser_properties_on_random_blocks(orc):
 
 
 # ---------------------------------------------------------------------------
+# Q8_0 x Q8_1
+# ---------------------------------------------------------------------------
+
+def _golden_q8_0():
+    with open(os.path.join(GOLDEN, "q8_0_q8_1_worked.json")) as f:
+        return json.load(f)
+
+
+def _py_decode_q8_0(blk):
+    d = Fraction(float(np.frombuffer(bytes(blk[:2]), dtype=np.float16)[0]))
+    return [d * int(v) for v in np.frombuffer(bytes(blk[2:34]), dtype=np.int8)]
+
+
+def _random_q8_0_blocks(g, nblk):
+    b = g.integers(0, 256, size=(nblk, 34), dtype=np.uint8)
+    b[:, 2:][b[:, 2:] == 0x80] = 0x81          # codes stay in [-127, 127]
+    scales = (g.standard_normal(nblk) * 0.3).astype(np.float16).view(np.uint16)
+    b[:, 0] = scales & 0xFF
+    b[:, 1] = scales >> 8
+    return b
+
+
+def test_q8_0_worked_blocks(orc):
+    for ex in _golden_q8_0()["dot_examples"]:
+        W, X = _hex(ex["q8_0_block_hex"]), _hex(ex["q8_1_block_hex"])
+        assert W.size == 34 and X.size == 36
+        y = orc.gemv_q8_0_q8_1(W, X, N=1, K=32, M=1)
+        assert y[0, 0] == ex["y"], ex["name"]
+
+
+def test_q8_0_against_brute_force_dequantise_then_dot(orc):
+    g = np.random.default_rng(31)
+    N, K, M = 3, 128, 2
+    nb = K // 32
+    W = _random_q8_0_blocks(g, N * nb)
+    X = _random_blocks(g, M * nb, "q8")
+    Y = orc.gemv_q8_0_q8_1(W, X, N=N, K=K, M=M)
+    for m in range(M):
+        xv = sum((_py_decode_q8_1(X[m * nb + b]) for b in range(nb)), [])
+        for n in range(N):
+            wv = sum((_py_decode_q8_0(W[n * nb + b]) for b in range(nb)), [])
+            exact = sum((a * c for a, c in zip(wv, xv)), Fraction(0))
+            assert abs(Fraction(float(Y[m, n])) - exact) <= abs(exact) * Fraction(nb, 2 ** 52) + Fraction(1, 2 ** 1000)
+    for blk in W[:6]:
+        assert [Fraction(v) for v in orc.dequant_q8_0_block(blk)] == _py_decode_q8_0(blk)
+
+
+def test_q8_0_invariants(orc):
+    g = np.random.default_rng(37)
+    N, K = 4, 128
+    nb = K // 32
+    W = _random_q8_0_blocks(g, N * nb)
+    X1 = _random_blocks(g, nb, "q8")
+    X = np.concatenate([X1, X1])
+    Y = orc.gemv_q8_0_q8_1(W, X, N=N, K=K, M=2)
+    assert np.array_equal(Y[0], Y[1])
+    # negating every weight code (exact for codes in [-127, 127]) negates y exactly
+    Wn = W.copy()
+    Wn[:, 2:] = (-(W[:, 2:].view(np.int8).astype(np.int16))).astype(np.int8).view(np.uint8)
+    assert np.array_equal(orc.gemv_q8_0_q8_1(Wn, X1, N=N, K=K, M=1)[0], -Y[0])
+
+
+def test_q8_0_quantiser_worked_blocks_and_properties(orc):
+    for ex in _golden_q8_0()["q8_0_quantiser_examples"]:
+        got = orc.quantize_q8_0(np.array(ex["x"], dtype=np.float32).reshape(1, 32))
+        assert bytes(got.reshape(-1)) == bytes(_hex(ex["block_hex"])), ex["name"]
+    g = np.random.default_rng(41)
+    w = g.standard_normal((16, 256)).astype(np.float32)
+    for blk, x in zip(orc.quantize_q8_0(w).reshape(-1, 34), w.reshape(-1, 32)):
+        d32 = np.float32(np.max(np.abs(x))) / np.float32(127.0)
+        q = np.frombuffer(bytes(blk[2:]), np.int8).astype(np.int64)
+        assert np.frombuffer(bytes(blk[:2]), np.float16)[0] == np.float16(d32)
+        assert abs(q[np.argmax(np.abs(x))]) == 127
+        assert np.all(np.abs(x - q * float(d32)) <= float(d32) * (0.5 + 1e-5))
+
+
+# ---------------------------------------------------------------------------
 # argmax
 # ---------------------------------------------------------------------------
 
