@@ -156,6 +156,21 @@ def q4_copies(cfg, N, K, ncopies):
     return Ws
 
 
+def q8_0_copies(cfg, N, K, ncopies):
+    import synth
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    Ws = []
+    for c in range(ncopies):
+        w = synth.gpu_normal((cfg, synth.KIND_W, c, 0), (N, K), 1.0, torch.float32)
+        Wq = torch.empty(N * (K // 32) * 34, dtype=torch.uint8, device="cuda")
+        dg.dg_quantize_q8_0(w, Wq, N, K)
+        torch.cuda.synchronize()
+        del w
+        Ws.append(Wq)
+    return Ws
+
+
 def q8_columns(cfg, K, M):
     import synth
     import memory_bound_decode_gemv_amd as dg
@@ -418,6 +433,8 @@ def suite(args):
         suite_q4_m1(dg, torch, emit, ceil_gbps)
     if want("q4m"):
         suite_q4_small_m(dg, torch, emit, ceil_gbps)
+    if want("q8"):
+        suite_q8_0(dg, torch, emit, ceil_gbps)
     if want("argmax"):
         suite_argmax(dg, torch, emit, ceil_gbps)
     if want("tail"):
@@ -570,6 +587,44 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
 
 
 
+def bytes_q8_0(N, K, M):
+    return 34 * N * K // 32 + M * 36 * K // 32 + 4 * M * N
+
+
+def suite_q8_0(dg, torch, emit, ceil_gbps):
+    """Q8_0 x Q8_1: M = 1 at the 70B MLP shape (default and row-buffer depths),
+    then M = 1..24 on the decoder shapes with the default dispatch."""
+    nq = copies_for(34 * Q4_N * Q4_K // 32)
+    Wq = q8_0_copies(4, Q4_N, Q4_K, nq)
+    Xq = q8_columns(4, Q4_K, 1)
+    Yq = torch.empty(Q4_N, dtype=torch.float32, device="cuda")
+    for lname, launch in [("default", None)] + [(f"ldsrow d{d} g{g} b{b}", dict(variant=21, grid=g, block=b, unroll=d))
+                                                for d in (2, 3) for g in (0, 1024) for b in (128, 256)]:
+        calls = [(lambda c=c, launch=launch: dg.dg_gemv_q8_0(Wq[c % nq], Xq, Yq, Q4_N, Q4_K, 1, launch=launch))
+                 for c in range(3 * nq)]
+        us, iqr = time_per_call(calls)
+        emit(record(f"gemv_q8_0 {Q4_N}x{Q4_K} M=1", us, iqr, bytes_q8_0(Q4_N, Q4_K, 1), ceil_gbps, variant=lname,
+                    copies=nq))
+    del Wq
+    torch.cuda.empty_cache()
+    for (N, K) in [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)]:
+        nc = copies_for(34 * N * K // 32)
+        Wq = q8_0_copies(5, N, K, nc)
+        prev = None
+        for M in (1, 2, 4, 8, 12, 16, 24):
+            Xq = q8_columns(5, K, M)
+            Y = torch.empty(M * N, dtype=torch.float32, device="cuda")
+            calls = [(lambda c=c: dg.dg_gemv_q8_0(Wq[c % nc], Xq, Y, N, K, M)) for c in range(max(nc, 20))]
+            us, iqr = time_per_call(calls)
+            cps = M / (us * 1e-6)
+            dip = None if prev is None else round(cps / prev - 1.0, 4)
+            prev = cps
+            emit(record(f"gemv_q8_0 {N}x{K}", us, iqr, bytes_q8_0(N, K, M), ceil_gbps, M=M, copies=nc,
+                        variant="default", columns_per_s=round(cps, 1), change_vs_prev_M=dip))
+        del Wq
+        torch.cuda.empty_cache()
+
+
 def suite_argmax(dg, torch, emit, ceil_gbps):
     # argmax: hot (one buffer) and cold (rotated copies for the 256 MB shape)
     import synth
@@ -649,7 +704,7 @@ def main():
     ap.add_argument("--profile-kernels", action="store_true",
                     help="launch each profiled kernel eagerly on known workloads (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
-                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,argmax,tail")
+                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q8,argmax,tail")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     args = ap.parse_args()

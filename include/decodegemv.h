@@ -143,7 +143,25 @@ dg_status dg_gemv_q4_0(const void* Wq, const void* Xq, float* Y,
                        int64_t N, int64_t K, int M, dg_stream stream);
 
 /* ------------------------------------------------------------------------
- * Quantisers (the step before dg_gemv_q4_0)
+ * Q8_0 weights x Q8_1 activations, M = 1..24 activation columns
+ *
+ *   Y[m][n] = sum_b dw(n,b) * d8(m,b) * sum_{j<32} qw(n,b,j) * q8(m,b,j)
+ *
+ * The 8-bit weight format that "The kernel that waited for itself" runs next
+ * to Q4_0 through the same Q8_1-activation path (its four-model comparison).
+ * Exact int32 inner sums, fp32 scaling and sum over blocks.
+ *
+ *   Wq  device, N rows of K/32 Q8_0 blocks, 34 bytes each (binary16 d, then
+ *       32 int8 codes), rows packed back to back; 16-byte aligned.
+ *   Xq, Y, N, K, M  as for dg_gemv_q4_0 (Xq 16-byte aligned, K % 256 == 0,
+ *       M <= 24).
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+dg_status dg_gemv_q8_0(const void* Wq, const void* Xq, float* Y,
+                       int64_t N, int64_t K, int M, dg_stream stream);
+
+/* ------------------------------------------------------------------------
+ * Quantisers (the step before dg_gemv_q4_0 / dg_gemv_q8_0)
  *
  * Q8_1, per 32-activation block: a = max|x|; d = a/127 (fp32); q = x/d
  * rounded half away from zero, clamped to [-127, 127] (d = 0 gives q = 0);
@@ -151,19 +169,24 @@ dg_status dg_gemv_q4_0(const void* Wq, const void* Xq, float* Y,
  * Q4_0, per 32-weight block: m = the first element of largest |x|, sign
  * kept; d = m/-8 (fp32); q = min(15, floor(x/d + 8.5)) (d = 0 gives q = 8);
  * stored d = binary16(d).
+ * Q8_0, per 32-weight block: a = max|x|; d = a/127 (fp32); q = x/d rounded
+ * half away from zero, clamped to [-127, 127] (d = 0 gives q = 0); stored
+ * d = binary16(d).
  * The per-call conversion cost of activations is the subject of the
  * "Capability Gain" paper's note on unfused conversion; the formats are those
  * of the Q4_0/Q8_1 harness in "The kernel that waited for itself".
  *
  *   x / w   device float32 [M][K] / [N][K], 16-byte aligned, rows packed.
- *   Xq / Wq device output, layouts as for dg_gemv_q4_0; Xq 4-byte aligned,
- *           Wq 2-byte aligned.
+ *   Xq / Wq device output, layouts as for dg_gemv_q4_0 / dg_gemv_q8_0; Xq
+ *           4-byte aligned, Wq 2-byte aligned.
  *   K       multiple of 32.
  * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_HIP.
  * ------------------------------------------------------------------------ */
 dg_status dg_quantize_q8_1(const float* x, void* Xq, int64_t M, int64_t K,
                            dg_stream stream);
 dg_status dg_quantize_q4_0(const float* w, void* Wq, int64_t N, int64_t K,
+                           dg_stream stream);
+dg_status dg_quantize_q8_0(const float* w, void* Wq, int64_t N, int64_t K,
                            dg_stream stream);
 
 /* ------------------------------------------------------------------------
@@ -209,7 +232,11 @@ typedef struct {
     int unroll;    /* loads in flight per lane per step, 0 = default;
                       dense DG_VARIANT_DENSE_WIDE: U + 100*(S-1) also splits
                       each row's K over S in {1,2,4} waves of a workgroup;
-                      Q4_0 DG_VARIANT_Q4_LDS: rows per wave (1, 2, 4)       */
+                      Q4_0 DG_VARIANT_Q4_LDS: rows per wave (1, 2, 4);
+                      *_LDSROW: row buffers per wave (2..4);
+                      *_MFMA: RT*10000 + KS*100 + DEPTH*10 + CB/8 (row
+                      tiles and K parts per workgroup, pipeline depth,
+                      blocks per chunk)                                      */
 } dg_launch;
 
 enum {
@@ -222,7 +249,10 @@ enum {
     DG_VARIANT_Q4_REGS = 11,        /* activations in registers, one row per wave (M = 1)       */
     DG_VARIANT_Q4_LDS = 12,         /* activations staged in LDS, several rows per wave          */
     DG_VARIANT_Q4_LDSROW = 13,      /* M = 1: weight rows copied to LDS with coalesced loads     */
-    DG_VARIANT_Q4_MFMA = 14         /* int8 matrix cores, 16 rows x 16 columns per instruction   */
+    DG_VARIANT_Q4_MFMA = 14,        /* int8 matrix cores, 16 rows x 16 columns per instruction   */
+    /* Q8_0 */
+    DG_VARIANT_Q8_LDSROW = 21,      /* M = 1: weight rows copied to LDS (K <= 16384)             */
+    DG_VARIANT_Q8_MFMA = 22         /* int8 matrix cores                                          */
 };
 
 dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K,
@@ -230,6 +260,8 @@ dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64
 dg_status dg_gemv_bf16_ex(const void* W, const void* x, float* y, int64_t N, int64_t K,
                           int64_t ldw, const dg_launch* cfg, dg_stream stream);
 dg_status dg_gemv_q4_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K,
+                          int M, const dg_launch* cfg, dg_stream stream);
+dg_status dg_gemv_q8_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K,
                           int M, const dg_launch* cfg, dg_stream stream);
 
 #ifdef __cplusplus

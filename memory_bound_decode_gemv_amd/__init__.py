@@ -38,6 +38,8 @@ DG_VARIANT_Q4_REGS = 11
 DG_VARIANT_Q4_LDS = 12
 DG_VARIANT_Q4_LDSROW = 13
 DG_VARIANT_Q4_MFMA = 14
+DG_VARIANT_Q8_LDSROW = 21
+DG_VARIANT_Q8_MFMA = 22
 
 # Every symbol include/decodegemv.h declares.
 EXPORTED = (
@@ -46,6 +48,7 @@ EXPORTED = (
     "dg_quantize_q8_1", "dg_quantize_q4_0",
     "dg_argmax_workspace_bytes", "dg_argmax_rows",
     "dg_gemv_f16_ex", "dg_gemv_bf16_ex", "dg_gemv_q4_0_ex",
+    "dg_gemv_q8_0", "dg_gemv_q8_0_ex", "dg_quantize_q8_0",
 )
 
 
@@ -108,14 +111,16 @@ def _lib():
         getattr(lib, n).restype = st
         getattr(lib, n + "_ex").argtypes = [P, P, P, I64, I64, I64, ctypes.POINTER(dg_launch), P]
         getattr(lib, n + "_ex").restype = st
-    lib.dg_gemv_q4_0.argtypes = [P, P, P, I64, I64, I32, P]
-    lib.dg_gemv_q4_0.restype = st
-    lib.dg_gemv_q4_0_ex.argtypes = [P, P, P, I64, I64, I32, ctypes.POINTER(dg_launch), P]
-    lib.dg_gemv_q4_0_ex.restype = st
+    for n in ("dg_gemv_q4_0", "dg_gemv_q8_0"):
+        getattr(lib, n).argtypes = [P, P, P, I64, I64, I32, P]
+        getattr(lib, n).restype = st
+        getattr(lib, n + "_ex").argtypes = [P, P, P, I64, I64, I32, ctypes.POINTER(dg_launch), P]
+        getattr(lib, n + "_ex").restype = st
     lib.dg_quantize_q8_1.argtypes = [P, P, I64, I64, P]
     lib.dg_quantize_q8_1.restype = st
-    lib.dg_quantize_q4_0.argtypes = [P, P, I64, I64, P]
-    lib.dg_quantize_q4_0.restype = st
+    for n in ("dg_quantize_q4_0", "dg_quantize_q8_0"):
+        getattr(lib, n).argtypes = [P, P, I64, I64, P]
+        getattr(lib, n).restype = st
     lib.dg_argmax_workspace_bytes.argtypes = [I64, I64]
     lib.dg_argmax_workspace_bytes.restype = ctypes.c_size_t
     lib.dg_argmax_rows.argtypes = [P, P, I64, I64, I64, P, ctypes.c_size_t, P]
@@ -236,26 +241,35 @@ def dg_gemv_bf16(W, x, y, N=None, K=None, ldw=None, launch=None, stream=None):
     return _dense("dg_gemv_bf16", W, x, y, N, K, ldw, launch, stream, torch.bfloat16, torch.float32)
 
 
-def dg_gemv_q4_0(Wq, Xq, Y, N, K, M, launch=None, stream=None):
-    """Y[M][N] (float32) from Q4_0 weight bytes and Q8_1 activation bytes (uint8 tensors)."""
+def _gemv_quant(name, block_bytes, Wq, Xq, Y, N, K, M, launch, stream):
     torch = _torch()
     _need(Wq, (torch.uint8,), "Wq")
     _need(Xq, (torch.uint8,), "Xq")
     _need(Y, (torch.float32,), "Y")
     N, K, M = int(N), int(K), int(M)
     if N > 0 and K > 0 and M > 0:
-        _fits(Wq, N * (K // 32) * 18, "Wq")
+        _fits(Wq, N * (K // 32) * block_bytes, "Wq")
         _fits(Xq, M * (K // 32) * 36, "Xq")
     if N > 0 and M > 0:
         _fits(Y, M * N * 4, "Y")
     lib = _lib()
     if launch is None:
-        st = lib.dg_gemv_q4_0(_ptr(Wq), _ptr(Xq), _ptr(Y), int(N), int(K), int(M), _stream(stream))
+        st = getattr(lib, name)(_ptr(Wq), _ptr(Xq), _ptr(Y), N, K, M, _stream(stream))
     else:
-        st = lib.dg_gemv_q4_0_ex(_ptr(Wq), _ptr(Xq), _ptr(Y), int(N), int(K), int(M),
-                                 ctypes.byref(_cfg(**launch)), _stream(stream))
-    _check(st, "dg_gemv_q4_0")
+        st = getattr(lib, name + "_ex")(_ptr(Wq), _ptr(Xq), _ptr(Y), N, K, M, ctypes.byref(_cfg(**launch)),
+                                        _stream(stream))
+    _check(st, name)
     return Y
+
+
+def dg_gemv_q4_0(Wq, Xq, Y, N, K, M, launch=None, stream=None):
+    """Y[M][N] (float32) from Q4_0 weight bytes and Q8_1 activation bytes (uint8 tensors)."""
+    return _gemv_quant("dg_gemv_q4_0", 18, Wq, Xq, Y, N, K, M, launch, stream)
+
+
+def dg_gemv_q8_0(Wq, Xq, Y, N, K, M, launch=None, stream=None):
+    """Y[M][N] (float32) from Q8_0 weight bytes and Q8_1 activation bytes (uint8 tensors)."""
+    return _gemv_quant("dg_gemv_q8_0", 34, Wq, Xq, Y, N, K, M, launch, stream)
 
 
 def dg_quantize_q8_1(x, Xq, M, K, stream=None):
@@ -279,6 +293,18 @@ def dg_quantize_q4_0(w, Wq, N, K, stream=None):
         _fits(w, int(N) * int(K) * 4, "w")
         _fits(Wq, int(N) * (int(K) // 32) * 18, "Wq")
     _check(_lib().dg_quantize_q4_0(_ptr(w), _ptr(Wq), int(N), int(K), _stream(stream)), "dg_quantize_q4_0")
+    return Wq
+
+
+def dg_quantize_q8_0(w, Wq, N, K, stream=None):
+    """float32 [N][K] -> Q8_0 bytes (uint8 [N*K/32*34])."""
+    torch = _torch()
+    _need(w, (torch.float32,), "w")
+    _need(Wq, (torch.uint8,), "Wq")
+    if N > 0 and K > 0:
+        _fits(w, int(N) * int(K) * 4, "w")
+        _fits(Wq, int(N) * (int(K) // 32) * 34, "Wq")
+    _check(_lib().dg_quantize_q8_0(_ptr(w), _ptr(Wq), int(N), int(K), _stream(stream)), "dg_quantize_q8_0")
     return Wq
 
 

@@ -49,8 +49,8 @@ dg_status gemv_dense_checked(bool bf16, const void* W, const void* x, void* y, i
     return hip_status(e);
 }
 
-dg_status gemv_q4_0_checked(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K, int M,
-                            const dg_launch* cfg, dg_stream stream) {
+dg_status gemv_quant_checked(bool q8, const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                             const dg_launch* cfg, dg_stream stream) {
     if (N < 0 || N > kI32Max || K < 0 || K > kI32Max || K % 256 != 0 || M < 0 || M > 24)
         return DG_ERR_SHAPE;
     if (!launch_ok(cfg)) return DG_ERR_ARG;
@@ -64,7 +64,8 @@ dg_status gemv_q4_0_checked(const void* Wq, const void* Xq, float* Y, int64_t N,
                            (hipStream_t)stream, Y, n);
         return hip_status(hipGetLastError());
     }
-    hipError_t e = launch_gemv_q4_0(Wq, Xq, Y, (int)N, (int)K, M, cfg, (hipStream_t)stream);
+    hipError_t e = q8 ? launch_gemv_q8_0(Wq, Xq, Y, (int)N, (int)K, M, cfg, (hipStream_t)stream)
+                      : launch_gemv_q4_0(Wq, Xq, Y, (int)N, (int)K, M, cfg, (hipStream_t)stream);
     if (e == hipErrorInvalidValue && cfg && (cfg->variant || cfg->unroll || cfg->block)) return DG_ERR_ARG;
     return hip_status(e);
 }
@@ -152,12 +153,22 @@ dg_status dg_gemv_bf16_ex(const void* W, const void* x, float* y, int64_t N, int
 
 dg_status dg_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K, int M,
                        dg_stream stream) {
-    return gemv_q4_0_checked(Wq, Xq, Y, N, K, M, nullptr, stream);
+    return gemv_quant_checked(false, Wq, Xq, Y, N, K, M, nullptr, stream);
 }
 
 dg_status dg_gemv_q4_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K, int M,
                           const dg_launch* cfg, dg_stream stream) {
-    return gemv_q4_0_checked(Wq, Xq, Y, N, K, M, cfg, stream);
+    return gemv_quant_checked(false, Wq, Xq, Y, N, K, M, cfg, stream);
+}
+
+dg_status dg_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                       dg_stream stream) {
+    return gemv_quant_checked(true, Wq, Xq, Y, N, K, M, nullptr, stream);
+}
+
+dg_status dg_gemv_q8_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                          const dg_launch* cfg, dg_stream stream) {
+    return gemv_quant_checked(true, Wq, Xq, Y, N, K, M, cfg, stream);
 }
 
 dg_status dg_quantize_q8_1(const float* x, void* Xq, int64_t M, int64_t K, dg_stream stream) {
@@ -174,6 +185,14 @@ dg_status dg_quantize_q4_0(const float* w, void* Wq, int64_t N, int64_t K, dg_st
     if (!w || !Wq) return DG_ERR_NULL;
     if (!aligned(w, 16) || !aligned(Wq, 2)) return DG_ERR_MISALIGNED;
     return hip_status(launch_quantize_q4_0(w, Wq, N, K, (hipStream_t)stream));
+}
+
+dg_status dg_quantize_q8_0(const float* w, void* Wq, int64_t N, int64_t K, dg_stream stream) {
+    if (N < 0 || K < 0 || K % 32 != 0 || N * (K / 32) > kI32Max * 256LL) return DG_ERR_SHAPE;
+    if (N == 0 || K == 0) return DG_OK;
+    if (!w || !Wq) return DG_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(Wq, 2)) return DG_ERR_MISALIGNED;
+    return hip_status(launch_quantize_q8_0(w, Wq, N, K, (hipStream_t)stream));
 }
 
 size_t dg_argmax_workspace_bytes(int64_t R, int64_t C) { return argmax_workspace_bytes(R, C); }

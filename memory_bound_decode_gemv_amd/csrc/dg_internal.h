@@ -33,13 +33,20 @@ hipError_t launch_gemv_dense(bool bf16, const void* W, const void* x, void* y,
 hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int K, int M,
                             const dg_launch* cfg, hipStream_t s);
 // The M = 1 kernel with rows copied to LDS (depth = row buffers per wave) and
-// the matrix-core kernel for M = 2..24 (unroll = CB + 100 * KS); a zero
+// the matrix-core kernel for M = 2..24 (unroll = RT*10000 + KS*100 + DEPTH*10
+// + CB/8); a zero
 // depth, unroll, grid or block selects the default.
 hipError_t launch_q4_m1_ldsrow(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
                                int block, hipStream_t s);
 hipError_t launch_q4_mfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
                           hipStream_t s);
 
+hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int K, int M,
+                            const dg_launch* cfg, hipStream_t s);
+hipError_t launch_q8_mfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
+                          hipStream_t s);
+
+hipError_t launch_quantize_q8_0(const float* w, void* Wq, int64_t N, int64_t K, hipStream_t s);
 hipError_t launch_quantize_q8_1(const float* x, void* Xq, int64_t M, int64_t K, hipStream_t s);
 hipError_t launch_quantize_q4_0(const float* w, void* Wq, int64_t N, int64_t K, hipStream_t s);
 

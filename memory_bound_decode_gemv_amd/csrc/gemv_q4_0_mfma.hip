@@ -59,15 +59,45 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr long kNeg8 = (long)0xF8F8F8F8F8F8F8F8ull;   // eight int8 k-slots of -8
 
-template <int CB, int MP, int RT, int KS>
+// Weight formats.  decode(w, g, bop, d): from the dwords w of one block pair
+// in LDS, the B operands (k-slots 4g..4g+3 and 16+4g..16+4g+3, as int8) and
+// the fp32 scales of the pair's two blocks.
+struct FmtQ4_0 {   // 18-byte blocks: binary16 d, 16 bytes of nibbles; weight = (q - 8) d
+    static constexpr int kBlockBytes = 18;
+    static constexpr bool kOffset = true;   // codes 0..15 stand for q - 8
+    __device__ __forceinline__ static void decode(const uint32_t* w, int g, long bop[2], float d[2]) {
+        const uint32_t c0 = __builtin_amdgcn_alignbit(w[g + 1], w[g], 16);   // codes at bytes 2..17
+        const uint32_t c1 = w[5 + g];                                         // codes at bytes 20..35
+        bop[0] = (long)((uint64_t)(c0 & kNib) | ((uint64_t)((c0 >> 4) & kNib) << 32));
+        bop[1] = (long)((uint64_t)(c1 & kNib) | ((uint64_t)((c1 >> 4) & kNib) << 32));
+        d[0] = half_lo_to_f32(w[0]);
+        d[1] = half_hi_to_f32(w[4]);
+    }
+};
+struct FmtQ8_0 {   // 34-byte blocks: binary16 d, 32 int8 codes; weight = q d
+    static constexpr int kBlockBytes = 34;
+    static constexpr bool kOffset = false;
+    __device__ __forceinline__ static void decode(const uint32_t* w, int g, long bop[2], float d[2]) {
+        // block a: codes at bytes 2..33, so code dword i straddles dwords i and i + 1
+        const uint32_t a0 = __builtin_amdgcn_alignbit(w[g + 1], w[g], 16);
+        const uint32_t a1 = __builtin_amdgcn_alignbit(w[g + 5], w[g + 4], 16);
+        bop[0] = (long)((uint64_t)a0 | ((uint64_t)a1 << 32));
+        // block b: scale in bytes 34-35 (high half of dword 8), codes in dwords 9..16
+        bop[1] = (long)((uint64_t)w[9 + g] | ((uint64_t)w[13 + g] << 32));
+        d[0] = half_lo_to_f32(w[0]);
+        d[1] = half_hi_to_f32(w[8]);
+    }
+};
+
+template <class WF, int CB, int MP, int RT, int KS>
 struct MfmaGeom {
     static_assert(CB % 8 == 0, "chunks hold whole 144-byte groups of 8 blocks");
     static_assert(MP == 4 || MP == 8 || MP == 16 || MP == 32, "padded column count");
     static constexpr int kW = RT * KS;                           // waves per workgroup
     static_assert(kW == 4 || kW == 8 || kW == 16, "4, 8 or 16 waves");
     static constexpr int kNT = (MP + 15) / 16;                   // 16-column MFMA tiles
-    // weights: 16 rows x CB blocks of 18 bytes
-    static constexpr int kWSlotsUsed = CB * 18 / 16;
+    // weights: 16 rows x CB blocks
+    static constexpr int kWSlotsUsed = CB * WF::kBlockBytes / 16;
     static constexpr int kWRowSlots = kWSlotsUsed | 1;           // odd stride in slots
     static constexpr int kCw = (16 * kWRowSlots + 63) / 64;      // copy instructions per wave
     static constexpr int kWBufBytes = kCw * 1024;                // per wave, per buffer
@@ -84,9 +114,9 @@ struct MfmaGeom {
 
 // LDS: DEPTH stages, then one fp32 table of d8 per wave (CB x MP scales of
 // the chunk it computes); after the loop the stages hold the KS partial sums.
-template <int CB, int MP, int RT, int KS, int DEPTH>
+template <class WF, int CB, int MP, int RT, int KS, int DEPTH>
 constexpr size_t mfma_lds_bytes() {
-    using G = MfmaGeom<CB, MP, RT, KS>;
+    using G = MfmaGeom<WF, CB, MP, RT, KS>;
     const size_t main = (size_t)DEPTH * G::kStageBytes;
     const size_t red = (size_t)G::kW * G::kNT * 4 * 64 * 4;   // partial sums of the KS parts
     return (main > red ? main : red) + (size_t)G::kW * CB * MP * 4;
@@ -95,14 +125,14 @@ constexpr size_t mfma_lds_bytes() {
 // This wave's weight copies of chunk ch: 16 rows from n0, blocks [ch*CB, ..).
 // Every lane loads a valid address: rows past N, slots past the chunk and
 // chunks past the end are clamped onto real data (that the compute skips).
-template <int CB, int MP, int RT, int KS>
+template <class WF, int CB, int MP, int RT, int KS>
 __device__ __forceinline__ void copy_weights(const uint8_t* __restrict__ Wq, size_t row_bytes, int n0, int N,
                                              int nblk, int nchunks, int ch, uint8_t* buf, int lane) {
-    using G = MfmaGeom<CB, MP, RT, KS>;
+    using G = MfmaGeom<WF, CB, MP, RT, KS>;
     const int chc = ch < nchunks ? ch : nchunks - 1;
     const int blk0 = chc * CB;
     const int cb = nblk - blk0 < CB ? nblk - blk0 : CB;
-    const int used = cb * 18 / 16;
+    const int used = cb * WF::kBlockBytes / 16;
 #pragma unroll
     for (int j = 0; j < G::kCw; ++j) {
         const int q = j * kWave + lane;
@@ -111,7 +141,7 @@ __device__ __forceinline__ void copy_weights(const uint8_t* __restrict__ Wq, siz
         const int rc = r < 16 ? r : 15;
         const int n = n0 + rc < N ? n0 + rc : N - 1;
         const int cc = c < used ? c : used - 1;
-        const uint8_t* src = Wq + (size_t)n * row_bytes + (size_t)blk0 * 18 + (size_t)cc * 16;
+        const uint8_t* src = Wq + (size_t)n * row_bytes + (size_t)blk0 * WF::kBlockBytes + (size_t)cc * 16;
         __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + j * 1024), 16, 0, kAuxNonTemporal);
     }
 }
@@ -119,10 +149,10 @@ __device__ __forceinline__ void copy_weights(const uint8_t* __restrict__ Wq, siz
 // This wave's share (instructions wave*kCa .. wave*kCa + kCa - 1) of the
 // activation copies of iteration it: slot s of the buffer is part p, column m,
 // 16-byte slot c of that column's CB blocks.  Clamped like the weights.
-template <int CB, int MP, int RT, int KS>
+template <class WF, int CB, int MP, int RT, int KS>
 __device__ __forceinline__ void copy_acts(const uint8_t* __restrict__ Xq, int nblk, int nchunks, int M, int it,
                                           int wave, uint8_t* abuf, int lane) {
-    using G = MfmaGeom<CB, MP, RT, KS>;
+    using G = MfmaGeom<WF, CB, MP, RT, KS>;
 #pragma unroll
     for (int j = 0; j < G::kCa; ++j) {
         const int s = (wave * G::kCa + j) * kWave + lane;
@@ -152,11 +182,11 @@ __device__ __forceinline__ void wait_iterations_ahead(int q) {
     else wait_vmcnt<(DEPTH > 1 ? (DEPTH - 1) * COPIES : 0)>();
 }
 
-template <int CB, int MP, int RT, int KS, int DEPTH>
+template <class WF, int CB, int MP, int RT, int KS, int DEPTH>
 __global__ void __launch_bounds__(64 * RT * KS)
-k_q4_mfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
-          int N, int K, int M) {
-    using G = MfmaGeom<CB, MP, RT, KS>;
+k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
+        int N, int K, int M) {
+    using G = MfmaGeom<WF, CB, MP, RT, KS>;
     constexpr int NT = G::kNT;
     static_assert(DEPTH >= 1 && DEPTH <= 3, "pipeline depth");
     static_assert(G::kCopies * (DEPTH - 1) <= 63, "wait count exceeds the vmcnt field");
@@ -168,7 +198,7 @@ k_q4_mfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float*
     const int part = wave - tile * KS;         // this wave's part of K
     const int g = lane >> 4, rn = lane & 15;
     const int nblk = K >> 5;
-    const size_t row_bytes = (size_t)nblk * 18;
+    const size_t row_bytes = (size_t)nblk * WF::kBlockBytes;
     const int nchunks = (nblk + CB - 1) / CB;
     const int iters = (nchunks + KS - 1) / KS;
     const int ngroups = (N + 16 * RT - 1) / (16 * RT);
@@ -177,14 +207,14 @@ k_q4_mfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float*
     const int acol = MP < 16 ? (rn & (MP - 1)) : rn;
     auto wbuf = [&](int d) { return lds + d * G::kStageBytes + wave * G::kWBufBytes; };
     auto abuf = [&](int d) { return lds + d * G::kStageBytes + G::kW * G::kWBufBytes; };
-    constexpr size_t kTabOff = mfma_lds_bytes<CB, MP, RT, KS, DEPTH>() - (size_t)G::kW * CB * MP * 4;
+    constexpr size_t kTabOff = mfma_lds_bytes<WF, CB, MP, RT, KS, DEPTH>() - (size_t)G::kW * CB * MP * 4;
     float* const d8tab = reinterpret_cast<float*>(lds + kTabOff) + wave * CB * MP;
 
     for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {   // workgroup-uniform
         const int n0 = (grp * RT + tile) * 16;
         auto issue = [&](int it2, int d) {
-            copy_weights<CB, MP, RT, KS>(Wq, row_bytes, n0, N, nblk, nchunks, it2 * KS + part, wbuf(d), lane);
-            copy_acts<CB, MP, RT, KS>(Xq, nblk, nchunks, M, it2, wave, abuf(d), lane);
+            copy_weights<WF, CB, MP, RT, KS>(Wq, row_bytes, n0, N, nblk, nchunks, it2 * KS + part, wbuf(d), lane);
+            copy_acts<WF, CB, MP, RT, KS>(Xq, nblk, nchunks, M, it2, wave, abuf(d), lane);
         };
         lds_barrier();   // the previous group's reads of every buffer are done
 #pragma unroll
@@ -233,15 +263,9 @@ k_q4_mfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float*
                     long bop[8];
                     float d4[8];
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {   // block pairs o + 2p, o + 2p + 1
-                        const uint32_t* w = reinterpret_cast<const uint32_t*>(rowp + ((o >> 1) + p) * kPairBytes);
-                        const uint32_t wg0 = w[g], wg1 = w[g + 1], ws0 = w[0], ws4 = w[4], wb = w[5 + g];
-                        const uint32_t c0 = __builtin_amdgcn_alignbit(wg1, wg0, 16);
-                        bop[2 * p] = (long)((uint64_t)(c0 & kNib) | ((uint64_t)((c0 >> 4) & kNib) << 32));
-                        bop[2 * p + 1] = (long)((uint64_t)(wb & kNib) | ((uint64_t)((wb >> 4) & kNib) << 32));
-                        d4[2 * p] = half_lo_to_f32(ws0);
-                        d4[2 * p + 1] = half_hi_to_f32(ws4);
-                    }
+                    for (int p = 0; p < 4; ++p)   // block pairs o + 2p, o + 2p + 1
+                        WF::decode(reinterpret_cast<const uint32_t*>(rowp + ((o >> 1) + p) * 2 * WF::kBlockBytes), g,
+                                   bop + 2 * p, d4 + 2 * p);
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
                         long aop[8];
@@ -255,7 +279,9 @@ k_q4_mfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float*
                         i32x4 dsum[8];
 #pragma unroll
                         for (int i = 0; i < 8; ++i)
-                            dsum[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[i], kNeg8, i32x4{0, 0, 0, 0}, 0, 0, 0);
+                            dsum[i] = WF::kOffset ? __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[i], kNeg8,
+                                                                                         i32x4{0, 0, 0, 0}, 0, 0, 0)
+                                                  : i32x4{0, 0, 0, 0};
 #pragma unroll
                         for (int i = 0; i < 8; ++i)
                             dsum[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[i], bop[i], dsum[i], 0, 0, 0);
@@ -309,42 +335,47 @@ k_q4_mfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float*
     }
 }
 
-template <int CB, int MP, int RT, int KS, int DEPTH>
+template <class WF, int CB, int MP, int RT, int KS, int DEPTH>
 hipError_t launch_mfma_cfg(const void* Wq, const void* Xq, float* Y, int N, int K, int M, int grid, hipStream_t s) {
-    const size_t lds = mfma_lds_bytes<CB, MP, RT, KS, DEPTH>();
+    const size_t lds = mfma_lds_bytes<WF, CB, MP, RT, KS, DEPTH>();
     if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
     const int groups = (N + 16 * RT - 1) / (16 * RT);
     const int g = grid ? grid : groups;
-    hipLaunchKernelGGL((k_q4_mfma<CB, MP, RT, KS, DEPTH>), dim3(g), dim3(64 * RT * KS), lds, s,
+    hipLaunchKernelGGL((k_qmfma<WF, CB, MP, RT, KS, DEPTH>), dim3(g), dim3(64 * RT * KS), lds, s,
                        (const uint8_t*)Wq, (const uint8_t*)Xq, Y, N, K, M);
     return hipGetLastError();
 }
 
+template <class WF, int CB, int MP, int RT, int KS, int DEPTH>
+constexpr bool mfma_builds() {
+    // the stages fit the LDS of one workgroup, the wait counts fit the vmcnt
+    // field, and 16-wave workgroups (128 VGPRs per lane) are kept to 16 columns
+    return mfma_lds_bytes<WF, CB, MP, RT, KS, DEPTH>() <= 160 * 1024 &&
+           MfmaGeom<WF, CB, MP, RT, KS>::kCopies * (DEPTH - 1) <= 63 && (RT * KS < 16 || MP <= 16);
+}
+
 // The built configurations for one padded column count MP.
-template <int MP>
+template <class WF, int MP>
 hipError_t launch_mfma_mp(int RT, int KS, int DEPTH, int CB, const void* Wq, const void* Xq, float* Y, int N, int K,
                           int M, int grid, hipStream_t s) {
-#define DG_MF(RR, SS, DD, CC)                                      \
-    if (RT == RR && KS == SS && DEPTH == DD && CB == CC)           \
-        return launch_mfma_cfg<CC, MP, RR, SS, DD>(Wq, Xq, Y, N, K, M, grid, s);
-    // 16 waves
-    if constexpr (MP <= 16) { DG_MF(1, 16, 1, 8) DG_MF(2, 8, 1, 8) }   // (2, 8, 1) spills at 32 columns
-    if constexpr (MP <= 8) { DG_MF(4, 4, 2, 8) }
-    // 8 waves
-    DG_MF(1, 8, 1, 8) DG_MF(2, 4, 2, 8) DG_MF(4, 2, 2, 8) DG_MF(8, 1, 2, 8)
-    if constexpr (MP <= 16) { DG_MF(1, 8, 2, 8) }
-    // 4 waves
-    DG_MF(4, 1, 2, 8) DG_MF(4, 1, 3, 8) DG_MF(2, 2, 2, 8) DG_MF(1, 4, 2, 8)
+#define DG_MF(RR, SS, DD, CC)                                                          \
+    if constexpr (mfma_builds<WF, CC, MP, RR, SS, DD>()) {                             \
+        if (RT == RR && KS == SS && DEPTH == DD && CB == CC)                           \
+            return launch_mfma_cfg<WF, CC, MP, RR, SS, DD>(Wq, Xq, Y, N, K, M, grid, s); \
+    }
+    DG_MF(1, 16, 1, 8) DG_MF(2, 8, 1, 8) DG_MF(4, 4, 2, 8)                       // 16 waves
+    DG_MF(1, 8, 1, 8) DG_MF(1, 8, 2, 8) DG_MF(2, 4, 2, 8) DG_MF(4, 2, 2, 8)      // 8 waves
+    DG_MF(8, 1, 2, 8)
+    DG_MF(4, 1, 2, 8) DG_MF(4, 1, 3, 8) DG_MF(2, 2, 2, 8) DG_MF(1, 4, 2, 8)      // 4 waves
 #undef DG_MF
     return hipErrorInvalidValue;
 }
 
-}  // namespace
-
 // unroll = RT * 10000 + KS * 100 + DEPTH * 10 + CB / 8 selects a configuration
 // for sweeps (0: the default for the shape); the padded column count follows M.
-hipError_t launch_q4_mfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
-                          hipStream_t s) {
+template <class WF>
+hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
+                        hipStream_t s) {
     int RT, KS, DEPTH, CB;
     if (unroll) {
         RT = unroll / 10000;
@@ -352,8 +383,8 @@ hipError_t launch_q4_mfma(int M, int unroll, const void* Wq, const void* Xq, flo
         DEPTH = (unroll / 10) % 10;
         CB = (unroll % 10) * 8;
     } else {
-        // Measured on MI355X (decoder shapes, M = 2..24): split K over 8 waves
-        // (4 for 9..16 columns) when there are few row tiles; share each
+        // Measured on MI355X (Q4_0, decoder shapes, M = 2..24): split K over 8
+        // waves (4 for 9..16 columns) when there are few row tiles; share each
         // activation chunk between two row tiles when there are many.
         const int tiles = (N + 15) / 16;
         CB = 8;
@@ -368,10 +399,22 @@ hipError_t launch_q4_mfma(int M, int unroll, const void* Wq, const void* Xq, flo
             else { RT = 2; KS = 2; }
         }
     }
-    if (M <= 4) return launch_mfma_mp<4>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
-    if (M <= 8) return launch_mfma_mp<8>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
-    if (M <= 16) return launch_mfma_mp<16>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
-    return launch_mfma_mp<32>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
+    if (M <= 4) return launch_mfma_mp<WF, 4>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
+    if (M <= 8) return launch_mfma_mp<WF, 8>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
+    if (M <= 16) return launch_mfma_mp<WF, 16>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
+    return launch_mfma_mp<WF, 32>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
+}
+
+}  // namespace
+
+hipError_t launch_q4_mfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
+                          hipStream_t s) {
+    return launch_qmfma<FmtQ4_0>(M, unroll, Wq, Xq, Y, N, K, grid, s);
+}
+
+hipError_t launch_q8_mfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
+                          hipStream_t s) {
+    return launch_qmfma<FmtQ8_0>(M, unroll, Wq, Xq, Y, N, K, grid, s);
 }
 
 }  // namespace dg

@@ -1,0 +1,159 @@
+// gemv_q8_0.hip -- Q8_0 weights x Q8_1 activations, M = 1..24 columns.
+//
+// Y[m][n] = sum_b dw(n,b) d8(m,b) sum_{j<32} qw q8: the Q8_0 model files that
+// "The kernel that waited for itself" runs through the same Q8_1-activation
+// path as Q4_0 (four-model comparison).  A Q8_0 block is 34 bytes (binary16 d,
+// 32 int8 codes), so a row moves 34/32 bytes per weight, 1.9 times the Q4_0
+// row; the decode is simpler (no nibbles, no -8 offset).
+//  * M = 1: the rows stream through LDS like the Q4_0 M = 1 kernel (one wave
+//    per row, global_load_lds_dwordx4 copies, DEPTH row buffers per wave,
+//    explicit vmcnt waits); a block pair is 68 bytes = 17 dwords, an odd lane
+//    stride, so the ds_read of the 64 lanes are free of bank conflicts.
+//  * M = 2..24, and M = 1 rows longer than 256 block pairs: the matrix-core
+//    kernel of the Q4_0 path with a Q8_0 decoder (one v_mfma_i32_16x16x32_i8
+//    per block and 16 x 16 tile, no offset operation).
+#include "dg_internal.h"
+#include "q4_common.h"
+
+namespace dg {
+namespace {
+
+using namespace q4;
+
+constexpr int kQ80PairBytes = 68;
+
+template <int S, int C, int DEPTH>
+__global__ void __launch_bounds__(256)
+k_q8_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __restrict__ Y, int N, int K) {
+    static_assert(DEPTH >= 2 && DEPTH <= 4, "pipeline depth");
+    static_assert(C * (DEPTH - 1) <= 63, "wait count exceeds the vmcnt field");
+    extern __shared__ u32x4 lds_rows8[];
+    const int lane = lane_id();
+    const int wave = wave_in_block();
+    const int wpb = blockDim.x / kWave;
+    const int npairs = K >> 6;
+    const int row_bytes = (K >> 5) * 34;
+    const int nchunks = row_bytes >> 4;
+    const int rstride = gridDim.x * wpb;
+    const int row0 = blockIdx.x * wpb + wave;
+    if (row0 >= N) return;
+    uint8_t* const lds_base = reinterpret_cast<uint8_t*>(lds_rows8) + wave * DEPTH * row_bytes;
+
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d) {
+        const int r = row0 + d * rstride;
+        if (r < N) copy_row_to_lds<C>(Wq + (size_t)r * row_bytes, lds_base + d * row_bytes, nchunks, lane);
+    }
+
+    int pc[S];
+    ActPair act[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int p = s * kWave + lane;
+        pc[s] = p < npairs ? p : npairs - 1;
+        load_act_pair(Xq, pc[s], act[s]);
+        if (p >= npairs) {   // lanes past the end of the row contribute exactly 0
+            act[s].da = 0.0f;
+            act[s].db = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { act[s].qa[i] = 0; act[s].qb[i] = 0; }
+        }
+    }
+
+    // outputs held back and stored 64 rows at a time (lane i holds the i-th row)
+    float out = 0.0f;
+    int nout = 0;
+    int out_row0 = row0;
+    int slot = 0;
+    for (int row = row0; row < N; row += rstride) {
+        const int ahead = row + (DEPTH - 1) * rstride;
+        if (ahead < N) {
+            int aslot = slot + DEPTH - 1;
+            if (aslot >= DEPTH) aslot -= DEPTH;
+            copy_row_to_lds<C>(Wq + (size_t)ahead * row_bytes, lds_base + aslot * row_bytes, nchunks, lane);
+        }
+        const int left = __builtin_amdgcn_readfirstlane((N - 1 - row) / rstride);   // wave-uniform
+        wait_rows_ahead<C, DEPTH>(left < DEPTH - 1 ? left : DEPTH - 1);
+
+        const uint8_t* rowbuf = lds_base + slot * row_bytes;
+        float acc = 0.0f;
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const uint32_t* w = reinterpret_cast<const uint32_t*>(rowbuf + (size_t)pc[s] * kQ80PairBytes);
+            uint32_t v[17];
+#pragma unroll
+            for (int i = 0; i < 17; ++i) v[i] = w[i];
+            int sa = 0, sb = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sa = dot4_i8(__builtin_amdgcn_alignbit(v[i + 1], v[i], 16), act[s].qa[i], sa);   // codes at bytes 2..33
+                sb = dot4_i8(v[9 + i], act[s].qb[i], sb);                                         // codes at bytes 36..67
+            }
+            acc = fmaf((float)sa, half_lo_to_f32(v[0]) * act[s].da, acc);
+            acc = fmaf((float)sb, half_hi_to_f32(v[8]) * act[s].db, acc);
+        }
+        acc = wave_sum_f32(acc);   // wave-uniform
+        if (lane == nout) out = acc;
+        if (++nout == kWave) {
+            Y[out_row0 + (int64_t)lane * rstride] = out;
+            nout = 0;
+            out_row0 = row + rstride;
+        }
+        slot = slot + 1 == DEPTH ? 0 : slot + 1;
+    }
+    if (lane < nout) Y[out_row0 + (int64_t)lane * rstride] = out;
+}
+
+hipError_t launch_q8_m1_ldsrow(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
+                               int block, hipStream_t s) {
+    if (!depth) depth = 2;
+    if (!block) block = 256;
+    if (block > 256) return hipErrorInvalidValue;   // compiled for <= 256 threads
+    if (!grid) {
+        const int rows_grid = (N + block / kWave - 1) / (block / kWave);
+        grid = rows_grid < 2048 ? rows_grid : 2048;
+    }
+    const size_t row_bytes = (size_t)(K / 32) * 34;
+    const size_t lds = (size_t)(block / kWave) * depth * row_bytes;
+    if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
+    const int C = (int)((row_bytes + 1023) / 1024);
+    const int S = (K / 64 + kWave - 1) / kWave;
+    const uint8_t* w = (const uint8_t*)Wq;
+    const uint8_t* x = (const uint8_t*)Xq;
+#define DG_SCD(SS, CC, DD)                                                                              \
+    else if (S == SS && C == CC && depth == DD)                                                         \
+        hipLaunchKernelGGL((k_q8_m1_ldsrow<SS, CC, DD>), dim3(grid), dim3(block), lds, s, w, x, Y, N, K);
+#define DG_SC(SS, CC) DG_SCD(SS, CC, 2) DG_SCD(SS, CC, 3) DG_SCD(SS, CC, 4)
+    // C = ceil(34 K / 32768) for the K % 256 == 0 of each S = ceil(K / 4096)
+    if (false) {
+    }
+    DG_SC(1, 1) DG_SC(1, 2) DG_SC(1, 3) DG_SC(1, 4) DG_SC(1, 5)
+    DG_SC(2, 5) DG_SC(2, 6) DG_SC(2, 7) DG_SC(2, 8) DG_SC(2, 9)
+    DG_SC(3, 9) DG_SC(3, 10) DG_SC(3, 11) DG_SC(3, 12) DG_SC(3, 13)
+    DG_SC(4, 14) DG_SC(4, 15) DG_SC(4, 16) DG_SC(4, 17)
+    else return hipErrorInvalidValue;
+#undef DG_SC
+#undef DG_SCD
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int K, int M,
+                            const dg_launch* cfg, hipStream_t s) {
+    const int S = (K / 64 + kWave - 1) / kWave;
+    int variant = cfg && cfg->variant ? cfg->variant : 0;
+    if (variant == 0) variant = (M == 1 && S <= 4) ? DG_VARIANT_Q8_LDSROW : DG_VARIANT_Q8_MFMA;
+    if (variant == DG_VARIANT_Q8_LDSROW) {
+        if (M != 1 || S > 4) return hipErrorInvalidValue;
+        return launch_q8_m1_ldsrow(K, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, cfg ? cfg->grid : 0,
+                                   cfg ? cfg->block : 0, s);
+    }
+    if (variant == DG_VARIANT_Q8_MFMA) {
+        if (cfg && cfg->block) return hipErrorInvalidValue;   // the configuration fixes the workgroup size
+        return launch_q8_mfma(M, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, K, cfg ? cfg->grid : 0, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace dg

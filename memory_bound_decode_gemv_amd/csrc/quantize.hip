@@ -94,7 +94,44 @@ k_quantize_q4_0(const float* __restrict__ w, uint8_t* __restrict__ Wq, int64_t n
     }
 }
 
+// One thread per 32-weight block: d = max|x| / 127, codes rounded half away
+// from zero (the same rule as the activation quantiser, without the sum).
+__global__ void __launch_bounds__(256)
+k_quantize_q8_0(const float* __restrict__ w, uint8_t* __restrict__ Wq, int64_t nblocks) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= nblocks) return;
+    float v[32];
+    load_block32(w + t * 32, v);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    const float d = bind_f32(amax / 127.0f);
+    uint16_t* out = reinterpret_cast<uint16_t*>(Wq + t * 34);   // blocks are 2-byte aligned
+    out[0] = f32_to_half_bits(d);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        uint32_t h = 0;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            int c = 0;
+            if (d != 0.0f) {
+                c = (int)roundf(v[2 * i + b] / d);   // halves away from zero
+                c = c > 127 ? 127 : (c < -127 ? -127 : c);
+            }
+            h |= (uint32_t)(uint8_t)(int8_t)c << (8 * b);
+        }
+        out[1 + i] = (uint16_t)h;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_q8_0(const float* w, void* Wq, int64_t N, int64_t K, hipStream_t s) {
+    const int64_t nblocks = N * (K / 32);
+    const int64_t grid = (nblocks + 255) / 256;
+    hipLaunchKernelGGL(k_quantize_q8_0, dim3((unsigned)grid), dim3(256), 0, s, w, (uint8_t*)Wq, nblocks);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_q8_1(const float* x, void* Xq, int64_t M, int64_t K, hipStream_t s) {
     const int64_t nblocks = M * (K / 32);

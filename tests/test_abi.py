@@ -78,6 +78,7 @@ def test_gemv_f16_rejects_before_launch(lib, args, expect):
 ])
 def test_gemv_q4_0_rejects_before_launch(lib, args, expect):
     assert lib.dg_gemv_q4_0(*args, None) == expect
+    assert lib.dg_gemv_q8_0(*args, None) == expect
 
 
 def test_launch_overrides_rejected(lib):
@@ -86,6 +87,7 @@ def test_launch_overrides_rejected(lib):
     for cfg in bad:
         assert lib.dg_gemv_f16_ex(A16, A16, A16, 4, 16, 16, ctypes.byref(cfg), None) == 6
         assert lib.dg_gemv_q4_0_ex(A16, A16, A16, 4, 256, 1, ctypes.byref(cfg), None) == 6
+        assert lib.dg_gemv_q8_0_ex(A16, A16, A16, 4, 256, 1, ctypes.byref(cfg), None) == 6
 
 
 def test_stream_read_rejects_before_launch(lib):
@@ -118,6 +120,9 @@ def test_quantisers_reject_before_launch(lib):
     assert lib.dg_quantize_q8_1(A2, A16, 2, 64, None) == 2
     assert lib.dg_quantize_q4_0(None, A16, 2, 64, None) == 1
     assert lib.dg_quantize_q8_1(None, None, 0, 64, None) == 0
+    assert lib.dg_quantize_q8_0(A16, A16, 2, 48, None) == 3
+    assert lib.dg_quantize_q8_0(A16, P(0x1001), 2, 64, None) == 2
+    assert lib.dg_quantize_q8_0(None, A16, 2, 64, None) == 1
 
 
 def test_binding_refuses_tensors_smaller_than_the_call_touches():

@@ -14,8 +14,9 @@ def _gpu_q(dg, dev, a, kind):
     import torch
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
     R, K = a.shape
-    out = torch.zeros(R * (K // 32) * (36 if kind == "q8_1" else 18), dtype=torch.uint8, device=dev)
-    (dg.dg_quantize_q8_1 if kind == "q8_1" else dg.dg_quantize_q4_0)(t, out, R, K)
+    size = {"q8_1": 36, "q4_0": 18, "q8_0": 34}[kind]
+    out = torch.zeros(R * (K // 32) * size, dtype=torch.uint8, device=dev)
+    {"q8_1": dg.dg_quantize_q8_1, "q4_0": dg.dg_quantize_q4_0, "q8_0": dg.dg_quantize_q8_0}[kind](t, out, R, K)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -33,12 +34,12 @@ def _tricky(K):
     return np.stack(rows).astype(np.float32)
 
 
-@pytest.mark.parametrize("kind", ["q8_1", "q4_0"])
+@pytest.mark.parametrize("kind", ["q8_1", "q4_0", "q8_0"])
 @pytest.mark.parametrize("R,K", [(1, 32), (3, 256), (17, 4096), (4, 14336)])
 def test_quantiser_bytes_match_oracle(dg, dev, orc, kind, R, K):
     a = synth.normal_f32((300, synth.KIND_X, R, K), (R, K))
     a = np.concatenate([a, _tricky(K)])
-    ref = (orc.quantize_q8_1 if kind == "q8_1" else orc.quantize_q4_0)(a).reshape(-1)
+    ref = {"q8_1": orc.quantize_q8_1, "q4_0": orc.quantize_q4_0, "q8_0": orc.quantize_q8_0}[kind](a).reshape(-1)
     got = _gpu_q(dg, dev, a, kind)
     bad = np.nonzero(got != ref)[0]
     assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
@@ -57,3 +58,9 @@ def test_quantiser_worked_blocks(dg, dev):
     for e in g["q4_0_quantiser_examples"]:
         x = xs[e["x"]].astype(np.float32).reshape(1, 32)
         assert bytes(_gpu_q(dg, dev, x, "q4_0")) == bytes.fromhex(e["block_hex"].replace(" ", "")), e["name"]
+
+    with open(os.path.join(os.path.dirname(__file__), "golden", "q8_0_q8_1_worked.json")) as f:
+        g8 = json.load(f)
+    for e in g8["q8_0_quantiser_examples"]:
+        x = np.array(e["x"], dtype=np.float32).reshape(1, 32)
+        assert bytes(_gpu_q(dg, dev, x, "q8_0")) == bytes.fromhex(e["block_hex"].replace(" ", "")), e["name"]
