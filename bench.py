@@ -435,6 +435,8 @@ def suite(args):
         suite_q4_small_m(dg, torch, emit, ceil_gbps)
     if want("q8"):
         suite_q8_0(dg, torch, emit, ceil_gbps)
+    if want("m1"):
+        suite_m1_rows_vs_units(dg, torch, emit, ceil_gbps)
     if want("argmax"):
         suite_argmax(dg, torch, emit, ceil_gbps)
     if want("tail"):
@@ -625,6 +627,36 @@ def suite_q8_0(dg, torch, emit, ceil_gbps):
         torch.cuda.empty_cache()
 
 
+def suite_m1_rows_vs_units(dg, torch, emit, ceil_gbps):
+    """M = 1, both quantised formats, over the decoder shapes and the 70B MLP:
+    rows streamed through LDS whole (LDS-row kernels) or in 64-pair units."""
+    fmts = [("q4_0", 18, q4_copies, dg.dg_gemv_q4_0, bytes_q4, 13, 15),
+            ("q8_0", 34, q8_0_copies, dg.dg_gemv_q8_0, bytes_q8_0, 21, 23)]
+    for name, bb, make, gemv, nbytes, v_rows, v_units in fmts:
+        for (N, K) in [(4096, 4096), (14336, 4096), (4096, 14336), (Q4_N, Q4_K)]:
+            nc = copies_for(bb * N * K // 32)
+            Wq = make(6, N, K, nc)
+            Xq = q8_columns(6, K, 1)
+            Y = torch.empty(N, dtype=torch.float32, device="cuda")
+            launches = [("default", None)]
+            launches += [(f"rows d{d} g{g} b{b}", dict(variant=v_rows, unroll=d, grid=g, block=b))
+                         for d in (2, 3) for g in (0, 1024) for b in (128, 256)]
+            launches += [(f"units d{d} g{g} b{b}", dict(variant=v_units, unroll=d, grid=g, block=b))
+                         for d in (2, 3, 4) for g in (0, 1024) for b in (128, 256)]
+            for lname, launch in launches:
+                calls = [(lambda c=c, launch=launch: gemv(Wq[c % nc], Xq, Y, N, K, 1, launch=launch))
+                         for c in range(max(nc, 20))]
+                try:
+                    calls[0]()
+                except dg.DGError:   # a buffer depth that does not fit this row length
+                    continue
+                us, iqr = time_per_call(calls)
+                emit(record(f"gemv_{name} {N}x{K} M=1", us, iqr, nbytes(N, K, 1), ceil_gbps, variant=lname,
+                            copies=nc))
+            del Wq
+            torch.cuda.empty_cache()
+
+
 def suite_argmax(dg, torch, emit, ceil_gbps):
     # argmax: hot (one buffer) and cold (rotated copies for the 256 MB shape)
     import synth
@@ -704,7 +736,7 @@ def main():
     ap.add_argument("--profile-kernels", action="store_true",
                     help="launch each profiled kernel eagerly on known workloads (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
-                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q8,argmax,tail")
+                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q8,m1,argmax,tail")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     args = ap.parse_args()

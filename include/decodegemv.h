@@ -233,7 +233,8 @@ typedef struct {
                       dense DG_VARIANT_DENSE_WIDE: U + 100*(S-1) also splits
                       each row's K over S in {1,2,4} waves of a workgroup;
                       Q4_0 DG_VARIANT_Q4_LDS: rows per wave (1, 2, 4);
-                      *_LDSROW: row buffers per wave (2..4);
+                      *_LDSROW / *_UNITS: row (unit) buffers per wave
+                      (2..4);
                       *_MFMA: RT*10000 + KS*100 + DEPTH*10 + CB/8 (row
                       tiles and K parts per workgroup, pipeline depth,
                       blocks per chunk)                                      */
@@ -250,9 +251,11 @@ enum {
     DG_VARIANT_Q4_LDS = 12,         /* activations staged in LDS, several rows per wave          */
     DG_VARIANT_Q4_LDSROW = 13,      /* M = 1: weight rows copied to LDS with coalesced loads     */
     DG_VARIANT_Q4_MFMA = 14,        /* int8 matrix cores, 16 rows x 16 columns per instruction   */
+    DG_VARIANT_Q4_UNITS = 15,       /* M = 1: rows copied to LDS in units of 64 block pairs      */
     /* Q8_0 */
     DG_VARIANT_Q8_LDSROW = 21,      /* M = 1: weight rows copied to LDS (K <= 16384)             */
-    DG_VARIANT_Q8_MFMA = 22         /* int8 matrix cores                                          */
+    DG_VARIANT_Q8_MFMA = 22,        /* int8 matrix cores                                          */
+    DG_VARIANT_Q8_UNITS = 23        /* M = 1: rows copied to LDS in units of 64 block pairs      */
 };
 
 dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K,

@@ -17,6 +17,19 @@ struct Launch {
     int unroll;
 };
 
+// Default launch shape of the M = 1 quantised kernels (measured on MI355X over
+// the decoder shapes and the 70B MLP, both formats): every wave gets at least
+// two rows so that its copy pipeline has something to overlap (one row per
+// wave leaves the pipeline empty), with about 2048 waves for up to 8192 rows
+// and 1024 or 2048 workgroups of four waves beyond.
+inline void m1_default_launch(int N, int& grid, int& block) {
+    block = N <= 8192 ? 128 : 256;
+    const int wpb = block / 64;
+    const int g = N >= 16384 ? 2048 : 1024;
+    const int need = (N + wpb - 1) / wpb;
+    grid = need < g ? need : g;
+}
+
 // Device properties used to size grids and check launches; cached per device.
 int device_cu_count();
 size_t device_max_lds_per_block();
@@ -38,6 +51,12 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
 // depth, unroll, grid or block selects the default.
 hipError_t launch_q4_m1_ldsrow(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
                                int block, hipStream_t s);
+// M = 1 with rows streamed through LDS in units of 64 block pairs (depth =
+// unit buffers per wave); K <= 16384.
+hipError_t launch_q4_m1_units(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
+                              int block, hipStream_t s);
+hipError_t launch_q8_m1_units(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
+                              int block, hipStream_t s);
 hipError_t launch_q4_mfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
                           hipStream_t s);
 

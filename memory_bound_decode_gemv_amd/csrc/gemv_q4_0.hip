@@ -286,8 +286,14 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
     }
     if (variant == DG_VARIANT_Q4_LDSROW) {
         if (M != 1) return hipErrorInvalidValue;
-        return launch_q4_m1_ldsrow(K, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, cfg ? cfg->grid : 0,
-                                   cfg ? cfg->block : 0, s);
+        int grid = cfg ? cfg->grid : 0, block = cfg ? cfg->block : 0;
+        if (!grid && !block) m1_default_launch(N, grid, block);
+        return launch_q4_m1_ldsrow(K, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, grid, block, s);
+    }
+    if (variant == DG_VARIANT_Q4_UNITS) {
+        if (M != 1 || S > 4) return hipErrorInvalidValue;
+        return launch_q4_m1_units(K, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, cfg ? cfg->grid : 0,
+                                  cfg ? cfg->block : 0, s);
     }
     if (variant == DG_VARIANT_Q4_MFMA) {
         if (cfg && cfg->block) return hipErrorInvalidValue;   // the configuration fixes the workgroup size

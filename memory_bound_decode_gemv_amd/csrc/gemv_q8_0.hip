@@ -143,11 +143,23 @@ hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int
                             const dg_launch* cfg, hipStream_t s) {
     const int S = (K / 64 + kWave - 1) / kWave;
     int variant = cfg && cfg->variant ? cfg->variant : 0;
-    if (variant == 0) variant = (M == 1 && S <= 4) ? DG_VARIANT_Q8_LDSROW : DG_VARIANT_Q8_MFMA;
-    if (variant == DG_VARIANT_Q8_LDSROW) {
+    int depth = cfg ? cfg->unroll : 0;
+    if (variant == 0) {
+        // Measured on MI355X: rows of 8192 weights and more (8.5 KiB) stream in
+        // 64-pair units three deep; shorter rows whole, two deep.
+        if (M == 1 && S <= 4) {
+            variant = K >= 8192 ? DG_VARIANT_Q8_UNITS : DG_VARIANT_Q8_LDSROW;
+            depth = K >= 8192 ? 3 : 2;
+        } else {
+            variant = DG_VARIANT_Q8_MFMA;
+        }
+    }
+    if (variant == DG_VARIANT_Q8_LDSROW || variant == DG_VARIANT_Q8_UNITS) {
         if (M != 1 || S > 4) return hipErrorInvalidValue;
-        return launch_q8_m1_ldsrow(K, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, cfg ? cfg->grid : 0,
-                                   cfg ? cfg->block : 0, s);
+        int grid = cfg ? cfg->grid : 0, block = cfg ? cfg->block : 0;
+        if (!grid && !block) m1_default_launch(N, grid, block);
+        return variant == DG_VARIANT_Q8_LDSROW ? launch_q8_m1_ldsrow(K, depth, Wq, Xq, Y, N, grid, block, s)
+                                               : launch_q8_m1_units(K, depth, Wq, Xq, Y, N, grid, block, s);
     }
     if (variant == DG_VARIANT_Q8_MFMA) {
         if (cfg && cfg->block) return hipErrorInvalidValue;   // the configuration fixes the workgroup size

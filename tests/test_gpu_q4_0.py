@@ -79,10 +79,25 @@ def test_q4_0_m1_variants(dg, dev, orc, launch):
     assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, str(launch))
 
 
+@pytest.mark.parametrize("N,K", [(1, 256), (7, 4096), (70, 4352), (33, 8192), (64, 12288), (19, 14336),
+                                 (5, 16384), (130, 2304)])
+@pytest.mark.parametrize("launch", [dict(variant=15), dict(variant=15, unroll=2), dict(variant=15, unroll=4),
+                                    dict(variant=15, grid=2, block=128), dict(variant=15, grid=1, block=64),
+                                    dict(variant=15, unroll=2, grid=3, block=192)])
+def test_q4_0_m1_units(dg, dev, orc, N, K, launch):
+    """M = 1 with rows copied in units of 64 block pairs (ragged last units,
+    several rows and units per wave)."""
+    Wq, Xq = _operands(orc, 228, N, K, 1)
+    got = _gpu(dg, dev, Wq, Xq, N, K, 1, launch=launch)
+    assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"{N}x{K} {launch}")
+
+
 @pytest.mark.parametrize("N,launch", [(300, dict(variant=13, grid=1, block=64)),
                                       (129, dict(variant=13, grid=1, block=64, unroll=3)),
                                       (1000, dict(variant=13, grid=2, block=128, unroll=4)),
-                                      (64, dict(variant=13, grid=1, block=64))])
+                                      (64, dict(variant=13, grid=1, block=64)),
+                                      (300, dict(variant=15, grid=1, block=64)),
+                                      (1000, dict(variant=15, grid=2, block=128, unroll=4))])
 def test_q4_0_m1_many_rows_per_wave(dg, dev, orc, N, launch):
     """One wave computing more than 64 rows: its results are stored 64 rows at
     a time, then the remainder."""
@@ -199,7 +214,8 @@ def test_q4_0_overrides_beyond_kernel_limits_are_rejected(dg, dev):
                       (5, dict(variant=12, unroll=4)), (1, dict(variant=99)),
                       (4, dict(variant=14, unroll=124)), (4, dict(variant=14, unroll=21622)),
                       (4, dict(variant=14, unroll=10412)), (4, dict(variant=14, unroll=10441)),
-                      (20, dict(variant=14, unroll=11611)), (20, dict(variant=14, unroll=10821))):
+                      (20, dict(variant=14, unroll=11611)), (20, dict(variant=14, unroll=10821)),
+                      (2, dict(variant=15)), (1, dict(variant=15, block=512)), (1, dict(variant=15, unroll=5))):
         with pytest.raises(dg.DGError) as e:
             dg.dg_gemv_q4_0(W, X, Y, N, K, M, launch=launch)
         assert e.value.status == dg.DG_ERR_ARG, launch

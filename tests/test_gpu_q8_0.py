@@ -76,11 +76,23 @@ def test_q8_0_m1_variants(dg, dev, orc, N, K, launch):
                  f"{N}x{K} {launch}")
 
 
-def test_q8_0_m1_many_rows_per_wave(dg, dev, orc):
-    N, K = 300, 512
+@pytest.mark.parametrize("launch", [dict(variant=21, grid=1, block=64), dict(variant=23, grid=1, block=64),
+                                    dict(variant=23, grid=1, block=128, unroll=4)])
+def test_q8_0_m1_many_rows_per_wave(dg, dev, orc, launch):
+    N, K = 300, 4352
     Wq, Xq = _operands(orc, 425, N, K, 1)
-    got = _gpu(dg, dev, Wq, Xq, N, K, 1, launch=dict(variant=21, grid=1, block=64))
-    assert_close(got[0], orc.gemv_q8_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, "one wave, 300 rows")
+    got = _gpu(dg, dev, Wq, Xq, N, K, 1, launch=launch)
+    assert_close(got[0], orc.gemv_q8_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"300 rows {launch}")
+
+
+@pytest.mark.parametrize("N,K", [(1, 256), (7, 4096), (70, 4352), (33, 8192), (64, 12288), (19, 14336),
+                                 (5, 16384), (130, 2304)])
+@pytest.mark.parametrize("launch", [dict(variant=23), dict(variant=23, unroll=2), dict(variant=23, unroll=4),
+                                    dict(variant=23, grid=2, block=128), dict(variant=23, unroll=2, grid=3, block=192)])
+def test_q8_0_m1_units(dg, dev, orc, N, K, launch):
+    Wq, Xq = _operands(orc, 428, N, K, 1)
+    got = _gpu(dg, dev, Wq, Xq, N, K, 1, launch=launch)
+    assert_close(got[0], orc.gemv_q8_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"{N}x{K} {launch}")
 
 
 MFMA_CFGS = [dict(variant=22)] + [dict(variant=22, unroll=_unroll(*c)) for c in MFMA_TABLE]
@@ -147,7 +159,8 @@ def test_q8_0_overrides_beyond_kernel_limits_are_rejected(dg, dev):
     Y = torch.zeros(24 * N, dtype=torch.float32, device=dev)
     for M, launch in ((1, dict(variant=21, block=512)), (2, dict(variant=21)), (1, dict(variant=12)),
                       (4, dict(variant=22, unroll=40421)), (12, dict(variant=22, unroll=11611)),
-                      (4, dict(variant=22, block=256)), (1, dict(variant=99))):
+                      (4, dict(variant=22, block=256)), (1, dict(variant=99)), (2, dict(variant=23)),
+                      (1, dict(variant=23, unroll=5))):
         with pytest.raises(dg.DGError) as e:
             dg.dg_gemv_q8_0(W, X, Y, N, K, M, launch=launch)
         assert e.value.status == dg.DG_ERR_ARG, launch
