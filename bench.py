@@ -589,6 +589,12 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
 
 
 
+# matrix-core configurations built for Q8_0 weights (larger weight buffers than Q4_0)
+MFMA_BUILT_Q8 = {(1, 16, 1, 8): 8, (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (1, 8, 2, 8): 8, (2, 4, 2, 8): 16,
+                 (4, 2, 2, 8): 24, (8, 1, 2, 8): 24, (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24,
+                 (1, 4, 2, 8): 24}
+
+
 def bytes_q8_0(N, K, M):
     return 34 * N * K // 32 + M * 36 * K // 32 + 4 * M * N
 
@@ -623,6 +629,16 @@ def suite_q8_0(dg, torch, emit, ceil_gbps):
             prev = cps
             emit(record(f"gemv_q8_0 {N}x{K}", us, iqr, bytes_q8_0(N, K, M), ceil_gbps, M=M, copies=nc,
                         variant="default", columns_per_s=round(cps, 1), change_vs_prev_M=dip))
+            if M in (2, 8, 16, 24):
+                for (rt, ks, d, cb), mmax in MFMA_BUILT_Q8.items():
+                    if M > mmax:
+                        continue
+                    launch = dict(variant=22, unroll=rt * 10000 + ks * 100 + d * 10 + cb // 8)
+                    calls = [(lambda c=c, launch=launch: dg.dg_gemv_q8_0(Wq[c % nc], Xq, Y, N, K, M, launch=launch))
+                             for c in range(max(nc, 20))]
+                    us, iqr = time_per_call(calls)
+                    emit(record(f"gemv_q8_0 {N}x{K}", us, iqr, bytes_q8_0(N, K, M), ceil_gbps, M=M, copies=nc,
+                                variant="mfma", RT=rt, KS=ks, DEPTH=d, CB=cb))
         del Wq
         torch.cuda.empty_cache()
 

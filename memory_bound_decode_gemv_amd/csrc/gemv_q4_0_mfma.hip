@@ -383,12 +383,19 @@ hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float
         DEPTH = (unroll / 10) % 10;
         CB = (unroll % 10) * 8;
     } else {
-        // Measured on MI355X (Q4_0, decoder shapes, M = 2..24): split K over 8
+        // Measured on MI355X (decoder shapes, M = 2..24).  Q4_0: split K over 8
         // waves (4 for 9..16 columns) when there are few row tiles; share each
         // activation chunk between two row tiles when there are many.
         const int tiles = (N + 15) / 16;
         CB = 8;
-        if (tiles <= 512) {
+        if (WF::kBlockBytes == 34) {
+            // Q8_0 (measured): its weight buffers are twice those of Q4_0, so
+            // fewer parts of K share a workgroup's LDS.
+            DEPTH = 2;
+            if (tiles <= 512) { RT = 1; KS = 4; }
+            else if (M <= 16) { RT = 2; KS = 2; }
+            else { RT = 4; KS = 2; }
+        } else if (tiles <= 512) {
             RT = 1;
             KS = (M <= 8 || M > 16) ? 8 : 4;
             DEPTH = M > 16 ? 1 : 2;
