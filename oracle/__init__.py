@@ -77,6 +77,7 @@ def _bind(lib):
     lib.orc_dequant_q8_0_block.argtypes = [P, P]
     lib.orc_quantize_q8_0.argtypes = [P, P, I64, I64]
     lib.orc_argmax_rows.argtypes = [P, P, I64, I64, I64]
+    lib.orc_argcompare_rows.argtypes = [P, ctypes.c_int, ctypes.c_int, P, I64, I64, I64]
     lib.orc_checksum_u32.argtypes = [P, ctypes.c_size_t]
     lib.orc_checksum_u32.restype = ctypes.c_uint32
     return lib
@@ -254,6 +255,26 @@ def argmax_rows(x: np.ndarray, C: int | None = None, ld: int | None = None) -> n
     assert C >= 1 and ld >= C
     idx = np.zeros(R, dtype=np.int64)
     _load().orc_argmax_rows(_ptr(a), _ptr(idx), R, C, ld)
+    return idx
+
+
+ARG_DTYPES = {"f32": (0, np.float32), "f16": (1, np.uint16), "bf16": (2, np.uint16)}
+
+
+def argcompare_rows(x: np.ndarray, dtype: str = "f32", op: str = "max", C: int | None = None,
+                    ld: int | None = None) -> np.ndarray:
+    """int64 index of the first maximum / minimum of each row.  x holds float32
+    values ("f32") or binary16 / bfloat16 bit patterns (uint16)."""
+    code, npt = ARG_DTYPES[dtype]
+    a = _c(x, npt)
+    if a.ndim == 1:
+        a = a.reshape(1, -1)
+    R = a.shape[0]
+    ld = a.shape[1] if ld is None else ld
+    C = a.shape[1] if C is None else C
+    assert C >= 1 and ld >= C
+    idx = np.zeros(R, dtype=np.int64)
+    _load().orc_argcompare_rows(_ptr(a), code, {"max": 0, "min": 1}[op], _ptr(idx), R, C, ld)
     return idx
 
 

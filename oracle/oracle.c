@@ -301,6 +301,28 @@ void orc_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t
     }
 }
 
+static double argcompare_value(const void* x, int dtype, int64_t i)
+{
+    if (dtype == 1) return orc_half_to_double(((const uint16_t*)x)[i]);
+    if (dtype == 2) return orc_bf16_to_double(((const uint16_t*)x)[i]);
+    return (double)((const float*)x)[i];
+}
+
+void orc_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int64_t R, int64_t C, int64_t ld)
+{
+    for (int64_t r = 0; r < R; ++r) {
+        int64_t best = 0;
+        double bv = argcompare_value(x, dtype, r * ld);
+        for (int64_t c = 1; c < C; ++c) {
+            if (isnan(bv)) break;                 /* the first NaN wins */
+            double v = argcompare_value(x, dtype, r * ld + c);
+            /* only a strictly more extreme value replaces */
+            if (isnan(v) || (op == 0 ? v > bv : v < bv)) { bv = v; best = c; }
+        }
+        idx[r] = best;
+    }
+}
+
 /* ---------------------------------------------------------------------- */
 /* Streaming-read checksum                                                */
 /* ---------------------------------------------------------------------- */

@@ -122,6 +122,16 @@ void orc_quantize_q8_0(const float* w, uint8_t* Wq, int64_t N, int64_t K);
  * than every number and the first NaN of a row wins.  C >= 1. */
 void orc_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld);
 
+/* ArgCompare over rows of float32, binary16 or bfloat16 values (IREE
+ * discussion "ArgCompare Benchmark Results and Performance Analysis": argmax
+ * and argmin over the last axis, inputs in f32/f16/bf16, int64 out).
+ * dtype: 0 = float32, 1 = binary16, 2 = bfloat16; op: 0 = max, 1 = min.
+ * idx[r] = the lowest c < C whose value equals the row's maximum (op 0) or
+ * minimum (op 1); values are decoded exactly and compared as IEEE numbers
+ * (-0 equals +0); a NaN counts as the extreme for both ops (it propagates)
+ * and the first NaN of a row wins.  x points to R rows of ld elements. */
+void orc_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int64_t R, int64_t C, int64_t ld);
+
 /* ---- streaming-read checksum ---- */
 
 /* Wrapping (mod 2^32) sum of n 32-bit words. */

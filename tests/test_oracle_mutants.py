@@ -51,6 +51,12 @@ MUTANTS = [
      "const uint8_t* wb = Wq + (n * nb + b) * 34;\n                const uint8_t* xb = Xq + b * 36;"),
     ("q8_0 quantiser rounds half to even", "c = (int)roundf(x[j] / d);   /* halves away from zero */",
      "c = (int)rintf(x[j] / d);"),
+    ("argcompare min compares like max", "(op == 0 ? v > bv : v < bv)", "(op == 0 ? v > bv : v > bv)"),
+    ("argcompare min keeps the last tie", "(op == 0 ? v > bv : v < bv)", "(op == 0 ? v > bv : v <= bv)"),
+    ("argcompare bfloat16 decoded as binary16", "if (dtype == 2) return orc_bf16_to_double(((const uint16_t*)x)[i]);",
+     "if (dtype == 2) return orc_half_to_double(((const uint16_t*)x)[i]);"),
+    ("argcompare ignores ld", "double v = argcompare_value(x, dtype, r * ld + c);",
+     "double v = argcompare_value(x, dtype, r * C + c);"),
     ("checksum xor instead of add", "for (size_t i = 0; i < n; ++i) s += w[i];", "for (size_t i = 0; i < n; ++i) s ^= w[i];"),
 ]
 

@@ -415,6 +415,59 @@ def test_argmax_is_invariant_under_any_chunking(orc):
         assert best == whole
 
 
+def _golden_argcompare():
+    with open(os.path.join(GOLDEN, "argcompare_rows.json")) as f:
+        return json.load(f)
+
+
+def test_argcompare_hand_rows(orc):
+    g = _golden_argcompare()
+    for r in g["f32_min_rows"]:
+        x = np.array([_parse(v) for v in r["x"]], dtype=np.float32)
+        assert orc.argcompare_rows(x, "f32", "min")[0] == r["idx"], r
+    for r in g["bits_rows"]:
+        bits = np.array([int(b, 16) for b in r["bits"]], dtype=np.uint16)
+        assert orc.argcompare_rows(bits, r["dtype"], r["op"])[0] == r["idx"], r
+    # argmax on float32 is the argmax routine's own definition
+    with open(os.path.join(GOLDEN, "argmax_rows.json")) as f:
+        for r in json.load(f)["rows"]:
+            x = np.array([_parse(v) for v in r["x"]], dtype=np.float32)
+            assert orc.argcompare_rows(x, "f32", "max")[0] == r["idx"], r
+
+
+def test_argcompare_against_numpy_every_dtype_with_heavy_ties(orc):
+    g = np.random.default_rng(43)
+    R, C, ld = 120, 61, 64
+    for op in ("max", "min"):
+        npfn = np.argmax if op == "max" else np.argmin
+        v = (g.integers(0, 3, size=(R, ld)) - 1).astype(np.float32)
+        v[:, C:] = np.nan                                 # padding beyond C must be ignored
+        v[3, 20] = np.nan
+        v[4, [2, 30]] = np.nan
+        v[5, :] = -0.0
+        v[5, 11] = 0.0
+        h = v.astype(np.float16)
+        b = (v.view(np.uint32) >> 16).astype(np.uint16)   # exact: these values fit in bfloat16
+        ref = npfn(v[:, :C], axis=1)                      # numpy: first extreme, first NaN
+        assert np.array_equal(orc.argcompare_rows(v, "f32", op, C=C, ld=ld), ref)
+        assert np.array_equal(orc.argcompare_rows(h.view(np.uint16), "f16", op, C=C, ld=ld),
+                              npfn(h[:, :C], axis=1))
+        assert np.array_equal(orc.argcompare_rows(b, "bf16", op, C=C, ld=ld), ref)
+
+
+def test_argmin_is_argmax_of_the_negation(orc):
+    """-x reverses every comparison and keeps NaN a NaN and +-0 equal, so the
+    first minimum of x is the first maximum of -x, bit patterns included."""
+    g = np.random.default_rng(47)
+    x = g.integers(-3, 4, size=(50, 200)).astype(np.float32) * np.float32(0.5)
+    x[1, 7] = np.nan
+    x[2, :] = 0.0
+    x[2, 5] = -0.0
+    assert np.array_equal(orc.argcompare_rows(x, "f32", "min"), orc.argmax_rows(-x))
+    h = x.astype(np.float16).view(np.uint16)
+    assert np.array_equal(orc.argcompare_rows(h, "f16", "min"), orc.argcompare_rows(h ^ np.uint16(0x8000), "f16", "max"))
+
+
 # ---------------------------------------------------------------------------
 # streaming-read checksum
 # ---------------------------------------------------------------------------
