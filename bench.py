@@ -691,7 +691,19 @@ def suite_argmax(dg, torch, emit, ceil_gbps):
             emit(record(f"argmax_rows [{R},{C}]", us, iqr, nb, ceil_gbps, cache="cold", copies=ncold))
         del xs
         torch.cuda.empty_cache()
-
+    # ArgCompare on the discussion's 16-bit shapes, and argmin
+    for (R, C, dt, op) in [(1, 128000, torch.bfloat16, "max"), (32, 128000, torch.bfloat16, "max"),
+                           (1, 128000, torch.float16, "min"), (64, 1000000, torch.float32, "min")]:
+        x = synth.gpu_uniform((5, synth.KIND_X, 0, 0), (R, C), -10.0, 10.0).to(dt)
+        idx = torch.empty(R, dtype=torch.int64, device="cuda")
+        ws = torch.zeros(max(8, dg.dg_argmax_workspace_bytes(R, C)), dtype=torch.uint8, device="cuda")
+        nb = x.element_size() * R * C + 8 * R
+        calls = [(lambda: dg.dg_argcompare_rows(x, idx, op=op, ws=ws))] * 20
+        us, iqr = time_per_call(calls)
+        emit(record(f"argcompare_rows {op} {str(dt).replace('torch.', '')} [{R},{C}]", us, iqr, nb, ceil_gbps,
+                    cache="hot"))
+        del x
+        torch.cuda.empty_cache()
 
 
 def suite_tail(dg, torch, emit, ceil_gbps):

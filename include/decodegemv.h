@@ -217,6 +217,33 @@ dg_status dg_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C,
                          int64_t ld, void* ws, size_t ws_bytes, dg_stream stream);
 
 /* ------------------------------------------------------------------------
+ * ArgCompare over rows: argmax or argmin of float32, binary16 or bfloat16
+ *
+ *   idx[r] = min{ c < C : x[r*ld + c] = max (or min) over c' < C of x[r*ld + c'] }
+ *
+ * The census of the IREE discussion "ArgCompare Benchmark Results and
+ * Performance Analysis" lists argmax and argmin over the last axis of f16,
+ * bf16 and f32 tensors with an int64 result; this is that operation.  The
+ * 16-bit inputs are widened exactly; comparisons are IEEE (-0 equals +0); a
+ * NaN counts as the extreme for both operations (it propagates) and the
+ * first NaN of a row wins.  Same split reduction as dg_argmax_rows.
+ *
+ *   x        device, R rows of ld elements of `dtype`, aligned to the
+ *            element size.
+ *   dtype    DG_DTYPE_F32, DG_DTYPE_F16 or DG_DTYPE_BF16.
+ *   op       DG_ARG_MAX or DG_ARG_MIN.
+ *   idx, R, C, ld, ws, ws_bytes  as for dg_argmax_rows (the workspace size
+ *            is dg_argmax_workspace_bytes(R, C) for every dtype).
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_WORKSPACE,
+ * DG_ERR_ARG (unknown dtype or op), DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+enum { DG_DTYPE_F32 = 0, DG_DTYPE_F16 = 1, DG_DTYPE_BF16 = 2 };
+enum { DG_ARG_MAX = 0, DG_ARG_MIN = 1 };
+
+dg_status dg_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int64_t R, int64_t C,
+                             int64_t ld, void* ws, size_t ws_bytes, dg_stream stream);
+
+/* ------------------------------------------------------------------------
  * Launch overrides (measurement and A/B runs)
  *
  * The *_ex variants take a launch configuration instead of the library's

@@ -30,6 +30,12 @@ DG_READ_GRID_STRIDE = 2
 DG_READ_DEEP = 4
 DG_READ_DEFAULT_GRID = 1024
 
+DG_DTYPE_F32 = 0
+DG_DTYPE_F16 = 1
+DG_DTYPE_BF16 = 2
+DG_ARG_MAX = 0
+DG_ARG_MIN = 1
+
 DG_VARIANT_DENSE_WIDE = 1
 DG_VARIANT_DENSE_XREG = 2
 DG_VARIANT_DENSE_NARROW1 = 3
@@ -51,6 +57,7 @@ EXPORTED = (
     "dg_argmax_workspace_bytes", "dg_argmax_rows",
     "dg_gemv_f16_ex", "dg_gemv_bf16_ex", "dg_gemv_q4_0_ex",
     "dg_gemv_q8_0", "dg_gemv_q8_0_ex", "dg_quantize_q8_0",
+    "dg_argcompare_rows",
 )
 
 
@@ -127,6 +134,8 @@ def _lib():
     lib.dg_argmax_workspace_bytes.restype = ctypes.c_size_t
     lib.dg_argmax_rows.argtypes = [P, P, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.dg_argmax_rows.restype = st
+    lib.dg_argcompare_rows.argtypes = [P, I32, I32, P, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.dg_argcompare_rows.restype = st
     _handle = lib
     return lib
 
@@ -336,4 +345,32 @@ def dg_argmax_rows(x, idx, R=None, C=None, ld=None, ws=None, stream=None):
     ws_bytes = ws.numel() * ws.element_size()
     _check(_lib().dg_argmax_rows(_ptr(x), _ptr(idx), int(R), int(C), int(ld), _ptr(ws), ws_bytes,
                                  _stream(stream)), "dg_argmax_rows")
+    return idx
+
+
+def dg_argcompare_rows(x, idx, op="max", R=None, C=None, ld=None, ws=None, stream=None):
+    """idx[R] (int64) = lowest index of each row's maximum (op "max") or minimum
+    (op "min") of x (float32, float16 or bfloat16 [R][ld]); a NaN wins for both.
+    ws: a device workspace of dg_argmax_workspace_bytes(R, C) bytes."""
+    torch = _torch()
+    _need(x, (torch.float32, torch.float16, torch.bfloat16), "x")
+    _need(idx, (torch.int64,), "idx")
+    dtype = {torch.float32: DG_DTYPE_F32, torch.float16: DG_DTYPE_F16, torch.bfloat16: DG_DTYPE_BF16}[x.dtype]
+    if R is None:
+        R = x.shape[0] if x.dim() == 2 else 1
+    if C is None:
+        C = x.shape[-1]
+    if ld is None:
+        ld = x.shape[-1]
+    R, C, ld = int(R), int(C), int(ld)
+    if R > 0 and C > 0 and ld >= C:
+        _fits(x, ((R - 1) * ld + C) * x.element_size(), "x")
+        _fits(idx, R * 8, "idx")
+    need = dg_argmax_workspace_bytes(R, C)
+    if ws is None:
+        raise ValueError(f"dg_argcompare_rows needs a device workspace of {need} bytes")
+    _need(ws, (torch.uint8, torch.int64), "ws")
+    ws_bytes = ws.numel() * ws.element_size()
+    _check(_lib().dg_argcompare_rows(_ptr(x), dtype, {"max": DG_ARG_MAX, "min": DG_ARG_MIN}[op], _ptr(idx),
+                                     R, C, ld, _ptr(ws), ws_bytes, _stream(stream)), "dg_argcompare_rows")
     return idx

@@ -197,6 +197,20 @@ dg_status dg_quantize_q8_0(const float* w, void* Wq, int64_t N, int64_t K, dg_st
 
 size_t dg_argmax_workspace_bytes(int64_t R, int64_t C) { return argmax_workspace_bytes(R, C); }
 
+dg_status dg_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int64_t R, int64_t C, int64_t ld,
+                             void* ws, size_t ws_bytes, dg_stream stream) {
+    if (dtype != DG_DTYPE_F32 && dtype != DG_DTYPE_F16 && dtype != DG_DTYPE_BF16) return DG_ERR_ARG;
+    if (op != DG_ARG_MAX && op != DG_ARG_MIN) return DG_ERR_ARG;
+    if (R < 0 || R > kI32Max || C < 1 || C >= kI32Max || ld < C) return DG_ERR_SHAPE;
+    if (R == 0) return DG_OK;
+    if (!x || !idx) return DG_ERR_NULL;
+    if (!aligned(x, dtype == DG_DTYPE_F32 ? 4 : 2) || !aligned(idx, 8)) return DG_ERR_MISALIGNED;
+    const size_t need = argmax_workspace_bytes(R, C);
+    if (need > 0 && (!ws || ws_bytes < need)) return DG_ERR_WORKSPACE;
+    if (ws && !aligned(ws, 8)) return DG_ERR_MISALIGNED;
+    return hip_status(launch_argcompare_rows(x, dtype, op, idx, R, C, ld, ws, (hipStream_t)stream));
+}
+
 dg_status dg_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld, void* ws,
                          size_t ws_bytes, dg_stream stream) {
     if (R < 0 || R > kI32Max || C < 1 || C >= kI32Max || ld < C) return DG_ERR_SHAPE;

@@ -60,27 +60,69 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v) {
     return r;
 }
 
+// Input element types: decode(raw) is exact (binary16 and bfloat16 widen to
+// binary32 without rounding); a 16-byte vector holds kPerVec elements.
+struct ElemF32 {
+    using raw = float;
+    static constexpr int kPerVec = 4;
+    __device__ __forceinline__ static float load(const raw* p) { return *p; }
+    __device__ __forceinline__ static float from_vec(const u32x4& v, int j) {
+        const uint32_t w = j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+        return __builtin_bit_cast(float, w);
+    }
+};
+struct ElemF16 {
+    using raw = uint16_t;
+    static constexpr int kPerVec = 8;
+    __device__ __forceinline__ static float load(const raw* p) { return (float)__builtin_bit_cast(_Float16, *p); }
+    __device__ __forceinline__ static float from_vec(const u32x4& v, int j) {
+        const uint32_t w = (j >> 1) == 0 ? v.x : (j >> 1) == 1 ? v.y : (j >> 1) == 2 ? v.z : v.w;
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * (j & 1))));
+    }
+};
+struct ElemBF16 {
+    using raw = uint16_t;
+    static constexpr int kPerVec = 8;
+    __device__ __forceinline__ static float load(const raw* p) { return __builtin_bit_cast(float, (uint32_t)*p << 16); }
+    __device__ __forceinline__ static float from_vec(const u32x4& v, int j) {
+        const uint32_t w = (j >> 1) == 0 ? v.x : (j >> 1) == 1 ? v.y : (j >> 1) == 2 ? v.z : v.w;
+        return __builtin_bit_cast(float, (j & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+};
+
+// The 32-bit image an element contributes to the key: larger image = more
+// extreme value (MIN reverses the order of numbers); every NaN maps to the
+// top, so a NaN wins for both operations.
+template <bool MIN>
+__device__ __forceinline__ uint32_t extreme_image(float v) {
+    if (v != v) return 0xFFFFFFFFu;
+    const uint32_t img = order_image(v);   // never 0xFFFFFFFF for a number
+    return MIN ? ~img : img;
+}
+
 // Pass 1: workgroup (s, r) reduces elements [s*chunk, min(C, (s+1)*chunk)) of
-// row r into one key.  VEC: rows are 16-byte aligned and chunk % 4 == 0, so
-// every thread reads float4s; each thread visits its elements in increasing
-// index order and keeps the first of equal maxima.
-template <bool VEC>
+// row r into one key.  VEC: rows are 16-byte aligned and C is a multiple of
+// the elements per 16-byte vector, so every thread reads whole vectors; each
+// thread visits its elements in increasing index order and keeps the first
+// of equal extremes.
+template <class E, bool MIN, bool VEC>
 __global__ void __launch_bounds__(kArgBlock)
-k_argmax_partial(const float* __restrict__ x, uint64_t* __restrict__ ws, int C, int64_t ld, int chunk) {
+k_argcmp_partial(const typename E::raw* __restrict__ x, uint64_t* __restrict__ ws, int C, int64_t ld, int chunk) {
+    constexpr int kP = E::kPerVec;
     const int r = blockIdx.y;
     const int s = blockIdx.x;
-    const float* __restrict__ row = x + (int64_t)r * ld;
+    const typename E::raw* __restrict__ row = x + (int64_t)r * ld;
     const int c0 = s * chunk;
     const int c1 = min(C, c0 + chunk);
     uint32_t best = 0u, bidx = 0xFFFFFFFFu;
     if constexpr (VEC) {
-        constexpr int kU = 4;   // float4 loads in flight per thread
-        const float4* __restrict__ rv = reinterpret_cast<const float4*>(row);
-        const int v0 = c0 >> 2;
-        const int v1 = (c1 + 3) >> 2;   // the last vector may be partial
-        const int vlast = (C - 1) >> 2;
+        constexpr int kU = 4;   // 16-byte loads in flight per thread
+        const u32x4* __restrict__ rv = reinterpret_cast<const u32x4*>(row);
+        const int v0 = c0 / kP;
+        const int v1 = (c1 + kP - 1) / kP;   // the last vector may be partial
+        const int vlast = (C - 1) / kP;
         for (int vb = v0 + threadIdx.x; vb < v1; vb += kU * kArgBlock) {
-            float4 f[kU];
+            u32x4 f[kU];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int v = vb + u * kArgBlock;
@@ -89,18 +131,17 @@ k_argmax_partial(const float* __restrict__ x, uint64_t* __restrict__ ws, int C, 
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int v = vb + u * kArgBlock;
-                const float e[4] = {f[u].x, f[u].y, f[u].z, f[u].w};
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int c = 4 * v + j;
-                    const uint32_t img = order_image(e[j]);
+                for (int j = 0; j < kP; ++j) {
+                    const int c = kP * v + j;
+                    const uint32_t img = extreme_image<MIN>(E::from_vec(f[u], j));
                     if (v < v1 && c < c1 && img > best) { best = img; bidx = (uint32_t)c; }
                 }
             }
         }
     } else {
         for (int c = c0 + threadIdx.x; c < c1; c += kArgBlock) {
-            const uint32_t img = order_image(row[c]);
+            const uint32_t img = extreme_image<MIN>(E::load(row + c));
             if (img > best) { best = img; bidx = (uint32_t)c; }
         }
     }
@@ -135,21 +176,24 @@ size_t argmax_workspace_bytes(int64_t R, int64_t C) {
     return (size_t)(R * S) * sizeof(uint64_t);
 }
 
-hipError_t launch_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld,
-                              void* ws, hipStream_t s) {
+namespace {
+
+template <class E, bool MIN>
+hipError_t launch_argcmp(const void* xv, int64_t* idx, int64_t R, int64_t C, int64_t ld, void* ws, hipStream_t s) {
+    const typename E::raw* x = (const typename E::raw*)xv;
     const int chunk = pick_chunk(R, C);
     const int S = (int)((C + chunk - 1) / chunk);
-    // float4 path only when no vector can reach past column C-1 of any row
-    const bool vec = ((uintptr_t)x % 16 == 0) && (ld % 4 == 0) && (C % 4 == 0);
+    // vector path only when no vector can reach past column C-1 of any row
+    const bool vec = ((uintptr_t)x % 16 == 0) && (ld % E::kPerVec == 0) && (C % E::kPerVec == 0);
     uint64_t* w = (uint64_t*)ws;
     constexpr int64_t kMaxGridY = 65535;
     for (int64_t r0 = 0; r0 < R; r0 += kMaxGridY) {   // grid.y is limited to 65535 rows per launch
         const int64_t rn = R - r0 < kMaxGridY ? R - r0 : kMaxGridY;
         dim3 g1((unsigned)S, (unsigned)rn);
-        const float* xr = x + r0 * ld;
+        const typename E::raw* xr = x + r0 * ld;
         uint64_t* wr = w + r0 * S;
-        if (vec) hipLaunchKernelGGL(k_argmax_partial<true>, g1, dim3(kArgBlock), 0, s, xr, wr, (int)C, ld, chunk);
-        else hipLaunchKernelGGL(k_argmax_partial<false>, g1, dim3(kArgBlock), 0, s, xr, wr, (int)C, ld, chunk);
+        if (vec) hipLaunchKernelGGL((k_argcmp_partial<E, MIN, true>), g1, dim3(kArgBlock), 0, s, xr, wr, (int)C, ld, chunk);
+        else hipLaunchKernelGGL((k_argcmp_partial<E, MIN, false>), g1, dim3(kArgBlock), 0, s, xr, wr, (int)C, ld, chunk);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -157,6 +201,27 @@ hipError_t launch_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C
     hipLaunchKernelGGL(k_argmax_final, dim3((unsigned)((R + rows_per_block - 1) / rows_per_block)), dim3(256), 0, s,
                        (const uint64_t*)w, idx, (int)R, S);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int64_t R, int64_t C, int64_t ld,
+                                  void* ws, hipStream_t s) {
+    const bool mn = op == DG_ARG_MIN;
+    switch (dtype) {
+        case DG_DTYPE_F32: return mn ? launch_argcmp<ElemF32, true>(x, idx, R, C, ld, ws, s)
+                                     : launch_argcmp<ElemF32, false>(x, idx, R, C, ld, ws, s);
+        case DG_DTYPE_F16: return mn ? launch_argcmp<ElemF16, true>(x, idx, R, C, ld, ws, s)
+                                     : launch_argcmp<ElemF16, false>(x, idx, R, C, ld, ws, s);
+        case DG_DTYPE_BF16: return mn ? launch_argcmp<ElemBF16, true>(x, idx, R, C, ld, ws, s)
+                                      : launch_argcmp<ElemBF16, false>(x, idx, R, C, ld, ws, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld, void* ws,
+                              hipStream_t s) {
+    return launch_argcompare_rows(x, DG_DTYPE_F32, DG_ARG_MAX, idx, R, C, ld, ws, s);
 }
 
 }  // namespace dg

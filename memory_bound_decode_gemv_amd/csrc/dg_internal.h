@@ -72,5 +72,7 @@ hipError_t launch_quantize_q4_0(const float* w, void* Wq, int64_t N, int64_t K, 
 size_t argmax_workspace_bytes(int64_t R, int64_t C);
 hipError_t launch_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld,
                               void* ws, hipStream_t s);
+hipError_t launch_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int64_t R, int64_t C, int64_t ld,
+                                  void* ws, hipStream_t s);
 
 }  // namespace dg

@@ -114,6 +114,18 @@ def test_argmax_rejects_before_launch(lib):
     assert lib.dg_argmax_rows(None, None, 0, 10, 10, None, 0, None) == 0
 
 
+def test_argcompare_rejects_before_launch(lib):
+    need = lib.dg_argmax_workspace_bytes(4, 10)
+    assert lib.dg_argcompare_rows(A16, 3, 0, A16, 4, 10, 10, A16, 1 << 20, None) == 6      # unknown dtype
+    assert lib.dg_argcompare_rows(A16, 1, 2, A16, 4, 10, 10, A16, 1 << 20, None) == 6      # unknown op
+    assert lib.dg_argcompare_rows(A16, 1, 1, A16, 4, 10, 9, A16, 1 << 20, None) == 3       # ld < C
+    assert lib.dg_argcompare_rows(P(0x1001), 1, 1, A16, 4, 10, 10, A16, 1 << 20, None) == 2  # odd address
+    assert lib.dg_argcompare_rows(P(0x1002), 0, 1, A16, 4, 10, 10, A16, 1 << 20, None) == 2  # f32 needs 4
+    assert lib.dg_argcompare_rows(P(0x1002), 2, 1, A16, 4, 10, 10, None, 0, None) == (4 if need else 0)
+    assert lib.dg_argcompare_rows(None, 2, 0, A16, 4, 10, 10, A16, 1 << 20, None) == 1
+    assert lib.dg_argcompare_rows(None, 2, 0, None, 0, 10, 10, None, 0, None) == 0          # R = 0
+
+
 def test_quantisers_reject_before_launch(lib):
     assert lib.dg_quantize_q8_1(A16, A16, 2, 48, None) == 3
     assert lib.dg_quantize_q4_0(A16, A16, 2, 48, None) == 3
