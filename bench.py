@@ -720,7 +720,14 @@ def suite_tail(dg, torch, emit, ceil_gbps):
         calls.append(lambda: dg.dg_argmax_rows(logits.view(1, N), idx, ws=ws))
     us, iqr = time_per_call(calls)
     emit(record("greedy tail lm-head 128256x4096 + argmax", 2 * us, 2 * iqr,
-                bytes_dense(N, K, 4) + 4 * N + 8, ceil_gbps, note="us per token (two launches)"))
+                bytes_dense(N, K, 4) + 4 * N + 8, ceil_gbps, note="us per token (two calls)"))
+    # the fused call, logits stored and not stored
+    fws = torch.zeros(dg.dg_gemv_bf16_argmax_workspace_bytes(N, K), dtype=torch.uint8, device="cuda")
+    for name, y in (("logits stored", logits), ("logits not stored", None)):
+        calls = [(lambda c=c, y=y: dg.dg_gemv_bf16_argmax(Wb[c % nc], xb, idx, y=y, ws=fws)) for c in range(16)]
+        us, iqr = time_per_call(calls)
+        emit(record("greedy tail fused lm-head 128256x4096 + argmax", us, iqr,
+                    bytes_dense(N, K, 4 if y is not None else 0) + 8, ceil_gbps, note=f"us per token, {name}"))
 
 
 def profile_kernels(args):

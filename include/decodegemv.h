@@ -217,6 +217,35 @@ dg_status dg_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C,
                          int64_t ld, void* ws, size_t ws_bytes, dg_stream stream);
 
 /* ------------------------------------------------------------------------
+ * The greedy decode tail fused: bfloat16 lm-head GEMV and argmax of its logits
+ *
+ *   y[n] = sum_k W[n*ldw + k] * x[k]  (fp32, exactly as dg_gemv_bf16)
+ *   idx[0] = min{ n : y[n] = max_n' y[n'] }   (exactly as dg_argmax_rows on y)
+ *
+ * The last two steps of a greedy decode step: the logits of the vocabulary
+ * and the token they select ("The kernel that waited for itself" checks its
+ * small-batch kernel by the tokens it produces; the IREE discussion's census
+ * has the argmax over a 128K vocabulary).  It runs the GEMV, then the split
+ * argmax of the logits: on MI355X that is faster than argmax epilogues inside
+ * the GEMV, which were built and measured (a capped grid-stride GEMV, or one
+ * device-scope atomic max per workgroup, each cost more than the 0.5 MB
+ * argmax pass they save).
+ *
+ *   W, x, N, K, ldw  as for dg_gemv_bf16; N >= 1.
+ *   y        device float32 [N] for the logits, or NULL to skip storing them.
+ *   idx      device int64 [1], 8-byte aligned.
+ *   ws       device workspace of dg_gemv_bf16_argmax_workspace_bytes(N, K)
+ *            bytes (the logits when y is NULL, and the argmax's partials),
+ *            16-byte aligned; contents on entry do not matter; the call owns
+ *            it until the stream passes the call.
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_WORKSPACE,
+ * DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+size_t dg_gemv_bf16_argmax_workspace_bytes(int64_t N, int64_t K);
+dg_status dg_gemv_bf16_argmax(const void* W, const void* x, float* y, int64_t* idx, int64_t N, int64_t K,
+                              int64_t ldw, void* ws, size_t ws_bytes, dg_stream stream);
+
+/* ------------------------------------------------------------------------
  * ArgCompare over rows: argmax or argmin of float32, binary16 or bfloat16
  *
  *   idx[r] = min{ c < C : x[r*ld + c] = max (or min) over c' < C of x[r*ld + c'] }

@@ -57,7 +57,7 @@ EXPORTED = (
     "dg_argmax_workspace_bytes", "dg_argmax_rows",
     "dg_gemv_f16_ex", "dg_gemv_bf16_ex", "dg_gemv_q4_0_ex",
     "dg_gemv_q8_0", "dg_gemv_q8_0_ex", "dg_quantize_q8_0",
-    "dg_argcompare_rows",
+    "dg_argcompare_rows", "dg_gemv_bf16_argmax_workspace_bytes", "dg_gemv_bf16_argmax",
 )
 
 
@@ -136,6 +136,10 @@ def _lib():
     lib.dg_argmax_rows.restype = st
     lib.dg_argcompare_rows.argtypes = [P, I32, I32, P, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.dg_argcompare_rows.restype = st
+    lib.dg_gemv_bf16_argmax_workspace_bytes.argtypes = [I64, I64]
+    lib.dg_gemv_bf16_argmax_workspace_bytes.restype = ctypes.c_size_t
+    lib.dg_gemv_bf16_argmax.argtypes = [P, P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
+    lib.dg_gemv_bf16_argmax.restype = st
     _handle = lib
     return lib
 
@@ -373,4 +377,39 @@ def dg_argcompare_rows(x, idx, op="max", R=None, C=None, ld=None, ws=None, strea
     ws_bytes = ws.numel() * ws.element_size()
     _check(_lib().dg_argcompare_rows(_ptr(x), dtype, {"max": DG_ARG_MAX, "min": DG_ARG_MIN}[op], _ptr(idx),
                                      R, C, ld, _ptr(ws), ws_bytes, _stream(stream)), "dg_argcompare_rows")
+    return idx
+
+
+def dg_gemv_bf16_argmax_workspace_bytes(N, K):
+    return int(_lib().dg_gemv_bf16_argmax_workspace_bytes(int(N), int(K)))
+
+
+def dg_gemv_bf16_argmax(W, x, idx, y=None, N=None, K=None, ldw=None, ws=None, stream=None):
+    """The fused greedy tail: idx[0] (int64) = argmax over n of y[n] = W[n] . x
+    (bfloat16 operands, fp32 logits stored in y unless y is None)."""
+    torch = _torch()
+    _need(W, (torch.bfloat16,), "W")
+    _need(x, (torch.bfloat16,), "x")
+    _need(idx, (torch.int64,), "idx")
+    if y is not None:
+        _need(y, (torch.float32,), "y")
+    if N is None:
+        N = W.shape[0]
+    if K is None:
+        K = x.numel()
+    if ldw is None:
+        ldw = W.shape[1] if W.dim() == 2 else K
+    N, K, ldw = int(N), int(K), int(ldw)
+    if N > 0 and K > 0 and 0 <= K <= ldw:
+        _fits(W, ((N - 1) * ldw + K) * 2, "W")
+        _fits(x, K * 2, "x")
+    if y is not None:
+        _fits(y, max(N, 0) * 4, "y")
+    _fits(idx, 8, "idx")
+    if ws is None:
+        raise ValueError(f"dg_gemv_bf16_argmax needs a device workspace of "
+                         f"{dg_gemv_bf16_argmax_workspace_bytes(N, K)} bytes")
+    _need(ws, (torch.uint8, torch.int64), "ws")
+    _check(_lib().dg_gemv_bf16_argmax(_ptr(W), _ptr(x), _ptr(y), _ptr(idx), N, K, ldw, _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)), "dg_gemv_bf16_argmax")
     return idx

@@ -197,6 +197,36 @@ dg_status dg_quantize_q8_0(const float* w, void* Wq, int64_t N, int64_t K, dg_st
 
 size_t dg_argmax_workspace_bytes(int64_t R, int64_t C) { return argmax_workspace_bytes(R, C); }
 
+// The greedy tail as one call: the GEMV, then the split argmax of its
+// logits.  (Argmax epilogues inside the GEMV were measured and were slower on
+// MI355X: a grid-stride GEMV capped at 2048 workgroups, 167 us, and one
+// device-scope atomic max per workgroup, 177 us, against 153 us for this.)
+// Workspace: the logits when the caller stores none, then the argmax's.
+size_t tail_logits_bytes(int64_t N) { return ((size_t)N * sizeof(float) + 15) & ~(size_t)15; }
+
+size_t dg_gemv_bf16_argmax_workspace_bytes(int64_t N, int64_t K) {
+    (void)K;
+    if (N < 1) return 0;
+    return tail_logits_bytes(N) + argmax_workspace_bytes(1, N);
+}
+
+dg_status dg_gemv_bf16_argmax(const void* W, const void* x, float* y, int64_t* idx, int64_t N, int64_t K,
+                              int64_t ldw, void* ws, size_t ws_bytes, dg_stream stream) {
+    if (N < 1 || N > kI32Max || K < 0 || K > kI32Max || K % 8 != 0 || ldw < K || ldw % 8 != 0)
+        return DG_ERR_SHAPE;
+    if (!idx || (K > 0 && (!W || !x))) return DG_ERR_NULL;
+    if (!aligned(idx, 8) || (y && !aligned(y, 4))) return DG_ERR_MISALIGNED;
+    if (K > 0 && (!aligned(W, 16) || !aligned(x, 16))) return DG_ERR_MISALIGNED;
+    const size_t need = dg_gemv_bf16_argmax_workspace_bytes(N, K);
+    if (!ws || ws_bytes < need) return DG_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return DG_ERR_MISALIGNED;
+    float* logits = y ? y : (float*)ws;
+    void* aws = (uint8_t*)ws + tail_logits_bytes(N);
+    dg_status st = gemv_dense_checked(true, W, x, logits, N, K, ldw, nullptr, stream);
+    if (st != DG_OK) return st;
+    return hip_status(launch_argmax_rows(logits, idx, 1, N, N, aws, (hipStream_t)stream));
+}
+
 dg_status dg_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int64_t R, int64_t C, int64_t ld,
                              void* ws, size_t ws_bytes, dg_stream stream) {
     if (dtype != DG_DTYPE_F32 && dtype != DG_DTYPE_F16 && dtype != DG_DTYPE_BF16) return DG_ERR_ARG;

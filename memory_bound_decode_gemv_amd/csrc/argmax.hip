@@ -14,6 +14,7 @@
 // to the largest image (a NaN beats every number; among NaNs the lowest index
 // wins).  The maximum of keys is order-independent, so the split into chunks
 // and the order of the merges cannot change the result.
+#include "argkey.h"
 #include "dg_device.h"
 #include "dg_internal.h"
 
@@ -24,29 +25,6 @@ constexpr int kArgBlock = 256;
 constexpr int kMaxChunk = 16384;
 constexpr int kMinChunk = 1024;
 constexpr int kTargetGroups = 256;
-
-__device__ __forceinline__ uint32_t order_image(float v) {
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    if (v != v) return 0xFFFFFFFFu;       // NaN above everything
-    if (u == 0x80000000u) u = 0u;         // -0 == +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ uint64_t pack_key(uint32_t img, uint32_t idx) {
-    return ((uint64_t)img << 32) | (uint64_t)(0xFFFFFFFFu - idx);
-}
-
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off, kWave);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off, kWave);
-        v = umax64(v, ((uint64_t)hi << 32) | lo);
-    }
-    return v;
-}
 
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v) {
     __shared__ uint64_t part[kArgBlock / kWave];
@@ -158,7 +136,7 @@ k_argmax_final(const uint64_t* __restrict__ ws, int64_t* __restrict__ idx, int R
     uint64_t best = 0ull;
     for (int s = lane_id(); s < S; s += kWave) best = umax64(best, kr[s]);
     best = wave_max_u64(best);
-    if (lane_id() == 0) idx[r] = (int64_t)(0xFFFFFFFFu - (uint32_t)best);
+    if (lane_id() == 0) idx[r] = (int64_t)key_index(best);
 }
 
 int pick_chunk(int64_t R, int64_t C) {

@@ -126,6 +126,18 @@ def test_argcompare_rejects_before_launch(lib):
     assert lib.dg_argcompare_rows(None, 2, 0, None, 0, 10, 10, None, 0, None) == 0          # R = 0
 
 
+def test_fused_tail_rejects_before_launch(lib):
+    need = lib.dg_gemv_bf16_argmax_workspace_bytes(100, 64)
+    assert need >= 400 + lib.dg_argmax_workspace_bytes(1, 100)
+    assert lib.dg_gemv_bf16_argmax_workspace_bytes(0, 64) == 0
+    assert lib.dg_gemv_bf16_argmax(A16, A16, A16, A16, 0, 64, 64, A16, need, None) == 3      # N = 0
+    assert lib.dg_gemv_bf16_argmax(A16, A16, A16, A16, 100, 60, 64, A16, need, None) == 3    # K % 8
+    assert lib.dg_gemv_bf16_argmax(A16, A16, A16, None, 100, 64, 64, A16, need, None) == 1   # no idx
+    assert lib.dg_gemv_bf16_argmax(A16, A16, None, P(0x1004), 100, 64, 64, A16, need, None) == 2
+    assert lib.dg_gemv_bf16_argmax(A16, A16, None, A16, 100, 64, 64, A16, need - 1, None) == 4
+    assert lib.dg_gemv_bf16_argmax(A16, A16, None, A16, 100, 64, 64, None, need, None) == 4
+
+
 def test_quantisers_reject_before_launch(lib):
     assert lib.dg_quantize_q8_1(A16, A16, 2, 48, None) == 3
     assert lib.dg_quantize_q4_0(A16, A16, 2, 48, None) == 3
