@@ -14,7 +14,8 @@ overhead of a per-call Python loop would otherwise dominate a 5 us kernel).
 
 Printed: ONE JSON line with the aggregate algorithmic GB/s of the step, a
 per-kernel breakdown (us/call as the median of 30 repetitions of back-to-back
-rotated calls after 10 warm-ups, GB/s, bandwidth utilisation against the
+rotated calls -- as many as the timed region holds -- after at least 10
+warm-ups and 10 ms of untimed work, GB/s, bandwidth utilisation against the
 streaming-read ceiling measured in the same run and against the 8 TB/s spec),
 the roofline of the dominant kernel (Q4_0) and the CPU oracle timed on a
 bounded sample.
@@ -59,6 +60,17 @@ def copies_for(nbytes, floor=4 * LLC_BYTES):
     return max(2, -(-floor // nbytes))
 
 
+# Launches per timed graph: enough that the fixed cost of starting one graph
+# replay (about 13 us on MI355X, measured) stays below 0.1 us per launch, as
+# in a decode step of many kernels; in whole rotations of the weight copies,
+# so every copy is read equally often.
+MIN_CALLS = 200
+
+
+def n_calls(ncopies, minimum=MIN_CALLS):
+    return ncopies * -(-minimum // ncopies)
+
+
 # ---------------------------------------------------------------------------
 # timing helpers
 # ---------------------------------------------------------------------------
@@ -88,7 +100,9 @@ def capture(calls):
 
 def time_per_call(calls, reps=30, warm=10, graph=True):
     """Median and inter-quartile range (us per call) of `reps` timed runs of the
-    back-to-back calls, after `warm` untimed runs."""
+    back-to-back calls, after at least `warm` untimed runs and at least about
+    10 ms of untimed work (the first timing after new operands were allocated
+    otherwise catches the clocks still ramping)."""
     torch = _torch()
     if graph:
         g = capture(calls)
@@ -97,7 +111,11 @@ def time_per_call(calls, reps=30, warm=10, graph=True):
         def run():
             for c in calls:
                 c()
-    for _ in range(warm):
+    t0 = time.perf_counter()
+    run()
+    torch.cuda.synchronize()
+    once = max(time.perf_counter() - t0, 1e-6)
+    for _ in range(max(warm, min(int(0.010 / once), 2000))):
         run()
     torch.cuda.synchronize()
     ts = []
@@ -238,7 +256,7 @@ def read_probe(bufs, shapes=READ_PROBE_SHAPES, records=None, label=""):
     for grid, block, flags in shapes:
         calls = [(lambda c=c, g=grid, b=block, f=flags: dg.dg_stream_read(bufs[c % n], cs, grid_blocks=g,
                                                                            block_threads=b, flags=f))
-                 for c in range(max(20, n))]
+                 for c in range(n_calls(n))]
         us, iqr = time_per_call(calls)
         cfg = dict(grid=grid, block=block, nontemporal=flags & 1, loads_per_lane=16 if flags & 4 else 8)
         if records is not None:
@@ -326,9 +344,10 @@ def headline(args):
     b16 = bytes_dense(FP16_N, FP16_K, 2)
     bq4 = bytes_q4(Q4_N, Q4_K, 1)
 
-    # per-kernel: back-to-back rotated calls (a whole rotation per timed run)
-    us16, iqr16 = time_per_call([f16_call(i) for i in range(max(20, n16))])
-    usq, iqrq = time_per_call([q4_call(i) for i in range(max(20, 3 * nq))])
+    # per kernel: as many back-to-back rotated launches as the timed region holds
+    nb = max(args.steps, MIN_CALLS)
+    us16, iqr16 = time_per_call([f16_call(i) for i in range(nb)])
+    usq, iqrq = time_per_call([q4_call(i) for i in range(nb)])
     log(f"[fp16 4096x4096] {us16:.2f} us/call, {b16 / us16 / 1e3:.0f} GB/s")
     log(f"[q4_0 28672x8192] {usq:.2f} us/call, {bq4 / usq / 1e3:.0f} GB/s")
     rp16 = read_probe(W16)
@@ -468,7 +487,7 @@ def suite_dense(dg, torch, emit, ceil_gbps):
     # the launch floor: a 16-byte read by one wave, back to back in a graph
     tiny = torch.zeros(64, dtype=torch.int32, device="cuda")
     cs = torch.zeros(1, dtype=torch.int32, device="cuda")
-    calls = [(lambda: dg.dg_stream_read(tiny, cs, nbytes=16, grid_blocks=1, block_threads=64))] * 64
+    calls = [(lambda: dg.dg_stream_read(tiny, cs, nbytes=16, grid_blocks=1, block_threads=64))] * MIN_CALLS
     us, iqr = time_per_call(calls)
     emit(record("launch floor (16-byte read, 1 wave)", us, iqr, 16, None))
 
@@ -486,18 +505,18 @@ def suite_dense(dg, torch, emit, ceil_gbps):
                     continue
                 launch = dict(v, grid=grid, block=block)
                 calls = [(lambda c=c, launch=launch: dg.dg_gemv_f16(W16[c % n16], x16, y16, launch=launch))
-                         for c in range(n16)]
+                         for c in range(n_calls(n16))]
                 us, iqr = time_per_call(calls)
                 emit(record("gemv_f16 4096x4096", us, iqr, b16, ceil_gbps, variant=vname, grid=grid, block=block))
     for unroll in (8, 4, 104, 102, 108, 302, 304):
         for block in (256, 512):
             launch = dict(variant=1, unroll=unroll, block=block)
             calls = [(lambda c=c, launch=launch: dg.dg_gemv_f16(W16[c % n16], x16, y16, launch=launch))
-                     for c in range(n16)]
+                     for c in range(n_calls(n16))]
             us, iqr = time_per_call(calls)
             emit(record("gemv_f16 4096x4096", us, iqr, b16, ceil_gbps, variant="wide", U=unroll % 100,
                         KS=unroll // 100 + 1, block=block))
-    calls = [(lambda c=c: dg.dg_gemv_f16(W16[c % n16], x16, y16)) for c in range(n16)]
+    calls = [(lambda c=c: dg.dg_gemv_f16(W16[c % n16], x16, y16)) for c in range(n_calls(n16))]
     us, iqr = time_per_call(calls)
     emit(record("gemv_f16 4096x4096", us, iqr, b16, ceil_gbps, variant="default"))
     us, iqr = time_per_call(calls, graph=False)
@@ -511,12 +530,12 @@ def suite_dense(dg, torch, emit, ceil_gbps):
         Wb, xb = dense_copies(1, N, K, nc, torch.bfloat16)
         yb = torch.empty(N, dtype=torch.float32, device="cuda")
         nb = bytes_dense(N, K, 4)
-        calls = [(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, yb)) for c in range(max(nc, 8))]
+        calls = [(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, yb)) for c in range(n_calls(nc))]
         us, iqr = time_per_call(calls)
         emit(record(f"gemv_bf16 {N}x{K}", us, iqr, nb, ceil_gbps, copies=nc, variant="default"))
         for unroll in (8, 4, 104, 108, 102, 304, 302):
             launch = dict(variant=1, unroll=unroll, block=256)
-            calls = [(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, yb, launch=launch)) for c in range(max(nc, 8))]
+            calls = [(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, yb, launch=launch)) for c in range(n_calls(nc))]
             us, iqr = time_per_call(calls)
             emit(record(f"gemv_bf16 {N}x{K}", us, iqr, nb, ceil_gbps, copies=nc, U=unroll % 100,
                         KS=unroll // 100 + 1))
@@ -539,7 +558,7 @@ def suite_q4_m1(dg, torch, emit, ceil_gbps):
                 for d in (2, 3, 4) for g in (0, 512, 768, 1024, 1792, 2048, 3584, 7168) for b in (128, 256)]
     for lname, launch in launches:
         calls = [(lambda c=c, launch=launch: dg.dg_gemv_q4_0(Wq[c % nq], Xq, Yq, Q4_N, Q4_K, 1, launch=launch))
-                 for c in range(3 * nq)]
+                 for c in range(n_calls(nq))]
         us, iqr = time_per_call(calls)
         emit(record("gemv_q4_0 28672x8192 M=1", us, iqr, bq, ceil_gbps, variant=lname))
     del Wq
@@ -563,7 +582,7 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
         for M in (1, 2, 4, 8, 12, 16, 24):
             Xq = q8_columns(3, K, M)
             Y = torch.empty(M * N, dtype=torch.float32, device="cuda")
-            calls = [(lambda c=c: dg.dg_gemv_q4_0(Wq[c % nc], Xq, Y, N, K, M)) for c in range(max(nc, 20))]
+            calls = [(lambda c=c: dg.dg_gemv_q4_0(Wq[c % nc], Xq, Y, N, K, M)) for c in range(n_calls(nc))]
             us, iqr = time_per_call(calls)
             cps = M / (us * 1e-6)
             dip = None if prev is None else round(cps / prev - 1.0, 4)
@@ -577,7 +596,7 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
                 launches += [(dict(variant=12, unroll=r), dict(variant="dot4-lds", R=r)) for r in (1, 2, 4)]
                 for launch, tag in launches:
                     calls = [(lambda c=c, launch=launch: dg.dg_gemv_q4_0(Wq[c % nc], Xq, Y, N, K, M, launch=launch))
-                             for c in range(max(nc, 20))]
+                             for c in range(n_calls(nc))]
                     try:
                         calls[0]()
                     except dg.DGError:   # an ablation variant that does not take this column count
@@ -609,7 +628,7 @@ def suite_q8_0(dg, torch, emit, ceil_gbps):
     for lname, launch in [("default", None)] + [(f"ldsrow d{d} g{g} b{b}", dict(variant=21, grid=g, block=b, unroll=d))
                                                 for d in (2, 3) for g in (0, 1024) for b in (128, 256)]:
         calls = [(lambda c=c, launch=launch: dg.dg_gemv_q8_0(Wq[c % nq], Xq, Yq, Q4_N, Q4_K, 1, launch=launch))
-                 for c in range(3 * nq)]
+                 for c in range(n_calls(nq))]
         us, iqr = time_per_call(calls)
         emit(record(f"gemv_q8_0 {Q4_N}x{Q4_K} M=1", us, iqr, bytes_q8_0(Q4_N, Q4_K, 1), ceil_gbps, variant=lname,
                     copies=nq))
@@ -622,7 +641,7 @@ def suite_q8_0(dg, torch, emit, ceil_gbps):
         for M in (1, 2, 4, 8, 12, 16, 24):
             Xq = q8_columns(5, K, M)
             Y = torch.empty(M * N, dtype=torch.float32, device="cuda")
-            calls = [(lambda c=c: dg.dg_gemv_q8_0(Wq[c % nc], Xq, Y, N, K, M)) for c in range(max(nc, 20))]
+            calls = [(lambda c=c: dg.dg_gemv_q8_0(Wq[c % nc], Xq, Y, N, K, M)) for c in range(n_calls(nc))]
             us, iqr = time_per_call(calls)
             cps = M / (us * 1e-6)
             dip = None if prev is None else round(cps / prev - 1.0, 4)
@@ -635,7 +654,7 @@ def suite_q8_0(dg, torch, emit, ceil_gbps):
                         continue
                     launch = dict(variant=22, unroll=rt * 10000 + ks * 100 + d * 10 + cb // 8)
                     calls = [(lambda c=c, launch=launch: dg.dg_gemv_q8_0(Wq[c % nc], Xq, Y, N, K, M, launch=launch))
-                             for c in range(max(nc, 20))]
+                             for c in range(n_calls(nc))]
                     us, iqr = time_per_call(calls)
                     emit(record(f"gemv_q8_0 {N}x{K}", us, iqr, bytes_q8_0(N, K, M), ceil_gbps, M=M, copies=nc,
                                 variant="mfma", RT=rt, KS=ks, DEPTH=d, CB=cb))
@@ -656,12 +675,12 @@ def suite_m1_rows_vs_units(dg, torch, emit, ceil_gbps):
             Y = torch.empty(N, dtype=torch.float32, device="cuda")
             launches = [("default", None)]
             launches += [(f"rows d{d} g{g} b{b}", dict(variant=v_rows, unroll=d, grid=g, block=b))
-                         for d in (2, 3) for g in (0, 1024) for b in (128, 256)]
+                         for d in (2, 3) for g in (0, 512, 1024) for b in (128, 256)]
             launches += [(f"units d{d} g{g} b{b}", dict(variant=v_units, unroll=d, grid=g, block=b))
-                         for d in (2, 3, 4) for g in (0, 1024) for b in (128, 256)]
+                         for d in (2, 3, 4) for g in (0, 512, 1024) for b in (128, 256)]
             for lname, launch in launches:
                 calls = [(lambda c=c, launch=launch: gemv(Wq[c % nc], Xq, Y, N, K, 1, launch=launch))
-                         for c in range(max(nc, 20))]
+                         for c in range(n_calls(nc))]
                 try:
                     calls[0]()
                 except dg.DGError:   # a buffer depth that does not fit this row length
@@ -682,11 +701,11 @@ def suite_argmax(dg, torch, emit, ceil_gbps):
         idx = torch.empty(R, dtype=torch.int64, device="cuda")
         ws = torch.zeros(max(8, dg.dg_argmax_workspace_bytes(R, C)), dtype=torch.uint8, device="cuda")
         nb = 4 * R * C + 8 * R
-        calls = [(lambda: dg.dg_argmax_rows(xs[0], idx, ws=ws))] * 20
+        calls = [(lambda: dg.dg_argmax_rows(xs[0], idx, ws=ws))] * MIN_CALLS
         us, iqr = time_per_call(calls)
         emit(record(f"argmax_rows [{R},{C}]", us, iqr, nb, ceil_gbps, cache="hot"))
         if ncold > 1:
-            calls = [(lambda c=c: dg.dg_argmax_rows(xs[c % ncold], idx, ws=ws)) for c in range(max(20, ncold))]
+            calls = [(lambda c=c: dg.dg_argmax_rows(xs[c % ncold], idx, ws=ws)) for c in range(n_calls(ncold))]
             us, iqr = time_per_call(calls)
             emit(record(f"argmax_rows [{R},{C}]", us, iqr, nb, ceil_gbps, cache="cold", copies=ncold))
         del xs
@@ -698,7 +717,7 @@ def suite_argmax(dg, torch, emit, ceil_gbps):
         idx = torch.empty(R, dtype=torch.int64, device="cuda")
         ws = torch.zeros(max(8, dg.dg_argmax_workspace_bytes(R, C)), dtype=torch.uint8, device="cuda")
         nb = x.element_size() * R * C + 8 * R
-        calls = [(lambda: dg.dg_argcompare_rows(x, idx, op=op, ws=ws))] * 20
+        calls = [(lambda: dg.dg_argcompare_rows(x, idx, op=op, ws=ws))] * MIN_CALLS
         us, iqr = time_per_call(calls)
         emit(record(f"argcompare_rows {op} {str(dt).replace('torch.', '')} [{R},{C}]", us, iqr, nb, ceil_gbps,
                     cache="hot"))
@@ -715,7 +734,7 @@ def suite_tail(dg, torch, emit, ceil_gbps):
     idx = torch.empty(1, dtype=torch.int64, device="cuda")
     ws = torch.zeros(dg.dg_argmax_workspace_bytes(1, N), dtype=torch.uint8, device="cuda")
     calls = []
-    for c in range(8):
+    for c in range(n_calls(nc)):
         calls.append(lambda c=c: dg.dg_gemv_bf16(Wb[c % nc], xb, logits))
         calls.append(lambda: dg.dg_argmax_rows(logits.view(1, N), idx, ws=ws))
     us, iqr = time_per_call(calls)
@@ -724,7 +743,8 @@ def suite_tail(dg, torch, emit, ceil_gbps):
     # the fused call, logits stored and not stored
     fws = torch.zeros(dg.dg_gemv_bf16_argmax_workspace_bytes(N, K), dtype=torch.uint8, device="cuda")
     for name, y in (("logits stored", logits), ("logits not stored", None)):
-        calls = [(lambda c=c, y=y: dg.dg_gemv_bf16_argmax(Wb[c % nc], xb, idx, y=y, ws=fws)) for c in range(16)]
+        calls = [(lambda c=c, y=y: dg.dg_gemv_bf16_argmax(Wb[c % nc], xb, idx, y=y, ws=fws))
+                 for c in range(n_calls(nc))]
         us, iqr = time_per_call(calls)
         emit(record("greedy tail fused lm-head 128256x4096 + argmax", us, iqr,
                     bytes_dense(N, K, 4 if y is not None else 0) + 8, ceil_gbps, note=f"us per token, {name}"))

@@ -17,7 +17,8 @@ struct Launch {
     int unroll;
 };
 
-// Default launch shape of the M = 1 quantised kernels (measured on MI355X over
+// Launch shape of the LDS-row M = 1 kernels when no grid or block is given
+// (the Q4_0 default from 16384 rows on at K <= 8192; measured on MI355X over
 // the decoder shapes and the 70B MLP, both formats): every wave gets at least
 // two rows so that its copy pipeline has something to overlap (one row per
 // wave leaves the pipeline empty), with about 2048 waves for up to 8192 rows
@@ -28,6 +29,21 @@ inline void m1_default_launch(int N, int& grid, int& block) {
     const int g = N >= 16384 ? 2048 : 1024;
     const int need = (N + wpb - 1) / wpb;
     grid = need < g ? need : g;
+}
+
+// Default launch of the M = 1 kernels that stream rows in 64-pair units, the
+// default M = 1 path of both quantised formats (measured on MI355X over the
+// decoder shapes, the 70B MLP and 3584 and 7168 rows at K = 8192, against the
+// LDS-row kernels and other grids, depths and workgroup sizes): workgroups
+// of four waves, 512 of them (2048 from 16384 rows on) but never more than
+// the rows need; S = ceil(K / 4096) units per row, kept two deep when a row
+// is one unit and three deep otherwise.
+inline void m1_units_default(int N, int S, int& grid, int& block, int& depth) {
+    block = 256;
+    const int need = (N + 3) / 4;
+    const int g = N >= 16384 ? 2048 : 512;
+    grid = need < g ? need : g;
+    depth = S == 1 ? 2 : 3;
 }
 
 // Device properties used to size grids and check launches; cached per device.

@@ -15,8 +15,9 @@
 // active (lanes past the unit's bytes re-read the unit's first 16 bytes into
 // the unused tail of the buffer), so each unit is exactly kC vector-memory
 // operations and "at most q * kC outstanding" proves that the unit q steps
-// back has landed (loads complete in issue order; the activations are loaded
-// before the first copy and the outputs are stored after the last wait).
+// back has landed (loads complete in issue order; the workgroup's copy of
+// the activation column is issued before the first unit and the outputs are
+// stored after the last wait).
 #include "dg_internal.h"
 #include "q4_common.h"
 
@@ -80,14 +81,6 @@ __device__ __forceinline__ void copy_unit(const uint8_t* __restrict__ row, int s
     }
 }
 
-template <int COPIES, int DEPTH>
-__device__ __forceinline__ void wait_units_ahead(int q) {
-    if (q == 0) wait_vmcnt<0>();
-    else if (DEPTH > 2 && q == 1) wait_vmcnt<COPIES>();
-    else if (DEPTH > 3 && q == 2) wait_vmcnt<(DEPTH > 3 ? 2 * COPIES : 0)>();
-    else wait_vmcnt<(DEPTH - 1) * COPIES>();
-}
-
 template <class F, int S, int DEPTH>
 __global__ void __launch_bounds__(256)
 k_m1_units(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __restrict__ Y, int N, int K) {
@@ -102,24 +95,11 @@ k_m1_units(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float
     const size_t row_bytes = (size_t)(K >> 5) * F::kBlockBytes;
     const int rstride = gridDim.x * wpb;
     const int row0 = blockIdx.x * wpb + wave;
-    if (row0 >= N) return;
-    uint8_t* const bufs = reinterpret_cast<uint8_t*>(lds_units) + wave * DEPTH * G::kBufBytes;
+    uint8_t* const acts = reinterpret_cast<uint8_t*>(lds_units);
+    uint8_t* const bufs = acts + column_lds_bytes(K) + wave * DEPTH * G::kBufBytes;
 
-    // activations first: their loads precede every copy in the wave's queue
-    ActPair act[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int p = s * kWave + lane;
-        load_act_pair(Xq, p < npairs ? p : npairs - 1, act[s]);
-        if (p >= npairs) {   // lanes past the end of the row contribute exactly 0
-            act[s].da = 0.0f;
-            act[s].db = 0.0f;
-            act[s].ca = 0;
-            act[s].cb = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) { act[s].qa[i] = 0; act[s].qb[i] = 0; }
-        }
-    }
+    // the workgroup's copy of the activation column first, then the first units
+    copy_column_to_lds(Xq, K, acts, wave, wpb, lane);
 
     // issue pointer: the next unit (irow, is) to copy, into slot islot
     int irow = row0, is = 0, islot = 0;
@@ -133,6 +113,22 @@ k_m1_units(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d) issue();
 
+    {   // this wave's column copies have landed once only its issued units can be outstanding
+        const int units = row0 < N ? ((N - 1 - row0) / rstride + 1) * S : 0;   // wave-uniform
+        wait_ahead<G::kC, DEPTH>(units < DEPTH - 1 ? units : DEPTH - 1);
+        lds_barrier();
+    }
+    if (row0 >= N) return;   // after the barrier: every wave takes part in it
+
+    ActPair act[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int p = s * kWave + lane;
+        uint32_t v[18];
+        load_act_raw(acts, p < npairs ? p : npairs - 1, v);
+        decode_act_pair(v, p < npairs, act[s]);   // past the row: contributes 0
+    }
+
     float out = 0.0f;
     int nout = 0;
     int out_row0 = row0;
@@ -145,7 +141,7 @@ k_m1_units(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float
         for (int s = 0; s < S; ++s) {
             issue();
             const int after = rows_after * S + (S - 1 - s);
-            wait_units_ahead<G::kC, DEPTH>(after < DEPTH - 1 ? after : DEPTH - 1);
+            wait_ahead<G::kC, DEPTH>(after < DEPTH - 1 ? after : DEPTH - 1);
             const int p = s * kWave + lane;
             const uint32_t* w = reinterpret_cast<const uint32_t*>(bufs + slot * G::kBufBytes) +
                                 (p < npairs ? lane : 0) * F::kPairDwords;
@@ -174,7 +170,7 @@ hipError_t launch_units(int K, int depth, const void* Wq, const void* Xq, float*
         const int rows_grid = (N + block / kWave - 1) / (block / kWave);
         grid = rows_grid < 2048 ? rows_grid : 2048;
     }
-    const size_t lds = (size_t)(block / kWave) * depth * G::kBufBytes;
+    const size_t lds = (size_t)column_lds_bytes(K) + (size_t)(block / kWave) * depth * G::kBufBytes;
     if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
     const int S = (K / 64 + kWave - 1) / kWave;
     const uint8_t* w = (const uint8_t*)Wq;

@@ -62,19 +62,12 @@ k_q4_m1_regs(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
 #pragma unroll
     for (int s = 0; s < S; ++s) load_weight_pair(Wq + (size_t)row * row_bytes, pc[s], w[s]);
 
+    uint32_t araw[S][18];
+#pragma unroll
+    for (int s = 0; s < S; ++s) load_act_raw(Xq, pc[s], araw[s]);
     ActPair act[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-        load_act_pair(Xq, pc[s], act[s]);
-        if (s * kWave + lane >= npairs) {  // lanes past the end of the row contribute exactly 0
-            act[s].da = 0.0f;
-            act[s].db = 0.0f;
-            act[s].ca = 0;
-            act[s].cb = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) { act[s].qa[i] = 0; act[s].qb[i] = 0; }
-        }
-    }
+    for (int s = 0; s < S; ++s) decode_act_pair(araw[s], s * kWave + lane < npairs, act[s]);   // past the row: 0
 
     while (true) {
         const int next = row + rstride;
@@ -261,14 +254,16 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
     int variant = cfg && cfg->variant ? cfg->variant : 0;
     int lds_rows = 0;   // rows per wave of the dot4 LDS kernel chosen by default
     if (variant == 0) {
-        // Measured on MI355X over the decoder shapes and M = 1..24 (every
-        // kernel family is exact to the same bound, so the choice is speed
-        // only): one column streams rows through LDS; two columns, and every
-        // column count of a matrix of at most 1024 rows, take the dot4
-        // kernel (the matrix cores' fixed cost per 16 x 16 tile does not pay
-        // there); the rest take the matrix cores.
+        // Measured on MI355X over the decoder shapes, the 70B MLP and M =
+        // 1..24 (every kernel family is exact to the same bound, so the
+        // choice is speed only): one column streams rows through LDS, whole
+        // and two deep for many short rows (16384 rows and more, K <= 8192),
+        // in 64-pair units otherwise; two columns, and every column count of
+        // a matrix of at most 1024 rows, take the dot4 kernel (the matrix
+        // cores' fixed cost per 16 x 16 tile does not pay there); the rest
+        // take the matrix cores.
         if (M == 1) {
-            variant = S <= 4 ? DG_VARIANT_Q4_LDSROW : DG_VARIANT_Q4_LDS;
+            variant = S > 4 ? DG_VARIANT_Q4_LDS : (N >= 16384 && S <= 2 ? DG_VARIANT_Q4_LDSROW : DG_VARIANT_Q4_UNITS);
         } else if (M == 2 || N <= 1024) {
             variant = DG_VARIANT_Q4_LDS;
             lds_rows = N > 2048 ? 2 : 1;
@@ -292,8 +287,11 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
     }
     if (variant == DG_VARIANT_Q4_UNITS) {
         if (M != 1 || S > 4) return hipErrorInvalidValue;
-        return launch_q4_m1_units(K, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, cfg ? cfg->grid : 0,
-                                  cfg ? cfg->block : 0, s);
+        int grid = cfg ? cfg->grid : 0, block = cfg ? cfg->block : 0, depth = cfg ? cfg->unroll : 0;
+        int g0, b0, d0;
+        m1_units_default(N, S, g0, b0, d0);
+        if (!grid && !block) { grid = g0; block = b0; }
+        return launch_q4_m1_units(K, depth ? depth : d0, Wq, Xq, Y, N, grid, block, s);
     }
     if (variant == DG_VARIANT_Q4_MFMA) {
         if (cfg && cfg->block) return hipErrorInvalidValue;   // the configuration fixes the workgroup size

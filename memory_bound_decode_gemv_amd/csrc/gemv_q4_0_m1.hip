@@ -42,19 +42,26 @@ k_q4_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
     const int nchunks = row_bytes >> 4;
     const int rstride = gridDim.x * wpb;
     const int row0 = blockIdx.x * wpb + wave;
-    if (row0 >= N) return;
-    // Byte offset of the wave's buffers; addresses are always formed from the
-    // __shared__ array itself, so that they stay LDS addresses (ds_read) rather
-    // than generic ones (flat_load).
-    const int buf_off = wave * DEPTH * row_bytes;
-    uint8_t* const lds_base = reinterpret_cast<uint8_t*>(lds_rows) + buf_off;
+    // Byte offsets of the column and the wave's buffers; addresses are always
+    // formed from the __shared__ array itself, so that they stay LDS
+    // addresses (ds_read) rather than generic ones (flat_load).
+    uint8_t* const acts = reinterpret_cast<uint8_t*>(lds_rows);
+    uint8_t* const lds_base = acts + column_lds_bytes(K) + wave * DEPTH * row_bytes;
 
-    // rows row0 + i*rstride for i = 0, 1, ...; the first DEPTH - 1 are requested now
+    // the workgroup's copy of the activation column first, then the copies of
+    // the first DEPTH - 1 rows (rows row0 + i*rstride for i = 0, 1, ...)
+    copy_column_to_lds(Xq, K, acts, wave, wpb, lane);
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d) {
         const int r = row0 + d * rstride;
         if (r < N) copy_row_to_lds<C>(Wq + (size_t)r * row_bytes, lds_base + d * row_bytes, nchunks, lane);
     }
+    {   // this wave's column copies have landed once only its issued rows can be outstanding
+        const int rows = row0 < N ? (N - 1 - row0) / rstride + 1 : 0;   // wave-uniform
+        wait_rows_ahead<C, DEPTH>(rows < DEPTH - 1 ? rows : DEPTH - 1);
+        lds_barrier();
+    }
+    if (row0 >= N) return;   // after the barrier: every wave takes part in it
 
     int pc[S];
     ActPair act[S];
@@ -62,15 +69,9 @@ k_q4_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
     for (int s = 0; s < S; ++s) {
         const int p = s * kWave + lane;
         pc[s] = p < npairs ? p : npairs - 1;
-        load_act_pair(Xq, pc[s], act[s]);
-        if (p >= npairs) {   // lanes past the end of the row contribute exactly 0
-            act[s].da = 0.0f;
-            act[s].db = 0.0f;
-            act[s].ca = 0;
-            act[s].cb = 0;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) { act[s].qa[i] = 0; act[s].qb[i] = 0; }
-        }
+        uint32_t v[18];
+        load_act_raw(acts, pc[s], v);
+        decode_act_pair(v, p < npairs, act[s]);   // past the row: contributes 0
     }
 
     // Results are held back and stored 64 rows at a time (lane i holds the
@@ -132,7 +133,7 @@ hipError_t launch_q4_m1_ldsrow(int K, int depth, const void* Wq, const void* Xq,
     const uint8_t* w = (const uint8_t*)Wq;
     const uint8_t* x = (const uint8_t*)Xq;
     const size_t row_bytes = (size_t)(K / 32) * 18;
-    const size_t lds = (size_t)(block / kWave) * depth * row_bytes;
+    const size_t lds = (size_t)column_lds_bytes(K) + (size_t)(block / kWave) * depth * row_bytes;
     if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
     const int C = (int)((row_bytes + 1023) / 1024);
     const int S = (K / 64 + kWave - 1) / kWave;

@@ -36,14 +36,22 @@ k_q8_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, f
     const int nchunks = row_bytes >> 4;
     const int rstride = gridDim.x * wpb;
     const int row0 = blockIdx.x * wpb + wave;
-    if (row0 >= N) return;
-    uint8_t* const lds_base = reinterpret_cast<uint8_t*>(lds_rows8) + wave * DEPTH * row_bytes;
+    uint8_t* const acts = reinterpret_cast<uint8_t*>(lds_rows8);
+    uint8_t* const lds_base = acts + column_lds_bytes(K) + wave * DEPTH * row_bytes;
 
+    // the workgroup's copy of the activation column first, then the first rows
+    copy_column_to_lds(Xq, K, acts, wave, wpb, lane);
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d) {
         const int r = row0 + d * rstride;
         if (r < N) copy_row_to_lds<C>(Wq + (size_t)r * row_bytes, lds_base + d * row_bytes, nchunks, lane);
     }
+    {   // this wave's column copies have landed once only its issued rows can be outstanding
+        const int rows = row0 < N ? (N - 1 - row0) / rstride + 1 : 0;   // wave-uniform
+        wait_rows_ahead<C, DEPTH>(rows < DEPTH - 1 ? rows : DEPTH - 1);
+        lds_barrier();
+    }
+    if (row0 >= N) return;   // after the barrier: every wave takes part in it
 
     int pc[S];
     ActPair act[S];
@@ -51,13 +59,9 @@ k_q8_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, f
     for (int s = 0; s < S; ++s) {
         const int p = s * kWave + lane;
         pc[s] = p < npairs ? p : npairs - 1;
-        load_act_pair(Xq, pc[s], act[s]);
-        if (p >= npairs) {   // lanes past the end of the row contribute exactly 0
-            act[s].da = 0.0f;
-            act[s].db = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) { act[s].qa[i] = 0; act[s].qb[i] = 0; }
-        }
+        uint32_t v[18];
+        load_act_raw(acts, pc[s], v);
+        decode_act_pair(v, p < npairs, act[s]);   // past the row: contributes 0
     }
 
     // outputs held back and stored 64 rows at a time (lane i holds the i-th row)
@@ -114,7 +118,7 @@ hipError_t launch_q8_m1_ldsrow(int K, int depth, const void* Wq, const void* Xq,
         grid = rows_grid < 2048 ? rows_grid : 2048;
     }
     const size_t row_bytes = (size_t)(K / 32) * 34;
-    const size_t lds = (size_t)(block / kWave) * depth * row_bytes;
+    const size_t lds = (size_t)column_lds_bytes(K) + (size_t)(block / kWave) * depth * row_bytes;
     if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
     const int C = (int)((row_bytes + 1023) / 1024);
     const int S = (K / 64 + kWave - 1) / kWave;
@@ -145,21 +149,23 @@ hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int
     int variant = cfg && cfg->variant ? cfg->variant : 0;
     int depth = cfg ? cfg->unroll : 0;
     if (variant == 0) {
-        // Measured on MI355X: rows of 8192 weights and more (8.5 KiB) stream in
-        // 64-pair units three deep; shorter rows whole, two deep.
-        if (M == 1 && S <= 4) {
-            variant = K >= 8192 ? DG_VARIANT_Q8_UNITS : DG_VARIANT_Q8_LDSROW;
-            depth = K >= 8192 ? 3 : 2;
-        } else {
-            variant = DG_VARIANT_Q8_MFMA;
-        }
+        // Measured on MI355X over the decoder shapes and the 70B MLP: one
+        // column streams rows through LDS in 64-pair units.
+        variant = M == 1 && S <= 4 ? DG_VARIANT_Q8_UNITS : DG_VARIANT_Q8_MFMA;
     }
-    if (variant == DG_VARIANT_Q8_LDSROW || variant == DG_VARIANT_Q8_UNITS) {
+    if (variant == DG_VARIANT_Q8_UNITS) {
+        if (M != 1 || S > 4) return hipErrorInvalidValue;
+        int grid = cfg ? cfg->grid : 0, block = cfg ? cfg->block : 0;
+        int g0, b0, d0;
+        m1_units_default(N, S, g0, b0, d0);
+        if (!grid && !block) { grid = g0; block = b0; }
+        return launch_q8_m1_units(K, depth ? depth : d0, Wq, Xq, Y, N, grid, block, s);
+    }
+    if (variant == DG_VARIANT_Q8_LDSROW) {
         if (M != 1 || S > 4) return hipErrorInvalidValue;
         int grid = cfg ? cfg->grid : 0, block = cfg ? cfg->block : 0;
         if (!grid && !block) m1_default_launch(N, grid, block);
-        return variant == DG_VARIANT_Q8_LDSROW ? launch_q8_m1_ldsrow(K, depth, Wq, Xq, Y, N, grid, block, s)
-                                               : launch_q8_m1_units(K, depth, Wq, Xq, Y, N, grid, block, s);
+        return launch_q8_m1_ldsrow(K, depth, Wq, Xq, Y, N, grid, block, s);
     }
     if (variant == DG_VARIANT_Q8_MFMA) {
         if (cfg && cfg->block) return hipErrorInvalidValue;   // the configuration fixes the workgroup size

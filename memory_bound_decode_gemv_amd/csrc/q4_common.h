@@ -30,14 +30,25 @@ __device__ __forceinline__ int block_code_sum(const uint32_t* q) {
 }
 
 // Reads the Q8_1 blocks 2p and 2p+1 of a column (72 bytes, 8-byte aligned
-// when the column start is) from global memory.
-__device__ __forceinline__ void load_act_pair(const uint8_t* col, int p, ActPair& a) {
+// when the column start is) from global memory, as stored.  Kept apart from
+// the decoding so that a kernel can issue every activation load, then its
+// first weight copies, and only then wait: decoding one pair before loading
+// the next would cost one memory round trip per pair before the weight
+// stream starts.
+__device__ __forceinline__ void load_act_raw(const uint8_t* col, int p, uint32_t v[18]) {
     const uint32_t* b = reinterpret_cast<const uint32_t*>(col + (size_t)p * (2 * kQ81Bytes));
-    uint32_t v[18];
 #pragma unroll
     for (int i = 0; i < 18; ++i) v[i] = b[i];
-    a.da = half_lo_to_f32(v[0]);
-    a.db = half_lo_to_f32(v[9]);
+}
+
+// The pair load_act_raw read.  valid == false marks a lane past the end of
+// the row (its loads re-read the row's last pair): only the two scales are
+// zeroed, which makes its contribution exactly 0 in every kernel (the integer
+// block sums are multiplied by them), and no load depends on the flag, so the
+// compiler cannot move the loads into a branch behind later copies.
+__device__ __forceinline__ void decode_act_pair(const uint32_t v[18], bool valid, ActPair& a) {
+    a.da = valid ? half_lo_to_f32(v[0]) : 0.0f;
+    a.db = valid ? half_lo_to_f32(v[9]) : 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         a.qa[i] = v[1 + i];
@@ -45,6 +56,12 @@ __device__ __forceinline__ void load_act_pair(const uint8_t* col, int p, ActPair
     }
     a.ca = -8 * block_code_sum(a.qa);
     a.cb = -8 * block_code_sum(a.qb);
+}
+
+__device__ __forceinline__ void load_act_pair(const uint8_t* col, int p, ActPair& a) {
+    uint32_t v[18];
+    load_act_raw(col, p, v);
+    decode_act_pair(v, true, a);
 }
 
 // Loads the 9 dwords of block pair p of a weight row (non-temporal).
@@ -134,13 +151,49 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Waits until at most q*C vector-memory operations are outstanding (q < DEPTH).
+// Waits until at most q*C vector-memory operations are outstanding
+// (0 <= q < DEPTH; larger q waits as for DEPTH - 1).
+template <int C, int DEPTH, int Q = 0>
+__device__ __forceinline__ void wait_ahead(int q) {
+    if constexpr (Q >= DEPTH - 1) {
+        wait_vmcnt<(DEPTH - 1) * C>();
+    } else {
+        if (q == Q) {
+            wait_vmcnt<Q * C>();
+            return;
+        }
+        wait_ahead<C, DEPTH, Q + 1>(q);
+    }
+}
+
 template <int C, int DEPTH>
 __device__ __forceinline__ void wait_rows_ahead(int q) {
-    if (q == 0) wait_vmcnt<0>();
-    else if (DEPTH > 2 && q == 1) wait_vmcnt<C>();
-    else if (DEPTH > 3 && q == 2) wait_vmcnt<(DEPTH > 3 ? 2 * C : 0)>();
-    else wait_vmcnt<(DEPTH - 1) * C>();
+    wait_ahead<C, DEPTH>(q);
+}
+
+// LDS bytes that hold one Q8_1 column of K elements (K % 256 == 0, so the
+// column is a whole number of 16-byte slots), in whole 1 KiB copies.
+__host__ __device__ constexpr int column_lds_bytes(int K) {
+    return ((K / 32) * kQ81Bytes / 16 + kWave - 1) / kWave * 1024;
+}
+
+// The M = 1 kernels give every workgroup one copy of the activation column
+// in LDS instead of one per wave: the 1 KiB copies are split over the
+// workgroup's waves (wave w issues copies w, w + wpb, ...) and are issued
+// before any weight copy, so a wave's own share has landed once at most its
+// weight copies are outstanding; a barrier then makes every share visible.
+// Every copy has all 64 lanes active (lanes past the column re-read its first
+// slot into the unused tail of the last KiB).  dst is formed from the
+// kernel's __shared__ array.
+__device__ __forceinline__ void copy_column_to_lds(const uint8_t* __restrict__ col, int K, uint8_t* dst, int wave,
+                                                   int wpb, int lane) {
+    const int slots = (K / 32) * kQ81Bytes / 16;
+    const int copies = (slots + kWave - 1) / kWave;
+    for (int j = wave; j < copies; j += wpb) {
+        const int c = j * kWave + lane;
+        __builtin_amdgcn_global_load_lds(col + (size_t)(c < slots ? c : 0) * 16, (lds_void_t*)(dst + j * 1024), 16,
+                                         0, 0);
+    }
 }
 
 __device__ __forceinline__ void read_pair_lds(const uint8_t* buf, int p, uint32_t w[9]) {

@@ -14,6 +14,7 @@ traffic only while that hash still matches the tree.
     python -m memory_bound_decode_gemv_amd.profiling counters FETCH.csv WRITE.csv
     python -m memory_bound_decode_gemv_amd.profiling trace KERNEL_STATS.csv --md OUT.md
     python -m memory_bound_decode_gemv_amd.profiling suite SUITE.jsonl --md OUT.md
+    python -m memory_bound_decode_gemv_amd.profiling suite A.jsonl B.jsonl --condense --filter RE --md OUT.md
 """
 from __future__ import annotations
 
@@ -37,7 +38,7 @@ KERNELS = {
     "gemv_q4_0_m1_28672x8192": (
         r"k_q4_m1_ldsrow<", "Q4_0 x Q8_1, M = 1, N = 28672, K = 8192",
         18 * 28672 * 8192 // 32 + 36 * 8192 // 32 + 4 * 28672,
-        ["gemv_q4_0_m1.hip", "q4_common.h", "dg_device.h"]),
+        ["gemv_q4_0_m1.hip", "q4_common.h", "dg_device.h", "dg_internal.h"]),
     "gemv_f16_4096x4096": (
         r"k_gemv_wide<false", "fp16 GEMV, N = K = 4096",
         2 * 4096 * 4096 + 2 * 4096 + 2 * 4096,
@@ -151,6 +152,64 @@ def suite_markdown(jsonl, command, name_filter=None):
     return "\n".join(lines) + "\n"
 
 
+_RECORD_KEYS = {"name", "us_per_call", "iqr_us", "bytes", "gbps", "mbu_spec", "mbu_ceiling", "M", "copies",
+                "variant", "columns_per_s", "change_vs_prev_M", "note", "cache"}
+
+
+def _config(r) -> str:
+    """The launch configuration a record was timed with, as one short string."""
+    parts = [str(r["variant"])] if "variant" in r else []
+    parts += [f"{k}={r[k]}" for k in sorted(r) if k not in _RECORD_KEYS]
+    for k in ("note", "cache"):
+        if k in r:
+            parts.append(str(r[k]))
+    return " ".join(parts)
+
+
+def suite_condensed_markdown(jsonls, command, name_filter=None):
+    """One line per (workload, M) of `bench.py --suite` records: the library's
+    default launch (the record whose variant is "default", else the only one)
+    and the fastest configuration the sweep tried, with the run's ceiling."""
+    recs, ceilings = [], []
+    for path in jsonls:
+        with open(path) as f:
+            for line in f:
+                r = json.loads(line)
+                if r.get("name") == "ceiling":
+                    ceilings.append(r["gbps"])
+                if name_filter and not re.search(name_filter, r.get("name", "")):
+                    continue
+                if "us_per_call" in r:
+                    recs.append(r)
+    groups = collections.OrderedDict()
+    for r in recs:
+        label = " ".join([r["name"]] + [str(r[k]) for k in ("cache", "note") if k in r])
+        groups.setdefault((label, r.get("M")), []).append(r)
+    lines = ["# bench.py --suite, condensed", "", "Commands:", ""] + [f"    {c}" for c in command.split(" ;; ")]
+    lines += ["", "Measured streaming-read ceiling of the run(s): " +
+              (", ".join(f"{g:.1f} GB/s" for g in ceilings) or "not in these records") + ".",
+              "`default` is the launch the library picks by itself; `best` is the fastest configuration the "
+              "sweep timed (median of HIP-graph replays, microseconds per call).", "",
+              "| workload | M | default us | default GB/s | of ceiling | columns/s | vs previous M | best us | "
+              "best configuration | configs timed |", "|---|---|---|---|---|---|---|---|---|---|"]
+    for (name, m), rs in groups.items():
+        dflt = [r for r in rs if r.get("variant") == "default"]
+        d = dflt[0] if dflt else (rs[0] if len(rs) == 1 else None)
+        b = min(rs, key=lambda r: r["us_per_call"])
+        cells = [name, "" if m is None else str(m)]
+        if d is not None:
+            chg = d.get("change_vs_prev_M")
+            cells += [f"{d['us_per_call']:.3f}", f"{d.get('gbps', 0):.1f}",
+                      "" if d.get("mbu_ceiling") is None else f"{d['mbu_ceiling']:.3f}",
+                      "" if d.get("columns_per_s") is None else f"{d['columns_per_s']:.0f}",
+                      "" if chg is None else f"{chg:+.3f}"]
+        else:
+            cells += ["", "", "", "", ""]
+        cells += [f"{b['us_per_call']:.3f}", _config(b), str(len(rs))]
+        lines.append("| " + " | ".join(cells) + " |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -162,10 +221,12 @@ def main(argv=None):
     c.add_argument("--command-fetch", default="")
     c.add_argument("--command-write", default="")
     q = sub.add_parser("suite")
-    q.add_argument("jsonl")
+    q.add_argument("jsonl", nargs="+")
     q.add_argument("--md", required=True)
     q.add_argument("--command", default="")
     q.add_argument("--filter", default=None)
+    q.add_argument("--condense", action="store_true",
+                   help="one line per (workload, M): the default launch and the best configuration")
     t = sub.add_parser("trace")
     t.add_argument("stats_csv")
     t.add_argument("--md", required=True)
@@ -181,7 +242,10 @@ def main(argv=None):
         print(json.dumps(s, indent=1))
     elif a.cmd == "suite":
         with open(a.md, "w") as f:
-            f.write(suite_markdown(a.jsonl, a.command, a.filter))
+            if a.condense:
+                f.write(suite_condensed_markdown(a.jsonl, a.command, a.filter))
+            else:
+                f.write(suite_markdown(a.jsonl[0], a.command, a.filter))
     else:
         with open(a.md, "w") as f:
             f.write(trace_markdown(a.stats_csv, a.command))

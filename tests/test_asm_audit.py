@@ -82,6 +82,10 @@ def test_q4_kernels_use_dot4_lds_dma_and_matrix_cores(asm):
     assert "global_load_lds_dwordx4" in mf
     assert "flat_load" not in mf
     assert not re.search(r"v_accvgpr_read", mf)   # results stay in VGPRs
+    un = asm["gemv_m1_units.hip"]
+    assert "global_load_lds_dwordx4" in un and "s_barrier" in un
+    assert "v_dot4_i32_i8" in un or "v_dot4c_i32_i8" in un
+    assert "flat_load" not in un
 
 
 def test_stream_probe_has_no_atomics(asm):
