@@ -12,7 +12,7 @@ Each entry records a hash of the kernel's source files; bench.py reports the
 traffic only while that hash still matches the tree.
 
     python -m memory_bound_decode_gemv_amd.profiling counters FETCH.csv WRITE.csv
-    python -m memory_bound_decode_gemv_amd.profiling trace KERNEL_STATS.csv --md OUT.md
+    python -m memory_bound_decode_gemv_amd.profiling trace KERNEL_STATS.csv [--runs KERNEL_TRACE.csv] --md OUT.md
     python -m memory_bound_decode_gemv_amd.profiling suite SUITE.jsonl --md OUT.md
     python -m memory_bound_decode_gemv_amd.profiling suite A.jsonl B.jsonl --condense --filter RE --md OUT.md
 """
@@ -121,9 +121,40 @@ def counters_markdown(summary, command_fetch, command_write):
     return "\n".join(lines) + "\n"
 
 
-def trace_markdown(stats_csv, command):
-    lines = ["# Kernel durations from rocprofv3 --kernel-trace --stats", "", "Command:", "", f"    {command}", "",
-             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+def trace_segments(trace_csv, min_launches=30, idle_us=200.0):
+    """Per-kernel runs of launches from a rocprofv3 kernel-trace CSV: a run
+    ends where the kernel was idle for more than idle_us (each timed graph of
+    a benchmark is one run).  -> {kernel: [(launches, mean us, median us)]}"""
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            if "dg::" in r["Kernel_Name"]:
+                rows.append((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    rows.sort(key=lambda r: r[1])
+    out = {}
+    for name in sorted({r[0] for r in rows}):
+        q = [r for r in rows if r[0] == name]
+        runs, cur = [], [q[0]]
+        for a, b in zip(q, q[1:]):
+            if (b[1] - a[2]) / 1e3 > idle_us:
+                runs.append(cur)
+                cur = []
+            cur.append(b)
+        runs.append(cur)
+        res = []
+        for run in runs:
+            if len(run) >= min_launches:
+                d = sorted((e - s) / 1e3 for _, s, e in run)
+                res.append((len(d), sum(d) / len(d), d[len(d) // 2]))
+        if res:
+            out[short_name(name)] = res
+    return out
+
+
+def trace_markdown(stats_csv, command, trace_csv=None):
+    lines = ["# Kernel durations from rocprofv3 --kernel-trace --stats", "", "Commands:", ""]
+    lines += [f"    {c}" for c in command.split(" ;; ")]
+    lines += ["", "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     with open(stats_csv) as f:
         for row in csv.DictReader(f):
             if "dg::" not in row["Name"]:
@@ -131,6 +162,15 @@ def trace_markdown(stats_csv, command):
             lines.append(f"| {short_name(row['Name'])} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.3f} | "
                          f"{float(row['MinNs']) / 1e3:.3f} | {float(row['MaxNs']) / 1e3:.3f} | "
                          f"{float(row['Percentage']):.2f} |")
+    if trace_csv:
+        lines += ["", "Runs of back-to-back launches of the GEMV kernels (one per timed graph, in program order; a "
+                  "run ends at an idle gap of more than 200 us):", "", "| kernel | launches | mean us | median us |",
+                  "|---|---|---|---|"]
+        for name, runs in trace_segments(trace_csv).items():
+            if "stream_read" in name:
+                continue
+            for n, mean, med in runs:
+                lines.append(f"| {name} | {n} | {mean:.3f} | {med:.3f} |")
     return "\n".join(lines) + "\n"
 
 
@@ -231,6 +271,7 @@ def main(argv=None):
     t.add_argument("stats_csv")
     t.add_argument("--md", required=True)
     t.add_argument("--command", default="")
+    t.add_argument("--runs", default=None, help="kernel-trace CSV: add per-run durations")
     a = ap.parse_args(argv)
     if a.cmd == "counters":
         s = counters_summary(a.fetch_csv, a.write_csv)
@@ -248,7 +289,7 @@ def main(argv=None):
                 f.write(suite_markdown(a.jsonl[0], a.command, a.filter))
     else:
         with open(a.md, "w") as f:
-            f.write(trace_markdown(a.stats_csv, a.command))
+            f.write(trace_markdown(a.stats_csv, a.command, a.runs))
     return 0
 
 
