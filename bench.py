@@ -594,6 +594,8 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
                              dict(variant="mfma", RT=rt, KS=ks, DEPTH=d, CB=cb))
                             for (rt, ks, d, cb), mmax in MFMA_BUILT.items() if M <= mmax]
                 launches += [(dict(variant=12, unroll=r), dict(variant="dot4-lds", R=r)) for r in (1, 2, 4)]
+                launches += [(dict(variant=15, unroll=d, grid=g, block=256), dict(variant="units", DEPTH=d, grid=g))
+                             for d in (2, 3) for g in (0, 512, 1024)]
                 for launch, tag in launches:
                     calls = [(lambda c=c, launch=launch: dg.dg_gemv_q4_0(Wq[c % nc], Xq, Y, N, K, M, launch=launch))
                              for c in range(n_calls(nc))]
@@ -648,16 +650,22 @@ def suite_q8_0(dg, torch, emit, ceil_gbps):
             prev = cps
             emit(record(f"gemv_q8_0 {N}x{K}", us, iqr, bytes_q8_0(N, K, M), ceil_gbps, M=M, copies=nc,
                         variant="default", columns_per_s=round(cps, 1), change_vs_prev_M=dip))
-            if M in (2, 8, 16, 24):
-                for (rt, ks, d, cb), mmax in MFMA_BUILT_Q8.items():
-                    if M > mmax:
-                        continue
-                    launch = dict(variant=22, unroll=rt * 10000 + ks * 100 + d * 10 + cb // 8)
+            if M in (2, 4, 8, 16, 24):
+                launches = [(dict(variant=22, unroll=rt * 10000 + ks * 100 + d * 10 + cb // 8),
+                             dict(variant="mfma", RT=rt, KS=ks, DEPTH=d, CB=cb))
+                            for (rt, ks, d, cb), mmax in MFMA_BUILT_Q8.items() if M <= mmax]
+                launches += [(dict(variant=23, unroll=d, grid=g, block=256), dict(variant="units", DEPTH=d, grid=g))
+                             for d in (2, 3) for g in (0, 512, 1024)]
+                for launch, tag in launches:
                     calls = [(lambda c=c, launch=launch: dg.dg_gemv_q8_0(Wq[c % nc], Xq, Y, N, K, M, launch=launch))
                              for c in range(n_calls(nc))]
+                    try:
+                        calls[0]()
+                    except dg.DGError:   # a units kernel that does not take this column count
+                        continue
                     us, iqr = time_per_call(calls)
                     emit(record(f"gemv_q8_0 {N}x{K}", us, iqr, bytes_q8_0(N, K, M), ceil_gbps, M=M, copies=nc,
-                                variant="mfma", RT=rt, KS=ks, DEPTH=d, CB=cb))
+                                **tag))
         del Wq
         torch.cuda.empty_cache()
 

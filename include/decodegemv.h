@@ -307,11 +307,12 @@ enum {
     DG_VARIANT_Q4_LDS = 12,         /* activations staged in LDS, several rows per wave          */
     DG_VARIANT_Q4_LDSROW = 13,      /* M = 1: weight rows copied to LDS with coalesced loads     */
     DG_VARIANT_Q4_MFMA = 14,        /* int8 matrix cores, 16 rows x 16 columns per instruction   */
-    DG_VARIANT_Q4_UNITS = 15,       /* M = 1: rows copied to LDS in units of 64 block pairs      */
+    DG_VARIANT_Q4_UNITS = 15,       /* rows copied to LDS in units of 64 block pairs, every
+                                       column from one read (M * ceil(K/4096) <= 8, K <= 16384) */
     /* Q8_0 */
     DG_VARIANT_Q8_LDSROW = 21,      /* M = 1: weight rows copied to LDS (K <= 16384)             */
     DG_VARIANT_Q8_MFMA = 22,        /* int8 matrix cores                                          */
-    DG_VARIANT_Q8_UNITS = 23        /* M = 1: rows copied to LDS in units of 64 block pairs      */
+    DG_VARIANT_Q8_UNITS = 23        /* as DG_VARIANT_Q4_UNITS, Q8_0 weights                        */
 };
 
 dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K,

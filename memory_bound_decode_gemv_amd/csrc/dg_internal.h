@@ -31,19 +31,18 @@ inline void m1_default_launch(int N, int& grid, int& block) {
     grid = need < g ? need : g;
 }
 
-// Default launch of the M = 1 kernels that stream rows in 64-pair units, the
-// default M = 1 path of both quantised formats (measured on MI355X over the
-// decoder shapes, the 70B MLP and 3584 and 7168 rows at K = 8192, against the
-// LDS-row kernels and other grids, depths and workgroup sizes): workgroups
-// of four waves, 512 of them (2048 from 16384 rows on) but never more than
-// the rows need; S = ceil(K / 4096) units per row, kept two deep when a row
-// is one unit and three deep otherwise.
-inline void m1_units_default(int N, int S, int& grid, int& block, int& depth) {
+// Default grid of the kernels that stream rows in 64-pair units, the default
+// path of both quantised formats for few columns (measured on MI355X over
+// the decoder shapes, the 70B MLP and 3584 and 7168 rows at K = 8192, against
+// the LDS-row kernels and other grids, depths and workgroup sizes):
+// workgroups of four waves, 512 of them (2048 from 16384 rows on for one
+// column) but never more than the rows need.  The unit depth is chosen by
+// the launcher, which knows the LDS a workgroup needs.
+inline void units_default_grid(int N, int M, int& grid, int& block) {
     block = 256;
     const int need = (N + 3) / 4;
-    const int g = N >= 16384 ? 2048 : 512;
+    const int g = M == 1 && N >= 16384 ? 2048 : 512;
     grid = need < g ? need : g;
-    depth = S == 1 ? 2 : 3;
 }
 
 // Device properties used to size grids and check launches; cached per device.
@@ -67,12 +66,13 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
 // depth, unroll, grid or block selects the default.
 hipError_t launch_q4_m1_ldsrow(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
                                int block, hipStream_t s);
-// M = 1 with rows streamed through LDS in units of 64 block pairs (depth =
-// unit buffers per wave); K <= 16384.
-hipError_t launch_q4_m1_units(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
-                              int block, hipStream_t s);
-hipError_t launch_q8_m1_units(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
-                              int block, hipStream_t s);
+// M columns with rows streamed through LDS in units of 64 block pairs (depth
+// = unit buffers per wave); M * ceil(K / 4096) <= 8 (activation pairs held in
+// registers).
+hipError_t launch_q4_units(int K, int M, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
+                           int block, hipStream_t s);
+hipError_t launch_q8_units(int K, int M, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
+                           int block, hipStream_t s);
 hipError_t launch_q4_mfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
                           hipStream_t s);
 

@@ -26,34 +26,48 @@ namespace {
 
 using namespace q4;
 
+// A format policy reads one weight block pair of a unit from LDS once and
+// adds its products with MC activation columns into acc[0..MC-1] (each
+// column summed exactly as with one column alone).
 struct UnitsQ4_0 {
     static constexpr int kBlockBytes = 18;
     static constexpr int kPairDwords = 9;
-    __device__ __forceinline__ static float pair(const uint32_t* w, const ActPair& a, float acc) {
+    template <int MC>
+    __device__ __forceinline__ static void pairs(const uint32_t* w, const ActPair* a, float* acc) {
         uint32_t v[9];
 #pragma unroll
         for (int i = 0; i < 9; ++i) v[i] = w[i];
         WeightPair u;
         unpack_weight_pair(v, u);
-        return pair_dot(u, a.qa, a.qb, a.da, a.db, a.ca, a.cb, acc);
+#pragma unroll
+        for (int m = 0; m < MC; ++m)
+            acc[m] = pair_dot(u, a[m].qa, a[m].qb, a[m].da, a[m].db, a[m].ca, a[m].cb, acc[m]);
     }
 };
 
 struct UnitsQ8_0 {
     static constexpr int kBlockBytes = 34;
     static constexpr int kPairDwords = 17;
-    __device__ __forceinline__ static float pair(const uint32_t* w, const ActPair& a, float acc) {
+    template <int MC>
+    __device__ __forceinline__ static void pairs(const uint32_t* w, const ActPair* a, float* acc) {
         uint32_t v[17];
 #pragma unroll
         for (int i = 0; i < 17; ++i) v[i] = w[i];
-        int sa = 0, sb = 0;
+        uint32_t qa[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            sa = dot4_i8(__builtin_amdgcn_alignbit(v[i + 1], v[i], 16), a.qa[i], sa);   // codes at bytes 2..33
-            sb = dot4_i8(v[9 + i], a.qb[i], sb);                                         // codes at bytes 36..67
+        for (int i = 0; i < 8; ++i) qa[i] = __builtin_amdgcn_alignbit(v[i + 1], v[i], 16);   // codes at bytes 2..33
+        const float dwa = half_lo_to_f32(v[0]), dwb = half_hi_to_f32(v[8]);
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+            int sa = 0, sb = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sa = dot4_i8(qa[i], a[m].qa[i], sa);
+                sb = dot4_i8(v[9 + i], a[m].qb[i], sb);   // codes at bytes 36..67
+            }
+            acc[m] = fmaf((float)sa, dwa * a[m].da, acc[m]);
+            acc[m] = fmaf((float)sb, dwb * a[m].db, acc[m]);
         }
-        acc = fmaf((float)sa, half_lo_to_f32(v[0]) * a.da, acc);
-        return fmaf((float)sb, half_hi_to_f32(v[8]) * a.db, acc);
     }
 };
 
@@ -81,25 +95,29 @@ __device__ __forceinline__ void copy_unit(const uint8_t* __restrict__ row, int s
     }
 }
 
-template <class F, int S, int DEPTH>
+template <class F, int S, int MC, int DEPTH>
 __global__ void __launch_bounds__(256)
-k_m1_units(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __restrict__ Y, int N, int K) {
+k_units(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __restrict__ Y, int N, int K) {
     using G = UnitGeom<F>;
     static_assert(DEPTH >= 2 && DEPTH <= 4, "pipeline depth");
     static_assert(G::kC * (DEPTH - 1) <= 63, "wait count exceeds the vmcnt field");
+    static_assert(MC >= 1 && MC * S <= 8, "activation pairs held in registers");
     extern __shared__ u32x4 lds_units[];
     const int lane = lane_id();
     const int wave = wave_in_block();
     const int wpb = blockDim.x / kWave;
     const int npairs = K >> 6;
     const size_t row_bytes = (size_t)(K >> 5) * F::kBlockBytes;
+    const size_t col_bytes = (size_t)(K >> 5) * kQ81Bytes;
+    const int col_lds = column_lds_bytes(K);
     const int rstride = gridDim.x * wpb;
     const int row0 = blockIdx.x * wpb + wave;
     uint8_t* const acts = reinterpret_cast<uint8_t*>(lds_units);
-    uint8_t* const bufs = acts + column_lds_bytes(K) + wave * DEPTH * G::kBufBytes;
+    uint8_t* const bufs = acts + MC * col_lds + wave * DEPTH * G::kBufBytes;
 
-    // the workgroup's copy of the activation column first, then the first units
-    copy_column_to_lds(Xq, K, acts, wave, wpb, lane);
+    // the workgroup's copy of the activation columns first, then the first units
+#pragma unroll
+    for (int m = 0; m < MC; ++m) copy_column_to_lds(Xq + m * col_bytes, K, acts + m * col_lds, wave, wpb, lane);
 
     // issue pointer: the next unit (irow, is) to copy, into slot islot
     int irow = row0, is = 0, islot = 0;
@@ -120,23 +138,30 @@ k_m1_units(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float
     }
     if (row0 >= N) return;   // after the barrier: every wave takes part in it
 
-    ActPair act[S];
+    ActPair act[S][MC];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int p = s * kWave + lane;
-        uint32_t v[18];
-        load_act_raw(acts, p < npairs ? p : npairs - 1, v);
-        decode_act_pair(v, p < npairs, act[s]);   // past the row: contributes 0
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+            uint32_t v[18];
+            load_act_raw(acts + m * col_lds, p < npairs ? p : npairs - 1, v);
+            decode_act_pair(v, p < npairs, act[s][m]);   // past the row: contributes 0
+        }
     }
 
-    float out = 0.0f;
+    float out[MC];
+#pragma unroll
+    for (int m = 0; m < MC; ++m) out[m] = 0.0f;
     int nout = 0;
     int out_row0 = row0;
     int slot = 0;
     for (int row = row0; row < N; row += rstride) {
         // units left after the last one of this row (wave-uniform)
         const int rows_after = __builtin_amdgcn_readfirstlane((N - 1 - row) / rstride);
-        float acc = 0.0f;
+        float acc[MC];
+#pragma unroll
+        for (int m = 0; m < MC; ++m) acc[m] = 0.0f;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             issue();
@@ -145,58 +170,75 @@ k_m1_units(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float
             const int p = s * kWave + lane;
             const uint32_t* w = reinterpret_cast<const uint32_t*>(bufs + slot * G::kBufBytes) +
                                 (p < npairs ? lane : 0) * F::kPairDwords;
-            acc = F::pair(w, act[s], acc);
+            F::template pairs<MC>(w, act[s], acc);
             slot = slot + 1 == DEPTH ? 0 : slot + 1;
         }
-        acc = wave_sum_f32(acc);   // wave-uniform
-        if (lane == nout) out = acc;
+#pragma unroll
+        for (int m = 0; m < MC; ++m) {
+            const float r = wave_sum_f32(acc[m]);   // wave-uniform
+            if (lane == nout) out[m] = r;
+        }
         if (++nout == kWave) {
-            Y[out_row0 + (int64_t)lane * rstride] = out;
+#pragma unroll
+            for (int m = 0; m < MC; ++m) Y[(int64_t)m * N + out_row0 + (int64_t)lane * rstride] = out[m];
             nout = 0;
             out_row0 = row + rstride;
         }
     }
-    if (lane < nout) Y[out_row0 + (int64_t)lane * rstride] = out;
+    if (lane < nout) {
+#pragma unroll
+        for (int m = 0; m < MC; ++m) Y[(int64_t)m * N + out_row0 + (int64_t)lane * rstride] = out[m];
+    }
 }
 
 template <class F>
-hipError_t launch_units(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid, int block,
+hipError_t launch_units(int K, int M, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid, int block,
                         hipStream_t s) {
     using G = UnitGeom<F>;
-    if (!depth) depth = 3;
     if (!block) block = 256;
     if (block > 256) return hipErrorInvalidValue;   // compiled for <= 256 threads
     if (!grid) {
         const int rows_grid = (N + block / kWave - 1) / (block / kWave);
         grid = rows_grid < 2048 ? rows_grid : 2048;
     }
-    const size_t lds = (size_t)column_lds_bytes(K) + (size_t)(block / kWave) * depth * G::kBufBytes;
-    if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
     const int S = (K / 64 + kWave - 1) / kWave;
+    const size_t cols = (size_t)M * column_lds_bytes(K), per_depth = (size_t)(block / kWave) * G::kBufBytes;
+    if (!depth) {
+        // Measured on MI355X: one column keeps two units in flight when a row
+        // is one unit and three otherwise; several columns keep two, or three
+        // for rows of three units and more when two workgroups still fit a CU.
+        if (M == 1) depth = S == 1 ? 2 : 3;
+        else depth = S >= 3 && cols + 3 * per_depth <= 80 * 1024 ? 3 : 2;
+    }
+    const size_t lds = cols + depth * per_depth;
+    if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
     const uint8_t* w = (const uint8_t*)Wq;
     const uint8_t* x = (const uint8_t*)Xq;
-#define DG_SD(SS, DD)                                                                                    \
-    if (S == SS && depth == DD) {                                                                        \
-        hipLaunchKernelGGL((k_m1_units<F, SS, DD>), dim3(grid), dim3(block), lds, s, w, x, Y, N, K);    \
-        return hipGetLastError();                                                                        \
+#define DG_SMD(SS, MM, DD)                                                                                 \
+    if (S == SS && M == MM && depth == DD) {                                                               \
+        hipLaunchKernelGGL((k_units<F, SS, MM, DD>), dim3(grid), dim3(block), lds, s, w, x, Y, N, K);  \
+        return hipGetLastError();                                                                          \
     }
-#define DG_S(SS) DG_SD(SS, 2) DG_SD(SS, 3) DG_SD(SS, 4)
-    DG_S(1) DG_S(2) DG_S(3) DG_S(4)
-#undef DG_S
-#undef DG_SD
+#define DG_SM(SS, MM) DG_SMD(SS, MM, 2) DG_SMD(SS, MM, 3) DG_SMD(SS, MM, 4)
+    DG_SM(1, 1) DG_SM(1, 2) DG_SM(1, 3) DG_SM(1, 4) DG_SM(1, 5) DG_SM(1, 6) DG_SM(1, 7) DG_SM(1, 8)
+    DG_SM(2, 1) DG_SM(2, 2) DG_SM(2, 3) DG_SM(2, 4)
+    DG_SM(3, 1) DG_SM(3, 2)
+    DG_SM(4, 1) DG_SM(4, 2)
+#undef DG_SM
+#undef DG_SMD
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_q4_m1_units(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
-                              int block, hipStream_t s) {
-    return launch_units<UnitsQ4_0>(K, depth, Wq, Xq, Y, N, grid, block, s);
+hipError_t launch_q4_units(int K, int M, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
+                           int block, hipStream_t s) {
+    return launch_units<UnitsQ4_0>(K, M, depth, Wq, Xq, Y, N, grid, block, s);
 }
 
-hipError_t launch_q8_m1_units(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
-                              int block, hipStream_t s) {
-    return launch_units<UnitsQ8_0>(K, depth, Wq, Xq, Y, N, grid, block, s);
+hipError_t launch_q8_units(int K, int M, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
+                           int block, hipStream_t s) {
+    return launch_units<UnitsQ8_0>(K, M, depth, Wq, Xq, Y, N, grid, block, s);
 }
 
 }  // namespace dg

@@ -258,12 +258,16 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
         // 1..24 (every kernel family is exact to the same bound, so the
         // choice is speed only): one column streams rows through LDS, whole
         // and two deep for many short rows (16384 rows and more, K <= 8192),
-        // in 64-pair units otherwise; two columns, and every column count of
-        // a matrix of at most 1024 rows, take the dot4 kernel (the matrix
-        // cores' fixed cost per 16 x 16 tile does not pay there); the rest
-        // take the matrix cores.
+        // in 64-pair units otherwise; up to four columns share the units
+        // kernel's weight reads while M * ceil(K / 4096) <= 8 (beyond two
+        // columns only above 1024 rows); the rest of two columns, and every
+        // column count of a matrix of at most 1024 rows, take the dot4 kernel
+        // (the matrix cores' fixed cost per 16 x 16 tile does not pay there);
+        // the rest take the matrix cores.
         if (M == 1) {
             variant = S > 4 ? DG_VARIANT_Q4_LDS : (N >= 16384 && S <= 2 ? DG_VARIANT_Q4_LDSROW : DG_VARIANT_Q4_UNITS);
+        } else if (M <= 4 && M * S <= 8 && (N > 1024 || M <= 2)) {
+            variant = DG_VARIANT_Q4_UNITS;
         } else if (M == 2 || N <= 1024) {
             variant = DG_VARIANT_Q4_LDS;
             lds_rows = N > 2048 ? 2 : 1;
@@ -286,12 +290,10 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
         return launch_q4_m1_ldsrow(K, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, grid, block, s);
     }
     if (variant == DG_VARIANT_Q4_UNITS) {
-        if (M != 1 || S > 4) return hipErrorInvalidValue;
-        int grid = cfg ? cfg->grid : 0, block = cfg ? cfg->block : 0, depth = cfg ? cfg->unroll : 0;
-        int g0, b0, d0;
-        m1_units_default(N, S, g0, b0, d0);
-        if (!grid && !block) { grid = g0; block = b0; }
-        return launch_q4_m1_units(K, depth ? depth : d0, Wq, Xq, Y, N, grid, block, s);
+        if (S > 4 || M * S > 8) return hipErrorInvalidValue;
+        int grid = cfg ? cfg->grid : 0, block = cfg ? cfg->block : 0;
+        if (!grid && !block) units_default_grid(N, M, grid, block);
+        return launch_q4_units(K, M, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, grid, block, s);
     }
     if (variant == DG_VARIANT_Q4_MFMA) {
         if (cfg && cfg->block) return hipErrorInvalidValue;   // the configuration fixes the workgroup size

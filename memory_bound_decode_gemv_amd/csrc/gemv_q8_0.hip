@@ -149,17 +149,18 @@ hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int
     int variant = cfg && cfg->variant ? cfg->variant : 0;
     int depth = cfg ? cfg->unroll : 0;
     if (variant == 0) {
-        // Measured on MI355X over the decoder shapes and the 70B MLP: one
-        // column streams rows through LDS in 64-pair units.
-        variant = M == 1 && S <= 4 ? DG_VARIANT_Q8_UNITS : DG_VARIANT_Q8_MFMA;
+        // Measured on MI355X over the decoder shapes, the 70B MLP and M =
+        // 1..24: up to eight columns stream rows through LDS in 64-pair units
+        // while M * ceil(K / 4096) <= 8 (at most four columns for matrices of
+        // 1024 rows or fewer, where eight would outrun twelve on the matrix
+        // cores); the rest take the matrix cores.
+        variant = S <= 4 && M * S <= 8 && (N > 1024 || M <= 4) ? DG_VARIANT_Q8_UNITS : DG_VARIANT_Q8_MFMA;
     }
     if (variant == DG_VARIANT_Q8_UNITS) {
-        if (M != 1 || S > 4) return hipErrorInvalidValue;
+        if (S > 4 || M * S > 8) return hipErrorInvalidValue;
         int grid = cfg ? cfg->grid : 0, block = cfg ? cfg->block : 0;
-        int g0, b0, d0;
-        m1_units_default(N, S, g0, b0, d0);
-        if (!grid && !block) { grid = g0; block = b0; }
-        return launch_q8_m1_units(K, depth ? depth : d0, Wq, Xq, Y, N, grid, block, s);
+        if (!grid && !block) units_default_grid(N, M, grid, block);
+        return launch_q8_units(K, M, depth, Wq, Xq, Y, N, grid, block, s);
     }
     if (variant == DG_VARIANT_Q8_LDSROW) {
         if (M != 1 || S > 4) return hipErrorInvalidValue;

@@ -90,6 +90,17 @@ def test_launch_overrides_rejected(lib):
         assert lib.dg_gemv_q8_0_ex(A16, A16, A16, 4, 256, 1, ctypes.byref(cfg), None) == 6
 
 
+def test_units_kernel_rejects_too_many_columns(lib):
+    """The units kernels hold M * ceil(K / 4096) <= 8 activation pairs per lane."""
+    import memory_bound_decode_gemv_amd as m
+    cfg = m.dg_launch(15, 0, 0, 0)
+    assert lib.dg_gemv_q4_0_ex(A16, A16, A16, 4, 8192, 5, ctypes.byref(cfg), None) == 6
+    assert lib.dg_gemv_q4_0_ex(A16, A16, A16, 4, 4096, 9, ctypes.byref(cfg), None) == 6
+    cfg = m.dg_launch(23, 0, 0, 0)
+    assert lib.dg_gemv_q8_0_ex(A16, A16, A16, 4, 16384, 3, ctypes.byref(cfg), None) == 6
+    assert lib.dg_gemv_q8_0_ex(A16, A16, A16, 4, 20480, 1, ctypes.byref(cfg), None) == 6   # rows over 4 units
+
+
 def test_stream_read_rejects_before_launch(lib):
     assert lib.dg_stream_read(A16, 24, A16, 0, 0, 1, None) == 3          # bytes % 16
     assert lib.dg_stream_read(A16, 32, A16, 0, 96, 1, None) == 6         # block not a multiple of 64

@@ -92,19 +92,47 @@ def test_q4_0_m1_units(dg, dev, orc, N, K, launch):
     assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"{N}x{K} {launch}")
 
 
+UNITS_FEW = [None, dict(variant=15), dict(variant=15, unroll=2), dict(variant=15, unroll=4),
+             dict(variant=15, grid=2, block=128), dict(variant=15, grid=1, block=64),
+             dict(variant=15, unroll=2, grid=3, block=192)]
+
+
+@pytest.mark.parametrize("N,K,M", [(1, 256, 4), (7, 4096, 4), (70, 2304, 3), (33, 8192, 2), (130, 4352, 2),
+                                   (301, 4096, 2), (64, 512, 3), (19, 16384, 1), (9, 4096, 8), (40, 1792, 6),
+                                   (33, 8192, 4), (19, 14336, 2), (64, 12288, 2)])
+@pytest.mark.parametrize("launch", UNITS_FEW, ids=[str(v) for v in UNITS_FEW])
+def test_q4_0_units_few_columns(dg, dev, orc, N, K, M, launch):
+    """Two to eight columns through the 64-pair units kernel (the weights of a
+    pair are read and unpacked once for every column; M * ceil(K / 4096) <= 8)."""
+    Wq, Xq = _operands(orc, 232, N, K, M)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
+    assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M), TOL, f"{N}x{K} M={M} {launch}")
+
+
+def test_q4_0_units_reject_too_many_columns(dg, dev, orc):
+    """M * ceil(K / 4096) > 8 does not fit the units kernel's registers: an
+    explicit request is an argument error, launching nothing."""
+    Wq, Xq = _operands(orc, 233, 8, 8192, 5)
+    with pytest.raises(dg.DGError):
+        _gpu(dg, dev, Wq, Xq, 8, 8192, 5, launch=dict(variant=15))
+
+
 @pytest.mark.parametrize("N,launch", [(300, dict(variant=13, grid=1, block=64)),
                                       (129, dict(variant=13, grid=1, block=64, unroll=3)),
                                       (1000, dict(variant=13, grid=2, block=128, unroll=4)),
                                       (64, dict(variant=13, grid=1, block=64)),
                                       (300, dict(variant=15, grid=1, block=64)),
                                       (1000, dict(variant=15, grid=2, block=128, unroll=4))])
-def test_q4_0_m1_many_rows_per_wave(dg, dev, orc, N, launch):
+@pytest.mark.parametrize("M", [1, 3])
+def test_q4_0_m1_many_rows_per_wave(dg, dev, orc, N, launch, M):
     """One wave computing more than 64 rows: its results are stored 64 rows at
-    a time, then the remainder."""
+    a time, then the remainder (three columns: the units kernel only)."""
+    if M > 1 and launch["variant"] != 15:
+        pytest.skip("the LDS-row kernel takes one column")
     K = 512
-    Wq, Xq = _operands(orc, 227, N, K, 1)
-    got = _gpu(dg, dev, Wq, Xq, N, K, 1, launch=launch)
-    assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"{N} {launch}")
+    Wq, Xq = _operands(orc, 227, N, K, M)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
+    assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M), TOL, f"{N} M={M} {launch}")
 
 
 @pytest.mark.parametrize("N,K", [(1, 256), (7, 4096), (70, 4352), (33, 8192), (64, 12288), (130, 2304)])
@@ -215,7 +243,7 @@ def test_q4_0_overrides_beyond_kernel_limits_are_rejected(dg, dev):
                       (4, dict(variant=14, unroll=124)), (4, dict(variant=14, unroll=21622)),
                       (4, dict(variant=14, unroll=10412)), (4, dict(variant=14, unroll=10441)),
                       (20, dict(variant=14, unroll=11611)), (20, dict(variant=14, unroll=10821)),
-                      (2, dict(variant=15)), (1, dict(variant=15, block=512)), (1, dict(variant=15, unroll=5))):
+                      (5, dict(variant=15)), (1, dict(variant=15, block=512)), (1, dict(variant=15, unroll=5))):
         with pytest.raises(dg.DGError) as e:
             dg.dg_gemv_q4_0(W, X, Y, N, K, M, launch=launch)
         assert e.value.status == dg.DG_ERR_ARG, launch

@@ -95,6 +95,21 @@ def test_q8_0_m1_units(dg, dev, orc, N, K, launch):
     assert_close(got[0], orc.gemv_q8_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"{N}x{K} {launch}")
 
 
+UNITS_FEW = [None, dict(variant=23), dict(variant=23, unroll=2), dict(variant=23, unroll=4),
+             dict(variant=23, grid=2, block=128), dict(variant=23, unroll=2, grid=3, block=192)]
+
+
+@pytest.mark.parametrize("N,K,M", [(1, 256, 4), (7, 4096, 4), (70, 2304, 3), (33, 8192, 2), (130, 4352, 2),
+                                   (301, 4096, 2), (1000, 512, 3), (9, 4096, 8), (33, 8192, 4), (19, 14336, 2),
+                                   (64, 12288, 2)])
+@pytest.mark.parametrize("launch", UNITS_FEW, ids=[str(v) for v in UNITS_FEW])
+def test_q8_0_units_few_columns(dg, dev, orc, N, K, M, launch):
+    """Two to eight columns through the 64-pair units kernel (M * ceil(K / 4096) <= 8)."""
+    Wq, Xq = _operands(orc, 432, N, K, M)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
+    assert_close(got, orc.gemv_q8_0_q8_1(Wq, Xq, N, K, M), TOL, f"{N}x{K} M={M} {launch}")
+
+
 MFMA_CFGS = [dict(variant=22)] + [dict(variant=22, unroll=_unroll(*c)) for c in MFMA_TABLE]
 
 
@@ -159,7 +174,7 @@ def test_q8_0_overrides_beyond_kernel_limits_are_rejected(dg, dev):
     Y = torch.zeros(24 * N, dtype=torch.float32, device=dev)
     for M, launch in ((1, dict(variant=21, block=512)), (2, dict(variant=21)), (1, dict(variant=12)),
                       (4, dict(variant=22, unroll=40421)), (12, dict(variant=22, unroll=11611)),
-                      (4, dict(variant=22, block=256)), (1, dict(variant=99)), (2, dict(variant=23)),
+                      (4, dict(variant=22, block=256)), (1, dict(variant=99)), (5, dict(variant=23)),
                       (1, dict(variant=23, unroll=5))):
         with pytest.raises(dg.DGError) as e:
             dg.dg_gemv_q8_0(W, X, Y, N, K, M, launch=launch)
