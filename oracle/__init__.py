@@ -76,6 +76,10 @@ def _bind(lib):
     lib.orc_gemv_q8_0_q8_1.argtypes = [P, P, P, I64, I64, I64]
     lib.orc_dequant_q8_0_block.argtypes = [P, P]
     lib.orc_quantize_q8_0.argtypes = [P, P, I64, I64]
+    lib.orc_gemv_nf4.argtypes = [P, P, P, P, P, I64, I64, I64]
+    lib.orc_gemv_nf4.restype = None
+    lib.orc_quantize_nf4.argtypes = [P, P, P, P, I64, I64, I64]
+    lib.orc_quantize_nf4.restype = None
     lib.orc_argmax_rows.argtypes = [P, P, I64, I64, I64]
     lib.orc_argcompare_rows.argtypes = [P, ctypes.c_int, ctypes.c_int, P, I64, I64, I64]
     lib.orc_checksum_u32.argtypes = [P, ctypes.c_size_t]
@@ -240,6 +244,38 @@ def quantize_q8_0(w: np.ndarray) -> np.ndarray:
     out = np.zeros((N, K // 32 * 34), dtype=np.uint8)
     _load().orc_quantize_q8_0(_ptr(w), _ptr(out), N, K)
     return out
+
+
+# ---- NF4 ----------------------------------------------------------------------
+
+def gemv_nf4(codes: np.ndarray, absmax: np.ndarray, table: np.ndarray, x_bits: np.ndarray,
+             N: int, K: int, B: int) -> np.ndarray:
+    """fp64 y[N] from NF4 codes (uint8 [N][K/2]), float32 absmax [N][K/B], a
+    16-entry float32 table and bfloat16 activation bits x[K]."""
+    assert K % B == 0 and K % 2 == 0
+    c = _c(codes, np.uint8).reshape(-1)
+    a = _c(absmax, np.float32).reshape(-1)
+    t = _c(table, np.float32).reshape(-1)
+    x = _c(x_bits, np.uint16).reshape(-1)
+    assert c.size >= N * K // 2 and a.size >= N * (K // B) and t.size == 16 and x.size >= K
+    y = np.zeros(N, dtype=np.float64)
+    _load().orc_gemv_nf4(_ptr(c), _ptr(a), _ptr(t), _ptr(x), _ptr(y), N, K, B)
+    return y
+
+
+def quantize_nf4(w: np.ndarray, table: np.ndarray, B: int):
+    """w: float32 [N][K] -> (codes uint8 [N][K/2], absmax float32 [N][K/B])."""
+    w = _c(w, np.float32)
+    if w.ndim == 1:
+        w = w.reshape(1, -1)
+    N, K = w.shape
+    assert K % B == 0 and K % 2 == 0
+    t = _c(table, np.float32).reshape(-1)
+    assert t.size == 16
+    codes = np.zeros((N, K // 2), dtype=np.uint8)
+    absmax = np.zeros((N, K // B), dtype=np.float32)
+    _load().orc_quantize_nf4(_ptr(w), _ptr(codes), _ptr(absmax), _ptr(t), N, K, B)
+    return codes, absmax
 
 
 # ---- argmax and checksum ---------------------------------------------------

@@ -283,6 +283,61 @@ void orc_quantize_q8_0(const float* w, uint8_t* Wq, int64_t N, int64_t K)
 }
 
 /* ---------------------------------------------------------------------- */
+/* NF4                                                                    */
+/* ---------------------------------------------------------------------- */
+
+/* The 4-bit code of weight k of a row: byte k/2, the high nibble for even k. */
+static int nf4_code(const uint8_t* row, int64_t k)
+{
+    const uint8_t byte = row[k / 2];
+    return (k % 2 == 0) ? (byte >> 4) : (byte & 0x0F);
+}
+
+void orc_gemv_nf4(const uint8_t* codes, const float* absmax, const float* table,
+                  const uint16_t* x, double* y, int64_t N, int64_t K, int64_t B)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        const uint8_t* row = codes + n * (K / 2);
+        const float* a = absmax + n * (K / B);
+        double acc = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const double w = (double)table[nf4_code(row, k)] * (double)a[k / B];
+            acc += w * orc_bf16_to_double(x[k]);
+        }
+        y[n] = acc;
+    }
+}
+
+void orc_quantize_nf4(const float* w, uint8_t* codes, float* absmax, const float* table,
+                      int64_t N, int64_t K, int64_t B)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        uint8_t* row = codes + n * (K / 2);
+        for (int64_t j = 0; j < K / 2; ++j) row[j] = 0;
+        for (int64_t b = 0; b < K / B; ++b) {
+            const float* x = w + n * K + b * B;
+            float amax = 0.0f;
+            for (int64_t i = 0; i < B; ++i) {
+                float m = fabsf(x[i]);
+                if (m > amax) amax = m;
+            }
+            absmax[n * (K / B) + b] = amax;
+            for (int64_t i = 0; i < B; ++i) {
+                const float r = amax != 0.0f ? x[i] / amax : 0.0f;
+                int c = 0;
+                for (int j = 0; j < 15; ++j) {
+                    const float mid = (table[j] + table[j + 1]) * 0.5f;
+                    if (r > mid) ++c;
+                }
+                const int64_t k = b * B + i;
+                if (k % 2 == 0) row[k / 2] |= (uint8_t)(c << 4);
+                else row[k / 2] |= (uint8_t)c;
+            }
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
 /* argmax                                                                 */
 /* ---------------------------------------------------------------------- */
 

@@ -9,6 +9,11 @@
  * is involved.
  *
  * Sources (the pages each routine follows):
+ *  - bitsandbytes issue "70B 4-bit LLM decode bottlenecked by HIP kernel
+ *    (kgemm_4bit_inference_naive) efficiency", benchmark table and the
+ *    optimisation phases of its first comment: an M = 1 GEMV over 4-bit
+ *    weights that index a 16-entry float table, scaled per block by an
+ *    absmax, with bfloat16 activations and float arithmetic.
  *  - batch1-cdna README ("Microbenchmarks for the batch-size-1 LLM decode
  *    regime on AMD CDNA3"), FP16 GEMV section: y = W x, one output per row,
  *    fp16 operands, checked against a CPU reference that accumulates in double.
@@ -114,6 +119,28 @@ void orc_dequant_q8_0_block(const uint8_t* blk, double out[32]);
  * to [-127, 127]; a block of zeros gets d = 0 and codes 0; stored
  * d = binary16(d).  w is [N][K]. */
 void orc_quantize_q8_0(const float* w, uint8_t* Wq, int64_t N, int64_t K);
+
+/* ---- NF4: 4-bit table codes with a per-block absmax, bfloat16 activations ----
+ *
+ * Layout (readings; the page names the table, the block-wise absmax and the
+ * bfloat16 activations but not the byte layout):
+ *   codes   N rows of K/2 bytes; byte j of a row holds weight 2j in its HIGH
+ *           nibble and weight 2j+1 in its LOW nibble;
+ *   absmax  float32 [N][K/B]: absmax[n][b] scales weights bB .. bB+B-1 of row n;
+ *   table   16 float32 values (the code table);
+ *   x       K bfloat16 bits.
+ *   y[n] = sum_{k<K} table[q(n,k)] * absmax[n][k/B] * x[k]
+ * summed in increasing k in double.  K must be a multiple of B. */
+void orc_gemv_nf4(const uint8_t* codes, const float* absmax, const float* table,
+                  const uint16_t* x, double* y, int64_t N, int64_t K, int64_t B);
+
+/* The quantiser that produces the test operands, per block of B weights of a
+ * row: absmax = the largest |w| (binary32); r = w / absmax in binary32 (r = 0
+ * when absmax is 0); the code is the number of j in 0..14 with
+ * r > (table[j] + table[j+1]) * 0.5f, each midpoint in binary32: the nearest
+ * table level, a tie going to the lower one.  table must be increasing. */
+void orc_quantize_nf4(const float* w, uint8_t* codes, float* absmax, const float* table,
+                      int64_t N, int64_t K, int64_t B);
 
 /* ---- argmax over rows ---- */
 

@@ -12,7 +12,10 @@ Recipe (the workloads of the pages, with synthetic values):
   * weights to be quantised to Q4_0 and activations to be quantised to Q8_1
     are N(0, 1) float32 (the quantisers live in the library and in the oracle);
   * argmax logits are uniform(-10, 10) float32, with exact duplicate maxima
-    planted in about 1% of the rows (at least one row).
+    planted in about 1% of the rows (at least one row);
+  * weights to be quantised to NF4 are N(0, 1) float32 with bfloat16
+    activations x ~ N(0, 1), and the 16-level code table both sides receive
+    is ``nf4_table()``.
 
 Every stream comes from numpy's PCG64 seeded with
 ``SeedSequence([0xD6, config, kind, copy, column])``; ``kind`` is 0 for weights,
@@ -118,3 +121,28 @@ def gpu_uniform(key, shape, lo: float, hi: float):
     g = gpu_generator(*key)
     t = torch.rand(shape, generator=g, device="cuda", dtype=torch.float32)
     return t.mul_(hi - lo).add_(lo)
+
+
+def nf4_table() -> np.ndarray:
+    """The 16-entry code table of the NF4 workload, float32, increasing.
+
+    An input of both the library and the oracle (the kernel takes its table as
+    an argument, as the bitsandbytes kernel takes its quant_map), not part of
+    the method's arithmetic.  It is a NormalFloat table in the manner of QLoRA
+    (Dettmers et al., 2023, "4-bit NormalFloat Quantization"): levels at
+    standard-normal quantiles of evenly spaced probabilities, eight on the
+    non-negative side and seven on the negative side of an exact zero,
+    normalised so that the extremes are -1 and 1.  The outermost probability
+    is 1 - (1/32 + 1/30)/2; the positive levels are the quantiles at 8 evenly
+    spaced probabilities from there down to 1/2 (exclusive), the negative ones
+    at 7.  This reading is not claimed to match any library's table bit for
+    bit; the kernel works with any increasing table.
+    """
+    from statistics import NormalDist
+    inv = NormalDist().inv_cdf
+    p_hi = 1.0 - (1.0 / 32.0 + 1.0 / 30.0) / 2.0
+    pos = [inv(p_hi + (0.5 - p_hi) * i / 8.0) for i in range(8)]    # p_hi .. just above 1/2
+    neg = [-inv(p_hi + (0.5 - p_hi) * i / 7.0) for i in range(7)]
+    top = inv(p_hi)
+    levels = sorted([v / top for v in pos] + [0.0] + [v / top for v in neg])
+    return np.array(levels, dtype=np.float32)

@@ -57,6 +57,16 @@ MUTANTS = [
      "if (dtype == 2) return orc_half_to_double(((const uint16_t*)x)[i]);"),
     ("argcompare ignores ld", "double v = argcompare_value(x, dtype, r * ld + c);",
      "double v = argcompare_value(x, dtype, r * C + c);"),
+    ("nf4 nibble order swapped", "return (k % 2 == 0) ? (byte >> 4) : (byte & 0x0F);",
+     "return (k % 2 == 0) ? (byte & 0x0F) : (byte >> 4);"),
+    ("nf4 absmax of the first block only", "(double)a[k / B];", "(double)a[0];"),
+    ("nf4 absmax ignored", "const double w = (double)table[nf4_code(row, k)] * (double)a[k / B];",
+     "const double w = (double)table[nf4_code(row, k)];"),
+    ("nf4 absmax rows strided by B", "const float* a = absmax + n * (K / B);", "const float* a = absmax + n * B;"),
+    ("nf4 quantiser ties go up", "if (r > mid) ++c;", "if (r >= mid) ++c;"),
+    ("nf4 quantiser signed maximum", "float m = fabsf(x[i]);", "float m = x[i];"),
+    ("nf4 quantiser packs the low nibble first", "if (k % 2 == 0) row[k / 2] |= (uint8_t)(c << 4);\n                else row[k / 2] |= (uint8_t)c;",
+     "if (k % 2 == 1) row[k / 2] |= (uint8_t)(c << 4);\n                else row[k / 2] |= (uint8_t)c;"),
     ("checksum xor instead of add", "for (size_t i = 0; i < n; ++i) s += w[i];", "for (size_t i = 0; i < n; ++i) s ^= w[i];"),
 ]
 

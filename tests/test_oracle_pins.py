@@ -480,3 +480,128 @@ def test_checksum_closed_forms(orc):
     g = np.random.default_rng(29)
     w = g.integers(0, 2**32, size=12345, dtype=np.uint64).astype(np.uint32)
     assert orc.checksum_u32(w) == int(sum(int(v) for v in w)) % 2**32
+
+
+# ---------------------------------------------------------------------------
+# NF4: 4-bit table codes, per-block absmax, bfloat16 activations
+# ---------------------------------------------------------------------------
+
+def _golden_nf4():
+    with open(os.path.join(GOLDEN, "nf4_worked.json")) as f:
+        return json.load(f)
+
+
+def _bf16(v):
+    """bfloat16 bits of values that bfloat16 holds exactly."""
+    a = np.asarray(v, dtype=np.float32)
+    bits = a.view(np.uint32)
+    assert np.all(bits & 0xFFFF == 0)
+    return (bits >> 16).astype(np.uint16)
+
+
+def test_nf4_worked_example(orc):
+    g = _golden_nf4()
+    codes = np.stack([_hex(h) for h in g["codes_hex"]])
+    y = orc.gemv_nf4(codes, np.array(g["absmax"], np.float32), np.array(g["table"], np.float32),
+                     _bf16(g["x"]), g["N"], g["K"], g["B"])
+    assert list(y) == g["y"]
+
+
+def test_nf4_closed_forms(orc):
+    """Constant codes and absmax: y = table[c] * a * sum(x); one nibble of each
+    byte selected by the activations; one block selected by the activations."""
+    t = np.array([(j - 7) / 4 for j in range(16)], np.float32)
+    K, B = 256, 64
+    g = np.random.default_rng(5)
+    x = np.round(g.standard_normal(K) * 8) / 8                      # exact in bfloat16
+    xb = _bf16(x)
+    for c in (0, 3, 7, 15):
+        codes = np.full((1, K // 2), c * 17, np.uint8)
+        y = orc.gemv_nf4(codes, np.full((1, K // B), 0.5, np.float32), t, xb, 1, K, B)
+        assert y[0] == float(t[c]) * 0.5 * math.fsum(x)
+    hi, lo = 13, 2
+    codes = np.full((1, K // 2), hi * 16 + lo, np.uint8)
+    even = np.zeros(K)
+    even[0::2] = 1.0
+    y = orc.gemv_nf4(codes, np.ones((1, K // B), np.float32), t, _bf16(even), 1, K, B)
+    assert y[0] == float(t[hi]) * (K // 2)                          # even weights: the high nibble
+    y = orc.gemv_nf4(codes, np.ones((1, K // B), np.float32), t, _bf16(1.0 - even), 1, K, B)
+    assert y[0] == float(t[lo]) * (K // 2)
+    absmax = np.array([[1.0, 2.0, 4.0, 8.0]], np.float32)
+    codes = np.full((1, K // 2), 15 * 17, np.uint8)
+    for b in range(K // B):
+        sel = np.zeros(K)
+        sel[b * B:(b + 1) * B] = 1.0
+        y = orc.gemv_nf4(codes, absmax, t, _bf16(sel), 1, K, B)
+        assert y[0] == float(t[15]) * float(absmax[0, b]) * B
+
+
+def test_nf4_against_brute_force_in_rationals(orc):
+    """Tiny random operands evaluated exactly (fractions) from the definition;
+    the double sum may differ only by its own rounding."""
+    g = np.random.default_rng(41)
+    t = np.sort(g.standard_normal(16)).astype(np.float32)
+    N, K, B = 3, 64, 32
+    codes = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    absmax = np.abs(g.standard_normal((N, K // B))).astype(np.float32)
+    x = g.standard_normal(K).astype(np.float32)
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    xv = [Fraction(float((np.uint32(v) << 16).view(np.float32))) for v in xb]
+    y = orc.gemv_nf4(codes, absmax, t, xb, N, K, B)
+    for n in range(N):
+        exact = Fraction(0)
+        for j in range(K // 2):
+            for k, q in ((2 * j, int(codes[n, j]) >> 4), (2 * j + 1, int(codes[n, j]) & 15)):
+                exact += Fraction(float(t[q])) * Fraction(float(absmax[n, k // B])) * xv[k]
+        assert abs(Fraction(y[n]) - exact) <= Fraction(2.0 ** -40) * sum(
+            abs(Fraction(float(t[q]))) for q in range(16)) * max(abs(v) for v in xv) * 64
+
+
+def test_nf4_quantiser_round_trip_nearest_level_and_ties(orc):
+    import synth
+    t = synth.nf4_table()
+    g = np.random.default_rng(43)
+    N, K, B = 4, 256, 64
+    q = g.integers(0, 16, size=(N, K))
+    q[:, ::B] = 15                                                  # every block holds the level 1.0
+    a = np.float32(2.0) ** g.integers(-3, 4, size=(N, K // B)).astype(np.float32)
+    w = t[q] * np.repeat(a, B, axis=1)
+    codes, absmax = orc.quantize_nf4(w.astype(np.float32), t, B)
+    assert np.array_equal(absmax, a)
+    got = np.stack([codes >> 4, codes & 15], axis=2).reshape(N, K)
+    assert np.array_equal(got, q)
+    # random weights: the nearest level of r = w / absmax (binary32), ties to the lower
+    w = g.standard_normal((N, K)).astype(np.float32)
+    codes, absmax = orc.quantize_nf4(w, t, B)
+    assert np.array_equal(absmax, np.abs(w).reshape(N, K // B, B).max(axis=2))
+    got = np.stack([codes >> 4, codes & 15], axis=2).reshape(N, K)
+    r = (w.reshape(N, K // B, B) / absmax[:, :, None]).reshape(N, K).astype(np.float64)
+    dist = np.abs(r[:, :, None] - t.astype(np.float64)[None, None, :])
+    best = dist.min(axis=2)
+    assert np.all(dist[np.arange(N)[:, None], np.arange(K)[None, :], got] == best)
+    # exact ties: r on a midpoint of a dyadic table goes to the lower level
+    td = np.array([(j - 7) / 8 for j in range(16)], np.float32)
+    wt = np.array([[1.0, 0.0625, -0.0625, 0.1875, 0.0, -1.0, 0.5, 0.4375]], np.float32)
+    codes, absmax = orc.quantize_nf4(wt, td, 8)
+    got = np.stack([codes >> 4, codes & 15], axis=2).reshape(-1)
+    assert list(got) == [15, 7, 6, 8, 7, 0, 11, 10]
+    assert absmax[0, 0] == 1.0
+    # a block of zeros: absmax 0, every code the level of 0
+    codes, absmax = orc.quantize_nf4(np.zeros((1, 64), np.float32), t, 64)
+    assert absmax[0, 0] == 0 and np.all(codes == 7 * 17)
+
+
+def test_nf4_workload_table(orc):
+    """The NF4 workload's table: increasing, exact 0 and +-1 at the ends, and
+    its levels are standard-normal quantiles (scipy's, an independent routine)."""
+    import synth
+    from scipy.stats import norm
+    t = synth.nf4_table()
+    assert t.dtype == np.float32 and t.size == 16 and np.all(np.diff(t) > 0)
+    assert t[0] == -1.0 and t[7] == 0.0 and t[15] == 1.0
+    p_hi = 1.0 - (1.0 / 32.0 + 1.0 / 30.0) / 2.0
+    top = norm.ppf(p_hi)
+    pos = norm.ppf(np.linspace(p_hi, 0.5, 9)[:-1]) / top
+    neg = -norm.ppf(np.linspace(p_hi, 0.5, 8)[:-1]) / top
+    ref = np.sort(np.concatenate([pos, [0.0], neg])).astype(np.float32)
+    assert np.allclose(t, ref, rtol=0, atol=2e-7)
