@@ -22,7 +22,7 @@ bounded sample.
 
 --suite instead measures every configuration of the path (ceiling sweep, the
 fp16 ablation variants, bf16 decoder shapes, the lm-head, Q4_0 M = 1..24,
-argmax, the greedy tail) and writes one JSON record per measurement.
+argmax, the greedy tail, Q8_0 and NF4) and writes one JSON record per measurement.
 """
 from __future__ import annotations
 
@@ -187,6 +187,25 @@ def q8_0_copies(cfg, N, K, ncopies):
         del w
         Ws.append(Wq)
     return Ws
+
+
+def nf4_copies(cfg, N, K, B, ncopies):
+    """NF4 codes and per-block absmax (the library's quantiser, the NormalFloat
+    table of the seeded generators) for `ncopies` seeded weight draws."""
+    import synth
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    table = torch.from_numpy(synth.nf4_table()).to("cuda")
+    out = []
+    for c in range(ncopies):
+        w = synth.gpu_normal((cfg, synth.KIND_W, c, 0), (N, K), 1.0, torch.float32)
+        codes = torch.empty(N * K // 2, dtype=torch.uint8, device="cuda")
+        absmax = torch.empty(N * (K // B), dtype=torch.float32, device="cuda")
+        dg.dg_quantize_nf4(w, codes, absmax, table, N, K, B)
+        torch.cuda.synchronize()
+        del w
+        out.append((codes, absmax))
+    return out, table
 
 
 def q8_columns(cfg, K, M):
@@ -460,6 +479,8 @@ def suite(args):
         suite_argmax(dg, torch, emit, ceil_gbps)
     if want("tail"):
         suite_tail(dg, torch, emit, ceil_gbps)
+    if want("nf4"):
+        suite_nf4(dg, torch, emit, ceil_gbps)
     return recs
 
 
@@ -733,6 +754,51 @@ def suite_argmax(dg, torch, emit, ceil_gbps):
         torch.cuda.empty_cache()
 
 
+def bytes_nf4(N, K, B):
+    # codes, per-block absmax (fp32), the bf16 column, the 16-entry table, fp32 outputs
+    return N * K // 2 + 4 * N * (K // B) + 2 * K + 64 + 4 * N
+
+
+def suite_nf4(dg, torch, emit, ceil_gbps):
+    """NF4 x bf16 at M = 1: the decoder shapes and the 70B MLP pair at block 64
+    (default launch and a sweep of table copies, rows in flight and grid), the
+    70B up-projection at every block size, and the read probe over its codes."""
+    import synth
+    for (N, K) in [(4096, 4096), (14336, 4096), (4096, 14336), (Q4_N, Q4_K), (Q4_K, Q4_N)]:
+        B = 64
+        nc = copies_for(bytes_nf4(N, K, B))
+        ops, table = nf4_copies(6, N, K, B, nc)
+        x = synth.gpu_normal((6, synth.KIND_X, 0, 0), (K,), 1.0, torch.bfloat16)
+        y = torch.empty(N, dtype=torch.float32, device="cuda")
+        launches = [("default", None)] + [(f"tc{tc} ahead{h} g{g}", dict(variant=31, unroll=tc + 1000 * h, grid=g))
+                                          for tc in (8, 16) for h in (4, 8) for g in (256, 512, 1024, 2048)]
+        for lname, launch in launches:
+            calls = [(lambda c=c, launch=launch: dg.dg_gemv_nf4(ops[c % nc][0], ops[c % nc][1], table, x, y,
+                                                               N=N, K=K, B=B, launch=launch))
+                     for c in range(n_calls(nc))]
+            us, iqr = time_per_call(calls)
+            emit(record(f"gemv_nf4 {N}x{K} B={B}", us, iqr, bytes_nf4(N, K, B), ceil_gbps, variant=lname,
+                        copies=nc))
+        if (N, K) == (Q4_N, Q4_K):
+            emit({"name": f"gemv_nf4 {N}x{K} read probe (codes only)",
+                  **read_probe([c for c, _ in ops], label=f"nf4 codes {N}x{K}")})
+        del ops
+        torch.cuda.empty_cache()
+    N, K = Q4_N, Q4_K
+    for B in (32, 128, 256):
+        nc = copies_for(bytes_nf4(N, K, B))
+        ops, table = nf4_copies(7, N, K, B, nc)
+        x = synth.gpu_normal((7, synth.KIND_X, 0, 0), (K,), 1.0, torch.bfloat16)
+        y = torch.empty(N, dtype=torch.float32, device="cuda")
+        calls = [(lambda c=c: dg.dg_gemv_nf4(ops[c % nc][0], ops[c % nc][1], table, x, y, N=N, K=K, B=B))
+                 for c in range(n_calls(nc))]
+        us, iqr = time_per_call(calls)
+        emit(record(f"gemv_nf4 {N}x{K} B={B}", us, iqr, bytes_nf4(N, K, B), ceil_gbps, variant="default",
+                    copies=nc))
+        del ops
+        torch.cuda.empty_cache()
+
+
 def suite_tail(dg, torch, emit, ceil_gbps):
     # the greedy tail: lm-head bf16 GEMV -> fp32 logits -> argmax
     N, K = 128256, 4096
@@ -761,7 +827,8 @@ def suite_tail(dg, torch, emit, ceil_gbps):
 def profile_kernels(args):
     """Launches each profiled kernel eagerly (one dispatch each) on known
     workloads, for rocprofv3 counter runs: the Q4_0 M=1 decode GEMV at
-    28672x8192, the fp16 GEMV at 4096x4096, the streaming read of 1 GiB, and a
+    28672x8192, the fp16 GEMV at 4096x4096, the NF4 GEMV at 28672x8192 (block
+    64), the streaming read of 1 GiB, and a
     plain 1 GiB device-to-device copy whose FETCH_SIZE / WRITE_SIZE calibrate
     the counters (known bytes read and written)."""
     import memory_bound_decode_gemv_amd as dg
@@ -773,6 +840,10 @@ def profile_kernels(args):
     n16 = copies_for(2 * FP16_N * FP16_K)
     W16, x16 = dense_copies(0, FP16_N, FP16_K, n16, torch.float16)
     y16 = torch.empty(FP16_N, dtype=torch.float16, device="cuda")
+    nn = copies_for(bytes_nf4(Q4_N, Q4_K, 64))
+    nf, table = nf4_copies(6, Q4_N, Q4_K, 64, nn)
+    xn = torch.ones(Q4_K, dtype=torch.bfloat16, device="cuda")
+    yn = torch.empty(Q4_N, dtype=torch.float32, device="cuda")
     src = torch.empty(GIB // 4, dtype=torch.int32, device="cuda").fill_(3)
     dst = torch.empty_like(src)
     cs = torch.zeros(768, dtype=torch.int32, device="cuda")
@@ -781,12 +852,14 @@ def profile_kernels(args):
         dg.dg_gemv_q4_0(Wq[c % nq], Xq, Yq, Q4_N, Q4_K, 1)
     for c in range(n16):
         dg.dg_gemv_f16(W16[c], x16, y16)
+    for c in range(2 * nn):
+        dg.dg_gemv_nf4(nf[c % nn][0], nf[c % nn][1], table, xn, yn, N=Q4_N, K=Q4_K, B=64)
     for _ in range(4):
         dg.dg_stream_read(src, cs, grid_blocks=768, block_threads=64, flags=dg.DG_READ_NONTEMPORAL)
     for _ in range(4):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"[profile-kernels] q4_0 x{2 * nq}, f16 x{n16}, stream_read 1 GiB x4, copy 1 GiB x4")
+    log(f"[profile-kernels] q4_0 x{2 * nq}, f16 x{n16}, nf4 x{2 * nn}, stream_read 1 GiB x4, copy 1 GiB x4")
 
 
 def main():
@@ -799,7 +872,7 @@ def main():
     ap.add_argument("--profile-kernels", action="store_true",
                     help="launch each profiled kernel eagerly on known workloads (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
-                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q8,m1,argmax,tail")
+                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q8,m1,argmax,tail,nf4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     args = ap.parse_args()

@@ -161,6 +161,53 @@ dg_status dg_gemv_q8_0(const void* Wq, const void* Xq, float* Y,
                        int64_t N, int64_t K, int M, dg_stream stream);
 
 /* ------------------------------------------------------------------------
+ * NF4 weights (4-bit codes into a 16-entry float table, per-block absmax)
+ * x bfloat16 activations, one column
+ *
+ *   y[n] = sum_k table[q(n,k)] * absmax[n][k/B] * x[k]
+ *
+ * The lookup-table 4-bit M = 1 GEMV of the bitsandbytes issue on 70B 4-bit
+ * decode (benchmark table: 28672 x 8192 NF4 weights against a bfloat16
+ * activation; its optimisation phases: a float table quant_map, a per-block
+ * absmax, float arithmetic).  The page fixes no byte layout; this library
+ * reads it as follows:
+ *
+ *   codes   device, N rows of K/2 bytes, rows back to back; byte j of a row
+ *           holds weight 2j in its HIGH nibble and weight 2j+1 in its LOW
+ *           nibble; 16-byte aligned.
+ *   absmax  device float32 [N][K/B] (absmax[n][b] scales weights bB..bB+B-1
+ *           of row n); 16-byte aligned.
+ *   table   device float32 [16], any finite values (the kernel keeps each
+ *           value as the sum of two bfloat16 parts, within 2^-17 of it);
+ *           16-byte aligned.
+ *   x       device bfloat16 [K]; 16-byte aligned.
+ *   y       device float32 [N]; 4-byte aligned.
+ *   N       rows, 0 <= N < 2^31.
+ *   K       multiple of 256 and of 4*B, 0 <= K <= 32768 (a workgroup has
+ *           one wave per 2048 weights of a row).
+ *   B       block size: 32, 64, 128 or 256.
+ * Products and sums are fp32; K = 0 gives y = 0.
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+dg_status dg_gemv_nf4(const void* codes, const float* absmax, const float* table, const void* x, float* y,
+                      int64_t N, int64_t K, int B, dg_stream stream);
+
+/* NF4 quantiser (the step that produces the operands of dg_gemv_nf4), per
+ * block of B weights of a row: absmax = the largest |w| (binary32); r = w /
+ * absmax correctly rounded in binary32 (r = 0 when absmax is 0); the code is
+ * the number of j in 0..14 with r > (table[j] + table[j+1]) * 0.5f, each
+ * midpoint in binary32 -- the nearest table level, a tie going to the lower
+ * one.  table must be increasing.
+ *   w       device float32 [N][K]; 16-byte aligned.
+ *   codes   device, N*K/2 bytes, layout as for dg_gemv_nf4; 2-byte aligned.
+ *   absmax  device float32 [N][K/B]; 4-byte aligned.
+ *   table   device float32 [16]; 4-byte aligned.
+ *   K multiple of B, B in {32, 64, 128, 256}.
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_HIP. */
+dg_status dg_quantize_nf4(const float* w, void* codes, float* absmax, const float* table,
+                          int64_t N, int64_t K, int B, dg_stream stream);
+
+/* ------------------------------------------------------------------------
  * Quantisers (the step before dg_gemv_q4_0 / dg_gemv_q8_0)
  *
  * Q8_1, per 32-activation block: a = max|x|; d = a/127 (fp32); q = x/d
@@ -293,7 +340,9 @@ typedef struct {
                       (2..4);
                       *_MFMA: RT*10000 + KS*100 + DEPTH*10 + CB/8 (row
                       tiles and K parts per workgroup, pipeline depth,
-                      blocks per chunk)                                      */
+                      blocks per chunk);
+                      NF4: code-pair table copies (8 or 16) + 100 * partial
+                      sums per lane (1, 2) + 1000 * rows in flight (4, 8)    */
 } dg_launch;
 
 enum {
@@ -312,7 +361,10 @@ enum {
     /* Q8_0 */
     DG_VARIANT_Q8_LDSROW = 21,      /* M = 1: weight rows copied to LDS (K <= 16384)             */
     DG_VARIANT_Q8_MFMA = 22,        /* int8 matrix cores                                          */
-    DG_VARIANT_Q8_UNITS = 23        /* as DG_VARIANT_Q4_UNITS, Q8_0 weights                        */
+    DG_VARIANT_Q8_UNITS = 23,       /* as DG_VARIANT_Q4_UNITS, Q8_0 weights                        */
+    /* NF4 */
+    DG_VARIANT_NF4_UNITS = 31       /* code bytes looked up in a byte-pair table in LDS; one
+                                       wave per 2048 weights of a row (block = 64*ceil(K/2048)) */
 };
 
 dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K,
@@ -323,6 +375,8 @@ dg_status dg_gemv_q4_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, i
                           int M, const dg_launch* cfg, dg_stream stream);
 dg_status dg_gemv_q8_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K,
                           int M, const dg_launch* cfg, dg_stream stream);
+dg_status dg_gemv_nf4_ex(const void* codes, const float* absmax, const float* table, const void* x, float* y,
+                         int64_t N, int64_t K, int B, const dg_launch* cfg, dg_stream stream);
 
 #ifdef __cplusplus
 }

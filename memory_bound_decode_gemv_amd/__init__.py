@@ -58,6 +58,7 @@ EXPORTED = (
     "dg_gemv_f16_ex", "dg_gemv_bf16_ex", "dg_gemv_q4_0_ex",
     "dg_gemv_q8_0", "dg_gemv_q8_0_ex", "dg_quantize_q8_0",
     "dg_argcompare_rows", "dg_gemv_bf16_argmax_workspace_bytes", "dg_gemv_bf16_argmax",
+    "dg_gemv_nf4", "dg_gemv_nf4_ex", "dg_quantize_nf4",
 )
 
 
@@ -140,6 +141,12 @@ def _lib():
     lib.dg_gemv_bf16_argmax_workspace_bytes.restype = ctypes.c_size_t
     lib.dg_gemv_bf16_argmax.argtypes = [P, P, P, P, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.dg_gemv_bf16_argmax.restype = st
+    lib.dg_gemv_nf4.argtypes = [P, P, P, P, P, I64, I64, I32, P]
+    lib.dg_gemv_nf4.restype = st
+    lib.dg_gemv_nf4_ex.argtypes = [P, P, P, P, P, I64, I64, I32, ctypes.POINTER(dg_launch), P]
+    lib.dg_gemv_nf4_ex.restype = st
+    lib.dg_quantize_nf4.argtypes = [P, P, P, P, I64, I64, I32, P]
+    lib.dg_quantize_nf4.restype = st
     _handle = lib
     return lib
 
@@ -285,6 +292,53 @@ def dg_gemv_q4_0(Wq, Xq, Y, N, K, M, launch=None, stream=None):
 def dg_gemv_q8_0(Wq, Xq, Y, N, K, M, launch=None, stream=None):
     """Y[M][N] (float32) from Q8_0 weight bytes and Q8_1 activation bytes (uint8 tensors)."""
     return _gemv_quant("dg_gemv_q8_0", 34, Wq, Xq, Y, N, K, M, launch, stream)
+
+
+def dg_gemv_nf4(codes, absmax, table, x, y, N=None, K=None, B=64, launch=None, stream=None):
+    """y[N] (float32) from NF4 codes (uint8 [N*K/2]), float32 absmax [N*K/B],
+    a float32 table [16] and bfloat16 activations x [K]."""
+    torch = _torch()
+    _need(codes, (torch.uint8,), "codes")
+    _need(absmax, (torch.float32,), "absmax")
+    _need(table, (torch.float32,), "table")
+    _need(x, (torch.bfloat16,), "x")
+    _need(y, (torch.float32,), "y")
+    K = x.numel() if K is None else int(K)
+    N = y.numel() if N is None else int(N)
+    B = int(B)
+    if N > 0 and K > 0 and B > 0:
+        _fits(codes, N * K // 2, "codes")
+        _fits(absmax, N * (K // B) * 4, "absmax")
+        _fits(table, 64, "table")
+        _fits(x, K * 2, "x")
+    if N > 0:
+        _fits(y, N * 4, "y")
+    lib = _lib()
+    args = (_ptr(codes), _ptr(absmax), _ptr(table), _ptr(x), _ptr(y), N, K, B)
+    if launch is None:
+        st = lib.dg_gemv_nf4(*args, _stream(stream))
+    else:
+        st = lib.dg_gemv_nf4_ex(*args, ctypes.byref(_cfg(**launch)), _stream(stream))
+    _check(st, "dg_gemv_nf4")
+    return y
+
+
+def dg_quantize_nf4(w, codes, absmax, table, N, K, B=64, stream=None):
+    """float32 [N][K] -> NF4 codes (uint8 [N*K/2]) and float32 absmax [N*K/B]."""
+    torch = _torch()
+    _need(w, (torch.float32,), "w")
+    _need(codes, (torch.uint8,), "codes")
+    _need(absmax, (torch.float32,), "absmax")
+    _need(table, (torch.float32,), "table")
+    N, K, B = int(N), int(K), int(B)
+    if N > 0 and K > 0 and B > 0:
+        _fits(w, N * K * 4, "w")
+        _fits(codes, N * K // 2, "codes")
+        _fits(absmax, N * (K // B) * 4, "absmax")
+        _fits(table, 64, "table")
+    _check(_lib().dg_quantize_nf4(_ptr(w), _ptr(codes), _ptr(absmax), _ptr(table), N, K, B, _stream(stream)),
+           "dg_quantize_nf4")
+    return codes, absmax
 
 
 def dg_quantize_q8_1(x, Xq, M, K, stream=None):

@@ -70,6 +70,28 @@ dg_status gemv_quant_checked(bool q8, const void* Wq, const void* Xq, float* Y, 
     return hip_status(e);
 }
 
+bool nf4_block_ok(int B) { return B == 32 || B == 64 || B == 128 || B == 256; }
+
+dg_status gemv_nf4_checked(const void* codes, const float* absmax, const float* table, const void* x, float* y,
+                           int64_t N, int64_t K, int B, const dg_launch* cfg, dg_stream stream) {
+    if (N < 0 || N > kI32Max || K < 0 || K > 32768 || K % 256 != 0 || !nf4_block_ok(B) || K % (4 * B) != 0)
+        return DG_ERR_SHAPE;
+    if (!launch_ok(cfg)) return DG_ERR_ARG;
+    if (N == 0) return DG_OK;
+    if (!y || (K > 0 && (!codes || !absmax || !table || !x))) return DG_ERR_NULL;
+    if (!aligned(y, 4)) return DG_ERR_MISALIGNED;
+    if (K > 0 && (!aligned(codes, 16) || !aligned(absmax, 16) || !aligned(table, 16) || !aligned(x, 16)))
+        return DG_ERR_MISALIGNED;
+    if (K == 0) {   // empty sums: y = 0
+        hipLaunchKernelGGL(k_fill_zero_f32, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                           y, N);
+        return hip_status(hipGetLastError());
+    }
+    hipError_t e = launch_gemv_nf4(codes, absmax, table, x, y, (int)N, (int)K, B, cfg, (hipStream_t)stream);
+    if (e == hipErrorInvalidValue && cfg && (cfg->variant || cfg->unroll || cfg->block)) return DG_ERR_ARG;
+    return hip_status(e);
+}
+
 }  // namespace
 
 int device_cu_count() {
@@ -193,6 +215,25 @@ dg_status dg_quantize_q8_0(const float* w, void* Wq, int64_t N, int64_t K, dg_st
     if (!w || !Wq) return DG_ERR_NULL;
     if (!aligned(w, 16) || !aligned(Wq, 2)) return DG_ERR_MISALIGNED;
     return hip_status(launch_quantize_q8_0(w, Wq, N, K, (hipStream_t)stream));
+}
+
+dg_status dg_gemv_nf4(const void* codes, const float* absmax, const float* table, const void* x, float* y,
+                      int64_t N, int64_t K, int B, dg_stream stream) {
+    return gemv_nf4_checked(codes, absmax, table, x, y, N, K, B, nullptr, stream);
+}
+
+dg_status dg_gemv_nf4_ex(const void* codes, const float* absmax, const float* table, const void* x, float* y,
+                         int64_t N, int64_t K, int B, const dg_launch* cfg, dg_stream stream) {
+    return gemv_nf4_checked(codes, absmax, table, x, y, N, K, B, cfg, stream);
+}
+
+dg_status dg_quantize_nf4(const float* w, void* codes, float* absmax, const float* table, int64_t N, int64_t K,
+                          int B, dg_stream stream) {
+    if (N < 0 || K < 0 || !nf4_block_ok(B) || K % B != 0 || N * (K / B) > kI32Max * 256LL) return DG_ERR_SHAPE;
+    if (N == 0 || K == 0) return DG_OK;
+    if (!w || !codes || !absmax || !table) return DG_ERR_NULL;
+    if (!aligned(w, 16) || !aligned(codes, 2) || !aligned(absmax, 4) || !aligned(table, 4)) return DG_ERR_MISALIGNED;
+    return hip_status(launch_quantize_nf4(w, codes, absmax, table, N, K, B, (hipStream_t)stream));
 }
 
 size_t dg_argmax_workspace_bytes(int64_t R, int64_t C) { return argmax_workspace_bytes(R, C); }

@@ -82,6 +82,13 @@ hipError_t launch_q8_mfma(int M, int unroll, const void* Wq, const void* Xq, flo
                           hipStream_t s);
 
 hipError_t launch_quantize_q8_0(const float* w, void* Wq, int64_t N, int64_t K, hipStream_t s);
+
+// NF4 x bfloat16, one column (K <= 32768; B in {32, 64, 128, 256}; K % (4B) == 0),
+// and the NF4 quantiser.
+hipError_t launch_gemv_nf4(const void* codes, const float* absmax, const float* table, const void* x, float* y,
+                           int N, int K, int B, const dg_launch* cfg, hipStream_t s);
+hipError_t launch_quantize_nf4(const float* w, void* codes, float* absmax, const float* table, int64_t N,
+                               int64_t K, int B, hipStream_t s);
 hipError_t launch_quantize_q8_1(const float* x, void* Xq, int64_t M, int64_t K, hipStream_t s);
 hipError_t launch_quantize_q4_0(const float* w, void* Wq, int64_t N, int64_t K, hipStream_t s);
 

@@ -1,0 +1,307 @@
+// gemv_nf4.hip -- NF4 x bfloat16 GEMV for one activation column, and the NF4
+// quantiser.
+//
+// The lookup-table 4-bit M = 1 GEMV of the bitsandbytes issue on 70B 4-bit
+// decode: each weight is a 4-bit index into a 16-entry float table, scaled by
+// its block's absmax, against bfloat16 activations, in float arithmetic.
+// Layout (codes: two per byte, the first weight in the high nibble; absmax:
+// float32 per block of B weights) as documented in include/decodegemv.h.
+//
+// The page's kernel dequantises every weight through a float table in shared
+// memory.  On gfx950 the per-weight work is what would bound this kernel, so
+// here every code BYTE -- two weights -- is one lookup:
+//   * each workgroup builds in LDS a 256-entry table indexed by the code
+//     byte; an entry holds the two weights' table values as binary16 pairs,
+//     each value scaled by a power of two 2^st (largest |table| near 2^14)
+//     and split into a high part (rounded to binary16) and a low part (the
+//     rest, rounded to binary16): 22 significant bits, within about 2^-23 of
+//     the float value;
+//   * each lane converts its 32 activations of a unit to binary16 once,
+//     scaled by a power of two 2^sx that puts their largest near 2^14: a
+//     bfloat16 value (8 significant bits) converts exactly unless it lies
+//     some 2^28 below that largest;
+//   * two v_dot2_f32_f16 multiply the pair with the two activations (one
+//     dword of binary16 x) and add into fp32 -- the products are exact -- and
+//     the unit's sum is scaled back by 2^-st, 2^-sx and its absmax: the float
+//     GEMV up to fp32 rounding;
+//   * the table is replicated TC times (copy = lane % TC) so that the 8-byte
+//     lookups of 16 lanes fall in distinct banks.
+// The K of a row is split over the S = K/2048 waves of a workgroup: wave w
+// owns weights 2048w .. 2048w + 2047 of every row the workgroup takes, a lane
+// 32 of them -- 16 code bytes, one 16-byte load (the wave's 64 lanes read 1 KiB
+// of consecutive bytes), and its block's absmax -- so a lane holds only 32
+// activations and the kernel keeps many waves per CU.  Each wave streams its
+// slice of successive rows with AHEAD rows of loads in flight, straight to
+// registers: with nothing but plain loads in flight the compiler's own vmcnt
+// waits are exact (LDS-DMA copies in flight would make it wait for all of
+// them before every table lookup).  The waves' per-row partials meet in LDS
+// every 64 rows and are added in unit order, so results do not depend on the
+// launch shape.
+#include "dg_internal.h"
+#include "q4_common.h"
+
+namespace dg {
+namespace {
+
+using namespace q4;
+
+constexpr int kUnitWeights = 2048;    // weights per unit: 64 lanes x 32
+constexpr int kUnitCodes = 1024;      // code bytes per unit
+constexpr int kMaxUnits = 16;         // K <= 32768: one wave per unit, 1024 threads
+
+__device__ __forceinline__ uint32_t f32_to_f16_bits(float f) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);   // round to nearest even
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+
+// 2^e as a float, e clamped to the normal range.
+__device__ __forceinline__ float pow2f(int e) {
+    e = e < -126 ? -126 : (e > 127 ? 127 : e);
+    return __builtin_bit_cast(float, (uint32_t)(e + 127) << 23);
+}
+
+// The power of two that brings a biased binary32/bfloat16 exponent field to 14.
+__device__ __forceinline__ int scale_exp(uint32_t biased) { return 14 - ((int)biased - 127); }
+
+
+// Loads a lane's 16 code bytes of one unit of row r and their block's absmax
+// (for r >= N, the same fixed bytes in every lane: an instruction that moves
+// no new data, so that no branch ever surrounds a load and the compiler's
+// in-order vmcnt accounting stays exact).
+__device__ __forceinline__ void load_unit(const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
+                                          int r, int N, int K, int nab, bool lane_valid, int code_off, int ab_off,
+                                          u32x4& c, float& a) {
+    const bool live = lane_valid && r < N;
+    c = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(live ? codes + (size_t)r * (K >> 1) + code_off : codes));
+    a = __builtin_nontemporal_load(live ? absmax + (size_t)r * nab + ab_off : absmax);
+}
+
+// A lane's 16 code bytes against its 32 activations: NA independent partial
+// sums (byte i to sum i % NA), added in a fixed order.
+template <int TC, int NA>
+__device__ __forceinline__ float unit_dot(const u32x4& c, const uint32_t (&xr)[16], const uint2* tab_lane) {
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    float p[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) p[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t v = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+        const uint2 e = tab_lane[v * TC];
+        p[i % NA] = dot2_f16(e.x, xr[i], p[i % NA]);
+        p[i % NA] = dot2_f16(e.y, xr[i], p[i % NA]);
+    }
+    float s = p[0];
+#pragma unroll
+    for (int j = 1; j < NA; ++j) s += p[j];
+    return s;
+}
+
+// One workgroup of S waves takes rows b, b + grid, b + 2*grid, ...; wave w
+// owns unit w (weights 2048w .. 2048w + 2047) of every one of them, so a lane
+// keeps only its 32 activations of that unit.  Each wave reduces a row's unit
+// over its lanes (DPP) and lane k keeps the k-th row of a batch of 64; after
+// the batch the waves' partials meet in LDS and wave 0 adds them in unit
+// order and stores the 64 results.
+template <int TC, int NA, int AHEAD>
+__global__ void __launch_bounds__(1024)
+k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const float* __restrict__ table,
+      const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K, int B) {
+    static_assert(TC == 8 || TC == 16, "table copies");
+    static_assert(AHEAD >= 2 && AHEAD <= 8 && (kWave % AHEAD) == 0, "rows in flight");
+    __shared__ uint2 ptab[256 * TC];
+    __shared__ float red[16][kWave];
+    __shared__ float tl[16];
+    const int lane = lane_id();
+    const int wave = wave_in_block();           // = the unit
+    const int S = blockDim.x / kWave;
+    const int grid = gridDim.x;
+    const int nab = K / B;
+    const int k0 = wave * kUnitWeights + lane * 32;
+    const bool lane_valid = k0 < K;
+    const int code_off = wave * kUnitCodes + lane * 16;
+    const int ab_off = wave * (kUnitWeights / B) + (lane * 32) / B;
+
+    // the activations are requested first, then the first AHEAD rows of
+    // weights; building the pair table and converting x wait only for the
+    // older loads, so the weight stream starts at once
+    u32x4 xraw[4];
+    {
+        const u32x4* src = reinterpret_cast<const u32x4*>(x + (lane_valid ? k0 : 0));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xraw[q] = src[q];
+    }
+    const int b = blockIdx.x;
+    const int nrows = b < N ? (N - 1 - b) / grid + 1 : 0;   // rows of this workgroup (uniform)
+    // rows in flight: q[j] holds row k + j of the workgroup's sequence
+    u32x4 qc[AHEAD];
+    float qa[AHEAD];
+#pragma unroll
+    for (int j = 0; j < AHEAD; ++j)
+        load_unit(codes, absmax, b + j * grid, N, K, nab, lane_valid, code_off, ab_off, qc[j], qa[j]);
+
+    // the byte-pair table: entry v = (weights 2j, 2j+1 with codes v >> 4 and v & 15).
+    // The 16 values are read with uniform (scalar) loads, which do not count
+    // in vmcnt, and passed on through LDS: a per-thread indexed read of the
+    // table here would be a vector load behind the weight loads, and waiting
+    // for it would wait for them too.
+    uint32_t tmax = 0;
+    float tv = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float v = table[j];
+        tmax = max(tmax, __builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu);
+        tv = threadIdx.x == (unsigned)j ? v : tv;
+    }
+    if (threadIdx.x < 16) tl[threadIdx.x] = tv;
+    lds_barrier();
+    const int st = scale_exp(tmax >> 23);
+    {
+        const float ts = pow2f(st);
+        for (int i = threadIdx.x; i < 256 * TC; i += blockDim.x) {
+            const int v = i / TC;
+            const float a = tl[v >> 4] * ts, b2 = tl[v & 15] * ts;
+            const uint32_t ha = f32_to_f16_bits(a), hb = f32_to_f16_bits(b2);
+            const uint32_t la = f32_to_f16_bits(a - f16_bits_to_f32(ha));
+            const uint32_t lb = f32_to_f16_bits(b2 - f16_bits_to_f32(hb));
+            ptab[i] = uint2{ha | (hb << 16), la | (lb << 16)};   // the first weight in the low half, as x[2j]
+        }
+    }
+    // the lane's activations as binary16 scaled by 2^sx; back = 2^-st * 2^-sx
+    uint32_t xr[16];
+    float back;
+    {
+        uint32_t raw[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            raw[4 * q + 0] = lane_valid ? xraw[q].x : 0u;   // lanes past the row: 0 times any table value
+            raw[4 * q + 1] = lane_valid ? xraw[q].y : 0u;
+            raw[4 * q + 2] = lane_valid ? xraw[q].z : 0u;
+            raw[4 * q + 3] = lane_valid ? xraw[q].w : 0u;
+        }
+        uint32_t emax = 0;   // largest bfloat16 exponent field of the 32 values
+#pragma unroll
+        for (int i = 0; i < 16; ++i) emax = max(emax, max((raw[i] >> 7) & 0xFFu, (raw[i] >> 23) & 0xFFu));
+        const int sx = scale_exp(emax);
+        const float xs = pow2f(sx);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float lo = __builtin_bit_cast(float, raw[i] << 16) * xs;
+            const float hi = __builtin_bit_cast(float, raw[i] & 0xFFFF0000u) * xs;
+            xr[i] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+        }
+        back = pow2f(-st) * pow2f(-sx);
+    }
+    lds_barrier();   // the pair table is complete
+
+    const uint2* const tab_lane = ptab + (lane % TC);
+    float part = 0.0f;
+    for (int k0r = 0; k0r < nrows; k0r += AHEAD) {
+#pragma unroll
+        for (int j = 0; j < AHEAD; ++j) {
+            const int k = k0r + j;
+            const float s = unit_dot<TC, NA>(qc[j], xr, tab_lane);
+            const float a = lane_valid ? qa[j] : 0.0f;
+            load_unit(codes, absmax, b + (k + AHEAD) * grid, N, K, nab, lane_valid, code_off, ab_off, qc[j], qa[j]);
+            const float r = wave_sum_f32(s * back * a);   // this unit of row k, wave-uniform
+            if (lane == (k & (kWave - 1))) part = r;
+            if ((k & (kWave - 1)) == kWave - 1 || k == nrows - 1) {   // a batch of 64 rows is complete
+                const int kb = k & ~(kWave - 1);
+                if (S == 1) {
+                    if (lane <= (k & (kWave - 1))) y[b + (int64_t)(kb + lane) * grid] = part;
+                } else {
+                    red[wave][lane] = part;
+                    lds_barrier();
+                    if (wave == 0 && lane <= (k & (kWave - 1))) {
+                        float t = red[0][lane];
+                        for (int w = 1; w < S; ++w) t += red[w][lane];
+                        y[b + (int64_t)(kb + lane) * grid] = t;
+                    }
+                    lds_barrier();
+                }
+            }
+            if (k == nrows - 1) break;
+        }
+    }
+}
+
+// One thread per block of B weights: absmax, then the nearest table level of
+// each w / absmax (binary32, correctly rounded division), a tie going to the
+// lower level; two codes per byte, the first weight in the high nibble.
+__global__ void k_quantize_nf4(const float* __restrict__ w, uint8_t* __restrict__ codes, float* __restrict__ absmax,
+                               const float* __restrict__ table, int64_t nblocks, int B) {
+    const int64_t blk = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blk >= nblocks) return;
+    float mid[15];
+#pragma unroll
+    for (int j = 0; j < 15; ++j) mid[j] = bind_f32(table[j] + table[j + 1]) * 0.5f;
+    const float* xb = w + blk * B;
+    float amax = 0.0f;
+    for (int i = 0; i < B; ++i) amax = fmaxf(amax, fabsf(xb[i]));
+    absmax[blk] = amax;
+    uint8_t* cb = codes + blk * (B / 2);
+    for (int i = 0; i < B; i += 2) {
+        int c[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float r = amax != 0.0f ? xb[i + h] / amax : 0.0f;
+            int q = 0;
+#pragma unroll
+            for (int j = 0; j < 15; ++j) q += r > mid[j] ? 1 : 0;
+            c[h] = q;
+        }
+        cb[i / 2] = (uint8_t)((c[0] << 4) | c[1]);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemv_nf4(const void* codes, const float* absmax, const float* table, const void* x, float* y,
+                           int N, int K, int B, const dg_launch* cfg, hipStream_t s) {
+    if (cfg && cfg->variant && cfg->variant != DG_VARIANT_NF4_UNITS) return hipErrorInvalidValue;
+    const int S = (K + kUnitWeights - 1) / kUnitWeights;   // waves per workgroup: one per unit
+    if (S > kMaxUnits) return hipErrorInvalidValue;
+    if (cfg && cfg->block && cfg->block != S * kWave) return hipErrorInvalidValue;   // fixed by K
+    // unroll: table copies (8 or 16) + 100 * independent partial sums (1, 2)
+    //         + 1000 * rows in flight per wave (4 or 8)
+    const int u = cfg ? cfg->unroll : 0;
+    const int copies = u % 100 ? u % 100 : 8;
+    const int na = (u / 100) % 10 ? (u / 100) % 10 : 1;
+    const int ahead = u / 1000 ? u / 1000 : 4;
+    if ((copies != 8 && copies != 16) || (na != 1 && na != 2) || (ahead != 4 && ahead != 8))
+        return hipErrorInvalidValue;
+    int grid = cfg && cfg->grid ? cfg->grid : 0;
+    if (!grid) {
+        // about 4096 waves in multiples of 256 workgroups, between 256 and
+        // 1024 workgroups (the fastest of grids 256..2048 measured on MI355X
+        // at K = 4096, 8192, 14336 and 28672); never more workgroups than rows
+        int g = (4096 / S) & ~255;
+        g = g < 256 ? 256 : (g > 1024 ? 1024 : g);
+        grid = N < g ? N : g;
+    }
+    const uint8_t* c8 = (const uint8_t*)codes;
+    const uint16_t* x16 = (const uint16_t*)x;
+#define DG_NF4(TT, AA, HH)                                                                                    \
+    if (copies == TT && na == AA && ahead == HH) {                                                            \
+        hipLaunchKernelGGL((k_nf4<TT, AA, HH>), dim3(grid), dim3(S * kWave), 0, s, c8, absmax, table, x16, y, N, \
+                           K, B);                                                                             \
+        return hipGetLastError();                                                                             \
+    }
+    DG_NF4(16, 1, 4) DG_NF4(16, 2, 4) DG_NF4(8, 1, 4) DG_NF4(8, 2, 4)
+    DG_NF4(16, 1, 8) DG_NF4(16, 2, 8) DG_NF4(8, 1, 8) DG_NF4(8, 2, 8)
+#undef DG_NF4
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_quantize_nf4(const float* w, void* codes, float* absmax, const float* table, int64_t N,
+                               int64_t K, int B, hipStream_t s) {
+    const int64_t nblocks = N * (K / B);
+    if (nblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_quantize_nf4, dim3((unsigned)((nblocks + 255) / 256)), dim3(256), 0, s, w,
+                       (uint8_t*)codes, absmax, table, nblocks, B);
+    return hipGetLastError();
+}
+
+}  // namespace dg

@@ -178,22 +178,26 @@ __host__ __device__ constexpr int column_lds_bytes(int K) {
 }
 
 // The M = 1 kernels give every workgroup one copy of the activation column
-// in LDS instead of one per wave: the 1 KiB copies are split over the
-// workgroup's waves (wave w issues copies w, w + wpb, ...) and are issued
-// before any weight copy, so a wave's own share has landed once at most its
-// weight copies are outstanding; a barrier then makes every share visible.
-// Every copy has all 64 lanes active (lanes past the column re-read its first
-// slot into the unused tail of the last KiB).  dst is formed from the
-// kernel's __shared__ array.
-__device__ __forceinline__ void copy_column_to_lds(const uint8_t* __restrict__ col, int K, uint8_t* dst, int wave,
-                                                   int wpb, int lane) {
-    const int slots = (K / 32) * kQ81Bytes / 16;
+// (in general, of any run of 16-byte slots) in LDS instead of one per wave:
+// the 1 KiB copies are split over the workgroup's waves (wave w issues copies
+// w, w + wpb, ...) and are issued before any weight copy, so a wave's own
+// share has landed once at most its weight copies are outstanding; a barrier
+// then makes every share visible.  Every copy has all 64 lanes active (lanes
+// past the end re-read the first slot into the unused tail of the last KiB).
+// dst is formed from the kernel's __shared__ array.
+__device__ __forceinline__ void copy_slots_to_lds(const uint8_t* __restrict__ src, int slots, uint8_t* dst, int wave,
+                                                  int wpb, int lane) {
     const int copies = (slots + kWave - 1) / kWave;
     for (int j = wave; j < copies; j += wpb) {
         const int c = j * kWave + lane;
-        __builtin_amdgcn_global_load_lds(col + (size_t)(c < slots ? c : 0) * 16, (lds_void_t*)(dst + j * 1024), 16,
+        __builtin_amdgcn_global_load_lds(src + (size_t)(c < slots ? c : 0) * 16, (lds_void_t*)(dst + j * 1024), 16,
                                          0, 0);
     }
+}
+
+__device__ __forceinline__ void copy_column_to_lds(const uint8_t* __restrict__ col, int K, uint8_t* dst, int wave,
+                                                   int wpb, int lane) {
+    copy_slots_to_lds(col, (K / 32) * kQ81Bytes / 16, dst, wave, wpb, lane);
 }
 
 __device__ __forceinline__ void read_pair_lds(const uint8_t* buf, int p, uint32_t w[9]) {

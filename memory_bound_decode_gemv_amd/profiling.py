@@ -43,6 +43,10 @@ KERNELS = {
         r"k_gemv_wide<false", "fp16 GEMV, N = K = 4096",
         2 * 4096 * 4096 + 2 * 4096 + 2 * 4096,
         ["gemv_dense.hip", "dg_device.h"]),
+    "gemv_nf4_28672x8192_b64": (
+        r"k_nf4<", "NF4 x bf16, M = 1, N = 28672, K = 8192, block 64",
+        28672 * 8192 // 2 + 4 * 28672 * (8192 // 64) + 2 * 8192 + 64 + 4 * 28672,
+        ["gemv_nf4.hip", "dg_device.h", "dg_internal.h"]),
     "stream_read_1GiB": (
         r"k_stream_read_wave<", "streaming read of 1 GiB", GIB,
         ["stream_read.hip", "dg_device.h"]),

@@ -149,6 +149,33 @@ def test_fused_tail_rejects_before_launch(lib):
     assert lib.dg_gemv_bf16_argmax(A16, A16, None, A16, 100, 64, 64, None, need, None) == 4
 
 
+def test_nf4_rejects_before_launch(lib):
+    g = lib.dg_gemv_nf4
+    assert g(A16, A16, A16, A16, A16, 4, 300, 64, None) == 3           # K % 256
+    assert g(A16, A16, A16, A16, A16, 4, 33024, 64, None) == 3         # K > 32768
+    assert g(A16, A16, A16, A16, A16, 4, 512, 48, None) == 3           # block size
+    assert g(A16, A16, A16, A16, A16, 4, 768, 256, None) == 3          # K % (4 B)
+    assert g(A16, A16, A16, A16, A16, -1, 512, 64, None) == 3
+    assert g(None, A16, A16, A16, A16, 4, 512, 64, None) == 1
+    assert g(A16, A16, None, A16, A16, 4, 512, 64, None) == 1
+    assert g(A16, A16, A16, A16, None, 4, 512, 64, None) == 1
+    assert g(A16, A16, P(0x1004), A16, A16, 4, 512, 64, None) == 2    # table 16-byte aligned
+    assert g(A16, P(0x1008), A16, A16, A16, 4, 512, 64, None) == 2    # absmax 16-byte aligned
+    assert g(A16, A16, A16, A2, A16, 4, 512, 64, None) == 2           # x
+    assert g(A16, A16, A16, A16, P(0x1002), 4, 512, 64, None) == 2    # y
+    assert g(None, None, None, None, None, 0, 512, 64, None) == 0     # N = 0
+    import memory_bound_decode_gemv_amd as m
+    for cfg in (m.dg_launch(5, 0, 0, 0), m.dg_launch(31, 0, 128, 0), m.dg_launch(31, 0, 0, 5),
+                m.dg_launch(31, 0, 0, 122), m.dg_launch(31, 0, 0, 308), m.dg_launch(31, 0, 0, 6008)):
+        assert lib.dg_gemv_nf4_ex(A16, A16, A16, A16, A16, 4, 512, 64, ctypes.byref(cfg), None) == 6
+    q = lib.dg_quantize_nf4
+    assert q(A16, A16, A16, A16, 2, 100, 64, None) == 3              # K % B
+    assert q(A16, A16, A16, A16, 2, 128, 16, None) == 3              # block size
+    assert q(A2, A16, A16, A16, 2, 128, 64, None) == 2               # w 16-byte aligned
+    assert q(A16, A16, A16, None, 2, 128, 64, None) == 1
+    assert q(None, None, None, None, 0, 128, 64, None) == 0
+
+
 def test_quantisers_reject_before_launch(lib):
     assert lib.dg_quantize_q8_1(A16, A16, 2, 48, None) == 3
     assert lib.dg_quantize_q4_0(A16, A16, 2, 48, None) == 3

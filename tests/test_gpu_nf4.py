@@ -1,0 +1,161 @@
+"""Parity of dg_gemv_nf4 and dg_quantize_nf4 with the oracle (GPU).
+
+Operands are drawn by the seeded generators and quantised on the CPU by the
+oracle's NF4 quantiser, with the workload's NormalFloat table; the GPU
+quantiser is checked byte for byte against the oracle's separately.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import synth
+from tests._parity import assert_close
+
+pytestmark = pytest.mark.gpu
+
+# fp32 products and sums; table values held to 22 bits (binary16 hi + lo, scaled)
+TOL = 2e-4
+
+
+@functools.lru_cache(maxsize=16)
+def _operands(orc, cfg, N, K, B):
+    w = synth.normal_f32((cfg, synth.KIND_W, 0, 0), (N, K))
+    codes, absmax = orc.quantize_nf4(w, synth.nf4_table(), B)
+    xb = synth.normal_bf16_bits((cfg, synth.KIND_X, 0, 0), (K,), 1.0)
+    return codes, absmax, xb
+
+
+def _gpu(dg, dev, codes, absmax, table, xb, N, K, B, launch=None):
+    import torch
+    c = torch.from_numpy(np.ascontiguousarray(codes).reshape(-1)).to(dev)
+    a = torch.from_numpy(np.ascontiguousarray(absmax, dtype=np.float32).reshape(-1)).to(dev)
+    t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.float32)).to(dev)
+    x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.full((max(N, 1),), float("nan"), dtype=torch.float32, device=dev)
+    dg.dg_gemv_nf4(c, a, t, x, y, N=N, K=K, B=B, launch=launch)
+    torch.cuda.synchronize()
+    return y[:N].cpu().numpy().astype(np.float64)
+
+
+SHAPES = [(1, 256, 64), (7, 2048, 32), (33, 4352, 64), (70, 8192, 64), (19, 14336, 128), (5, 16384, 256),
+          (130, 1024, 256), (300, 2560, 64), (64, 6144, 32), (9, 28672, 64), (3, 32768, 128)]
+
+
+@pytest.mark.parametrize("N,K,B", SHAPES)
+def test_nf4_matches_oracle(dg, dev, orc, N, K, B):
+    codes, absmax, xb = _operands(orc, 600 + K % 97, N, K, B)
+    t = synth.nf4_table()
+    got = _gpu(dg, dev, codes, absmax, t, xb, N, K, B)
+    assert_close(got, orc.gemv_nf4(codes, absmax, t, xb, N, K, B), TOL, f"{N}x{K} B={B}")
+
+
+LAUNCHES = [dict(variant=31), dict(variant=31, unroll=8), dict(variant=31, unroll=16), dict(variant=31, unroll=108),
+            dict(variant=31, unroll=216), dict(variant=31, unroll=8216), dict(variant=31, unroll=4108),
+            dict(variant=31, unroll=8008), dict(variant=31, grid=3),
+            dict(variant=31, grid=2, unroll=16), dict(variant=31, grid=5, unroll=8208), dict(variant=31, grid=1),
+            dict(variant=31, grid=4000)]
+
+
+@pytest.mark.parametrize("launch", LAUNCHES, ids=[str(v) for v in LAUNCHES])
+@pytest.mark.parametrize("N,K,B", [(301, 8192, 64), (1000, 512, 32), (64, 4352, 64), (40, 6144, 128)])
+def test_nf4_launch_variants(dg, dev, orc, launch, N, K, B):
+    """Table copies, partial sums, and grids from one workgroup (every row in
+    one workgroup: batches of 64 rows, then the rest) to more workgroups than
+    rows."""
+    codes, absmax, xb = _operands(orc, 620, N, K, B)
+    t = synth.nf4_table()
+    got = _gpu(dg, dev, codes, absmax, t, xb, N, K, B, launch=launch)
+    assert_close(got, orc.gemv_nf4(codes, absmax, t, xb, N, K, B), TOL, f"{launch}")
+
+
+def test_nf4_any_table(dg, dev, orc):
+    """The kernel takes any finite table: unordered, with repeats, wide range."""
+    N, K, B = 90, 4096, 64
+    g = np.random.default_rng(77)
+    codes = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    absmax = np.abs(g.standard_normal((N, K // B))).astype(np.float32) * 3
+    xb = synth.normal_bf16_bits((640, synth.KIND_X, 0, 0), (K,), 1.0)
+    for t in (g.standard_normal(16).astype(np.float32) * 100, np.repeat(np.float32([0.5, -2.0]), 8),
+              np.float32([1e-3 * (j - 8) for j in range(16)])):
+        got = _gpu(dg, dev, codes, absmax, t, xb, N, K, B)
+        assert_close(got, orc.gemv_nf4(codes, absmax, t, xb, N, K, B), TOL, f"table {t[:3]}")
+
+
+def test_nf4_70b_mlp_shape_sampled_rows(dg, dev, orc):
+    """28672 x 8192 with the default launch (the shape of the page's
+    benchmark); sampled rows against the oracle."""
+    import torch
+    N, K, B = 28672, 8192, 64
+    w = synth.gpu_normal((7, synth.KIND_W, 0, 0), (N, K), 1.0, torch.float32)
+    t = torch.from_numpy(synth.nf4_table()).to(dev)
+    codes = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+    absmax = torch.empty(N * K // B, dtype=torch.float32, device=dev)
+    dg.dg_quantize_nf4(w, codes, absmax, t, N, K, B)
+    xb = synth.normal_bf16_bits((7, synth.KIND_X, 0, 0), (K,), 1.0)
+    x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    y = torch.empty(N, dtype=torch.float32, device=dev)
+    dg.dg_gemv_nf4(codes, absmax, t, x, y, N=N, K=K, B=B)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([np.arange(0, N, 97), [N - 1]]))
+    c = codes.view(N, K // 2)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    a = absmax.view(N, K // B)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+    ref = orc.gemv_nf4(c, a, synth.nf4_table(), xb, len(rows), K, B)
+    assert_close(y.cpu().numpy()[rows], ref, TOL, "28672x8192 sampled")
+
+
+def test_nf4_rejects_a_block_size_other_than_one_wave_per_unit(dg, dev, orc):
+    codes, absmax, xb = _operands(orc, 630, 8, 8192, 64)
+    with pytest.raises(dg.DGError):
+        _gpu(dg, dev, codes, absmax, synth.nf4_table(), xb, 8, 8192, 64, launch=dict(variant=31, block=128))
+
+
+def test_nf4_empty_and_zero_k(dg, dev):
+    import torch
+    t = torch.zeros(16, dtype=torch.float32, device=dev)
+    c = torch.zeros(16, dtype=torch.uint8, device=dev)
+    a = torch.zeros(16, dtype=torch.float32, device=dev)
+    x = torch.zeros(8, dtype=torch.bfloat16, device=dev)
+    y = torch.full((5,), 7.0, dtype=torch.float32, device=dev)
+    dg.dg_gemv_nf4(c, a, t, x, y, N=0, K=256, B=64)        # nothing launched
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    dg.dg_gemv_nf4(c, a, t, x, y, N=5, K=0, B=64)          # empty sums
+    torch.cuda.synchronize()
+    assert torch.all(y == 0.0)
+
+
+def _gpu_quantize(dg, dev, w, table, B):
+    import torch
+    N, K = w.shape
+    wt = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(dev)
+    t = torch.from_numpy(np.ascontiguousarray(table, dtype=np.float32)).to(dev)
+    codes = torch.full((N * K // 2,), 0xA5, dtype=torch.uint8, device=dev)
+    absmax = torch.full((N * (K // B),), float("nan"), dtype=torch.float32, device=dev)
+    dg.dg_quantize_nf4(wt, codes, absmax, t, N, K, B)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy().reshape(N, K // 2), absmax.cpu().numpy().reshape(N, K // B)
+
+
+@pytest.mark.parametrize("N,K,B", [(1, 32, 32), (3, 256, 64), (17, 4096, 128), (4, 14336, 256), (9, 2048, 64)])
+def test_nf4_quantiser_bytes_match_oracle(dg, dev, orc, N, K, B):
+    w = synth.normal_f32((650, synth.KIND_W, N, K), (N, K))
+    for table in (synth.nf4_table(), np.float32([(j - 7) / 8 for j in range(16)])):
+        c, a = _gpu_quantize(dg, dev, w, table, B)
+        rc, ra = orc.quantize_nf4(w, table, B)
+        assert np.array_equal(a, ra) and np.array_equal(c, rc)
+
+
+def test_nf4_quantiser_ties_zeros_and_extremes(dg, dev, orc):
+    """Values on exact midpoints of a dyadic table, all-zero blocks, the
+    extreme levels and negative zero."""
+    td = np.float32([(j - 7) / 8 for j in range(16)])
+    mids = (td[:-1] + td[1:]) / 2
+    K, B = 256, 32
+    rows = [np.tile(np.concatenate([[1.0], mids, mids[:16 - 1], [-1.0]]).astype(np.float32), K // 32)[:K],
+            np.zeros(K, np.float32), np.full(K, -0.0, np.float32),
+            np.tile(np.float32([-3.0, 3.0] + [0.375] * 30), K // 32)]
+    w = np.stack(rows).astype(np.float32)
+    c, a = _gpu_quantize(dg, dev, w, td, B)
+    rc, ra = orc.quantize_nf4(w, td, B)
+    assert np.array_equal(a, ra) and np.array_equal(c, rc)
