@@ -341,6 +341,9 @@ typedef struct {
                       *_MFMA: RT*10000 + KS*100 + DEPTH*10 + CB/8 (row
                       tiles and K parts per workgroup, pipeline depth,
                       blocks per chunk);
+                      *_MFMA_RES: RT*10000 + KS*100 + P*10 (row tiles and
+                      K parts per workgroup, 8-block chunks in flight per
+                      wave);
                       NF4: code-pair table copies (8 or 16) + 100 * partial
                       sums per lane (1, 2) + 1000 * rows in flight (4, 8)    */
 } dg_launch;
@@ -358,10 +361,14 @@ enum {
     DG_VARIANT_Q4_MFMA = 14,        /* int8 matrix cores, 16 rows x 16 columns per instruction   */
     DG_VARIANT_Q4_UNITS = 15,       /* rows copied to LDS in units of 64 block pairs, every
                                        column from one read (M * ceil(K/4096) <= 8, K <= 16384) */
+    DG_VARIANT_Q4_MFMA_RES = 16,    /* int8 matrix cores with every activation column resident in
+                                       LDS for the whole K; weights through registers (the
+                                       columns must fit one workgroup's LDS)                   */
     /* Q8_0 */
     DG_VARIANT_Q8_LDSROW = 21,      /* M = 1: weight rows copied to LDS (K <= 16384)             */
     DG_VARIANT_Q8_MFMA = 22,        /* int8 matrix cores                                          */
     DG_VARIANT_Q8_UNITS = 23,       /* as DG_VARIANT_Q4_UNITS, Q8_0 weights                        */
+    DG_VARIANT_Q8_MFMA_RES = 24,    /* as DG_VARIANT_Q4_MFMA_RES, Q8_0 weights                     */
     /* NF4 */
     DG_VARIANT_NF4_UNITS = 31       /* code bytes looked up in a byte-pair table in LDS; one
                                        wave per 2048 weights of a row (block = 64*ceil(K/2048)) */

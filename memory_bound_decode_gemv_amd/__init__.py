@@ -45,9 +45,11 @@ DG_VARIANT_Q4_LDS = 12
 DG_VARIANT_Q4_LDSROW = 13
 DG_VARIANT_Q4_MFMA = 14
 DG_VARIANT_Q4_UNITS = 15
+DG_VARIANT_Q4_MFMA_RES = 16
 DG_VARIANT_Q8_LDSROW = 21
 DG_VARIANT_Q8_MFMA = 22
 DG_VARIANT_Q8_UNITS = 23
+DG_VARIANT_Q8_MFMA_RES = 24
 
 # Every symbol include/decodegemv.h declares.
 EXPORTED = (

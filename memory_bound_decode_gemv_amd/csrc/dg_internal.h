@@ -81,6 +81,16 @@ hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int
 hipError_t launch_q8_mfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
                           hipStream_t s);
 
+// The matrix-core kernel with the activation columns resident in LDS, for
+// both formats (unroll = RT*10000 + KS*100 + P*10: row tiles and K parts per
+// workgroup, chunks in flight per wave; 0 = default).  hipErrorInvalidValue
+// when the configuration is not built, K/32 is not a multiple of 8*KS, or
+// the workgroup's LDS would not fit.
+hipError_t launch_q4_res(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
+                         hipStream_t s);
+hipError_t launch_q8_res(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
+                         hipStream_t s);
+
 hipError_t launch_quantize_q8_0(const float* w, void* Wq, int64_t N, int64_t K, hipStream_t s);
 
 // NF4 x bfloat16, one column (K <= 32768; B in {32, 64, 128, 256}; K % (4B) == 0),

@@ -271,6 +271,10 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
         } else if (M == 2 || N <= 1024) {
             variant = DG_VARIANT_Q4_LDS;
             lds_rows = N > 2048 ? 2 : 1;
+        } else if ((N >= 8192 && K <= 4096 && M >= 8) || (M <= 4 && K > 8192 && (K / 32) % 64 == 0)) {
+            // the activation columns resident in LDS: many row tiles at eight
+            // columns and more, and up to four columns of long rows
+            variant = DG_VARIANT_Q4_MFMA_RES;
         } else {
             variant = DG_VARIANT_Q4_MFMA;
         }
@@ -298,6 +302,10 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
     if (variant == DG_VARIANT_Q4_MFMA) {
         if (cfg && cfg->block) return hipErrorInvalidValue;   // the configuration fixes the workgroup size
         return launch_q4_mfma(M, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, K, cfg ? cfg->grid : 0, s);
+    }
+    if (variant == DG_VARIANT_Q4_MFMA_RES) {
+        if (cfg && cfg->block) return hipErrorInvalidValue;   // the configuration fixes the workgroup size
+        return launch_q4_res(M, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, K, cfg ? cfg->grid : 0, s);
     }
     if (variant == DG_VARIANT_Q4_LDS) {
         if (cfg && cfg->block && cfg->block != kLdsBlock) return hipErrorInvalidValue;

@@ -153,8 +153,11 @@ hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int
         // 1..24: up to eight columns stream rows through LDS in 64-pair units
         // while M * ceil(K / 4096) <= 8 (at most four columns for matrices of
         // 1024 rows or fewer, where eight would outrun twelve on the matrix
-        // cores); the rest take the matrix cores.
-        variant = S <= 4 && M * S <= 8 && (N > 1024 || M <= 4) ? DG_VARIANT_Q8_UNITS : DG_VARIANT_Q8_MFMA;
+        // cores); the rest take the matrix cores, with the columns resident
+        // in LDS from twelve columns on for matrices of many row tiles.
+        variant = S <= 4 && M * S <= 8 && (N > 1024 || M <= 4) ? DG_VARIANT_Q8_UNITS
+                  : (N >= 8192 && K <= 4096 && M >= 12)      ? DG_VARIANT_Q8_MFMA_RES
+                                                             : DG_VARIANT_Q8_MFMA;
     }
     if (variant == DG_VARIANT_Q8_UNITS) {
         if (S > 4 || M * S > 8) return hipErrorInvalidValue;
@@ -171,6 +174,10 @@ hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int
     if (variant == DG_VARIANT_Q8_MFMA) {
         if (cfg && cfg->block) return hipErrorInvalidValue;   // the configuration fixes the workgroup size
         return launch_q8_mfma(M, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, K, cfg ? cfg->grid : 0, s);
+    }
+    if (variant == DG_VARIANT_Q8_MFMA_RES) {
+        if (cfg && cfg->block) return hipErrorInvalidValue;
+        return launch_q8_res(M, cfg ? cfg->unroll : 0, Wq, Xq, Y, N, K, cfg ? cfg->grid : 0, s);
     }
     return hipErrorInvalidValue;
 }

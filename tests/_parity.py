@@ -26,3 +26,45 @@ def assert_close(got, ref, tol, what=""):
         f"{what}: max floored relative error {err.max():.3e} > {tol} at {worst}: "
         f"got {np.asarray(got).reshape(-1)[worst]!r} ref {np.asarray(ref).reshape(-1)[worst]!r}")
     return float(err.max()) if err.size else 0.0
+
+
+# Configurations of the resident-activation matrix-core kernel the library
+# builds: (RT row tiles, KS parts of K, P chunks in flight); launch override
+# unroll = RT*10000 + KS*100 + P*10.  A configuration runs a shape when K/32
+# is a multiple of 8*KS and the workgroup's LDS fits (160 KiB on gfx950):
+# the M activation columns (36-byte blocks, odd number of 16-byte slots per
+# column), the fp32 d8 table, one transpose buffer per wave and the partial
+# sums of the upper K parts.
+RES_CFGS = [(1, 16, 2), (2, 8, 2), (4, 4, 2), (1, 8, 2), (2, 4, 2), (4, 2, 2), (8, 1, 2), (1, 4, 2), (2, 2, 2),
+            (4, 1, 2), (1, 8, 3), (2, 4, 3), (1, 4, 3)]
+LDS_PER_WORKGROUP = 160 * 1024
+
+
+def res_unroll(rt, ks, p):
+    return rt * 10000 + ks * 100 + p * 10
+
+
+def res_runs(block_bytes, rt, ks, M, K):
+    nblk = K // 32
+    if nblk % (8 * ks) or M < 1 or M > 32:
+        return False
+    nt = 1 if M <= 16 else 2
+    if block_bytes == 34 and nt == 2 and rt * ks == 16:
+        return False   # not built: it would spill
+    g = 8 * block_bytes // 16
+    buf = -(-16 * g // 64) * 1024
+    cstr = ((nblk * 36 // 16) | 1) * 16
+    lds = M * cstr + nblk * 16 * nt * 4 + rt * ks * buf + rt * (ks - 1) * nt * 1024
+    return lds <= LDS_PER_WORKGROUP
+
+
+def res_default(block_bytes, N, M, K):
+    """The configuration the library picks when no override is given: four row
+    tiles per workgroup for more than 512 tiles (K in two parts for Q4_0, whole
+    for Q8_0), else one tile with K in eight parts; one tile with K in four
+    parts when that does not fit."""
+    tiles = (N + 15) // 16
+    cfg = ((4, 1 if block_bytes == 34 else 2, 2) if tiles > 512 else (1, 8, 2))
+    if not res_runs(block_bytes, cfg[0], cfg[1], M, K):
+        cfg = (1, 4, 2)
+    return cfg

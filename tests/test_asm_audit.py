@@ -88,6 +88,18 @@ def test_q4_kernels_use_dot4_lds_dma_and_matrix_cores(asm):
     assert "flat_load" not in un
 
 
+def test_resident_matrix_core_kernel(asm):
+    """Weights reach the matrix cores through registers and a per-wave LDS
+    transpose (16-byte non-temporal loads, ds_write_b128), the activation
+    operands come from LDS, and MFMA results stay in VGPRs."""
+    t = asm["gemv_qmfma_res.hip"]
+    assert "v_mfma_i32_16x16x32_i8" in t
+    assert re.search(r"global_load_dwordx4 .* nt", t)
+    assert "ds_write_b128" in t and "ds_read_b128" in t
+    assert "global_load_lds" not in t and "flat_load" not in t
+    assert not re.search(r"v_accvgpr_read", t)
+
+
 def test_stream_probe_has_no_atomics(asm):
     t = asm["stream_read.hip"]
     assert "global_atomic" not in t

@@ -281,3 +281,52 @@ def test_q4_0_deterministic(dg, dev, orc):
     a = _gpu(dg, dev, Wq, Xq, N, K, M)
     b = _gpu(dg, dev, Wq, Xq, N, K, M)
     assert np.array_equal(a, b)
+
+
+# ---- the resident-activation matrix-core kernel (variant 16) ----
+from tests._parity import RES_CFGS, res_default, res_runs, res_unroll  # noqa: E402
+
+RES_LAUNCHES = [dict(variant=16)] + [dict(variant=16, unroll=res_unroll(*c)) for c in RES_CFGS]
+RES_SHAPES = [(37, 4096, 2), (130, 8192, 7), (64, 4096, 16), (200, 4096, 17), (33, 4096, 24), (16, 4096, 3),
+              (1, 4096, 24), (700, 4096, 12), (90, 8192, 4), (45, 4096, 1), (50, 12288, 8), (301, 2048, 5),
+              (77, 14336, 4), (19, 1024, 9)]
+
+
+def _res_expected(launch, N, M, K):
+    u = launch.get("unroll", 0) or res_unroll(*res_default(18, N, M, K))
+    return res_runs(18, u // 10000, (u // 100) % 100, M, K)
+
+
+@pytest.mark.parametrize("launch", RES_LAUNCHES, ids=[str(v) for v in RES_LAUNCHES])
+@pytest.mark.parametrize("N,K,M", RES_SHAPES)
+def test_q4_0_res_matches_oracle(dg, dev, orc, launch, N, K, M):
+    """Every built configuration on shapes with ragged row tiles and groups;
+    configurations that cannot take a shape must be refused, not run."""
+    Wq, Xq = _operands(orc, 270, N, K, M)
+    if not _res_expected(launch, N, M, K):
+        with pytest.raises(dg.DGError):
+            _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
+        return
+    got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
+    assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M), TOL, f"res {launch} {N}x{K} M={M}")
+
+
+@pytest.mark.parametrize("grid", [1, 3, 7, 1000])
+@pytest.mark.parametrize("unroll", [10820, 20420, 40120, 10430, 11620])
+def test_q4_0_res_any_grid_covers_every_row_group(dg, dev, orc, grid, unroll):
+    """Grids smaller than the row groups loop over them; larger grids leave
+    workgroups without rows (they still meet every barrier)."""
+    N, K, M = 333, 4096, 6
+    Wq, Xq = _operands(orc, 275, N, K, M)
+    launch = dict(variant=16, grid=grid, unroll=unroll)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
+    assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M), TOL, str(launch))
+
+
+@pytest.mark.parametrize("M", [2, 13, 16, 24])
+def test_q4_0_res_identical_columns_give_identical_outputs(dg, dev, orc, M):
+    N, K = 300, 4096
+    Wq, Xq = _operands(orc, 240, N, K, M, same_columns=True)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=dict(variant=16, unroll=res_unroll(1, 4, 2)))
+    for m in range(1, M):
+        assert np.array_equal(got[m], got[0])

@@ -179,3 +179,23 @@ def test_q8_0_overrides_beyond_kernel_limits_are_rejected(dg, dev):
         with pytest.raises(dg.DGError) as e:
             dg.dg_gemv_q8_0(W, X, Y, N, K, M, launch=launch)
         assert e.value.status == dg.DG_ERR_ARG, launch
+
+
+# ---- the resident-activation matrix-core kernel (variant 24) ----
+from tests._parity import RES_CFGS, res_default, res_runs, res_unroll  # noqa: E402
+
+RES_LAUNCHES = [dict(variant=24)] + [dict(variant=24, unroll=res_unroll(*c)) for c in RES_CFGS]
+
+
+@pytest.mark.parametrize("launch", RES_LAUNCHES, ids=[str(v) for v in RES_LAUNCHES])
+@pytest.mark.parametrize("N,K,M", [(37, 4096, 2), (130, 8192, 7), (64, 4096, 16), (200, 4096, 17), (33, 4096, 24),
+                                   (700, 4096, 12), (45, 2048, 1), (50, 12288, 8), (77, 14336, 3)])
+def test_q8_0_res_matches_oracle(dg, dev, orc, launch, N, K, M):
+    Wq, Xq = _operands(orc, 440, N, K, M)
+    u = launch.get("unroll", 0) or res_unroll(*res_default(34, N, M, K))
+    if not res_runs(34, u // 10000, (u // 100) % 100, M, K):
+        with pytest.raises(dg.DGError):
+            _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
+        return
+    assert_close(_gpu(dg, dev, Wq, Xq, N, K, M, launch=launch), orc.gemv_q8_0_q8_1(Wq, Xq, N, K, M), TOL,
+                 f"res {launch} {N}x{K} M={M}")
