@@ -344,7 +344,7 @@ typedef struct {
                       *_MFMA_RES: RT*10000 + KS*100 + P*10 (row tiles and
                       K parts per workgroup, 8-block chunks in flight per
                       wave);
-                      NF4: code-pair table copies (8 or 16) + 100 * partial
+                      NF4: code-pair table copies (8, 16, 32) + 100 * partial
                       sums per lane (1, 2) + 1000 * rows in flight (4, 8)    */
 } dg_launch;
 

@@ -25,7 +25,9 @@
 //     the unit's sum is scaled back by 2^-st, 2^-sx and its absmax: the float
 //     GEMV up to fp32 rounding;
 //   * the table is replicated TC times (copy = lane % TC) so that the 8-byte
-//     lookups of 16 lanes fall in distinct banks.
+//     lookups of 16 (TC = 16) or 32 lanes fall in distinct banks; with 32
+//     copies an entry spans 256 bytes and one byte permute per code byte
+//     forms the lookup address.
 // The K of a row is split over the S = K/2048 waves of a workgroup: wave w
 // owns weights 2048w .. 2048w + 2047 of every row the workgroup takes, a lane
 // 32 of them -- 16 code bytes, one 16-byte load (the wave's 64 lanes read 1 KiB
@@ -79,17 +81,31 @@ __device__ __forceinline__ void load_unit(const uint8_t* __restrict__ codes, con
 }
 
 // A lane's 16 code bytes against its 32 activations: NA independent partial
-// sums (byte i to sum i % NA), added in a fixed order.
+// sums (byte i to sum i % NA), added in a fixed order.  tab_lane is the
+// lane's copy of the pair table (entry v at tab_lane[v * TC]).  With 32
+// copies an entry is 256 bytes, so the byte offset of entry v in the lane's
+// copy is v << 8 plus the copy's 8 * (lane % 32): one byte permute forms it
+// from the code word (byte v into bits 8..15, the copy offset into bits
+// 0..7), where fewer copies need a byte extract and a shift-add.
 template <int TC, int NA>
-__device__ __forceinline__ float unit_dot(const u32x4& c, const uint32_t (&xr)[16], const uint2* tab_lane) {
+__device__ __forceinline__ float unit_dot(const u32x4& c, const uint32_t (&xr)[16], const uint2* tab_lane,
+                                          const uint2* tab0, uint32_t copy_off) {
     const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
     float p[NA];
 #pragma unroll
     for (int j = 0; j < NA; ++j) p[j] = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const uint32_t v = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        const uint2 e = tab_lane[v * TC];
+        uint2 e;
+        if constexpr (TC == 32) {
+            // D = bytes {copy_off.b0, code byte i & 3, 0, 0} (selector 4 + k picks byte k of
+            // the first operand, 0 byte 0 of the second, 0x0C a zero byte)
+            const uint32_t off = __builtin_amdgcn_perm(cw[i >> 2], copy_off, 0x0C0C0000u | ((4u + (i & 3)) << 8));
+            e = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint8_t*>(tab0) + off);
+        } else {
+            const uint32_t v = (cw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+            e = tab_lane[v * TC];
+        }
         p[i % NA] = dot2_f16(e.x, xr[i], p[i % NA]);
         p[i % NA] = dot2_f16(e.y, xr[i], p[i % NA]);
     }
@@ -109,7 +125,7 @@ template <int TC, int NA, int AHEAD>
 __global__ void __launch_bounds__(1024)
 k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const float* __restrict__ table,
       const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K, int B) {
-    static_assert(TC == 8 || TC == 16, "table copies");
+    static_assert(TC == 8 || TC == 16 || TC == 32, "table copies");
     static_assert(AHEAD >= 2 && AHEAD <= 8 && (kWave % AHEAD) == 0, "rows in flight");
     __shared__ uint2 ptab[256 * TC];
     __shared__ float red[16][kWave];
@@ -197,12 +213,13 @@ k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const
     lds_barrier();   // the pair table is complete
 
     const uint2* const tab_lane = ptab + (lane % TC);
+    const uint32_t copy_off = (uint32_t)(lane % TC) * 8u;
     float part = 0.0f;
     for (int k0r = 0; k0r < nrows; k0r += AHEAD) {
 #pragma unroll
         for (int j = 0; j < AHEAD; ++j) {
             const int k = k0r + j;
-            const float s = unit_dot<TC, NA>(qc[j], xr, tab_lane);
+            const float s = unit_dot<TC, NA>(qc[j], xr, tab_lane, ptab, copy_off);
             const float a = lane_valid ? qa[j] : 0.0f;
             load_unit(codes, absmax, b + (k + AHEAD) * grid, N, K, nab, lane_valid, code_off, ab_off, qc[j], qa[j]);
             const float r = wave_sum_f32(s * back * a);   // this unit of row k, wave-uniform
@@ -264,13 +281,13 @@ hipError_t launch_gemv_nf4(const void* codes, const float* absmax, const float* 
     const int S = (K + kUnitWeights - 1) / kUnitWeights;   // waves per workgroup: one per unit
     if (S > kMaxUnits) return hipErrorInvalidValue;
     if (cfg && cfg->block && cfg->block != S * kWave) return hipErrorInvalidValue;   // fixed by K
-    // unroll: table copies (8 or 16) + 100 * independent partial sums (1, 2)
+    // unroll: table copies (8, 16 or 32) + 100 * independent partial sums (1, 2)
     //         + 1000 * rows in flight per wave (4 or 8)
     const int u = cfg ? cfg->unroll : 0;
     const int copies = u % 100 ? u % 100 : 8;
     const int na = (u / 100) % 10 ? (u / 100) % 10 : 1;
     const int ahead = u / 1000 ? u / 1000 : 4;
-    if ((copies != 8 && copies != 16) || (na != 1 && na != 2) || (ahead != 4 && ahead != 8))
+    if ((copies != 8 && copies != 16 && copies != 32) || (na != 1 && na != 2) || (ahead != 4 && ahead != 8))
         return hipErrorInvalidValue;
     int grid = cfg && cfg->grid ? cfg->grid : 0;
     if (!grid) {
@@ -291,6 +308,7 @@ hipError_t launch_gemv_nf4(const void* codes, const float* absmax, const float* 
     }
     DG_NF4(16, 1, 4) DG_NF4(16, 2, 4) DG_NF4(8, 1, 4) DG_NF4(8, 2, 4)
     DG_NF4(16, 1, 8) DG_NF4(16, 2, 8) DG_NF4(8, 1, 8) DG_NF4(8, 2, 8)
+    DG_NF4(32, 1, 4) DG_NF4(32, 2, 4) DG_NF4(32, 1, 8) DG_NF4(32, 2, 8)
 #undef DG_NF4
     return hipErrorInvalidValue;
 }

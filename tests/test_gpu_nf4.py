@@ -54,7 +54,8 @@ LAUNCHES = [dict(variant=31), dict(variant=31, unroll=8), dict(variant=31, unrol
             dict(variant=31, unroll=216), dict(variant=31, unroll=8216), dict(variant=31, unroll=4108),
             dict(variant=31, unroll=8008), dict(variant=31, grid=3),
             dict(variant=31, grid=2, unroll=16), dict(variant=31, grid=5, unroll=8208), dict(variant=31, grid=1),
-            dict(variant=31, grid=4000)]
+            dict(variant=31, grid=4000), dict(variant=31, unroll=32), dict(variant=31, unroll=132),
+            dict(variant=31, unroll=8032), dict(variant=31, unroll=4132, grid=3)]
 
 
 @pytest.mark.parametrize("launch", LAUNCHES, ids=[str(v) for v in LAUNCHES])
