@@ -772,6 +772,8 @@ def suite_nf4(dg, torch, emit, ceil_gbps):
         y = torch.empty(N, dtype=torch.float32, device="cuda")
         launches = [("default", None)] + [(f"tc{tc} ahead{h} g{g}", dict(variant=31, unroll=tc + 1000 * h, grid=g))
                                           for tc in (8, 16, 32) for h in (4, 8) for g in (256, 512, 1024, 2048)]
+        if K in (2048, 4096, 8192):
+            launches += [(f"mfma g{g}", dict(variant=32, grid=g)) for g in (0, 128, 512)]
         for lname, launch in launches:
             calls = [(lambda c=c, launch=launch: dg.dg_gemv_nf4(ops[c % nc][0], ops[c % nc][1], table, x, y,
                                                                N=N, K=K, B=B, launch=launch))

@@ -370,8 +370,12 @@ enum {
     DG_VARIANT_Q8_UNITS = 23,       /* as DG_VARIANT_Q4_UNITS, Q8_0 weights                        */
     DG_VARIANT_Q8_MFMA_RES = 24,    /* as DG_VARIANT_Q4_MFMA_RES, Q8_0 weights                     */
     /* NF4 */
-    DG_VARIANT_NF4_UNITS = 31       /* code bytes looked up in a byte-pair table in LDS; one
+    DG_VARIANT_NF4_UNITS = 31,      /* code bytes looked up in a byte-pair table in LDS; one
                                        wave per 2048 weights of a row (block = 64*ceil(K/2048)) */
+    DG_VARIANT_NF4_MFMA = 32        /* the looked-up pairs as operands of f16 matrix-core
+                                       products, 16 rows x 32 weights per instruction; K = 2048,
+                                       4096 or 8192, K/128 <= B <= K/16; no block or unroll
+                                       override                                                */
 };
 
 dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K,

@@ -50,6 +50,8 @@ DG_VARIANT_Q8_LDSROW = 21
 DG_VARIANT_Q8_MFMA = 22
 DG_VARIANT_Q8_UNITS = 23
 DG_VARIANT_Q8_MFMA_RES = 24
+DG_VARIANT_NF4_UNITS = 31
+DG_VARIANT_NF4_MFMA = 32
 
 # Every symbol include/decodegemv.h declares.
 EXPORTED = (

@@ -173,7 +173,7 @@ k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const
     }
     if (threadIdx.x < 16) tl[threadIdx.x] = tv;
     lds_barrier();
-    const int st = scale_exp(tmax >> 23);
+    const int st = min(scale_exp(tmax >> 23), 126);   // 2^st and 2^-st both normal
     {
         const float ts = pow2f(st);
         for (int i = threadIdx.x; i < 256 * TC; i += blockDim.x) {
@@ -185,9 +185,9 @@ k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const
             ptab[i] = uint2{ha | (hb << 16), la | (lb << 16)};   // the first weight in the low half, as x[2j]
         }
     }
-    // the lane's activations as binary16 scaled by 2^sx; back = 2^-st * 2^-sx
+    // the lane's activations as binary16 scaled by 2^sx; bx = 2^-sx, bt = 2^-st
     uint32_t xr[16];
-    float back;
+    float bx;
     {
         uint32_t raw[16];
 #pragma unroll
@@ -200,7 +200,7 @@ k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const
         uint32_t emax = 0;   // largest bfloat16 exponent field of the 32 values
 #pragma unroll
         for (int i = 0; i < 16; ++i) emax = max(emax, max((raw[i] >> 7) & 0xFFu, (raw[i] >> 23) & 0xFFu));
-        const int sx = scale_exp(emax);
+        const int sx = min(scale_exp(emax), 126);
         const float xs = pow2f(sx);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -208,8 +208,9 @@ k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const
             const float hi = __builtin_bit_cast(float, raw[i] & 0xFFFF0000u) * xs;
             xr[i] = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
         }
-        back = pow2f(-st) * pow2f(-sx);
+        bx = pow2f(-sx);
     }
+    const float bt = pow2f(-st);
     lds_barrier();   // the pair table is complete
 
     const uint2* const tab_lane = ptab + (lane % TC);
@@ -222,7 +223,7 @@ k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const
             const float s = unit_dot<TC, NA>(qc[j], xr, tab_lane, ptab, copy_off);
             const float a = lane_valid ? qa[j] : 0.0f;
             load_unit(codes, absmax, b + (k + AHEAD) * grid, N, K, nab, lane_valid, code_off, ab_off, qc[j], qa[j]);
-            const float r = wave_sum_f32(s * back * a);   // this unit of row k, wave-uniform
+            const float r = wave_sum_f32(s * bt * bx * a);   // this unit of row k, wave-uniform
             if (lane == (k & (kWave - 1))) part = r;
             if ((k & (kWave - 1)) == kWave - 1 || k == nrows - 1) {   // a batch of 64 rows is complete
                 const int kb = k & ~(kWave - 1);
@@ -241,6 +242,241 @@ k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const
             }
             if (k == nrows - 1) break;
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// NF4 on the matrix cores (K = 2048, 4096 or 8192).
+//
+// The same products, with the per-byte work moved from the vector unit to
+// v_mfma_f32_16x16x32_f16.  A workgroup of 16 waves takes tiles of 16 rows;
+// wave w owns part w of K (K/16 weights, whole blocks of B), so a tile is 16
+// rows x K/16 weights per wave, in k-steps of 32 weights of one block:
+//   each lane group g covers weights 8g..8g+7 of a k-step of row j (4 code
+//     bytes), in two MFMAs of two bytes each.  A byte's table entry is its
+//     two weights' high binary16 parts and their remainders (two dwords, as
+//     one 8-byte LDS read lands them); two entries side by side are the
+//     lane's B operand, so B holds (hi, hi, lo, lo) of two weights twice
+//     over, and A holds the matching activations twice: x pair, x pair,
+//     next x pair, next x pair (x is stored in LDS with every binary16 pair
+//     duplicated, so one 16-byte read is the operand).  The MFMA's sum over
+//     its 32 k-slots is then the exact hi*x + lo*x over 16 weights;
+//   every row of A is the same, so every row of D is the same and lane
+//     (g, j) holds row j's sum in each of its four D registers;
+//   after the B/32 k-steps of a block, the block's D is scaled by the row's
+//     absmax and added to the lane's running sum (fp32); four D accumulators
+//     alternate so that consecutive MFMAs do not wait for each other.
+// Loads: lane (g, j) reads 16 consecutive code bytes of row j per instruction
+// -- k-step 4c + g, all four lane groups' bytes -- and four permlane swaps
+// (v_permlane16_swap, v_permlane32_swap: a 4 x 4 transpose across the lane
+// groups) hand each lane group its own dword of the four k-steps.  The next
+// tile's codes and absmax values are loaded while this tile computes.  The
+// 16 parts of a tile meet in LDS and are added in part order (deterministic).
+// Arithmetic: products exact (binary16 x binary16), sums in fp32 inside the
+// MFMA and in the running sum; x is scaled by one power of two for the whole
+// of K (exact unless a value lies some 2^28 below the largest).
+// ---------------------------------------------------------------------------
+constexpr int kMW = 16;   // waves per workgroup = parts of K
+
+__device__ __forceinline__ float u32_as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_mov_u32<kDppRowShr1, 0xF>(v));
+    v = max(v, dpp_mov_u32<kDppRowShr2, 0xF>(v));
+    v = max(v, dpp_mov_u32<kDppRowShr4, 0xF>(v));
+    v = max(v, dpp_mov_u32<kDppRowShr8, 0xF>(v));
+    v = max(v, dpp_mov_u32<kDppRowBcast15, 0xA>(v));
+    v = max(v, dpp_mov_u32<kDppRowBcast31, 0xC>(v));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4m __attribute__((ext_vector_type(4)));
+
+// 4 x 4 transpose of dwords across the four 16-lane groups: in, lane group g
+// holds v[0..3] of its own k-step; out, lane group g holds dword g of k-steps
+// 0..3 (v[s] = dword g of k-step s).
+__device__ __forceinline__ void xpose4(uint32_t (&v)[4]) {
+    // rows (lane groups) 0<->1 and 2<->3 exchange: v0' = (v0.r0, v1.r0, v0.r2, v1.r2),
+    // v1' = (v0.r1, v1.r1, v0.r3, v1.r3); likewise v2, v3
+    const auto a = __builtin_amdgcn_permlane16_swap(v[0], v[1], false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(v[2], v[3], false, false);
+    // halves exchange: (a0, b0) -> k-steps 0 and 2; (a1, b1) -> k-steps 1 and 3
+    const auto c = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+    v[0] = c[0];
+    v[2] = c[1];
+    v[1] = d[0];
+    v[3] = d[1];
+}
+
+template <int KSP, int BPK>   // k-steps per part (K / 512), k-steps per block (B / 32)
+__global__ void __launch_bounds__(kMW * kWave)
+k_nf4_mfma(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const float* __restrict__ table,
+           const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K, int B) {
+    static_assert(KSP == 4 || KSP == 8 || KSP == 16, "K = 2048, 4096 or 8192");
+    static_assert(BPK >= 1 && BPK <= KSP, "whole blocks per part");
+    constexpr int NB = KSP / BPK;           // blocks per part
+    constexpr int NC = KSP / 4;             // 16-byte code loads per lane per tile
+    constexpr int NAL = NB >= 4 ? NB / 4 : NB;   // absmax loads per lane per tile
+    __shared__ uint2 ptab[256 * 32];        // the byte-pair table, 32 copies (64 KiB)
+    __shared__ uint32_t xh[8192];           // x as scaled binary16 pairs, each pair twice
+    __shared__ float red[2][kMW][16];       // the parts of a tile (double-buffered)
+    __shared__ float tl[16];
+    __shared__ uint32_t emax_w[kMW];
+    const int lane = lane_id();
+    const int wave = wave_in_block();
+    const int g = lane >> 4, j = lane & 15;
+    const int ntiles = (N + 15) / 16;
+    const int nab = K / B;                  // absmax values per row
+    const int pbyte = wave * KSP * 16;      // first code byte of this part in a row
+    const int pblk = wave * NB;             // first block of this part
+
+    // code and absmax loads of tile t (rows past N re-read row N - 1)
+    auto load_tile = [&](int t, u32x4 (&c)[NC], float (&am)[NB]) {
+        const int r = min(t * 16 + j, N - 1);
+        const uint8_t* rowc = codes + (size_t)r * (K >> 1) + pbyte + 16 * g;
+#pragma unroll
+        for (int q = 0; q < NC; ++q) c[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowc + 64 * q));
+        const float* rowa = absmax + (size_t)r * nab + pblk;
+        if constexpr (NB >= 4) {
+#pragma unroll
+            for (int q = 0; q < NAL; ++q) {
+                // elements pass through u32_as_f32 by value: a bit cast applied to a
+                // vector element lvalue (v.y) reads element 0 on this compiler
+                const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowa + 4 * q));
+                am[4 * q + 0] = u32_as_f32(v.x);
+                am[4 * q + 1] = u32_as_f32(v.y);
+                am[4 * q + 2] = u32_as_f32(v.z);
+                am[4 * q + 3] = u32_as_f32(v.w);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NB; ++q) am[q] = __builtin_nontemporal_load(rowa + q);
+        }
+    };
+
+    // x first (one 16-byte load per thread covers K = 8192), then the first tile
+    const int nxv = K / 8;                   // 16-byte vectors of x
+    u32x4 xv = reinterpret_cast<const u32x4*>(x)[(int)threadIdx.x < nxv ? (int)threadIdx.x : 0];
+    int t = blockIdx.x;
+    u32x4 cc[NC];
+    float am[NB];
+    if (t < ntiles) load_tile(t, cc, am);
+
+    // the byte-pair table (as in k_nf4), 32 copies
+    uint32_t tmax = 0;
+    float tv = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const float v = table[q];
+        tmax = max(tmax, __builtin_bit_cast(uint32_t, v) & 0x7FFFFFFFu);
+        tv = threadIdx.x == (unsigned)q ? v : tv;
+    }
+    if (threadIdx.x < 16) tl[threadIdx.x] = tv;
+    // the largest bfloat16 exponent field of x, over the workgroup
+    uint32_t em = 0;
+    if ((int)threadIdx.x < nxv) {
+        const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) em = max(em, max((w4[q] >> 7) & 0xFFu, (w4[q] >> 23) & 0xFFu));
+    }
+    em = wave_max_u32(em);
+    if (lane == 0) emax_w[wave] = em;
+    lds_barrier();
+    const int st = min(scale_exp(tmax >> 23), 126);
+    {
+        const float ts = pow2f(st);
+        for (int i = threadIdx.x; i < 256 * 32; i += kMW * kWave) {
+            const int v = i >> 5;
+            const float a = tl[v >> 4] * ts, b2 = tl[v & 15] * ts;
+            const uint32_t ha = f32_to_f16_bits(a), hb = f32_to_f16_bits(b2);
+            const uint32_t la = f32_to_f16_bits(a - f16_bits_to_f32(ha));
+            const uint32_t lb = f32_to_f16_bits(b2 - f16_bits_to_f32(hb));
+            ptab[i] = uint2{ha | (hb << 16), la | (lb << 16)};   // the first weight in the low half
+        }
+    }
+    uint32_t emx = 0;
+#pragma unroll
+    for (int w = 0; w < kMW; ++w) emx = max(emx, emax_w[w]);
+    const int sx = min(scale_exp(emx), 126);
+    if ((int)threadIdx.x < nxv) {
+        const float xs = pow2f(sx);
+        const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float lo = __builtin_bit_cast(float, w4[q] << 16) * xs;
+            const float hi = __builtin_bit_cast(float, w4[q] & 0xFFFF0000u) * xs;
+            const uint32_t pr = f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+            xh[8 * threadIdx.x + 2 * q] = pr;
+            xh[8 * threadIdx.x + 2 * q + 1] = pr;
+        }
+    }
+    const float bt = pow2f(-st), bx = pow2f(-sx);
+    lds_barrier();   // table and x complete
+
+    const uint32_t copy_off = (uint32_t)(lane & 31) * 8u;
+    const uint8_t* const tab0 = reinterpret_cast<const uint8_t*>(ptab);
+    const uint32_t* const xpart = xh + wave * KSP * 32 + 8 * g;   // this part's x (doubled), lane group g's
+    int par = 0;
+    for (; t < ntiles; t += gridDim.x) {   // workgroup-uniform
+        u32x4 cur[NC];
+        float amc[NB];
+#pragma unroll
+        for (int q = 0; q < NC; ++q) cur[q] = cc[q];
+#pragma unroll
+        for (int q = 0; q < NB; ++q) amc[q] = am[q];
+        if (t + (int)gridDim.x < ntiles) load_tile(t + gridDim.x, cc, am);
+
+        float acc = 0.0f;
+        f32x4m d[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) d[u] = f32x4m{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int q = 0; q < NC; ++q) {
+            uint32_t v[4] = {cur[q].x, cur[q].y, cur[q].z, cur[q].w};
+            xpose4(v);   // v[s'] = this lane group's code dword of k-step 4q + s'
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int ks = 4 * q + s2;
+                uint2 e[4];
+#pragma unroll
+                for (int b4 = 0; b4 < 4; ++b4) {
+                    const uint32_t off = __builtin_amdgcn_perm(v[s2], copy_off, 0x0C0C0000u | ((4u + b4) << 8));
+                    e[b4] = *reinterpret_cast<const uint2*>(tab0 + off);
+                }
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {   // bytes 2h, 2h + 1 of the lane's four
+                    const u32x4 bop = u32x4{e[2 * h].x, e[2 * h].y, e[2 * h + 1].x, e[2 * h + 1].y};
+                    const u32x4 aop = *reinterpret_cast<const u32x4*>(xpart + ks * 32 + 4 * h);
+                    f32x4m& dd = d[2 * (ks & 1) + h];
+                    dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, aop),
+                                                                __builtin_bit_cast(f16x8, bop), dd, 0, 0, 0);
+                }
+                if ((ks + 1) % BPK == 0) {   // the block is complete: scale by its absmax
+                    float bs;
+                    if constexpr (BPK == 1) {
+                        bs = d[2 * (ks & 1)][0] + d[2 * (ks & 1) + 1][0];
+                        d[2 * (ks & 1)] = f32x4m{0.0f, 0.0f, 0.0f, 0.0f};
+                        d[2 * (ks & 1) + 1] = f32x4m{0.0f, 0.0f, 0.0f, 0.0f};
+                    } else {
+                        bs = (d[0][0] + d[1][0]) + (d[2][0] + d[3][0]);
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) d[u] = f32x4m{0.0f, 0.0f, 0.0f, 0.0f};
+                    }
+                    acc = fmaf(bs, amc[ks / BPK], acc);
+                }
+            }
+        }
+        if (lane < 16) red[par][wave][j] = acc * bt * bx;
+        lds_barrier();
+        if (wave == 0 && lane < 16 && t * 16 + j < N) {
+            float sum = red[par][0][j];
+#pragma unroll
+            for (int w = 1; w < kMW; ++w) sum += red[par][w][j];
+            y[t * 16 + j] = sum;
+        }
+        par ^= 1;
     }
 }
 
@@ -273,10 +509,34 @@ __global__ void k_quantize_nf4(const float* __restrict__ w, uint8_t* __restrict_
     }
 }
 
+hipError_t launch_nf4_mfma(const uint8_t* c8, const float* absmax, const float* table, const uint16_t* x16, float* y,
+                           int N, int K, int B, int grid, hipStream_t s) {
+    const int ksp = K / 512, bpk = B / 32;
+    if (K != 512 * ksp || (ksp != 4 && ksp != 8 && ksp != 16) || bpk > ksp || ksp / bpk > 8)
+        return hipErrorInvalidValue;   // at most 8 absmax blocks per part (registers)
+    const int ntiles = (N + 15) / 16;
+    if (!grid) grid = ntiles < device_cu_count() ? ntiles : device_cu_count();   // one workgroup per CU (LDS)
+#define DG_NF4M(KK, BB)                                                                                       \
+    if (ksp == KK && bpk == BB) {                                                                             \
+        hipLaunchKernelGGL((k_nf4_mfma<KK, BB>), dim3(grid), dim3(kMW * kWave), 0, s, c8, absmax, table, x16, y, \
+                           N, K, B);                                                                          \
+        return hipGetLastError();                                                                             \
+    }
+    DG_NF4M(4, 1) DG_NF4M(4, 2) DG_NF4M(4, 4)
+    DG_NF4M(8, 1) DG_NF4M(8, 2) DG_NF4M(8, 4) DG_NF4M(8, 8)
+    DG_NF4M(16, 2) DG_NF4M(16, 4) DG_NF4M(16, 8)   // K = 8192 with B = 32 would spill
+#undef DG_NF4M
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_gemv_nf4(const void* codes, const float* absmax, const float* table, const void* x, float* y,
                            int N, int K, int B, const dg_launch* cfg, hipStream_t s) {
+    if (cfg && cfg->variant == DG_VARIANT_NF4_MFMA) {
+        if (cfg->block || cfg->unroll) return hipErrorInvalidValue;   // fixed: 16 waves, one table
+        return launch_nf4_mfma((const uint8_t*)codes, absmax, table, (const uint16_t*)x, y, N, K, B, cfg->grid, s);
+    }
     if (cfg && cfg->variant && cfg->variant != DG_VARIANT_NF4_UNITS) return hipErrorInvalidValue;
     const int S = (K + kUnitWeights - 1) / kUnitWeights;   // waves per workgroup: one per unit
     if (S > kMaxUnits) return hipErrorInvalidValue;

@@ -70,6 +70,44 @@ def test_nf4_launch_variants(dg, dev, orc, launch, N, K, B):
     assert_close(got, orc.gemv_nf4(codes, absmax, t, xb, N, K, B), TOL, f"{launch}")
 
 
+@pytest.mark.parametrize("N,K,B", [(1, 2048, 32), (17, 2048, 128), (33, 4096, 64), (300, 4096, 256), (70, 8192, 64),
+                                   (5, 8192, 256), (1000, 4096, 32), (64, 8192, 128)])
+@pytest.mark.parametrize("grid", [0, 1, 3])
+def test_nf4_matrix_cores_match_oracle(dg, dev, orc, N, K, B, grid):
+    """The matrix-core variant: K = 2048, 4096, 8192; block sizes from K/128 to
+    K/16; ragged tiles; grids smaller than the tiles (workgroups loop)."""
+    codes, absmax, xb = _operands(orc, 660 + K % 89, N, K, B)
+    t = synth.nf4_table()
+    got = _gpu(dg, dev, codes, absmax, t, xb, N, K, B, launch=dict(variant=32, grid=grid))
+    assert_close(got, orc.gemv_nf4(codes, absmax, t, xb, N, K, B), TOL, f"mfma {N}x{K} B={B} grid={grid}")
+
+
+@pytest.mark.parametrize("N,K,B", [(16, 1024, 64), (16, 14336, 64), (16, 2048, 256), (16, 8192, 32)])
+def test_nf4_matrix_cores_refuse_other_shapes(dg, dev, orc, N, K, B):
+    """K outside {2048, 4096, 8192}, a block longer than K/16 (256 > 2048/16)
+    or shorter than K/128 (32 < 8192/128) is refused."""
+    codes, absmax, xb = _operands(orc, 670, N, K, B)
+    with pytest.raises(dg.DGError):
+        _gpu(dg, dev, codes, absmax, synth.nf4_table(), xb, N, K, B, launch=dict(variant=32))
+
+
+def test_nf4_matrix_cores_any_table_and_tiny_x(dg, dev, orc):
+    """Unordered tables with repeats and a wide range; x with a tiny and a
+    zero column stretch (one power-of-two scale for all of K)."""
+    N, K, B = 45, 4096, 64
+    g = np.random.default_rng(78)
+    codes = g.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    absmax = np.abs(g.standard_normal((N, K // B))).astype(np.float32) * 3
+    xf = g.standard_normal(K).astype(np.float32)
+    xf[:512] *= 1e-3
+    xf[512:640] = 0.0
+    xb = (xf.view(np.uint32) >> 16).astype(np.uint16)   # truncation to bfloat16 bits (any bits are valid input)
+    for t in (g.standard_normal(16).astype(np.float32) * 100, np.repeat(np.float32([0.5, -2.0]), 8),
+              synth.nf4_table()):
+        got = _gpu(dg, dev, codes, absmax, t, xb, N, K, B, launch=dict(variant=32))
+        assert_close(got, orc.gemv_nf4(codes, absmax, t, xb, N, K, B), TOL, f"table {t[:3]}")
+
+
 def test_nf4_any_table(dg, dev, orc):
     """The kernel takes any finite table: unordered, with repeats, wide range."""
     N, K, B = 90, 4096, 64
