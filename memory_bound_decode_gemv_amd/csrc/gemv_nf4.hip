@@ -215,32 +215,40 @@ k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const
 
     const uint2* const tab_lane = ptab + (lane % TC);
     const uint32_t copy_off = (uint32_t)(lane % TC) * 8u;
-    float part = 0.0f;
-    for (int k0r = 0; k0r < nrows; k0r += AHEAD) {
+    // Rows in batches of 64: the inner loop holds nothing but loads, lookups
+    // and reductions (rows past the workgroup's last re-read a fixed address
+    // and are dropped), and the batch's results are stored after it.  With a
+    // store or an early exit inside the loop the compiler's vmcnt analysis
+    // merged unequal histories at the loop head and drained every load there
+    // (vmcnt(0) once per AHEAD rows); without them its waits are exact.
+    const int nrows_pad = (nrows + AHEAD - 1) / AHEAD * AHEAD;   // uniform
+    for (int kb = 0; kb < nrows_pad; kb += kWave) {
+        const int kend = kb + kWave < nrows_pad ? kb + kWave : nrows_pad;
+        float part = 0.0f;
+        for (int k0r = kb; k0r < kend; k0r += AHEAD) {
 #pragma unroll
-        for (int j = 0; j < AHEAD; ++j) {
-            const int k = k0r + j;
-            const float s = unit_dot<TC, NA>(qc[j], xr, tab_lane, ptab, copy_off);
-            const float a = lane_valid ? qa[j] : 0.0f;
-            load_unit(codes, absmax, b + (k + AHEAD) * grid, N, K, nab, lane_valid, code_off, ab_off, qc[j], qa[j]);
-            const float r = wave_sum_f32(s * bt * bx * a);   // this unit of row k, wave-uniform
-            if (lane == (k & (kWave - 1))) part = r;
-            if ((k & (kWave - 1)) == kWave - 1 || k == nrows - 1) {   // a batch of 64 rows is complete
-                const int kb = k & ~(kWave - 1);
-                if (S == 1) {
-                    if (lane <= (k & (kWave - 1))) y[b + (int64_t)(kb + lane) * grid] = part;
-                } else {
-                    red[wave][lane] = part;
-                    lds_barrier();
-                    if (wave == 0 && lane <= (k & (kWave - 1))) {
-                        float t = red[0][lane];
-                        for (int w = 1; w < S; ++w) t += red[w][lane];
-                        y[b + (int64_t)(kb + lane) * grid] = t;
-                    }
-                    lds_barrier();
-                }
+            for (int j = 0; j < AHEAD; ++j) {
+                const int k = k0r + j;
+                const float s = unit_dot<TC, NA>(qc[j], xr, tab_lane, ptab, copy_off);
+                const float a = lane_valid ? qa[j] : 0.0f;
+                load_unit(codes, absmax, b + (k + AHEAD) * grid, N, K, nab, lane_valid, code_off, ab_off, qc[j],
+                          qa[j]);
+                const float r = wave_sum_f32(s * bt * bx * a);   // this unit of row k, wave-uniform
+                if (lane == (k & (kWave - 1))) part = r;
             }
-            if (k == nrows - 1) break;
+        }
+        const bool mine = kb + lane < nrows;   // lane i holds row kb + i of the workgroup's sequence
+        if (S == 1) {
+            if (mine) y[b + (int64_t)(kb + lane) * grid] = part;
+        } else {
+            red[wave][lane] = part;
+            lds_barrier();
+            if (wave == 0 && mine) {
+                float t = red[0][lane];
+                for (int w = 1; w < S; ++w) t += red[w][lane];
+                y[b + (int64_t)(kb + lane) * grid] = t;
+            }
+            lds_barrier();
         }
     }
 }
