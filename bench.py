@@ -864,6 +864,31 @@ def profile_kernels(args):
     log(f"[profile-kernels] q4_0 x{2 * nq}, f16 x{n16}, nf4 x{2 * nn}, stream_read 1 GiB x4, copy 1 GiB x4")
 
 
+SMALL_M_CASES = [(4096, 4096), (14336, 4096), (4096, 14336)]
+SMALL_M_COLUMNS = (4, 8, 16, 24)
+
+
+def profile_small_m(args):
+    """Launches the Q4_0 x Q8_1 small-batch GEMV eagerly, four dispatches per
+    (shape, M) with the library's default kernel choice, in the order of
+    SMALL_M_CASES x SMALL_M_COLUMNS, for rocprofv3 counter runs of the
+    matrix-core and units kernels."""
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    for (N, K) in SMALL_M_CASES:
+        Wq = q4_copies(1, N, K, 2)
+        for M in SMALL_M_COLUMNS:
+            Xq = q8_columns(1, K, M)
+            Y = torch.empty(M * N, dtype=torch.float32, device="cuda")
+            torch.cuda.synchronize()
+            for i in range(4):
+                dg.dg_gemv_q4_0(Wq[i % 2], Xq, Y, N, K, M)
+            torch.cuda.synchronize()
+            log(f"[profile-small-m] {N}x{K} M={M}: 4 launches")
+        del Wq
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -873,6 +898,8 @@ def main():
     ap.add_argument("--suite-out", default=None, help="append suite records (JSON lines) to this file")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="launch each profiled kernel eagerly on known workloads (for rocprofv3 --pmc)")
+    ap.add_argument("--profile-small-m", action="store_true",
+                    help="launch the small-batch Q4_0 GEMV eagerly on the decoder shapes (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
                     help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q8,m1,argmax,tail,nf4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -889,6 +916,8 @@ def main():
     dg.raw()
     if args.profile_kernels:
         profile_kernels(args)
+    elif args.profile_small_m:
+        profile_small_m(args)
     elif args.suite:
         suite(args)
     else:

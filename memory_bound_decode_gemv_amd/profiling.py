@@ -15,6 +15,14 @@ traffic only while that hash still matches the tree.
     python -m memory_bound_decode_gemv_amd.profiling trace KERNEL_STATS.csv [--runs KERNEL_TRACE.csv] --md OUT.md
     python -m memory_bound_decode_gemv_amd.profiling suite SUITE.jsonl --md OUT.md
     python -m memory_bound_decode_gemv_amd.profiling suite A.jsonl B.jsonl --condense --filter RE --md OUT.md
+    python -m memory_bound_decode_gemv_amd.profiling pmc PASS1.csv PASS2.csv ... --kernels RE --labels L1,L2,.. \
+        --per 4 --md OUT.md
+
+pmc: SQ counters of `bench.py --profile-small-m` (several --pmc passes of the
+same program): the dispatches of the kernels matching --kernels, in program
+order, are grouped --per at a time (one group per label) and each counter is
+averaged over a group, with a few derived figures (instructions per wave,
+vector-ALU busy share).
 """
 from __future__ import annotations
 
@@ -254,6 +262,62 @@ def suite_condensed_markdown(jsonls, command, name_filter=None):
     return "\n".join(lines) + "\n"
 
 
+def pmc_summary(csvs, kernel_re, labels, per):
+    """Per-label averages of every counter in the --pmc CSVs (one CSV per pass)."""
+    rows = None
+    meta = []
+    for path in csvs:
+        disp = collections.OrderedDict()
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if not re.search(kernel_re, r["Kernel_Name"]):
+                    continue
+                d = disp.setdefault(int(r["Dispatch_Id"]), {"_name": r["Kernel_Name"], "_vgpr": r["VGPR_Count"],
+                                                            "_wg": r["Workgroup_Size"], "_grid": r["Grid_Size"],
+                                                            "_lds": r["LDS_Block_Size"]})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        seq = [v for _, v in sorted(disp.items())]
+        if rows is None:
+            rows = [dict(v) for v in seq]
+        else:
+            for a, b in zip(rows, seq):
+                a.update({k: v for k, v in b.items() if not k.startswith("_")})
+    out = []
+    for i, lab in enumerate(labels):
+        grp = rows[i * per:(i + 1) * per]
+        if not grp:
+            break
+        avg = {k: sum(g[k] for g in grp) / len(grp) for k in grp[0] if not k.startswith("_")}
+        short = re.sub(r"^void |dg::|\(anonymous namespace\)::|mfma::", "", grp[0]["_name"])
+        short = short.split("(")[0]
+        out.append({"label": lab, "kernel": short, "vgpr": grp[0]["_vgpr"], "wg": grp[0]["_wg"],
+                    "grid_threads": grp[0]["_grid"], "lds": grp[0]["_lds"], **avg})
+    return out
+
+
+def pmc_markdown(summary, command):
+    lines = ["# SQ counters of the small-batch Q4_0 GEMV", "", "Command (one run per counter pass):", "",
+             f"    {command}", "",
+             "Per launch, averaged over four dispatches.  `VALU/wave` and `LDS/wave` are instructions per wave; "
+             "`VALU busy` is SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES x waves per SIMD (both counters in units of "
+             "four cycles): the share of a SIMD's cycles spent issuing vector instructions.", "",
+             "| workload | kernel | VGPRs | threads/WG | waves | waves/SIMD | VALU/wave | MFMA | LDS/wave | "
+             "LDS bank-conflict cycles | VALU busy |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in summary:
+        waves = r.get("SQ_WAVES", 0.0)
+        wps = waves / 1024.0
+        valu = r.get("SQ_INSTS_VALU", 0.0)
+        busy = ""
+        if r.get("SQ_WAVE_CYCLES") and r.get("SQ_ACTIVE_INST_VALU"):
+            busy = f"{r['SQ_ACTIVE_INST_VALU'] / r['SQ_WAVE_CYCLES'] * min(wps, 8):.2f}"
+        lines.append(f"| {r['label']} | `{r['kernel'][:60]}` | {r['vgpr']} | {r['wg']} | {waves:.0f} | {wps:.2f} | "
+                     f"{valu / max(waves, 1):.0f} | {r.get('SQ_INSTS_MFMA', 0):.0f} | "
+                     f"{r.get('SQ_INSTS_LDS', 0) / max(waves, 1):.0f} | {r.get('SQ_LDS_BANK_CONFLICT', 0):.3g} | "
+                     f"{busy} |")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -264,6 +328,13 @@ def main(argv=None):
     c.add_argument("--md", default=os.path.join(PROFILES, "hbm_traffic_counters.md"))
     c.add_argument("--command-fetch", default="")
     c.add_argument("--command-write", default="")
+    pm = sub.add_parser("pmc")
+    pm.add_argument("csvs", nargs="+")
+    pm.add_argument("--kernels", required=True)
+    pm.add_argument("--labels", required=True)
+    pm.add_argument("--per", type=int, default=4)
+    pm.add_argument("--md", required=True)
+    pm.add_argument("--command", default="")
     q = sub.add_parser("suite")
     q.add_argument("jsonl", nargs="+")
     q.add_argument("--md", required=True)
@@ -285,6 +356,10 @@ def main(argv=None):
         with open(a.md, "w") as f:
             f.write(counters_markdown(s, a.command_fetch, a.command_write))
         print(json.dumps(s, indent=1))
+    elif a.cmd == "pmc":
+        s = pmc_summary(a.csvs, a.kernels, a.labels.split(","), a.per)
+        with open(a.md, "w") as f:
+            f.write(pmc_markdown(s, a.command))
     elif a.cmd == "suite":
         with open(a.md, "w") as f:
             if a.condense:
