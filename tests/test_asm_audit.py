@@ -100,6 +100,15 @@ def test_resident_matrix_core_kernel(asm):
     assert not re.search(r"v_accvgpr_read", t)
 
 
+def test_nf4_row_loop_keeps_loads_in_flight(asm):
+    """The NF4 kernels stream rows into registers with the compiler's own
+    vmcnt waits; a store or an early exit inside the row loop once made it
+    drain every load at the loop head.  No vmcnt(0) may appear in them."""
+    for name, body in _kernels(asm["gemv_nf4.hip"]):
+        if "k_nf4I" in name:
+            assert "s_waitcnt vmcnt(0)" not in body, name
+
+
 def test_stream_probe_has_no_atomics(asm):
     t = asm["stream_read.hip"]
     assert "global_atomic" not in t
