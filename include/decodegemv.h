@@ -135,7 +135,7 @@ dg_status dg_gemv_bf16(const void* W, const void* x, float* y,
  *       binary16 s, 32 int8 codes), column m starting at block m*K/32;
  *       16-byte aligned (the kernels copy it in 16-byte pieces).
  *   Y   device float32 [M][N] (column m of the result at Y + m*N).
- *   N   rows, 0 <= N < 2^31.  K: multiple of 256, 0 <= K < 2^31.
+ *   N   rows, 0 <= N < 2^31.  K: multiple of 256, 0 <= K <= 2^26.
  *   M   columns, 0 <= M <= 24 (0 launches nothing).
  * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_HIP.
  * ------------------------------------------------------------------------ */
@@ -154,7 +154,7 @@ dg_status dg_gemv_q4_0(const void* Wq, const void* Xq, float* Y,
  *   Wq  device, N rows of K/32 Q8_0 blocks, 34 bytes each (binary16 d, then
  *       32 int8 codes), rows packed back to back; 16-byte aligned.
  *   Xq, Y, N, K, M  as for dg_gemv_q4_0 (Xq 16-byte aligned, K % 256 == 0,
- *       M <= 24).
+ *       K <= 2^26, M <= 24).
  * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_HIP.
  * ------------------------------------------------------------------------ */
 dg_status dg_gemv_q8_0(const void* Wq, const void* Xq, float* Y,

@@ -14,6 +14,7 @@ namespace {
 thread_local std::string g_last_hip_error;
 
 constexpr int64_t kI32Max = 2147483647;
+constexpr int64_t kQuantMaxK = int64_t(1) << 26;   // Q4_0 / Q8_0 rows: 32-bit copy offsets in every kernel
 
 dg_status hip_status(hipError_t e) {
     if (e == hipSuccess) return DG_OK;
@@ -51,7 +52,7 @@ dg_status gemv_dense_checked(bool bf16, const void* W, const void* x, void* y, i
 
 dg_status gemv_quant_checked(bool q8, const void* Wq, const void* Xq, float* Y, int64_t N, int64_t K, int M,
                              const dg_launch* cfg, dg_stream stream) {
-    if (N < 0 || N > kI32Max || K < 0 || K > kI32Max || K % 256 != 0 || M < 0 || M > 24)
+    if (N < 0 || N > kI32Max || K < 0 || K > kQuantMaxK || K % 256 != 0 || M < 0 || M > 24)
         return DG_ERR_SHAPE;
     if (!launch_ok(cfg)) return DG_ERR_ARG;
     if (N == 0 || M == 0) return DG_OK;

@@ -42,7 +42,11 @@ using namespace mfma;
 //    block, column spans padded to an odd number of slots) into a buffer
 //    shared by the workgroup; every weight row tile reuses it, and L2 serves
 //    it to every workgroup.  With MP < 16 the MFMA rows past MP re-read
-//    columns (their results are discarded).
+//    columns (their results are discarded).  With one row tile per
+//    workgroup (RT = 1) nothing is shared: each wave copies its own part's
+//    columns into a region of its own and waits only for its own copies, so
+//    the waves of a workgroup drift apart and overlap one another's loads
+//    and arithmetic.
 // DEPTH buffers of each kind keep DEPTH - 1 iterations in flight while one is
 // computed.  No global load goes through VGPRs inside the loop, so the only
 // vector-memory operations a wave has outstanding are its own copies, which
@@ -50,8 +54,9 @@ using namespace mfma;
 // instructions per iteration (lanes without a slot of the data re-read a
 // valid address next to the real data into a slot nobody reads, so that no
 // line becomes a hot spot for the whole chip), so "at most q * (kCw + kCa) outstanding"
-// proves that the iteration q steps back has landed, and a barrier after each
-// wave's own wait makes the shared activation chunk complete for all.
+// proves that the iteration q steps back has landed, and (shared columns
+// only) a barrier after each wave's own wait makes the activation chunk
+// complete for all.
 // Outputs: the KS partial results of a row tile meet in LDS and are added in
 // the fixed order 0..KS-1 (deterministic).
 // ---------------------------------------------------------------------------
@@ -72,7 +77,13 @@ struct MfmaGeom {
     static constexpr int kAColSlots = kASlotsUsed | 1;           // odd stride in slots
     static constexpr int kAPartSlots = MP * kAColSlots;
     static constexpr int kASlots = KS * kAPartSlots;
-    static constexpr int kCa = (kASlots + kW * 64 - 1) / (kW * 64);  // copy instructions per wave
+    // One row tile per workgroup (RT = 1): each wave copies its own part's
+    // columns into a private region, so no wave waits for another inside the
+    // loop.  Otherwise the W waves share the copies of the KS parts.
+    static constexpr bool kPriv = RT == 1;
+    static constexpr int kCa = kPriv ? (kAPartSlots + 63) / 64                    // copy instructions
+                                     : (kASlots + kW * 64 - 1) / (kW * 64);      // per wave
+    static constexpr int kAPartBytes = kPriv ? kCa * 1024 : kAPartSlots * 16;   // part stride
     static constexpr int kABufBytes = kCa * kW * 1024;           // per workgroup, per buffer
     static constexpr int kCopies = kCw + kCa;                    // per wave, per iteration
     static constexpr int kStageBytes = kW * kWBufBytes + kABufBytes;
@@ -88,54 +99,85 @@ constexpr size_t mfma_lds_bytes() {
     return (main > red ? main : red) + (size_t)G::kW * CB * MP * 4;
 }
 
-// This wave's weight copies of chunk ch: 16 rows from n0, blocks [ch*CB, ..).
-// Every lane loads a valid address: rows past N, slots past the chunk and
-// chunks past the end are clamped onto real data (that the compute skips).
+// Copy addresses.  A weight copy of chunk ch is a scalar base (row tile n0,
+// block ch * CB) plus a per-lane offset woff[j] fixed for the row tile: lane
+// slot q = j * 64 + lane is 16-byte slot c of row r of the tile (q = r *
+// kWRowSlots + c), with rows past N and slots past the chunk clamped onto
+// real data (that the compute skips).  An activation copy of iteration it is
+// a scalar base (block it * KS * CB) plus a per-lane offset aoff[j] fixed for
+// the launch: slot s = (wave * kCa + j) * 64 + lane of the shared buffer is
+// part p, column m, slot c (clamped the same way; with private parts, slot
+// j * 64 + lane of the wave's own part).  Chunks hold whole groups
+// of 8 blocks (K % 256 == 0) and every offset fits 32 bits (K <= 2^26), so the
+// loop issues each copy with no address arithmetic.
 template <class WF, int CB, int MP, int RT, int KS>
-__device__ __forceinline__ void copy_weights(const uint8_t* __restrict__ Wq, size_t row_bytes, int n0, int N,
-                                             int nblk, int nchunks, int ch, uint8_t* buf, int lane) {
+__device__ __forceinline__ void weight_offsets(uint32_t row_bytes, int rmax, int lane,
+                                               uint32_t (&woff)[MfmaGeom<WF, CB, MP, RT, KS>::kCw]) {
     using G = MfmaGeom<WF, CB, MP, RT, KS>;
-    const int chc = ch < nchunks ? ch : nchunks - 1;
-    const int blk0 = chc * CB;
-    const int cb = nblk - blk0 < CB ? nblk - blk0 : CB;
-    const int used = cb * WF::kBlockBytes / 16;
 #pragma unroll
     for (int j = 0; j < G::kCw; ++j) {
         const int q = j * kWave + lane;
         const int r = q / G::kWRowSlots;
         const int c = q - r * G::kWRowSlots;
-        const int rc = r < 16 ? r : 15;
-        const int n = n0 + rc < N ? n0 + rc : N - 1;
-        const int cc = c < used ? c : used - 1;
-        const uint8_t* src = Wq + (size_t)n * row_bytes + (size_t)blk0 * WF::kBlockBytes + (size_t)cc * 16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(buf + j * 1024), 16, 0, kAuxNonTemporal);
+        int rr = r < 16 ? r : 15;
+        rr = rr < rmax ? rr : rmax;
+        const int cc = c < G::kWSlotsUsed ? c : G::kWSlotsUsed - 1;
+        woff[j] = (uint32_t)rr * row_bytes + (uint32_t)cc * 16;
     }
 }
 
-// This wave's share (instructions wave*kCa .. wave*kCa + kCa - 1) of the
-// activation copies of iteration it: slot s of the buffer is part p, column m,
-// 16-byte slot c of that column's CB blocks.  Clamped like the weights.
 template <class WF, int CB, int MP, int RT, int KS>
-__device__ __forceinline__ void copy_acts(const uint8_t* __restrict__ Xq, int nblk, int nchunks, int M, int it,
-                                          int wave, uint8_t* abuf, int lane) {
+__device__ __forceinline__ void act_offsets(int nblk, int M, int wave, int lane,
+                                            uint32_t (&aoff)[MfmaGeom<WF, CB, MP, RT, KS>::kCa]) {
     using G = MfmaGeom<WF, CB, MP, RT, KS>;
 #pragma unroll
     for (int j = 0; j < G::kCa; ++j) {
         const int s = (wave * G::kCa + j) * kWave + lane;
-        int p = s / G::kAPartSlots;
-        const int e = s - p * G::kAPartSlots;
+        int p = G::kPriv ? wave : s / G::kAPartSlots;
+        const int e = G::kPriv ? j * kWave + lane : s - p * G::kAPartSlots;
         const int m = e / G::kAColSlots;
         const int c = e - m * G::kAColSlots;
         p = p < KS ? p : KS - 1;
-        int ch = it * KS + p;
-        ch = ch < nchunks ? ch : nchunks - 1;
-        const int blk0 = ch * CB;
-        const int cb = nblk - blk0 < CB ? nblk - blk0 : CB;
-        const int used = cb * 36 / 16;
         const int mc = m < M ? m : M - 1;
-        const int cc = c < used ? c : used - 1;
-        const uint8_t* src = Xq + ((size_t)mc * nblk + blk0) * kQ81Bytes + (size_t)cc * 16;
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(abuf + (wave * G::kCa + j) * 1024), 16, 0, 0);
+        const int cc = c < G::kASlotsUsed ? c : G::kASlotsUsed - 1;
+        aoff[j] = ((uint32_t)mc * nblk + (uint32_t)p * CB) * kQ81Bytes + (uint32_t)cc * 16;
+    }
+}
+
+// This wave's weight copies of chunk ch (past the last chunk: the last one
+// again, which the compute skips).
+template <class WF, int CB, int L>
+__device__ __forceinline__ void copy_weights(const uint8_t* __restrict__ Wq, size_t row_bytes, int n0c, int nchunks,
+                                             int ch, const uint32_t* woff, uint8_t* buf) {
+    const int chc = ch < nchunks ? ch : nchunks - 1;   // wave-uniform
+    const uint8_t* src = Wq + (size_t)n0c * row_bytes + (size_t)chc * (CB * WF::kBlockBytes);
+#pragma unroll
+    for (int j = 0; j < L; ++j)
+        __builtin_amdgcn_global_load_lds(src + woff[j], (lds_void_t*)(buf + j * 1024), 16, 0, kAuxNonTemporal);
+}
+
+// This wave's share (instructions wave*kCa .. wave*kCa + kCa - 1) of the
+// activation copies of iteration it.  In an iteration with fewer than KS
+// chunks left, the parts without a chunk (never read) re-read their chunk of
+// the iteration before, or, in a first and only iteration, the last 16 bytes
+// of the columns.
+template <int CB, int KS, int L>
+__device__ __forceinline__ void copy_acts(const uint8_t* __restrict__ Xq, uint32_t xlast, int nchunks, int it,
+                                          int wave, const uint32_t* aoff, uint8_t* abuf) {
+    constexpr uint32_t kIterBytes = KS * CB * kQ81Bytes;
+    const uint32_t base = (uint32_t)it * kIterBytes;
+    if ((it + 1) * KS <= nchunks) {   // wave-uniform
+#pragma unroll
+        for (int j = 0; j < L; ++j)
+            __builtin_amdgcn_global_load_lds(Xq + base + aoff[j], (lds_void_t*)(abuf + (wave * L + j) * 1024),
+                                             16, 0, 0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < L; ++j) {
+            uint32_t o = base + aoff[j];
+            if (o > xlast) o = it > 0 ? o - kIterBytes : xlast;
+            __builtin_amdgcn_global_load_lds(Xq + o, (lds_void_t*)(abuf + (wave * L + j) * 1024), 16, 0, 0);
+        }
     }
 }
 
@@ -176,16 +218,22 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
     constexpr size_t kTabOff = mfma_lds_bytes<WF, CB, MP, RT, KS, DEPTH>() - (size_t)G::kW * CB * MP * 4;
     float* const d8tab = reinterpret_cast<float*>(lds + kTabOff) + wave * CB * MP;
 
+    const uint32_t xlast = (uint32_t)M * nblk * kQ81Bytes - 16;   // the columns' last 16 bytes
+    uint32_t aoff[G::kCa];
+    act_offsets<WF, CB, MP, RT, KS>(nblk, M, wave, lane, aoff);
+
     for (int grp = blockIdx.x; grp < ngroups; grp += gridDim.x) {   // workgroup-uniform
         const int n0 = (grp * RT + tile) * 16;
-        auto issue = [&](int it2, int d) {
-            copy_weights<WF, CB, MP, RT, KS>(Wq, row_bytes, n0, N, nblk, nchunks, it2 * KS + part, wbuf(d), lane);
-            copy_acts<WF, CB, MP, RT, KS>(Xq, nblk, nchunks, M, it2, wave, abuf(d), lane);
-        };
+        const int n0c = n0 < N ? n0 : N - 1;   // tiles past N re-read row N - 1
+        uint32_t woff[G::kCw];
+        weight_offsets<WF, CB, MP, RT, KS>((uint32_t)row_bytes, N - 1 - n0c, lane, woff);
         lds_barrier();   // the previous group's reads of every buffer are done
 #pragma unroll
         for (int d = 0; d < DEPTH - 1; ++d)
-            if (d < iters) issue(d, d);
+            if (d < iters) {
+                copy_weights<WF, CB, G::kCw>(Wq, row_bytes, n0c, nchunks, d * KS + part, woff, wbuf(d));
+                copy_acts<CB, KS, G::kCa>(Xq, xlast, nchunks, d, wave, aoff, abuf(d));
+            }
 
         f32x4 acc[NT];
 #pragma unroll
@@ -193,22 +241,26 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
 
         int slot = 0;
         for (int it = 0; it < iters; ++it) {
-            lds_barrier();   // every wave is done with the buffer the next copies overwrite
+            // shared columns: every wave is done with the buffer the next
+            // copies overwrite (private buffers: the wave's own reads of it
+            // have returned, since their results were used)
+            if constexpr (!G::kPriv) lds_barrier();
             const int ahead = it + DEPTH - 1;
             if (ahead < iters) {
                 int aslot = slot + DEPTH - 1;
                 if (aslot >= DEPTH) aslot -= DEPTH;
-                issue(ahead, aslot);
+                copy_weights<WF, CB, G::kCw>(Wq, row_bytes, n0c, nchunks, ahead * KS + part, woff, wbuf(aslot));
+                copy_acts<CB, KS, G::kCa>(Xq, xlast, nchunks, ahead, wave, aoff, abuf(aslot));
             }
             const int left = iters - 1 - it;
             wait_iterations_ahead<G::kCopies, DEPTH>(left < DEPTH - 1 ? left : DEPTH - 1);
-            lds_barrier();   // every wave's copies of this iteration have landed
+            if constexpr (!G::kPriv) lds_barrier();   // every wave's copies of this iteration have landed
 
             const int ch = it * KS + part;
             if (ch < nchunks) {   // wave-uniform
                 const int cb = nblk - ch * CB < CB ? nblk - ch * CB : CB;   // a multiple of 8
                 const uint8_t* rowp = wbuf(slot) + rn * G::kWRowSlots * 16;
-                const uint8_t* ap = abuf(slot) + part * G::kAPartSlots * 16;
+                const uint8_t* ap = abuf(slot) + part * G::kAPartBytes;
                 // d8 of the chunk as fp32, [block][column], converted once per wave
                 // (the same wave reads it back: LDS operations of a wave are in order)
 #pragma unroll
@@ -305,6 +357,7 @@ template <class WF, int CB, int MP, int RT, int KS, int DEPTH>
 hipError_t launch_mfma_cfg(const void* Wq, const void* Xq, float* Y, int N, int K, int M, int grid, hipStream_t s) {
     const size_t lds = mfma_lds_bytes<WF, CB, MP, RT, KS, DEPTH>();
     if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
+    if ((K >> 5) % CB != 0 || K > (1 << 26)) return hipErrorInvalidValue;   // whole chunks, 32-bit offsets
     const int groups = (N + 16 * RT - 1) / (16 * RT);
     const int g = grid ? grid : groups;
     hipLaunchKernelGGL((k_qmfma<WF, CB, MP, RT, KS, DEPTH>), dim3(g), dim3(64 * RT * KS), lds, s,
@@ -349,22 +402,23 @@ hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float
         DEPTH = (unroll / 10) % 10;
         CB = (unroll % 10) * 8;
     } else {
-        // Measured on MI355X (decoder shapes, M = 2..24).  Q4_0: split K over 8
-        // waves (4 for 9..16 columns) when there are few row tiles; share each
-        // activation chunk between two row tiles when there are many.
+        // Measured on MI355X (decoder shapes, M = 2..24), both formats: split K
+        // over 8 waves (4 for 13..16 columns, and for 9..12 except Q4_0 rows
+        // longer than 8192) when there are few row tiles, two chunks deep (one beyond 16
+        // columns, whose chunks fill the LDS); share each activation chunk
+        // between row tiles when there are many.
         const int tiles = (N + 15) / 16;
         CB = 8;
-        if (WF::kBlockBytes == 34) {
-            // Q8_0 (measured): its weight buffers are twice those of Q4_0, so
-            // fewer parts of K share a workgroup's LDS.
-            DEPTH = 2;
-            if (tiles <= 512) { RT = 1; KS = 4; }
-            else if (M <= 16) { RT = 2; KS = 2; }
-            else { RT = 4; KS = 2; }
-        } else if (tiles <= 512) {
+        if (tiles <= 512) {
             RT = 1;
-            KS = (M <= 8 || M > 16) ? 8 : 4;
+            KS = (M <= 8 || M > 16 || (M <= 12 && K > 8192 && WF::kBlockBytes == 18)) ? 8 : 4;
             DEPTH = M > 16 ? 1 : 2;
+        } else if (WF::kBlockBytes == 34) {
+            // Q8_0: its weight buffers are twice those of Q4_0, so fewer row
+            // tiles share a workgroup's LDS.
+            DEPTH = 2;
+            if (M <= 16) { RT = 2; KS = 2; }
+            else { RT = 4; KS = 2; }
         } else {
             DEPTH = 2;
             if (M <= 4) { RT = 2; KS = 4; }

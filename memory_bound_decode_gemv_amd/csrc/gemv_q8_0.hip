@@ -150,12 +150,14 @@ hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int
     int depth = cfg ? cfg->unroll : 0;
     if (variant == 0) {
         // Measured on MI355X over the decoder shapes, the 70B MLP and M =
-        // 1..24: up to eight columns stream rows through LDS in 64-pair units
-        // while M * ceil(K / 4096) <= 8 (at most four columns for matrices of
-        // 1024 rows or fewer, where eight would outrun twelve on the matrix
-        // cores); the rest take the matrix cores, with the columns resident
-        // in LDS from twelve columns on for matrices of many row tiles.
-        variant = S <= 4 && M * S <= 8 && (N > 1024 || M <= 4) ? DG_VARIANT_Q8_UNITS
+        // 1..24: up to four columns stream rows through LDS in 64-pair units
+        // while M * ceil(K / 4096) <= 8, and so do up to eight columns of a
+        // matrix of at most 1024 rows or of more than 512 row tiles (in
+        // between, the matrix cores' parts of K run every CU); the rest take
+        // the matrix cores, with the columns resident in LDS from twelve
+        // columns on for matrices of many row tiles.
+        const bool units_m = M <= 4 || (M <= 8 && (N <= 1024 || N > 8192));
+        variant = S <= 4 && M * S <= 8 && units_m                ? DG_VARIANT_Q8_UNITS
                   : (N >= 8192 && K <= 4096 && M >= 12)      ? DG_VARIANT_Q8_MFMA_RES
                                                              : DG_VARIANT_Q8_MFMA;
     }

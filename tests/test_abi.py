@@ -67,6 +67,7 @@ def test_gemv_f16_rejects_before_launch(lib, args, expect):
 @pytest.mark.parametrize("args,expect", [
     ((A16, A16, A16, 4, 100, 1), 3),      # K % 256
     ((A16, A16, A16, 4, 256, 25), 3),     # M > 24
+    ((A16, A16, A16, 4, (1 << 26) + 256, 1), 3),   # K > 2^26
     ((A16, A16, A16, 4, 256, -1), 3),
     ((None, A16, A16, 4, 256, 1), 1),
     ((A16, None, A16, 4, 256, 1), 1),

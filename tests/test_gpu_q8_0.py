@@ -134,12 +134,25 @@ def test_q8_0_70b_mlp_shape_sampled_rows(dg, dev, orc):
     assert_close(got[0, rows], ref[0], TOL, "28672x8192 sampled")
 
 
-@pytest.mark.parametrize("N,K", [(4096, 4096), (14336, 4096), (4096, 14336)])
-@pytest.mark.parametrize("M", [2, 8, 16, 24])
+@pytest.mark.parametrize("N,K", [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)])
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 12, 16, 24])
 def test_q8_0_decoder_layer_shapes_sampled_rows(dg, dev, orc, N, K, M):
     Wq, Xq = _operands(orc, 3, N, K, M)
     got = _gpu(dg, dev, Wq, Xq, N, K, M)
     rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 97)), [N - 1]]))
+    ref = orc.gemv_q8_0_q8_1(Wq.reshape(N, -1)[rows], Xq, len(rows), K, M)
+    assert_close(got[:, rows], ref, TOL, f"{N}x{K} M={M}")
+
+
+# The default kernel and configuration follow the column count, the row-tile
+# count and the row length; these three shapes take every branch of that
+# choice for every M.
+@pytest.mark.parametrize("N,K", [(1024, 4096), (14336, 4096), (4096, 14336)])
+@pytest.mark.parametrize("M", list(range(1, 25)))
+def test_q8_0_default_launch_every_column_count(dg, dev, orc, N, K, M):
+    Wq, Xq = _operands(orc, 3, N, K, M)
+    got = _gpu(dg, dev, Wq, Xq, N, K, M)
+    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 29)), [N - 1]]))
     ref = orc.gemv_q8_0_q8_1(Wq.reshape(N, -1)[rows], Xq, len(rows), K, M)
     assert_close(got[:, rows], ref, TOL, f"{N}x{K} M={M}")
 
