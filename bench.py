@@ -589,7 +589,7 @@ def suite_q4_m1(dg, torch, emit, ceil_gbps):
 
 # matrix-core configurations (RT, KS, DEPTH, CB) -> the largest column count they serve;
 # launch override unroll = RT*10000 + KS*100 + DEPTH*10 + CB/8
-MFMA_BUILT = {(1, 16, 1, 8): 16, (4, 4, 2, 8): 8, (1, 8, 2, 8): 16,
+MFMA_BUILT = {(1, 16, 1, 8): 8, (4, 4, 2, 8): 16, (1, 8, 2, 8): 16,
               (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (2, 4, 2, 8): 24, (4, 2, 2, 8): 24, (8, 1, 2, 8): 24,
               (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24, (1, 4, 2, 8): 24}
 
@@ -632,7 +632,7 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
 
 
 # matrix-core configurations built for Q8_0 weights (larger weight buffers than Q4_0)
-MFMA_BUILT_Q8 = {(1, 16, 1, 8): 8, (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (1, 8, 2, 8): 8, (2, 4, 2, 8): 16,
+MFMA_BUILT_Q8 = {(1, 16, 1, 8): 8, (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (1, 8, 2, 8): 16, (2, 4, 2, 8): 24,
                  (4, 2, 2, 8): 24, (8, 1, 2, 8): 24, (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24,
                  (1, 4, 2, 8): 24}
 

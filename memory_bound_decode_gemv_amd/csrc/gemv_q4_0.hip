@@ -264,7 +264,7 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
         // eight columns of a matrix of at most 1024 rows, take the dot4
         // kernel (the matrix cores' fixed cost per 16 x 16 tile does not pay
         // there); the rest take the matrix cores, with the columns resident
-        // in LDS from eight columns on for matrices of many row tiles.
+        // in LDS for 9..16 columns of matrices of many row tiles.
         if (M == 1) {
             variant = S > 4 ? DG_VARIANT_Q4_LDS : (N >= 16384 && S <= 2 ? DG_VARIANT_Q4_LDSROW : DG_VARIANT_Q4_UNITS);
         } else if (M <= 4 && M * S <= 8 && (N > 1024 || M <= 2)) {
@@ -272,7 +272,7 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
         } else if (M == 2 || (N <= 1024 && M <= 8)) {
             variant = DG_VARIANT_Q4_LDS;
             lds_rows = N > 2048 ? 2 : 1;
-        } else if (N >= 8192 && K <= 4096 && M >= 8) {
+        } else if (N >= 8192 && K <= 4096 && M >= 9 && M <= 16) {
             variant = DG_VARIANT_Q4_MFMA_RES;
         } else {
             variant = DG_VARIANT_Q4_MFMA;

@@ -22,7 +22,9 @@ using namespace mfma;
 //   B (32 x 16, int8)  = the 4-bit codes (0..15) of 16 weight rows,
 //   D0 = A * (-8)      = -8 * sum(q8) per column (a second MFMA against a
 //                        constant operand: the offset of q - 8, exact),
-//   D  = A * B + D0    = the exact int32 block sums, scaled by d4 * d8 in fp32.
+//   D  = A * B + D0    = the exact int32 block sums, scaled by d4 * d8 in fp32,
+//   S  = d8 (x) d4     = those 16 x 16 scale products, from one f16 MFMA
+//                        of the raw binary16 scales (exact in fp32).
 // The order of the 32 terms inside the instruction is irrelevant (integers);
 // each lane supplies A and B bytes for the same 8 k-slots: lane group g = l/16
 // carries weights 4g..4g+3 (low nibbles of code dword g) and 16+4g..16+4g+3
@@ -89,14 +91,13 @@ struct MfmaGeom {
     static constexpr int kStageBytes = kW * kWBufBytes + kABufBytes;
 };
 
-// LDS: DEPTH stages, then one fp32 table of d8 per wave (CB x MP scales of
-// the chunk it computes); after the loop the stages hold the KS partial sums.
+// LDS: DEPTH stages; after the loop they hold the KS partial sums.
 template <class WF, int CB, int MP, int RT, int KS, int DEPTH>
 constexpr size_t mfma_lds_bytes() {
     using G = MfmaGeom<WF, CB, MP, RT, KS>;
     const size_t main = (size_t)DEPTH * G::kStageBytes;
     const size_t red = (size_t)G::kW * G::kNT * 4 * 64 * 4;   // partial sums of the KS parts
-    return (main > red ? main : red) + (size_t)G::kW * CB * MP * 4;
+    return main > red ? main : red;
 }
 
 // Copy addresses.  A weight copy of chunk ch is a scalar base (row tile n0,
@@ -215,8 +216,7 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
     const int acol = MP < 16 ? (rn & (MP - 1)) : rn;
     auto wbuf = [&](int d) { return lds + d * G::kStageBytes + wave * G::kWBufBytes; };
     auto abuf = [&](int d) { return lds + d * G::kStageBytes + G::kW * G::kWBufBytes; };
-    constexpr size_t kTabOff = mfma_lds_bytes<WF, CB, MP, RT, KS, DEPTH>() - (size_t)G::kW * CB * MP * 4;
-    float* const d8tab = reinterpret_cast<float*>(lds + kTabOff) + wave * CB * MP;
+    const uint32_t dwidth = g == 0 ? 16u : 0u;   // lane group 0 feeds d4 to k-slot 0 of the scale products
 
     const uint32_t xlast = (uint32_t)M * nblk * kQ81Bytes - 16;   // the columns' last 16 bytes
     uint32_t aoff[G::kCa];
@@ -261,38 +261,33 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
                 const int cb = nblk - ch * CB < CB ? nblk - ch * CB : CB;   // a multiple of 8
                 const uint8_t* rowp = wbuf(slot) + rn * G::kWRowSlots * 16;
                 const uint8_t* ap = abuf(slot) + part * G::kAPartBytes;
-                // d8 of the chunk as fp32, [block][column], converted once per wave
-                // (the same wave reads it back: LDS operations of a wave are in order)
-#pragma unroll
-                for (int i = 0; i < (CB * MP + kWave - 1) / kWave; ++i) {
-                    const int e = i * kWave + lane;
-                    if (CB * MP % kWave == 0 || e < CB * MP) {
-                        const int b = e / MP, m = e - (e / MP) * MP;
-                        const uint32_t dw = *reinterpret_cast<const uint32_t*>(
-                            ap + (m * G::kAColSlots * 16 + b * kQ81Bytes));
-                        d8tab[e] = half_lo_to_f32(dw);
-                    }
-                }
                 // Groups of 8 blocks in three phases, so that the 16 (or 32)
                 // matrix-core operations of a group are independent of one
                 // another and of the scaling (each block has its own result
                 // registers): operands, then every MFMA, then the fp32 scaling.
                 for (int o = 0; o < cb; o += 8) {
                     long bop[8];
-                    float d4[8];
+                    uint32_t h4[8];
 #pragma unroll
-                    for (int p = 0; p < 4; ++p)   // block pairs o + 2p, o + 2p + 1
-                        WF::decode(reinterpret_cast<const uint32_t*>(rowp + ((o >> 1) + p) * 2 * WF::kBlockBytes), g,
-                                   bop + 2 * p, d4 + 2 * p);
+                    for (int p = 0; p < 4; ++p) {   // block pairs o + 2p, o + 2p + 1
+                        const uint32_t* wp =
+                            reinterpret_cast<const uint32_t*>(rowp + ((o >> 1) + p) * 2 * WF::kBlockBytes);
+                        float dunused[2];
+                        WF::decode(wp, g, bop + 2 * p, dunused);
+                        WF::scale_bits(wp, dwidth, h4 + 2 * p);
+                    }
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
                         long aop[8];
+                        uint32_t a8[8];
 #pragma unroll
                         for (int i = 0; i < 8; ++i) {
-                            // A: code dwords g and 4 + g of column 16t + acol, block o + i
+                            // A: code dwords g and 4 + g of column 16t + acol, block o + i,
+                            // and the block's binary16 d8 (the low half of its first dword)
                             const uint32_t* ab = reinterpret_cast<const uint32_t*>(
-                                ap + ((16 * t + acol) * G::kAColSlots * 16 + (o + i) * kQ81Bytes + 4 * g));
-                            aop[i] = (long)((uint64_t)ab[1] | ((uint64_t)ab[5] << 32));
+                                ap + ((16 * t + acol) * G::kAColSlots * 16 + (o + i) * kQ81Bytes));
+                            aop[i] = (long)((uint64_t)ab[1 + g] | ((uint64_t)ab[5 + g] << 32));
+                            a8[i] = ab[0] & 0xFFFFu;
                         }
                         i32x4 dsum[8];
 #pragma unroll
@@ -303,15 +298,13 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
 #pragma unroll
                         for (int i = 0; i < 8; ++i)
                             dsum[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[i], bop[i], dsum[i], 0, 0, 0);
-                        // d8 of output columns 16t + 4g + r, r = 0..3 (columns past MP wrap)
-                        const int c0 = MP < 16 ? ((4 * g) & (MP - 1)) : 16 * t + 4 * g;
+                        f32x4 sc[8];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            const f32x4 d8 = *reinterpret_cast<const f32x4*>(d8tab + (o + i) * MP + c0);
+                        for (int i = 0; i < 8; ++i) sc[i] = scale_outer(a8[i], h4[i]);
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                acc[t][r] = fmaf((float)dsum[i][r], d4[i] * d8[r], acc[t][r]);
-                        }
+                        for (int i = 0; i < 8; ++i)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)dsum[i][r], sc[i][r], acc[t][r]);
                     }
                 }
             }
@@ -368,9 +361,12 @@ hipError_t launch_mfma_cfg(const void* Wq, const void* Xq, float* Y, int N, int 
 template <class WF, int CB, int MP, int RT, int KS, int DEPTH>
 constexpr bool mfma_builds() {
     // the stages fit the LDS of one workgroup, the wait counts fit the vmcnt
-    // field, and 16-wave workgroups (128 VGPRs per lane) are kept to 16 columns
+    // field, and 16-wave workgroups (128 VGPRs per lane) are kept to 16
+    // columns, and to 8 when each of the 16 waves has a part of K (more
+    // activation copies per wave)
     return mfma_lds_bytes<WF, CB, MP, RT, KS, DEPTH>() <= 160 * 1024 &&
-           MfmaGeom<WF, CB, MP, RT, KS>::kCopies * (DEPTH - 1) <= 63 && (RT * KS < 16 || MP <= 16);
+           MfmaGeom<WF, CB, MP, RT, KS>::kCopies * (DEPTH - 1) <= 63 && (RT * KS < 16 || MP <= 16) &&
+           (KS < 16 || MP <= 8);
 }
 
 // The built configurations for one padded column count MP.
@@ -402,27 +398,27 @@ hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float
         DEPTH = (unroll / 10) % 10;
         CB = (unroll % 10) * 8;
     } else {
-        // Measured on MI355X (decoder shapes, M = 2..24), both formats: split K
-        // over 8 waves (4 for 13..16 columns, and for 9..12 except Q4_0 rows
-        // longer than 8192) when there are few row tiles, two chunks deep (one beyond 16
-        // columns, whose chunks fill the LDS); share each activation chunk
-        // between row tiles when there are many.
+        // Measured on MI355X (decoder shapes, M = 2..24), both formats.  Up to
+        // 512 row tiles: one tile per workgroup, K split over 8 waves up to 8
+        // columns and beyond 16 on rows up to 8192 (one chunk deep there, as
+        // the chunks of 32 columns fill the LDS), else over 4 waves two deep.
+        // More row tiles: tiles share each activation chunk.
         const int tiles = (N + 15) / 16;
         CB = 8;
         if (tiles <= 512) {
             RT = 1;
-            KS = (M <= 8 || M > 16 || (M <= 12 && K > 8192 && WF::kBlockBytes == 18)) ? 8 : 4;
-            DEPTH = M > 16 ? 1 : 2;
+            const bool wide = M > 16 && K <= 8192;
+            KS = (M <= 8 || wide) ? 8 : 4;
+            DEPTH = wide ? 1 : 2;
         } else if (WF::kBlockBytes == 34) {
             // Q8_0: its weight buffers are twice those of Q4_0, so fewer row
             // tiles share a workgroup's LDS.
             DEPTH = 2;
             if (M <= 16) { RT = 2; KS = 2; }
-            else { RT = 4; KS = 2; }
+            else { RT = 4; KS = 1; }
         } else {
             DEPTH = 2;
             if (M <= 4) { RT = 2; KS = 4; }
-            else if (M <= 8) { RT = 4; KS = 2; }
             else { RT = 2; KS = 2; }
         }
     }

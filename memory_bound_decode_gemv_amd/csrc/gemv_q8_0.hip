@@ -154,11 +154,11 @@ hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int
         // while M * ceil(K / 4096) <= 8, and so do up to eight columns of a
         // matrix of at most 1024 rows or of more than 512 row tiles (in
         // between, the matrix cores' parts of K run every CU); the rest take
-        // the matrix cores, with the columns resident in LDS from twelve
-        // columns on for matrices of many row tiles.
+        // the matrix cores, with the columns resident in LDS for 12..16
+        // columns of matrices of many row tiles.
         const bool units_m = M <= 4 || (M <= 8 && (N <= 1024 || N > 8192));
         variant = S <= 4 && M * S <= 8 && units_m                ? DG_VARIANT_Q8_UNITS
-                  : (N >= 8192 && K <= 4096 && M >= 12)      ? DG_VARIANT_Q8_MFMA_RES
+                  : (N >= 8192 && K <= 4096 && M >= 12 && M <= 16) ? DG_VARIANT_Q8_MFMA_RES
                                                              : DG_VARIANT_Q8_MFMA;
     }
     if (variant == DG_VARIANT_Q8_UNITS) {

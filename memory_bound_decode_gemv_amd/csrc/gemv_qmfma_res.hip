@@ -6,14 +6,14 @@
 // block and per tile of 16 rows x 16 columns, v_mfma_i32_16x16x32_i8 gives
 // the exact int32 block sums (A = 16 columns of q8 codes, B = 16 rows of
 // codes, Q4_0's -8 offset as a second MFMA against a constant -8 operand),
-// and each sum is scaled by d4 * d8 in fp32 and added in block order.
+// and each sum is scaled in fp32 by d8 * d4 (the 16 x 16 products from one
+// f16 MFMA of the raw binary16 scales, exact) and added in block order.
 //
 // What differs is the data flow, chosen from counters of the streaming kernel
 // (one or two waves per SIMD, two workgroup barriers per 8-block chunk, a
 // quarter of the vector instructions spent on copy addresses):
 //  * every workgroup copies all M activation columns (raw Q8_1 blocks) into
-//    LDS once, with the d8 scales converted to an fp32 table [block][column],
-//    and keeps them for every row tile it computes; workgroups are persistent
+//    LDS once and keeps them for every row tile it computes; workgroups are persistent
 //    and take row groups b, b + grid, ...;
 //  * a workgroup is RT x KS waves: RT row tiles of 16 rows, each row's K split
 //    into KS equal parts.  Wave (t, p) owns part p of tile t; it walks its
@@ -44,13 +44,12 @@ struct ResGeom {
     static constexpr int kBufBytes = kL * 1024;             // per-wave transpose buffer
 };
 
-// LDS bytes of one workgroup: the activation columns (cstr bytes each), the
-// fp32 d8 table, one transpose buffer per wave, and the partial sums of the
-// KS - 1 upper parts of each row tile.
+// LDS bytes of one workgroup: the activation columns (cstr bytes each), one
+// transpose buffer per wave, and the partial sums of the KS - 1 upper parts
+// of each row tile.
 template <class WF>
-__host__ __device__ constexpr size_t res_lds_bytes(int M, int cstr, int nblk, int NT, int RT, int KS) {
-    return (size_t)M * cstr + (size_t)nblk * 16 * NT * 4 + (size_t)RT * KS * ResGeom<WF>::kBufBytes +
-           (size_t)RT * (KS - 1) * NT * 1024;
+__host__ __device__ constexpr size_t res_lds_bytes(int M, int cstr, int NT, int RT, int KS) {
+    return (size_t)M * cstr + (size_t)RT * KS * ResGeom<WF>::kBufBytes + (size_t)RT * (KS - 1) * NT * 1024;
 }
 
 // Bytes per activation column in LDS: the column's 36-byte blocks rounded up
@@ -101,10 +100,9 @@ k_qres(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __
     const int cstr = res_col_bytes(nblk);
     const int ngroups = (N + 16 * RT - 1) / (16 * RT);
     uint8_t* const acts = lds;
-    float* const d8tab = reinterpret_cast<float*>(lds + (size_t)M * cstr);
-    uint8_t* const tbuf = reinterpret_cast<uint8_t*>(d8tab + (size_t)nblk * MP) + wave * G::kBufBytes;
-    float* const red = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(d8tab + (size_t)nblk * MP) +
-                                                W * G::kBufBytes);
+    uint8_t* const tbuf = lds + (size_t)M * cstr + wave * G::kBufBytes;
+    float* const red = reinterpret_cast<float*>(lds + (size_t)M * cstr + W * G::kBufBytes);
+    const uint32_t dwidth = g == 0 ? 16u : 0u;   // lane group 0 feeds d4 to k-slot 0 of the scale products
 
     // this workgroup's row groups, and its items (row group, chunk) in order
     const int mygroups = (int)blockIdx.x < ngroups ? (ngroups - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
@@ -159,13 +157,6 @@ k_qres(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __
     }
 
     lds_barrier();   // every column is in LDS
-    // d8 of every block and (padded) column as fp32: [block][column]
-    for (int e = threadIdx.x; e < nblk * MP; e += 64 * W) {
-        const int b = e / MP, m = e - (e / MP) * MP;
-        const int mc = m < M ? m : M - 1;
-        d8tab[e] = half_lo_to_f32(*reinterpret_cast<const uint32_t*>(acts + (size_t)mc * cstr + b * kQ81Bytes));
-    }
-    lds_barrier();
 
     int acol[NT];   // the activation column this lane feeds to tile t (padded columns re-read M - 1)
 #pragma unroll
@@ -191,19 +182,24 @@ k_qres(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __
             constexpr int kH = kCB / 2;
             const int blk0 = item_blk0(i) + h * kH;
             long bop[kH];
-            float d4[kH];
+            uint32_t h4[kH];
 #pragma unroll
-            for (int p = 0; p < kH / 2; ++p)
-                WF::decode(reinterpret_cast<const uint32_t*>(rowp + (h * kH / 2 + p) * 2 * WF::kBlockBytes), g,
-                           bop + 2 * p, d4 + 2 * p);
+            for (int p = 0; p < kH / 2; ++p) {
+                const uint32_t* wp = reinterpret_cast<const uint32_t*>(rowp + (h * kH / 2 + p) * 2 * WF::kBlockBytes);
+                float dunused[2];
+                WF::decode(wp, g, bop + 2 * p, dunused);
+                WF::scale_bits(wp, dwidth, h4 + 2 * p);
+            }
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const uint8_t* ap = acts + (size_t)acol[t] * cstr + (size_t)blk0 * kQ81Bytes + 4 + 4 * g;
+                const uint8_t* ap = acts + (size_t)acol[t] * cstr + (size_t)blk0 * kQ81Bytes;
                 long aop[kH];
+                uint32_t a8[kH];   // the block's binary16 d8
 #pragma unroll
                 for (int b = 0; b < kH; ++b) {
                     const uint32_t* ab = reinterpret_cast<const uint32_t*>(ap + b * kQ81Bytes);
-                    aop[b] = (long)((uint64_t)ab[0] | ((uint64_t)ab[4] << 32));
+                    aop[b] = (long)((uint64_t)ab[1 + g] | ((uint64_t)ab[5 + g] << 32));
+                    a8[b] = ab[0] & 0xFFFFu;
                 }
                 i32x4 dsum[kH];
 #pragma unroll
@@ -214,13 +210,13 @@ k_qres(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __
 #pragma unroll
                 for (int b = 0; b < kH; ++b)
                     dsum[b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[b], bop[b], dsum[b], 0, 0, 0);
-                const float* dp = d8tab + (size_t)blk0 * MP + 16 * t + 4 * g;
+                f32x4 sc[kH];
 #pragma unroll
-                for (int b = 0; b < kH; ++b) {
-                    const f32x4 d8 = *reinterpret_cast<const f32x4*>(dp + b * MP);
+                for (int b = 0; b < kH; ++b) sc[b] = scale_outer(a8[b], h4[b]);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)dsum[b][r], d4[b] * d8[r], acc[t][r]);
-                }
+                for (int b = 0; b < kH; ++b)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)dsum[b][r], sc[b][r], acc[t][r]);
             }
         }
         if (i - (i / nch) * nch == nch - 1) {   // the tile's last chunk: combine the parts, store
@@ -272,7 +268,7 @@ template <class WF, int NT, int RT, int KS, int P>
 hipError_t launch_res_cfg(const void* Wq, const void* Xq, float* Y, int N, int K, int M, int grid, hipStream_t s) {
     const int nblk = K / 32;
     if (nblk % (KS * kCB) != 0) return hipErrorInvalidValue;
-    const size_t lds = res_lds_bytes<WF>(M, res_col_bytes(nblk), nblk, NT, RT, KS);
+    const size_t lds = res_lds_bytes<WF>(M, res_col_bytes(nblk), NT, RT, KS);
     const size_t cap = device_max_lds_per_block();
     if (lds > cap) return hipErrorInvalidValue;
     const int groups = (N + 16 * RT - 1) / (16 * RT);
@@ -288,11 +284,12 @@ hipError_t launch_res_cfg(const void* Wq, const void* Xq, float* Y, int N, int K
     return hipGetLastError();
 }
 
-// 16-wave workgroups (128 VGPRs per lane) are built for Q8_0 only with one
-// column tile: its 5-load chunks and two tiles would spill.
+// 16-wave workgroups (128 VGPRs per lane) with two column tiles are built
+// only for Q4_0 with one row tile: Q8_0's 5-load chunks, or several row
+// tiles' offsets, would spill.
 template <class WF, int NT, int RT, int KS>
 constexpr bool res_builds() {
-    return !(WF::kBlockBytes == 34 && NT == 2 && RT * KS == 16);
+    return !(NT == 2 && RT * KS == 16 && (WF::kBlockBytes == 34 || RT > 1));
 }
 
 template <class WF, int NT>
@@ -333,7 +330,7 @@ hipError_t launch_res(int M, int unroll, const void* Wq, const void* Xq, float* 
         else { RT = 1; KS = 8; }
         const int nblk = K / 32, NT = M <= 16 ? 1 : 2;
         if (nblk % (KS * kCB) != 0 ||
-            res_lds_bytes<WF>(M, res_col_bytes(nblk), nblk, NT, RT, KS) > device_max_lds_per_block()) {
+            res_lds_bytes<WF>(M, res_col_bytes(nblk), NT, RT, KS) > device_max_lds_per_block()) {
             RT = 1;
             KS = 4;
         }
@@ -344,11 +341,6 @@ hipError_t launch_res(int M, int unroll, const void* Wq, const void* Xq, float* 
 }
 
 }  // namespace
-
-size_t q4_res_lds_bytes(int M, int K, int unroll) {
-    const int nblk = K / 32, RT = unroll / 10000, KS = (unroll / 100) % 100;
-    return res_lds_bytes<FmtQ4_0>(M, res_col_bytes(nblk), nblk, M <= 16 ? 1 : 2, RT, KS);
-}
 
 hipError_t launch_q4_res(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
                          hipStream_t s) {

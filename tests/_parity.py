@@ -33,8 +33,8 @@ def assert_close(got, ref, tol, what=""):
 # unroll = RT*10000 + KS*100 + P*10.  A configuration runs a shape when K/32
 # is a multiple of 8*KS and the workgroup's LDS fits (160 KiB on gfx950):
 # the M activation columns (36-byte blocks, odd number of 16-byte slots per
-# column), the fp32 d8 table, one transpose buffer per wave and the partial
-# sums of the upper K parts.
+# column), one transpose buffer per wave and the partial sums of the upper K
+# parts.
 RES_CFGS = [(1, 16, 2), (2, 8, 2), (4, 4, 2), (1, 8, 2), (2, 4, 2), (4, 2, 2), (8, 1, 2), (1, 4, 2), (2, 2, 2),
             (4, 1, 2), (1, 8, 3), (2, 4, 3), (1, 4, 3)]
 LDS_PER_WORKGROUP = 160 * 1024
@@ -49,12 +49,12 @@ def res_runs(block_bytes, rt, ks, M, K):
     if nblk % (8 * ks) or M < 1 or M > 32:
         return False
     nt = 1 if M <= 16 else 2
-    if block_bytes == 34 and nt == 2 and rt * ks == 16:
+    if nt == 2 and rt * ks == 16 and (block_bytes == 34 or rt > 1):
         return False   # not built: it would spill
     g = 8 * block_bytes // 16
     buf = -(-16 * g // 64) * 1024
     cstr = ((nblk * 36 // 16) | 1) * 16
-    lds = M * cstr + nblk * 16 * nt * 4 + rt * ks * buf + rt * (ks - 1) * nt * 1024
+    lds = M * cstr + rt * ks * buf + rt * (ks - 1) * nt * 1024
     return lds <= LDS_PER_WORKGROUP
 
 

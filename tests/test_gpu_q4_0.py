@@ -149,7 +149,7 @@ def test_q4_0_lds_row_copy_shapes(dg, dev, orc, N, K, launch):
 # Matrix-core configurations the library builds: (RT row tiles, KS parts of K,
 # DEPTH, CB) -> the largest column count they serve (their LDS must fit one
 # workgroup).  Launch override: unroll = RT*10000 + KS*100 + DEPTH*10 + CB/8.
-MFMA_TABLE = {(1, 16, 1, 8): 16, (4, 4, 2, 8): 8, (1, 8, 2, 8): 16,
+MFMA_TABLE = {(1, 16, 1, 8): 8, (4, 4, 2, 8): 16, (1, 8, 2, 8): 16,
               (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (2, 4, 2, 8): 24, (4, 2, 2, 8): 24, (8, 1, 2, 8): 24,
               (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24, (1, 4, 2, 8): 24}
 

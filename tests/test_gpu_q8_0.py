@@ -20,7 +20,7 @@ TOL = 1e-3   # per-row floored relative error vs the oracle
 
 # Matrix-core configurations built for Q8_0: (RT, KS, DEPTH, CB) -> the
 # largest column count they serve (their LDS must fit one workgroup).
-MFMA_TABLE = {(1, 16, 1, 8): 8, (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (1, 8, 2, 8): 8, (2, 4, 2, 8): 16,
+MFMA_TABLE = {(1, 16, 1, 8): 8, (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (1, 8, 2, 8): 16, (2, 4, 2, 8): 24,
               (4, 2, 2, 8): 24, (8, 1, 2, 8): 24, (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24,
               (1, 4, 2, 8): 24}
 
