@@ -144,6 +144,26 @@ def test_q8_0_decoder_layer_shapes_sampled_rows(dg, dev, orc, N, K, M):
     assert_close(got[:, rows], ref, TOL, f"{N}x{K} M={M}")
 
 
+# Scales below the binary16 normal range (|w| ~ 1e-5 gives weight scales of
+# about 1e-6, |x| ~ 1e-4 activation scales of about 1e-6): every kernel family
+# keeps them, the matrix-core kernels included, which multiply the raw
+# binary16 scales on the f16 matrix cores.
+@pytest.mark.parametrize("M,launch", [(1, None), (3, None), (12, None), (24, None), (12, dict(variant=24)),
+                                      (24, dict(variant=24))])
+def test_q8_0_subnormal_scales(dg, dev, orc, M, launch):
+    N, K = 300, 4096
+    Wq = orc.quantize_q8_0(synth.normal_f32((900, synth.KIND_W, 0, 0), (N, K)) * np.float32(1e-5))
+    cols = [synth.normal_f32((900, synth.KIND_X, 0, m), (K,)) * np.float32(1e-4) for m in range(M)]
+    Xq = orc.quantize_q8_1(np.stack(cols))
+    d_w = np.ascontiguousarray(Wq).reshape(N, K // 32, 34)[:, :, :2].copy().view(np.float16)
+    d_x = np.ascontiguousarray(Xq).reshape(M, K // 32, 36)[:, :, :2].copy().view(np.float16)
+    assert np.all(np.abs(d_w) < 2.0 ** -14) and np.all(np.abs(d_x) < 2.0 ** -14)
+    assert np.count_nonzero(d_w) > 0 and np.count_nonzero(d_x) > 0
+    got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
+    ref = orc.gemv_q8_0_q8_1(Wq, Xq, N, K, M)
+    assert_close(got, ref, TOL, f"subnormal scales M={M} {launch}")
+
+
 # The default kernel and configuration follow the column count, the row-tile
 # count and the row length; these three shapes take every branch of that
 # choice for every M.
