@@ -400,15 +400,17 @@ hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float
     } else {
         // Measured on MI355X (decoder shapes, M = 2..24), both formats.  Up to
         // 512 row tiles: one tile per workgroup, K split over 8 waves up to 8
-        // columns and beyond 16 on rows up to 8192 (one chunk deep there, as
-        // the chunks of 32 columns fill the LDS), else over 4 waves two deep.
-        // More row tiles: tiles share each activation chunk.
+        // columns (4 for Q4_0 rows up to 4096) and beyond 16 on rows up to
+        // 8192 (one chunk deep there, as the chunks of 32 columns fill the
+        // LDS), else over 4 waves two deep.  More row tiles: tiles share each
+        // activation chunk.
         const int tiles = (N + 15) / 16;
         CB = 8;
         if (tiles <= 512) {
             RT = 1;
             const bool wide = M > 16 && K <= 8192;
-            KS = (M <= 8 || wide) ? 8 : 4;
+            const bool few = M <= 8 && (K > 4096 || WF::kBlockBytes == 34);
+            KS = (few || wide) ? 8 : 4;
             DEPTH = wide ? 1 : 2;
         } else if (WF::kBlockBytes == 34) {
             // Q8_0: its weight buffers are twice those of Q4_0, so fewer row
