@@ -88,6 +88,31 @@ def test_q4_kernels_use_dot4_lds_dma_and_matrix_cores(asm):
     assert "flat_load" not in un
 
 
+def test_matrix_core_scale_products_and_private_parts(asm):
+    """Both int8 matrix-core kernels take the d8 x d4 scale products from the
+    f16 matrix cores; the streaming kernel with one row tile per workgroup
+    (template RT = 1) meets its waves only at the row-group start and the
+    two-step K-part reduction (3 barriers), the shared-column forms also
+    inside the loop."""
+    for src in ("gemv_q4_0_mfma.hip", "gemv_qmfma_res.hip"):
+        ks = [(n, b) for n, b in _kernels(asm[src]) if "k_qmfma" in n or "k_qres" in n]
+        assert ks, src
+        for n, b in ks:
+            assert "v_mfma_f32_16x16x16_f16" in b, n
+    seen = 0
+    for n, b in _kernels(asm["gemv_q4_0_mfma.hip"]):
+        m = re.search(r"k_qmfma.*?ELi8ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", n)
+        if not m:
+            continue
+        rt, ks = int(m.group(2)), int(m.group(3))
+        if rt == 1:
+            assert b.count("s_barrier") == 3, n
+            seen += 1
+        elif ks > 1:
+            assert b.count("s_barrier") > 3, n
+    assert seen >= 8
+
+
 def test_resident_matrix_core_kernel(asm):
     """Weights reach the matrix cores through registers and a per-wave LDS
     transpose (16-byte non-temporal loads, ds_write_b128), the activation
