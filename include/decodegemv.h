@@ -77,12 +77,17 @@ const char* dg_last_hip_error(void);
  *                the whole grid on consecutive vectors (else each wave reads
  *                8 KiB of consecutive bytes per step);
  *                DG_READ_DEEP: 16 loads in flight per lane instead of 8
- *                (wave-contiguous order only).
+ *                (16 KiB per wave step); DG_READ_SHORT: 4 (4 KiB);
+ *                DG_READ_SHORTER: 2 (2 KiB) -- at most one of the three, and
+ *                only in the wave-contiguous order.  A grid of
+ *                bytes / (waves per workgroup * chunk) workgroups gives each
+ *                wave one chunk, the shape of a one-shot GEMV launch.
  * Errors: DG_ERR_NULL (buf or d_partials NULL with bytes > 0),
  * DG_ERR_MISALIGNED (buf not 16-byte aligned, d_partials not 4-byte aligned),
  * DG_ERR_SHAPE (bytes % 16 != 0), DG_ERR_ARG (grid/block/flags out of range).
  * ------------------------------------------------------------------------ */
-enum { DG_READ_NONTEMPORAL = 1, DG_READ_GRID_STRIDE = 2, DG_READ_DEEP = 4, DG_READ_DEFAULT_GRID = 1024 };
+enum { DG_READ_NONTEMPORAL = 1, DG_READ_GRID_STRIDE = 2, DG_READ_DEEP = 4, DG_READ_SHORT = 8,
+       DG_READ_SHORTER = 16, DG_READ_DEFAULT_GRID = 1024 };
 
 dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_partials,
                          int grid_blocks, int block_threads, int flags,

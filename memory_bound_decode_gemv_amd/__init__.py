@@ -28,6 +28,8 @@ DG_ERR_ARG = 6
 DG_READ_NONTEMPORAL = 1
 DG_READ_GRID_STRIDE = 2
 DG_READ_DEEP = 4
+DG_READ_SHORT = 8
+DG_READ_SHORTER = 16
 DG_READ_DEFAULT_GRID = 1024
 
 DG_DTYPE_F32 = 0

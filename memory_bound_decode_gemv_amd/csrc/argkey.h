@@ -27,14 +27,34 @@ __device__ __forceinline__ uint32_t key_index(uint64_t key) { return 0xFFFFFFFFu
 
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
+// The key of another lane, moved by one DPP step: both 32-bit halves take the
+// same control, so they come from the same source lane.  Lanes whose source
+// is outside the row, and rows the mask leaves out, receive 0 -- the
+// identity of the maximum, since every key is >= 0 and an empty lane holds 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_key(uint64_t v) {
+    const uint32_t lo = dpp_mov_u32<CTRL, ROW_MASK>((uint32_t)v);
+    const uint32_t hi = dpp_mov_u32<CTRL, ROW_MASK>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum key of the wave on DPP (IEEE discussion "ArgCompare Benchmark
+// Results and Performance Analysis": the DPP reduction beat the shuffle-only
+// one in every configuration it measured).  row_shr 1, 2, 4, 8 leave each
+// 16-lane row's maximum in its lane 15; row_bcast:15 folds row 0 into row 1
+// and row 2 into row 3, row_bcast:31 rows 0-1 into rows 2-3, so lane 63
+// holds the wave's maximum, returned to every lane through readlane.  The
+// maximum does not depend on the order of the steps.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, off, kWave);
-        const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), off, kWave);
-        v = umax64(v, ((uint64_t)hi << 32) | lo);
-    }
-    return v;
+    v = umax64(v, dpp_key<kDppRowShr1, 0xF>(v));
+    v = umax64(v, dpp_key<kDppRowShr2, 0xF>(v));
+    v = umax64(v, dpp_key<kDppRowShr4, 0xF>(v));
+    v = umax64(v, dpp_key<kDppRowShr8, 0xF>(v));
+    v = umax64(v, dpp_key<kDppRowBcast15, 0xA>(v));
+    v = umax64(v, dpp_key<kDppRowBcast31, 0xC>(v));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 }  // namespace dg

@@ -12,9 +12,11 @@
 //
 // Two access orders:
 //  * wave-contiguous (default): each wave reads 64 lanes x U x 16 B = 8 KiB
-//    (U = 8) or 16 KiB (U = 16, DG_READ_DEEP) of consecutive bytes per step,
-//    then jumps by the whole grid's share -- the order in which a GEMV wave
-//    reads its weight row;
+//    (U = 8), 16 KiB (U = 16, DG_READ_DEEP), 4 KiB (U = 4, DG_READ_SHORT) or
+//    2 KiB (U = 2, DG_READ_SHORTER) of consecutive bytes per step, then jumps
+//    by the whole grid's share -- the order in which a GEMV wave reads its
+//    weight row.  With a grid of bytes / (waves * chunk) workgroups every wave
+//    reads one chunk and exits, the shape of a one-shot GEMV launch;
 //  * grid-stride (the page's kernel): consecutive lanes of the whole grid read
 //    consecutive 16-byte vectors, and a lane's kUnroll loads in flight are one
 //    grid-size apart.
@@ -95,6 +97,12 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* d_partial
     } else if (flags & DG_READ_DEEP) {
         if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, 16>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
         else hipLaunchKernelGGL((k_stream_read_wave<false, 16>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
+    } else if (flags & DG_READ_SHORT) {
+        if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, 4>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
+        else hipLaunchKernelGGL((k_stream_read_wave<false, 4>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
+    } else if (flags & DG_READ_SHORTER) {
+        if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, 2>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
+        else hipLaunchKernelGGL((k_stream_read_wave<false, 2>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
     } else {
         if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, 8>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
         else hipLaunchKernelGGL((k_stream_read_wave<false, 8>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);

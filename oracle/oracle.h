@@ -159,6 +159,32 @@ void orc_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t
  * and the first NaN of a row wins.  x points to R rows of ld elements. */
 void orc_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int64_t R, int64_t C, int64_t ld);
 
+/* ---- row-partitioned multi-threaded driver (oracle_par.c) ----
+ *
+ * Each routine runs the single-threaded routine above of the same name on up
+ * to nthreads disjoint, contiguous ranges of output rows (columns, for the
+ * Q8_1 quantiser), one POSIX thread per range, and joins them.  No arithmetic
+ * is added or reordered: the outputs are bit-identical to one single-threaded
+ * call.  Returns 0, or -1 if a scratch buffer could not be allocated. */
+int orc_par_gemv_f16(const uint16_t* W, const uint16_t* x, double* y, int64_t N, int64_t K, int64_t ldw,
+                     int nthreads);
+int orc_par_gemv_bf16(const uint16_t* W, const uint16_t* x, double* y, int64_t N, int64_t K, int64_t ldw,
+                      int nthreads);
+int orc_par_gemv_q4_0_q8_1(const uint8_t* Wq, const uint8_t* Xq, double* Y, int64_t N, int64_t K, int64_t M,
+                           int nthreads);
+int orc_par_gemv_q8_0_q8_1(const uint8_t* Wq, const uint8_t* Xq, double* Y, int64_t N, int64_t K, int64_t M,
+                           int nthreads);
+int orc_par_gemv_nf4(const uint8_t* codes, const float* absmax, const float* table, const uint16_t* x,
+                     double* y, int64_t N, int64_t K, int64_t B, int nthreads);
+int orc_par_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld, int nthreads);
+int orc_par_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int64_t R, int64_t C, int64_t ld,
+                            int nthreads);
+int orc_par_quantize_q4_0(const float* w, uint8_t* Wq, int64_t N, int64_t K, int nthreads);
+int orc_par_quantize_q8_0(const float* w, uint8_t* Wq, int64_t N, int64_t K, int nthreads);
+int orc_par_quantize_q8_1(const float* x, uint8_t* Xq, int64_t M, int64_t K, int nthreads);
+int orc_par_quantize_nf4(const float* w, uint8_t* codes, float* absmax, const float* table, int64_t N, int64_t K,
+                         int64_t B, int nthreads);
+
 /* ---- streaming-read checksum ---- */
 
 /* Wrapping (mod 2^32) sum of n 32-bit words. */

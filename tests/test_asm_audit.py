@@ -138,3 +138,12 @@ def test_stream_probe_has_no_atomics(asm):
     t = asm["stream_read.hip"]
     assert "global_atomic" not in t
     assert re.search(r"global_load_dwordx4 .* nt", t)
+
+
+def test_argmax_wave_reduction_on_dpp(asm):
+    """The argmax reductions combine the lanes' 64-bit keys with DPP row_shr /
+    row_bcast moves, not with LDS-routed shuffles (ds_bpermute / ds_swizzle
+    would be the shuffle lowering)."""
+    t = asm["argmax.hip"]
+    assert "row_shr:1" in t and "row_shr:8" in t and "row_bcast:15" in t and "row_bcast:31" in t
+    assert "ds_bpermute" not in t

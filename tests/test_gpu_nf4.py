@@ -14,14 +14,19 @@ from tests._parity import assert_close
 
 pytestmark = pytest.mark.gpu
 
-# fp32 products and sums; table values held to 22 bits (binary16 hi + lo, scaled)
-TOL = 2e-4
+# Floored relative error (the R5 form) against the fp64 oracle.  No page states
+# a bound for NF4; it is a 4-bit weight GEMV like Q4_0, so it takes Q4_0's
+# per-row bound.  Its fp32 products and sums (table values held to 22 bits)
+# leave an absolute error of a few 1e-5 on rows whose |y| is ~1e-3 of the
+# rms: over all 28672 rows of the 70B shape the worst such row reaches about
+# 3e-4.  One dropped weight moves y by ~0.1..1, far above 1e-3 of the rms.
+TOL = 1e-3
 
 
 @functools.lru_cache(maxsize=16)
 def _operands(orc, cfg, N, K, B):
     w = synth.normal_f32((cfg, synth.KIND_W, 0, 0), (N, K))
-    codes, absmax = orc.quantize_nf4(w, synth.nf4_table(), B)
+    codes, absmax = orc.quantize_nf4(w, synth.nf4_table(), B, threads=0)
     xb = synth.normal_bf16_bits((cfg, synth.KIND_X, 0, 0), (K,), 1.0)
     return codes, absmax, xb
 
@@ -121,26 +126,17 @@ def test_nf4_any_table(dg, dev, orc):
         assert_close(got, orc.gemv_nf4(codes, absmax, t, xb, N, K, B), TOL, f"table {t[:3]}")
 
 
-def test_nf4_70b_mlp_shape_sampled_rows(dg, dev, orc):
+def test_nf4_70b_mlp_shape_all_rows(dg, dev, orc):
     """28672 x 8192 with the default launch (the shape of the page's
-    benchmark); sampled rows against the oracle."""
-    import torch
+    benchmark), operands quantised by the oracle; every row against it."""
     N, K, B = 28672, 8192, 64
-    w = synth.gpu_normal((7, synth.KIND_W, 0, 0), (N, K), 1.0, torch.float32)
-    t = torch.from_numpy(synth.nf4_table()).to(dev)
-    codes = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
-    absmax = torch.empty(N * K // B, dtype=torch.float32, device=dev)
-    dg.dg_quantize_nf4(w, codes, absmax, t, N, K, B)
+    w = synth.normal_f32((7, synth.KIND_W, 0, 0), (N, K))
+    table = synth.nf4_table()
+    codes, absmax = orc.quantize_nf4(w, table, B, threads=0)
+    del w
     xb = synth.normal_bf16_bits((7, synth.KIND_X, 0, 0), (K,), 1.0)
-    x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
-    y = torch.empty(N, dtype=torch.float32, device=dev)
-    dg.dg_gemv_nf4(codes, absmax, t, x, y, N=N, K=K, B=B)
-    torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([np.arange(0, N, 97), [N - 1]]))
-    c = codes.view(N, K // 2)[torch.from_numpy(rows).to(dev)].cpu().numpy()
-    a = absmax.view(N, K // B)[torch.from_numpy(rows).to(dev)].cpu().numpy()
-    ref = orc.gemv_nf4(c, a, synth.nf4_table(), xb, len(rows), K, B)
-    assert_close(y.cpu().numpy()[rows], ref, TOL, "28672x8192 sampled")
+    got = _gpu(dg, dev, codes, absmax, table, xb, N, K, B)
+    assert_close(got, orc.gemv_nf4(codes, absmax, table, xb, N, K, B, threads=0), TOL, "28672x8192 all rows")
 
 
 def test_nf4_rejects_a_block_size_other_than_one_wave_per_unit(dg, dev, orc):

@@ -21,7 +21,7 @@ TOL = 1e-3   # per-row floored relative error vs the oracle
 
 @functools.lru_cache(maxsize=8)
 def _weights(orc, cfg, N, K, copy):
-    return orc.quantize_q4_0(synth.normal_f32((cfg, synth.KIND_W, copy, 0), (N, K)))
+    return orc.quantize_q4_0(synth.normal_f32((cfg, synth.KIND_W, copy, 0), (N, K)), threads=0)
 
 
 def _operands(orc, cfg, N, K, M, copy=0, same_columns=False):
@@ -199,24 +199,21 @@ def test_q4_0_lds_rows_per_wave(dg, dev, orc, M, R):
     assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M), TOL, f"M={M} R={R}")
 
 
-def test_q4_0_70b_mlp_shape_sampled_rows(dg, dev, orc):
-    """The 4-bit M = 1 decode shape: N = 28672, K = 8192."""
+def test_q4_0_70b_mlp_shape_all_rows(dg, dev, orc):
+    """The 4-bit M = 1 decode shape, N = 28672, K = 8192: every row against the
+    oracle (the output starts as NaN, so a row never written fails too)."""
     N, K = 28672, 8192
     Wq, Xq = _operands(orc, 2, N, K, 1)
     got = _gpu(dg, dev, Wq, Xq, N, K, 1)
-    rows = np.unique(np.concatenate([np.arange(0, N, 37), [N - 1]]))
-    ref = orc.gemv_q4_0_q8_1(Wq.reshape(N, -1)[rows], Xq, len(rows), K, 1)
-    assert_close(got[0, rows], ref[0], TOL, "28672x8192 sampled")
+    assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1, threads=0), TOL, "28672x8192 all rows")
 
 
 @pytest.mark.parametrize("N,K", [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)])
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 12, 16, 24])
-def test_q4_0_decoder_layer_shapes_sampled_rows(dg, dev, orc, N, K, M):
+def test_q4_0_decoder_layer_shapes_all_rows(dg, dev, orc, N, K, M):
     Wq, Xq = _operands(orc, 3, N, K, M)
     got = _gpu(dg, dev, Wq, Xq, N, K, M)
-    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 97)), [N - 1]]))
-    ref = orc.gemv_q4_0_q8_1(Wq.reshape(N, -1)[rows], Xq, len(rows), K, M)
-    assert_close(got[:, rows], ref, TOL, f"{N}x{K} M={M}")
+    assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M, threads=0), TOL, f"{N}x{K} M={M}")
 
 
 # Scales below the binary16 normal range (|w| ~ 1e-5 gives weight scales of
@@ -247,9 +244,7 @@ def test_q4_0_subnormal_scales(dg, dev, orc, M, launch):
 def test_q4_0_default_launch_every_column_count(dg, dev, orc, N, K, M):
     Wq, Xq = _operands(orc, 3, N, K, M)
     got = _gpu(dg, dev, Wq, Xq, N, K, M)
-    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 29)), [N - 1]]))
-    ref = orc.gemv_q4_0_q8_1(Wq.reshape(N, -1)[rows], Xq, len(rows), K, M)
-    assert_close(got[:, rows], ref, TOL, f"{N}x{K} M={M}")
+    assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M, threads=0), TOL, f"{N}x{K} M={M}")
 
 
 @pytest.mark.parametrize("M", [2, 13, 16, 24])

@@ -31,7 +31,7 @@ def _unroll(rt, ks, d, cb):
 
 @functools.lru_cache(maxsize=8)
 def _weights(orc, cfg, N, K, copy):
-    return orc.quantize_q8_0(synth.normal_f32((cfg, synth.KIND_W, copy, 0), (N, K)))
+    return orc.quantize_q8_0(synth.normal_f32((cfg, synth.KIND_W, copy, 0), (N, K)), threads=0)
 
 
 def _operands(orc, cfg, N, K, M, same_columns=False):
@@ -125,23 +125,19 @@ def test_q8_0_mfma_matches_oracle(dg, dev, orc, launch, N, K, M):
                  f"mfma {launch} {N}x{K} M={M}")
 
 
-def test_q8_0_70b_mlp_shape_sampled_rows(dg, dev, orc):
+def test_q8_0_70b_mlp_shape_all_rows(dg, dev, orc):
     N, K = 28672, 8192
     Wq, Xq = _operands(orc, 2, N, K, 1)
     got = _gpu(dg, dev, Wq, Xq, N, K, 1)
-    rows = np.unique(np.concatenate([np.arange(0, N, 37), [N - 1]]))
-    ref = orc.gemv_q8_0_q8_1(Wq.reshape(N, -1)[rows], Xq, len(rows), K, 1)
-    assert_close(got[0, rows], ref[0], TOL, "28672x8192 sampled")
+    assert_close(got, orc.gemv_q8_0_q8_1(Wq, Xq, N, K, 1, threads=0), TOL, "28672x8192 all rows")
 
 
 @pytest.mark.parametrize("N,K", [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)])
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 12, 16, 24])
-def test_q8_0_decoder_layer_shapes_sampled_rows(dg, dev, orc, N, K, M):
+def test_q8_0_decoder_layer_shapes_all_rows(dg, dev, orc, N, K, M):
     Wq, Xq = _operands(orc, 3, N, K, M)
     got = _gpu(dg, dev, Wq, Xq, N, K, M)
-    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 97)), [N - 1]]))
-    ref = orc.gemv_q8_0_q8_1(Wq.reshape(N, -1)[rows], Xq, len(rows), K, M)
-    assert_close(got[:, rows], ref, TOL, f"{N}x{K} M={M}")
+    assert_close(got, orc.gemv_q8_0_q8_1(Wq, Xq, N, K, M, threads=0), TOL, f"{N}x{K} M={M}")
 
 
 # Scales below the binary16 normal range (|w| ~ 1e-5 gives weight scales of
@@ -172,9 +168,7 @@ def test_q8_0_subnormal_scales(dg, dev, orc, M, launch):
 def test_q8_0_default_launch_every_column_count(dg, dev, orc, N, K, M):
     Wq, Xq = _operands(orc, 3, N, K, M)
     got = _gpu(dg, dev, Wq, Xq, N, K, M)
-    rows = np.unique(np.concatenate([np.arange(0, N, max(1, N // 29)), [N - 1]]))
-    ref = orc.gemv_q8_0_q8_1(Wq.reshape(N, -1)[rows], Xq, len(rows), K, M)
-    assert_close(got[:, rows], ref, TOL, f"{N}x{K} M={M}")
+    assert_close(got, orc.gemv_q8_0_q8_1(Wq, Xq, N, K, M, threads=0), TOL, f"{N}x{K} M={M}")
 
 
 @pytest.mark.parametrize("M", [2, 16, 24])

@@ -26,7 +26,9 @@ def _run(dg, dev, buf, nbytes, **kw):
                                     dict(grid_blocks=1, block_threads=64), dict(grid_blocks=7, block_threads=1024),
                                     dict(grid_blocks=4096, block_threads=512, flags=3),
                                     dict(grid_blocks=3, block_threads=192, flags=1), dict(flags=5),
-                                    dict(grid_blocks=9, block_threads=128, flags=4)])
+                                    dict(grid_blocks=9, block_threads=128, flags=4), dict(flags=9), dict(flags=17),
+                                    dict(grid_blocks=5, block_threads=256, flags=8),
+                                    dict(grid_blocks=65537, block_threads=256, flags=17)])
 def test_stream_checksum_matches_oracle(dg, dev, orc, nbytes, launch):
     import torch
     g = np.random.default_rng(nbytes)
@@ -59,7 +61,11 @@ def test_stream_full_size_closed_form(dg, dev):
     n = (8 << 30) // 4
     buf = torch.arange(n, dtype=torch.int32, device=dev)    # 0 .. 2^31 - 1
     expect = (n * (n - 1) // 2) % 2**32
-    for flags in (0, 1, 2, 3, 5):
+    for flags in (0, 1, 2, 3, 5, 9, 17):
         assert _run(dg, dev, buf, n * 4, flags=flags) == expect
+    # one-shot grids: every wave reads one chunk (8, 4 and 2 KiB per wave)
+    for flags, chunk in ((1, 8192), (9, 4096), (17, 2048)):
+        grid = n * 4 // (4 * chunk)
+        assert _run(dg, dev, buf, n * 4, flags=flags, grid_blocks=grid, block_threads=256) == expect
     del buf
     torch.cuda.empty_cache()
