@@ -81,13 +81,23 @@ const char* dg_last_hip_error(void);
  *                DG_READ_SHORTER: 2 (2 KiB) -- at most one of the three, and
  *                only in the wave-contiguous order.  A grid of
  *                bytes / (waves per workgroup * chunk) workgroups gives each
- *                wave one chunk, the shape of a one-shot GEMV launch.
+ *                wave one chunk, the shape of a one-shot GEMV launch;
+ *                DG_READ_CAP(n), n in 1..15: at most n workgroups resident
+ *                per CU (the launch reserves 1/n of a CU's 160 KiB of LDS
+ *                that the kernel never touches), which bounds the streams
+ *                in flight;
+ *                DG_READ_HALF: only the even waves of each workgroup read,
+ *                the odd ones hold their slots (the occupancy of a GEMV that
+ *                gives each row to two waves of which one covers it);
+ *                wave-contiguous order, a multiple of 128 threads per
+ *                workgroup.
  * Errors: DG_ERR_NULL (buf or d_partials NULL with bytes > 0),
  * DG_ERR_MISALIGNED (buf not 16-byte aligned, d_partials not 4-byte aligned),
  * DG_ERR_SHAPE (bytes % 16 != 0), DG_ERR_ARG (grid/block/flags out of range).
  * ------------------------------------------------------------------------ */
 enum { DG_READ_NONTEMPORAL = 1, DG_READ_GRID_STRIDE = 2, DG_READ_DEEP = 4, DG_READ_SHORT = 8,
-       DG_READ_SHORTER = 16, DG_READ_DEFAULT_GRID = 1024 };
+       DG_READ_SHORTER = 16, DG_READ_HALF = 32, DG_READ_CAP_SHIFT = 8, DG_READ_DEFAULT_GRID = 1024 };
+#define DG_READ_CAP(n) ((int)(n) << DG_READ_CAP_SHIFT)
 
 dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_partials,
                          int grid_blocks, int block_threads, int flags,

@@ -30,6 +30,13 @@ DG_READ_GRID_STRIDE = 2
 DG_READ_DEEP = 4
 DG_READ_SHORT = 8
 DG_READ_SHORTER = 16
+DG_READ_HALF = 32
+DG_READ_CAP_SHIFT = 8
+
+
+def DG_READ_CAP(n: int) -> int:
+    """flags bits: at most n (1..15) workgroups of dg_stream_read resident per CU."""
+    return int(n) << DG_READ_CAP_SHIFT
 DG_READ_DEFAULT_GRID = 1024
 
 DG_DTYPE_F32 = 0

@@ -145,10 +145,13 @@ dg_status dg_stream_read(const void* buf, size_t bytes, uint32_t* d_partials, in
     if (bytes % 16 != 0) return DG_ERR_SHAPE;
     constexpr int kDepthFlags = DG_READ_DEEP | DG_READ_SHORT | DG_READ_SHORTER;
     if (grid_blocks < 0 || block_threads < 0 ||
-        (flags & ~(DG_READ_NONTEMPORAL | DG_READ_GRID_STRIDE | kDepthFlags)))
+        (flags & ~(DG_READ_NONTEMPORAL | DG_READ_GRID_STRIDE | kDepthFlags | DG_READ_HALF |
+                   (0xF << DG_READ_CAP_SHIFT))))
         return DG_ERR_ARG;
     const int depth = flags & kDepthFlags;
     if ((depth & (depth - 1)) != 0 || (depth && (flags & DG_READ_GRID_STRIDE))) return DG_ERR_ARG;
+    if ((flags & DG_READ_HALF) && ((flags & DG_READ_GRID_STRIDE) || (block_threads ? block_threads : 512) % 128 != 0))
+        return DG_ERR_ARG;
     if (block_threads && (block_threads % kWave != 0 || block_threads > 1024)) return DG_ERR_ARG;
     if (bytes == 0) return DG_OK;
     if (!buf || !d_partials) return DG_ERR_NULL;

@@ -20,7 +20,10 @@
 //  * grid-stride (the page's kernel): consecutive lanes of the whole grid read
 //    consecutive 16-byte vectors, and a lane's kUnroll loads in flight are one
 //    grid-size apart.
-// The ceiling is the best rate over both orders and the launch shapes.
+// The ceiling is the best rate over both orders and the launch shapes, with
+// and without a cap on the workgroups resident per CU: a read with every
+// wave slot of the chip streaming (tens of MB in flight) was measured slower
+// on MI355X than one with a few streams per CU.
 #include "dg_device.h"
 #include "dg_internal.h"
 
@@ -28,6 +31,7 @@ namespace dg {
 namespace {
 
 constexpr int kUnroll = 8;  // 16-byte loads in flight per lane per step (grid-stride order)
+constexpr int kLdsPerCu = 160 * 1024;
 
 __device__ __forceinline__ uint32_t add4(u32x4 v) { return (v.x + v.y) + (v.z + v.w); }
 
@@ -61,25 +65,32 @@ k_stream_read_grid(const u32x4* __restrict__ p, uint64_t nvec, uint32_t* __restr
     finish(acc, partials);
 }
 
-template <bool NT, int U>
+// HALF: only the even waves of a workgroup read; the odd ones hold their
+// slots and meet the workgroup's barrier (the occupancy of a GEMV launch that
+// splits each row over two waves when one wave's span covers the row).
+template <bool NT, int U, bool HALF>
 __global__ void __launch_bounds__(1024)
 k_stream_read_wave(const u32x4* __restrict__ p, uint64_t nvec, uint32_t* __restrict__ partials) {
     constexpr uint64_t kChunk = (uint64_t)kWave * U;   // vectors per wave step
-    const uint64_t nwaves = (uint64_t)gridDim.x * (blockDim.x / kWave);
-    const uint64_t wave = (uint64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    constexpr int kShift = HALF ? 1 : 0;
+    const int wib = threadIdx.x / kWave;
+    const uint64_t nwaves = (uint64_t)gridDim.x * ((blockDim.x / kWave) >> kShift);
+    const uint64_t wave = (uint64_t)blockIdx.x * ((blockDim.x / kWave) >> kShift) + (wib >> kShift);
     const int lane = lane_id();
     uint32_t acc = 0;
-    uint64_t c = wave;
-    for (; (c + 1) * kChunk <= nvec; c += nwaves) {
-        const u32x4* q = p + c * kChunk + lane;
-        u32x4 v[U];
+    if (!(HALF && (wib & 1))) {   // wave-uniform
+        uint64_t c = wave;
+        for (; (c + 1) * kChunk <= nvec; c += nwaves) {
+            const u32x4* q = p + c * kChunk + lane;
+            u32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = load_vec<NT>(q + u * kWave);
+            for (int u = 0; u < U; ++u) v[u] = load_vec<NT>(q + u * kWave);
 #pragma unroll
-        for (int u = 0; u < U; ++u) acc += add4(v[u]);
-    }
-    if (c * kChunk < nvec) {   // the one partial chunk at the end of the buffer
-        for (uint64_t i = c * kChunk + lane; i < nvec; i += kWave) acc += add4(load_vec<NT>(p + i));
+            for (int u = 0; u < U; ++u) acc += add4(v[u]);
+        }
+        if (c * kChunk < nvec) {   // the one partial chunk at the end of the buffer
+            for (uint64_t i = c * kChunk + lane; i < nvec; i += kWave) acc += add4(load_vec<NT>(p + i));
+        }
     }
     finish(acc, partials);
 }
@@ -91,22 +102,38 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* d_partial
     const uint64_t nvec = bytes / 16;
     const bool nt = flags & DG_READ_NONTEMPORAL;
     const u32x4* p = (const u32x4*)buf;
+    // Occupancy cap: dynamic LDS nobody reads, sized so that at most `cap`
+    // workgroups fit one CU's 160 KiB, limits the streams in flight per CU.
+    const int cap = (flags >> DG_READ_CAP_SHIFT) & 0xF;
+    const size_t lds = cap ? (size_t)(kLdsPerCu / cap / 512 * 512) - 256 : 0;
     if (flags & DG_READ_GRID_STRIDE) {
-        if (nt) hipLaunchKernelGGL(k_stream_read_grid<true>, dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
-        else hipLaunchKernelGGL(k_stream_read_grid<false>, dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
-    } else if (flags & DG_READ_DEEP) {
-        if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, 16>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
-        else hipLaunchKernelGGL((k_stream_read_wave<false, 16>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
-    } else if (flags & DG_READ_SHORT) {
-        if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, 4>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
-        else hipLaunchKernelGGL((k_stream_read_wave<false, 4>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
-    } else if (flags & DG_READ_SHORTER) {
-        if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, 2>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
-        else hipLaunchKernelGGL((k_stream_read_wave<false, 2>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
-    } else {
-        if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, 8>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
-        else hipLaunchKernelGGL((k_stream_read_wave<false, 8>), dim3(grid), dim3(block), 0, s, p, nvec, d_partials);
+        if (nt) hipLaunchKernelGGL(k_stream_read_grid<true>, dim3(grid), dim3(block), lds, s, p, nvec, d_partials);
+        else hipLaunchKernelGGL(k_stream_read_grid<false>, dim3(grid), dim3(block), lds, s, p, nvec, d_partials);
+        return hipGetLastError();
     }
+    const int u = (flags & DG_READ_DEEP) ? 16 : (flags & DG_READ_SHORT) ? 4 : (flags & DG_READ_SHORTER) ? 2 : 8;
+    const bool half = flags & DG_READ_HALF;
+#define DG_READ_CASE(UU)                                                                                        \
+    case UU:                                                                                                    \
+        if (half) {                                                                                             \
+            if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, UU, true>), dim3(grid), dim3(block), lds, s, p, \
+                                       nvec, d_partials);                                                       \
+            else hipLaunchKernelGGL((k_stream_read_wave<false, UU, true>), dim3(grid), dim3(block), lds, s, p,  \
+                                    nvec, d_partials);                                                          \
+        } else {                                                                                                \
+            if (nt) hipLaunchKernelGGL((k_stream_read_wave<true, UU, false>), dim3(grid), dim3(block), lds, s,   \
+                                       p, nvec, d_partials);                                                    \
+            else hipLaunchKernelGGL((k_stream_read_wave<false, UU, false>), dim3(grid), dim3(block), lds, s, p, \
+                                    nvec, d_partials);                                                          \
+        }                                                                                                       \
+        break;
+    switch (u) {
+        DG_READ_CASE(2)
+        DG_READ_CASE(4)
+        DG_READ_CASE(8)
+        DG_READ_CASE(16)
+    }
+#undef DG_READ_CASE
     return hipGetLastError();
 }
 

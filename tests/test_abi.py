@@ -105,10 +105,14 @@ def test_units_kernel_rejects_too_many_columns(lib):
 def test_stream_read_rejects_before_launch(lib):
     assert lib.dg_stream_read(A16, 24, A16, 0, 0, 1, None) == 3          # bytes % 16
     assert lib.dg_stream_read(A16, 32, A16, 0, 96, 1, None) == 6         # block not a multiple of 64
-    assert lib.dg_stream_read(A16, 32, A16, 0, 0, 32, None) == 6         # unknown flag
+    assert lib.dg_stream_read(A16, 32, A16, 0, 0, 64, None) == 6         # unknown flag
     assert lib.dg_stream_read(A16, 32, A16, 0, 0, 4 | 8, None) == 6      # two chunk depths
     assert lib.dg_stream_read(A16, 32, A16, 0, 0, 8 | 16, None) == 6
     assert lib.dg_stream_read(A16, 32, A16, 0, 0, 2 | 16, None) == 6     # a depth with the grid-stride order
+    assert lib.dg_stream_read(A16, 32, A16, 0, 64, 32, None) == 6        # half the waves of a 1-wave group
+    assert lib.dg_stream_read(A16, 32, A16, 0, 192, 32, None) == 6       # ... of an odd wave count
+    assert lib.dg_stream_read(A16, 32, A16, 0, 0, 2 | 32, None) == 6     # half with the grid-stride order
+    assert lib.dg_stream_read(A16, 32, A16, 0, 0, 1 << 12, None) == 6    # past the cap field
     assert lib.dg_stream_read(None, 32, A16, 0, 0, 1, None) == 1
     assert lib.dg_stream_read(A2, 32, A16, 0, 0, 1, None) == 2
     assert lib.dg_stream_read(A16, 32, A2, 0, 0, 1, None) == 2          # partials not 4-byte aligned

@@ -28,7 +28,11 @@ def _run(dg, dev, buf, nbytes, **kw):
                                     dict(grid_blocks=3, block_threads=192, flags=1), dict(flags=5),
                                     dict(grid_blocks=9, block_threads=128, flags=4), dict(flags=9), dict(flags=17),
                                     dict(grid_blocks=5, block_threads=256, flags=8),
-                                    dict(grid_blocks=65537, block_threads=256, flags=17)])
+                                    dict(grid_blocks=65537, block_threads=256, flags=17),
+                                    dict(grid_blocks=11, block_threads=256, flags=33),
+                                    dict(grid_blocks=6, block_threads=384, flags=33 | 8 | (5 << 8)),
+                                    dict(grid_blocks=3000, block_threads=128, flags=1 | 32 | (4 << 8)),
+                                    dict(flags=1 | (1 << 8)), dict(grid_blocks=300, block_threads=64, flags=(15 << 8))])
 def test_stream_checksum_matches_oracle(dg, dev, orc, nbytes, launch):
     import torch
     g = np.random.default_rng(nbytes)
@@ -67,5 +71,9 @@ def test_stream_full_size_closed_form(dg, dev):
     for flags, chunk in ((1, 8192), (9, 4096), (17, 2048)):
         grid = n * 4 // (4 * chunk)
         assert _run(dg, dev, buf, n * 4, flags=flags, grid_blocks=grid, block_threads=256) == expect
+    # capped residency, and half the waves of each workgroup reading
+    for flags, block, waves in ((1 | (5 << 8), 128, 2), (17 | (4 << 8), 512, 8), (1 | 32 | (5 << 8), 256, 2)):
+        grid = n * 4 // (waves * (2048 if flags & 16 else 8192))
+        assert _run(dg, dev, buf, n * 4, flags=flags, grid_blocks=grid, block_threads=block) == expect
     del buf
     torch.cuda.empty_cache()
