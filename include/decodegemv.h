@@ -279,6 +279,29 @@ dg_status dg_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C,
                          int64_t ld, void* ws, size_t ws_bytes, dg_stream stream);
 
 /* ------------------------------------------------------------------------
+ * argmax over rows without a caller workspace, allocating nothing
+ *
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Results are bit-identical to dg_argmax_rows (same kernels, same
+ * chunking).  The chunk keys live in a fixed array of DG_ARGMAX_SCRATCH_BYTES
+ * in device memory that the library holds on each GPU it runs on until the
+ * process ends; the call itself allocates nothing.  Every call on a GPU
+ * shares that GPU's array, so calls that overlap on one GPU (two streams, two
+ * threads) race: serialise them.  The keys need no clearing (every key read
+ * is written first by the same call).
+ *
+ *   x, idx, R, C, ld  as for dg_argmax_rows.
+ * Errors: as dg_argmax_rows; DG_ERR_WORKSPACE when
+ * dg_argmax_workspace_bytes(R, C) > DG_ARGMAX_SCRATCH_BYTES (checked before
+ * any launch); DG_ERR_HIP when the array's device address cannot be found on
+ * the current device.
+ * ------------------------------------------------------------------------ */
+#define DG_ARGMAX_SCRATCH_BYTES (1u << 20)
+dg_status dg_argmax_rows_noalloc(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld,
+                                 dg_stream stream);
+
+/* ------------------------------------------------------------------------
  * The greedy decode tail fused: bfloat16 lm-head GEMV and argmax of its logits
  *
  *   y[n] = sum_k W[n*ldw + k] * x[k]  (fp32, exactly as dg_gemv_bf16)

@@ -72,7 +72,11 @@ EXPORTED = (
     "dg_gemv_q8_0", "dg_gemv_q8_0_ex", "dg_quantize_q8_0",
     "dg_argcompare_rows", "dg_gemv_bf16_argmax_workspace_bytes", "dg_gemv_bf16_argmax",
     "dg_gemv_nf4", "dg_gemv_nf4_ex", "dg_quantize_nf4",
+    "dg_argmax_rows_noalloc",
 )
+
+# Size of the library's fixed per-device argmax key array (include/decodegemv.h).
+DG_ARGMAX_SCRATCH_BYTES = 1 << 20
 
 
 class DGError(RuntimeError):
@@ -148,6 +152,8 @@ def _lib():
     lib.dg_argmax_workspace_bytes.restype = ctypes.c_size_t
     lib.dg_argmax_rows.argtypes = [P, P, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.dg_argmax_rows.restype = st
+    lib.dg_argmax_rows_noalloc.argtypes = [P, P, I64, I64, I64, P]
+    lib.dg_argmax_rows_noalloc.restype = st
     lib.dg_argcompare_rows.argtypes = [P, I32, I32, P, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.dg_argcompare_rows.restype = st
     lib.dg_gemv_bf16_argmax_workspace_bytes.argtypes = [I64, I64]
@@ -416,6 +422,27 @@ def dg_argmax_rows(x, idx, R=None, C=None, ld=None, ws=None, stream=None):
     ws_bytes = ws.numel() * ws.element_size()
     _check(_lib().dg_argmax_rows(_ptr(x), _ptr(idx), int(R), int(C), int(ld), _ptr(ws), ws_bytes,
                                  _stream(stream)), "dg_argmax_rows")
+    return idx
+
+
+def dg_argmax_rows_noalloc(x, idx, R=None, C=None, ld=None, stream=None):
+    """As dg_argmax_rows, with the chunk keys in the library's fixed per-device
+    array instead of a workspace: the call allocates nothing.  Calls that
+    overlap on one GPU race (they share the array)."""
+    torch = _torch()
+    _need(x, (torch.float32,), "x")
+    _need(idx, (torch.int64,), "idx")
+    if R is None:
+        R = x.shape[0] if x.dim() == 2 else 1
+    if C is None:
+        C = x.shape[-1]
+    if ld is None:
+        ld = x.shape[-1]
+    R, C, ld = int(R), int(C), int(ld)
+    if R > 0 and C > 0 and ld >= C:
+        _fits(x, ((R - 1) * ld + C) * 4, "x")
+        _fits(idx, R * 8, "idx")
+    _check(_lib().dg_argmax_rows_noalloc(_ptr(x), _ptr(idx), R, C, ld, _stream(stream)), "dg_argmax_rows_noalloc")
     return idx
 
 

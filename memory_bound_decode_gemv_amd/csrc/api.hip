@@ -290,6 +290,16 @@ dg_status dg_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int
     return hip_status(launch_argcompare_rows(x, dtype, op, idx, R, C, ld, ws, (hipStream_t)stream));
 }
 
+dg_status dg_argmax_rows_noalloc(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld,
+                                 dg_stream stream) {
+    if (R < 0 || R > kI32Max || C < 1 || C >= kI32Max || ld < C) return DG_ERR_SHAPE;
+    if (R == 0) return DG_OK;
+    if (!x || !idx) return DG_ERR_NULL;
+    if (!aligned(x, 4) || !aligned(idx, 8)) return DG_ERR_MISALIGNED;
+    if (argmax_workspace_bytes(R, C) > DG_ARGMAX_SCRATCH_BYTES) return DG_ERR_WORKSPACE;
+    return hip_status(launch_argmax_rows_noalloc(x, idx, R, C, ld, (hipStream_t)stream));
+}
+
 dg_status dg_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld, void* ws,
                          size_t ws_bytes, dg_stream stream) {
     if (R < 0 || R > kI32Max || C < 1 || C >= kI32Max || ld < C) return DG_ERR_SHAPE;

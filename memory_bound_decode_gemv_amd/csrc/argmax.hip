@@ -18,6 +18,8 @@
 #include "dg_device.h"
 #include "dg_internal.h"
 
+#include <mutex>
+
 namespace dg {
 namespace {
 
@@ -208,6 +210,48 @@ hipError_t launch_argcompare_rows(const void* x, int dtype, int op, int64_t* idx
 
 hipError_t launch_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld, void* ws,
                               hipStream_t s) {
+    return launch_argcompare_rows(x, DG_DTYPE_F32, DG_ARG_MAX, idx, R, C, ld, ws, s);
+}
+
+// ---------------------------------------------------------------------------
+// The argmax without a caller workspace: its chunk keys go to a fixed array in
+// device memory that the library's code object holds (one copy per GPU, alive
+// until the process ends), so the call allocates nothing.  The array's name is
+// a host-side stand-in in host code; its device address is looked up once per
+// device with hipGetSymbolAddress and only that address reaches the kernels.
+// Every call on a GPU shares the array: calls that overlap on one GPU race.
+// The keys need no clearing: pass 1 writes every key that pass 2 reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint64_t scratch[DG_ARGMAX_SCRATCH_BYTES / sizeof(uint64_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device ordinal
+}  // namespace
+
+hipError_t argmax_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));   // with `dev` current: its own copy
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_argmax_rows_noalloc(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld,
+                                      hipStream_t s) {
+    void* ws = nullptr;
+    hipError_t e = argmax_scratch(&ws);
+    if (e != hipSuccess) return e;
     return launch_argcompare_rows(x, DG_DTYPE_F32, DG_ARG_MAX, idx, R, C, ld, ws, s);
 }
 

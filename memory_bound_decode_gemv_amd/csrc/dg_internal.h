@@ -107,5 +107,9 @@ hipError_t launch_argmax_rows(const float* x, int64_t* idx, int64_t R, int64_t C
                               void* ws, hipStream_t s);
 hipError_t launch_argcompare_rows(const void* x, int dtype, int op, int64_t* idx, int64_t R, int64_t C, int64_t ld,
                                   void* ws, hipStream_t s);
+// The same argmax with its chunk keys in the library's fixed per-device array
+// (DG_ARGMAX_SCRATCH_BYTES); the caller has checked the size.
+hipError_t launch_argmax_rows_noalloc(const float* x, int64_t* idx, int64_t R, int64_t C, int64_t ld,
+                                      hipStream_t s);
 
 }  // namespace dg

@@ -133,6 +133,39 @@ def test_argmax_rejects_before_launch(lib):
     assert lib.dg_argmax_rows(None, None, 0, 10, 10, None, 0, None) == 0
 
 
+def test_argmax_noalloc_rejects_before_launch(lib):
+    """The no-allocation argmax checks its arguments, and that the chunk keys fit
+    the library's fixed array, before touching the HIP runtime."""
+    import memory_bound_decode_gemv_amd as m
+    f = lib.dg_argmax_rows_noalloc
+    assert f(A16, A16, 4, 0, 4, None) == 3                     # C = 0
+    assert f(A16, A16, 4, 10, 9, None) == 3                    # ld < C
+    assert f(None, A16, 4, 10, 10, None) == 1
+    assert f(A16, P(0x1004), 4, 10, 10, None) == 2
+    assert f(None, None, 0, 10, 10, None) == 0                 # empty: nothing launched
+    # the largest row count whose keys still fit, and one more row
+    C = 1 << 20
+    rmax = noalloc_max_rows(lib, C, m.DG_ARGMAX_SCRATCH_BYTES)
+    assert rmax >= 64        # the [64, 1M] workload fits
+    assert lib.dg_argmax_workspace_bytes(rmax + 1, C) > m.DG_ARGMAX_SCRATCH_BYTES
+    assert f(A16, A16, rmax + 1, C, C, None) == 4
+
+
+def noalloc_max_rows(lib, C, limit):
+    """The largest R with dg_argmax_workspace_bytes(R, C) <= limit (the key
+    count per row depends on R through the chunk choice, so search)."""
+    lo, hi = 0, 1
+    while lib.dg_argmax_workspace_bytes(hi, C) <= limit:
+        lo, hi = hi, 2 * hi
+    while hi - lo > 1:
+        mid = (lo + hi) // 2
+        if lib.dg_argmax_workspace_bytes(mid, C) <= limit:
+            lo = mid
+        else:
+            hi = mid
+    return lo
+
+
 def test_argcompare_rejects_before_launch(lib):
     need = lib.dg_argmax_workspace_bytes(4, 10)
     assert lib.dg_argcompare_rows(A16, 3, 0, A16, 4, 10, 10, A16, 1 << 20, None) == 6      # unknown dtype
