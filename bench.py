@@ -780,11 +780,13 @@ def suite_q4_m1(dg, torch, emit, ceil_gbps):
 
 
 
-# matrix-core configurations (RT, KS, DEPTH, CB) -> the largest column count they serve;
-# launch override unroll = RT*10000 + KS*100 + DEPTH*10 + CB/8
-MFMA_BUILT = {(1, 16, 1, 8): 8, (4, 4, 2, 8): 16, (1, 8, 2, 8): 16,
-              (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (2, 4, 2, 8): 24, (4, 2, 2, 8): 24, (8, 1, 2, 8): 24,
-              (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24, (1, 4, 2, 8): 24}
+# matrix-core configurations (RT, KS, DEPTH, CB); a configuration that does
+# not take a column count (its LDS or registers) is refused by the library and
+# skipped.  launch override unroll = RT*10000 + KS*100 + DEPTH*10 + CB/8
+MFMA_SWEEP = [(1, 16, 1, 8), (2, 8, 1, 8), (4, 4, 2, 8), (1, 12, 1, 8), (3, 4, 1, 8), (1, 8, 1, 8), (1, 8, 2, 8),
+              (2, 4, 2, 8), (4, 2, 2, 8), (8, 1, 2, 8), (4, 1, 2, 8), (4, 1, 3, 8), (2, 2, 2, 8), (1, 4, 2, 8),
+              (1, 4, 3, 8), (1, 4, 4, 8), (1, 4, 5, 8), (2, 2, 3, 8), (2, 2, 4, 8)]
+MFMA_BUILT = {c: 24 for c in MFMA_SWEEP}
 
 
 def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
@@ -803,7 +805,7 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
             prev = cps
             emit(record(f"gemv_q4_0 {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M, copies=nc,
                         variant="default", columns_per_s=round(cps, 1), change_vs_prev_M=dip))
-            if M in (2, 4, 8, 12, 16, 24) and sweep:
+            if M in (2, 4, 8, 12, 16, 17, 24) and sweep:
                 launches = [(dict(variant=14, unroll=rt * 10000 + ks * 100 + d * 10 + cb // 8),
                              dict(variant="mfma", RT=rt, KS=ks, DEPTH=d, CB=cb))
                             for (rt, ks, d, cb), mmax in MFMA_BUILT.items() if M <= mmax]
@@ -824,10 +826,7 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
 
 
 
-# matrix-core configurations built for Q8_0 weights (larger weight buffers than Q4_0)
-MFMA_BUILT_Q8 = {(1, 16, 1, 8): 8, (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (1, 8, 2, 8): 16, (2, 4, 2, 8): 24,
-                 (4, 2, 2, 8): 24, (8, 1, 2, 8): 24, (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24,
-                 (1, 4, 2, 8): 24}
+MFMA_BUILT_Q8 = {c: 24 for c in MFMA_SWEEP}
 
 
 def bytes_q8_0(N, K, M):
@@ -1057,6 +1056,58 @@ def profile_kernels(args):
     log(f"[profile-kernels] q4_0 x{2 * nq}, f16 x{n16}, nf4 x{2 * nn}, stream_read 1 GiB x4, copy 1 GiB x4")
 
 
+# Workloads of --profile-launch-cost, in launch order (one graph each), with
+# their algorithmic bytes per launch.
+LAUNCH_COST_CASES = [("launch floor: 16-byte read by one wave", 16), ("read 8.4 MB", 2 * 1024 * 4096),
+                     ("read 33.5 MB", 2 * 4096 * 4096), ("read 134 MB", 8 * 4096 * 4096),
+                     ("read 537 MB", 32 * 4096 * 4096), ("gemv_f16 4096x4096 default", 2 * 4096 * 4096 + 4 * 4096),
+                     ("gemv_f16 4096x4096 grid 1024 x 256 threads", 2 * 4096 * 4096 + 4 * 4096),
+                     ("gemv_f16 4096x4096 grid 512 x 256 threads", 2 * 4096 * 4096 + 4 * 4096)]
+
+
+def profile_launch_cost(args):
+    """Graphs of back-to-back launches for a rocprofv3 --kernel-trace run that
+    splits the per-launch cost of a GEMV: the 16-byte read of one wave (the
+    launch floor), one-shot streaming reads of 8.4 MB to 537 MB (rotated
+    copies; duration against bytes gives the in-kernel fixed cost and the
+    streaming rate), and the fp16 4096 x 4096 GEMV with its default grid and
+    two persistent grids.  400 launches per graph (100 for 537 MB), 50 ms of
+    idle between graphs so that each is one run in the trace."""
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    cs = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+
+    def run(calls, reps=3):
+        g = capture(calls)
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        time.sleep(0.05)
+
+    tiny = torch.zeros(64, dtype=torch.int32, device="cuda")
+    run([lambda: dg.dg_stream_read(tiny, cs, nbytes=16, grid_blocks=1, block_threads=64)] * 400)
+    log(f"[launch-cost] {LAUNCH_COST_CASES[0][0]}")
+    flags = _NT | _cap(5)
+    for nbytes, ncalls, label in ((2 * 1024 * 4096, 400, 1), (2 * 4096 * 4096, 400, 2), (8 * 4096 * 4096, 400, 3),
+                                  (32 * 4096 * 4096, 100, 4)):
+        n = copies_for(nbytes)
+        big = torch.ones(n * nbytes // 4, dtype=torch.int32, device="cuda")
+        bufs = [big[c * nbytes // 4:(c + 1) * nbytes // 4] for c in range(n)]
+        grid = nbytes // (2 * 8192)
+        run([(lambda c=c: dg.dg_stream_read(bufs[c % n], cs, grid_blocks=grid, block_threads=128, flags=flags))
+             for c in range(ncalls)])
+        log(f"[launch-cost] {LAUNCH_COST_CASES[label][0]}: {n} copies, one-shot grid {grid} x 128 threads, cap 5")
+        del bufs, big
+        torch.cuda.empty_cache()
+    n16 = copies_for(2 * FP16_N * FP16_K)
+    W16, x16 = dense_copies(0, FP16_N, FP16_K, n16, torch.float16)
+    y16 = torch.empty(FP16_N, dtype=torch.float16, device="cuda")
+    for i, launch in enumerate((None, dict(variant=1, grid=1024, block=256, unroll=102),
+                                dict(variant=1, grid=512, block=256, unroll=102))):
+        run([(lambda c=c: dg.dg_gemv_f16(W16[c % n16], x16, y16, launch=launch)) for c in range(400)])
+        log(f"[launch-cost] {LAUNCH_COST_CASES[5 + i][0]}")
+
+
 SMALL_M_CASES = [(4096, 4096), (14336, 4096), (4096, 14336)]
 SMALL_M_COLUMNS = (4, 8, 16, 24)
 
@@ -1091,6 +1142,8 @@ def main():
     ap.add_argument("--suite-out", default=None, help="append suite records (JSON lines) to this file")
     ap.add_argument("--profile-kernels", action="store_true",
                     help="launch each profiled kernel eagerly on known workloads (for rocprofv3 --pmc)")
+    ap.add_argument("--profile-launch-cost", action="store_true",
+                    help="graphs of back-to-back launches for a kernel-trace split of the per-launch cost")
     ap.add_argument("--profile-small-m", action="store_true",
                     help="launch the small-batch Q4_0 GEMV eagerly on the decoder shapes (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
@@ -1112,6 +1165,8 @@ def main():
         profile_kernels(args)
     elif args.profile_small_m:
         profile_small_m(args)
+    elif args.profile_launch_cost:
+        profile_launch_cost(args)
     elif args.suite:
         suite(args)
     else:

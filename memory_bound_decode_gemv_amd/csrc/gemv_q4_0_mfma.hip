@@ -65,9 +65,9 @@ using namespace mfma;
 template <class WF, int CB, int MP, int RT, int KS>
 struct MfmaGeom {
     static_assert(CB % 8 == 0, "chunks hold whole 144-byte groups of 8 blocks");
-    static_assert(MP == 4 || MP == 8 || MP == 16 || MP == 32, "padded column count");
+    static_assert(MP == 4 || MP == 8 || MP == 16 || MP == 24 || MP == 32, "padded column count");
     static constexpr int kW = RT * KS;                           // waves per workgroup
-    static_assert(kW == 4 || kW == 8 || kW == 16, "4, 8 or 16 waves");
+    static_assert(kW == 4 || kW == 8 || kW == 12 || kW == 16, "4, 8, 12 or 16 waves");
     static constexpr int kNT = (MP + 15) / 16;                   // 16-column MFMA tiles
     // weights: 16 rows x CB blocks
     static constexpr int kWSlotsUsed = CB * WF::kBlockBytes / 16;
@@ -182,12 +182,14 @@ __device__ __forceinline__ void copy_acts(const uint8_t* __restrict__ Xq, uint32
     }
 }
 
-// Waits until at most q iterations' copies of this wave are outstanding.
+// Waits until at most q iterations' copies of this wave are outstanding
+// (q <= DEPTH - 1; the count is an immediate, so each q has its own wait).
 template <int COPIES, int DEPTH>
 __device__ __forceinline__ void wait_iterations_ahead(int q) {
     if (DEPTH == 1 || q == 0) wait_vmcnt<0>();
-    else if (DEPTH > 2 && q == 1) wait_vmcnt<COPIES>();
+    else if (q == 1) wait_vmcnt<COPIES>();
     else if (DEPTH > 3 && q == 2) wait_vmcnt<(DEPTH > 3 ? 2 * COPIES : 0)>();
+    else if (DEPTH > 4 && q == 3) wait_vmcnt<(DEPTH > 4 ? 3 * COPIES : 0)>();
     else wait_vmcnt<(DEPTH > 1 ? (DEPTH - 1) * COPIES : 0)>();
 }
 
@@ -197,7 +199,8 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
         int N, int K, int M) {
     using G = MfmaGeom<WF, CB, MP, RT, KS>;
     constexpr int NT = G::kNT;
-    static_assert(DEPTH >= 1 && DEPTH <= 3, "pipeline depth");
+    constexpr int GB = RT * KS >= 12 ? 4 : 8;   // blocks per operand group
+    static_assert(DEPTH >= 1 && DEPTH <= 5, "pipeline depth");
     static_assert(G::kCopies * (DEPTH - 1) <= 63, "wait count exceeds the vmcnt field");
     extern __shared__ u32x4 mfma_lds[];
     uint8_t* const lds = reinterpret_cast<uint8_t*>(mfma_lds);
@@ -211,9 +214,10 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
     const int nchunks = (nblk + CB - 1) / CB;
     const int iters = (nchunks + KS - 1) / KS;
     const int ngroups = (N + 16 * RT - 1) / (16 * RT);
-    // A-operand column of this lane and d8 columns of its outputs (MP < 16:
-    // the MFMA rows past MP re-read columns m % MP; those results are dropped)
-    const int acol = MP < 16 ? (rn & (MP - 1)) : rn;
+    // A-operand column of this lane in column tile t: 16t + rn, or, for the
+    // MFMA rows past MP (MP = 4, 8, 24), a column of the same tile re-read
+    // (16t + rn % (MP - 16t)); those results are dropped
+    auto acol = [&](int t) { return 16 * t + rn < MP ? 16 * t + rn : 16 * t + rn % (MP - 16 * t); };
     auto wbuf = [&](int d) { return lds + d * G::kStageBytes + wave * G::kWBufBytes; };
     auto abuf = [&](int d) { return lds + d * G::kStageBytes + G::kW * G::kWBufBytes; };
     const uint32_t dwidth = g == 0 ? 16u : 0u;   // lane group 0 feeds d4 to k-slot 0 of the scale products
@@ -261,15 +265,17 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
                 const int cb = nblk - ch * CB < CB ? nblk - ch * CB : CB;   // a multiple of 8
                 const uint8_t* rowp = wbuf(slot) + rn * G::kWRowSlots * 16;
                 const uint8_t* ap = abuf(slot) + part * G::kAPartBytes;
-                // Groups of 8 blocks in three phases, so that the 16 (or 32)
-                // matrix-core operations of a group are independent of one
-                // another and of the scaling (each block has its own result
-                // registers): operands, then every MFMA, then the fp32 scaling.
-                for (int o = 0; o < cb; o += 8) {
-                    long bop[8];
-                    uint32_t h4[8];
+                // Groups of GB blocks (8, or 4 in workgroups of 12 or more
+                // waves, whose 128-170 VGPRs would not hold 8) in three
+                // phases, so that the matrix-core operations of a group are
+                // independent of one another and of the scaling (each block
+                // has its own result registers): operands, then every MFMA,
+                // then the fp32 scaling.
+                for (int o = 0; o < cb; o += GB) {
+                    long bop[GB];
+                    uint32_t h4[GB];
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) {   // block pairs o + 2p, o + 2p + 1
+                    for (int p = 0; p < GB / 2; ++p) {   // block pairs o + 2p, o + 2p + 1
                         const uint32_t* wp =
                             reinterpret_cast<const uint32_t*>(rowp + ((o >> 1) + p) * 2 * WF::kBlockBytes);
                         float dunused[2];
@@ -278,31 +284,31 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
                     }
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
-                        long aop[8];
-                        uint32_t a8[8];
+                        long aop[GB];
+                        uint32_t a8[GB];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            // A: code dwords g and 4 + g of column 16t + acol, block o + i,
+                        for (int i = 0; i < GB; ++i) {
+                            // A: code dwords g and 4 + g of column acol(t), block o + i,
                             // and the block's binary16 d8 (the low half of its first dword)
                             const uint32_t* ab = reinterpret_cast<const uint32_t*>(
-                                ap + ((16 * t + acol) * G::kAColSlots * 16 + (o + i) * kQ81Bytes));
+                                ap + (acol(t) * G::kAColSlots * 16 + (o + i) * kQ81Bytes));
                             aop[i] = (long)((uint64_t)ab[1 + g] | ((uint64_t)ab[5 + g] << 32));
                             a8[i] = ab[0] & 0xFFFFu;
                         }
-                        i32x4 dsum[8];
+                        i32x4 dsum[GB];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i)
+                        for (int i = 0; i < GB; ++i)
                             dsum[i] = WF::kOffset ? __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[i], kNeg8,
                                                                                          i32x4{0, 0, 0, 0}, 0, 0, 0)
                                                   : i32x4{0, 0, 0, 0};
 #pragma unroll
-                        for (int i = 0; i < 8; ++i)
+                        for (int i = 0; i < GB; ++i)
                             dsum[i] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[i], bop[i], dsum[i], 0, 0, 0);
-                        f32x4 sc[8];
+                        f32x4 sc[GB];
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) sc[i] = scale_outer(a8[i], h4[i]);
+                        for (int i = 0; i < GB; ++i) sc[i] = scale_outer(a8[i], h4[i]);
 #pragma unroll
-                        for (int i = 0; i < 8; ++i)
+                        for (int i = 0; i < GB; ++i)
 #pragma unroll
                             for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)dsum[i][r], sc[i][r], acc[t][r]);
                     }
@@ -361,12 +367,13 @@ hipError_t launch_mfma_cfg(const void* Wq, const void* Xq, float* Y, int N, int 
 template <class WF, int CB, int MP, int RT, int KS, int DEPTH>
 constexpr bool mfma_builds() {
     // the stages fit the LDS of one workgroup, the wait counts fit the vmcnt
-    // field, and 16-wave workgroups (128 VGPRs per lane) are kept to 16
-    // columns, and to 8 when each of the 16 waves has a part of K (more
-    // activation copies per wave)
+    // field, and the workgroups whose waves would exceed their registers (128
+    // per lane at 16 waves, 170 at 12) and spill are not built: 12 and 16
+    // waves up to 24 columns, 16 parts of K up to 16, and Q8_0 (wider
+    // weight operands) at 16 waves up to 16
     return mfma_lds_bytes<WF, CB, MP, RT, KS, DEPTH>() <= 160 * 1024 &&
-           MfmaGeom<WF, CB, MP, RT, KS>::kCopies * (DEPTH - 1) <= 63 && (RT * KS < 16 || MP <= 16) &&
-           (KS < 16 || MP <= 8);
+           MfmaGeom<WF, CB, MP, RT, KS>::kCopies * (DEPTH - 1) <= 63 && (RT * KS < 12 || MP <= 24) &&
+           (KS < 16 || MP <= 16) && (RT * KS < 16 || MP <= 16 || WF::kBlockBytes == 18);
 }
 
 // The built configurations for one padded column count MP.
@@ -379,9 +386,11 @@ hipError_t launch_mfma_mp(int RT, int KS, int DEPTH, int CB, const void* Wq, con
             return launch_mfma_cfg<WF, CC, MP, RR, SS, DD>(Wq, Xq, Y, N, K, M, grid, s); \
     }
     DG_MF(1, 16, 1, 8) DG_MF(2, 8, 1, 8) DG_MF(4, 4, 2, 8)                       // 16 waves
+    DG_MF(1, 12, 1, 8) DG_MF(3, 4, 1, 8)                                          // 12 waves
     DG_MF(1, 8, 1, 8) DG_MF(1, 8, 2, 8) DG_MF(2, 4, 2, 8) DG_MF(4, 2, 2, 8)      // 8 waves
     DG_MF(8, 1, 2, 8)
     DG_MF(4, 1, 2, 8) DG_MF(4, 1, 3, 8) DG_MF(2, 2, 2, 8) DG_MF(1, 4, 2, 8)      // 4 waves
+    DG_MF(1, 4, 3, 8) DG_MF(1, 4, 4, 8) DG_MF(1, 4, 5, 8) DG_MF(2, 2, 3, 8) DG_MF(2, 2, 4, 8)
 #undef DG_MF
     return hipErrorInvalidValue;
 }
@@ -401,8 +410,9 @@ hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float
         // Measured on MI355X (decoder shapes, M = 2..24), both formats.  Up to
         // 512 row tiles: one tile per workgroup, K split over 8 waves up to 8
         // columns (4 for Q4_0 rows up to 4096) and beyond 16 on rows up to
-        // 8192 (one chunk deep there, as the chunks of 32 columns fill the
-        // LDS), else over 4 waves two deep.  More row tiles: tiles share each
+        // 8192 (one chunk deep there, as the chunks of 24 columns fill the
+        // LDS), over 12 waves one deep beyond 16 on longer Q4_0 rows, else
+        // over 4 waves two deep.  More row tiles: tiles share each
         // activation chunk.
         const int tiles = (N + 15) / 16;
         CB = 8;
@@ -412,6 +422,7 @@ hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float
             const bool few = M <= 8 && (K > 4096 || WF::kBlockBytes == 34);
             KS = (few || wide) ? 8 : 4;
             DEPTH = wide ? 1 : 2;
+            if (M > 16 && K > 8192 && WF::kBlockBytes == 18) { KS = 12; DEPTH = 1; }   // 17..24 columns, long rows
         } else if (WF::kBlockBytes == 34) {
             // Q8_0: its weight buffers are twice those of Q4_0, so fewer row
             // tiles share a workgroup's LDS.
@@ -427,7 +438,7 @@ hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float
     if (M <= 4) return launch_mfma_mp<WF, 4>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
     if (M <= 8) return launch_mfma_mp<WF, 8>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
     if (M <= 16) return launch_mfma_mp<WF, 16>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
-    return launch_mfma_mp<WF, 32>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
+    return launch_mfma_mp<WF, 24>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
 }
 
 }  // namespace

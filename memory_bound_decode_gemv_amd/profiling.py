@@ -163,6 +163,77 @@ def trace_segments(trace_csv, min_launches=30, idle_us=200.0):
     return out
 
 
+def launch_runs(trace_csv, min_launches=30, idle_us=5000.0):
+    """Every run of back-to-back launches (any kernel of the library) in
+    launch order: a run ends at an idle gap of more than idle_us.  For each:
+    kernel, launches, median duration (end - start), median gap (next start -
+    this end) and median period (next start - this start), in microseconds."""
+    rows = []
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            if "dg::" in r["Kernel_Name"]:
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    runs, cur = [], [rows[0]] if rows else []
+    for a, b in zip(rows, rows[1:]):
+        if (b[0] - a[1]) / 1e3 > idle_us:
+            runs.append(cur)
+            cur = []
+        cur.append(b)
+    if cur:
+        runs.append(cur)
+    out = []
+    for run in runs:
+        if len(run) < min_launches:
+            continue
+        med = lambda v: sorted(v)[len(v) // 2]
+        dur = [(e - s) / 1e3 for s, e, _ in run]
+        gap = [(b[0] - a[1]) / 1e3 for a, b in zip(run, run[1:])]
+        per = [(b[0] - a[0]) / 1e3 for a, b in zip(run, run[1:])]
+        out.append((short_name(run[0][2]), len(run), med(dur), med(gap), med(per)))
+    return out
+
+
+def launch_cost_markdown(trace_csv, command, labels, nbytes):
+    """The runs of a --profile-launch-cost trace, and for each workload that is
+    not a plain read the split of its duration into streaming (bytes over the
+    rate fitted between the two largest reads), the launch floor (the first
+    workload: one wave, one 16-byte load) and the rest (ramp and drain)."""
+    runs = launch_runs(trace_csv)
+    lines = ["# Per-launch cost of back-to-back launches (rocprofv3 --kernel-trace)", "", "Command:", ""]
+    lines += [f"    {c}" for c in command.split(" ;; ")]
+    lines += ["",
+              "Each row is one graph of back-to-back launches, replayed three times back to back (medians over "
+              "every launch of the run).  duration = end - start of a kernel; gap = next start - this end; "
+              "period = next start - this start, the time per launch back to back.", "",
+              "| workload | bytes per launch | kernel | launches | median duration us | median gap us | "
+              "median period us |", "|---|---|---|---|---|---|---|"]
+    rows = list(zip(labels, nbytes, runs))
+    for lab, nb, (name, n, dur, gap, per) in rows:
+        lines.append(f"| {lab} | {nb} | {name} | {n} | {dur:.3f} | {gap:.3f} | {per:.3f} |")
+    reads = sorted([(nb, r[2]) for lab, nb, r in rows if lab.startswith("read ")])
+    if len(reads) >= 2 and rows:
+        (b1, t1), (b2, t2) = reads[-2], reads[-1]
+        rate = (b2 - b1) / (t2 - t1) / 1e3   # GB/s
+        floor = rows[0][2][2]
+        lines += ["", "Under kernel tracing every dispatch carries the profiler's own overhead (the gaps of the "
+                  "short kernels); for kernels longer than that the next dispatch is ready before the current one "
+                  "ends (gap 0), as in a graph replayed without the profiler.", "",
+                  f"Split of each GEMV's duration: streaming = bytes / {rate:.0f} GB/s (the slope between the two "
+                  f"largest reads), the launch floor {floor:.3f} us (the shortest kernel that reads memory), and "
+                  "the rest (ramp and drain).  No kernel that reads HBM finishes below the floor, so a launch over "
+                  "B bytes cannot take less than floor + B / rate.", "",
+                  "| workload | streaming us | floor us | rest us | duration us | floor + streaming: best GB/s |",
+                  "|---|---|---|---|---|---|"]
+        for lab, nb, (name, n, dur, gap, per) in rows[1:]:
+            if lab.startswith("read ") or not nb:
+                continue
+            st = nb / rate / 1e3
+            lines.append(f"| {lab} | {st:.2f} | {floor:.2f} | {dur - floor - st:.2f} | {dur:.2f} | "
+                         f"{nb / (floor + st) / 1e3:.0f} |")
+    return "\n".join(lines) + "\n"
+
+
 def trace_markdown(stats_csv, command, trace_csv=None):
     lines = ["# Kernel durations from rocprofv3 --kernel-trace --stats", "", "Commands:", ""]
     lines += [f"    {c}" for c in command.split(" ;; ")]
@@ -356,6 +427,12 @@ def main(argv=None):
     q.add_argument("--filter", default=None)
     q.add_argument("--condense", action="store_true",
                    help="one line per (workload, M): the default launch and the best configuration")
+    lc = sub.add_parser("launchcost")
+    lc.add_argument("trace_csv")
+    lc.add_argument("--md", required=True)
+    lc.add_argument("--command", default="")
+    lc.add_argument("--labels", required=True, help="comma-separated workload names, in launch order")
+    lc.add_argument("--bytes", required=True, help="comma-separated algorithmic bytes per launch, same order")
     t = sub.add_parser("trace")
     t.add_argument("stats_csv")
     t.add_argument("--md", required=True)
@@ -380,6 +457,10 @@ def main(argv=None):
                 f.write(suite_condensed_markdown(a.jsonl, a.command, a.filter))
             else:
                 f.write(suite_markdown(a.jsonl[0], a.command, a.filter))
+    elif a.cmd == "launchcost":
+        with open(a.md, "w") as f:
+            f.write(launch_cost_markdown(a.trace_csv, a.command, a.labels.split(","),
+                                         [int(x) for x in a.bytes.split(",")]))
     else:
         with open(a.md, "w") as f:
             f.write(trace_markdown(a.stats_csv, a.command, a.runs))

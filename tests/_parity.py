@@ -68,3 +68,43 @@ def res_default(block_bytes, N, M, K):
     if not res_runs(block_bytes, cfg[0], cfg[1], M, K):
         cfg = (1, 4, 2)
     return cfg
+
+
+# Configurations of the streaming matrix-core kernel the library builds:
+# (RT row tiles, KS parts of K, DEPTH chunks staged, CB blocks per chunk);
+# launch override unroll = RT*10000 + KS*100 + DEPTH*10 + CB/8.  Which column
+# counts each serves follows from its LDS (one stage: every wave's 16 weight
+# rows of a chunk, rows padded to an odd number of 16-byte slots, and the
+# activation chunks of MP >= M columns; MP = 4, 8, 16 or 24) and the limits
+# the library applies against register spills (12- and 16-wave workgroups up
+# to 24 columns, 16 parts of K up to 16, Q8_0 at 16 waves up to 16).
+MFMA_CONFIGS = [(1, 16, 1, 8), (2, 8, 1, 8), (4, 4, 2, 8), (1, 12, 1, 8), (3, 4, 1, 8), (1, 8, 1, 8), (1, 8, 2, 8),
+                (2, 4, 2, 8), (4, 2, 2, 8), (8, 1, 2, 8), (4, 1, 2, 8), (4, 1, 3, 8), (2, 2, 2, 8), (1, 4, 2, 8),
+                (1, 4, 3, 8), (1, 4, 4, 8), (1, 4, 5, 8), (2, 2, 3, 8), (2, 2, 4, 8)]
+
+
+def mfma_unroll(rt, ks, d, cb):
+    return rt * 10000 + ks * 100 + d * 10 + cb // 8
+
+
+def mfma_builds(block_bytes, rt, ks, depth, cb, mp):
+    w = rt * ks
+    nt = (mp + 15) // 16
+    wrow = (cb * block_bytes // 16) | 1
+    cw = (16 * wrow + 63) // 64
+    acol = (cb * 36 // 16) | 1
+    apart = mp * acol
+    ca = (apart + 63) // 64 if rt == 1 else (ks * apart + w * 64 - 1) // (w * 64)
+    stage = w * cw * 1024 + ca * w * 1024
+    lds = max(depth * stage, w * nt * 4 * 64 * 4)
+    return (lds <= LDS_PER_WORKGROUP and (cw + ca) * (depth - 1) <= 63 and (w < 12 or mp <= 24)
+            and (ks < 16 or mp <= 16) and (w < 16 or mp <= 16 or block_bytes == 18))
+
+
+def mfma_max_columns(block_bytes, rt, ks, depth, cb):
+    """The largest column count the configuration takes (0: not built)."""
+    best = 0
+    for mp in (4, 8, 16, 24):
+        if mfma_builds(block_bytes, rt, ks, depth, cb, mp):
+            best = mp
+    return best

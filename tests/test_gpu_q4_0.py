@@ -146,19 +146,11 @@ def test_q4_0_lds_row_copy_shapes(dg, dev, orc, N, K, launch):
     assert_close(got[0], orc.gemv_q4_0_q8_1(Wq, Xq, N, K, 1)[0], TOL, f"{N}x{K} {launch}")
 
 
-# Matrix-core configurations the library builds: (RT row tiles, KS parts of K,
-# DEPTH, CB) -> the largest column count they serve (their LDS must fit one
-# workgroup).  Launch override: unroll = RT*10000 + KS*100 + DEPTH*10 + CB/8.
-MFMA_TABLE = {(1, 16, 1, 8): 8, (4, 4, 2, 8): 16, (1, 8, 2, 8): 16,
-              (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (2, 4, 2, 8): 24, (4, 2, 2, 8): 24, (8, 1, 2, 8): 24,
-              (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24, (1, 4, 2, 8): 24}
+from tests._parity import MFMA_CONFIGS, mfma_max_columns, mfma_unroll  # noqa: E402
 
-
-def _mfma_unroll(rt, ks, d, cb):
-    return rt * 10000 + ks * 100 + d * 10 + cb // 8
-
-
-MFMA_CFGS = [dict(variant=14)] + [dict(variant=14, unroll=_mfma_unroll(*c)) for c in MFMA_TABLE]
+MFMA_TABLE = {c: mfma_max_columns(18, *c) for c in MFMA_CONFIGS}
+_mfma_unroll = mfma_unroll
+MFMA_CFGS = [dict(variant=14)] + [dict(variant=14, unroll=mfma_unroll(*c)) for c in MFMA_CONFIGS if MFMA_TABLE[c]]
 
 
 def _mfma_supported(launch, M):
@@ -269,7 +261,7 @@ def test_q4_0_overrides_beyond_kernel_limits_are_rejected(dg, dev):
                       (2, dict(variant=11)), (2, dict(variant=13)), (1, dict(variant=12, block=128)),
                       (5, dict(variant=12, unroll=4)), (1, dict(variant=99)),
                       (4, dict(variant=14, unroll=124)), (4, dict(variant=14, unroll=21622)),
-                      (4, dict(variant=14, unroll=10412)), (4, dict(variant=14, unroll=10441)),
+                      (4, dict(variant=14, unroll=10412)), (4, dict(variant=14, unroll=10461)),
                       (20, dict(variant=14, unroll=11611)), (20, dict(variant=14, unroll=10821)),
                       (5, dict(variant=15)), (1, dict(variant=15, block=512)), (1, dict(variant=15, unroll=5))):
         with pytest.raises(dg.DGError) as e:

@@ -20,9 +20,9 @@ TOL = 1e-3   # per-row floored relative error vs the oracle
 
 # Matrix-core configurations built for Q8_0: (RT, KS, DEPTH, CB) -> the
 # largest column count they serve (their LDS must fit one workgroup).
-MFMA_TABLE = {(1, 16, 1, 8): 8, (2, 8, 1, 8): 16, (1, 8, 1, 8): 24, (1, 8, 2, 8): 16, (2, 4, 2, 8): 24,
-              (4, 2, 2, 8): 24, (8, 1, 2, 8): 24, (4, 1, 2, 8): 24, (4, 1, 3, 8): 24, (2, 2, 2, 8): 24,
-              (1, 4, 2, 8): 24}
+from tests._parity import MFMA_CONFIGS, mfma_max_columns  # noqa: E402
+
+MFMA_TABLE = {c: c_max for c in MFMA_CONFIGS if (c_max := mfma_max_columns(34, *c))}
 
 
 def _unroll(rt, ks, d, cb):
@@ -200,7 +200,7 @@ def test_q8_0_overrides_beyond_kernel_limits_are_rejected(dg, dev):
     X = torch.zeros(24 * K // 32 * 36, dtype=torch.uint8, device=dev)
     Y = torch.zeros(24 * N, dtype=torch.float32, device=dev)
     for M, launch in ((1, dict(variant=21, block=512)), (2, dict(variant=21)), (1, dict(variant=12)),
-                      (4, dict(variant=22, unroll=40421)), (12, dict(variant=22, unroll=11611)),
+                      (4, dict(variant=22, unroll=40421)), (20, dict(variant=22, unroll=11611)),
                       (4, dict(variant=22, block=256)), (1, dict(variant=99)), (5, dict(variant=23)),
                       (1, dict(variant=23, unroll=5))):
         with pytest.raises(dg.DGError) as e:
