@@ -4,11 +4,16 @@ Each mutant is a copy of oracle/oracle.c with one plausible mistake planted in
 it (a dropped term, a wrong sign or offset, swapped nibbles, a transposed
 operand, a misused leading dimension, a wrong tie rule, a wrong rounding).
 The mutant is compiled into a temporary library and every pin in
-test_oracle_pins.py is run against it: at least one pin must fail.  The
-planted mistakes exist only in the temporary copies, never in oracle.c.
+test_oracle_pins.py is run against it, in a child process: at least one pin
+must fail.  A mistake in an index can also make a pin read outside its
+arrays; when the child dies of a signal, that pin has caught the mutant too
+(and the test process survives it).  The planted mistakes exist only in the
+temporary copies, never in oracle.c.
 """
 import inspect
 import os
+import subprocess
+import sys
 
 import pytest
 
@@ -90,6 +95,28 @@ def test_mutant_list_applies_to_the_current_source():
         assert src.count(old) >= 1, name
 
 
+def run_pins(lib):
+    """Every pin against the library at `lib`; returns the names of the pins
+    that failed (the child process's side)."""
+    failed = []
+    with oracle.use_library(lib):
+        for pin_name, fn, kw in _pin_calls():
+            try:
+                fn(oracle, **kw)
+            except (AssertionError, ValueError, IndexError, OverflowError):
+                failed.append(pin_name)
+    return failed
+
+
+_CHILD = """
+import sys
+from tests import test_oracle_mutants as m
+failed = m.run_pins(sys.argv[1])
+print("caught by:", ", ".join(failed) if failed else "-")
+sys.exit(0 if failed else 1)
+"""
+
+
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_some_pin_catches_the_mutant(tmp_path, orc, name, old, new):
     src = open(SRC).read()
@@ -97,11 +124,10 @@ def test_some_pin_catches_the_mutant(tmp_path, orc, name, old, new):
     mutant = tmp_path / "oracle_mutant.c"
     mutant.write_text(src.replace(old, new, 1))
     lib = oracle.compile_c(str(mutant), str(tmp_path / "liboracle_mutant.so"))
-    failed = []
-    with oracle.use_library(lib):
-        for pin_name, fn, kw in _pin_calls():
-            try:
-                fn(orc, **kw)
-            except (AssertionError, ValueError, IndexError, OverflowError):
-                failed.append(pin_name)
-    assert failed, f"no pin caught the mutant '{name}'"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTHONPATH=os.pathsep.join([root, os.environ.get("PYTHONPATH", "")]))
+    r = subprocess.run([sys.executable, "-c", _CHILD, lib], cwd=root, env=env, capture_output=True, text=True,
+                       timeout=600)
+    if r.returncode < 0:
+        return   # a pin ran into the planted mistake hard enough to kill the process
+    assert r.returncode == 0, f"no pin caught the mutant '{name}'\n{r.stdout}\n{r.stderr[-2000:]}"
