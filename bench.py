@@ -656,6 +656,8 @@ def suite(args):
         suite_q8_0(dg, torch, emit, ceil_gbps)
     if want("m1"):
         suite_m1_rows_vs_units(dg, torch, emit, ceil_gbps)
+    if want("fused"):
+        suite_fused_quant(dg, torch, emit, ceil_gbps)
     if want("argmax"):
         suite_argmax(dg, torch, emit, ceil_gbps)
     if want("tail"):
@@ -913,6 +915,59 @@ def suite_m1_rows_vs_units(dg, torch, emit, ceil_gbps):
             torch.cuda.empty_cache()
 
 
+def suite_fused_quant(dg, torch, emit, ceil_gbps):
+    """The Q8_1 conversion before a Q4_0 GEMV: the GEMV alone on Q8_1 columns,
+    the quantiser's launch followed by the GEMV's, dg_gemv_q4_0_f32 (the same
+    two launches in one call) and, for one column, its one-launch form over
+    grids and row depths; per call over rotated weight copies."""
+    import synth
+    for (N, K, M) in [(Q4_N, Q4_K, 1), (4096, 4096, 1), (14336, 4096, 1), (4096, 14336, 24), (14336, 4096, 24)]:
+        nc = copies_for(18 * N * K // 32)
+        Wq = q4_copies(8, N, K, nc)
+        x = torch.stack([synth.gpu_normal((8, synth.KIND_X, 0, m), (K,), 1.0, torch.float32) for m in range(M)])
+        x = x.contiguous()
+        Xq = torch.empty(M * (K // 32) * 36, dtype=torch.uint8, device="cuda")
+        dg.dg_quantize_q8_1(x, Xq, M, K)
+        Y = torch.empty(M * N, dtype=torch.float32, device="cuda")
+        nb = bytes_q4(N, K, M)
+        calls = [(lambda c=c: dg.dg_gemv_q4_0(Wq[c % nc], Xq, Y, N, K, M)) for c in range(n_calls(nc))]
+        us_g, iqr = time_per_call(calls)
+        emit(record(f"gemv_q4_0 {N}x{K}", us_g, iqr, nb, ceil_gbps, M=M, copies=nc, variant="Q8_1 given"))
+        calls = [(lambda: dg.dg_quantize_q8_1(x, Xq, M, K))] * MIN_CALLS
+        us_q, iqr = time_per_call(calls)
+        emit(record(f"quantize_q8_1 [{M},{K}]", us_q, iqr, M * K * 4 + M * (K // 32) * 36, None))
+        calls = []
+        for c in range(n_calls(nc)):
+            calls.append(lambda: dg.dg_quantize_q8_1(x, Xq, M, K))
+            calls.append(lambda c=c: dg.dg_gemv_q4_0(Wq[c % nc], Xq, Y, N, K, M))
+        us2, iqr = time_per_call(calls)
+        us_two = 2 * us2
+        emit(record(f"gemv_q4_0 {N}x{K}", us_two, 2 * iqr, nb + M * K * 4, ceil_gbps, M=M, copies=nc,
+                    variant="quantiser, then GEMV (two launches)"))
+        calls = [(lambda c=c: dg.dg_gemv_q4_0_f32(Wq[c % nc], x, Y, N, K, M, Xq=Xq)) for c in range(n_calls(nc))]
+        us_f, iqr = time_per_call(calls)
+        emit(record(f"gemv_q4_0 {N}x{K}", us_f, iqr, nb + M * K * 4, ceil_gbps, M=M, copies=nc,
+                    variant="dg_gemv_q4_0_f32", saved_vs_two_launches_us=round(us_two - us_f, 3),
+                    over_gemv_alone_us=round(us_f - us_g, 3)))
+        if M == 1:   # the one-launch form's grid and row depth
+            for g in (0, 256, 512, 768, 1024, 1536):
+                for d in ((0,) if g == 0 else (2, 3, 4)):
+                    launch = dict(variant=13, grid=g, block=256 if g else 0, unroll=d)
+                    calls = [(lambda c=c, launch=launch: dg.dg_gemv_q4_0_f32(Wq[c % nc], x, Y, N, K, M, Xq=Xq,
+                                                                             launch=launch))
+                             for c in range(n_calls(nc))]
+                    try:
+                        calls[0]()
+                    except dg.DGError:
+                        continue
+                    us, iqr = time_per_call(calls)
+                    emit(record(f"gemv_q4_0 {N}x{K}", us, iqr, nb + M * K * 4, ceil_gbps, M=M, copies=nc,
+                                variant=(f"dg_gemv_q4_0_f32 one launch, grid {g} depth {d}" if g else
+                                         "dg_gemv_q4_0_f32 one launch, default grid")))
+        del Wq
+        torch.cuda.empty_cache()
+
+
 def suite_argmax(dg, torch, emit, ceil_gbps):
     # argmax: hot (one buffer) and cold (rotated copies for the 256 MB shape)
     import synth
@@ -1147,7 +1202,7 @@ def main():
     ap.add_argument("--profile-small-m", action="store_true",
                     help="launch the small-batch Q4_0 GEMV eagerly on the decoder shapes (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
-                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q8,m1,argmax,tail,nf4")
+                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q8,m1,fused,argmax,tail,nf4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=16.0,
                     help="seconds of oracle work for cpu_baseline (half on one core, half on all)")

@@ -158,6 +158,38 @@ dg_status dg_gemv_q4_0(const void* Wq, const void* Xq, float* Y,
                        int64_t N, int64_t K, int M, dg_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Q4_0 weights x fp32 activations: the Q8_1 quantisation and the GEMV in one
+ * call
+ *
+ *   Xq = Q8_1(x) exactly as dg_quantize_q8_1 stores it, then
+ *   Y  = exactly dg_gemv_q4_0(Wq, Xq, Y, N, K, M)
+ *
+ * The activation conversion before every quantised GEMV is the unfused step
+ * the "Capability Gain" paper's LLM-decode notes price at 27.9 us per call,
+ * more than the matrix product at a fifth of its cells.  Here it is the
+ * quantiser's launch (one lane per activation, about 1.8 us for a column of
+ * 8192), then the GEMV's.  A one-launch form for one column (M = 1, K <=
+ * 16384), in which every workgroup of the row-streaming GEMV quantises the
+ * column into its LDS copy while its first weight rows are in flight, is
+ * selected by dg_gemv_q4_0_f32_ex with variant DG_VARIANT_Q4_LDSROW; on
+ * MI355X it is slower than the two launches (each of hundreds of workgroups
+ * repeats the whole conversion), so it is not the default.  With several
+ * columns, whose matrix-core kernels re-stage the columns for every 16-row
+ * tile, a conversion inside the GEMV would be repeated for every tile.
+ *
+ *   Wq, Y, N, K, M  as for dg_gemv_q4_0.
+ *   x   device float32 [M][K], rows packed; 16-byte aligned.
+ *   Xq  device, M columns of K/32 Q8_1 blocks (36 bytes each), 16-byte
+ *       aligned: receives the quantised columns, byte for byte those of
+ *       dg_quantize_q8_1 (so later calls on the same activations, such as
+ *       the gate and up projections, can use dg_gemv_q4_0 on them).
+ *       Required, except by the one-launch form (there NULL stores nothing).
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+dg_status dg_gemv_q4_0_f32(const void* Wq, const float* x, float* Y, void* Xq,
+                           int64_t N, int64_t K, int M, dg_stream stream);
+
+/* ------------------------------------------------------------------------
  * Q8_0 weights x Q8_1 activations, M = 1..24 activation columns
  *
  *   Y[m][n] = sum_b dw(n,b) * d8(m,b) * sum_{j<32} qw(n,b,j) * q8(m,b,j)
@@ -426,6 +458,12 @@ dg_status dg_gemv_q8_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, i
                           int M, const dg_launch* cfg, dg_stream stream);
 dg_status dg_gemv_nf4_ex(const void* codes, const float* absmax, const float* table, const void* x, float* y,
                          int64_t N, int64_t K, int B, const dg_launch* cfg, dg_stream stream);
+/* dg_gemv_q4_0_f32 with a launch override: variant DG_VARIANT_Q4_LDSROW
+ * selects the one-launch form (M = 1, K <= 16384), with its grid, block and
+ * unroll (row buffers per wave, 2..4); 0 fields are defaults.  The default
+ * (two-launch) form takes no other override. */
+dg_status dg_gemv_q4_0_f32_ex(const void* Wq, const float* x, float* Y, void* Xq, int64_t N, int64_t K, int M,
+                              const dg_launch* cfg, dg_stream stream);
 
 #ifdef __cplusplus
 }

@@ -72,7 +72,7 @@ EXPORTED = (
     "dg_gemv_q8_0", "dg_gemv_q8_0_ex", "dg_quantize_q8_0",
     "dg_argcompare_rows", "dg_gemv_bf16_argmax_workspace_bytes", "dg_gemv_bf16_argmax",
     "dg_gemv_nf4", "dg_gemv_nf4_ex", "dg_quantize_nf4",
-    "dg_argmax_rows_noalloc",
+    "dg_argmax_rows_noalloc", "dg_gemv_q4_0_f32", "dg_gemv_q4_0_f32_ex",
 )
 
 # Size of the library's fixed per-device argmax key array (include/decodegemv.h).
@@ -154,6 +154,10 @@ def _lib():
     lib.dg_argmax_rows.restype = st
     lib.dg_argmax_rows_noalloc.argtypes = [P, P, I64, I64, I64, P]
     lib.dg_argmax_rows_noalloc.restype = st
+    lib.dg_gemv_q4_0_f32.argtypes = [P, P, P, P, I64, I64, I32, P]
+    lib.dg_gemv_q4_0_f32.restype = st
+    lib.dg_gemv_q4_0_f32_ex.argtypes = [P, P, P, P, I64, I64, I32, P, P]
+    lib.dg_gemv_q4_0_f32_ex.restype = st
     lib.dg_argcompare_rows.argtypes = [P, I32, I32, P, I64, I64, I64, P, ctypes.c_size_t, P]
     lib.dg_argcompare_rows.restype = st
     lib.dg_gemv_bf16_argmax_workspace_bytes.argtypes = [I64, I64]
@@ -306,6 +310,36 @@ def _gemv_quant(name, block_bytes, Wq, Xq, Y, N, K, M, launch, stream):
 def dg_gemv_q4_0(Wq, Xq, Y, N, K, M, launch=None, stream=None):
     """Y[M][N] (float32) from Q4_0 weight bytes and Q8_1 activation bytes (uint8 tensors)."""
     return _gemv_quant("dg_gemv_q4_0", 18, Wq, Xq, Y, N, K, M, launch, stream)
+
+
+def dg_gemv_q4_0_f32(Wq, x, Y, N, K, M, Xq=None, launch=None, stream=None):
+    """Y[M][N] (float32) from Q4_0 weight bytes and float32 activations x[M][K]:
+    the Q8_1 quantisation and the GEMV in one call (two launches; the
+    one-launch form for M = 1 is launch=dict(variant=DG_VARIANT_Q4_LDSROW)).
+    Xq (uint8, M*K/32*36 bytes) receives the quantised columns; required
+    except by the one-launch form."""
+    torch = _torch()
+    _need(Wq, (torch.uint8,), "Wq")
+    _need(x, (torch.float32,), "x")
+    _need(Y, (torch.float32,), "Y")
+    N, K, M = int(N), int(K), int(M)
+    if Xq is not None:
+        _need(Xq, (torch.uint8,), "Xq")
+    if N > 0 and K > 0 and M > 0:
+        _fits(Wq, N * (K // 32) * 18, "Wq")
+        _fits(x, M * K * 4, "x")
+        if Xq is not None:
+            _fits(Xq, M * (K // 32) * 36, "Xq")
+    if N > 0 and M > 0:
+        _fits(Y, M * N * 4, "Y")
+    xq = _ptr(Xq) if Xq is not None else None
+    if launch is None:
+        st = _lib().dg_gemv_q4_0_f32(_ptr(Wq), _ptr(x), _ptr(Y), xq, N, K, M, _stream(stream))
+    else:
+        st = _lib().dg_gemv_q4_0_f32_ex(_ptr(Wq), _ptr(x), _ptr(Y), xq, N, K, M, ctypes.byref(_cfg(**launch)),
+                                        _stream(stream))
+    _check(st, "dg_gemv_q4_0_f32")
+    return Y
 
 
 def dg_gemv_q8_0(Wq, Xq, Y, N, K, M, launch=None, stream=None):

@@ -201,8 +201,33 @@ dg_status dg_gemv_q8_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, i
     return gemv_quant_checked(true, Wq, Xq, Y, N, K, M, cfg, stream);
 }
 
+dg_status dg_gemv_q4_0_f32_ex(const void* Wq, const float* x, float* Y, void* Xq, int64_t N, int64_t K, int M,
+                              const dg_launch* cfg, dg_stream stream) {
+    if (N < 0 || N > kI32Max || K < 0 || K > kQuantMaxK || K % 256 != 0 || M < 0 || M > 24) return DG_ERR_SHAPE;
+    if (!launch_ok(cfg) || (cfg && cfg->variant && cfg->variant != DG_VARIANT_Q4_LDSROW)) return DG_ERR_ARG;
+    if (N == 0 || M == 0) return DG_OK;
+    const bool one_launch = cfg && cfg->variant == DG_VARIANT_Q4_LDSROW;
+    if (!Y || (K > 0 && (!Wq || !x || (!one_launch && !Xq)))) return DG_ERR_NULL;
+    if (!aligned(Y, 4)) return DG_ERR_MISALIGNED;
+    if (K > 0 && (!aligned(Wq, 16) || !aligned(x, 16) || (Xq && !aligned(Xq, 16)))) return DG_ERR_MISALIGNED;
+    if (K == 0) {   // empty sums: Y = 0 (there are no blocks to store)
+        const int64_t n = N * (int64_t)M;
+        hipLaunchKernelGGL(k_fill_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                           (hipStream_t)stream, Y, n);
+        return hip_status(hipGetLastError());
+    }
+    hipError_t e = launch_gemv_q4_0_f32(Wq, x, Xq, Y, (int)N, (int)K, M, cfg, (hipStream_t)stream);
+    if (e == hipErrorInvalidValue && cfg) return DG_ERR_ARG;
+    return hip_status(e);
+}
+
+dg_status dg_gemv_q4_0_f32(const void* Wq, const float* x, float* Y, void* Xq, int64_t N, int64_t K, int M,
+                           dg_stream stream) {
+    return dg_gemv_q4_0_f32_ex(Wq, x, Y, Xq, N, K, M, nullptr, stream);
+}
+
 dg_status dg_quantize_q8_1(const float* x, void* Xq, int64_t M, int64_t K, dg_stream stream) {
-    if (M < 0 || K < 0 || K % 32 != 0 || M * (K / 32) > kI32Max * 256LL) return DG_ERR_SHAPE;
+    if (M < 0 || K < 0 || K % 32 != 0 || M * (K / 32) > kI32Max * 8LL) return DG_ERR_SHAPE;   // 8 blocks per workgroup
     if (M == 0 || K == 0) return DG_OK;
     if (!x || !Xq) return DG_ERR_NULL;
     if (!aligned(x, 16) || !aligned(Xq, 4)) return DG_ERR_MISALIGNED;

@@ -64,8 +64,14 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
 // the matrix-core kernel for M = 2..24 (unroll = RT*10000 + KS*100 + DEPTH*10
 // + CB/8); a zero
 // depth, unroll, grid or block selects the default.
+// xf != nullptr: fp32 activations quantised by each workgroup into its LDS
+// column (Xq unused); Xq_out, when given, receives the Q8_1 bytes.
 hipError_t launch_q4_m1_ldsrow(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
-                               int block, hipStream_t s);
+                               int block, hipStream_t s, const float* xf = nullptr, void* Xq_out = nullptr);
+// Q4_0 GEMV from fp32 activations: M = 1 (K <= 16384) quantises inside the
+// GEMV (one launch); otherwise the quantiser into Xq, then the GEMV.
+hipError_t launch_gemv_q4_0_f32(const void* Wq, const float* x, void* Xq, float* Y, int N, int K, int M,
+                                const dg_launch* cfg, hipStream_t s);
 // M columns with rows streamed through LDS in units of 64 block pairs (depth
 // = unit buffers per wave); M * ceil(K / 4096) <= 8 (activation pairs held in
 // registers).

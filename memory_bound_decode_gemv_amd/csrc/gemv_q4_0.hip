@@ -247,6 +247,29 @@ hipError_t launch_regs(int S, const void* Wq, const void* Xq, float* Y, int N, i
 
 }  // namespace
 
+// Default: the quantiser's launch, then the GEMV's.  variant
+// DG_VARIANT_Q4_LDSROW selects the one-launch form for one column (K <=
+// 16384): every workgroup of the row-streaming kernel quantises the column
+// into its LDS copy.  Measured on MI355X it is slower than the two launches
+// at every decoder shape (28672 x 8192: 23.8 us at its best grid of 768
+// workgroups against 23.6 us), because each of hundreds of workgroups
+// repeats the conversion of the whole column, while the quantiser's launch
+// costs about 1.8 us.
+hipError_t launch_gemv_q4_0_f32(const void* Wq, const float* x, void* Xq, float* Y, int N, int K, int M,
+                                const dg_launch* cfg, hipStream_t s) {
+    const int S = (K / 64 + kWave - 1) / kWave;
+    if (cfg && cfg->variant == DG_VARIANT_Q4_LDSROW) {
+        if (M != 1 || S > 4) return hipErrorInvalidValue;
+        int grid = cfg->grid, block = cfg->block;
+        if (!grid && !block) { grid = N < 3072 ? (N + 3) / 4 : 768; block = 256; }
+        return launch_q4_m1_ldsrow(K, cfg->unroll, Wq, nullptr, Y, N, grid, block, s, x, Xq);
+    }
+    if (cfg && (cfg->grid || cfg->block || cfg->unroll || cfg->variant)) return hipErrorInvalidValue;
+    hipError_t e = launch_quantize_q8_1(x, Xq, M, K, s);
+    if (e != hipSuccess) return e;
+    return launch_gemv_q4_0(Wq, Xq, Y, N, K, M, nullptr, s);
+}
+
 hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int K, int M,
                             const dg_launch* cfg, hipStream_t s) {
     const int npairs = K / 64;

@@ -4,6 +4,7 @@
 // waited for itself".
 #include "dg_internal.h"
 #include "q4_common.h"
+#include "q81_rules.h"
 
 namespace dg {
 namespace {
@@ -28,10 +29,18 @@ using namespace q4;
 // row r has arrived (stores only make the wait longer).  C = ceil(row bytes /
 // 1 KiB) is a template parameter because the wait count is an immediate.
 // ---------------------------------------------------------------------------
-template <int S, int C, int DEPTH>
+//
+// FX (fp32 activations): the workgroup quantises the column itself instead of
+// copying Q8_1 blocks.  The first DEPTH - 1 rows' copies are issued first, so
+// their latency overlaps the quantisation; each lane then takes whole
+// 32-element blocks of x (16-byte loads), applies the Q8_1 rules of
+// q81_rules.h (the standalone quantiser's, byte for byte) and writes the
+// 36-byte block into the LDS column; workgroup 0 also stores the blocks to
+// Xq_out when it is given.
+template <int S, int C, int DEPTH, bool FX>
 __global__ void __launch_bounds__(256)
-k_q4_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
-               float* __restrict__ Y, int N, int K) {
+k_q4_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, const float* __restrict__ xf,
+               uint8_t* __restrict__ Xq_out, float* __restrict__ Y, int N, int K) {
     static_assert(DEPTH >= 2 && DEPTH <= 4, "pipeline depth");
     extern __shared__ u32x4 lds_rows[];
     const int lane = lane_id();
@@ -48,15 +57,38 @@ k_q4_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
     uint8_t* const acts = reinterpret_cast<uint8_t*>(lds_rows);
     uint8_t* const lds_base = acts + column_lds_bytes(K) + wave * DEPTH * row_bytes;
 
-    // the workgroup's copy of the activation column first, then the copies of
-    // the first DEPTH - 1 rows (rows row0 + i*rstride for i = 0, 1, ...)
-    copy_column_to_lds(Xq, K, acts, wave, wpb, lane);
+    if constexpr (FX) {
+        // the first DEPTH - 1 rows' copies, then the column quantised into LDS
 #pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d) {
-        const int r = row0 + d * rstride;
-        if (r < N) copy_row_to_lds<C>(Wq + (size_t)r * row_bytes, lds_base + d * row_bytes, nchunks, lane);
-    }
-    {   // this wave's column copies have landed once only its issued rows can be outstanding
+        for (int d = 0; d < DEPTH - 1; ++d) {
+            const int r = row0 + d * rstride;
+            if (r < N) copy_row_to_lds<C>(Wq + (size_t)r * row_bytes, lds_base + d * row_bytes, nchunks, lane);
+        }
+        const int nblk = K >> 5;
+        const bool store = Xq_out != nullptr && blockIdx.x == 0;
+        for (int b = wave * kWave + lane; b < nblk; b += wpb * kWave) {
+            uint32_t blk[9];
+            quantize_q81_block(xf + (size_t)b * 32, blk);
+            uint32_t* dst = reinterpret_cast<uint32_t*>(acts + b * kQ81Bytes);
+#pragma unroll
+            for (int i = 0; i < 9; ++i) dst[i] = blk[i];
+            if (store) {
+                uint32_t* g = reinterpret_cast<uint32_t*>(Xq_out + (size_t)b * kQ81Bytes);
+#pragma unroll
+                for (int i = 0; i < 9; ++i) g[i] = blk[i];
+            }
+        }
+        lds_barrier();   // every wave's blocks are in the column
+    } else {
+        // the workgroup's copy of the activation column first, then the copies of
+        // the first DEPTH - 1 rows (rows row0 + i*rstride for i = 0, 1, ...)
+        copy_column_to_lds(Xq, K, acts, wave, wpb, lane);
+#pragma unroll
+        for (int d = 0; d < DEPTH - 1; ++d) {
+            const int r = row0 + d * rstride;
+            if (r < N) copy_row_to_lds<C>(Wq + (size_t)r * row_bytes, lds_base + d * row_bytes, nchunks, lane);
+        }
+        // this wave's column copies have landed once only its issued rows can be outstanding
         const int rows = row0 < N ? (N - 1 - row0) / rstride + 1 : 0;   // wave-uniform
         wait_rows_ahead<C, DEPTH>(rows < DEPTH - 1 ? rows : DEPTH - 1);
         lds_barrier();
@@ -122,7 +154,7 @@ k_q4_m1_ldsrow(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq,
 // 28672 x 8192: two row buffers per wave and at most 2048 workgroups of four
 // waves (a few rows per wave) read fastest.
 hipError_t launch_q4_m1_ldsrow(int K, int depth, const void* Wq, const void* Xq, float* Y, int N, int grid,
-                               int block, hipStream_t s) {
+                               int block, hipStream_t s, const float* xf, void* Xq_out) {
     if (!depth) depth = 2;
     if (!block) block = 256;
     if (block > 256) return hipErrorInvalidValue;   // compiled for <= 256 threads
@@ -137,9 +169,16 @@ hipError_t launch_q4_m1_ldsrow(int K, int depth, const void* Wq, const void* Xq,
     if (lds > device_max_lds_per_block()) return hipErrorInvalidValue;
     const int C = (int)((row_bytes + 1023) / 1024);
     const int S = (K / 64 + kWave - 1) / kWave;
-#define DG_SCD(SS, CC, DD)                                                                              \
-    else if (S == SS && C == CC && depth == DD)                                                         \
-        hipLaunchKernelGGL((k_q4_m1_ldsrow<SS, CC, DD>), dim3(grid), dim3(block), lds, s, w, x, Y, N, K);
+    uint8_t* xo = (uint8_t*)Xq_out;
+#define DG_SCD(SS, CC, DD)                                                                                   \
+    else if (S == SS && C == CC && depth == DD) {                                                            \
+        if (xf)                                                                                              \
+            hipLaunchKernelGGL((k_q4_m1_ldsrow<SS, CC, DD, true>), dim3(grid), dim3(block), lds, s, w, x, xf,   \
+                               xo, Y, N, K);                                                                 \
+        else                                                                                                 \
+            hipLaunchKernelGGL((k_q4_m1_ldsrow<SS, CC, DD, false>), dim3(grid), dim3(block), lds, s, w, x, xf,  \
+                               xo, Y, N, K);                                                                 \
+    }
 #define DG_SC(SS, CC) DG_SCD(SS, CC, 2) DG_SCD(SS, CC, 3) DG_SCD(SS, CC, 4)
     if (false) {
     }

@@ -10,6 +10,7 @@
 // (bind_f32), so the bytes are reproducible on any IEEE machine.
 #include "dg_device.h"
 #include "dg_internal.h"
+#include "q81_rules.h"
 
 #pragma clang fp contract(off)
 
@@ -29,38 +30,29 @@ __device__ __forceinline__ void load_block32(const float* __restrict__ src, floa
     }
 }
 
-// One thread per 32-activation block (block t of the flattened [M][K] input).
+// One lane per activation: the 32 lanes of each half of a wave hold one block
+// (block t of the flattened [M][K] input), so a block's largest magnitude
+// and its code sum are reductions over 32 lanes (both exact in any order)
+// and every lane takes one division.  A wave writes two whole 36-byte blocks:
+// lane j of a half stores code byte j, lane 0 the header dword.
 __global__ void __launch_bounds__(256)
 k_quantize_q8_1(const float* __restrict__ x, uint8_t* __restrict__ Xq, int64_t nblocks) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= nblocks) return;
-    float v[32];
-    load_block32(x + t * 32, v);
-    float amax = 0.0f;
+    const int64_t t = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+    const int j = threadIdx.x & 31;
+    const bool live = t < nblocks;
+    const float v = live ? x[t * 32 + j] : 0.0f;
+    float amax = fabsf(v);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    const float d = bind_f32(amax / 127.0f);
-    uint32_t packed[8];
-    int sum = 0;
+    for (int o = 16; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 32));
+    const float d = q81_scale(amax);
+    const int c = q81_code(v, d);
+    int sum = c;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            int c = 0;
-            if (d != 0.0f) {
-                c = (int)roundf(v[4 * i + b] / d);   // halves away from zero
-                c = c > 127 ? 127 : (c < -127 ? -127 : c);
-            }
-            sum += c;
-            w |= (uint32_t)(uint8_t)(int8_t)c << (8 * b);
-        }
-        packed[i] = w;
-    }
-    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + t * 36);
-    out[0] = (uint32_t)f32_to_half_bits(d) | ((uint32_t)f32_to_half_bits(bind_f32(d * (float)sum)) << 16);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) out[1 + i] = packed[i];
+    for (int o = 16; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 32);
+    if (!live) return;
+    uint8_t* blk = Xq + t * 36;
+    blk[4 + j] = (uint8_t)(int8_t)c;
+    if (j == 0) *reinterpret_cast<uint32_t*>(blk) = q81_header(d, sum);
 }
 
 // One thread per 32-weight block.
@@ -135,7 +127,7 @@ hipError_t launch_quantize_q8_0(const float* w, void* Wq, int64_t N, int64_t K, 
 
 hipError_t launch_quantize_q8_1(const float* x, void* Xq, int64_t M, int64_t K, hipStream_t s) {
     const int64_t nblocks = M * (K / 32);
-    const int64_t grid = (nblocks + 255) / 256;
+    const int64_t grid = (nblocks + 7) / 8;   // eight blocks of 32 lanes per workgroup
     hipLaunchKernelGGL(k_quantize_q8_1, dim3((unsigned)grid), dim3(256), 0, s, x, (uint8_t*)Xq, nblocks);
     return hipGetLastError();
 }

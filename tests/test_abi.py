@@ -241,3 +241,15 @@ def test_binding_refuses_tensors_smaller_than_the_call_touches():
     dg._fits(f[1:], 32, "f")
     with pytest.raises(ValueError):
         dg._fits(f[1:], 33, "f")
+
+
+def test_gemv_q4_0_f32_rejects_before_launch(lib):
+    f = lib.dg_gemv_q4_0_f32
+    assert f(A16, A16, A16, None, 4, 256, 1, None) == 1          # the two-launch form needs the Q8_1 buffer
+    assert f(A16, A16, A16, None, 4, 256, 2, None) == 1
+    assert f(A16, None, A16, None, 4, 256, 1, None) == 1          # no activations
+    assert f(A16, A16, A16, P(0x1004), 4, 256, 1, None) == 2      # Q8_1 buffer not 16-byte aligned
+    assert f(A16, P(0x1008), A16, A16, 4, 256, 1, None) == 2      # x not 16-byte aligned
+    assert f(A16, A16, A16, A16, 4, 250, 1, None) == 3            # K % 256
+    assert f(A16, A16, A16, A16, 4, 256, 25, None) == 3           # M > 24
+    assert f(None, None, None, None, 0, 256, 1, None) == 0        # empty: nothing launched
