@@ -1074,12 +1074,13 @@ def suite_tail(dg, torch, emit, ceil_gbps):
 
 
 def profile_kernels(args):
-    """Launches each profiled kernel eagerly (one dispatch each) on known
-    workloads, for rocprofv3 counter runs: the Q4_0 M=1 decode GEMV at
-    28672x8192, the fp16 GEMV at 4096x4096, the NF4 GEMV at 28672x8192 (block
-    64), the streaming read of 1 GiB, and a
-    plain 1 GiB device-to-device copy whose FETCH_SIZE / WRITE_SIZE calibrate
-    the counters (known bytes read and written)."""
+    """Launches each profiled kernel eagerly on known workloads, over weight
+    copies that together exceed the last-level cache, for rocprofv3 counter
+    runs: the Q4_0 M=1 decode GEMV at 28672x8192, the fp16 GEMV at 4096x4096,
+    the NF4 GEMV at 28672x8192 (block 64), the Q8_0 M=1 GEMV at 28672x8192,
+    the Q4_0 GEMV with 16 columns at 4096x14336 (matrix cores), the streaming
+    read of 1 GiB, and a plain 1 GiB device-to-device copy whose counters
+    calibrate the others (known bytes read and written)."""
     import memory_bound_decode_gemv_amd as dg
     torch = _torch()
     nq = copies_for(18 * Q4_N * Q4_K // 32)
@@ -1093,6 +1094,13 @@ def profile_kernels(args):
     nf, table = nf4_copies(6, Q4_N, Q4_K, 64, nn)
     xn = torch.ones(Q4_K, dtype=torch.bfloat16, device="cuda")
     yn = torch.empty(Q4_N, dtype=torch.float32, device="cuda")
+    n8 = copies_for(bytes_q8_0(Q4_N, Q4_K, 1))
+    W8 = q8_0_copies(3, Q4_N, Q4_K, n8)
+    NS, KS, MS = SMALL_M_PROFILE
+    ns = copies_for(bytes_q4(NS, KS, MS))
+    Ws = q4_copies(4, NS, KS, ns)
+    Xs = q8_columns(4, KS, MS)
+    Ys = torch.empty(MS * NS, dtype=torch.float32, device="cuda")
     src = torch.empty(GIB // 4, dtype=torch.int32, device="cuda").fill_(3)
     dst = torch.empty_like(src)
     cs = torch.zeros(768, dtype=torch.int32, device="cuda")
@@ -1103,12 +1111,17 @@ def profile_kernels(args):
         dg.dg_gemv_f16(W16[c], x16, y16)
     for c in range(2 * nn):
         dg.dg_gemv_nf4(nf[c % nn][0], nf[c % nn][1], table, xn, yn, N=Q4_N, K=Q4_K, B=64)
+    for c in range(2 * n8):
+        dg.dg_gemv_q8_0(W8[c % n8], Xq, Yq, Q4_N, Q4_K, 1)
+    for c in range(2 * ns):
+        dg.dg_gemv_q4_0(Ws[c % ns], Xs, Ys, NS, KS, MS)
     for _ in range(4):
         dg.dg_stream_read(src, cs, grid_blocks=768, block_threads=64, flags=dg.DG_READ_NONTEMPORAL)
     for _ in range(4):
         dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"[profile-kernels] q4_0 x{2 * nq}, f16 x{n16}, nf4 x{2 * nn}, stream_read 1 GiB x4, copy 1 GiB x4")
+    log(f"[profile-kernels] q4_0 x{2 * nq}, f16 x{n16}, nf4 x{2 * nn}, q8_0 x{2 * n8}, q4_0 M={MS} x{2 * ns}, "
+        f"stream_read 1 GiB x4, copy 1 GiB x4")
 
 
 # Workloads of --profile-launch-cost, in launch order (one graph each), with
@@ -1164,7 +1177,8 @@ def profile_launch_cost(args):
 
 
 SMALL_M_CASES = [(4096, 4096), (14336, 4096), (4096, 14336)]
-SMALL_M_COLUMNS = (4, 8, 16, 24)
+SMALL_M_COLUMNS = (4, 8, 16, 17, 24)
+SMALL_M_PROFILE = (4096, 14336, 16)   # the matrix-core workload of --profile-kernels
 
 
 def profile_small_m(args):

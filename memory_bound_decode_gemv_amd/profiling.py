@@ -3,15 +3,26 @@
 Counters: two `rocprofv3 --pmc` runs (FETCH_SIZE, then WRITE_SIZE) of
 `bench.py --profile-kernels`, which launches each kernel eagerly on a known
 workload next to a plain 1 GiB device-to-device copy.  The copy's counters
-calibrate the others: on MI355X FETCH_SIZE reads about half the bytes a
-kernel actually fetches while WRITE_SIZE reads them exactly, so each counter
-is scaled by (bytes the copy moved) / (what the counter read for it).  The
-HBM traffic per launch of a kernel is then
+calibrate the others: on MI355X FETCH_SIZE reads half the bytes a kernel
+fetches while WRITE_SIZE reads them exactly, so each counter is scaled by
+(bytes the copy moved) / (what the counter read for it).  The HBM traffic per
+launch of a kernel is then
     FETCH_SIZE * fetch_scale + WRITE_SIZE * write_scale     (KiB * 1024).
 Each entry records a hash of the kernel's source files; bench.py reports the
 traffic only while that hash still matches the tree.
 
-    python -m memory_bound_decode_gemv_amd.profiling counters FETCH.csv WRITE.csv
+Why FETCH_SIZE reads half: for gfx950 rocprofiler-sdk derives it as
+    (TCC_BUBBLE*128 + (TCC_EA0_RDREQ - TCC_BUBBLE - TCC_EA0_RDREQ_32B)*64
+     + TCC_EA0_RDREQ_32B*32) / 1024,
+i.e. it takes TCC_BUBBLE to count the 128-byte read requests.  On MI355X
+TCC_BUBBLE reads 0 while every L2-to-memory read request carries 128 bytes
+(TCC_EA0_RDREQ of a 1 GiB streaming read is 2^30 / 128 plus a few hundred,
+TCC_EA0_RDREQ_32B is 0), so each request is counted as 64 bytes.  Two more
+passes (--tcc) record those request counters and the L2 tag counters
+(TCC_REQ, TCC_READ, TCC_HIT, TCC_MISS); 128 * TCC_EA0_RDREQ is then a second
+estimate of the bytes read from memory that needs no calibration.
+
+    python -m memory_bound_decode_gemv_amd.profiling counters FETCH.csv WRITE.csv [--tcc TCCA.csv TCCB.csv]
     python -m memory_bound_decode_gemv_amd.profiling trace KERNEL_STATS.csv [--runs KERNEL_TRACE.csv] --md OUT.md
     python -m memory_bound_decode_gemv_amd.profiling suite SUITE.jsonl --md OUT.md
     python -m memory_bound_decode_gemv_amd.profiling suite A.jsonl B.jsonl --condense --filter RE --md OUT.md
@@ -46,7 +57,15 @@ KERNELS = {
     "gemv_q4_0_m1_28672x8192": (
         r"k_q4_m1_ldsrow<", "Q4_0 x Q8_1, M = 1, N = 28672, K = 8192",
         18 * 28672 * 8192 // 32 + 36 * 8192 // 32 + 4 * 28672,
-        ["gemv_q4_0_m1.hip", "q4_common.h", "dg_device.h", "dg_internal.h"]),
+        ["gemv_q4_0_m1.hip", "q4_common.h", "q81_rules.h", "dg_device.h", "dg_internal.h"]),
+    "gemv_q8_0_m1_28672x8192": (
+        r"k_units<[^>]*UnitsQ8_0", "Q8_0 x Q8_1, M = 1, N = 28672, K = 8192",
+        34 * 28672 * 8192 // 32 + 36 * 8192 // 32 + 4 * 28672,
+        ["gemv_m1_units.hip", "q4_common.h", "dg_device.h", "dg_internal.h"]),
+    "gemv_q4_0_m16_4096x14336": (
+        r"k_q(mfma|res)<", "Q4_0 x Q8_1, M = 16, N = 4096, K = 14336 (matrix cores)",
+        18 * 4096 * 14336 // 32 + 16 * 36 * 14336 // 32 + 4 * 16 * 4096,
+        ["gemv_q4_0_mfma.hip", "gemv_qmfma_res.hip", "mfma_formats.h", "q4_common.h", "dg_device.h", "dg_internal.h"]),
     "gemv_f16_4096x4096": (
         r"k_gemv_wide<false", "fp16 GEMV, N = K = 4096",
         2 * 4096 * 4096 + 2 * 4096 + 2 * 4096,
@@ -91,7 +110,20 @@ def _values(d, pattern, counter):
     return out
 
 
-def counters_summary(fetch_csv, write_csv):
+TCC_COUNTERS = ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum", "TCC_EA0_RDREQ_DRAM_sum",
+                "TCC_REQ_sum", "TCC_READ_sum", "TCC_HIT_sum", "TCC_MISS_sum")
+
+
+def _tcc_means(tcc, pattern, pick_max=False):
+    out = {}
+    for ctr in TCC_COUNTERS:
+        v = _values(tcc, pattern, ctr)
+        if v:
+            out[ctr] = max(v) if pick_max else sum(v) / len(v)
+    return out
+
+
+def counters_summary(fetch_csv, write_csv, tcc_csvs=()):
     fetch = load_counter_csv(fetch_csv)
     write = load_counter_csv(write_csv)
     cal_pat, cal_bytes = CALIBRATION
@@ -99,9 +131,14 @@ def counters_summary(fetch_csv, write_csv):
     cal_w = max(_values(write, cal_pat, "WRITE_SIZE"))
     fs = cal_bytes / (cal_f * 1024)
     ws = cal_bytes / (cal_w * 1024)
+    tcc = {}
+    for path in tcc_csvs:
+        tcc.update(load_counter_csv(path))
     out = {"calibration": {"kernel": "1 GiB device-to-device copy", "bytes": cal_bytes,
                            "fetch_kib": cal_f, "write_kib": cal_w,
                            "fetch_scale": round(fs, 5), "write_scale": round(ws, 5)}}
+    if tcc:
+        out["calibration"]["tcc"] = {k: round(v, 1) for k, v in _tcc_means(tcc, cal_pat, pick_max=True).items()}
     for key, (pat, what, alg, files) in KERNELS.items():
         fv = _values(fetch, pat, "FETCH_SIZE")
         wv = _values(write, pat, "WRITE_SIZE")
@@ -114,13 +151,20 @@ def counters_summary(fetch_csv, write_csv):
                     "write_kib": round(w_kib, 2), "hbm_bytes_per_launch": traffic,
                     "algorithmic_bytes_per_launch": alg, "traffic_over_algorithmic": round(traffic / alg, 4),
                     "sources": files, "source_sha256_16": sources_hash(files)}
+        t = _tcc_means(tcc, pat) if tcc else {}
+        if t:
+            out[key]["tcc"] = {k: round(v, 1) for k, v in t.items()}
+            if "TCC_EA0_RDREQ_sum" in t:
+                rd = 128 * t["TCC_EA0_RDREQ_sum"]
+                out[key]["read_bytes_128b_requests"] = int(round(rd))
     return out
 
 
-def counters_markdown(summary, command_fetch, command_write):
+def counters_markdown(summary, command_fetch, command_write, command_tcc=""):
     lines = ["# HBM traffic per launch from rocprofv3 counters", "",
-             "Commands (run from /tmp on the MI355X box, repository at $R):", "",
-             f"    {command_fetch}", f"    {command_write}", "",
+             "Commands (run from /tmp on an MI355X, repository at $R):", "",
+             f"    {command_fetch}", f"    {command_write}"] + \
+            [f"    {c}" for c in command_tcc.split(" ;; ") if c] + ["",
              "Calibration: " + json.dumps(summary["calibration"]), "",
              "| kernel | workload | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch "
              "| algorithmic bytes | ratio |", "|---|---|---|---|---|---|---|---|"]
@@ -130,6 +174,34 @@ def counters_markdown(summary, command_fetch, command_write):
         lines.append(f"| {k} | {v['workload']} | {v['dispatches']} | {v['fetch_kib']} | {v['write_kib']} | "
                      f"{v['hbm_bytes_per_launch']} | {v['algorithmic_bytes_per_launch']} | "
                      f"{v['traffic_over_algorithmic']} |")
+    rows = [(k, v) for k, v in summary.items() if k != "calibration" and v.get("tcc")]
+    cal = summary["calibration"].get("tcc")
+    if rows or cal:
+        lines += ["", "## Why FETCH_SIZE reads half, and a calibration-free cross-check", "",
+                  "rocprofiler-sdk derives FETCH_SIZE on gfx950 as (TCC_BUBBLE x 128 + (TCC_EA0_RDREQ - TCC_BUBBLE "
+                  "- TCC_EA0_RDREQ_32B) x 64 + TCC_EA0_RDREQ_32B x 32) / 1024 KiB: TCC_BUBBLE is taken to count the "
+                  "128-byte read requests.  The passes below show TCC_BUBBLE = 0 and TCC_EA0_RDREQ_32B = 0 for every "
+                  "kernel, while TCC_EA0_RDREQ of the 1 GiB streaming read is 2^30 / 128 (8388608) plus a few "
+                  "hundred: each L2-to-memory read request moves 128 bytes and the formula counts it as 64.  Hence "
+                  "the factor 2 of the calibration.  128 x TCC_EA0_RDREQ estimates the bytes read from memory "
+                  "without any calibration; `L2 hit share` is TCC_HIT / (TCC_HIT + TCC_MISS).", "",
+                  "| kernel | TCC_EA0_RDREQ | _32B | TCC_BUBBLE | _DRAM | TCC_REQ | TCC_HIT | TCC_MISS | L2 hit share "
+                  "| 128 x RDREQ bytes | over algorithmic |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+        if cal:
+            rows = [("1 GiB copy (calibration)", {"tcc": cal, "algorithmic_bytes_per_launch": GIB})] + rows
+        for k, v in rows:
+            t = v["tcc"]
+            cells = ["" if c not in t else f"{t[c]:.0f}" for c in
+                     ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_BUBBLE_sum", "TCC_EA0_RDREQ_DRAM_sum",
+                      "TCC_REQ_sum", "TCC_HIT_sum", "TCC_MISS_sum")]
+            hm = t.get("TCC_HIT_sum", 0) + t.get("TCC_MISS_sum", 0)
+            cells.append(f"{t.get('TCC_HIT_sum', 0) / hm:.3f}" if hm else "")
+            if "TCC_EA0_RDREQ_sum" in t:
+                rd = 128 * t["TCC_EA0_RDREQ_sum"]
+                cells += [f"{rd:.0f}", f"{rd / v['algorithmic_bytes_per_launch']:.4f}"]
+            else:
+                cells += ["", ""]
+            lines.append(f"| {k} | " + " | ".join(cells) + " |")
     return "\n".join(lines) + "\n"
 
 
@@ -413,6 +485,8 @@ def main(argv=None):
     c.add_argument("--md", default=os.path.join(PROFILES, "hbm_traffic_counters.md"))
     c.add_argument("--command-fetch", default="")
     c.add_argument("--command-write", default="")
+    c.add_argument("--tcc", nargs="*", default=[], help="counter CSVs of the TCC request passes")
+    c.add_argument("--command-tcc", default="")
     pm = sub.add_parser("pmc")
     pm.add_argument("csvs", nargs="+")
     pm.add_argument("--kernels", required=True)
@@ -440,12 +514,12 @@ def main(argv=None):
     t.add_argument("--runs", default=None, help="kernel-trace CSV: add per-run durations")
     a = ap.parse_args(argv)
     if a.cmd == "counters":
-        s = counters_summary(a.fetch_csv, a.write_csv)
+        s = counters_summary(a.fetch_csv, a.write_csv, a.tcc)
         with open(a.json, "w") as f:
             json.dump(s, f, indent=1)
             f.write("\n")
         with open(a.md, "w") as f:
-            f.write(counters_markdown(s, a.command_fetch, a.command_write))
+            f.write(counters_markdown(s, a.command_fetch, a.command_write, a.command_tcc))
         print(json.dumps(s, indent=1))
     elif a.cmd == "pmc":
         s = pmc_summary(a.csvs, a.kernels, a.labels.split(","), a.per)
