@@ -1008,8 +1008,9 @@ def bytes_nf4(N, K, B):
 
 def suite_nf4(dg, torch, emit, ceil_gbps):
     """NF4 x bf16 at M = 1: the decoder shapes and the 70B MLP pair at block 64
-    (default launch and a sweep of table copies, rows in flight and grid), the
-    70B up-projection at every block size, and the read probe over its codes."""
+    (default launch and a sweep of the kernels' row groups, rows in flight and
+    grid), the 70B up-projection at every block size, and the read probe over
+    its codes."""
     import synth
     for (N, K) in [(4096, 4096), (14336, 4096), (4096, 14336), (Q4_N, Q4_K), (Q4_K, Q4_N)]:
         B = 64
@@ -1017,8 +1018,12 @@ def suite_nf4(dg, torch, emit, ceil_gbps):
         ops, table = nf4_copies(6, N, K, B, nc)
         x = synth.gpu_normal((6, synth.KIND_X, 0, 0), (K,), 1.0, torch.bfloat16)
         y = torch.empty(N, dtype=torch.float32, device="cuda")
-        launches = [("default", None)] + [(f"tc{tc} ahead{h} g{g}", dict(variant=31, unroll=tc + 1000 * h, grid=g))
-                                          for tc in (8, 16, 32) for h in (4, 8) for g in (256, 512, 1024, 2048)]
+        S = (K + 2047) // 2048
+        launches = [("default", None)] + [(f"tc{tc} ahead4 g{g}", dict(variant=31, unroll=tc + 4000, grid=g))
+                                          for tc in (8, 32) for g in (512, 1024)]
+        launches += [(f"rows G{G} ahead{h} g{g}", dict(variant=33, block=G * S * 64, unroll=h, grid=g))
+                     for G in sorted({1, 2, 4, 16 // S}) if G * S <= 16
+                     for h in (4, 8) for g in (0, 256, 512, 1024)]
         if K in (2048, 4096, 8192):
             launches += [(f"mfma g{g}", dict(variant=32, grid=g)) for g in (0, 128, 512)]
         for lname, launch in launches:

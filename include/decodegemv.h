@@ -224,16 +224,20 @@ dg_status dg_gemv_q8_0(const void* Wq, const void* Xq, float* Y,
  *           nibble; 16-byte aligned.
  *   absmax  device float32 [N][K/B] (absmax[n][b] scales weights bB..bB+B-1
  *           of row n); 16-byte aligned.
- *   table   device float32 [16], any finite values (the kernel keeps each
- *           value as the sum of two bfloat16 parts, within 2^-17 of it);
- *           16-byte aligned.
+ *   table   device float32 [16], any finite values; 16-byte aligned.  The
+ *           default kernel multiplies by the values themselves; variants
+ *           DG_VARIANT_NF4_UNITS and DG_VARIANT_NF4_MFMA hold each value
+ *           (scaled by a power of two) as a binary16 high part plus a
+ *           binary16 remainder, about 22 significant bits (within about
+ *           2^-23 of it, relative).
  *   x       device bfloat16 [K]; 16-byte aligned.
  *   y       device float32 [N]; 4-byte aligned.
  *   N       rows, 0 <= N < 2^31.
  *   K       multiple of 256 and of 4*B, 0 <= K <= 32768 (a workgroup has
  *           one wave per 2048 weights of a row).
  *   B       block size: 32, 64, 128 or 256.
- * Products and sums are fp32; K = 0 gives y = 0.
+ * Products and sums are fp32 (bfloat16 activations widened exactly); the
+ * sum order is fixed by K, not by the launch.  K = 0 gives y = 0.
  * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_HIP.
  * ------------------------------------------------------------------------ */
 dg_status dg_gemv_nf4(const void* codes, const float* absmax, const float* table, const void* x, float* y,
@@ -442,10 +446,16 @@ enum {
     /* NF4 */
     DG_VARIANT_NF4_UNITS = 31,      /* code bytes looked up in a byte-pair table in LDS; one
                                        wave per 2048 weights of a row (block = 64*ceil(K/2048)) */
-    DG_VARIANT_NF4_MFMA = 32        /* the looked-up pairs as operands of f16 matrix-core
+    DG_VARIANT_NF4_MFMA = 32,       /* the looked-up pairs as operands of f16 matrix-core
                                        products, 16 rows x 32 weights per instruction; K = 2048,
                                        4096 or 8192, K/128 <= B <= K/16; no block or unroll
                                        override                                                */
+    DG_VARIANT_NF4_ROWS = 33        /* the default: code bytes looked up in a table of binary32
+                                       value pairs (32 conflict-free copies in LDS), fp32 FMA,
+                                       lane sums reduced four rows at a time; block = G row groups
+                                       x 64*ceil(K/2048) (<= 1024), unroll = rows in flight (4, 8)
+                                       + 100 * partial sums per lane (1, 2, 4; 4 only with 4 rows
+                                       in flight)                                               */
 };
 
 dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K,

@@ -61,6 +61,7 @@ DG_VARIANT_Q8_UNITS = 23
 DG_VARIANT_Q8_MFMA_RES = 24
 DG_VARIANT_NF4_UNITS = 31
 DG_VARIANT_NF4_MFMA = 32
+DG_VARIANT_NF4_ROWS = 33
 
 # Every symbol include/decodegemv.h declares.
 EXPORTED = (

@@ -254,6 +254,219 @@ k_nf4(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const
 }
 
 // ---------------------------------------------------------------------------
+// NF4 on the vector unit in float arithmetic, rows reduced four at a time
+// (the default).
+//
+// A code byte is still one lookup (one byte permute forms the address, one
+// 8-byte LDS read returns both weights), but the entry holds the two table
+// values as binary32, and the lane multiplies them with its activations
+// (bfloat16 widened to binary32, exact) by two v_fmac_f32: the products and
+// sums are the float GEMV's, with nothing approximated.  This is also the
+// faster form on gfx950: v_dot2_f32_f16 issues at half the rate of
+// v_fmac_f32 (timed here: with the weight stream cached, k_nf4's two dot2 per
+// code byte put its arithmetic alone at about 20 us for 28672 x 8192), so the
+// binary16 split of k_nf4 -- two dot2, four multiplies per byte -- costs twice
+// the cycles of two fmac.  Beyond that, two changes remove most of k_nf4's
+// per-row work:
+//   * the lookups are free of bank conflicts: entry v of copy c sits at byte
+//     256v + 8c, so the lanes that the LDS serves together (c = lane % 32)
+//     hit distinct banks whatever their codes.  With 8 copies, k_nf4 at
+//     28672 x 8192 stalled on bank conflicts for 3.5 times its busy LDS
+//     cycles;
+//   * a wave's lane sums of four rows are reduced together: a
+//     v_permlane32_swap and an add fold rows (0, 1) and (2, 3) into half
+//     waves, a v_permlane16_swap and an add fold those into 16-lane rows
+//     (rows 0, 2, 1, 3), and four DPP row_shr adds finish the four at once
+//     in lanes 15, 31, 47 and 63: ten instructions for four rows, where a
+//     whole-wave reduction takes about a dozen per row.
+// The 64 KiB table is built once per workgroup, so a workgroup holds G row
+// groups of S = ceil(K/2048) waves (wave u of a group owns weights
+// 2048u .. 2048u + 2047 of each of its rows, as in k_nf4); group g of
+// workgroup b takes rows bG + g, bG + g + gridG, ....  The unit sums of a
+// row meet in LDS every 64 rows and are added in unit order, so results do
+// not depend on the launch shape.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float f32_of(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t bits_of(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Sums over the wave of four per-lane values: the sum of p0 ends in lane
+// 15, of p2 in lane 31, of p1 in lane 47, of p3 in lane 63.
+__device__ __forceinline__ float sum_four_rows(float p0, float p1, float p2, float p3) {
+    // halves: p0' = (p0.lo, p1.lo), p1' = (p0.hi, p1.hi)
+    const auto a = __builtin_amdgcn_permlane32_swap(bits_of(p0), bits_of(p1), false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(bits_of(p2), bits_of(p3), false, false);
+    const float q01 = f32_of(a[0]) + f32_of(a[1]);   // lanes 0..31: row 0, 32..63: row 1
+    const float q23 = f32_of(b[0]) + f32_of(b[1]);   // row 2, row 3
+    // 16-lane rows: q01' = (q01.r0, q23.r0, q01.r2, q23.r2), q23' = (q01.r1, q23.r1, q01.r3, q23.r3)
+    const auto c = __builtin_amdgcn_permlane16_swap(bits_of(q01), bits_of(q23), false, false);
+    float r = f32_of(c[0]) + f32_of(c[1]);           // 16-lane rows hold rows 0, 2, 1, 3
+    r += dpp_mov_f32<kDppRowShr1, 0xF>(r);
+    r += dpp_mov_f32<kDppRowShr2, 0xF>(r);
+    r += dpp_mov_f32<kDppRowShr4, 0xF>(r);
+    r += dpp_mov_f32<kDppRowShr8, 0xF>(r);
+    return r;
+}
+
+// A lane's 16 code bytes and absmax of row r: every load is in bounds and
+// unconditional (lanes past K read inside their row, rows past N read row
+// 0) and the values that do not belong to the result are dropped.
+// The row's base is wave-uniform and the lane's offset a 32-bit constant, so
+// the loads take the scalar-base form: no vector instruction forms an address.
+__device__ __forceinline__ void load_row_unit(const uint8_t* __restrict__ codes, const float* __restrict__ absmax,
+                                              int r, int row_bytes, int nab, uint32_t code_off, uint32_t ab_off,
+                                              u32x4& c, float& a) {
+    const uint8_t* crow = codes + (size_t)r * (size_t)row_bytes;
+    const float* arow = absmax + (size_t)r * (size_t)nab;
+    c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(crow + code_off));
+    a = __builtin_nontemporal_load(arow + ab_off);
+}
+
+// A lane's 16 code bytes against its 32 activations in binary32: NA
+// independent sums (byte i to sum i % NA), added in a fixed order.  Entry v
+// of the lane's table copy is at byte 256v + copy_off; one byte permute
+// forms that offset from the code word (byte v into bits 8..15, the copy
+// offset into bits 0..7).
+template <int NA>
+__device__ __forceinline__ float unit_dot_f32(const u32x4& c, const float (&xf)[32], const uint8_t* tab,
+                                              uint32_t copy_off) {
+    const uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    float2 e[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t off = __builtin_amdgcn_perm(cw[i >> 2], copy_off, 0x0C0C0000u | ((4u + (i & 3)) << 8));
+        e[i] = *reinterpret_cast<const float2*>(tab + off);
+    }
+    // One wait for all 16 reads (the empty asm takes them all), instead of a
+    // wait before each entry's first use: on this path the instructions a
+    // SIMD issues, waits included, are what bounds the kernel.
+    asm volatile("" ::"v"(e[0]), "v"(e[1]), "v"(e[2]), "v"(e[3]), "v"(e[4]), "v"(e[5]), "v"(e[6]), "v"(e[7]),
+                 "v"(e[8]), "v"(e[9]), "v"(e[10]), "v"(e[11]), "v"(e[12]), "v"(e[13]), "v"(e[14]), "v"(e[15]));
+    float p[NA];
+#pragma unroll
+    for (int j = 0; j < NA; ++j) p[j] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        p[i % NA] = fmaf(e[i].x, xf[2 * i], p[i % NA]);       // weight 2i: the high nibble
+        p[i % NA] = fmaf(e[i].y, xf[2 * i + 1], p[i % NA]);
+    }
+    float s = p[0];
+#pragma unroll
+    for (int j = 1; j < NA; ++j) s += p[j];
+    return s;
+}
+
+template <int AHEAD, int NA>
+__global__ void __launch_bounds__(1024)
+k_nf4_rows(const uint8_t* __restrict__ codes, const float* __restrict__ absmax, const float* __restrict__ table,
+           const uint16_t* __restrict__ x, float* __restrict__ y, int N, int K, int B, int S) {
+    static_assert(AHEAD == 4 || AHEAD == 8, "rows in flight: whole groups of four");
+    __shared__ float2 ftab[256 * 32];   // entry v of copy c at [32v + c]
+    __shared__ float red[16][kWave];    // [wave][row of the batch]
+    __shared__ float tl[16];
+    const int lane = lane_id();
+    const int wave = wave_in_block();
+    const int G = blockDim.x / (S * kWave);
+    const int unit = wave % S;
+    const int grp = wave / S;
+    const int nab = K / B;
+    const int row_bytes = K >> 1;
+    const int k0 = unit * kUnitWeights + lane * 32;
+    const bool lane_valid = k0 < K;
+    const int kl = lane_valid ? k0 : 0;   // lanes past K: weights 0..31 of the row
+    const uint32_t code_off = (uint32_t)(kl >> 1);
+    const uint32_t ab_off = (uint32_t)(kl / B);
+
+    u32x4 xraw[4];
+    {
+        const u32x4* src = reinterpret_cast<const u32x4*>(x + kl);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xraw[q] = src[q];
+    }
+    const int nstreams = gridDim.x * G;
+    const int stream = blockIdx.x * G + grp;
+    const int first = blockIdx.x * G;
+    const int nrows = stream < N ? (N - 1 - stream) / nstreams + 1 : 0;
+    const int nrows_wg = first < N ? (N - 1 - first) / nstreams + 1 : 0;   // the longest stream: uniform
+    // row k of this stream, or row 0 past its end (read and dropped)
+    auto row_at = [&](int k) -> int { return k < nrows ? stream + k * nstreams : 0; };
+    u32x4 qc[AHEAD];
+    float qa[AHEAD];
+#pragma unroll
+    for (int j = 0; j < AHEAD; ++j) load_row_unit(codes, absmax, row_at(j), row_bytes, nab, code_off, ab_off, qc[j], qa[j]);
+
+    // The 16 table values are read with uniform (scalar) loads, which do not
+    // count in vmcnt, and passed on through LDS: a per-thread indexed read of
+    // the table here would be a vector load behind the weight loads, and
+    // waiting for it would wait for them too.
+    float tv = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float v = table[j];
+        tv = threadIdx.x == (unsigned)j ? v : tv;
+    }
+    if (threadIdx.x < 16) tl[threadIdx.x] = tv;
+    lds_barrier();
+    if ((blockDim.x & 255) == 0) {
+        // entry v = thread % 256 into copies thread / 256, + blockDim / 256, ...; the
+        // lanes of a write (consecutive v) reach copies (c + v) % 32: distinct banks
+        const int v = threadIdx.x & 255;
+        const float2 e = float2{tl[v >> 4], tl[v & 15]};
+        for (int c = threadIdx.x >> 8; c < 32; c += blockDim.x >> 8) ftab[v * 32 + ((c + v) & 31)] = e;
+    } else {
+        for (int i = threadIdx.x; i < 256 * 32; i += blockDim.x) ftab[i] = float2{tl[i >> 9], tl[(i >> 5) & 15]};
+    }
+    // the lane's activations in binary32 (lanes past K: 0 times any table value)
+    float xf[32];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t w[4] = {xraw[q].x, xraw[q].y, xraw[q].z, xraw[q].w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            xf[8 * q + 2 * h] = lane_valid ? f32_of(w[h] << 16) : 0.0f;
+            xf[8 * q + 2 * h + 1] = lane_valid ? f32_of(w[h] & 0xFFFF0000u) : 0.0f;
+        }
+    }
+    lds_barrier();   // the table is complete
+
+    const uint8_t* const tab = reinterpret_cast<const uint8_t*>(ftab);
+    const uint32_t copy_off = (uint32_t)(lane & 31) * 8u;
+    const int h = lane >> 4;
+    const int row_of_lane = ((h & 1) << 1) | (h >> 1);   // lanes 15, 31, 47, 63 end rows 0, 2, 1, 3
+    float* const mine = red[wave];
+    const int nrows_pad = (nrows_wg + AHEAD - 1) / AHEAD * AHEAD;   // uniform
+    for (int kb = 0; kb < nrows_pad; kb += kWave) {
+        const int kend = kb + kWave < nrows_pad ? kb + kWave : nrows_pad;
+        for (int kr = kb; kr < kend; kr += AHEAD) {
+            float p[AHEAD];
+#pragma unroll
+            for (int j = 0; j < AHEAD; ++j) {
+                p[j] = unit_dot_f32<NA>(qc[j], xf, tab, copy_off) * (lane_valid ? qa[j] : 0.0f);
+                load_row_unit(codes, absmax, row_at(kr + j + AHEAD), row_bytes, nab, code_off, ab_off, qc[j],
+                              qa[j]);
+                // one row's lookups at a time: the row's sum is formed here (the empty
+                // asm takes it), not sunk to the reduction with every row's 16
+                // looked-up entries held in registers until then
+                asm volatile("" : "+v"(p[j]));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int q = 0; q < AHEAD / 4; ++q) {
+                const float r = sum_four_rows(p[4 * q], p[4 * q + 1], p[4 * q + 2], p[4 * q + 3]);
+                if ((lane & 15) == 15) mine[kr - kb + 4 * q + row_of_lane] = r;
+            }
+        }
+        lds_barrier();
+        if (unit == 0 && kb + lane < nrows) {
+            float t = red[grp * S][lane];
+            for (int u = 1; u < S; ++u) t += red[grp * S + u][lane];
+            y[stream + (int64_t)(kb + lane) * nstreams] = t;
+        }
+        lds_barrier();
+    }
+}
+
+// ---------------------------------------------------------------------------
 // NF4 on the matrix cores (K = 2048, 4096 or 8192).
 //
 // The same products, with the per-byte work moved from the vector unit to
@@ -539,25 +752,59 @@ hipError_t launch_nf4_mfma(const uint8_t* c8, const float* absmax, const float* 
 
 }  // namespace
 
+// block 0: about eight waves (G = max(1, 8 / S) row groups); grid 0: one
+// workgroup per CU.  Measured on MI355X over the decoder shapes (K = 4096 ..
+// 28672): a second workgroup per CU (LDS allows two) or more waves per
+// workgroup gain nothing or lose, and a grid past one round of workgroups
+// loses up to a third.
+static hipError_t launch_nf4_rows(const uint8_t* c8, const float* absmax, const float* table, const uint16_t* x16,
+                                  float* y, int N, int K, int B, int grid, int block, int unroll, hipStream_t s) {
+    const int S = (K + kUnitWeights - 1) / kUnitWeights;
+    if (S > kMaxUnits) return hipErrorInvalidValue;
+    const int G = block ? block / (S * kWave) : (S < 8 ? 8 / S : 1);
+    if (block && (block % (S * kWave) != 0 || block > 1024)) return hipErrorInvalidValue;
+    if (G < 1) return hipErrorInvalidValue;
+    // unroll: rows in flight (4, 8) + 100 * independent partial sums per lane (1, 2, 4)
+    const int na = unroll / 100 ? unroll / 100 : 1;
+    const int ahead = unroll % 100 ? unroll % 100 : 4;
+    if (!grid) {
+        const int need = (N + G - 1) / G;
+        grid = need < 256 ? need : 256;
+    }
+    const dim3 b3(G * S * kWave);
+#define DG_NF4R(HH, AA)                                                                                     \
+    if (ahead == HH && na == AA) {                                                                          \
+        hipLaunchKernelGGL((k_nf4_rows<HH, AA>), dim3(grid), b3, 0, s, c8, absmax, table, x16, y, N, K, B, S); \
+        return hipGetLastError();                                                                           \
+    }
+    DG_NF4R(4, 1) DG_NF4R(4, 2) DG_NF4R(4, 4) DG_NF4R(8, 1) DG_NF4R(8, 2)
+#undef DG_NF4R
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemv_nf4(const void* codes, const float* absmax, const float* table, const void* x, float* y,
                            int N, int K, int B, const dg_launch* cfg, hipStream_t s) {
-    if (cfg && cfg->variant == DG_VARIANT_NF4_MFMA) {
+    const int variant = cfg ? cfg->variant : 0;
+    if (variant == 0 || variant == DG_VARIANT_NF4_ROWS)   // the default
+        return launch_nf4_rows((const uint8_t*)codes, absmax, table, (const uint16_t*)x, y, N, K, B,
+                               cfg ? cfg->grid : 0, cfg ? cfg->block : 0, cfg ? cfg->unroll : 0, s);
+    if (variant == DG_VARIANT_NF4_MFMA) {
         if (cfg->block || cfg->unroll) return hipErrorInvalidValue;   // fixed: 16 waves, one table
         return launch_nf4_mfma((const uint8_t*)codes, absmax, table, (const uint16_t*)x, y, N, K, B, cfg->grid, s);
     }
-    if (cfg && cfg->variant && cfg->variant != DG_VARIANT_NF4_UNITS) return hipErrorInvalidValue;
+    if (variant != DG_VARIANT_NF4_UNITS) return hipErrorInvalidValue;
     const int S = (K + kUnitWeights - 1) / kUnitWeights;   // waves per workgroup: one per unit
     if (S > kMaxUnits) return hipErrorInvalidValue;
-    if (cfg && cfg->block && cfg->block != S * kWave) return hipErrorInvalidValue;   // fixed by K
+    if (cfg->block && cfg->block != S * kWave) return hipErrorInvalidValue;   // fixed by K
     // unroll: table copies (8, 16 or 32) + 100 * independent partial sums (1, 2)
     //         + 1000 * rows in flight per wave (4 or 8)
-    const int u = cfg ? cfg->unroll : 0;
+    const int u = cfg->unroll;
     const int copies = u % 100 ? u % 100 : 8;
     const int na = (u / 100) % 10 ? (u / 100) % 10 : 1;
     const int ahead = u / 1000 ? u / 1000 : 4;
     if ((copies != 8 && copies != 16 && copies != 32) || (na != 1 && na != 2) || (ahead != 4 && ahead != 8))
         return hipErrorInvalidValue;
-    int grid = cfg && cfg->grid ? cfg->grid : 0;
+    int grid = cfg->grid;
     if (!grid) {
         // about 4096 waves in multiples of 256 workgroups, between 256 and
         // 1024 workgroups (the fastest of grids 256..2048 measured on MI355X

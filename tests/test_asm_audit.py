@@ -129,9 +129,24 @@ def test_nf4_row_loop_keeps_loads_in_flight(asm):
     """The NF4 kernels stream rows into registers with the compiler's own
     vmcnt waits; a store or an early exit inside the row loop once made it
     drain every load at the loop head.  No vmcnt(0) may appear in them."""
+    seen = 0
     for name, body in _kernels(asm["gemv_nf4.hip"]):
-        if "k_nf4I" in name:
+        if "k_nf4I" in name or "k_nf4_rowsI" in name:
             assert "s_waitcnt vmcnt(0)" not in body, name
+            seen += 1
+    assert seen >= 2
+
+
+def test_nf4_default_kernel_form(asm):
+    """The default NF4 kernel: a code byte's entry comes from one byte permute
+    and one 8-byte LDS read, the products are fp32 FMAs (no binary16 dot),
+    and four rows are reduced with the permlane swaps."""
+    ks = [(n, b) for n, b in _kernels(asm["gemv_nf4.hip"]) if "k_nf4_rowsI" in n]
+    assert ks
+    for n, b in ks:
+        assert "v_perm_b32" in b and "ds_read_b64" in b, n
+        assert "v_fmac_f32" in b and "v_dot2" not in b, n
+        assert "v_permlane32_swap" in b and "v_permlane16_swap" in b, n
 
 
 def test_stream_probe_has_no_atomics(asm):

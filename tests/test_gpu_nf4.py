@@ -16,10 +16,11 @@ pytestmark = pytest.mark.gpu
 
 # Floored relative error (the R5 form) against the fp64 oracle.  No page states
 # a bound for NF4; it is a 4-bit weight GEMV like Q4_0, so it takes Q4_0's
-# per-row bound.  Its fp32 products and sums (table values held to 22 bits)
-# leave an absolute error of a few 1e-5 on rows whose |y| is ~1e-3 of the
-# rms: over all 28672 rows of the 70B shape the worst such row reaches about
-# 3e-4.  One dropped weight moves y by ~0.1..1, far above 1e-3 of the rms.
+# per-row bound.  Its fp32 products and sums (table values exact in the
+# default kernel, held to 22 bits in the other two) leave an absolute error
+# of a few 1e-5 on rows whose |y| is ~1e-3 of the rms: over all 28672 rows of
+# the 70B shape the worst such row reaches about 3e-4.  One dropped weight
+# moves y by ~0.1..1, far above 1e-3 of the rms.
 TOL = 1e-3
 
 
@@ -73,6 +74,37 @@ def test_nf4_launch_variants(dg, dev, orc, launch, N, K, B):
     t = synth.nf4_table()
     got = _gpu(dg, dev, codes, absmax, t, xb, N, K, B, launch=launch)
     assert_close(got, orc.gemv_nf4(codes, absmax, t, xb, N, K, B), TOL, f"{launch}")
+
+
+# variant 33: (row groups G per workgroup, rows in flight + 100 * partial sums, grid); 0 is the default
+ROWS_LAUNCHES = [(0, 0, 0), (0, 8, 0), (1, 4, 0), (1, 8, 1), (2, 4, 3), (3, 8, 5), (0, 4, 1), (0, 4, 4000),
+                 (1, 4, 4000), (0, 8, 2), (0, 104, 0), (2, 204, 3), (1, 404, 0), (0, 208, 1), (3, 108, 0)]
+
+
+@pytest.mark.parametrize("G,ahead,grid", ROWS_LAUNCHES)
+@pytest.mark.parametrize("N,K,B", [(301, 8192, 64), (1000, 512, 32), (64, 4352, 64), (40, 6144, 128), (9, 28672, 64),
+                                   (3, 32768, 128), (200, 2048, 256), (129, 14336, 32)])
+def test_nf4_four_row_kernel(dg, dev, orc, N, K, B, G, ahead, grid):
+    """The conflict-free table and four-row reduction: row groups per
+    workgroup, rows in flight (whole groups of four, with streams whose row
+    count is not a multiple of four or of 64), grids from one workgroup to
+    more workgroups than rows."""
+    S = (K + 2047) // 2048
+    if G * S > 16:
+        pytest.skip("more than 16 waves per workgroup")
+    launch = dict(variant=33, unroll=ahead, grid=grid, block=G * S * 64)
+    codes, absmax, xb = _operands(orc, 625, N, K, B)
+    t = synth.nf4_table()
+    got = _gpu(dg, dev, codes, absmax, t, xb, N, K, B, launch=launch)
+    assert_close(got, orc.gemv_nf4(codes, absmax, t, xb, N, K, B), TOL, f"{launch}")
+
+
+def test_nf4_four_row_kernel_rejects_bad_shapes(dg, dev, orc):
+    codes, absmax, xb = _operands(orc, 630, 8, 8192, 64)
+    for launch in (dict(variant=33, block=128), dict(variant=33, block=1280), dict(variant=33, unroll=2),
+                   dict(variant=33, unroll=6), dict(variant=33, unroll=304), dict(variant=33, unroll=408)):
+        with pytest.raises(dg.DGError):
+            _gpu(dg, dev, codes, absmax, synth.nf4_table(), xb, 8, 8192, 64, launch=launch)
 
 
 @pytest.mark.parametrize("N,K,B", [(1, 2048, 32), (17, 2048, 128), (33, 4096, 64), (300, 4096, 256), (70, 8192, 64),
