@@ -284,15 +284,16 @@ hipError_t launch_gemv_q4_0(const void* Wq, const void* Xq, float* Y, int N, int
         // in 64-pair units otherwise; up to four columns share the units
         // kernel's weight reads while M * ceil(K / 4096) <= 8 (beyond two
         // columns only above 1024 rows); the rest of two columns, and up to
-        // eight columns of a matrix of at most 1024 rows, take the dot4
-        // kernel (the matrix cores' fixed cost per 16 x 16 tile does not pay
-        // there); the rest take the matrix cores, with the columns resident
-        // in LDS for 9..16 columns of matrices of many row tiles.
+        // ten columns of a matrix of at most 1024 rows, take the dot4 kernel
+        // (the matrix cores' fixed cost per 16 x 16 tile does not pay there:
+        // 1024 x 4096 at 9 and 10 columns, 5.1 and 5.0 us against 5.4); the
+        // rest take the matrix cores, with the columns resident in LDS for
+        // 9..16 columns of matrices of many row tiles.
         if (M == 1) {
             variant = S > 4 ? DG_VARIANT_Q4_LDS : (N >= 16384 && S <= 2 ? DG_VARIANT_Q4_LDSROW : DG_VARIANT_Q4_UNITS);
         } else if (M <= 4 && M * S <= 8 && (N > 1024 || M <= 2)) {
             variant = DG_VARIANT_Q4_UNITS;
-        } else if (M == 2 || (N <= 1024 && M <= 8)) {
+        } else if (M == 2 || (N <= 1024 && M <= 10)) {
             variant = DG_VARIANT_Q4_LDS;
             lds_rows = N > 2048 ? 2 : 1;
         } else if (N >= 8192 && K <= 4096 && M >= 9 && M <= 16) {

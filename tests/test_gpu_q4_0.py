@@ -183,7 +183,7 @@ def test_q4_0_mfma_any_grid_covers_every_row_tile(dg, dev, orc, grid, unroll):
     assert_close(got, orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M), TOL, str(launch))
 
 
-@pytest.mark.parametrize("M,R", [(2, 1), (2, 2), (3, 4), (8, 1), (8, 2), (24, 1), (24, 2)])
+@pytest.mark.parametrize("M,R", [(2, 1), (2, 2), (3, 4), (8, 1), (8, 2), (9, 1), (10, 1), (10, 2), (24, 1), (24, 2)])
 def test_q4_0_lds_rows_per_wave(dg, dev, orc, M, R):
     N, K = 77, 4608
     Wq, Xq = _operands(orc, 230, N, K, M)
