@@ -71,7 +71,7 @@ KERNELS = {
         2 * 4096 * 4096 + 2 * 4096 + 2 * 4096,
         ["gemv_dense.hip", "dg_device.h"]),
     "gemv_nf4_28672x8192_b64": (
-        r"k_nf4<", "NF4 x bf16, M = 1, N = 28672, K = 8192, block 64",
+        r"k_nf4_rows<", "NF4 x bf16, M = 1, N = 28672, K = 8192, block 64",
         28672 * 8192 // 2 + 4 * 28672 * (8192 // 64) + 2 * 8192 + 64 + 4 * 28672,
         ["gemv_nf4.hip", "dg_device.h", "dg_internal.h"]),
     "stream_read_1GiB": (
