@@ -453,9 +453,10 @@ enum {
     DG_VARIANT_NF4_ROWS = 33        /* the default: code bytes looked up in a table of binary32
                                        value pairs (32 conflict-free copies in LDS), fp32 FMA,
                                        lane sums reduced four rows at a time; block = G row groups
-                                       x 64*ceil(K/2048) (<= 1024), unroll = rows in flight (4, 8)
-                                       + 100 * partial sums per lane (1, 2, 4; 4 only with 4 rows
-                                       in flight)                                               */
+                                       x 64*ceil(K/2048) (<= 1024; 0: at least eight waves),
+                                       unroll = rows in flight (4, 8; 0: 8 for K of 4097..8192,
+                                       else 4) + 100 * partial sums per lane (1, 2, 4; 4 only
+                                       with 4 rows in flight)                                   */
 };
 
 dg_status dg_gemv_f16_ex(const void* W, const void* x, void* y, int64_t N, int64_t K,

@@ -752,21 +752,26 @@ hipError_t launch_nf4_mfma(const uint8_t* c8, const float* absmax, const float* 
 
 }  // namespace
 
-// block 0: about eight waves (G = max(1, 8 / S) row groups); grid 0: one
-// workgroup per CU.  Measured on MI355X over the decoder shapes (K = 4096 ..
-// 28672): a second workgroup per CU (LDS allows two) or more waves per
-// workgroup gain nothing or lose, and a grid past one round of workgroups
-// loses up to a third.
+// block 0: the fewest row groups that make at least eight waves (G =
+// ceil(8 / S) below eight units, 8..16 waves); rows in flight 0: eight for
+// K of 4097..8192, else four; grid 0: one workgroup per CU.  Measured on MI355X over the
+// decoder shapes and the 70B MLP pair (K = 4096, 8192, 14336, 28672), each
+// launch timed against the others in turn on one device: K = 14336 with two
+// row groups (14 waves) instead of one took 9.0 instead of 9.9 us, and K =
+// 8192 with eight rows in flight 23.5 instead of 24.7 us at 28672 rows,
+// while eight rows in flight lost 5-18% at the other K.  A second workgroup
+// per CU (LDS allows two) or more waves per workgroup gain nothing or lose,
+// and a grid past one round of workgroups loses up to a third.
 static hipError_t launch_nf4_rows(const uint8_t* c8, const float* absmax, const float* table, const uint16_t* x16,
                                   float* y, int N, int K, int B, int grid, int block, int unroll, hipStream_t s) {
     const int S = (K + kUnitWeights - 1) / kUnitWeights;
     if (S > kMaxUnits) return hipErrorInvalidValue;
-    const int G = block ? block / (S * kWave) : (S < 8 ? 8 / S : 1);
+    const int G = block ? block / (S * kWave) : (S < 8 ? (8 + S - 1) / S : 1);
     if (block && (block % (S * kWave) != 0 || block > 1024)) return hipErrorInvalidValue;
     if (G < 1) return hipErrorInvalidValue;
     // unroll: rows in flight (4, 8) + 100 * independent partial sums per lane (1, 2, 4)
     const int na = unroll / 100 ? unroll / 100 : 1;
-    const int ahead = unroll % 100 ? unroll % 100 : 4;
+    const int ahead = unroll % 100 ? unroll % 100 : (S == 3 || S == 4 ? 8 : 4);
     if (!grid) {
         const int need = (N + G - 1) / G;
         grid = need < 256 ? need : 256;
