@@ -48,13 +48,15 @@ def _nthreads(threads) -> int:
 _lib = None
 
 
-def compile_c(src: str, out: str) -> str:
+def compile_c(src: str, out: str, extra_flags=()) -> str:
     """gcc -O2, no fast-math, no FMA contraction, src linked with the
-    row-partitioned driver (oracle_par.c, which calls src's routines)."""
+    row-partitioned driver (oracle_par.c, which calls src's routines).
+    extra_flags go after the defaults (the sanitizer test builds a copy with
+    AddressSanitizer and UndefinedBehaviorSanitizer this way)."""
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [
         "gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-pthread", "-ffp-contract=off",
-        "-fno-fast-math", "-Wall", "-Wextra", "-I", _HERE, "-o", tmp, src, _PAR_SRC, "-lm",
+        "-fno-fast-math", "-Wall", "-Wextra", *extra_flags, "-I", _HERE, "-o", tmp, src, _PAR_SRC, "-lm",
     ]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
@@ -70,13 +72,21 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+# Another build of oracle.c to load instead of liboracle.so (the sanitizer
+# test runs the pins in a child process against such a build).
+LIB_ENV = "DG_ORACLE_LIB"
+
+
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB):
-        build()
-    _lib = _bind(ctypes.CDLL(_LIB))
+    path = os.environ.get(LIB_ENV)
+    if not path:
+        if not os.path.exists(_LIB):
+            build()
+        path = _LIB
+    _lib = _bind(ctypes.CDLL(path))
     return _lib
 
 
