@@ -1227,8 +1227,8 @@ def main():
                     help="seconds of oracle work for cpu_baseline (half on one core, half on all)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the path shards by output rows with no exchange, but no multi-GPU run exists here.",
+        print(f"bench.py: the library and this benchmark run on one GPU (asked for --gpus {args.gpus}); "
+              "the path would shard by output rows with no exchange, but no multi-GPU path is implemented.",
               file=sys.stderr)
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0:

@@ -26,7 +26,8 @@ _PAR_SRC = os.path.join(_HERE, "oracle_par.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 # Host threads the row-partitioned driver uses when asked for "all": the
-# CPUs this process may run on, at most 16 (a GPU machine gives one GPU's job 16).
+# CPUs this process may run on, at most 16 (the host share of one GPU on an
+# MI355X node).
 MAX_THREADS = 16
 
 

@@ -8,8 +8,9 @@ outside an array, a use after free, a signed overflow, an invalid shift or a
 misaligned load in any oracle routine ends the child with a sanitizer report,
 and the test fails with it.  The child's pytest captures Python-level output
 only (--capture=sys), so a report written to file descriptor 2 as the
-process ends is not lost with pytest's own capture.  The pins must also all pass on this build: the
-sanitizers change no arithmetic (-ffp-contract=off is kept).
+process ends is not lost with pytest's own capture.  The pins must also all
+pass on the sanitized build: the sanitizers change no arithmetic
+(-ffp-contract=off is kept).
 """
 import os
 import shutil
