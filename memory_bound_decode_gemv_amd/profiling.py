@@ -457,8 +457,11 @@ def pmc_markdown(summary, command):
              f"    {command}", "",
              "Per launch, averaged over four dispatches.  `VALU/wave` and `LDS/wave` are instructions per wave; "
              "`VALU busy` is SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES x waves per SIMD (both counters in units of "
-             "four cycles): the share of a SIMD's cycles spent issuing vector instructions.", "",
-             "| workload | kernel | VGPRs | threads/WG | waves | waves/SIMD | VALU/wave | MFMA | LDS/wave | "
+             "four cycles): the share of a SIMD's cycles spent issuing vector instructions.  `rocprof VGPR_Count` "
+             "is the profiler's field as printed; on gfx950 it reads half the compiler's register count (60 for a "
+             "114-register kernel, 80 for 160: allocation granules of 8 counted as 4), so the register counts "
+             "and the occupancy they allow are taken from profiles/kernel_resources.md.", "",
+             "| workload | kernel | rocprof VGPR_Count | threads/WG | waves | waves/SIMD | VALU/wave | MFMA | LDS/wave | "
              "LDS bank-conflict cycles | VALU busy |",
              "|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in summary:
@@ -473,6 +476,108 @@ def pmc_markdown(summary, command):
                      f"{r.get('SQ_INSTS_LDS', 0) / max(waves, 1):.0f} | {r.get('SQ_LDS_BANK_CONFLICT', 0):.3g} | "
                      f"{busy} |")
     return "\n".join(lines) + "\n"
+
+
+_INFO_KEYS = {"TotalNumSgprs": "sgpr", "NumVgprs": "vgpr", "NumAgprs": "agpr", "ScratchSize": "scratch",
+              "Occupancy": "occupancy", "LDSByteSize": "lds_static"}
+
+
+def asm_resources(asm_text):
+    """Per kernel of one gfx950 assembly file: the compiler's resource report
+    (the "; Kernel info:" block that follows each kernel): VGPRs, AGPRs,
+    SGPRs, scratch bytes, statically sized LDS and the waves per SIMD its
+    registers allow ("Occupancy"; LDS sized at launch is not counted there)."""
+    out = []
+    for m in re.finditer(r"; Kernel info:\n((?:;[^\n]*\n)+)", asm_text):
+        head = asm_text[:m.start()]
+        names = re.findall(r"^\s*\.set\s+(_Z\w+)\.private_seg_size", head, re.M)
+        if not names:
+            continue
+        rec = {"mangled": names[-1]}
+        for line in m.group(1).splitlines():
+            k, _, v = line[1:].partition(":")
+            k = k.strip()
+            if k in _INFO_KEYS:
+                rec[_INFO_KEYS[k]] = int(re.match(r"\s*(\d+)", v).group(1))
+        out.append(rec)
+    return out
+
+
+def _demangle(names):
+    import subprocess
+    try:
+        r = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True, check=True)
+        return r.stdout.splitlines()
+    except (OSError, subprocess.CalledProcessError):
+        return list(names)
+
+
+def resources_markdown(command=""):
+    """Compiler resource report of every kernel the library builds, one line
+    per kernel template (its instantiations' ranges)."""
+    import tempfile
+    from . import _build
+    rows = []
+    with tempfile.TemporaryDirectory() as d:
+        for src in _build.sources():
+            out = _build.device_asm(src, os.path.join(d, os.path.basename(src) + ".s"))
+            with open(out) as f:
+                recs = asm_resources(f.read())
+            for r, dem in zip(recs, _demangle([r["mangled"] for r in recs])):
+                r["name"] = dem
+                r["source"] = os.path.basename(src)
+                rows.append(r)
+    def norm(name):
+        n = re.sub(r"^void\s+", "", name)
+        n = n.replace("dg::(anonymous namespace)::", "").replace("dg::mfma::", "").replace("dg::q4::", "")
+        return re.sub(r"\s+", "", n.split("(")[0])
+
+    groups = collections.OrderedDict()
+    for r in rows:
+        r["norm"] = norm(r["name"])
+        groups.setdefault((r["source"], re.sub(r"<.*", "", r["norm"])), []).append(r)
+
+    def rng(rs, k):
+        vals = [r.get(k, 0) for r in rs]
+        lo, hi = min(vals), max(vals)
+        return str(lo) if lo == hi else f"{lo}-{hi}"
+
+    lines = ["# Compiler resource report of every kernel (gfx950)", "",
+             "Command:", "", "    " + (command or "python -m memory_bound_decode_gemv_amd.profiling resources "
+                                      "--md profiles/kernel_resources.md"), "",
+             "From the \"; Kernel info\" block hipcc writes after each kernel in the device assembly "
+             "(the same build flags as the library).  One line per kernel template: ranges over its "
+             "instantiations.  `waves/SIMD` is the occupancy the registers allow (the compiler's "
+             "\"Occupancy\"); LDS sized at launch (every staged kernel's buffers) is not part of it and "
+             "lowers it further where a workgroup's LDS is large.  Scratch 0 everywhere means no spills.", "",
+             f"{len(rows)} kernels in {len(groups)} templates.", "",
+             "| source | kernel template | instantiations | VGPRs | AGPRs | SGPRs | static LDS B | scratch B | waves/SIMD |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for (src, tmpl), rs in groups.items():
+        lines.append(f"| {src} | `{tmpl}` | {len(rs)} | {rng(rs, 'vgpr')} | {rng(rs, 'agpr')} | {rng(rs, 'sgpr')} | "
+                     f"{rng(rs, 'lds_static')} | {rng(rs, 'scratch')} | {rng(rs, 'occupancy')} |")
+    lines += ["", "The instantiations the default dispatch launches for the headline and named workloads:", "",
+              "| workload | kernel | VGPRs | SGPRs | waves/SIMD (registers) |", "|---|---|---|---|---|"]
+    by_norm = {r["norm"]: r for r in rows}
+    for label, key in DEFAULT_KERNELS:
+        r = by_norm.get(key)
+        if r is not None:
+            lines.append(f"| {label} | `{key}` | {r.get('vgpr')} | {r.get('sgpr')} | {r.get('occupancy')} |")
+    return "\n".join(lines) + "\n"
+
+
+# (workload, kernel instantiation) of the default launches named in the report
+DEFAULT_KERNELS = [
+    ("fp16 GEMV 4096x4096", "k_gemv_wide<false,2,false,2>"),
+    ("bf16 GEMV (decoder shapes, lm-head)", "k_gemv_wide<true,2,false,2>"),
+    ("Q4_0 M=1 28672x8192", "k_q4_m1_ldsrow<2,5,2,false>"),
+    ("Q4_0 M=16 4096x14336", "k_qmfma<FmtQ4_0,8,16,1,4,2>"),
+    ("Q4_0 M=17..24 4096x14336", "k_qmfma<FmtQ4_0,8,24,1,12,1>"),
+    ("Q4_0 M=9..16 14336x4096 (resident columns)", "k_qres<FmtQ4_0,1,4,2,2>"),
+    ("NF4 M=1, K=8192", "k_nf4_rows<8,1>"),
+    ("NF4 M=1, other K", "k_nf4_rows<4,1>"),
+    ("Q8_1 quantiser", "k_quantize_q8_1"),
+]
 
 
 def main(argv=None):
@@ -512,7 +617,14 @@ def main(argv=None):
     t.add_argument("--md", required=True)
     t.add_argument("--command", default="")
     t.add_argument("--runs", default=None, help="kernel-trace CSV: add per-run durations")
+    rs = sub.add_parser("resources")
+    rs.add_argument("--md", default=os.path.join(PROFILES, "kernel_resources.md"))
+    rs.add_argument("--command", default="")
     a = ap.parse_args(argv)
+    if a.cmd == "resources":
+        with open(a.md, "w") as f:
+            f.write(resources_markdown(a.command))
+        return 0
     if a.cmd == "counters":
         s = counters_summary(a.fetch_csv, a.write_csv, a.tcc)
         with open(a.json, "w") as f:
