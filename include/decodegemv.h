@@ -441,7 +441,7 @@ enum {
     /* Q8_0 */
     DG_VARIANT_Q8_LDSROW = 21,      /* M = 1: weight rows copied to LDS (K <= 16384)             */
     DG_VARIANT_Q8_MFMA = 22,        /* int8 matrix cores                                          */
-    DG_VARIANT_Q8_UNITS = 23,       /* as DG_VARIANT_Q4_UNITS, Q8_0 weights; also 9 or 10 columns
+    DG_VARIANT_Q8_UNITS = 23,       /* as DG_VARIANT_Q4_UNITS, Q8_0 weights; also 9..12 columns
                                        when K <= 4096                                          */
     DG_VARIANT_Q8_MFMA_RES = 24,    /* as DG_VARIANT_Q4_MFMA_RES, Q8_0 weights                     */
     /* NF4 */

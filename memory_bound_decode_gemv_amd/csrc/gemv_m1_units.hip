@@ -101,7 +101,7 @@ k_units(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
     using G = UnitGeom<F>;
     static_assert(DEPTH >= 2 && DEPTH <= 4, "pipeline depth");
     static_assert(G::kC * (DEPTH - 1) <= 63, "wait count exceeds the vmcnt field");
-    static_assert(MC >= 1 && (MC * S <= 8 || (S == 1 && MC <= 10)), "activation pairs held in registers");
+    static_assert(MC >= 1 && (MC * S <= 8 || (S == 1 && MC <= 12)), "activation pairs held in registers");
     extern __shared__ u32x4 lds_units[];
     const int lane = lane_id();
     const int wave = wave_in_block();
@@ -221,8 +221,8 @@ hipError_t launch_units(int K, int M, int depth, const void* Wq, const void* Xq,
     }
 #define DG_SM(SS, MM) DG_SMD(SS, MM, 2) DG_SMD(SS, MM, 3) DG_SMD(SS, MM, 4)
     DG_SM(1, 1) DG_SM(1, 2) DG_SM(1, 3) DG_SM(1, 4) DG_SM(1, 5) DG_SM(1, 6) DG_SM(1, 7) DG_SM(1, 8)
-    if constexpr (F::kBlockBytes == 34) {   // 8-bit weights: nine and ten columns of rows of one unit
-        DG_SM(1, 9) DG_SM(1, 10)
+    if constexpr (F::kBlockBytes == 34) {   // 8-bit weights: 9..12 columns of rows of one unit
+        DG_SM(1, 9) DG_SM(1, 10) DG_SM(1, 11) DG_SM(1, 12)
     }
     DG_SM(2, 1) DG_SM(2, 2) DG_SM(2, 3) DG_SM(2, 4)
     DG_SM(3, 1) DG_SM(3, 2)

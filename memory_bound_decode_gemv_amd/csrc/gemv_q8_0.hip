@@ -152,21 +152,23 @@ hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int
         // Measured on MI355X over the decoder shapes, the 70B MLP and M =
         // 1..24: up to four columns stream rows through LDS in 64-pair units
         // while M * ceil(K / 4096) <= 8, and so do up to eight columns of a
-        // matrix of more than 512 row tiles and up to ten of a matrix of at
-        // most 1024 rows with K <= 4096 (1024 x 4096 at 9 and 10 columns:
-        // 4.8 and 5.0 us against 6.0 on the matrix cores, whose 64 row tiles
-        // leave most of the chip idle); in between, the matrix cores' parts
-        // of K run every CU.  The rest take the matrix cores, with the
-        // columns resident in LDS for 12..16 columns of matrices of many row
-        // tiles.
-        const bool units_m = M <= 4 || (M <= 8 && (N <= 1024 || N > 8192)) || (M <= 10 && N <= 1024 && S == 1);
-        const bool units_fit = M * S <= 8 || (S == 1 && M <= 10);
+        // matrix of more than 512 row tiles and, on matrices of at most 1024
+        // rows with rows of one unit, up to twelve columns for K of
+        // 2049..4096 and ten below (1024 x 4096 at 9..12 columns: 4.9, 5.1,
+        // 5.3 and 5.5 us against 6.0 on the matrix cores, whose 64 row tiles
+        // leave most of the chip idle; at K = 2048 the matrix cores win from
+        // 11 columns); in between, the matrix cores' parts of K run every
+        // CU.  The rest take the matrix cores, with the columns resident in
+        // LDS for 12..16 columns of matrices of many row tiles.
+        const bool units_small = N <= 1024 && S == 1 && (M <= 10 || (M <= 12 && K > 2048));
+        const bool units_m = M <= 4 || (M <= 8 && (N <= 1024 || N > 8192)) || units_small;
+        const bool units_fit = M * S <= 8 || (S == 1 && M <= 12);
         variant = S <= 4 && units_fit && units_m                 ? DG_VARIANT_Q8_UNITS
                   : (N >= 8192 && K <= 4096 && M >= 12 && M <= 16) ? DG_VARIANT_Q8_MFMA_RES
                                                              : DG_VARIANT_Q8_MFMA;
     }
     if (variant == DG_VARIANT_Q8_UNITS) {
-        if (S > 4 || (M * S > 8 && !(S == 1 && M <= 10))) return hipErrorInvalidValue;
+        if (S > 4 || (M * S > 8 && !(S == 1 && M <= 12))) return hipErrorInvalidValue;
         int grid = cfg ? cfg->grid : 0, block = cfg ? cfg->block : 0;
         if (!grid && !block) units_default_grid(N, M, grid, block);
         return launch_q8_units(K, M, depth, Wq, Xq, Y, N, grid, block, s);

@@ -101,11 +101,12 @@ UNITS_FEW = [None, dict(variant=23), dict(variant=23, unroll=2), dict(variant=23
 
 @pytest.mark.parametrize("N,K,M", [(1, 256, 4), (7, 4096, 4), (70, 2304, 3), (33, 8192, 2), (130, 4352, 2),
                                    (301, 4096, 2), (1000, 512, 3), (9, 4096, 8), (33, 8192, 4), (19, 14336, 2),
-                                   (64, 12288, 2), (9, 4096, 9), (70, 2304, 10), (1000, 512, 9), (130, 4096, 10)])
+                                   (64, 12288, 2), (9, 4096, 9), (70, 2304, 10), (1000, 512, 9), (130, 4096, 10),
+                                   (9, 4096, 11), (130, 4096, 12), (700, 2304, 12)])
 @pytest.mark.parametrize("launch", UNITS_FEW, ids=[str(v) for v in UNITS_FEW])
 def test_q8_0_units_few_columns(dg, dev, orc, N, K, M, launch):
-    """Two to ten columns through the 64-pair units kernel (M * ceil(K / 4096) <= 8, or up to ten columns of
-    rows of one unit, K <= 4096)."""
+    """Two to twelve columns through the 64-pair units kernel (M * ceil(K / 4096) <= 8, or up to twelve
+    columns of rows of one unit, K <= 4096)."""
     Wq, Xq = _operands(orc, 432, N, K, M)
     got = _gpu(dg, dev, Wq, Xq, N, K, M, launch=launch)
     assert_close(got, orc.gemv_q8_0_q8_1(Wq, Xq, N, K, M), TOL, f"{N}x{K} M={M} {launch}")
@@ -207,9 +208,9 @@ def test_q8_0_overrides_beyond_kernel_limits_are_rejected(dg, dev):
         with pytest.raises(dg.DGError) as e:
             dg.dg_gemv_q8_0(W, X, Y, N, K, M, launch=launch)
         assert e.value.status == dg.DG_ERR_ARG, launch
-    # rows of one unit (K <= 4096) take at most ten columns in the units kernel
+    # rows of one unit (K <= 4096) take at most twelve columns in the units kernel
     with pytest.raises(dg.DGError) as e:
-        dg.dg_gemv_q8_0(W, X, Y, N, 4096, 11, launch=dict(variant=23))
+        dg.dg_gemv_q8_0(W, X, Y, N, 4096, 13, launch=dict(variant=23))
     assert e.value.status == dg.DG_ERR_ARG
 
 
