@@ -159,12 +159,13 @@ hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int
         // leave most of the chip idle; at K = 2048 the matrix cores win from
         // 11 columns); in between, the matrix cores' parts of K run every
         // CU.  The rest take the matrix cores, with the columns resident in
-        // LDS for 12..16 columns of matrices of many row tiles.
+        // LDS for 9..16 columns of matrices of many row tiles (14336 x 4096
+        // at 9..11 columns: 16.7-16.8 us against 16.9-17.0 streaming).
         const bool units_small = N <= 1024 && S == 1 && (M <= 10 || (M <= 12 && K > 2048));
         const bool units_m = M <= 4 || (M <= 8 && (N <= 1024 || N > 8192)) || units_small;
         const bool units_fit = M * S <= 8 || (S == 1 && M <= 12);
         variant = S <= 4 && units_fit && units_m                 ? DG_VARIANT_Q8_UNITS
-                  : (N >= 8192 && K <= 4096 && M >= 12 && M <= 16) ? DG_VARIANT_Q8_MFMA_RES
+                  : (N >= 8192 && K <= 4096 && M >= 9 && M <= 16)  ? DG_VARIANT_Q8_MFMA_RES
                                                              : DG_VARIANT_Q8_MFMA;
     }
     if (variant == DG_VARIANT_Q8_UNITS) {
