@@ -141,7 +141,10 @@ dg_status dg_gemv_bf16(const void* W, const void* x, float* y,
  * (Q4_0/Q8_1 harness; the small-batch kernel for 1..24 columns) and of the
  * 4-bit M = 1 GEMV of the bitsandbytes issue on 70B 4-bit decode.  The inner
  * 32-term sum is exact in int32; the scaling and the sum over blocks are
- * fp32.  The fp16 block sum s of Q8_1 is not used.
+ * fp32.  The fp16 block sum s of Q8_1 is not used.  (With exactly 17 columns
+ * the 17th column's block sum is formed as four exact int32 partial sums of
+ * 8 terms, each scaled in fp32, so its rounding differs from the other
+ * columns' by a few fp32 ulps.)
  *
  *   Wq  device, N rows of K/32 Q4_0 blocks, 18 bytes each (binary16 d, then 16
  *       code bytes: byte i = weight i in the low nibble, weight i+16 in the
@@ -196,7 +199,8 @@ dg_status dg_gemv_q4_0_f32(const void* Wq, const float* x, float* Y, void* Xq,
  *
  * The 8-bit weight format that "The kernel that waited for itself" runs next
  * to Q4_0 through the same Q8_1-activation path (its four-model comparison).
- * Exact int32 inner sums, fp32 scaling and sum over blocks.
+ * Exact int32 inner sums, fp32 scaling and sum over blocks (the 17th column
+ * of a 17-column call as for Q4_0: four exact partial sums, each scaled).
  *
  *   Wq  device, N rows of K/32 Q8_0 blocks, 34 bytes each (binary16 d, then
  *       32 int8 codes), rows packed back to back; 16-byte aligned.

@@ -65,7 +65,7 @@ using namespace mfma;
 template <class WF, int CB, int MP, int RT, int KS>
 struct MfmaGeom {
     static_assert(CB % 8 == 0, "chunks hold whole 144-byte groups of 8 blocks");
-    static_assert(MP == 4 || MP == 8 || MP == 16 || MP == 24 || MP == 32, "padded column count");
+    static_assert(MP == 4 || MP == 8 || MP == 16 || MP == 17 || MP == 24 || MP == 32, "padded column count");
     static constexpr int kW = RT * KS;                           // waves per workgroup
     static_assert(kW == 4 || kW == 8 || kW == 12 || kW == 16, "4, 8, 12 or 16 waves");
     static constexpr int kNT = (MP + 15) / 16;                   // 16-column MFMA tiles
@@ -96,7 +96,7 @@ template <class WF, int CB, int MP, int RT, int KS, int DEPTH>
 constexpr size_t mfma_lds_bytes() {
     using G = MfmaGeom<WF, CB, MP, RT, KS>;
     const size_t main = (size_t)DEPTH * G::kStageBytes;
-    const size_t red = (size_t)G::kW * G::kNT * 4 * 64 * 4;   // partial sums of the KS parts
+    const size_t red = (size_t)G::kW * (G::kNT * 4 + (MP == 17)) * 64 * 4;   // partial sums of the KS parts
     return main > red ? main : red;
 }
 
@@ -198,7 +198,8 @@ __global__ void __launch_bounds__(64 * RT * KS)
 k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
         int N, int K, int M) {
     using G = MfmaGeom<WF, CB, MP, RT, KS>;
-    constexpr int NT = G::kNT;
+    constexpr bool TAIL = MP == 17;                // column 16 on the vector unit (below)
+    constexpr int NT = TAIL ? 1 : G::kNT;          // 16-column matrix-core tiles
     constexpr int GB = RT * KS >= 12 ? 4 : 8;   // blocks per operand group
     static_assert(DEPTH >= 1 && DEPTH <= 5, "pipeline depth");
     static_assert(G::kCopies * (DEPTH - 1) <= 63, "wait count exceeds the vmcnt field");
@@ -242,6 +243,7 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
         f32x4 acc[NT];
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        float tacc = 0.0f;   // the 17th column (TAIL): this lane's share of row rn
 
         int slot = 0;
         for (int it = 0; it < iters; ++it) {
@@ -274,12 +276,12 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
                 for (int o = 0; o < cb; o += GB) {
                     long bop[GB];
                     uint32_t h4[GB];
+                    float dw[GB];
 #pragma unroll
                     for (int p = 0; p < GB / 2; ++p) {   // block pairs o + 2p, o + 2p + 1
                         const uint32_t* wp =
                             reinterpret_cast<const uint32_t*>(rowp + ((o >> 1) + p) * 2 * WF::kBlockBytes);
-                        float dunused[2];
-                        WF::decode(wp, g, bop + 2 * p, dunused);
+                        WF::decode(wp, g, bop + 2 * p, dw + 2 * p);
                         WF::scale_bits(wp, dwidth, h4 + 2 * p);
                     }
 #pragma unroll
@@ -312,19 +314,45 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
 #pragma unroll
                             for (int r = 0; r < 4; ++r) acc[t][r] = fmaf((float)dsum[i][r], sc[i][r], acc[t][r]);
                     }
+                    if constexpr (TAIL) {
+                        // 17 columns: the 17th on the vector unit instead of a second,
+                        // mostly empty matrix-core tile.  The lane's B operand holds its
+                        // row's codes at 8 of the block's 32 k-slots; two v_dot4 with the
+                        // matching q8 codes give an exact partial block sum, which the
+                        // lane scales by d4 d8 (the other 24 k-slots are the other three
+                        // lane groups', added after the loop).
+#pragma unroll
+                        for (int i = 0; i < GB; ++i) {
+                            uint32_t wl = (uint32_t)(uint64_t)bop[i], wh = (uint32_t)((uint64_t)bop[i] >> 32);
+                            if constexpr (WF::kOffset) {   // codes 0..15 -> q - 8 as int8, byte by byte
+                                wl = (wl + 0x78787878u) ^ 0x80808080u;
+                                wh = (wh + 0x78787878u) ^ 0x80808080u;
+                            }
+                            const uint32_t* ab = reinterpret_cast<const uint32_t*>(
+                                ap + (16 * G::kAColSlots * 16 + (o + i) * kQ81Bytes));
+                            const int sdot = dot4_i8(wh, ab[5 + g], dot4_i8(wl, ab[1 + g], 0));
+                            tacc = fmaf((float)sdot, dw[i] * half_lo_to_f32(ab[0]), tacc);
+                        }
+                    }
                 }
             }
             slot = slot + 1 == DEPTH ? 0 : slot + 1;
         }
 
+        if constexpr (TAIL) {   // the four lane groups' shares of each row, in a fixed order
+            tacc += __shfl_xor(tacc, 16);
+            tacc += __shfl_xor(tacc, 32);
+        }
         // combine the KS parts of each row tile (fixed order) and store
         if constexpr (KS > 1) {
             lds_barrier();   // every wave is done reading the buffers: reuse them
             float* red = reinterpret_cast<float*>(lds);
+            float* const tred = red + G::kW * NT * 4 * 64;
 #pragma unroll
             for (int t = 0; t < NT; ++t)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) red[((wave * NT + t) * 4 + r) * 64 + lane] = acc[t][r];
+            if constexpr (TAIL) tred[wave * 64 + lane] = tacc;
             lds_barrier();
             if (part == 0) {
 #pragma unroll
@@ -335,6 +363,9 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
                         for (int s2 = 1; s2 < KS; ++s2) v += red[(((wave + s2) * NT + t) * 4 + r) * 64 + lane];
                         acc[t][r] = v;
                     }
+                if constexpr (TAIL) {
+                    for (int s2 = 1; s2 < KS; ++s2) tacc += tred[(wave + s2) * 64 + lane];
+                }
             }
         }
         if (part == 0) {
@@ -347,6 +378,9 @@ k_qmfma(const uint8_t* __restrict__ Wq, const uint8_t* __restrict__ Xq, float* _
                         const int m = t * 16 + g * 4 + r;
                         if (m < M) Y[(size_t)m * N + n] = acc[t][r];
                     }
+                if constexpr (TAIL) {
+                    if (g == 0) Y[(size_t)16 * N + n] = tacc;
+                }
             }
         }
     }
@@ -413,7 +447,11 @@ hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float
         // 8192 (one chunk deep there, as the chunks of 24 columns fill the
         // LDS), over 12 waves one deep beyond 16 on longer Q4_0 rows, else
         // over 4 waves two deep.  More row tiles: tiles share each
-        // activation chunk.
+        // activation chunk.  17 columns run one 16-column tile plus the 17th
+        // column on the vector unit (MP = 17), over 8 waves two deep up to
+        // 512 row tiles (Q4_0; Q8_0 as above) and over two tiles of two waves
+        // beyond: 4096 x 14336 Q4_0 15.8 against 16.8 us with a second
+        // matrix-core tile, 14336 x 4096 Q8_0 19.0 against 20.7 us.
         const int tiles = (N + 15) / 16;
         CB = 8;
         if (tiles <= 512) {
@@ -423,11 +461,12 @@ hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float
             KS = (few || wide) ? 8 : 4;
             DEPTH = wide ? 1 : 2;
             if (M > 16 && K > 8192 && WF::kBlockBytes == 18) { KS = 12; DEPTH = 1; }   // 17..24 columns, long rows
+            if (M == 17 && WF::kBlockBytes == 18) { KS = 8; DEPTH = 2; }         // 16 + 1 columns
         } else if (WF::kBlockBytes == 34) {
             // Q8_0: its weight buffers are twice those of Q4_0, so fewer row
             // tiles share a workgroup's LDS.
             DEPTH = 2;
-            if (M <= 16) { RT = 2; KS = 2; }
+            if (M <= 17) { RT = 2; KS = 2; }
             else { RT = 4; KS = 1; }
         } else {
             DEPTH = 2;
@@ -438,6 +477,7 @@ hipError_t launch_qmfma(int M, int unroll, const void* Wq, const void* Xq, float
     if (M <= 4) return launch_mfma_mp<WF, 4>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
     if (M <= 8) return launch_mfma_mp<WF, 8>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
     if (M <= 16) return launch_mfma_mp<WF, 16>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
+    if (M == 17) return launch_mfma_mp<WF, 17>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
     return launch_mfma_mp<WF, 24>(RT, KS, DEPTH, CB, Wq, Xq, Y, N, K, M, grid, s);
 }
 
