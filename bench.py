@@ -657,7 +657,9 @@ def suite(args):
     if want("q4m1"):
         suite_q4_m1(dg, torch, emit, ceil_gbps)
     if want("q4m"):
-        suite_q4_small_m(dg, torch, emit, ceil_gbps)
+        suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=not args.no_sweep)
+    if want("q4tiles"):
+        suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=not args.no_sweep)
     if want("q8"):
         suite_q8_0(dg, torch, emit, ceil_gbps)
     if want("m1"):
@@ -833,6 +835,56 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
         torch.cuda.empty_cache()
 
 
+
+# (RT, KW, D) configurations of the tiled Q4_0 kernel (dg_gemv_q4_0_tiles_ex:
+# unroll = KP*1000000 + RT*10000 + KW*100 + D)
+TILES_BUILT = [(1, 4, 2), (1, 4, 4), (1, 8, 2), (1, 8, 4), (1, 16, 2), (2, 4, 2), (2, 4, 4), (2, 2, 4), (2, 8, 2),
+               (4, 1, 4), (4, 2, 2), (4, 2, 4), (4, 4, 2), (4, 4, 4)]
+TILES_WS_BYTES = 40 << 20   # enough for every configuration of the four 8B shapes
+
+
+def suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=True, shapes=None, ms=None):
+    """The Q4_0 small-M sweep over the four 8B shapes with the weights in
+    16-row tiles (dg_repack_q4_0_tiles once, outside the timing), every M, and
+    at the named M every built configuration with K split 1..8 ways."""
+    for (N, K) in shapes or [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)]:
+        nc = copies_for(18 * N * K // 32)
+        Wts = []
+        for Wq in q4_copies(3, N, K, nc):
+            Wt = torch.empty(dg.dg_q4_0_tiles_bytes(N, K), dtype=torch.uint8, device="cuda")
+            dg.dg_repack_q4_0_tiles(Wq, Wt, N, K)
+            torch.cuda.synchronize()
+            del Wq
+            Wts.append(Wt)
+        ws = torch.zeros(TILES_WS_BYTES, dtype=torch.uint8, device="cuda")
+        prev = None
+        for M in ms or range(1, 25):
+            Xq = q8_columns(3, K, M)
+            Y = torch.empty(M * N, dtype=torch.float32, device="cuda")
+            calls = [(lambda c=c: dg.dg_gemv_q4_0_tiles(Wts[c % nc], Xq, Y, N, K, M, ws=ws))
+                     for c in range(n_calls(nc))]
+            us, iqr = time_per_call(calls)
+            cps = M / (us * 1e-6)
+            dip = None if prev is None else round(cps / prev - 1.0, 4)
+            prev = cps
+            emit(record(f"gemv_q4_0_tiles {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M, copies=nc,
+                        variant="default", columns_per_s=round(cps, 1), change_vs_prev_M=dip))
+            if sweep and M in (1, 4, 8, 16, 17, 24):
+                for (rt, kw, d) in TILES_BUILT:
+                    for kp in (1, 2, 4):
+                        launch = dict(unroll=kp * 1000000 + rt * 10000 + kw * 100 + d)
+                        calls = [(lambda c=c, launch=launch: dg.dg_gemv_q4_0_tiles(Wts[c % nc], Xq, Y, N, K, M,
+                                                                                  ws=ws, launch=launch))
+                                 for c in range(n_calls(nc))]
+                        try:
+                            calls[0]()
+                        except dg.DGError:   # does not fit this shape
+                            continue
+                        us, iqr = time_per_call(calls, reps=10)
+                        emit(record(f"gemv_q4_0_tiles {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M,
+                                    copies=nc, variant="tiles", RT=rt, KW=kw, D=d, KP=kp))
+        del Wts
+        torch.cuda.empty_cache()
 
 MFMA_BUILT_Q8 = {c: 24 for c in MFMA_SWEEP}
 
@@ -1227,8 +1279,10 @@ def main():
     ap.add_argument("--profile-small-m", action="store_true",
                     help="launch the small-batch Q4_0 GEMV eagerly on the decoder shapes (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
-                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q8,m1,fused,argmax,tail,nf4")
+                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q4tiles,q8,m1,fused,argmax,tail,nf4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="suite sections q4m and q4tiles: time the default launch only, not every configuration")
     ap.add_argument("--cpu-budget", type=float, default=16.0,
                     help="seconds of oracle work for cpu_baseline (half on one core, half on all)")
     args = ap.parse_args()

@@ -193,6 +193,59 @@ dg_status dg_gemv_q4_0_f32(const void* Wq, const float* x, float* Y, void* Xq,
                            int64_t N, int64_t K, int M, dg_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Q4_0 weights in 16-row tiles: the rearrangement, and the small-batch GEMV
+ * over it, M = 1..24 activation columns
+ *
+ *   Y = exactly the sums of dg_gemv_q4_0 (same blocks, same exact int32 block
+ *       sums and binary16 scale products), added in the order of this kernel
+ *
+ * The small-batch page ("The kernel that waited for itself", what remains
+ * open) ends at a floor set by the weight format, and the bitsandbytes issue
+ * on 4-bit decode (its analysis of the naive kernel) asks for a layout in
+ * which consecutive lanes read consecutive 128-bit chunks before unpacking.
+ * This is that layout for Q4_0: the same bytes as the row-major blocks,
+ * rearranged once (when the weights are loaded) so that each 16-byte load of
+ * a lane is directly the matrix-core operand of four blocks of one row.  For
+ * tile t (rows 16t..16t+15) and group s of 8 blocks, 2304 bytes at
+ * (t * K/256 + s) * 2304:
+ *   bytes    0..1023  16 bytes per lane l = 16g + n: dword j = code bytes
+ *                     4g..4g+3 of row 16t+n, block 8s+j;
+ *   bytes 1024..2047  the same for blocks 8s+4..8s+7;
+ *   bytes 2048..2303  16 bytes per row n: the binary16 scales of blocks
+ *                     8s..8s+7, block 8s+i in half i%2 of dword i/2.
+ * Rows past N (the last tile's padding) hold codes 0x88 and scale 0.
+ *
+ * dg_q4_0_tiles_bytes: bytes of the tiled copy, ceil(N/16) * K/256 * 2304
+ *   (0 for an invalid shape).
+ * dg_repack_q4_0_tiles: Wq (row-major Q4_0 as for dg_gemv_q4_0, 2-byte
+ *   aligned) -> Wt (device, dg_q4_0_tiles_bytes(N, K) bytes, 16-byte
+ *   aligned); K % 256 == 0, K <= 2^26, 0 <= N < 2^31.  Wq is unchanged.
+ * dg_gemv_q4_0_tiles: as dg_gemv_q4_0 with Wt in place of Wq.  Every
+ *   workgroup copies the activation columns of its range of K into LDS once;
+ *   when K is split over several workgroups of one row group (large K, or
+ *   too few row tiles for every CU), their partial sums meet in the caller's
+ *   workspace:
+ *   ws        device, ws_bytes >= dg_gemv_q4_0_tiles_workspace_bytes(N, K,
+ *             M) (0: ws may be NULL), 16-byte aligned.  Its first 64 KiB
+ *             hold ticket counters (one per row group, at the same place for
+ *             every shape), which must be zero before the first call: fill
+ *             the workspace with zeros once after allocating it.  Every call
+ *             leaves them zero again, so one workspace serves calls of any
+ *             shapes in turn; calls that may overlap in time need workspaces
+ *             of their own.
+ *   Partial sums are added in a fixed order (K parts within a workgroup,
+ *   then the workgroups' ranges in order of K): the result does not depend
+ *   on which workgroup finishes last.  K = 0 gives Y = 0.
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_WORKSPACE,
+ * DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+size_t dg_q4_0_tiles_bytes(int64_t N, int64_t K);
+dg_status dg_repack_q4_0_tiles(const void* Wq, void* Wt, int64_t N, int64_t K, dg_stream stream);
+size_t dg_gemv_q4_0_tiles_workspace_bytes(int64_t N, int64_t K, int M);
+dg_status dg_gemv_q4_0_tiles(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                             void* ws, size_t ws_bytes, dg_stream stream);
+
+/* ------------------------------------------------------------------------
  * Q8_0 weights x Q8_1 activations, M = 1..24 activation columns
  *
  *   Y[m][n] = sum_b dw(n,b) * d8(m,b) * sum_{j<32} qw(n,b,j) * q8(m,b,j)
@@ -474,6 +527,18 @@ dg_status dg_gemv_q8_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, i
                           int M, const dg_launch* cfg, dg_stream stream);
 dg_status dg_gemv_nf4_ex(const void* codes, const float* absmax, const float* table, const void* x, float* y,
                          int64_t N, int64_t K, int B, const dg_launch* cfg, dg_stream stream);
+/* dg_gemv_q4_0_tiles with a launch override: variant, grid and block 0;
+ * unroll = KP*1000000 + RT*10000 + KW*100 + D selects KP ranges of K per row
+ * group, RT row tiles and KW parts of the range per workgroup (RT*KW waves)
+ * and D groups of 8 blocks in flight per wave (built: (RT, KW, D) in (1,4,2),
+ * (1,4,4), (1,8,2), (1,8,4), (1,16,2), (2,4,2), (2,4,4), (2,2,4), (2,8,2),
+ * (4,1,4), (4,2,2), (4,2,4), (4,4,2), (4,4,4); KP 1..16).  The workspace
+ * this configuration needs is checked against ws_bytes (DG_ERR_WORKSPACE);
+ * a configuration not built or whose columns do not fit a workgroup's LDS
+ * gives DG_ERR_ARG. */
+dg_status dg_gemv_q4_0_tiles_ex(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                                void* ws, size_t ws_bytes, const dg_launch* cfg, dg_stream stream);
+
 /* dg_gemv_q4_0_f32 with a launch override: variant DG_VARIANT_Q4_LDSROW
  * selects the one-launch form (M = 1, K <= 16384), with its grid, block and
  * unroll (row buffers per wave, 2..4); 0 fields are defaults.  The default

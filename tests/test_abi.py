@@ -253,3 +253,54 @@ def test_gemv_q4_0_f32_rejects_before_launch(lib):
     assert f(A16, A16, A16, A16, 4, 250, 1, None) == 3            # K % 256
     assert f(A16, A16, A16, A16, 4, 256, 25, None) == 3           # M > 24
     assert f(None, None, None, None, 0, 256, 1, None) == 0        # empty: nothing launched
+
+
+def test_tiles_sizes(lib):
+    lib.dg_q4_0_tiles_bytes.restype = ctypes.c_size_t
+    lib.dg_q4_0_tiles_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    assert lib.dg_q4_0_tiles_bytes(16, 256) == 2304
+    assert lib.dg_q4_0_tiles_bytes(17, 512) == 2 * 2 * 2304
+    assert lib.dg_q4_0_tiles_bytes(4096, 14336) == 256 * 56 * 2304
+    assert lib.dg_q4_0_tiles_bytes(16, 100) == 0
+    assert lib.dg_q4_0_tiles_bytes(-1, 256) == 0
+    f = lib.dg_gemv_q4_0_tiles_workspace_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    assert f(4096, 14336, 16) > 0      # K split over workgroups
+    assert f(4096, 4000, 16) == 0      # invalid shape
+    assert f(4096, 14336, 25) == 0
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A16, A16, 4, 100), 3),              # K % 256
+    ((A16, A16, -1, 256), 3),
+    ((None, A16, 4, 256), 1),
+    ((A16, None, 4, 256), 1),
+    ((P(0x1001), A16, 4, 256), 2),        # Wq: 2-byte reads
+    ((A16, A2, 4, 256), 2),               # Wt must be 16-byte aligned
+    ((None, None, 0, 256), 0),            # N = 0
+    ((None, None, 4, 0), 0),              # K = 0
+])
+def test_repack_q4_0_tiles_rejects_before_launch(lib, args, expect):
+    assert lib.dg_repack_q4_0_tiles(*args, None) == expect
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((A16, A16, A16, 4, 100, 1, None, 0), 3),                 # K % 256
+    ((A16, A16, A16, 4, 256, 25, None, 0), 3),                # M > 24
+    ((A16, A16, A16, 4, (1 << 26) + 256, 1, None, 0), 3),
+    ((None, A16, A16, 4, 256, 1, None, 0), 1),
+    ((A16, None, A16, 4, 256, 1, None, 0), 1),
+    ((A16, A16, None, 4, 256, 1, None, 0), 1),
+    ((A2, A16, A16, 4, 256, 1, None, 0), 2),                  # Wt 16-byte aligned
+    ((A16, P(0x1004), A16, 4, 256, 1, None, 0), 2),           # Xq 16-byte aligned
+    ((A16, A16, A2, 4, 256, 1, None, 0), 2),                  # Y 4-byte aligned
+    ((A16, A16, A16, 4096, 14336, 16, A2, 1 << 24), 2),       # workspace 16-byte aligned
+    ((A16, A16, A16, 4096, 14336, 16, None, 0), 4),           # K split: workspace needed
+    ((A16, A16, A16, 4096, 14336, 16, A16, 64), 4),           # too small
+    ((None, None, None, 4, 256, 0, None, 0), 0),              # M = 0
+    ((None, None, None, 0, 256, 3, None, 0), 0),              # N = 0
+])
+def test_gemv_q4_0_tiles_rejects_before_launch(lib, args, expect):
+    lib.dg_gemv_q4_0_tiles.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, P, ctypes.c_size_t, P]
+    assert lib.dg_gemv_q4_0_tiles(*args, None) == expect
