@@ -839,7 +839,8 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
 # (RT, KW, D) configurations of the tiled Q4_0 kernel (dg_gemv_q4_0_tiles_ex:
 # unroll = KP*1000000 + RT*10000 + KW*100 + D)
 TILES_BUILT = [(1, 4, 2), (1, 4, 4), (1, 8, 2), (1, 8, 4), (1, 16, 2), (2, 4, 2), (2, 4, 4), (2, 2, 4), (2, 8, 2),
-               (4, 1, 4), (4, 2, 2), (4, 2, 4), (4, 4, 2), (4, 4, 4)]
+               (4, 1, 4), (4, 2, 2), (4, 2, 4), (4, 4, 2), (4, 4, 4),
+               (1, 8, 8), (2, 4, 8), (4, 2, 8), (1, 4, 8)]
 TILES_WS_BYTES = 40 << 20   # enough for every configuration of the four 8B shapes
 
 
@@ -869,7 +870,7 @@ def suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=True, shapes=None, ms=None)
             prev = cps
             emit(record(f"gemv_q4_0_tiles {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M, copies=nc,
                         variant="default", columns_per_s=round(cps, 1), change_vs_prev_M=dip))
-            if sweep and M in (1, 4, 8, 16, 17, 24):
+            if sweep and M in (1, 8, 16, 24):
                 for (rt, kw, d) in TILES_BUILT:
                     for kp in (1, 2, 4):
                         launch = dict(unroll=kp * 1000000 + rt * 10000 + kw * 100 + d)
@@ -1265,6 +1266,30 @@ def profile_small_m(args):
         torch.cuda.empty_cache()
 
 
+def profile_small_m_tiles(args):
+    """As --profile-small-m, for dg_gemv_q4_0_tiles (the weights rearranged
+    into 16-row tiles before the launches)."""
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    ws = torch.zeros(TILES_WS_BYTES, dtype=torch.uint8, device="cuda")
+    for (N, K) in SMALL_M_CASES:
+        Wts = []
+        for Wq in q4_copies(1, N, K, 2):
+            Wt = torch.empty(dg.dg_q4_0_tiles_bytes(N, K), dtype=torch.uint8, device="cuda")
+            dg.dg_repack_q4_0_tiles(Wq, Wt, N, K)
+            Wts.append(Wt)
+        for M in SMALL_M_COLUMNS:
+            Xq = q8_columns(1, K, M)
+            Y = torch.empty(M * N, dtype=torch.float32, device="cuda")
+            torch.cuda.synchronize()
+            for i in range(4):
+                dg.dg_gemv_q4_0_tiles(Wts[i % 2], Xq, Y, N, K, M, ws=ws)
+            torch.cuda.synchronize()
+            log(f"[profile-small-m-tiles] {N}x{K} M={M}: 4 launches")
+        del Wts
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -1276,6 +1301,8 @@ def main():
                     help="launch each profiled kernel eagerly on known workloads (for rocprofv3 --pmc)")
     ap.add_argument("--profile-launch-cost", action="store_true",
                     help="graphs of back-to-back launches for a kernel-trace split of the per-launch cost")
+    ap.add_argument("--profile-small-m-tiles", action="store_true",
+                    help="launch the tiled small-batch Q4_0 GEMV eagerly (for rocprofv3 --pmc)")
     ap.add_argument("--profile-small-m", action="store_true",
                     help="launch the small-batch Q4_0 GEMV eagerly on the decoder shapes (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
@@ -1299,6 +1326,8 @@ def main():
         profile_kernels(args)
     elif args.profile_small_m:
         profile_small_m(args)
+    elif args.profile_small_m_tiles:
+        profile_small_m_tiles(args)
     elif args.profile_launch_cost:
         profile_launch_cost(args)
     elif args.suite:

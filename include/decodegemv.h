@@ -196,24 +196,25 @@ dg_status dg_gemv_q4_0_f32(const void* Wq, const float* x, float* Y, void* Xq,
  * Q4_0 weights in 16-row tiles: the rearrangement, and the small-batch GEMV
  * over it, M = 1..24 activation columns
  *
- *   Y = exactly the sums of dg_gemv_q4_0 (same blocks, same exact int32 block
- *       sums and binary16 scale products), added in the order of this kernel
+ *   Y = the sums of dg_gemv_q4_0 (the same exact int32 block sums and exact
+ *       binary16 scale products), added in the order of this kernel
  *
  * The small-batch page ("The kernel that waited for itself", what remains
  * open) ends at a floor set by the weight format, and the bitsandbytes issue
  * on 4-bit decode (its analysis of the naive kernel) asks for a layout in
  * which consecutive lanes read consecutive 128-bit chunks before unpacking.
- * This is that layout for Q4_0: the same bytes as the row-major blocks,
- * rearranged once (when the weights are loaded) so that each 16-byte load of
- * a lane is directly the matrix-core operand of four blocks of one row.  For
- * tile t (rows 16t..16t+15) and group s of 8 blocks, 2304 bytes at
- * (t * K/256 + s) * 2304:
+ * This is that layout for Q4_0: the information of the row-major blocks byte
+ * for byte, rearranged once (when the weights are loaded) so that each
+ * 16-byte load of a lane is directly the matrix-core operand of four blocks
+ * of one row.  Scales are copied unchanged; each 4-bit code q is stored as q
+ * XOR 8 (the two's-complement nibble of q - 8).  For tile t (rows
+ * 16t..16t+15) and group s of 8 blocks, 2304 bytes at (t * K/256 + s) * 2304:
  *   bytes    0..1023  16 bytes per lane l = 16g + n: dword j = code bytes
- *                     4g..4g+3 of row 16t+n, block 8s+j;
+ *                     4g..4g+3 of row 16t+n, block 8s+j (nibbles XOR 8);
  *   bytes 1024..2047  the same for blocks 8s+4..8s+7;
  *   bytes 2048..2303  16 bytes per row n: the binary16 scales of blocks
  *                     8s..8s+7, block 8s+i in half i%2 of dword i/2.
- * Rows past N (the last tile's padding) hold codes 0x88 and scale 0.
+ * Rows past N (the last tile's padding) hold code nibbles 0 and scale 0.
  *
  * dg_q4_0_tiles_bytes: bytes of the tiled copy, ceil(N/16) * K/256 * 2304
  *   (0 for an invalid shape).
@@ -531,8 +532,9 @@ dg_status dg_gemv_nf4_ex(const void* codes, const float* absmax, const float* ta
  * unroll = KP*1000000 + RT*10000 + KW*100 + D selects KP ranges of K per row
  * group, RT row tiles and KW parts of the range per workgroup (RT*KW waves)
  * and D groups of 8 blocks in flight per wave (built: (RT, KW, D) in (1,4,2),
- * (1,4,4), (1,8,2), (1,8,4), (1,16,2), (2,4,2), (2,4,4), (2,2,4), (2,8,2),
- * (4,1,4), (4,2,2), (4,2,4), (4,4,2), (4,4,4); KP 1..16).  The workspace
+ * (1,4,4), (1,4,8), (1,8,2), (1,8,4), (1,8,8), (1,16,2), (2,4,2), (2,4,4),
+ * (2,4,8), (2,2,4), (2,8,2), (4,1,4), (4,2,2), (4,2,4), (4,2,8), (4,4,2),
+ * (4,4,4); KP 1..16).  The workspace
  * this configuration needs is checked against ws_bytes (DG_ERR_WORKSPACE);
  * a configuration not built or whose columns do not fit a workgroup's LDS
  * gives DG_ERR_ARG. */

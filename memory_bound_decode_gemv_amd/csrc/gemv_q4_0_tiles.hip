@@ -10,27 +10,29 @@
 // floor) names a different weight format as the next step, and the
 // bitsandbytes issue on 4-bit decode (its analysis of the naive kernel) asks
 // for a layout in which consecutive lanes read consecutive 128-bit chunks
-// before unpacking.  The tiled layout holds the same bytes (every block's
-// binary16 scale and its 16 code bytes, untouched), ordered so that one
-// 16-byte load per lane IS the B operand of four consecutive blocks:
+// before unpacking.  The tiled layout holds the blocks' information byte for
+// byte (every binary16 scale untouched; every 4-bit code q stored as q XOR 8,
+// the two's-complement nibble of q - 8), ordered so that one 16-byte load
+// per lane IS the B operand of four consecutive blocks:
 //
 //   tile t (rows 16t..16t+15) x group s (blocks 8s..8s+7): 2304 bytes at
 //   (t * K/256 + s) * 2304:
 //     bytes    0..1023: lane l (l = 16g + n) holds, in dword j, code bytes
-//                       4g..4g+3 of row 16t+n, block 8s+j;
+//                       4g..4g+3 of row 16t+n, block 8s+j (nibbles XOR 8);
 //     bytes 1024..2047: the same for blocks 8s+4..8s+7;
 //     bytes 2048..2303: row n's eight binary16 scales (blocks 8s..8s+7) at
 //                       2048 + 16n, block 8s+i in half i%2 of dword i/2.
-//   Rows past N (the last tile's padding) hold codes 0x88 and scale 0, so
-//   they add exact zeros.
+//   Rows past N (the last tile's padding) hold code nibbles 0 (q - 8 = 0)
+//   and scale 0, so they add exact zeros.
 //
-// The matrix-core arithmetic is that of the row-major kernels: per block, one
-// v_mfma_i32_16x16x32_i8 of the 16 columns' q8 codes against the 16 rows'
-// 4-bit codes, a second against the constant -8 (the offset of q - 8), and
-// the d8 * d4 products from one v_mfma_f32_16x16x16_f16 (exact in fp32); the
-// int32 block sums are converted and scaled in fp32.  Lane group g carries
-// k-slots 4g..4g+3 (low nibbles of code dword g) and 16+4g..16+4g+3 (high
-// nibbles), with the matching activation code dwords g and 4 + g.
+// The matrix-core arithmetic keeps the exact integer block sums of the
+// row-major kernels: per block, one v_mfma_i32_16x16x32_i8 of the 16
+// columns' q8 codes against 16 (q - 8) of the 16 rows (the signed nibbles
+// masked in place, no offset term), and the d8 * d4 products from one
+// v_mfma_f32_16x16x16_f16 (exact in fp32); the int32 block sums are
+// converted and scaled in fp32.  Lane group g carries k-slots 4g..4g+3 (low
+// nibbles of code dword g) and 16+4g..16+4g+3 (high nibbles), with the
+// matching activation code dwords g and 4 + g.
 //
 // Data flow.  A workgroup of RT x KW waves covers RT row tiles over one range
 // of K (KP ranges per row group, one per workgroup); wave (rt, kw) streams
@@ -61,6 +63,8 @@ constexpr int kGroupBlocks = 8;      // blocks per group of a tile
 constexpr int kGroupBytes = 2304;    // 16 rows x 8 blocks x 18 bytes
 constexpr int kCodeBytes = 2048;     // the group's code bytes; 256 bytes of scales follow
 constexpr int kGroupSlots = 18;      // 16-byte slots of one column's Q8_1 blocks per group (8 x 36 / 16)
+constexpr uint32_t kHiNib = 0xF0F0F0F0u;
+constexpr float kUnscale = 1.0f / 64.0f;   // the products gather 16 x 4 times each sum
 
 // ---------------------------------------------------------------------------
 // Rearrangement: one thread per 16-byte slot of the tiled layout (144 per
@@ -84,9 +88,9 @@ k_q4_tiles_pack(const uint8_t* __restrict__ Wq, uint8_t* __restrict__ Wt, int N,
             if (row < N) {
                 const uint16_t* p = reinterpret_cast<const uint16_t*>(
                     Wq + (size_t)row * row_bytes + (size_t)(kGroupBlocks * s + 4 * h + j) * 18 + 2 + 4 * g);
-                d[j] = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
+                d[j] = ((uint32_t)p[0] | ((uint32_t)p[1] << 16)) ^ 0x88888888u;   // q -> q - 8, signed nibbles
             } else {
-                d[j] = 0x88888888u;
+                d[j] = 0u;   // padding rows: q - 8 = 0
             }
         }
     } else {
@@ -114,85 +118,148 @@ __device__ __forceinline__ void load_group(const uint8_t* __restrict__ g0, int l
     w[2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g0 + kCodeBytes + rn * 16));
 }
 
+// Column tiles of a launch with MP padded columns: a full tile of 16 columns
+// (MP >= 16) and a pair tile of 8 columns from c0 = MP - 8 (MP = 8 or 24).
+// The pair tile computes two blocks per matrix-core instruction: a
+// v_mfma_i32_16x16x64_i8 (as fast as the 32-deep one on gfx950) whose 64
+// k-slots hold both blocks, A rows 0..7 carrying the 8 columns' codes of the
+// first block (zeros in the second block's k-slots, read from a zero column
+// in LDS) and rows 8..15 those of the second: output row m' is the block sum
+// of column c0 + m' % 8 and block i + m' / 8.  Per output that is half the
+// instructions of a 16-column tile with eight columns unused.
+template <int MP>
+struct TileSet {
+    static constexpr int kFull = MP >= 16 ? 1 : 0;
+    static constexpr int kPair = (MP == 8 || MP == 24) ? 1 : 0;
+    // f32x4 accumulators per lane: the full tile's even and odd blocks apart
+    // (so that every column is summed in the same order as the pair tile's:
+    // even blocks, odd blocks, then the two sums), then the pair tile's
+    static constexpr int kNA = 2 * kFull + kPair;
+    static constexpr int kPairAcc = 2 * kFull;
+    static constexpr int kC0 = MP - 8;          // first column of the pair tile
+};
+
+// Per-lane LDS byte offsets of the A operands within the column copy.
+struct ALanes {
+    uint32_t full;   // the full tile: column rn
+    uint32_t p01;    // pair tile, first block's k-slots: column c0 + rn (rn < 8), else the zero column
+    uint32_t p23;    // pair tile, second block's k-slots: column c0 + rn - 8 (rn >= 8), else the zero column
+    uint32_t ps;     // pair tile, d8: this row's column, one block further for rn >= 8
+    uint32_t sel;    // byte selector: that d8 into the low (rn < 8) or high half of a dword
+};
+
+// One group of 8 blocks: operands, matrix-core products, fp32 scaling into
+// acc, which gathers 64 times the sums (divided out at the store):
+//  * B (weights): the tiled codes are signed nibbles (q - 8), so masking the
+//    high nibbles of a code dword, and of the dword shifted left by 4, gives
+//    16 (q - 8) as int8 for the lane's 8 k-slots: one MFMA per block (per
+//    two blocks in the pair tile) gives 16 times the exact block sums (|16
+//    S| < 2^20), with no offset term;
+//  * the scale products come from one v_mfma_f32_16x16x16_f16 per block (per
+//    two blocks in the pair tile) in which B is the lane's raw pair of scale
+//    dwords (the d4 of four blocks, one per k-slot, repeated in all four lane
+//    groups) and A carries each output row's d8 at the k-slot of its block
+//    in every lane group, zeros elsewhere: each output is 4 d8 d4, exact in
+//    fp32 (binary16 products are exact, and so are sums of four equal ones).
+// blk is the group's first block within the LDS copy of the columns.
+template <int MP>
+__device__ __forceinline__ void tiles_group(const u32x4 (&w)[3], const uint8_t* lds, const ALanes& al, uint32_t blk,
+                                            int g, f32x4 (&acc)[TileSet<MP>::kNA]) {
+    using TS = TileSet<MP>;
+    const uint32_t code[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
+    const f16x4 d4q[2] = {__builtin_bit_cast(f16x4, u32x2{w[2].x, w[2].y}),    // blocks 0..3
+                          __builtin_bit_cast(f16x4, u32x2{w[2].z, w[2].w})};   // blocks 4..7
+    uint32_t blo[8], bhi[8];   // B operand dwords: 16 (q - 8) of the lane's low and high k-slots
+#pragma unroll
+    for (int i = 0; i < kGroupBlocks; ++i) {
+        blo[i] = (code[i] << 4) & kHiNib;
+        bhi[i] = code[i] & kHiNib;
+    }
+    if constexpr (TS::kFull) {
+#pragma unroll
+        for (int i = 0; i < kGroupBlocks; ++i) {
+            const uint32_t* ab = reinterpret_cast<const uint32_t*>(lds + al.full + (blk + i) * kQ81Bytes);
+            const long aop = (long)((uint64_t)ab[1 + g] | ((uint64_t)ab[5 + g] << 32));
+            const long bop = (long)((uint64_t)blo[i] | ((uint64_t)bhi[i] << 32));
+            const uint32_t h = (i & 1) ? ab[0] << 16 : ab[0] & 0xFFFFu;   // d8, in the half of k-slot i % 4
+            const f16x4 a8 = __builtin_bit_cast(f16x4, (i & 2) ? u32x2{0u, h} : u32x2{h, 0u});
+            const i32x4 dsum = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop, bop, i32x4{0, 0, 0, 0}, 0, 0, 0);
+            const f32x4 sc = __builtin_amdgcn_mfma_f32_16x16x16f16(a8, d4q[i >> 2], f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                   0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i & 1][r] = fmaf((float)dsum[r], sc[r], acc[i & 1][r]);
+        }
+    }
+    if constexpr (TS::kPair) {
+#pragma unroll
+        for (int i = 0; i < kGroupBlocks; i += 2) {
+            const uint32_t* x01 = reinterpret_cast<const uint32_t*>(lds + al.p01 + (blk + i) * kQ81Bytes);
+            const uint32_t* x23 = reinterpret_cast<const uint32_t*>(lds + al.p23 + (blk + i + 1) * kQ81Bytes);
+            const i32x4 aop = {(int)x01[1 + g], (int)x01[5 + g], (int)x23[1 + g], (int)x23[5 + g]};
+            const i32x4 bop = {(int)blo[i], (int)bhi[i], (int)blo[i + 1], (int)bhi[i + 1]};
+            const uint32_t d8 = *reinterpret_cast<const uint32_t*>(lds + al.ps + (blk + i) * kQ81Bytes);
+            const uint32_t h = __builtin_amdgcn_perm(0u, d8, al.sel);   // k-slot i % 4 + (row >= 8)
+            const f16x4 a8 = __builtin_bit_cast(f16x4, (i & 2) ? u32x2{0u, h} : u32x2{h, 0u});
+            const i32x4 dsum = __builtin_amdgcn_mfma_i32_16x16x64_i8(aop, bop, i32x4{0, 0, 0, 0}, 0, 0, 0);
+            const f32x4 sc = __builtin_amdgcn_mfma_f32_16x16x16f16(a8, d4q[i >> 2], f32x4{0.0f, 0.0f, 0.0f, 0.0f},
+                                                                   0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[TS::kPairAcc][r] = fmaf((float)dsum[r], sc[r], acc[TS::kPairAcc][r]);
+        }
+    }
+}
+
 // Marks a group's registers as written here (an empty asm): arithmetic on
 // them cannot move above this point, and its loads are waited for here.
 __device__ __forceinline__ void bind_group(u32x4 (&w)[3]) {
     asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2])::"memory");
 }
 
-template <int NT>
-__device__ __forceinline__ void store_tile(const f32x4 (&acc)[NT], float* __restrict__ Y, int N, int M, int t,
-                                           int g, int rn) {
+// Stores the tile's outputs (unscaled).  The full tile adds its even- and
+// odd-block sums; the pair tile's sit in lane groups g and g + 2 (output rows
+// m' and m' + 8).  All 64 lanes of the wave call this.
+template <int MP>
+__device__ __forceinline__ void store_tile(const f32x4 (&acc)[TileSet<MP>::kNA], float* __restrict__ Y, int N, int M,
+                                           int t, int g, int rn) {
+    using TS = TileSet<MP>;
     const int n = t * 16 + rn;
-    if (n >= N) return;
+    f32x4 pr = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (TS::kPair) {
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
+        for (int r = 0; r < 4; ++r) pr[r] = acc[TS::kPairAcc][r] + __shfl_xor(acc[TS::kPairAcc][r], 32);
+    }
+    if (n >= N) return;
+    if constexpr (TS::kFull) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int m = tt * 16 + g * 4 + r;
-            if (m < M) Y[(size_t)m * N + n] = acc[tt][r];
+            const int m = g * 4 + r;
+            if (m < M) Y[(size_t)m * N + n] = (acc[0][r] + acc[1][r]) * kUnscale;
         }
-}
-
-// One group of 8 blocks: operands, matrix-core products, fp32 scaling into
-// acc.  blk is the group's first block within the LDS copy of the columns;
-// width is 16 in lane group 0 (it feeds d4 to k-slot 0 of the scale
-// products), 0 elsewhere and for a group that must add exact zeros.
-template <int NT, int GB>
-__device__ __forceinline__ void tiles_group(const u32x4 (&w)[3], const uint8_t* lds, const uint32_t (&acol)[NT],
-                                            uint32_t blk, int g, uint32_t width, f32x4 (&acc)[NT]) {
-    const uint32_t code[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
-    const uint32_t scl[4] = {w[2].x, w[2].y, w[2].z, w[2].w};
+    }
+    if constexpr (TS::kPair) {
+        if (g < 2) {
 #pragma unroll
-    for (int o = 0; o < kGroupBlocks; o += GB) {
-        long bop[GB];
-        uint32_t h4[GB];
-#pragma unroll
-        for (int b = 0; b < GB; ++b) {
-            const uint32_t c = code[o + b];
-            bop[b] = (long)((uint64_t)(c & kNib) | ((uint64_t)((c >> 4) & kNib) << 32));
-            h4[b] = __builtin_amdgcn_ubfe(scl[(o + b) >> 1], ((o + b) & 1) * 16, width);
-        }
-#pragma unroll
-        for (int tt = 0; tt < NT; ++tt) {
-            long aop[GB];
-            uint32_t a8[GB];
-#pragma unroll
-            for (int b = 0; b < GB; ++b) {
-                const uint32_t* ab = reinterpret_cast<const uint32_t*>(lds + acol[tt] + (blk + o + b) * kQ81Bytes);
-                aop[b] = (long)((uint64_t)ab[1 + g] | ((uint64_t)ab[5 + g] << 32));
-                a8[b] = ab[0] & 0xFFFFu;
+            for (int r = 0; r < 4; ++r) {
+                const int m = TS::kC0 + g * 4 + r;
+                if (m < M) Y[(size_t)m * N + n] = pr[r] * kUnscale;
             }
-            i32x4 dsum[GB];
-#pragma unroll
-            for (int b = 0; b < GB; ++b)
-                dsum[b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[b], kNeg8, i32x4{0, 0, 0, 0}, 0, 0, 0);
-#pragma unroll
-            for (int b = 0; b < GB; ++b)
-                dsum[b] = __builtin_amdgcn_mfma_i32_16x16x32_i8(aop[b], bop[b], dsum[b], 0, 0, 0);
-            f32x4 sc[GB];
-#pragma unroll
-            for (int b = 0; b < GB; ++b) sc[b] = scale_outer(a8[b], h4[b]);
-#pragma unroll
-            for (int b = 0; b < GB; ++b)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[tt][r] = fmaf((float)dsum[b][r], sc[b][r], acc[tt][r]);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// The GEMV.  MP = 16 (M <= 16) or 32 (17..24 columns: two 16-column tiles,
-// the second one's rows past M re-reading column M - 1, results dropped).
+// The GEMV.  MP = 8 (M <= 8: one pair tile), 16 (one full tile) or 24 (a
+// full tile and a pair tile); columns past M re-read column M - 1, their
+// results dropped.
 // ---------------------------------------------------------------------------
 template <int MP, int RT, int KW, int D>
 __global__ void __launch_bounds__(64 * RT * KW)
 k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
            uint32_t* __restrict__ tickets, f32x4* __restrict__ part, int N, int K, int M, int KP, int spw,
            int cs_slots, uint32_t cs_magic) {
-    constexpr int NT = MP / 16;
+    using TS = TileSet<MP>;
+    constexpr int NA = TS::kNA;
     constexpr int W = RT * KW;
-    constexpr int GB = 2;   // blocks per operand batch
     extern __shared__ u32x4 tiles_lds[];
     __shared__ int last_ticket;
     uint8_t* const lds = reinterpret_cast<uint8_t*>(tiles_lds);
@@ -215,11 +282,14 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
     const uint8_t* const wbase = Wt + ((size_t)tc * S + s0 + (cnt > 0 ? w0 : 0)) * kGroupBytes;
     const int last = cnt > 0 ? cnt - 1 : 0;
 
-    // (1) the first D groups of this wave's weights (past its part: its last
-    // group again, never used), then (2) the activation columns of the range
-    u32x4 wb[D][3];
-#pragma unroll
-    for (int d = 0; d < D; ++d) load_group(wbase + (size_t)(d < cnt ? d : last) * kGroupBytes, lane, rn, wb[d]);
+    // (1) the activation columns of the range, copied into LDS by DMA, then
+    // (2) the first D groups of this wave's weights (past its part: its last
+    // group again, never used), both in flight together; then a wait for all
+    // of them.  The wait is the builtin (not inline asm) and waits for
+    // everything: only then does the compiler's own wait counting know that
+    // no copy into LDS is outstanding.  With copies possibly outstanding it
+    // treats the counter as out of order and waits for every load before
+    // each use (measured: vmcnt(0) at the top of every round of the loop).
     {
         const int used = ns * kGroupSlots;
         const int copies = (M * cs_slots + kWave - 1) / kWave;
@@ -232,27 +302,34 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
             const uint8_t* src = xr + (ok ? (size_t)m * nblk * kQ81Bytes + (size_t)c * 16 : 0);
             __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(lds + j * 1024), 16, 0, 0);
         }
+        if constexpr (TS::kPair) {   // the zero column after the copies (its used slots)
+            u32x4* const z = reinterpret_cast<u32x4*>(lds + copies * 1024);
+            for (int e = wave * kWave + lane; e < used; e += W * kWave) z[e] = u32x4{0u, 0u, 0u, 0u};
+        }
     }
-    // This wave's copies (and first weights) have landed, then every other
-    // wave's.  The wait is the builtin, not inline asm, so that the compiler's
-    // own wait counting knows nothing is outstanding past this point (after
-    // an asm wait it assumed the copies pending and waited for every load at
-    // the top of each round).
+    u32x4 wb[D][3];
+#pragma unroll
+    for (int d = 0; d < D; ++d) load_group(wbase + (size_t)(d < cnt ? d : last) * kGroupBytes, lane, rn, wb[d]);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt at their maximum: no wait
-    lds_barrier();
+    lds_barrier();   // every other wave's copies have landed too
 
-    // A operand addresses: column 16 tt + rn of each 16-column tile (past M:
-    // column M - 1 again, results dropped)
-    uint32_t acol[NT];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt) {
-        const int m = 16 * tt + rn < M ? 16 * tt + rn : M - 1;
-        acol[tt] = (uint32_t)m * (uint32_t)cs_slots * 16u;
+    // A operand offsets (columns past M: column M - 1 again, results dropped)
+    ALanes al;
+    {
+        const uint32_t stride = (uint32_t)cs_slots * 16u;
+        const uint32_t zero = (uint32_t)((M * cs_slots + kWave - 1) / kWave) * 1024u;   // the zero column
+        al.full = (uint32_t)(rn < M ? rn : M - 1) * stride;
+        const int c = TS::kC0 + (rn & 7);
+        const uint32_t pc = (uint32_t)(c < M ? c : M - 1) * stride;
+        const bool hi = rn >= 8;
+        al.p01 = hi ? zero : pc;
+        al.p23 = hi ? pc : zero;
+        al.ps = pc + (hi ? (uint32_t)kQ81Bytes : 0u);
+        al.sel = hi ? 0x01000C0Cu : 0x0C0C0100u;
     }
-    const uint32_t dwidth = g == 0 ? 16u : 0u;   // lane group 0 feeds d4 to k-slot 0 of the scale products
-    f32x4 acc[NT];
+    f32x4 acc[NA];
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt) acc[tt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int a = 0; a < NA; ++a) acc[a] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // D groups per round; the loads of the next round are issued right after
     // each group's products, with no branch between them, so the compiler's
@@ -263,7 +340,7 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int i = rd * D + d;
-            tiles_group<NT, GB>(wb[d], lds, acol, (uint32_t)(w0 + i) * kGroupBlocks, g, dwidth, acc);
+            tiles_group<MP>(wb[d], lds, al, (uint32_t)(w0 + i) * kGroupBlocks, g, acc);
             const int nx = i + D;
             load_group(wbase + (size_t)(nx < cnt ? nx : last) * kGroupBytes, lane, rn, wb[d]);
             // Keep the loads here and the next group's arithmetic behind them:
@@ -279,9 +356,8 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
         for (int d = 0; d < D; ++d) {
             const int i = (rounds - 1) * D + d;
             if (d > 0) bind_group(wb[d]);
-            const bool valid = i < cnt;   // past the part: the last group again, adding zeros
-            tiles_group<NT, GB>(wb[d], lds, acol, (uint32_t)(w0 + (valid ? i : last)) * kGroupBlocks, g,
-                                valid ? dwidth : 0u, acc);
+            if (i < cnt)   // wave-uniform; no loads follow, so the branch costs no wait
+                tiles_group<MP>(wb[d], lds, al, (uint32_t)(w0 + i) * kGroupBlocks, g, acc);
         }
     }
 
@@ -291,21 +367,21 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
         f32x4* red = reinterpret_cast<f32x4*>(lds);
         if (kw > 0) {
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) red[(wave * NT + tt) * kWave + lane] = acc[tt];
+            for (int a = 0; a < NA; ++a) red[(wave * NA + a) * kWave + lane] = acc[a];
         }
         lds_barrier();
         if (kw == 0) {
             for (int k2 = 1; k2 < KW; ++k2)
 #pragma unroll
-                for (int tt = 0; tt < NT; ++tt) {
-                    const f32x4 v = red[((wave + k2) * NT + tt) * kWave + lane];
+                for (int a = 0; a < NA; ++a) {
+                    const f32x4 v = red[((wave + k2) * NA + a) * kWave + lane];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[tt][r] += v[r];
+                    for (int r = 0; r < 4; ++r) acc[a][r] += v[r];
                 }
         }
     }
     if (KP == 1) {
-        if (kw == 0 && t < T) store_tile<NT>(acc, Y, N, M, t, g, rn);
+        if (kw == 0 && t < T) store_tile<MP>(acc, Y, N, M, t, g, rn);
         return;
     }
 
@@ -317,13 +393,13 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
     // Agent-scope release and acquire fences (an L2 write-back and an L2
     // invalidate on this chip, both of whole caches) measured 15-140 us per
     // call, and are not needed when every shared access is atomic.
-    float* const mine = reinterpret_cast<float*>(part + (((size_t)grp * KP + kp) * RT + rt) * NT * kWave);
+    float* const mine = reinterpret_cast<float*>(part + (((size_t)grp * KP + kp) * RT + rt) * NA * kWave);
     if (kw == 0) {
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
+        for (int a = 0; a < NA; ++a)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                __hip_atomic_store(mine + (tt * kWave + lane) * 4 + r, acc[tt][r], __ATOMIC_RELAXED,
+                __hip_atomic_store(mine + (a * kWave + lane) * 4 + r, acc[a][r], __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's partial sums are stored
@@ -334,30 +410,33 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
     __syncthreads();
     if (!last_ticket) return;   // workgroup-uniform
     if (kw == 0 && t < T) {
-        f32x4 sum[NT];
+        f32x4 sum[NA];
         for (int k2 = 0; k2 < KP; ++k2) {
             const float* const src =
-                reinterpret_cast<const float*>(part + (((size_t)grp * KP + k2) * RT + rt) * NT * kWave);
+                reinterpret_cast<const float*>(part + (((size_t)grp * KP + k2) * RT + rt) * NA * kWave);
 #pragma unroll
-            for (int tt = 0; tt < NT; ++tt) {
-                f32x4 v = acc[tt];
+            for (int a = 0; a < NA; ++a) {
+                f32x4 v = acc[a];
                 if (k2 != kp) {
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        v[r] = __hip_atomic_load(src + (tt * kWave + lane) * 4 + r, __ATOMIC_RELAXED,
+                        v[r] = __hip_atomic_load(src + (a * kWave + lane) * 4 + r, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
                 }
-                if (k2 == 0) sum[tt] = v;
+                if (k2 == 0) sum[a] = v;
                 else {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) sum[tt][r] += v[r];
+                    for (int r = 0; r < 4; ++r) sum[a][r] += v[r];
                 }
             }
         }
-        store_tile<NT>(sum, Y, N, M, t, g, rn);
+        store_tile<MP>(sum, Y, N, M, t, g, rn);
     }
     if (threadIdx.x == 0) __hip_atomic_store(tickets + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// f32x4 accumulators per lane for M columns (TileSet<MP>::kNA).
+int tiles_accumulators(int M) { return M <= 8 ? 1 : M <= 16 ? 2 : 3; }
 
 // A resolved configuration of the tiled kernel.
 struct TilesPlan {
@@ -380,7 +459,8 @@ constexpr size_t kTilesMaxLds = 160 * 1024 - 256;   // a gfx950 workgroup's LDS,
 // The built (RT, KW, D) configurations (launch_tiles_mp lists the same).
 bool tiles_built(int RT, int KW, int D) {
     static const int kBuilt[][3] = {{1, 4, 2}, {1, 4, 4}, {1, 8, 2}, {1, 8, 4}, {1, 16, 2}, {2, 4, 2}, {2, 4, 4},
-                                    {2, 2, 4}, {2, 8, 2}, {4, 1, 4}, {4, 2, 2}, {4, 2, 4}, {4, 4, 2}, {4, 4, 4}};
+                                    {2, 2, 4}, {2, 8, 2}, {4, 1, 4}, {4, 2, 2}, {4, 2, 4}, {4, 4, 2}, {4, 4, 4},
+                                    {1, 8, 8}, {2, 4, 8}, {4, 2, 8}, {1, 4, 8}};
     for (const auto& c : kBuilt)
         if (c[0] == RT && c[1] == KW && c[2] == D) return true;
     return false;
@@ -395,9 +475,10 @@ bool tiles_plan(int N, int K, int M, int RT, int KW, int D, int KP, TilesPlan& p
     p.spw = (S + KP - 1) / KP;
     p.KP = (S + p.spw - 1) / p.spw;   // no empty range
     p.cs_slots = kGroupSlots * p.spw + 1;
-    const int NT = M > 16 ? 2 : 1;
-    const size_t act = (size_t)((M * p.cs_slots + kWave - 1) / kWave) * 1024;
-    const size_t red = (size_t)RT * KW * NT * kWave * 16;
+    const int NA = tiles_accumulators(M);
+    const bool pair = M <= 8 || M > 16;
+    const size_t act = (size_t)((M * p.cs_slots + kWave - 1) / kWave) * 1024 + (pair ? (size_t)p.cs_slots * 16 : 0);
+    const size_t red = (size_t)RT * KW * NA * kWave * 16;
     p.lds = act > red ? act : red;
     p.groups = ((N + 15) / 16 + RT - 1) / RT;
     if (p.KP > 1 && p.groups > kTicketSlots) return false;   // one ticket counter per row group
@@ -407,16 +488,17 @@ bool tiles_plan(int N, int K, int M, int RT, int KW, int D, int KP, TilesPlan& p
 }
 
 // Default configuration, from a sweep of every built configuration on MI355X
-// over the four decoder-layer shapes at M = 1, 4, 8, 16, 17, 24 (K split 1, 2
-// or 4 ways).  K is split over workgroups only when the columns of a whole
-// row would not fit a workgroup's LDS (the ticket exchange costs 1.5-2.5 us
-// per call): then the ranges are as long as fit, and four row tiles per
-// workgroup keep the workgroup count near the CU count.  Otherwise one row
-// tile per workgroup (four from 512 row tiles on, which shares each column
-// copy between them), with K split over 8 waves, or over 4 waves for K <=
-// 4096 up to 16 columns on 256..511 row tiles; two groups in flight per wave.
-// Measured (us): 4096x4096 M = 16 / 24 5.60 / 7.17; 14336x4096 9.62 / 14.19;
-// 1024x4096 4.78 / 6.29; 4096x14336 M = 8 / 16 / 24 10.61 / 12.21 / 18.25.
+// over the four decoder-layer shapes at M = 1, 8, 16, 24 (K split 1, 2 or 4
+// ways).  K is split over workgroups only when the columns of a whole row
+// would not fit a workgroup's LDS (the ticket exchange costs 1.5-2.5 us per
+// call): then the ranges are as long as fit, with two row tiles per
+// workgroup over 4 waves each for two ranges and four tiles over 2 waves for
+// more.  Otherwise: from 512 row tiles on, two row tiles per workgroup (four
+// beyond 8 columns, sharing each column copy between more rows) over K in 4
+// parts; below, one row tile over K in 8 parts.  Two groups in flight per
+// wave.  Measured (us, M = 1 / 8 / 16 / 24): 4096x4096 4.51 / 4.91 / 5.72 /
+// 6.92; 14336x4096 7.37 / 8.64 / 9.73 / 11.72; 1024x4096 3.88 / 4.29 / 5.02 /
+// 6.28; 4096x14336 8.41 / 9.53 / 11.86 / 17.08.
 void tiles_default(int N, int K, int M, int& RT, int& KW, int& D, int& KP) {
     const int T = (N + 15) / 16;
     const int S = K >> 8;
@@ -426,13 +508,13 @@ void tiles_default(int N, int K, int M, int& RT, int& KW, int& D, int& KP) {
     while (KP < kTilesMaxKP && KP < S && (size_t)M * ((S + KP - 1) / KP) * kGroupSlots * 16 > fit) KP *= 2;
     if (KP > 1) {
         RT = KP >= 4 ? 4 : 2;
-        KW = 4;
+        KW = KP >= 4 ? 2 : 4;
     } else if (T >= 512) {
-        RT = 4;
-        KW = 2;
+        RT = M <= 8 ? 2 : 4;
+        KW = 4;
     } else {
         RT = 1;
-        KW = (K <= 4096 && M <= 16 && T >= 256) ? 4 : 8;
+        KW = 8;
     }
 }
 
@@ -456,6 +538,7 @@ hipError_t launch_tiles_mp(const TilesPlan& p, const void* Wt, const void* Xq, f
     DG_TL(1, 4, 2) DG_TL(1, 4, 4) DG_TL(1, 8, 2) DG_TL(1, 8, 4) DG_TL(1, 16, 2)
     DG_TL(2, 4, 2) DG_TL(2, 4, 4) DG_TL(2, 2, 4) DG_TL(2, 8, 2)
     DG_TL(4, 1, 4) DG_TL(4, 2, 2) DG_TL(4, 2, 4) DG_TL(4, 4, 2) DG_TL(4, 4, 4)
+    DG_TL(1, 8, 8) DG_TL(2, 4, 8) DG_TL(4, 2, 8) DG_TL(1, 4, 8)
 #undef DG_TL
     return hipErrorInvalidValue;
 }
@@ -477,8 +560,7 @@ hipError_t launch_q4_tiles_pack(const void* Wq, void* Wt, int64_t N, int64_t K, 
 // groups x RT x NT x 1 KiB of partial tile sums; none when KP = 1.
 static size_t tiles_ws_bytes(const TilesPlan& p, int M) {
     if (p.KP == 1) return 0;
-    const size_t nt = M > 16 ? 2 : 1;
-    return kTicketBytes + (size_t)p.KP * p.groups * p.RT * nt * 1024;
+    return kTicketBytes + (size_t)p.KP * p.groups * p.RT * tiles_accumulators(M) * 1024;
 }
 
 // unroll = KP * 1000000 + RT * 10000 + KW * 100 + D (0: the default).
@@ -506,8 +588,9 @@ hipError_t launch_q4_tiles(int M, int unroll, const void* Wt, const void* Xq, fl
                            hipStream_t s) {
     TilesPlan p;
     if (!tiles_resolve(N, K, M, unroll, p) || p.lds > device_max_lds_per_block()) return hipErrorInvalidValue;
+    if (M <= 8) return launch_tiles_mp<8>(p, Wt, Xq, Y, ws, N, K, M, s);
     if (M <= 16) return launch_tiles_mp<16>(p, Wt, Xq, Y, ws, N, K, M, s);
-    return launch_tiles_mp<32>(p, Wt, Xq, Y, ws, N, K, M, s);
+    return launch_tiles_mp<24>(p, Wt, Xq, Y, ws, N, K, M, s);
 }
 
 }  // namespace dg

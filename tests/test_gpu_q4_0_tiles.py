@@ -22,7 +22,8 @@ TICKET_BYTES = 64 * 1024   # the workspace's ticket counters (include/decodegemv
 # (RT, KW, D) configurations the library builds; unroll = KP*1000000 +
 # RT*10000 + KW*100 + D
 BUILT = [(1, 4, 2), (1, 4, 4), (1, 8, 2), (1, 8, 4), (1, 16, 2), (2, 4, 2), (2, 4, 4), (2, 2, 4), (2, 8, 2),
-         (4, 1, 4), (4, 2, 2), (4, 2, 4), (4, 4, 2), (4, 4, 4)]
+         (4, 1, 4), (4, 2, 2), (4, 2, 4), (4, 4, 2), (4, 4, 4),
+         (1, 8, 8), (2, 4, 8), (4, 2, 8), (1, 4, 8)]
 
 
 def unroll(kp, rt, kw, d):
@@ -30,14 +31,15 @@ def unroll(kp, rt, kw, d):
 
 
 def tiled_layout(Wq, N, K):
-    """The tiled bytes of row-major Q4_0 bytes Wq [N][K/32*18], by indexing."""
+    """The tiled bytes of row-major Q4_0 bytes Wq [N][K/32*18], by indexing:
+    each 4-bit code q is stored as q XOR 8, the two's-complement nibble of q - 8."""
     nb = K // 32
     S = K // 256
     T = (N + 15) // 16
     blocks = np.asarray(Wq, dtype=np.uint8).reshape(N, nb, 18)
     pad = np.zeros((T * 16, nb, 18), dtype=np.uint8)
-    pad[:, :, 2:] = 0x88
     pad[:N] = blocks
+    pad[:N, :, 2:] ^= 0x88   # codes as signed nibbles q - 8 (padding rows: 0)
     # [T, 16 rows, S, 8 blocks, 18]
     b = pad.reshape(T, 16, S, 8, 18)
     codes = b[..., 2:].reshape(T, 16, S, 8, 4, 4)            # [t, n, s, i, g, byte]
