@@ -74,7 +74,8 @@ def test_graph_replays_match_eager(dg, dev):
 
 def test_graph_replays_of_every_entry_point(dg, dev):
     """One captured graph holding a call of every computing entry point (the
-    small-batch matrix-core and units paths of both quantised formats, NF4,
+    small-batch matrix-core and units paths of both quantised formats, the
+    tiled Q4_0 path with and without K split over workgroups, NF4,
     the fp32-activation call, ArgCompare, the greedy tail and the
     no-allocation argmax, whose callers are exactly those that capture
     graphs): four replays with new inputs written eagerly in between, each
@@ -105,6 +106,12 @@ def test_graph_replays_of_every_entry_point(dg, dev):
                 tok=torch.empty(1, dtype=torch.int64, device=dev),
                 amin=torch.empty(16, dtype=torch.int64, device=dev),
                 anoalloc=torch.empty(16, dtype=torch.int64, device=dev))
+    Wt4 = torch.empty(dg.dg_q4_0_tiles_bytes(2048, K), dtype=torch.uint8, device=dev)
+    dg.dg_repack_q4_0_tiles(Wq4, Wt4, 2048, K)
+    ws_tiles = torch.zeros(1 << 22, dtype=torch.uint8, device=dev)
+    Xq24 = torch.empty(24 * K // 32 * 36, dtype=torch.uint8, device=dev)
+    outs.update(t16=torch.empty(16 * 2048, dtype=torch.float32, device=dev),
+                t24=torch.empty(24 * 2048, dtype=torch.float32, device=dev))
     ws_tail = torch.zeros(dg.dg_gemv_bf16_argmax_workspace_bytes(20000, K), dtype=torch.uint8, device=dev)
     ws_arg = torch.zeros(dg.dg_argmax_workspace_bytes(16, K), dtype=torch.uint8, device=dev)
 
@@ -113,6 +120,10 @@ def test_graph_replays_of_every_entry_point(dg, dev):
         xb.copy_(xf[0].to(torch.bfloat16))
         dg.dg_gemv_q4_0(Wq4, Xq, outs["y16"], 2048, K, 16)     # matrix cores
         dg.dg_gemv_q4_0(Wq4, Xq, outs["y8"], 2048, K, 8)       # matrix cores, eight columns
+        dg.dg_gemv_q4_0_tiles(Wt4, Xq, outs["t16"], 2048, K, 16, ws=ws_tiles)    # tiled copy
+        dg.dg_quantize_q8_1(xf.repeat(2, 1)[:24].contiguous(), Xq24, 24, K)
+        dg.dg_gemv_q4_0_tiles(Wt4, Xq24, outs["t24"], 2048, K, 24, ws=ws_tiles,      # K split: tickets
+                              launch=dict(unroll=2 * 1000000 + 2 * 10000 + 4 * 100 + 2))
         dg.dg_gemv_q8_0(Wq8, Xq, outs["q8_16"], 2048, K, 16)
         dg.dg_gemv_q8_0(Wq8, Xq, outs["q8_3"], 2048, K, 3)     # units
         dg.dg_gemv_nf4(codes, absmax, table, xb, outs["nf4"], N=2048, K=K, B=64)

@@ -101,6 +101,30 @@ def test_quantised_gemv_output_guards(dg, dev, orc, fmt, N, K, M):
     assert_close(Y.view.cpu().numpy().reshape(M, N), gemv(Wq, Xq, N, K, M, threads=0), 1e-3, f"{fmt} M={M}")
 
 
+@pytest.mark.parametrize("N,K,M,launch", [(1003, 4096, 3, None), (1003, 4096, 16, None), (2051, 4096, 17, None),
+                                          (1003, 14336, 16, None), (300, 5888, 24, dict(unroll=3040402))])
+def test_tiled_q4_0_output_workspace_and_weight_guards(dg, dev, orc, N, K, M, launch):
+    """The tiled copy, the outputs and the workspace (its ticket counters and
+    partial sums, K split over workgroups in the last two cases) stay within
+    their extents on ragged shapes; the counters end at zero."""
+    import torch
+    Wq = orc.quantize_q4_0(synth.normal_f32((906, synth.KIND_W, 0, 0), (N, K)), threads=0)
+    Xq = orc.quantize_q8_1(np.stack([synth.normal_f32((906, synth.KIND_X, 0, m), (K,)) for m in range(M)]))
+    Wt = Guarded(dev, dg.dg_q4_0_tiles_bytes(N, K), torch.uint8)
+    dg.dg_repack_q4_0_tiles(_dev_u8(dev, Wq), Wt.view, N, K)
+    Wt.assert_guards(f"tiles {N}x{K} Wt")
+    need = max(dg.dg_gemv_q4_0_tiles_workspace_bytes(N, K, M), 1 << 20)
+    ws = Guarded(dev, need, torch.uint8)
+    ws.view.zero_()
+    Y = Guarded(dev, M * N, torch.float32)
+    dg.dg_gemv_q4_0_tiles(Wt.view, _dev_u8(dev, Xq), Y.view, N, K, M, ws=ws.view, launch=launch)
+    Y.assert_guards(f"tiles {N}x{K} M={M} Y")
+    ws.assert_guards(f"tiles {N}x{K} M={M} ws")
+    assert not torch.any(ws.view[:64 * 1024] != 0).item()
+    assert_close(Y.view.cpu().numpy().reshape(M, N), orc.gemv_q4_0_q8_1(Wq, Xq, N, K, M, threads=0), 1e-3,
+                 f"tiles M={M}")
+
+
 @pytest.mark.parametrize("N,K,M,launch", [(1003, 4096, 1, None), (1003, 4096, 5, None), (2051, 8192, 1, dict(variant=13))])
 def test_fp32_activation_gemv_output_and_workspace_guards(dg, dev, orc, N, K, M, launch):
     import torch
