@@ -660,6 +660,8 @@ def suite(args):
         suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=not args.no_sweep)
     if want("q4tiles"):
         suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=not args.no_sweep)
+    if want("q8tiles"):
+        suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=not args.no_sweep, fmt="q8_0")
     if want("q8"):
         suite_q8_0(dg, torch, emit, ceil_gbps)
     if want("m1"):
@@ -839,21 +841,25 @@ def suite_q4_small_m(dg, torch, emit, ceil_gbps, sweep=True):
 # (RT, KW, D) configurations of the tiled Q4_0 kernel (dg_gemv_q4_0_tiles_ex:
 # unroll = KP*1000000 + RT*10000 + KW*100 + D)
 TILES_BUILT = [(1, 4, 2), (1, 4, 4), (1, 8, 2), (1, 8, 4), (1, 16, 2), (2, 4, 2), (2, 4, 4), (2, 2, 4), (2, 8, 2),
-               (4, 1, 4), (4, 2, 2), (4, 2, 4), (4, 4, 2), (4, 4, 4),
-               (1, 8, 8), (2, 4, 8), (4, 2, 8), (1, 4, 8)]
+               (4, 1, 4), (4, 2, 2), (4, 2, 4), (4, 4, 2), (4, 4, 4)]
 TILES_WS_BYTES = 40 << 20   # enough for every configuration of the four 8B shapes
 
 
-def suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=True, shapes=None, ms=None):
-    """The Q4_0 small-M sweep over the four 8B shapes with the weights in
-    16-row tiles (dg_repack_q4_0_tiles once, outside the timing), every M, and
-    at the named M every built configuration with K split 1..8 ways."""
+def suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=True, shapes=None, ms=None, fmt="q4_0"):
+    """The Q4_0 (or Q8_0) small-M sweep over the four 8B shapes with the
+    weights in 16-row tiles (dg_repack_*_tiles once, outside the timing), every
+    M, and at the named M every built configuration with K split 1, 2 or 4 ways."""
+    q8 = fmt == "q8_0"
+    nbytes = bytes_q8_0 if q8 else bytes_q4
+    tiles_bytes = dg.dg_q8_0_tiles_bytes if q8 else dg.dg_q4_0_tiles_bytes
+    repack = dg.dg_repack_q8_0_tiles if q8 else dg.dg_repack_q4_0_tiles
+    gemv = dg.dg_gemv_q8_0_tiles if q8 else dg.dg_gemv_q4_0_tiles
     for (N, K) in shapes or [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)]:
-        nc = copies_for(18 * N * K // 32)
+        nc = copies_for((34 if q8 else 18) * N * K // 32)
         Wts = []
-        for Wq in q4_copies(3, N, K, nc):
-            Wt = torch.empty(dg.dg_q4_0_tiles_bytes(N, K), dtype=torch.uint8, device="cuda")
-            dg.dg_repack_q4_0_tiles(Wq, Wt, N, K)
+        for Wq in (q8_0_copies if q8 else q4_copies)(3, N, K, nc):
+            Wt = torch.empty(tiles_bytes(N, K), dtype=torch.uint8, device="cuda")
+            repack(Wq, Wt, N, K)
             torch.cuda.synchronize()
             del Wq
             Wts.append(Wt)
@@ -862,27 +868,26 @@ def suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=True, shapes=None, ms=None)
         for M in ms or range(1, 25):
             Xq = q8_columns(3, K, M)
             Y = torch.empty(M * N, dtype=torch.float32, device="cuda")
-            calls = [(lambda c=c: dg.dg_gemv_q4_0_tiles(Wts[c % nc], Xq, Y, N, K, M, ws=ws))
-                     for c in range(n_calls(nc))]
+            calls = [(lambda c=c: gemv(Wts[c % nc], Xq, Y, N, K, M, ws=ws)) for c in range(n_calls(nc))]
             us, iqr = time_per_call(calls)
             cps = M / (us * 1e-6)
             dip = None if prev is None else round(cps / prev - 1.0, 4)
             prev = cps
-            emit(record(f"gemv_q4_0_tiles {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M, copies=nc,
+            emit(record(f"gemv_{fmt}_tiles {N}x{K}", us, iqr, nbytes(N, K, M), ceil_gbps, M=M, copies=nc,
                         variant="default", columns_per_s=round(cps, 1), change_vs_prev_M=dip))
             if sweep and M in (1, 8, 16, 24):
                 for (rt, kw, d) in TILES_BUILT:
                     for kp in (1, 2, 4):
                         launch = dict(unroll=kp * 1000000 + rt * 10000 + kw * 100 + d)
-                        calls = [(lambda c=c, launch=launch: dg.dg_gemv_q4_0_tiles(Wts[c % nc], Xq, Y, N, K, M,
-                                                                                  ws=ws, launch=launch))
+                        calls = [(lambda c=c, launch=launch: gemv(Wts[c % nc], Xq, Y, N, K, M, ws=ws,
+                                                                  launch=launch))
                                  for c in range(n_calls(nc))]
                         try:
                             calls[0]()
                         except dg.DGError:   # does not fit this shape
                             continue
                         us, iqr = time_per_call(calls, reps=10)
-                        emit(record(f"gemv_q4_0_tiles {N}x{K}", us, iqr, bytes_q4(N, K, M), ceil_gbps, M=M,
+                        emit(record(f"gemv_{fmt}_tiles {N}x{K}", us, iqr, nbytes(N, K, M), ceil_gbps, M=M,
                                     copies=nc, variant="tiles", RT=rt, KW=kw, D=d, KP=kp))
         del Wts
         torch.cuda.empty_cache()
@@ -1306,10 +1311,12 @@ def main():
     ap.add_argument("--profile-small-m", action="store_true",
                     help="launch the small-batch Q4_0 GEMV eagerly on the decoder shapes (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
-                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q4tiles,q8,m1,fused,argmax,tail,nf4")
+                    help="comma-separated suite sections: ceiling,readsize,dense,q4m1,q4m,q4tiles,q8tiles,q8,m1,fused,argmax,"
+                         "tail,nf4")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="suite sections q4m and q4tiles: time the default launch only, not every configuration")
+                    help="suite sections q4m, q4tiles and q8tiles: time the default launch only, not every "
+                         "configuration")
     ap.add_argument("--cpu-budget", type=float, default=16.0,
                     help="seconds of oracle work for cpu_baseline (half on one core, half on all)")
     args = ap.parse_args()

@@ -266,6 +266,41 @@ dg_status dg_gemv_q8_0(const void* Wq, const void* Xq, float* Y,
                        int64_t N, int64_t K, int M, dg_stream stream);
 
 /* ------------------------------------------------------------------------
+ * Q8_0 weights in 16-row tiles: the rearrangement, and the small-batch GEMV
+ * over it, M = 1..24 activation columns
+ *
+ *   Y = the sums of dg_gemv_q8_0 (exact int32 block sums, exact binary16
+ *       scale products), added in the order of this kernel
+ *
+ * The tiled layout of dg_repack_q4_0_tiles for the 8-bit format ("The kernel
+ * that waited for itself" runs Q8_0 through the same small-batch path; the
+ * bitsandbytes issue's 128-bit-chunk layout).  Scales and codes are copied
+ * unchanged.  For tile t (rows 16t..16t+15) and group s of 8 blocks, 4352
+ * bytes at (t * K/256 + s) * 4352:
+ *   bytes 1024h..1024h+1023 (h = 0..3)  16 bytes per lane l = 16g + n:
+ *                     code dwords g and 4 + g of row 16t+n, block 8s+2h,
+ *                     then the same of block 8s+2h+1;
+ *   bytes 4096..4351  16 bytes per row n: the binary16 scales of blocks
+ *                     8s..8s+7, block 8s+i in half i%2 of dword i/2.
+ * Rows past N hold codes 0 and scale 0.  Scales must be finite.
+ *
+ * dg_q8_0_tiles_bytes: ceil(N/16) * K/256 * 4352 (0 for an invalid shape).
+ * dg_repack_q8_0_tiles: Wq (row-major Q8_0 as for dg_gemv_q8_0, 2-byte
+ *   aligned) -> Wt (device, dg_q8_0_tiles_bytes(N, K) bytes, 16-byte
+ *   aligned); K % 256 == 0, K <= 2^26, 0 <= N < 2^31.
+ * dg_gemv_q8_0_tiles, dg_gemv_q8_0_tiles_workspace_bytes (and
+ *   dg_gemv_q8_0_tiles_ex, with the launch overrides below): as the Q4_0
+ *   tiled calls, with the same workspace rules.
+ * Errors: DG_ERR_NULL, DG_ERR_MISALIGNED, DG_ERR_SHAPE, DG_ERR_WORKSPACE,
+ * DG_ERR_ARG (an override not built or not fitting), DG_ERR_HIP.
+ * ------------------------------------------------------------------------ */
+size_t dg_q8_0_tiles_bytes(int64_t N, int64_t K);
+dg_status dg_repack_q8_0_tiles(const void* Wq, void* Wt, int64_t N, int64_t K, dg_stream stream);
+size_t dg_gemv_q8_0_tiles_workspace_bytes(int64_t N, int64_t K, int M);
+dg_status dg_gemv_q8_0_tiles(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                             void* ws, size_t ws_bytes, dg_stream stream);
+
+/* ------------------------------------------------------------------------
  * NF4 weights (4-bit codes into a 16-entry float table, per-block absmax)
  * x bfloat16 activations, one column
  *
@@ -532,13 +567,15 @@ dg_status dg_gemv_nf4_ex(const void* codes, const float* absmax, const float* ta
  * unroll = KP*1000000 + RT*10000 + KW*100 + D selects KP ranges of K per row
  * group, RT row tiles and KW parts of the range per workgroup (RT*KW waves)
  * and D groups of 8 blocks in flight per wave (built: (RT, KW, D) in (1,4,2),
- * (1,4,4), (1,4,8), (1,8,2), (1,8,4), (1,8,8), (1,16,2), (2,4,2), (2,4,4),
- * (2,4,8), (2,2,4), (2,8,2), (4,1,4), (4,2,2), (4,2,4), (4,2,8), (4,4,2),
- * (4,4,4); KP 1..16).  The workspace
+ * (1,4,4), (1,8,2), (1,8,4), (1,16,2), (2,4,2), (2,4,4), (2,2,4), (2,8,2),
+ * (4,1,4), (4,2,2), (4,2,4), (4,4,2), (4,4,4); KP 1..16).  The workspace
  * this configuration needs is checked against ws_bytes (DG_ERR_WORKSPACE);
  * a configuration not built or whose columns do not fit a workgroup's LDS
  * gives DG_ERR_ARG. */
 dg_status dg_gemv_q4_0_tiles_ex(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                                void* ws, size_t ws_bytes, const dg_launch* cfg, dg_stream stream);
+/* dg_gemv_q8_0_tiles with a launch override, as dg_gemv_q4_0_tiles_ex. */
+dg_status dg_gemv_q8_0_tiles_ex(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M,
                                 void* ws, size_t ws_bytes, const dg_launch* cfg, dg_stream stream);
 
 /* dg_gemv_q4_0_f32 with a launch override: variant DG_VARIANT_Q4_LDSROW

@@ -76,6 +76,8 @@ EXPORTED = (
     "dg_argmax_rows_noalloc", "dg_gemv_q4_0_f32", "dg_gemv_q4_0_f32_ex",
     "dg_q4_0_tiles_bytes", "dg_repack_q4_0_tiles", "dg_gemv_q4_0_tiles_workspace_bytes",
     "dg_gemv_q4_0_tiles", "dg_gemv_q4_0_tiles_ex",
+    "dg_q8_0_tiles_bytes", "dg_repack_q8_0_tiles", "dg_gemv_q8_0_tiles_workspace_bytes",
+    "dg_gemv_q8_0_tiles", "dg_gemv_q8_0_tiles_ex",
 )
 
 # Size of the library's fixed per-device argmax key array (include/decodegemv.h).
@@ -173,16 +175,18 @@ def _lib():
     lib.dg_gemv_nf4_ex.restype = st
     lib.dg_quantize_nf4.argtypes = [P, P, P, P, I64, I64, I32, P]
     lib.dg_quantize_nf4.restype = st
-    lib.dg_q4_0_tiles_bytes.argtypes = [I64, I64]
-    lib.dg_q4_0_tiles_bytes.restype = ctypes.c_size_t
-    lib.dg_repack_q4_0_tiles.argtypes = [P, P, I64, I64, P]
-    lib.dg_repack_q4_0_tiles.restype = st
-    lib.dg_gemv_q4_0_tiles_workspace_bytes.argtypes = [I64, I64, I32]
-    lib.dg_gemv_q4_0_tiles_workspace_bytes.restype = ctypes.c_size_t
-    lib.dg_gemv_q4_0_tiles.argtypes = [P, P, P, I64, I64, I32, P, ctypes.c_size_t, P]
-    lib.dg_gemv_q4_0_tiles.restype = st
-    lib.dg_gemv_q4_0_tiles_ex.argtypes = [P, P, P, I64, I64, I32, P, ctypes.c_size_t, ctypes.POINTER(dg_launch), P]
-    lib.dg_gemv_q4_0_tiles_ex.restype = st
+    for f in ("q4_0", "q8_0"):
+        getattr(lib, f"dg_{f}_tiles_bytes").argtypes = [I64, I64]
+        getattr(lib, f"dg_{f}_tiles_bytes").restype = ctypes.c_size_t
+        getattr(lib, f"dg_repack_{f}_tiles").argtypes = [P, P, I64, I64, P]
+        getattr(lib, f"dg_repack_{f}_tiles").restype = st
+        getattr(lib, f"dg_gemv_{f}_tiles_workspace_bytes").argtypes = [I64, I64, I32]
+        getattr(lib, f"dg_gemv_{f}_tiles_workspace_bytes").restype = ctypes.c_size_t
+        getattr(lib, f"dg_gemv_{f}_tiles").argtypes = [P, P, P, I64, I64, I32, P, ctypes.c_size_t, P]
+        getattr(lib, f"dg_gemv_{f}_tiles").restype = st
+        getattr(lib, f"dg_gemv_{f}_tiles_ex").argtypes = [P, P, P, I64, I64, I32, P, ctypes.c_size_t,
+                                                          ctypes.POINTER(dg_launch), P]
+        getattr(lib, f"dg_gemv_{f}_tiles_ex").restype = st
     _handle = lib
     return lib
 
@@ -355,26 +359,78 @@ def dg_gemv_q4_0_f32(Wq, x, Y, N, K, M, Xq=None, launch=None, stream=None):
     return Y
 
 
+def _tiles_fmt(fmt):
+    if fmt not in ("q4_0", "q8_0"):
+        raise ValueError(f"tiled format must be q4_0 or q8_0, not {fmt!r}")
+    return fmt, (18 if fmt == "q4_0" else 34)
+
+
 def dg_q4_0_tiles_bytes(N, K):
     """Bytes of the 16-row-tile copy of an N x K Q4_0 matrix (0 for an invalid shape)."""
     return int(_lib().dg_q4_0_tiles_bytes(int(N), int(K)))
 
 
-def dg_repack_q4_0_tiles(Wq, Wt, N, K, stream=None):
-    """Wt (uint8, dg_q4_0_tiles_bytes(N, K)) = the row-major Q4_0 bytes Wq rearranged into 16-row tiles."""
+def dg_q8_0_tiles_bytes(N, K):
+    """Bytes of the 16-row-tile copy of an N x K Q8_0 matrix (0 for an invalid shape)."""
+    return int(_lib().dg_q8_0_tiles_bytes(int(N), int(K)))
+
+
+def _repack_tiles(fmt, Wq, Wt, N, K, stream):
     torch = _torch()
+    fmt, block_bytes = _tiles_fmt(fmt)
     _need(Wq, (torch.uint8,), "Wq")
     _need(Wt, (torch.uint8,), "Wt")
     N, K = int(N), int(K)
     if N > 0 and K > 0:
-        _fits(Wq, N * (K // 32) * 18, "Wq")
-        _fits(Wt, dg_q4_0_tiles_bytes(N, K), "Wt")
-    _check(_lib().dg_repack_q4_0_tiles(_ptr(Wq), _ptr(Wt), N, K, _stream(stream)), "dg_repack_q4_0_tiles")
+        _fits(Wq, N * (K // 32) * block_bytes, "Wq")
+        _fits(Wt, int(getattr(_lib(), f"dg_{fmt}_tiles_bytes")(N, K)), "Wt")
+    name = f"dg_repack_{fmt}_tiles"
+    _check(getattr(_lib(), name)(_ptr(Wq), _ptr(Wt), N, K, _stream(stream)), name)
     return Wt
+
+
+def dg_repack_q4_0_tiles(Wq, Wt, N, K, stream=None):
+    """Wt (uint8, dg_q4_0_tiles_bytes(N, K)) = the row-major Q4_0 bytes Wq rearranged into 16-row tiles."""
+    return _repack_tiles("q4_0", Wq, Wt, N, K, stream)
+
+
+def dg_repack_q8_0_tiles(Wq, Wt, N, K, stream=None):
+    """Wt (uint8, dg_q8_0_tiles_bytes(N, K)) = the row-major Q8_0 bytes Wq rearranged into 16-row tiles."""
+    return _repack_tiles("q8_0", Wq, Wt, N, K, stream)
 
 
 def dg_gemv_q4_0_tiles_workspace_bytes(N, K, M):
     return int(_lib().dg_gemv_q4_0_tiles_workspace_bytes(int(N), int(K), int(M)))
+
+
+def dg_gemv_q8_0_tiles_workspace_bytes(N, K, M):
+    return int(_lib().dg_gemv_q8_0_tiles_workspace_bytes(int(N), int(K), int(M)))
+
+
+def _gemv_tiles(fmt, Wt, Xq, Y, N, K, M, ws, launch, stream):
+    torch = _torch()
+    fmt, _ = _tiles_fmt(fmt)
+    _need(Wt, (torch.uint8,), "Wt")
+    _need(Xq, (torch.uint8,), "Xq")
+    _need(Y, (torch.float32,), "Y")
+    N, K, M = int(N), int(K), int(M)
+    lib = _lib()
+    if N > 0 and K > 0 and M > 0:
+        _fits(Wt, int(getattr(lib, f"dg_{fmt}_tiles_bytes")(N, K)), "Wt")
+        _fits(Xq, M * (K // 32) * 36, "Xq")
+    if N > 0 and M > 0:
+        _fits(Y, M * N * 4, "Y")
+    if ws is not None:
+        _need(ws, (torch.uint8,), "ws")
+    wsp, wsb = (_ptr(ws), ws.numel()) if ws is not None else (None, 0)
+    name = f"dg_gemv_{fmt}_tiles"
+    if launch is None:
+        st = getattr(lib, name)(_ptr(Wt), _ptr(Xq), _ptr(Y), N, K, M, wsp, wsb, _stream(stream))
+    else:
+        st = getattr(lib, name + "_ex")(_ptr(Wt), _ptr(Xq), _ptr(Y), N, K, M, wsp, wsb,
+                                        ctypes.byref(_cfg(**launch)), _stream(stream))
+    _check(st, name)
+    return Y
 
 
 def dg_gemv_q4_0_tiles(Wt, Xq, Y, N, K, M, ws=None, launch=None, stream=None):
@@ -383,27 +439,13 @@ def dg_gemv_q4_0_tiles(Wt, Xq, Y, N, K, M, ws=None, launch=None, stream=None):
     counters must start at zero; every call leaves them zero), of at least
     dg_gemv_q4_0_tiles_workspace_bytes(N, K, M) bytes for the default launch;
     None is allowed when that is 0."""
-    torch = _torch()
-    _need(Wt, (torch.uint8,), "Wt")
-    _need(Xq, (torch.uint8,), "Xq")
-    _need(Y, (torch.float32,), "Y")
-    N, K, M = int(N), int(K), int(M)
-    if N > 0 and K > 0 and M > 0:
-        _fits(Wt, dg_q4_0_tiles_bytes(N, K), "Wt")
-        _fits(Xq, M * (K // 32) * 36, "Xq")
-    if N > 0 and M > 0:
-        _fits(Y, M * N * 4, "Y")
-    if ws is not None:
-        _need(ws, (torch.uint8,), "ws")
-    wsp, wsb = (_ptr(ws), ws.numel()) if ws is not None else (None, 0)
-    lib = _lib()
-    if launch is None:
-        st = lib.dg_gemv_q4_0_tiles(_ptr(Wt), _ptr(Xq), _ptr(Y), N, K, M, wsp, wsb, _stream(stream))
-    else:
-        st = lib.dg_gemv_q4_0_tiles_ex(_ptr(Wt), _ptr(Xq), _ptr(Y), N, K, M, wsp, wsb, ctypes.byref(_cfg(**launch)),
-                                       _stream(stream))
-    _check(st, "dg_gemv_q4_0_tiles")
-    return Y
+    return _gemv_tiles("q4_0", Wt, Xq, Y, N, K, M, ws, launch, stream)
+
+
+def dg_gemv_q8_0_tiles(Wt, Xq, Y, N, K, M, ws=None, launch=None, stream=None):
+    """Y[M][N] (float32) from the tiled Q8_0 copy Wt and Q8_1 activation bytes
+    (workspace as for dg_gemv_q4_0_tiles)."""
+    return _gemv_tiles("q8_0", Wt, Xq, Y, N, K, M, ws, launch, stream)
 
 
 def dg_gemv_q8_0(Wq, Xq, Y, N, K, M, launch=None, stream=None):

@@ -38,7 +38,7 @@ def common_flags() -> list[str]:
 # allows it) instead of AGPRs that every result would have to be copied out of.
 EXTRA_FLAGS = {"gemv_q4_0_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                "gemv_qmfma_res.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-               "gemv_q4_0_tiles.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+               "gemv_tiles.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources() -> list[str]:

@@ -71,8 +71,8 @@ dg_status gemv_quant_checked(bool q8, const void* Wq, const void* Xq, float* Y, 
     return hip_status(e);
 }
 
-dg_status gemv_tiles_checked(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M, void* ws,
-                             size_t ws_bytes, const dg_launch* cfg, dg_stream stream) {
+dg_status gemv_tiles_checked(bool q8, const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M,
+                             void* ws, size_t ws_bytes, const dg_launch* cfg, dg_stream stream) {
     if (N < 0 || N > kI32Max || K < 0 || K > kQuantMaxK || K % 256 != 0 || M < 0 || M > 24)
         return DG_ERR_SHAPE;
     if (!launch_ok(cfg) || (cfg && (cfg->variant || cfg->grid || cfg->block))) return DG_ERR_ARG;
@@ -87,11 +87,30 @@ dg_status gemv_tiles_checked(const void* Wt, const void* Xq, float* Y, int64_t N
         return hip_status(hipGetLastError());
     }
     size_t need = 0;
-    if (!q4_tiles_config((int)N, (int)K, M, cfg ? cfg->unroll : 0, &need)) return DG_ERR_ARG;
+    if (!tiles_config((int)N, (int)K, M, cfg ? cfg->unroll : 0, &need)) return DG_ERR_ARG;
     if (need > 0 && (!ws || ws_bytes < need)) return DG_ERR_WORKSPACE;
-    hipError_t e = launch_q4_tiles(M, cfg ? cfg->unroll : 0, Wt, Xq, Y, ws, (int)N, (int)K, (hipStream_t)stream);
+    hipError_t e = launch_tiles(q8, M, cfg ? cfg->unroll : 0, Wt, Xq, Y, ws, (int)N, (int)K, (hipStream_t)stream);
     if (e == hipErrorInvalidValue) return DG_ERR_ARG;
     return hip_status(e);
+}
+
+size_t tiles_bytes_checked(bool q8, int64_t N, int64_t K) {
+    if (N < 0 || N > kI32Max || K < 0 || K > kQuantMaxK || K % 256 != 0) return 0;
+    return tiles_bytes(q8, N, K);
+}
+
+dg_status repack_tiles_checked(bool q8, const void* Wq, void* Wt, int64_t N, int64_t K, dg_stream stream) {
+    if (N < 0 || N > kI32Max || K < 0 || K > kQuantMaxK || K % 256 != 0) return DG_ERR_SHAPE;
+    if (N == 0 || K == 0) return DG_OK;
+    if (!Wq || !Wt) return DG_ERR_NULL;
+    if (!aligned(Wq, 2) || !aligned(Wt, 16)) return DG_ERR_MISALIGNED;
+    return hip_status(launch_tiles_pack(q8, Wq, Wt, N, K, (hipStream_t)stream));
+}
+
+size_t tiles_workspace_checked(int64_t N, int64_t K, int M) {
+    size_t need = 0;
+    if (N <= 0 || N > kI32Max || K <= 0 || K > kQuantMaxK || K % 256 != 0 || M <= 0 || M > 24) return 0;
+    return tiles_config((int)N, (int)K, M, 0, &need) ? need : 0;
 }
 
 bool nf4_block_ok(int B) { return B == 32 || B == 64 || B == 128 || B == 256; }
@@ -224,33 +243,37 @@ dg_status dg_gemv_q8_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, i
     return gemv_quant_checked(true, Wq, Xq, Y, N, K, M, cfg, stream);
 }
 
-size_t dg_q4_0_tiles_bytes(int64_t N, int64_t K) {
-    if (N < 0 || N > kI32Max || K < 0 || K > kQuantMaxK || K % 256 != 0) return 0;
-    return q4_tiles_bytes(N, K);
-}
+size_t dg_q4_0_tiles_bytes(int64_t N, int64_t K) { return tiles_bytes_checked(false, N, K); }
+size_t dg_q8_0_tiles_bytes(int64_t N, int64_t K) { return tiles_bytes_checked(true, N, K); }
 
 dg_status dg_repack_q4_0_tiles(const void* Wq, void* Wt, int64_t N, int64_t K, dg_stream stream) {
-    if (N < 0 || N > kI32Max || K < 0 || K > kQuantMaxK || K % 256 != 0) return DG_ERR_SHAPE;
-    if (N == 0 || K == 0) return DG_OK;
-    if (!Wq || !Wt) return DG_ERR_NULL;
-    if (!aligned(Wq, 2) || !aligned(Wt, 16)) return DG_ERR_MISALIGNED;
-    return hip_status(launch_q4_tiles_pack(Wq, Wt, N, K, (hipStream_t)stream));
+    return repack_tiles_checked(false, Wq, Wt, N, K, stream);
+}
+dg_status dg_repack_q8_0_tiles(const void* Wq, void* Wt, int64_t N, int64_t K, dg_stream stream) {
+    return repack_tiles_checked(true, Wq, Wt, N, K, stream);
 }
 
-size_t dg_gemv_q4_0_tiles_workspace_bytes(int64_t N, int64_t K, int M) {
-    size_t need = 0;
-    if (N <= 0 || N > kI32Max || K <= 0 || K > kQuantMaxK || K % 256 != 0 || M <= 0 || M > 24) return 0;
-    return q4_tiles_config((int)N, (int)K, M, 0, &need) ? need : 0;
-}
+size_t dg_gemv_q4_0_tiles_workspace_bytes(int64_t N, int64_t K, int M) { return tiles_workspace_checked(N, K, M); }
+size_t dg_gemv_q8_0_tiles_workspace_bytes(int64_t N, int64_t K, int M) { return tiles_workspace_checked(N, K, M); }
 
 dg_status dg_gemv_q4_0_tiles(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M, void* ws,
                              size_t ws_bytes, dg_stream stream) {
-    return gemv_tiles_checked(Wt, Xq, Y, N, K, M, ws, ws_bytes, nullptr, stream);
+    return gemv_tiles_checked(false, Wt, Xq, Y, N, K, M, ws, ws_bytes, nullptr, stream);
 }
 
 dg_status dg_gemv_q4_0_tiles_ex(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M, void* ws,
                                 size_t ws_bytes, const dg_launch* cfg, dg_stream stream) {
-    return gemv_tiles_checked(Wt, Xq, Y, N, K, M, ws, ws_bytes, cfg, stream);
+    return gemv_tiles_checked(false, Wt, Xq, Y, N, K, M, ws, ws_bytes, cfg, stream);
+}
+
+dg_status dg_gemv_q8_0_tiles(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M, void* ws,
+                             size_t ws_bytes, dg_stream stream) {
+    return gemv_tiles_checked(true, Wt, Xq, Y, N, K, M, ws, ws_bytes, nullptr, stream);
+}
+
+dg_status dg_gemv_q8_0_tiles_ex(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M, void* ws,
+                                size_t ws_bytes, const dg_launch* cfg, dg_stream stream) {
+    return gemv_tiles_checked(true, Wt, Xq, Y, N, K, M, ws, ws_bytes, cfg, stream);
 }
 
 dg_status dg_gemv_q4_0_f32_ex(const void* Wq, const float* x, float* Y, void* Xq, int64_t N, int64_t K, int M,

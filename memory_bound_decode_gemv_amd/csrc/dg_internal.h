@@ -82,16 +82,18 @@ hipError_t launch_q8_units(int K, int M, int depth, const void* Wq, const void* 
 hipError_t launch_q4_mfma(int M, int unroll, const void* Wq, const void* Xq, float* Y, int N, int K, int grid,
                           hipStream_t s);
 
-// Q4_0 in 16-row tiles (the layout of dg_repack_q4_0_tiles): its size, the
-// rearrangement, and the matrix-core GEMV over it for 1..24 columns (unroll =
-// KP*1000000 + RT*10000 + KW*100 + D; 0 = default).  q4_tiles_config is false
-// for a configuration that is not built or does not fit, else gives the
-// workspace bytes it needs (0 when K is not split over workgroups).
-size_t q4_tiles_bytes(int64_t N, int64_t K);
-hipError_t launch_q4_tiles_pack(const void* Wq, void* Wt, int64_t N, int64_t K, hipStream_t s);
-bool q4_tiles_config(int N, int K, int M, int unroll, size_t* ws_bytes);
-hipError_t launch_q4_tiles(int M, int unroll, const void* Wt, const void* Xq, float* Y, void* ws, int N, int K,
-                           hipStream_t s);
+// Q4_0 or Q8_0 (q8) in 16-row tiles (the layouts of dg_repack_q4_0_tiles
+// and dg_repack_q8_0_tiles): their size, the rearrangement, and the
+// matrix-core GEMV over them for 1..24 columns (unroll = KP*1000000 +
+// RT*10000 + KW*100 + D; 0 = default).  tiles_config is false for a
+// configuration that is not built or does not fit, else gives the workspace
+// bytes it needs (0 when K is not split over workgroups); it does not depend
+// on the format.
+size_t tiles_bytes(bool q8, int64_t N, int64_t K);
+hipError_t launch_tiles_pack(bool q8, const void* Wq, void* Wt, int64_t N, int64_t K, hipStream_t s);
+bool tiles_config(int N, int K, int M, int unroll, size_t* ws_bytes);
+hipError_t launch_tiles(bool q8, int M, int unroll, const void* Wt, const void* Xq, float* Y, void* ws, int N, int K,
+                        hipStream_t s);
 
 hipError_t launch_gemv_q8_0(const void* Wq, const void* Xq, float* Y, int N, int K, int M,
                             const dg_launch* cfg, hipStream_t s);

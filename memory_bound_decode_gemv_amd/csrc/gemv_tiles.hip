@@ -1,5 +1,5 @@
-// gemv_q4_0_tiles.hip -- Q4_0 x Q8_1 for 1..24 activation columns from Q4_0
-// weights rearranged into 16-row tiles, and that rearrangement.
+// gemv_tiles.hip -- Q4_0 or Q8_0 x Q8_1 for 1..24 activation columns from
+// weights rearranged into 16-row tiles, and those rearrangements.
 //
 // Why a second weight layout.  In the row-major block format every 16-row
 // tile of the matrix-core kernels is 16 row segments of 144 bytes per 8
@@ -24,6 +24,11 @@
 //                       2048 + 16n, block 8s+i in half i%2 of dword i/2.
 //   Rows past N (the last tile's padding) hold code nibbles 0 (q - 8 = 0)
 //   and scale 0, so they add exact zeros.
+//
+// Q8_0 (34-byte blocks: binary16 d, 32 int8 codes) is tiled the same way,
+// codes unchanged: a group is 4352 bytes, four KiB of codes (KiB h: lane l
+// = 16g + n holds code dwords g and 4 + g of row n, blocks 2h and 2h + 1),
+// then the 256 bytes of scales; a lane's codes are its B operands as loaded.
 //
 // The matrix-core arithmetic keeps the exact integer block sums of the
 // row-major kernels: per block, one v_mfma_i32_16x16x32_i8 of the 16
@@ -60,11 +65,36 @@ using namespace q4;
 using namespace mfma;
 
 constexpr int kGroupBlocks = 8;      // blocks per group of a tile
-constexpr int kGroupBytes = 2304;    // 16 rows x 8 blocks x 18 bytes
-constexpr int kCodeBytes = 2048;     // the group's code bytes; 256 bytes of scales follow
 constexpr int kGroupSlots = 18;      // 16-byte slots of one column's Q8_1 blocks per group (8 x 36 / 16)
 constexpr uint32_t kHiNib = 0xF0F0F0F0u;
-constexpr float kUnscale = 1.0f / 64.0f;   // the products gather 16 x 4 times each sum
+
+// Tiled weight formats.  A group (16 rows x 8 blocks) is kCodeLoads KiB of
+// codes in lane order, then 256 bytes of scales (16 per row); a lane loads
+// kCodeLoads + 1 16-byte vectors per group.  bops gives the lane's B operand
+// dwords of block i for its low k-slots (activation code dword g) and high
+// k-slots (dword 4 + g); kUnscale divides out the factor the integer operands
+// and the scale products (4 d8 d4) carry.
+struct TilesQ4_0 {
+    static constexpr int kCodeLoads = 2;
+    static constexpr int kGroupBytes = 2304;     // 16 rows x 8 blocks x 18 bytes
+    static constexpr float kUnscale = 1.0f / 64.0f;   // 16 (q - 8) codes, 4 d8 d4
+    __device__ __forceinline__ static void bops(const u32x4* w, int i, uint32_t& lo, uint32_t& hi) {
+        const u32x4 v = w[i >> 2];
+        const uint32_t c = (i & 3) == 0 ? v.x : (i & 3) == 1 ? v.y : (i & 3) == 2 ? v.z : v.w;
+        lo = (c << 4) & kHiNib;   // signed nibbles (codes q XOR 8) in the high half of each byte: 16 (q - 8)
+        hi = c & kHiNib;
+    }
+};
+struct TilesQ8_0 {
+    static constexpr int kCodeLoads = 4;
+    static constexpr int kGroupBytes = 4352;     // 16 rows x 8 blocks x 34 bytes
+    static constexpr float kUnscale = 1.0f / 4.0f;    // codes as they are, 4 d8 d4
+    __device__ __forceinline__ static void bops(const u32x4* w, int i, uint32_t& lo, uint32_t& hi) {
+        const u32x4 v = w[i >> 1];
+        lo = (i & 1) ? v.z : v.x;
+        hi = (i & 1) ? v.w : v.y;
+    }
+};
 
 // ---------------------------------------------------------------------------
 // Rearrangement: one thread per 16-byte slot of the tiled layout (144 per
@@ -72,6 +102,7 @@ constexpr float kUnscale = 1.0f / 64.0f;   // the products gather 16 x 4 times e
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256)
 k_q4_tiles_pack(const uint8_t* __restrict__ Wq, uint8_t* __restrict__ Wt, int N, int S, int64_t slots) {
+    constexpr int kGroupBytes = TilesQ4_0::kGroupBytes;
     const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (u >= slots) return;
     const int64_t ts = u / 144;                 // tile * S + group
@@ -110,12 +141,55 @@ k_q4_tiles_pack(const uint8_t* __restrict__ Wq, uint8_t* __restrict__ Wt, int N,
     *reinterpret_cast<u32x4*>(Wt + (size_t)ts * kGroupBytes + (size_t)k * 16) = u32x4{d[0], d[1], d[2], d[3]};
 }
 
-// Three 16-byte loads per lane: the codes of blocks 0..3 and 4..7 of the
-// group (this lane's B operands) and its row's eight scales.
-__device__ __forceinline__ void load_group(const uint8_t* __restrict__ g0, int lane, int rn, u32x4 (&w)[3]) {
-    w[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g0 + lane * 16));
-    w[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g0 + 1024 + lane * 16));
-    w[2] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g0 + kCodeBytes + rn * 16));
+// Q8_0: 272 slots per group (256 of codes, 16 of scales).
+__global__ void __launch_bounds__(256)
+k_q8_tiles_pack(const uint8_t* __restrict__ Wq, uint8_t* __restrict__ Wt, int N, int S, int64_t slots) {
+    constexpr int kGroupBytes = TilesQ8_0::kGroupBytes;
+    const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= slots) return;
+    const int64_t ts = u / 272;                 // tile * S + group
+    const int k = (int)(u - ts * 272);
+    const int64_t t = ts / S;
+    const int s = (int)(ts - t * S);
+    const size_t row_bytes = (size_t)S * kGroupBlocks * 34;
+    uint32_t d[4] = {0u, 0u, 0u, 0u};
+    if (k < 256) {
+        const int h = k >> 6, l = k & 63, g = l >> 4, n = l & 15;
+        const int64_t row = t * 16 + n;
+        if (row < N) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {   // blocks 2h, 2h + 1: code dwords g, 4 + g
+                const int b = kGroupBlocks * s + 2 * h + (j >> 1);
+                const uint16_t* p = reinterpret_cast<const uint16_t*>(
+                    Wq + (size_t)row * row_bytes + (size_t)b * 34 + 2 + 4 * (g + 4 * (j & 1)));
+                d[j] = (uint32_t)p[0] | ((uint32_t)p[1] << 16);
+            }
+        }
+    } else {
+        const int n = k - 256;
+        const int64_t row = t * 16 + n;
+        if (row < N) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint8_t* r = Wq + (size_t)row * row_bytes + (size_t)(kGroupBlocks * s + 2 * j) * 34;
+                d[j] = (uint32_t)*reinterpret_cast<const uint16_t*>(r) |
+                       ((uint32_t)*reinterpret_cast<const uint16_t*>(r + 34) << 16);
+            }
+        }
+    }
+    *reinterpret_cast<u32x4*>(Wt + (size_t)ts * kGroupBytes + (size_t)k * 16) = u32x4{d[0], d[1], d[2], d[3]};
+}
+
+// One group of a lane's weights: kCodeLoads 16-byte loads of codes (its B
+// operands) and one of its row's eight scales.
+template <class TF>
+__device__ __forceinline__ void load_group(const uint8_t* __restrict__ g0, int lane, int rn,
+                                           u32x4 (&w)[TF::kCodeLoads + 1]) {
+#pragma unroll
+    for (int c = 0; c < TF::kCodeLoads; ++c)
+        w[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g0 + c * 1024 + lane * 16));
+    w[TF::kCodeLoads] =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g0 + TF::kCodeLoads * 1024 + rn * 16));
 }
 
 // Column tiles of a launch with MP padded columns: a full tile of 16 columns
@@ -149,12 +223,13 @@ struct ALanes {
 };
 
 // One group of 8 blocks: operands, matrix-core products, fp32 scaling into
-// acc, which gathers 64 times the sums (divided out at the store):
-//  * B (weights): the tiled codes are signed nibbles (q - 8), so masking the
-//    high nibbles of a code dword, and of the dword shifted left by 4, gives
-//    16 (q - 8) as int8 for the lane's 8 k-slots: one MFMA per block (per
-//    two blocks in the pair tile) gives 16 times the exact block sums (|16
-//    S| < 2^20), with no offset term;
+// acc, which gathers 1 / TF::kUnscale times the sums (divided out at the
+// store):
+//  * B (weights), Q4_0: the tiled codes are signed nibbles (q - 8), so
+//    masking the high nibbles of a code dword, and of the dword shifted left
+//    by 4, gives 16 (q - 8) as int8 for the lane's 8 k-slots: one MFMA per
+//    block (per two blocks in the pair tile) gives 16 times the exact block
+//    sums (|16 S| < 2^20), with no offset term; Q8_0: the codes as loaded;
 //  * the scale products come from one v_mfma_f32_16x16x16_f16 per block (per
 //    two blocks in the pair tile) in which B is the lane's raw pair of scale
 //    dwords (the d4 of four blocks, one per k-slot, repeated in all four lane
@@ -162,19 +237,17 @@ struct ALanes {
 //    in every lane group, zeros elsewhere: each output is 4 d8 d4, exact in
 //    fp32 (binary16 products are exact, and so are sums of four equal ones).
 // blk is the group's first block within the LDS copy of the columns.
-template <int MP>
-__device__ __forceinline__ void tiles_group(const u32x4 (&w)[3], const uint8_t* lds, const ALanes& al, uint32_t blk,
-                                            int g, f32x4 (&acc)[TileSet<MP>::kNA]) {
+template <class TF, int MP>
+__device__ __forceinline__ void tiles_group(const u32x4 (&w)[TF::kCodeLoads + 1], const uint8_t* lds,
+                                            const ALanes& al, uint32_t blk, int g,
+                                            f32x4 (&acc)[TileSet<MP>::kNA]) {
     using TS = TileSet<MP>;
-    const uint32_t code[8] = {w[0].x, w[0].y, w[0].z, w[0].w, w[1].x, w[1].y, w[1].z, w[1].w};
-    const f16x4 d4q[2] = {__builtin_bit_cast(f16x4, u32x2{w[2].x, w[2].y}),    // blocks 0..3
-                          __builtin_bit_cast(f16x4, u32x2{w[2].z, w[2].w})};   // blocks 4..7
-    uint32_t blo[8], bhi[8];   // B operand dwords: 16 (q - 8) of the lane's low and high k-slots
+    const u32x4 sv = w[TF::kCodeLoads];
+    const f16x4 d4q[2] = {__builtin_bit_cast(f16x4, u32x2{sv.x, sv.y}),    // blocks 0..3
+                          __builtin_bit_cast(f16x4, u32x2{sv.z, sv.w})};   // blocks 4..7
+    uint32_t blo[8], bhi[8];   // B operand dwords of the lane's low and high k-slots
 #pragma unroll
-    for (int i = 0; i < kGroupBlocks; ++i) {
-        blo[i] = (code[i] << 4) & kHiNib;
-        bhi[i] = code[i] & kHiNib;
-    }
+    for (int i = 0; i < kGroupBlocks; ++i) TF::bops(w, i, blo[i], bhi[i]);
     if constexpr (TS::kFull) {
 #pragma unroll
         for (int i = 0; i < kGroupBlocks; ++i) {
@@ -211,16 +284,20 @@ __device__ __forceinline__ void tiles_group(const u32x4 (&w)[3], const uint8_t* 
 
 // Marks a group's registers as written here (an empty asm): arithmetic on
 // them cannot move above this point, and its loads are waited for here.
-__device__ __forceinline__ void bind_group(u32x4 (&w)[3]) {
-    asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2])::"memory");
+template <int L>
+__device__ __forceinline__ void bind_group(u32x4 (&w)[L]) {
+    static_assert(L == 3 || L == 5, "three or five loads per group");
+    if constexpr (L == 3) asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2])::"memory");
+    else asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]), "+v"(w[4])::"memory");
 }
 
 // Stores the tile's outputs (unscaled).  The full tile adds its even- and
 // odd-block sums; the pair tile's sit in lane groups g and g + 2 (output rows
 // m' and m' + 8).  All 64 lanes of the wave call this.
-template <int MP>
+template <class TF, int MP>
 __device__ __forceinline__ void store_tile(const f32x4 (&acc)[TileSet<MP>::kNA], float* __restrict__ Y, int N, int M,
                                            int t, int g, int rn) {
+    constexpr float kUnscale = TF::kUnscale;
     using TS = TileSet<MP>;
     const int n = t * 16 + rn;
     f32x4 pr = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -252,9 +329,9 @@ __device__ __forceinline__ void store_tile(const f32x4 (&acc)[TileSet<MP>::kNA],
 // full tile and a pair tile); columns past M re-read column M - 1, their
 // results dropped.
 // ---------------------------------------------------------------------------
-template <int MP, int RT, int KW, int D>
+template <class TF, int MP, int RT, int KW, int D>
 __global__ void __launch_bounds__(64 * RT * KW)
-k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
+k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
            uint32_t* __restrict__ tickets, f32x4* __restrict__ part, int N, int K, int M, int KP, int spw,
            int cs_slots, uint32_t cs_magic) {
     using TS = TileSet<MP>;
@@ -279,6 +356,8 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
     const int cnt = max(0, min(spk, ns - w0));     // wave-uniform
     const int t = grp * RT + rt;
     const int tc = t < T ? t : T - 1;
+    constexpr int kGroupBytes = TF::kGroupBytes;
+    constexpr int L = TF::kCodeLoads + 1;   // 16-byte loads per lane and group
     const uint8_t* const wbase = Wt + ((size_t)tc * S + s0 + (cnt > 0 ? w0 : 0)) * kGroupBytes;
     const int last = cnt > 0 ? cnt - 1 : 0;
 
@@ -307,9 +386,10 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
             for (int e = wave * kWave + lane; e < used; e += W * kWave) z[e] = u32x4{0u, 0u, 0u, 0u};
         }
     }
-    u32x4 wb[D][3];
+    u32x4 wb[D][L];
 #pragma unroll
-    for (int d = 0; d < D; ++d) load_group(wbase + (size_t)(d < cnt ? d : last) * kGroupBytes, lane, rn, wb[d]);
+    for (int d = 0; d < D; ++d)
+        load_group<TF>(wbase + (size_t)(d < cnt ? d : last) * kGroupBytes, lane, rn, wb[d]);
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt at their maximum: no wait
     lds_barrier();   // every other wave's copies have landed too
 
@@ -340,9 +420,9 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
 #pragma unroll
         for (int d = 0; d < D; ++d) {
             const int i = rd * D + d;
-            tiles_group<MP>(wb[d], lds, al, (uint32_t)(w0 + i) * kGroupBlocks, g, acc);
+            tiles_group<TF, MP>(wb[d], lds, al, (uint32_t)(w0 + i) * kGroupBlocks, g, acc);
             const int nx = i + D;
-            load_group(wbase + (size_t)(nx < cnt ? nx : last) * kGroupBytes, lane, rn, wb[d]);
+            load_group<TF>(wbase + (size_t)(nx < cnt ? nx : last) * kGroupBytes, lane, rn, wb[d]);
             // Keep the loads here and the next group's arithmetic behind them:
             // binding that group's registers ("bind values, not memory", the
             // third finding of "The kernel that waited for itself") stops the
@@ -357,7 +437,7 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
             const int i = (rounds - 1) * D + d;
             if (d > 0) bind_group(wb[d]);
             if (i < cnt)   // wave-uniform; no loads follow, so the branch costs no wait
-                tiles_group<MP>(wb[d], lds, al, (uint32_t)(w0 + i) * kGroupBlocks, g, acc);
+                tiles_group<TF, MP>(wb[d], lds, al, (uint32_t)(w0 + i) * kGroupBlocks, g, acc);
         }
     }
 
@@ -381,7 +461,7 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
         }
     }
     if (KP == 1) {
-        if (kw == 0 && t < T) store_tile<MP>(acc, Y, N, M, t, g, rn);
+        if (kw == 0 && t < T) store_tile<TF, MP>(acc, Y, N, M, t, g, rn);
         return;
     }
 
@@ -430,7 +510,7 @@ k_q4_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float
                 }
             }
         }
-        store_tile<MP>(sum, Y, N, M, t, g, rn);
+        store_tile<TF, MP>(sum, Y, N, M, t, g, rn);
     }
     if (threadIdx.x == 0) __hip_atomic_store(tickets + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -459,8 +539,7 @@ constexpr size_t kTilesMaxLds = 160 * 1024 - 256;   // a gfx950 workgroup's LDS,
 // The built (RT, KW, D) configurations (launch_tiles_mp lists the same).
 bool tiles_built(int RT, int KW, int D) {
     static const int kBuilt[][3] = {{1, 4, 2}, {1, 4, 4}, {1, 8, 2}, {1, 8, 4}, {1, 16, 2}, {2, 4, 2}, {2, 4, 4},
-                                    {2, 2, 4}, {2, 8, 2}, {4, 1, 4}, {4, 2, 2}, {4, 2, 4}, {4, 4, 2}, {4, 4, 4},
-                                    {1, 8, 8}, {2, 4, 8}, {4, 2, 8}, {1, 4, 8}};
+                                    {2, 2, 4}, {2, 8, 2}, {4, 1, 4}, {4, 2, 2}, {4, 2, 4}, {4, 4, 2}, {4, 4, 4}};
     for (const auto& c : kBuilt)
         if (c[0] == RT && c[1] == KW && c[2] == D) return true;
     return false;
@@ -518,41 +597,60 @@ void tiles_default(int N, int K, int M, int& RT, int& KW, int& D, int& KP) {
     }
 }
 
-template <int MP, int RT, int KW, int D>
+template <class TF, int MP, int RT, int KW, int D>
 hipError_t launch_tiles_cfg(const TilesPlan& p, const void* Wt, const void* Xq, float* Y, void* ws, int N, int K,
                             int M, hipStream_t s) {
     uint32_t* tickets = reinterpret_cast<uint32_t*>(ws);
     f32x4* part = reinterpret_cast<f32x4*>(reinterpret_cast<uint8_t*>(ws) + kTicketBytes);
     const uint32_t magic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)p.cs_slots - 1) / (uint64_t)p.cs_slots);
-    hipLaunchKernelGGL((k_q4_tiles<MP, RT, KW, D>), dim3(p.groups * p.KP), dim3(64 * RT * KW), p.lds, s,
+    hipLaunchKernelGGL((k_tiles<TF, MP, RT, KW, D>), dim3(p.groups * p.KP), dim3(64 * RT * KW), p.lds, s,
                        (const uint8_t*)Wt, (const uint8_t*)Xq, Y, tickets, part, N, K, M, p.KP, p.spw, p.cs_slots,
                        magic);
     return hipGetLastError();
 }
 
-template <int MP>
+// Instantiations that would spill (a 16-wave workgroup has 128 VGPRs per
+// lane; Q8_0 holds five loads per group, and 24 columns three accumulators)
+// are not built; asking for one is an argument error.
+template <class TF, int MP, int RT, int KW, int D>
+constexpr bool tiles_instantiated() {
+    return !(TF::kCodeLoads == 4 && MP == 24 && RT * KW == 16 && D == 4);
+}
+
+template <class TF, int MP>
 hipError_t launch_tiles_mp(const TilesPlan& p, const void* Wt, const void* Xq, float* Y, void* ws, int N, int K,
                            int M, hipStream_t s) {
-#define DG_TL(RR, WW, DD) \
-    if (p.RT == RR && p.KW == WW && p.D == DD) return launch_tiles_cfg<MP, RR, WW, DD>(p, Wt, Xq, Y, ws, N, K, M, s);
+#define DG_TL(RR, WW, DD)                                                              \
+    if constexpr (tiles_instantiated<TF, MP, RR, WW, DD>())                            \
+        if (p.RT == RR && p.KW == WW && p.D == DD)                                     \
+            return launch_tiles_cfg<TF, MP, RR, WW, DD>(p, Wt, Xq, Y, ws, N, K, M, s);
     DG_TL(1, 4, 2) DG_TL(1, 4, 4) DG_TL(1, 8, 2) DG_TL(1, 8, 4) DG_TL(1, 16, 2)
     DG_TL(2, 4, 2) DG_TL(2, 4, 4) DG_TL(2, 2, 4) DG_TL(2, 8, 2)
     DG_TL(4, 1, 4) DG_TL(4, 2, 2) DG_TL(4, 2, 4) DG_TL(4, 4, 2) DG_TL(4, 4, 4)
-    DG_TL(1, 8, 8) DG_TL(2, 4, 8) DG_TL(4, 2, 8) DG_TL(1, 4, 8)
 #undef DG_TL
     return hipErrorInvalidValue;
 }
 
+template <class TF>
+hipError_t launch_tiles_fmt(const TilesPlan& p, const void* Wt, const void* Xq, float* Y, void* ws, int N, int K,
+                            int M, hipStream_t s) {
+    if (M <= 8) return launch_tiles_mp<TF, 8>(p, Wt, Xq, Y, ws, N, K, M, s);
+    if (M <= 16) return launch_tiles_mp<TF, 16>(p, Wt, Xq, Y, ws, N, K, M, s);
+    return launch_tiles_mp<TF, 24>(p, Wt, Xq, Y, ws, N, K, M, s);
+}
+
 }  // namespace
 
-size_t q4_tiles_bytes(int64_t N, int64_t K) { return (size_t)((N + 15) / 16) * (size_t)(K / 256) * kGroupBytes; }
+size_t tiles_bytes(bool q8, int64_t N, int64_t K) {
+    return (size_t)((N + 15) / 16) * (size_t)(K / 256) * (q8 ? TilesQ8_0::kGroupBytes : TilesQ4_0::kGroupBytes);
+}
 
-hipError_t launch_q4_tiles_pack(const void* Wq, void* Wt, int64_t N, int64_t K, hipStream_t s) {
+hipError_t launch_tiles_pack(bool q8, const void* Wq, void* Wt, int64_t N, int64_t K, hipStream_t s) {
     const int S = (int)(K / 256);
-    const int64_t slots = (N + 15) / 16 * S * 144;
+    const int64_t slots = (N + 15) / 16 * S * (q8 ? 272 : 144);
     if (slots == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_q4_tiles_pack, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0, s, (const uint8_t*)Wq,
-                       (uint8_t*)Wt, (int)N, S, slots);
+    hipLaunchKernelGGL(q8 ? k_q8_tiles_pack : k_q4_tiles_pack, dim3((unsigned)((slots + 255) / 256)), dim3(256), 0,
+                       s, (const uint8_t*)Wq, (uint8_t*)Wt, (int)N, S, slots);
     return hipGetLastError();
 }
 
@@ -577,20 +675,19 @@ static bool tiles_resolve(int N, int K, int M, int unroll, TilesPlan& p) {
     return tiles_plan(N, K, M, RT, KW, D, KP, p);
 }
 
-bool q4_tiles_config(int N, int K, int M, int unroll, size_t* ws_bytes) {
+bool tiles_config(int N, int K, int M, int unroll, size_t* ws_bytes) {
     TilesPlan p;
     if (N <= 0 || K <= 0 || M <= 0 || M > 24 || !tiles_resolve(N, K, M, unroll, p)) return false;
     *ws_bytes = tiles_ws_bytes(p, M);
     return true;
 }
 
-hipError_t launch_q4_tiles(int M, int unroll, const void* Wt, const void* Xq, float* Y, void* ws, int N, int K,
-                           hipStream_t s) {
+hipError_t launch_tiles(bool q8, int M, int unroll, const void* Wt, const void* Xq, float* Y, void* ws, int N, int K,
+                        hipStream_t s) {
     TilesPlan p;
     if (!tiles_resolve(N, K, M, unroll, p) || p.lds > device_max_lds_per_block()) return hipErrorInvalidValue;
-    if (M <= 8) return launch_tiles_mp<8>(p, Wt, Xq, Y, ws, N, K, M, s);
-    if (M <= 16) return launch_tiles_mp<16>(p, Wt, Xq, Y, ws, N, K, M, s);
-    return launch_tiles_mp<24>(p, Wt, Xq, Y, ws, N, K, M, s);
+    return q8 ? launch_tiles_fmt<TilesQ8_0>(p, Wt, Xq, Y, ws, N, K, M, s)
+              : launch_tiles_fmt<TilesQ4_0>(p, Wt, Xq, Y, ws, N, K, M, s);
 }
 
 }  // namespace dg

@@ -164,27 +164,33 @@ def test_argmax_wave_reduction_on_dpp(asm):
     assert "ds_bpermute" not in t
 
 
-def test_tiled_q4_kernel_form(asm):
-    """The tiled Q4_0 kernel: weights straight into registers with 16-byte
-    non-temporal loads (no LDS copy of weights), the activation columns by
-    LDS DMA, one int8 MFMA per block (no offset product) or per two blocks
-    (the 64-deep form of the pair tiles), the scale products on the f16
-    matrix cores, MFMA results in VGPRs.  The split-K ticket exchange uses
-    vector atomics and device-coherent loads and stores, never the whole-cache
-    write-back and invalidate of agent-scope fences."""
-    t = asm["gemv_q4_0_tiles.hip"]
-    ks = [(n, b) for n, b in _kernels(t) if "k_q4_tilesI" in n]
-    assert len(ks) >= 20
+def test_tiled_kernel_form(asm):
+    """The tiled Q4_0 / Q8_0 kernel: weights straight into registers with
+    16-byte non-temporal loads (no LDS copy of weights), the activation
+    columns by LDS DMA, one int8 MFMA per block (no offset product) or per two
+    blocks (the 64-deep form of the pair tiles), the scale products on the
+    f16 matrix cores, MFMA results in VGPRs.  The split-K ticket exchange
+    uses vector atomics and device-coherent loads and stores, never the
+    whole-cache write-back and invalidate of agent-scope fences."""
+    t = asm["gemv_tiles.hip"]
+    ks = [(n, b) for n, b in _kernels(t) if "k_tilesI" in n]
+    assert len(ks) >= 40
+    formats = set()
     for n, b in ks:
+        m = re.search(r"k_tilesINS0_\d+Tiles(Q4_0|Q8_0)ELi(\d+)E", n)
+        assert m, n
+        formats.add(m.group(1))
+        mp = int(m.group(2))
         assert re.search(r"global_load_dwordx4 .* nt", b), n
         assert "global_load_lds_dwordx4" in b, n
         assert "v_mfma_f32_16x16x16_f16" in b, n
         assert "buffer_wbl2" not in b and "buffer_inv" not in b, n
         assert "global_atomic_add" in b, n
         assert not re.search(r"v_accvgpr_read", b), n
-        mp = int(re.search(r"k_q4_tilesILi(\d+)E", n).group(1))
         assert ("v_mfma_i32_16x16x64_i8" in b) == (mp in (8, 24)), n
         assert ("v_mfma_i32_16x16x32_i8" in b) == (mp >= 16), n
-    # the rearrangement kernel writes whole 16-byte slots
-    pk = [b for n, b in _kernels(t) if "k_q4_tiles_pack" in n]
-    assert pk and "global_store_dwordx4" in pk[0]
+    assert formats == {"Q4_0", "Q8_0"}
+    # the rearrangement kernels write whole 16-byte slots
+    for pack in ("k_q4_tiles_pack", "k_q8_tiles_pack"):
+        pk = [b for n, b in _kernels(t) if pack in n]
+        assert pk and "global_store_dwordx4" in pk[0], pack
