@@ -848,7 +848,8 @@ TILES_WS_BYTES = 40 << 20   # enough for every configuration of the four 8B shap
 def suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=True, shapes=None, ms=None, fmt="q4_0"):
     """The Q4_0 (or Q8_0) small-M sweep over the four 8B shapes with the
     weights in 16-row tiles (dg_repack_*_tiles once, outside the timing), every
-    M, and at the named M every built configuration with K split 1, 2 or 4 ways."""
+    M, and at the named M every built configuration with K split 1, 2 or 4 ways
+    or the columns split 2 or 3 ways."""
     q8 = fmt == "q8_0"
     nbytes = bytes_q8_0 if q8 else bytes_q4
     tiles_bytes = dg.dg_q8_0_tiles_bytes if q8 else dg.dg_q4_0_tiles_bytes
@@ -877,8 +878,8 @@ def suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=True, shapes=None, ms=None,
                         variant="default", columns_per_s=round(cps, 1), change_vs_prev_M=dip))
             if sweep and M in (1, 8, 16, 24):
                 for (rt, kw, d) in TILES_BUILT:
-                    for kp in (1, 2, 4):
-                        launch = dict(unroll=kp * 1000000 + rt * 10000 + kw * 100 + d)
+                    for (kp, cs) in ((1, 1), (2, 1), (4, 1), (1, 2), (1, 3)):
+                        launch = dict(unroll=cs * 100000000 + kp * 1000000 + rt * 10000 + kw * 100 + d)
                         calls = [(lambda c=c, launch=launch: gemv(Wts[c % nc], Xq, Y, N, K, M, ws=ws,
                                                                   launch=launch))
                                  for c in range(n_calls(nc))]
@@ -888,7 +889,7 @@ def suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=True, shapes=None, ms=None,
                             continue
                         us, iqr = time_per_call(calls, reps=10)
                         emit(record(f"gemv_{fmt}_tiles {N}x{K}", us, iqr, nbytes(N, K, M), ceil_gbps, M=M,
-                                    copies=nc, variant="tiles", RT=rt, KW=kw, D=d, KP=kp))
+                                    copies=nc, variant="tiles", RT=rt, KW=kw, D=d, KP=kp, CS=cs))
         del Wts
         torch.cuda.empty_cache()
 

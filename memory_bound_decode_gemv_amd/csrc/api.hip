@@ -87,7 +87,7 @@ dg_status gemv_tiles_checked(bool q8, const void* Wt, const void* Xq, float* Y, 
         return hip_status(hipGetLastError());
     }
     size_t need = 0;
-    if (!tiles_config((int)N, (int)K, M, cfg ? cfg->unroll : 0, &need)) return DG_ERR_ARG;
+    if (!tiles_config(q8, (int)N, (int)K, M, cfg ? cfg->unroll : 0, &need)) return DG_ERR_ARG;
     if (need > 0 && (!ws || ws_bytes < need)) return DG_ERR_WORKSPACE;
     hipError_t e = launch_tiles(q8, M, cfg ? cfg->unroll : 0, Wt, Xq, Y, ws, (int)N, (int)K, (hipStream_t)stream);
     if (e == hipErrorInvalidValue) return DG_ERR_ARG;
@@ -107,10 +107,10 @@ dg_status repack_tiles_checked(bool q8, const void* Wq, void* Wt, int64_t N, int
     return hip_status(launch_tiles_pack(q8, Wq, Wt, N, K, (hipStream_t)stream));
 }
 
-size_t tiles_workspace_checked(int64_t N, int64_t K, int M) {
+size_t tiles_workspace_checked(bool q8, int64_t N, int64_t K, int M) {
     size_t need = 0;
     if (N <= 0 || N > kI32Max || K <= 0 || K > kQuantMaxK || K % 256 != 0 || M <= 0 || M > 24) return 0;
-    return tiles_config((int)N, (int)K, M, 0, &need) ? need : 0;
+    return tiles_config(q8, (int)N, (int)K, M, 0, &need) ? need : 0;
 }
 
 bool nf4_block_ok(int B) { return B == 32 || B == 64 || B == 128 || B == 256; }
@@ -253,8 +253,12 @@ dg_status dg_repack_q8_0_tiles(const void* Wq, void* Wt, int64_t N, int64_t K, d
     return repack_tiles_checked(true, Wq, Wt, N, K, stream);
 }
 
-size_t dg_gemv_q4_0_tiles_workspace_bytes(int64_t N, int64_t K, int M) { return tiles_workspace_checked(N, K, M); }
-size_t dg_gemv_q8_0_tiles_workspace_bytes(int64_t N, int64_t K, int M) { return tiles_workspace_checked(N, K, M); }
+size_t dg_gemv_q4_0_tiles_workspace_bytes(int64_t N, int64_t K, int M) {
+    return tiles_workspace_checked(false, N, K, M);
+}
+size_t dg_gemv_q8_0_tiles_workspace_bytes(int64_t N, int64_t K, int M) {
+    return tiles_workspace_checked(true, N, K, M);
+}
 
 dg_status dg_gemv_q4_0_tiles(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M, void* ws,
                              size_t ws_bytes, dg_stream stream) {

@@ -84,14 +84,14 @@ hipError_t launch_q4_mfma(int M, int unroll, const void* Wq, const void* Xq, flo
 
 // Q4_0 or Q8_0 (q8) in 16-row tiles (the layouts of dg_repack_q4_0_tiles
 // and dg_repack_q8_0_tiles): their size, the rearrangement, and the
-// matrix-core GEMV over them for 1..24 columns (unroll = KP*1000000 +
-// RT*10000 + KW*100 + D; 0 = default).  tiles_config is false for a
-// configuration that is not built or does not fit, else gives the workspace
-// bytes it needs (0 when K is not split over workgroups); it does not depend
-// on the format.
+// matrix-core GEMV over them for 1..24 columns (unroll = CS*100000000 +
+// KP*1000000 + RT*10000 + KW*100 + D; 0 = the format's default).
+// tiles_config is false for a configuration that is not built or does not
+// fit, else gives the workspace bytes it needs (0 when K is not split over
+// workgroups).
 size_t tiles_bytes(bool q8, int64_t N, int64_t K);
 hipError_t launch_tiles_pack(bool q8, const void* Wq, void* Wt, int64_t N, int64_t K, hipStream_t s);
-bool tiles_config(int N, int K, int M, int unroll, size_t* ws_bytes);
+bool tiles_config(bool q8, int N, int K, int M, int unroll, size_t* ws_bytes);
 hipError_t launch_tiles(bool q8, int M, int unroll, const void* Wt, const void* Xq, float* Y, void* ws, int N, int K,
                         hipStream_t s);
 

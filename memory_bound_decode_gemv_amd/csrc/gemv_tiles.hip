@@ -333,7 +333,7 @@ template <class TF, int MP, int RT, int KW, int D>
 __global__ void __launch_bounds__(64 * RT * KW)
 k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
            uint32_t* __restrict__ tickets, f32x4* __restrict__ part, int N, int K, int M, int KP, int spw,
-           int cs_slots, uint32_t cs_magic) {
+           int cs_slots, uint32_t cs_magic, int CS, int groups) {
     using TS = TileSet<MP>;
     constexpr int NA = TS::kNA;
     constexpr int W = RT * KW;
@@ -347,8 +347,27 @@ k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* _
     const int S = K >> 8;
     const int nblk = K >> 5;
     const int T = (N + 15) >> 4;
-    const int grp = (int)blockIdx.x / KP;
-    const int kp = (int)blockIdx.x - grp * KP;
+    int grp, kp;
+    if (CS == 1) {
+        grp = (int)blockIdx.x / KP;
+        kp = (int)blockIdx.x - grp * KP;
+    } else {
+        // Column split (KP = 1): the CS workgroups of a row group take Mh =
+        // ceil(M / CS) columns each and sit 8 workgroup ids apart, so the
+        // round-robin placement puts them on one XCD, whose L2 serves their
+        // shared weight rows once.  Row groups are padded to whole blocks of 8.
+        const int b = (int)blockIdx.x;
+        const int hi = b >> 3;
+        const int cs = hi % CS;
+        grp = (hi / CS) * 8 + (b & 7);
+        kp = 0;
+        if (grp >= groups) return;   // workgroup-uniform, before any barrier
+        const int Mh = (M + CS - 1) / CS;
+        const int mc0 = cs * Mh;
+        Xq += (size_t)mc0 * (size_t)(K >> 5) * kQ81Bytes;
+        Y += (size_t)mc0 * (size_t)N;
+        M = min(Mh, M - mc0);
+    }
     const int s0 = kp * spw;                       // first group of the workgroup's range
     const int ns = min(spw, S - s0);               // groups in the range (>= 1)
     const int spk = (ns + KW - 1) / KW;
@@ -521,6 +540,8 @@ int tiles_accumulators(int M) { return M <= 8 ? 1 : M <= 16 ? 2 : 3; }
 // A resolved configuration of the tiled kernel.
 struct TilesPlan {
     int RT, KW, D, KP;   // row tiles and K parts per workgroup, groups in flight per wave, K ranges
+    int CS;              // column slices per row group (KP = 1 when CS > 1)
+    int Mh;              // columns per workgroup: ceil(M / CS)
     int spw;             // groups per range
     int cs_slots;        // LDS column stride, 16-byte slots (odd)
     size_t lds;          // dynamic LDS per workgroup
@@ -528,6 +549,7 @@ struct TilesPlan {
 };
 
 constexpr int kTilesMaxKP = 16;
+constexpr int kTilesMaxCS = 8;
 // The ticket counters sit at the start of the workspace, one per row group,
 // at the same place for every shape: a call leaves all of them zero, so
 // calls of different shapes can share one workspace (partial sums, whose
@@ -545,12 +567,17 @@ bool tiles_built(int RT, int KW, int D) {
     return false;
 }
 
-bool tiles_plan(int N, int K, int M, int RT, int KW, int D, int KP, TilesPlan& p) {
+bool tiles_plan(int N, int K, int M, int RT, int KW, int D, int KP, int CS, TilesPlan& p) {
     const int S = K >> 8;
     if (S < 1 || KP < 1 || KP > kTilesMaxKP || !tiles_built(RT, KW, D)) return false;
+    if (CS < 1 || CS > kTilesMaxCS || (CS > 1 && KP != 1)) return false;
     p.RT = RT;
     p.KW = KW;
     p.D = D;
+    p.CS = CS;
+    p.Mh = (M + CS - 1) / CS;
+    if ((CS - 1) * p.Mh >= M) return false;   // every slice has columns
+    M = p.Mh;                                 // a workgroup's columns
     p.spw = (S + KP - 1) / KP;
     p.KP = (S + p.spw - 1) / p.spw;   // no empty range
     p.cs_slots = kGroupSlots * p.spw + 1;
@@ -566,35 +593,70 @@ bool tiles_plan(int N, int K, int M, int RT, int KW, int D, int KP, TilesPlan& p
     return p.lds <= kTilesMaxLds && p.cs_slots < (1 << 14) && M * p.cs_slots + kWave < (1 << 18);
 }
 
-// Default configuration, from a sweep of every built configuration on MI355X
-// over the four decoder-layer shapes at M = 1, 8, 16, 24 (K split 1, 2 or 4
-// ways).  K is split over workgroups only when the columns of a whole row
-// would not fit a workgroup's LDS (the ticket exchange costs 1.5-2.5 us per
-// call): then the ranges are as long as fit, with two row tiles per
-// workgroup over 4 waves each for two ranges and four tiles over 2 waves for
-// more.  Otherwise: from 512 row tiles on, two row tiles per workgroup (four
-// beyond 8 columns, sharing each column copy between more rows) over K in 4
-// parts; below, one row tile over K in 8 parts.  Two groups in flight per
-// wave.  Measured (us, M = 1 / 8 / 16 / 24): 4096x4096 4.51 / 4.91 / 5.72 /
-// 6.92; 14336x4096 7.37 / 8.64 / 9.73 / 11.72; 1024x4096 3.88 / 4.29 / 5.02 /
-// 6.28; 4096x14336 8.41 / 9.53 / 11.86 / 17.08.
-void tiles_default(int N, int K, int M, int& RT, int& KW, int& D, int& KP) {
+// Default configuration, from sweeps of every built configuration on MI355X
+// over the four decoder-layer shapes (1024, 4096 and 14336 rows of 4096
+// columns, 4096 rows of 14336) at M = 1..24, K split 1, 2 or 4 ways or the
+// columns in 2..8 slices.
+//
+// Column slices first.  Below 128 row tiles a row group per workgroup leaves
+// most of the chip idle: M / 2 slices, at most 4, 8 waves each over K.  Below
+// 512 row tiles and past 8 columns, 2 slices of 4 waves.  Where the columns
+// of whole rows do not fit a workgroup's LDS, 2 slices (Q4_0: 3 when 2 do not
+// fit) in place of a K split: the slices read each weight row once from HBM
+// and once more from their XCD's L2, and exchange nothing.  More than 2
+// slices on the larger shapes lose that L2 hit rate (measured 40-100% slower
+// at 3 to 8).  A slice whose columns need more than half the LDS (one
+// workgroup per CU) gets two row tiles per workgroup (four over two K parts,
+// four groups deep, for 3 slices).  Otherwise K is split over workgroups
+// only when the columns still do not fit (the ticket exchange costs 1.5-2.5
+// us per call): ranges as long as fit, two row tiles per workgroup over 4
+// waves each for two ranges and four tiles over 2 waves for more.  Without
+// slices or a split: from 512 row tiles on, two row tiles over K in 2 parts,
+// four groups deep, to 8 columns, four row tiles over 4 parts past 8; below
+// 512, one row tile over K in 8 parts.  Two groups in flight per wave unless
+// stated.
+void tiles_default(bool q8, int N, int K, int M, int& RT, int& KW, int& D, int& KP, int& CS) {
     const int T = (N + 15) / 16;
     const int S = K >> 8;
-    const size_t fit = 150 * 1024;   // the columns of one range in LDS
     D = 2;
     KP = 1;
-    while (KP < kTilesMaxKP && KP < S && (size_t)M * ((S + KP - 1) / KP) * kGroupSlots * 16 > fit) KP *= 2;
-    if (KP > 1) {
-        RT = KP >= 4 ? 4 : 2;
-        KW = KP >= 4 ? 2 : 4;
-    } else if (T >= 512) {
-        RT = M <= 8 ? 2 : 4;
-        KW = 4;
-    } else {
-        RT = 1;
-        KW = 8;
+    int want = T < 128 ? std::min(4, std::max(1, M / 2)) : (T < 512 && M > 8) ? 2 : 1;
+    while (want > 1 && (want - 1) * ((M + want - 1) / want) >= M) --want;   // no empty slice
+    const int cand[3] = {want, std::max(want, 2), q8 ? 0 : std::max(want, 3)};
+    TilesPlan p;
+    CS = 0;
+    for (int c : cand)
+        if (c > 0 && tiles_plan(N, K, M, 1, 4, 2, 1, c, p)) {
+            CS = c;
+            break;
+        }
+    if (CS > 1) {
+        if (p.lds > kTilesMaxLds / 2) {
+            RT = CS == 3 ? 4 : 2;
+            KW = CS == 3 ? 2 : 4;
+            D = CS == 3 ? 4 : 2;
+        } else {
+            RT = 1;
+            KW = T < 128 ? 8 : 4;
+        }
+        return;
     }
+    if (CS == 1) {
+        if (T >= 512) {
+            RT = M <= 8 ? 2 : 4;
+            KW = M <= 8 ? 2 : 4;
+            D = M <= 8 ? 4 : 2;
+        } else {
+            RT = 1;
+            KW = 8;
+        }
+        return;
+    }
+    CS = 1;
+    const size_t fit = 150 * 1024;   // the columns of one range in LDS
+    while (KP < kTilesMaxKP && KP < S && (size_t)M * ((S + KP - 1) / KP) * kGroupSlots * 16 > fit) KP *= 2;
+    RT = KP >= 4 ? 4 : 2;
+    KW = KP >= 4 ? 2 : 4;
 }
 
 template <class TF, int MP, int RT, int KW, int D>
@@ -603,9 +665,10 @@ hipError_t launch_tiles_cfg(const TilesPlan& p, const void* Wt, const void* Xq, 
     uint32_t* tickets = reinterpret_cast<uint32_t*>(ws);
     f32x4* part = reinterpret_cast<f32x4*>(reinterpret_cast<uint8_t*>(ws) + kTicketBytes);
     const uint32_t magic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)p.cs_slots - 1) / (uint64_t)p.cs_slots);
-    hipLaunchKernelGGL((k_tiles<TF, MP, RT, KW, D>), dim3(p.groups * p.KP), dim3(64 * RT * KW), p.lds, s,
-                       (const uint8_t*)Wt, (const uint8_t*)Xq, Y, tickets, part, N, K, M, p.KP, p.spw, p.cs_slots,
-                       magic);
+    const int grid = p.CS == 1 ? p.groups * p.KP : (p.groups + 7) / 8 * 8 * p.CS;
+    hipLaunchKernelGGL((k_tiles<TF, MP, RT, KW, D>), dim3(grid), dim3(64 * RT * KW), p.lds, s, (const uint8_t*)Wt,
+                       (const uint8_t*)Xq, Y, tickets, part, N, K, M, p.KP, p.spw, p.cs_slots, magic, p.CS,
+                       p.groups);
     return hipGetLastError();
 }
 
@@ -634,8 +697,8 @@ hipError_t launch_tiles_mp(const TilesPlan& p, const void* Wt, const void* Xq, f
 template <class TF>
 hipError_t launch_tiles_fmt(const TilesPlan& p, const void* Wt, const void* Xq, float* Y, void* ws, int N, int K,
                             int M, hipStream_t s) {
-    if (M <= 8) return launch_tiles_mp<TF, 8>(p, Wt, Xq, Y, ws, N, K, M, s);
-    if (M <= 16) return launch_tiles_mp<TF, 16>(p, Wt, Xq, Y, ws, N, K, M, s);
+    if (p.Mh <= 8) return launch_tiles_mp<TF, 8>(p, Wt, Xq, Y, ws, N, K, M, s);
+    if (p.Mh <= 16) return launch_tiles_mp<TF, 16>(p, Wt, Xq, Y, ws, N, K, M, s);
     return launch_tiles_mp<TF, 24>(p, Wt, Xq, Y, ws, N, K, M, s);
 }
 
@@ -658,26 +721,29 @@ hipError_t launch_tiles_pack(bool q8, const void* Wq, void* Wt, int64_t N, int64
 // groups x RT x NT x 1 KiB of partial tile sums; none when KP = 1.
 static size_t tiles_ws_bytes(const TilesPlan& p, int M) {
     if (p.KP == 1) return 0;
-    return kTicketBytes + (size_t)p.KP * p.groups * p.RT * tiles_accumulators(M) * 1024;
+    return kTicketBytes + (size_t)p.KP * p.groups * p.RT * tiles_accumulators(M) * 1024;   // CS = 1 here
 }
 
-// unroll = KP * 1000000 + RT * 10000 + KW * 100 + D (0: the default).
-static bool tiles_resolve(int N, int K, int M, int unroll, TilesPlan& p) {
-    int RT, KW, D, KP;
+// unroll = CS * 100000000 + KP * 1000000 + RT * 10000 + KW * 100 + D (0: the
+// default; CS 0 means 1).
+static bool tiles_resolve(bool q8, int N, int K, int M, int unroll, TilesPlan& p) {
+    int RT, KW, D, KP, CS;
     if (unroll) {
-        KP = unroll / 1000000;
+        CS = unroll / 100000000;
+        CS = CS ? CS : 1;
+        KP = (unroll / 1000000) % 100;
         RT = (unroll / 10000) % 100;
         KW = (unroll / 100) % 100;
         D = unroll % 100;
     } else {
-        tiles_default(N, K, M, RT, KW, D, KP);
+        tiles_default(q8, N, K, M, RT, KW, D, KP, CS);
     }
-    return tiles_plan(N, K, M, RT, KW, D, KP, p);
+    return tiles_plan(N, K, M, RT, KW, D, KP, CS, p);
 }
 
-bool tiles_config(int N, int K, int M, int unroll, size_t* ws_bytes) {
+bool tiles_config(bool q8, int N, int K, int M, int unroll, size_t* ws_bytes) {
     TilesPlan p;
-    if (N <= 0 || K <= 0 || M <= 0 || M > 24 || !tiles_resolve(N, K, M, unroll, p)) return false;
+    if (N <= 0 || K <= 0 || M <= 0 || M > 24 || !tiles_resolve(q8, N, K, M, unroll, p)) return false;
     *ws_bytes = tiles_ws_bytes(p, M);
     return true;
 }
@@ -685,7 +751,7 @@ bool tiles_config(int N, int K, int M, int unroll, size_t* ws_bytes) {
 hipError_t launch_tiles(bool q8, int M, int unroll, const void* Wt, const void* Xq, float* Y, void* ws, int N, int K,
                         hipStream_t s) {
     TilesPlan p;
-    if (!tiles_resolve(N, K, M, unroll, p) || p.lds > device_max_lds_per_block()) return hipErrorInvalidValue;
+    if (!tiles_resolve(q8, N, K, M, unroll, p) || p.lds > device_max_lds_per_block()) return hipErrorInvalidValue;
     return q8 ? launch_tiles_fmt<TilesQ8_0>(p, Wt, Xq, Y, ws, N, K, M, s)
               : launch_tiles_fmt<TilesQ4_0>(p, Wt, Xq, Y, ws, N, K, M, s);
 }

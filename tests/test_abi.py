@@ -266,7 +266,8 @@ def test_tiles_sizes(lib):
     f = lib.dg_gemv_q4_0_tiles_workspace_bytes
     f.restype = ctypes.c_size_t
     f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
-    assert f(4096, 14336, 16) > 0      # K split over workgroups
+    assert f(4096, 28672, 24) > 0      # K split over workgroups
+    assert f(4096, 14336, 16) == 0     # the columns in two slices instead
     assert f(4096, 4000, 16) == 0      # invalid shape
     assert f(4096, 14336, 25) == 0
 
@@ -295,12 +296,38 @@ def test_repack_q4_0_tiles_rejects_before_launch(lib, args, expect):
     ((A2, A16, A16, 4, 256, 1, None, 0), 2),                  # Wt 16-byte aligned
     ((A16, P(0x1004), A16, 4, 256, 1, None, 0), 2),           # Xq 16-byte aligned
     ((A16, A16, A2, 4, 256, 1, None, 0), 2),                  # Y 4-byte aligned
-    ((A16, A16, A16, 4096, 14336, 16, A2, 1 << 24), 2),       # workspace 16-byte aligned
-    ((A16, A16, A16, 4096, 14336, 16, None, 0), 4),           # K split: workspace needed
-    ((A16, A16, A16, 4096, 14336, 16, A16, 64), 4),           # too small
+    ((A16, A16, A16, 4096, 28672, 24, A2, 1 << 24), 2),       # workspace 16-byte aligned
+    ((A16, A16, A16, 4096, 28672, 24, None, 0), 4),           # K split: workspace needed
+    ((A16, A16, A16, 4096, 28672, 24, A16, 64), 4),           # too small
     ((None, None, None, 4, 256, 0, None, 0), 0),              # M = 0
     ((None, None, None, 0, 256, 3, None, 0), 0),              # N = 0
 ])
 def test_gemv_q4_0_tiles_rejects_before_launch(lib, args, expect):
     lib.dg_gemv_q4_0_tiles.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, P, ctypes.c_size_t, P]
     assert lib.dg_gemv_q4_0_tiles(*args, None) == expect
+
+
+def test_q8_0_tiles_sizes_and_rejections(lib):
+    f = lib.dg_q8_0_tiles_bytes
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64]
+    assert f(16, 256) == 4352
+    assert f(17, 512) == 2 * 2 * 4352
+    assert f(16, 100) == 0
+    assert lib.dg_repack_q8_0_tiles(A16, A16, 4, 100, None) == 3
+    assert lib.dg_repack_q8_0_tiles(P(0x1001), A16, 4, 256, None) == 2
+    assert lib.dg_repack_q8_0_tiles(None, A16, 4, 256, None) == 1
+    g = lib.dg_gemv_q8_0_tiles
+    g.argtypes = [P, P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, P, ctypes.c_size_t, P]
+    assert g(A16, A16, A16, 4, 100, 1, None, 0, None) == 3
+    assert g(A16, A16, A16, 4096, 14336, 24, None, 0, None) == 4   # Q8_0 splits K here, Q4_0 does not
+    w = lib.dg_gemv_q8_0_tiles_workspace_bytes
+    w.restype = ctypes.c_size_t
+    w.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    assert w(4096, 14336, 24) > 0
+    w4 = lib.dg_gemv_q4_0_tiles_workspace_bytes
+    w4.restype = ctypes.c_size_t
+    w4.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int]
+    assert w4(4096, 14336, 24) == 0
+    assert g(A2, A16, A16, 4, 256, 1, None, 0, None) == 2
+    assert g(None, None, None, 0, 256, 3, None, 0, None) == 0

@@ -20,8 +20,8 @@ pytestmark = pytest.mark.gpu
 TOL = 1e-3   # per-row floored relative error vs the oracle
 TICKET_BYTES = 64 * 1024   # the workspace's ticket counters (include/decodegemv.h)
 
-# (RT, KW, D) configurations the library builds; unroll = KP*1000000 +
-# RT*10000 + KW*100 + D
+# (RT, KW, D) configurations the library builds; unroll = CS*100000000 +
+# KP*1000000 + RT*10000 + KW*100 + D
 BUILT = [(1, 4, 2), (1, 4, 4), (1, 8, 2), (1, 8, 4), (1, 16, 2), (2, 4, 2), (2, 4, 4), (2, 2, 4), (2, 8, 2),
          (4, 1, 4), (4, 2, 2), (4, 2, 4), (4, 4, 2), (4, 4, 4)]
 FORMATS = ["q4_0", "q8_0"]
@@ -32,8 +32,8 @@ def built(fmt, cfg, M):
     return not (fmt == "q8_0" and M > 16 and cfg[0] * cfg[1] == 16 and cfg[2] == 4)
 
 
-def unroll(kp, rt, kw, d):
-    return kp * 1000000 + rt * 10000 + kw * 100 + d
+def unroll(kp, rt, kw, d, cs=0):
+    return cs * 100000000 + kp * 1000000 + rt * 10000 + kw * 100 + d
 
 
 def tiled_layout_q8(Wq, N, K):
@@ -107,8 +107,8 @@ def _gpu(dg, dev, fmt, Wt, Xq, N, K, M, launch=None, ws=None):
     X = torch.from_numpy(np.ascontiguousarray(Xq).reshape(-1)).to(dev)
     Y = torch.full((max(M, 1), max(N, 1)), float("nan"), dtype=torch.float32, device=dev)
     if ws is None:   # the default launch's workspace, and room for every override at the small shapes
-        ws = torch.zeros(max(dg.dg_gemv_q4_0_tiles_workspace_bytes(N, K, M), 1 << 23), dtype=torch.uint8,
-                         device=dev)
+        need = (dg.dg_gemv_q4_0_tiles_workspace_bytes if fmt == "q4_0" else dg.dg_gemv_q8_0_tiles_workspace_bytes)
+        ws = torch.zeros(max(need(N, K, M), 1 << 23), dtype=torch.uint8, device=dev)
     (dg.dg_gemv_q4_0_tiles if fmt == "q4_0" else dg.dg_gemv_q8_0_tiles)(Wt, X, Y, N, K, M, ws=ws, launch=launch)
     torch.cuda.synchronize()
     return Y[:M, :N].cpu().numpy().astype(np.float64)
@@ -156,6 +156,38 @@ def test_tiles_every_configuration(dg, dev, orc, fmt, cfg, kp, M):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("cfg", [(1, 8, 2), (2, 4, 2), (4, 2, 4)], ids=str)
+@pytest.mark.parametrize("cs", [2, 3, 5, 8])
+@pytest.mark.parametrize("M", [3, 9, 16, 17, 24])
+def test_tiles_column_slices(dg, dev, orc, fmt, cfg, cs, M):
+    """Columns split over CS workgroups per row group (ceil(M / CS) each, the
+    last slice shorter): row groups padded to whole blocks of 8 (N = 200),
+    a K that leaves waves without a part (23 groups of 8 blocks).  A split
+    that would leave a slice empty is an argument error."""
+    N, K = 200, 5888
+    Wq, Xq = _operands(orc, fmt, 650 + M, N, K, M)
+    Wt = _tiles(dg, dev, fmt, Wq, N, K)
+    if (cs - 1) * -(-M // cs) >= M:
+        with pytest.raises(dg.DGError):
+            _gpu(dg, dev, fmt, Wt, Xq, N, K, M, launch=dict(unroll=unroll(1, *cfg, cs=cs)))
+        return
+    got = _gpu(dg, dev, fmt, Wt, Xq, N, K, M, launch=dict(unroll=unroll(1, *cfg, cs=cs)))
+    assert_close(got, _ref(orc, fmt, Wq, Xq, N, K, M), TOL, f"{fmt} {cfg} CS={cs} M={M}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("cs,M", [(2, 10), (2, 16), (2, 17), (3, 24), (3, 20)])
+def test_tiles_column_slices_long_rows(dg, dev, orc, fmt, cs, M):
+    """A 4096 x 14336 matrix, whose columns fit a workgroup's LDS only in
+    slices, with no workspace."""
+    N, K = 4096, 14336
+    Wq, Xq = _operands(orc, fmt, 660 + M, N, K, M)
+    got = _gpu(dg, dev, fmt, _tiles(dg, dev, fmt, Wq, N, K), Xq, N, K, M,
+               launch=dict(unroll=unroll(1, 2, 4, 2, cs=cs)))
+    assert_close(got, _ref(orc, fmt, Wq, Xq, N, K, M, threads=0), TOL, f"{fmt} CS={cs} M={M}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("N,K", [(4096, 4096), (1024, 4096), (14336, 4096), (4096, 14336)])
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 12, 16, 17, 24])
 def test_tiles_decoder_layer_shapes_all_rows(dg, dev, orc, fmt, N, K, M):
@@ -191,30 +223,31 @@ def test_tiles_workspace_left_zero_and_calls_repeat_bit_for_bit(dg, dev, orc):
     repeated calls give identical bits, and calls of other shapes and the
     other format on the same workspace in between change nothing."""
     import torch
-    N, K, M = 4096, 14336, 16
-    need = dg.dg_gemv_q4_0_tiles_workspace_bytes(N, K, M)
-    assert need > 0   # this shape splits K
-    ws = torch.zeros(need, dtype=torch.uint8, device=dev)
-    Wq, Xq = _operands(orc, "q4_0", 640, N, K, M)
-    Wt = _tiles(dg, dev, "q4_0", Wq, N, K)
-    a = _gpu(dg, dev, "q4_0", Wt, Xq, N, K, M, ws=ws)
+    N, K, M = 4096, 14336, 24
+    need = dg.dg_gemv_q8_0_tiles_workspace_bytes(N, K, M)
+    assert need > 0   # Q8_0 splits K at this shape by default
+    ws = torch.zeros(8 << 20, dtype=torch.uint8, device=dev)
+    Wq, Xq = _operands(orc, "q8_0", 640, N, K, M)
+    Wt = _tiles(dg, dev, "q8_0", Wq, N, K)
+    a = _gpu(dg, dev, "q8_0", Wt, Xq, N, K, M, ws=ws)
     assert not torch.any(ws[:TICKET_BYTES] != 0).item()
-    b = _gpu(dg, dev, "q4_0", Wt, Xq, N, K, M, ws=ws)
+    b = _gpu(dg, dev, "q8_0", Wt, Xq, N, K, M, ws=ws)
     assert np.array_equal(a, b)
-    assert_close(a, _ref(orc, "q4_0", Wq, Xq, N, K, M, threads=0), TOL, "first call")
+    assert_close(a, _ref(orc, "q8_0", Wq, Xq, N, K, M, threads=0), TOL, "first call")
     n2, k2, m2 = 1000, 14336, 5   # K split eight ways: its partial sums cover more of the workspace
     for fmt in FORMATS:
         Wq2, Xq2 = _operands(orc, fmt, 641, n2, k2, m2)
-        c = _gpu(dg, dev, fmt, _tiles(dg, dev, fmt, Wq2, n2, k2), Xq2, n2, k2, m2, ws=ws)
+        c = _gpu(dg, dev, fmt, _tiles(dg, dev, fmt, Wq2, n2, k2), Xq2, n2, k2, m2, ws=ws,
+                 launch=dict(unroll=unroll(8, 4, 2, 2)))
         assert_close(c, _ref(orc, fmt, Wq2, Xq2, n2, k2, m2, threads=0), TOL, f"{fmt} smaller second call")
         assert not torch.any(ws[:TICKET_BYTES] != 0).item()
-    d = _gpu(dg, dev, "q4_0", Wt, Xq, N, K, M, ws=ws)   # the first shape again, after the others' partial sums
+    d = _gpu(dg, dev, "q8_0", Wt, Xq, N, K, M, ws=ws)   # the first shape again, after the others' partial sums
     assert np.array_equal(a, d)
 
 
 def test_tiles_argument_errors(dg, dev):
     import torch
-    N, K, M = 64, 14336, 16
+    N, K, M = 64, 28672, 24   # Q4_0 splits K at this shape by default
     lib = dg.raw()
     Wt = torch.zeros(dg.dg_q4_0_tiles_bytes(N, K), dtype=torch.uint8, device=dev)
     X = torch.zeros(M * K // 32 * 36, dtype=torch.uint8, device=dev)
@@ -227,6 +260,15 @@ def test_tiles_argument_errors(dg, dev):
     assert lib.dg_gemv_q4_0_tiles(P(Wt), P(X), P(Y), N, K, M, None, 0, None) == 4
     assert lib.dg_gemv_q4_0_tiles(P(Wt), P(X), P(Y), N, 4000, M, P(ws), need, None) == 3     # DG_ERR_SHAPE
     assert lib.dg_gemv_q4_0_tiles(P(Wt), P(X), P(Y), N, K, 25, P(ws), need, None) == 3
-    cfg = dg.dg_launch(0, 0, 0, unroll(2, 3, 3, 3))   # not built
-    assert lib.dg_gemv_q4_0_tiles_ex(P(Wt), P(X), P(Y), N, K, M, P(ws), need, cfg, None) == 6  # DG_ERR_ARG
+    for bad in (unroll(2, 3, 3, 3),          # not built
+                unroll(2, 2, 4, 2, cs=2),    # column slices with K split
+                unroll(1, 2, 4, 2, cs=9),    # more slices than allowed
+                unroll(1, 2, 4, 2, cs=3),    # 8 columns of rows this long do not fit the LDS
+                unroll(8, 4, 2, 2)):         # the default: fits
+        cfg = dg.dg_launch(0, 0, 0, bad)
+        rc = lib.dg_gemv_q4_0_tiles_ex(P(Wt), P(X), P(Y), N, K, M, P(ws), need, cfg, None)
+        assert rc == (0 if bad == unroll(8, 4, 2, 2) else 6), bad   # DG_ERR_ARG
+    for m, bad in ((2, unroll(1, 2, 4, 2, cs=3)), (1, unroll(1, 2, 4, 2, cs=2))):   # an empty slice
+        cfg = dg.dg_launch(0, 0, 0, bad)
+        assert lib.dg_gemv_q4_0_tiles_ex(P(Wt), P(X), P(Y), N, K, m, P(ws), need, cfg, None) == 6
     torch.cuda.synchronize()
