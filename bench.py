@@ -1296,6 +1296,42 @@ def profile_small_m_tiles(args):
         torch.cuda.empty_cache()
 
 
+# (format, M, label, unroll) for --profile-tiles-slices at 4096x14336: the
+# column slices against a K split and against more slices
+TILES_SLICE_CASES = [("q8_0", 20, "CS=2 RT=2 KW=4 D=2", 201020402), ("q8_0", 24, "KP=4 RT=4 KW=2 D=2", 4040202),
+                     ("q8_0", 24, "CS=3 RT=4 KW=2 D=2", 301040202), ("q8_0", 24, "CS=4 RT=4 KW=2 D=2", 401040202),
+                     ("q4_0", 24, "CS=3 RT=4 KW=2 D=4", 301040204), ("q4_0", 16, "CS=2 RT=2 KW=4 D=2", 201020402),
+                     ("q4_0", 16, "KP=2 RT=2 KW=4 D=2", 2020402), ("q4_0", 16, "CS=4 RT=2 KW=4 D=2", 401020402)]
+
+
+def profile_tiles_slices(args):
+    """Three eager launches of each TILES_SLICE_CASES entry at 4096x14336, in
+    that order, for L2 hit and HBM fetch counters (rocprofv3 --pmc); a large
+    fill between launches leaves no weights in the caches."""
+    import memory_bound_decode_gemv_amd as dg
+    torch = _torch()
+    N, K = 4096, 14336
+    ws = torch.zeros(TILES_WS_BYTES, dtype=torch.uint8, device="cuda")
+    Wt = {}
+    for fmt in ("q4_0", "q8_0"):
+        q8 = fmt == "q8_0"
+        Wq = (q8_0_copies if q8 else q4_copies)(3, N, K, 1)[0]
+        Wt[fmt] = torch.empty((dg.dg_q8_0_tiles_bytes if q8 else dg.dg_q4_0_tiles_bytes)(N, K), dtype=torch.uint8,
+                              device="cuda")
+        (dg.dg_repack_q8_0_tiles if q8 else dg.dg_repack_q4_0_tiles)(Wq, Wt[fmt], N, K)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for (fmt, M, label, unroll) in TILES_SLICE_CASES:
+        Xq = q8_columns(3, K, M)
+        Y = torch.empty(M * N, dtype=torch.float32, device="cuda")
+        gemv = dg.dg_gemv_q8_0_tiles if fmt == "q8_0" else dg.dg_gemv_q4_0_tiles
+        for _ in range(3):
+            flush.zero_()
+            gemv(Wt[fmt], Xq, Y, N, K, M, ws=ws, launch=dict(unroll=unroll))
+        torch.cuda.synchronize()
+        log(f"[profile-tiles-slices] {fmt} {N}x{K} M={M} {label}: 3 launches")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -1309,6 +1345,9 @@ def main():
                     help="graphs of back-to-back launches for a kernel-trace split of the per-launch cost")
     ap.add_argument("--profile-small-m-tiles", action="store_true",
                     help="launch the tiled small-batch Q4_0 GEMV eagerly (for rocprofv3 --pmc)")
+    ap.add_argument("--profile-tiles-slices", action="store_true",
+                    help="launch the tiled GEMV at 4096x14336 with column slices, K splits and more slices (for "
+                         "rocprofv3 --pmc)")
     ap.add_argument("--profile-small-m", action="store_true",
                     help="launch the small-batch Q4_0 GEMV eagerly on the decoder shapes (for rocprofv3 --pmc)")
     ap.add_argument("--only", default=None,
@@ -1336,6 +1375,8 @@ def main():
         profile_small_m(args)
     elif args.profile_small_m_tiles:
         profile_small_m_tiles(args)
+    elif args.profile_tiles_slices:
+        profile_tiles_slices(args)
     elif args.profile_launch_cost:
         profile_launch_cost(args)
     elif args.suite:

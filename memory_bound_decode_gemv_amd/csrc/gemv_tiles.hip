@@ -347,21 +347,22 @@ k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* _
     const int S = K >> 8;
     const int nblk = K >> 5;
     const int T = (N + 15) >> 4;
-    int grp, kp;
+    int grp, kp, cs = 0;
     if (CS == 1) {
         grp = (int)blockIdx.x / KP;
         kp = (int)blockIdx.x - grp * KP;
     } else {
-        // Column split (KP = 1): the CS workgroups of a row group take Mh =
-        // ceil(M / CS) columns each and sit 8 workgroup ids apart, so the
+        // Column slices: the CS workgroups of a (row group, K range) unit take
+        // Mh = ceil(M / CS) columns each and sit 8 workgroup ids apart, so the
         // round-robin placement puts them on one XCD, whose L2 serves their
-        // shared weight rows once.  Row groups are padded to whole blocks of 8.
+        // shared weight rows once.  Units are padded to whole blocks of 8.
         const int b = (int)blockIdx.x;
         const int hi = b >> 3;
-        const int cs = hi % CS;
-        grp = (hi / CS) * 8 + (b & 7);
-        kp = 0;
-        if (grp >= groups) return;   // workgroup-uniform, before any barrier
+        cs = hi % CS;
+        const int u = (hi / CS) * 8 + (b & 7);
+        if (u >= groups * KP) return;   // workgroup-uniform, before any barrier
+        grp = u / KP;
+        kp = u - grp * KP;
         const int Mh = (M + CS - 1) / CS;
         const int mc0 = cs * Mh;
         Xq += (size_t)mc0 * (size_t)(K >> 5) * kQ81Bytes;
@@ -492,7 +493,8 @@ k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* _
     // Agent-scope release and acquire fences (an L2 write-back and an L2
     // invalidate on this chip, both of whole caches) measured 15-140 us per
     // call, and are not needed when every shared access is atomic.
-    float* const mine = reinterpret_cast<float*>(part + (((size_t)grp * KP + kp) * RT + rt) * NA * kWave);
+    const int slot = grp * CS + cs;   // this slice's ticket counter and partial sums
+    float* const mine = reinterpret_cast<float*>(part + (((size_t)slot * KP + kp) * RT + rt) * NA * kWave);
     if (kw == 0) {
 #pragma unroll
         for (int a = 0; a < NA; ++a)
@@ -504,7 +506,7 @@ k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* _
     __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's partial sums are stored
     __syncthreads();
     if (threadIdx.x == 0)
-        last_ticket = __hip_atomic_fetch_add(tickets + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        last_ticket = __hip_atomic_fetch_add(tickets + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                       (uint32_t)(KP - 1);
     __syncthreads();
     if (!last_ticket) return;   // workgroup-uniform
@@ -512,7 +514,7 @@ k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* _
         f32x4 sum[NA];
         for (int k2 = 0; k2 < KP; ++k2) {
             const float* const src =
-                reinterpret_cast<const float*>(part + (((size_t)grp * KP + k2) * RT + rt) * NA * kWave);
+                reinterpret_cast<const float*>(part + (((size_t)slot * KP + k2) * RT + rt) * NA * kWave);
 #pragma unroll
             for (int a = 0; a < NA; ++a) {
                 f32x4 v = acc[a];
@@ -531,7 +533,7 @@ k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* _
         }
         store_tile<TF, MP>(sum, Y, N, M, t, g, rn);
     }
-    if (threadIdx.x == 0) __hip_atomic_store(tickets + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) __hip_atomic_store(tickets + slot, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // f32x4 accumulators per lane for M columns (TileSet<MP>::kNA).
@@ -540,7 +542,7 @@ int tiles_accumulators(int M) { return M <= 8 ? 1 : M <= 16 ? 2 : 3; }
 // A resolved configuration of the tiled kernel.
 struct TilesPlan {
     int RT, KW, D, KP;   // row tiles and K parts per workgroup, groups in flight per wave, K ranges
-    int CS;              // column slices per row group (KP = 1 when CS > 1)
+    int CS;              // column slices per row group and K range
     int Mh;              // columns per workgroup: ceil(M / CS)
     int spw;             // groups per range
     int cs_slots;        // LDS column stride, 16-byte slots (odd)
@@ -570,7 +572,7 @@ bool tiles_built(int RT, int KW, int D) {
 bool tiles_plan(int N, int K, int M, int RT, int KW, int D, int KP, int CS, TilesPlan& p) {
     const int S = K >> 8;
     if (S < 1 || KP < 1 || KP > kTilesMaxKP || !tiles_built(RT, KW, D)) return false;
-    if (CS < 1 || CS > kTilesMaxCS || (CS > 1 && KP != 1)) return false;
+    if (CS < 1 || CS > kTilesMaxCS) return false;
     p.RT = RT;
     p.KW = KW;
     p.D = D;
@@ -587,7 +589,7 @@ bool tiles_plan(int N, int K, int M, int RT, int KW, int D, int KP, int CS, Tile
     const size_t red = (size_t)RT * KW * NA * kWave * 16;
     p.lds = act > red ? act : red;
     p.groups = ((N + 15) / 16 + RT - 1) / RT;
-    if (p.KP > 1 && p.groups > kTicketSlots) return false;   // one ticket counter per row group
+    if (p.KP > 1 && p.groups * CS > kTicketSlots) return false;   // one ticket counter per row group and slice
     // LDS of one workgroup; the quotient by the column stride (a multiply-high
     // by ceil(2^32 / stride)) is exact for strides below 2^14 and slots below 2^18
     return p.lds <= kTilesMaxLds && p.cs_slots < (1 << 14) && M * p.cs_slots + kWave < (1 << 18);
@@ -595,22 +597,24 @@ bool tiles_plan(int N, int K, int M, int RT, int KW, int D, int KP, int CS, Tile
 
 // Default configuration, from sweeps of every built configuration on MI355X
 // over the four decoder-layer shapes (1024, 4096 and 14336 rows of 4096
-// columns, 4096 rows of 14336) at M = 1..24, K split 1, 2 or 4 ways or the
-// columns in 2..8 slices.
+// columns, 4096 rows of 14336) at M = 1..24, with K split 1..4 ways, the
+// columns in 2..8 slices, and both.
 //
-// Column slices first.  Below 128 row tiles a row group per workgroup leaves
-// most of the chip idle: M / 2 slices, at most 4, 8 waves each over K.  Below
-// 512 row tiles and past 8 columns, 2 slices of 4 waves.  Where the columns
-// of whole rows do not fit a workgroup's LDS, 2 slices (Q4_0: 3 when 2 do not
-// fit) in place of a K split: the slices read each weight row once from HBM
-// and once more from their XCD's L2, and exchange nothing.  More than 2
-// slices on the larger shapes lose that L2 hit rate (measured 40-100% slower
-// at 3 to 8).  A slice whose columns need more than half the LDS (one
-// workgroup per CU) gets two row tiles per workgroup (four over two K parts,
-// four groups deep, for 3 slices).  Otherwise K is split over workgroups
-// only when the columns still do not fit (the ticket exchange costs 1.5-2.5
-// us per call): ranges as long as fit, two row tiles per workgroup over 4
-// waves each for two ranges and four tiles over 2 waves for more.  Without
+// Column slices first.  Below 128 row tiles one workgroup per row group
+// leaves most of the chip idle: M / 2 slices, at most 4, of 8 waves over K.
+// Below 512 row tiles and past 8 columns, 2 slices of 4 waves.  Where the
+// columns of whole rows do not fit a workgroup's LDS, 2 slices (Q4_0: 3 when
+// 2 do not fit) in place of a K split: the slices of a row group read each
+// weight byte once from HBM and again from their XCD's L2, and exchange
+// nothing.  More slices than that on the larger shapes were 40-100% slower
+// (3 to 8 slices) with the same HBM traffic: every slice still moves every
+// weight byte of its rows into its CU, and the waves are latency-bound.  A
+// slice whose columns take more than half the LDS (one workgroup per CU)
+// gets two row tiles per workgroup (four over two K parts, four groups deep,
+// for 3 slices).  When even the slices do not fit, K is split over
+// workgroups as well (the ticket exchange costs 1.5-2.5 us per call), in 2
+// column slices: ranges as long as fit, four row tiles per workgroup over 2
+// waves (two over 4 when a row group has only two workgroups).  Without
 // slices or a split: from 512 row tiles on, two row tiles over K in 2 parts,
 // four groups deep, to 8 columns, four row tiles over 4 parts past 8; below
 // 512, one row tile over K in 8 parts.  Two groups in flight per wave unless
@@ -652,11 +656,12 @@ void tiles_default(bool q8, int N, int K, int M, int& RT, int& KW, int& D, int& 
         }
         return;
     }
-    CS = 1;
+    CS = M >= 2 ? 2 : 1;
+    const int Mh = (M + CS - 1) / CS;
     const size_t fit = 150 * 1024;   // the columns of one range in LDS
-    while (KP < kTilesMaxKP && KP < S && (size_t)M * ((S + KP - 1) / KP) * kGroupSlots * 16 > fit) KP *= 2;
-    RT = KP >= 4 ? 4 : 2;
-    KW = KP >= 4 ? 2 : 4;
+    while (KP < kTilesMaxKP && KP < S && (size_t)Mh * ((S + KP - 1) / KP) * kGroupSlots * 16 > fit) KP *= 2;
+    RT = KP * CS >= 4 ? 4 : 2;
+    KW = KP * CS >= 4 ? 2 : 4;
 }
 
 template <class TF, int MP, int RT, int KW, int D>
@@ -665,7 +670,7 @@ hipError_t launch_tiles_cfg(const TilesPlan& p, const void* Wt, const void* Xq, 
     uint32_t* tickets = reinterpret_cast<uint32_t*>(ws);
     f32x4* part = reinterpret_cast<f32x4*>(reinterpret_cast<uint8_t*>(ws) + kTicketBytes);
     const uint32_t magic = (uint32_t)((((uint64_t)1 << 32) + (uint64_t)p.cs_slots - 1) / (uint64_t)p.cs_slots);
-    const int grid = p.CS == 1 ? p.groups * p.KP : (p.groups + 7) / 8 * 8 * p.CS;
+    const int grid = p.CS == 1 ? p.groups * p.KP : (p.groups * p.KP + 7) / 8 * 8 * p.CS;
     hipLaunchKernelGGL((k_tiles<TF, MP, RT, KW, D>), dim3(grid), dim3(64 * RT * KW), p.lds, s, (const uint8_t*)Wt,
                        (const uint8_t*)Xq, Y, tickets, part, N, K, M, p.KP, p.spw, p.cs_slots, magic, p.CS,
                        p.groups);
@@ -718,10 +723,10 @@ hipError_t launch_tiles_pack(bool q8, const void* Wq, void* Wt, int64_t N, int64
 }
 
 // The workspace a configuration needs: the ticket counters (64 KiB), then KP x
-// groups x RT x NT x 1 KiB of partial tile sums; none when KP = 1.
-static size_t tiles_ws_bytes(const TilesPlan& p, int M) {
+// groups x CS x RT x NA x 1 KiB of partial tile sums; none when KP = 1.
+static size_t tiles_ws_bytes(const TilesPlan& p) {
     if (p.KP == 1) return 0;
-    return kTicketBytes + (size_t)p.KP * p.groups * p.RT * tiles_accumulators(M) * 1024;   // CS = 1 here
+    return kTicketBytes + (size_t)p.KP * p.groups * p.CS * p.RT * tiles_accumulators(p.Mh) * 1024;
 }
 
 // unroll = CS * 100000000 + KP * 1000000 + RT * 10000 + KW * 100 + D (0: the
@@ -744,7 +749,7 @@ static bool tiles_resolve(bool q8, int N, int K, int M, int unroll, TilesPlan& p
 bool tiles_config(bool q8, int N, int K, int M, int unroll, size_t* ws_bytes) {
     TilesPlan p;
     if (N <= 0 || K <= 0 || M <= 0 || M > 24 || !tiles_resolve(q8, N, K, M, unroll, p)) return false;
-    *ws_bytes = tiles_ws_bytes(p, M);
+    *ws_bytes = tiles_ws_bytes(p);
     return true;
 }
 

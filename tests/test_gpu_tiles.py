@@ -158,21 +158,23 @@ def test_tiles_every_configuration(dg, dev, orc, fmt, cfg, kp, M):
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("cfg", [(1, 8, 2), (2, 4, 2), (4, 2, 4)], ids=str)
 @pytest.mark.parametrize("cs", [2, 3, 5, 8])
+@pytest.mark.parametrize("kp", [1, 3])
 @pytest.mark.parametrize("M", [3, 9, 16, 17, 24])
-def test_tiles_column_slices(dg, dev, orc, fmt, cfg, cs, M):
-    """Columns split over CS workgroups per row group (ceil(M / CS) each, the
-    last slice shorter): row groups padded to whole blocks of 8 (N = 200),
-    a K that leaves waves without a part (23 groups of 8 blocks).  A split
-    that would leave a slice empty is an argument error."""
+def test_tiles_column_slices(dg, dev, orc, fmt, cfg, cs, kp, M):
+    """Columns split over CS workgroups per row group and K range (ceil(M /
+    CS) each, the last slice shorter), K in 1 or 3 ranges: units padded to
+    whole blocks of 8 (N = 200), a K that leaves waves without a part (23
+    groups of 8 blocks).  A split that would leave a slice empty is an
+    argument error."""
     N, K = 200, 5888
     Wq, Xq = _operands(orc, fmt, 650 + M, N, K, M)
     Wt = _tiles(dg, dev, fmt, Wq, N, K)
     if (cs - 1) * -(-M // cs) >= M:
         with pytest.raises(dg.DGError):
-            _gpu(dg, dev, fmt, Wt, Xq, N, K, M, launch=dict(unroll=unroll(1, *cfg, cs=cs)))
+            _gpu(dg, dev, fmt, Wt, Xq, N, K, M, launch=dict(unroll=unroll(kp, *cfg, cs=cs)))
         return
-    got = _gpu(dg, dev, fmt, Wt, Xq, N, K, M, launch=dict(unroll=unroll(1, *cfg, cs=cs)))
-    assert_close(got, _ref(orc, fmt, Wq, Xq, N, K, M), TOL, f"{fmt} {cfg} CS={cs} M={M}")
+    got = _gpu(dg, dev, fmt, Wt, Xq, N, K, M, launch=dict(unroll=unroll(kp, *cfg, cs=cs)))
+    assert_close(got, _ref(orc, fmt, Wq, Xq, N, K, M), TOL, f"{fmt} {cfg} CS={cs} KP={kp} M={M}")
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
@@ -237,10 +239,12 @@ def test_tiles_workspace_left_zero_and_calls_repeat_bit_for_bit(dg, dev, orc):
     n2, k2, m2 = 1000, 14336, 5   # K split eight ways: its partial sums cover more of the workspace
     for fmt in FORMATS:
         Wq2, Xq2 = _operands(orc, fmt, 641, n2, k2, m2)
-        c = _gpu(dg, dev, fmt, _tiles(dg, dev, fmt, Wq2, n2, k2), Xq2, n2, k2, m2, ws=ws,
-                 launch=dict(unroll=unroll(8, 4, 2, 2)))
-        assert_close(c, _ref(orc, fmt, Wq2, Xq2, n2, k2, m2, threads=0), TOL, f"{fmt} smaller second call")
-        assert not torch.any(ws[:TICKET_BYTES] != 0).item()
+        Wt2 = _tiles(dg, dev, fmt, Wq2, n2, k2)
+        ref2 = _ref(orc, fmt, Wq2, Xq2, n2, k2, m2, threads=0)
+        for u in (unroll(8, 4, 2, 2), unroll(4, 2, 4, 2, cs=2)):   # the second: a counter per row group and slice
+            c = _gpu(dg, dev, fmt, Wt2, Xq2, n2, k2, m2, ws=ws, launch=dict(unroll=u))
+            assert_close(c, ref2, TOL, f"{fmt} smaller second call {u}")
+            assert not torch.any(ws[:TICKET_BYTES] != 0).item()
     d = _gpu(dg, dev, "q8_0", Wt, Xq, N, K, M, ws=ws)   # the first shape again, after the others' partial sums
     assert np.array_equal(a, d)
 
@@ -261,13 +265,14 @@ def test_tiles_argument_errors(dg, dev):
     assert lib.dg_gemv_q4_0_tiles(P(Wt), P(X), P(Y), N, 4000, M, P(ws), need, None) == 3     # DG_ERR_SHAPE
     assert lib.dg_gemv_q4_0_tiles(P(Wt), P(X), P(Y), N, K, 25, P(ws), need, None) == 3
     for bad in (unroll(2, 3, 3, 3),          # not built
-                unroll(2, 2, 4, 2, cs=2),    # column slices with K split
                 unroll(1, 2, 4, 2, cs=9),    # more slices than allowed
                 unroll(1, 2, 4, 2, cs=3),    # 8 columns of rows this long do not fit the LDS
-                unroll(8, 4, 2, 2)):         # the default: fits
+                unroll(4, 4, 2, 2, cs=2)):   # the default here: fits
         cfg = dg.dg_launch(0, 0, 0, bad)
         rc = lib.dg_gemv_q4_0_tiles_ex(P(Wt), P(X), P(Y), N, K, M, P(ws), need, cfg, None)
-        assert rc == (0 if bad == unroll(8, 4, 2, 2) else 6), bad   # DG_ERR_ARG
+        assert rc == (0 if bad == unroll(4, 4, 2, 2, cs=2) else 6), bad   # DG_ERR_ARG
+    cfg = dg.dg_launch(0, 0, 0, unroll(8, 4, 2, 2))   # K in 8 ranges, no slices: more workspace than the default's
+    assert lib.dg_gemv_q4_0_tiles_ex(P(Wt), P(X), P(Y), N, K, M, P(ws), need, cfg, None) == 4
     for m, bad in ((2, unroll(1, 2, 4, 2, cs=3)), (1, unroll(1, 2, 4, 2, cs=2))):   # an empty slice
         cfg = dg.dg_launch(0, 0, 0, bad)
         assert lib.dg_gemv_q4_0_tiles_ex(P(Wt), P(X), P(Y), N, K, m, P(ws), need, cfg, None) == 6
