@@ -848,8 +848,8 @@ TILES_WS_BYTES = 40 << 20   # enough for every configuration of the four 8B shap
 def suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=True, shapes=None, ms=None, fmt="q4_0"):
     """The Q4_0 (or Q8_0) small-M sweep over the four 8B shapes with the
     weights in 16-row tiles (dg_repack_*_tiles once, outside the timing), every
-    M, and at the named M every built configuration with K split 1, 2 or 4 ways
-    or the columns split 2 or 3 ways."""
+    M, and at the named M every built configuration with K split 1, 2 or 4 ways,
+    the columns split 2 or 3 ways, or both split 2 ways."""
     q8 = fmt == "q8_0"
     nbytes = bytes_q8_0 if q8 else bytes_q4
     tiles_bytes = dg.dg_q8_0_tiles_bytes if q8 else dg.dg_q4_0_tiles_bytes
@@ -878,7 +878,7 @@ def suite_q4_tiles(dg, torch, emit, ceil_gbps, sweep=True, shapes=None, ms=None,
                         variant="default", columns_per_s=round(cps, 1), change_vs_prev_M=dip))
             if sweep and M in (1, 8, 16, 24):
                 for (rt, kw, d) in TILES_BUILT:
-                    for (kp, cs) in ((1, 1), (2, 1), (4, 1), (1, 2), (1, 3)):
+                    for (kp, cs) in ((1, 1), (2, 1), (4, 1), (1, 2), (1, 3), (2, 2)):
                         launch = dict(unroll=cs * 100000000 + kp * 1000000 + rt * 10000 + kw * 100 + d)
                         calls = [(lambda c=c, launch=launch: gemv(Wts[c % nc], Xq, Y, N, K, M, ws=ws,
                                                                   launch=launch))

@@ -222,14 +222,17 @@ dg_status dg_gemv_q4_0_f32(const void* Wq, const float* x, float* Y, void* Xq,
  *   aligned) -> Wt (device, dg_q4_0_tiles_bytes(N, K) bytes, 16-byte
  *   aligned); K % 256 == 0, K <= 2^26, 0 <= N < 2^31.  Wq is unchanged.
  * dg_gemv_q4_0_tiles: as dg_gemv_q4_0 with Wt in place of Wq.  Every
- *   workgroup copies the activation columns of its range of K into LDS once;
- *   when K is split over several workgroups of one row group (large K, or
- *   too few row tiles for every CU), their partial sums meet in the caller's
- *   workspace:
+ *   workgroup copies its activation columns over its range of K into LDS
+ *   once.  The columns may be split over several workgroups of one row group
+ *   (column slices: each computes its own columns, nothing is exchanged);
+ *   when K is split over several workgroups of one row group and slice (rows
+ *   too long for the columns to fit a workgroup's LDS), their partial sums
+ *   meet in the caller's workspace:
  *   ws        device, ws_bytes >= dg_gemv_q4_0_tiles_workspace_bytes(N, K,
  *             M) (0: ws may be NULL), 16-byte aligned.  Its first 64 KiB
- *             hold ticket counters (one per row group, at the same place for
- *             every shape), which must be zero before the first call: fill
+ *             hold ticket counters (one per row group and column slice, at
+ *             the same place for every shape), which must be zero before the
+ *             first call: fill
  *             the workspace with zeros once after allocating it.  Every call
  *             leaves them zero again, so one workspace serves calls of any
  *             shapes in turn; calls that may overlap in time need workspaces
@@ -564,14 +567,16 @@ dg_status dg_gemv_q8_0_ex(const void* Wq, const void* Xq, float* Y, int64_t N, i
 dg_status dg_gemv_nf4_ex(const void* codes, const float* absmax, const float* table, const void* x, float* y,
                          int64_t N, int64_t K, int B, const dg_launch* cfg, dg_stream stream);
 /* dg_gemv_q4_0_tiles with a launch override: variant, grid and block 0;
- * unroll = KP*1000000 + RT*10000 + KW*100 + D selects KP ranges of K per row
- * group, RT row tiles and KW parts of the range per workgroup (RT*KW waves)
- * and D groups of 8 blocks in flight per wave (built: (RT, KW, D) in (1,4,2),
- * (1,4,4), (1,8,2), (1,8,4), (1,16,2), (2,4,2), (2,4,4), (2,2,4), (2,8,2),
- * (4,1,4), (4,2,2), (4,2,4), (4,4,2), (4,4,4); KP 1..16).  The workspace
- * this configuration needs is checked against ws_bytes (DG_ERR_WORKSPACE);
- * a configuration not built or whose columns do not fit a workgroup's LDS
- * gives DG_ERR_ARG. */
+ * unroll = CS*100000000 + KP*1000000 + RT*10000 + KW*100 + D selects CS
+ * column slices (ceil(M/CS) columns each, none empty; CS 0 means 1) and KP
+ * ranges of K per row group, RT row tiles and KW parts of the range per
+ * workgroup (RT*KW waves) and D groups of 8 blocks in flight per wave
+ * (built: (RT, KW, D) in (1,4,2), (1,4,4), (1,8,2), (1,8,4), (1,16,2),
+ * (2,4,2), (2,4,4), (2,2,4), (2,8,2), (4,1,4), (4,2,2), (4,2,4), (4,4,2),
+ * (4,4,4); CS 1..8; KP 1..16).  The workspace this configuration needs is
+ * checked against ws_bytes (DG_ERR_WORKSPACE); a configuration not built,
+ * with an empty slice, or whose columns do not fit a workgroup's LDS gives
+ * DG_ERR_ARG. */
 dg_status dg_gemv_q4_0_tiles_ex(const void* Wt, const void* Xq, float* Y, int64_t N, int64_t K, int M,
                                 void* ws, size_t ws_bytes, const dg_launch* cfg, dg_stream stream);
 /* dg_gemv_q8_0_tiles with a launch override, as dg_gemv_q4_0_tiles_ex. */
