@@ -573,7 +573,9 @@ dg_status dg_gemv_nf4_ex(const void* codes, const float* absmax, const float* ta
  * workgroup (RT*KW waves) and D groups of 8 blocks in flight per wave
  * (built: (RT, KW, D) in (1,4,2), (1,4,4), (1,8,2), (1,8,4), (1,16,2),
  * (2,4,2), (2,4,4), (2,2,4), (2,8,2), (4,1,4), (4,2,2), (4,2,4), (4,4,2),
- * (4,4,4); CS 1..8; KP 1..16).  The workspace this configuration needs is
+ * (4,4,4); CS 1..8; KP 1..16; D + 10 issues the first D groups' weight
+ * loads before waiting for the column copies, an earlier order kept for
+ * measurements).  The workspace this configuration needs is
  * checked against ws_bytes (DG_ERR_WORKSPACE); a configuration not built,
  * with an empty slice, or whose columns do not fit a workgroup's LDS gives
  * DG_ERR_ARG. */

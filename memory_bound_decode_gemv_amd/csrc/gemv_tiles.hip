@@ -333,7 +333,7 @@ template <class TF, int MP, int RT, int KW, int D>
 __global__ void __launch_bounds__(64 * RT * KW)
 k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* __restrict__ Y,
            uint32_t* __restrict__ tickets, f32x4* __restrict__ part, int N, int K, int M, int KP, int spw,
-           int cs_slots, uint32_t cs_magic, int CS, int groups) {
+           int cs_slots, uint32_t cs_magic, int CS, int groups, int pre) {
     using TS = TileSet<MP>;
     constexpr int NA = TS::kNA;
     constexpr int W = RT * KW;
@@ -381,14 +381,18 @@ k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* _
     const uint8_t* const wbase = Wt + ((size_t)tc * S + s0 + (cnt > 0 ? w0 : 0)) * kGroupBytes;
     const int last = cnt > 0 ? cnt - 1 : 0;
 
-    // (1) the activation columns of the range, copied into LDS by DMA, then
-    // (2) the first D groups of this wave's weights (past its part: its last
-    // group again, never used), both in flight together; then a wait for all
-    // of them.  The wait is the builtin (not inline asm) and waits for
-    // everything: only then does the compiler's own wait counting know that
-    // no copy into LDS is outstanding.  With copies possibly outstanding it
-    // treats the counter as out of order and waits for every load before
-    // each use (measured: vmcnt(0) at the top of every round of the loop).
+    // (1) the activation columns of the range, copied into LDS by DMA, and a
+    // wait for them; then (2) the first D groups of this wave's weights (past
+    // its part: its last group again, never used).  The wait is the builtin
+    // (not inline asm) and waits for everything: only then does the
+    // compiler's own wait counting know that no copy into LDS is outstanding.
+    // With copies possibly outstanding it treats the counter as out of order
+    // and waits for every load before each use (measured: vmcnt(0) at the top
+    // of every round of the loop).  Waiting for the copies before the first
+    // weight loads leaves those loads to the compiler's exact counting, so the
+    // first group's products start when that group has arrived; with the
+    // weights issued before the wait (pre = 0, kept for measurements) they
+    // start when all D have.  Measured 2-16% faster on most shapes.
     {
         const int used = ns * kGroupSlots;
         const int copies = (M * cs_slots + kWave - 1) / kWave;
@@ -407,11 +411,19 @@ k_tiles(const uint8_t* __restrict__ Wt, const uint8_t* __restrict__ Xq, float* _
         }
     }
     u32x4 wb[D][L];
+    if (pre) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the copies only
+        lds_barrier();                        // every other wave's copies have landed too
 #pragma unroll
-    for (int d = 0; d < D; ++d)
-        load_group<TF>(wbase + (size_t)(d < cnt ? d : last) * kGroupBytes, lane, rn, wb[d]);
-    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt at their maximum: no wait
-    lds_barrier();   // every other wave's copies have landed too
+        for (int d = 0; d < D; ++d)
+            load_group<TF>(wbase + (size_t)(d < cnt ? d : last) * kGroupBytes, lane, rn, wb[d]);
+    } else {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            load_group<TF>(wbase + (size_t)(d < cnt ? d : last) * kGroupBytes, lane, rn, wb[d]);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt at their maximum: no wait
+        lds_barrier();   // every other wave's copies have landed too
+    }
 
     // A operand offsets (columns past M: column M - 1 again, results dropped)
     ALanes al;
@@ -543,6 +555,7 @@ int tiles_accumulators(int M) { return M <= 8 ? 1 : M <= 16 ? 2 : 3; }
 struct TilesPlan {
     int RT, KW, D, KP;   // row tiles and K parts per workgroup, groups in flight per wave, K ranges
     int CS;              // column slices per row group and K range
+    int pre;
     int Mh;              // columns per workgroup: ceil(M / CS)
     int spw;             // groups per range
     int cs_slots;        // LDS column stride, 16-byte slots (odd)
@@ -602,23 +615,23 @@ bool tiles_plan(int N, int K, int M, int RT, int KW, int D, int KP, int CS, Tile
 //
 // Column slices first.  Below 128 row tiles one workgroup per row group
 // leaves most of the chip idle: M / 2 slices, at most 4, of 8 waves over K.
-// Below 512 row tiles and past 8 columns, 2 slices of 4 waves.  Where the
-// columns of whole rows do not fit a workgroup's LDS, 2 slices (Q4_0: 3 when
-// 2 do not fit) in place of a K split: the slices of a row group read each
-// weight byte once from HBM and again from their XCD's L2, and exchange
-// nothing.  More slices than that on the larger shapes were 40-100% slower
-// (3 to 8 slices) with the same HBM traffic: every slice still moves every
-// weight byte of its rows into its CU, and the waves are latency-bound.  A
-// slice whose columns take more than half the LDS (one workgroup per CU)
-// gets two row tiles per workgroup (four over two K parts, four groups deep,
-// for 3 slices).  When even the slices do not fit, K is split over
-// workgroups as well (the ticket exchange costs 1.5-2.5 us per call), in 2
-// column slices: ranges as long as fit, four row tiles per workgroup over 2
-// waves (two over 4 when a row group has only two workgroups).  Without
-// slices or a split: from 512 row tiles on, two row tiles over K in 2 parts,
-// four groups deep, to 8 columns, four row tiles over 4 parts past 8; below
-// 512, one row tile over K in 8 parts.  Two groups in flight per wave unless
-// stated.
+// Below 512 row tiles and past 8 columns, 2 slices.  Where the columns of
+// whole rows do not fit a workgroup's LDS, 2 slices (Q4_0: 3 when 2 do not
+// fit) in place of a K split: the slices of a row group read each weight
+// byte once from HBM and again from their XCD's L2, and exchange nothing.
+// More slices than that on the larger shapes were 40-100% slower (3 to 8
+// slices) with the same HBM traffic: every slice still moves every weight
+// byte of its rows into its CU, and the waves are latency-bound.  A slice
+// whose columns take more than half the LDS (one workgroup per CU) gets two
+// row tiles per workgroup over 8 K parts (Q8_0: 4), or four over 4 for 3
+// slices; other slices two row tiles over 4 parts (below 128 row tiles one
+// over 8).  When even the slices do not fit, K is split over workgroups as
+// well (the ticket exchange costs 1.5-2.5 us per call), in 2 column slices:
+// ranges as long as fit, four row tiles per workgroup over 2 waves (two over
+// 4 when a row group has only two workgroups).  Without slices or a split:
+// from 512 row tiles on, four row tiles over K in 2 parts to 8 columns and in
+// 4 beyond (Q8_0: two over 4 parts to 16 columns, four over 2 beyond);
+// below 512, one row tile over K in 8 parts.  Two groups in flight per wave.
 void tiles_default(bool q8, int N, int K, int M, int& RT, int& KW, int& D, int& KP, int& CS) {
     const int T = (N + 15) / 16;
     const int S = K >> 8;
@@ -637,19 +650,20 @@ void tiles_default(bool q8, int N, int K, int M, int& RT, int& KW, int& D, int& 
     if (CS > 1) {
         if (p.lds > kTilesMaxLds / 2) {
             RT = CS == 3 ? 4 : 2;
-            KW = CS == 3 ? 2 : 4;
-            D = CS == 3 ? 4 : 2;
-        } else {
+            KW = CS == 3 || q8 ? 4 : 8;
+        } else if (T < 128) {
             RT = 1;
-            KW = T < 128 ? 8 : 4;
+            KW = 8;
+        } else {
+            RT = 2;
+            KW = 4;
         }
         return;
     }
     if (CS == 1) {
         if (T >= 512) {
-            RT = M <= 8 ? 2 : 4;
-            KW = M <= 8 ? 2 : 4;
-            D = M <= 8 ? 4 : 2;
+            RT = q8 && M > 16 ? 4 : q8 ? 2 : 4;
+            KW = q8 ? (M > 16 ? 2 : 4) : (M <= 8 ? 2 : 4);
         } else {
             RT = 1;
             KW = 8;
@@ -673,7 +687,7 @@ hipError_t launch_tiles_cfg(const TilesPlan& p, const void* Wt, const void* Xq, 
     const int grid = p.CS == 1 ? p.groups * p.KP : (p.groups * p.KP + 7) / 8 * 8 * p.CS;
     hipLaunchKernelGGL((k_tiles<TF, MP, RT, KW, D>), dim3(grid), dim3(64 * RT * KW), p.lds, s, (const uint8_t*)Wt,
                        (const uint8_t*)Xq, Y, tickets, part, N, K, M, p.KP, p.spw, p.cs_slots, magic, p.CS,
-                       p.groups);
+                       p.groups, p.pre);
     return hipGetLastError();
 }
 
@@ -743,7 +757,11 @@ static bool tiles_resolve(bool q8, int N, int K, int M, int unroll, TilesPlan& p
     } else {
         tiles_default(q8, N, K, M, RT, KW, D, KP, CS);
     }
-    return tiles_plan(N, K, M, RT, KW, D, KP, CS, p);
+    const int late = D >= 10;   // D + 10: the other prologue order (measurements only)
+    if (late) D -= 10;
+    const bool ok = tiles_plan(N, K, M, RT, KW, D, KP, CS, p);
+    p.pre = !late;
+    return ok;
 }
 
 bool tiles_config(bool q8, int N, int K, int M, int unroll, size_t* ws_bytes) {

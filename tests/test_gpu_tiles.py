@@ -178,6 +178,24 @@ def test_tiles_column_slices(dg, dev, orc, fmt, cfg, cs, kp, M):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("cfg,kp,cs", [((1, 8, 2), 2, 1), ((2, 2, 4), 3, 1), ((4, 4, 2), 1, 2), ((4, 2, 2), 2, 2)],
+                         ids=str)
+@pytest.mark.parametrize("M", [5, 16, 24])
+def test_tiles_prologue_orders_give_identical_bits(dg, dev, orc, fmt, cfg, kp, cs, M):
+    """The weight loads of the first groups issued after the column copies
+    have landed (the default) or before (D + 10): the same arithmetic in the
+    same order, so the same bits."""
+    N, K = 200, 5888
+    Wq, Xq = _operands(orc, fmt, 670 + M, N, K, M)
+    Wt = _tiles(dg, dev, fmt, Wq, N, K)
+    a = _gpu(dg, dev, fmt, Wt, Xq, N, K, M, launch=dict(unroll=unroll(kp, *cfg, cs=cs)))
+    rt, kw, d = cfg
+    b = _gpu(dg, dev, fmt, Wt, Xq, N, K, M, launch=dict(unroll=unroll(kp, rt, kw, d + 10, cs=cs)))
+    assert np.array_equal(a, b)
+    assert_close(a, _ref(orc, fmt, Wq, Xq, N, K, M), TOL, f"{fmt} {cfg} KP={kp} CS={cs} M={M}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("cs,M", [(2, 10), (2, 16), (2, 17), (3, 24), (3, 20)])
 def test_tiles_column_slices_long_rows(dg, dev, orc, fmt, cs, M):
     """A 4096 x 14336 matrix, whose columns fit a workgroup's LDS only in
