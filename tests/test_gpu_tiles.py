@@ -267,6 +267,35 @@ def test_tiles_workspace_left_zero_and_calls_repeat_bit_for_bit(dg, dev, orc):
     assert np.array_equal(a, d)
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("N", [1, 17])
+@pytest.mark.parametrize("M", [1, 5, 24])
+def test_tiles_one_group_of_k(dg, dev, orc, fmt, N, M):
+    """K = 256: one group of 8 blocks per row tile, so every wave but the
+    first of a workgroup has no part; the defaults slice the columns here."""
+    K = 256
+    Wq, Xq = _operands(orc, fmt, 680 + M, N, K, M)
+    got = _gpu(dg, dev, fmt, _tiles(dg, dev, fmt, Wq, N, K), Xq, N, K, M)
+    assert_close(got, _ref(orc, fmt, Wq, Xq, N, K, M), TOL, f"{fmt} N={N} M={M}")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_tiles_empty_sums_and_empty_shapes(dg, dev, fmt):
+    """K = 0 writes zeros; N = 0 or M = 0 launch nothing and touch nothing."""
+    import torch
+    lib = dg.raw()
+    gemv = lib.dg_gemv_q4_0_tiles if fmt == "q4_0" else lib.dg_gemv_q8_0_tiles
+    Y = torch.full((5 * 33,), float("nan"), dtype=torch.float32, device=dev)
+    assert gemv(None, None, Y.data_ptr(), 33, 0, 5, None, 0, None) == 0
+    torch.cuda.synchronize()
+    assert not torch.any(Y != 0).item()
+    Y.fill_(float("nan"))
+    assert gemv(None, None, Y.data_ptr(), 0, 4096, 5, None, 0, None) == 0
+    assert gemv(None, None, Y.data_ptr(), 33, 4096, 0, None, 0, None) == 0
+    torch.cuda.synchronize()
+    assert torch.isnan(Y).all().item()
+
+
 def test_tiles_argument_errors(dg, dev):
     import torch
     N, K, M = 64, 28672, 24   # Q4_0 splits K at this shape by default
